@@ -1,0 +1,117 @@
+"""fp64 CPU oracle for the 2DMamba 2D selective scan — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package. The product path (the HIP library and its Python
+binding) never imports, loads or calls it, and shares no code with it.
+
+The arithmetic lives in ``ssm2d_oracle.c`` (plain fp64 loops over the two
+recurrences of the 2D selective scan, see that file's header for the equations
+and the passages they follow). This module only marshals numpy arrays.
+
+Functions
+---------
+build()                 compile ssm2d_oracle.c into libssm2d_oracle.so (gcc)
+fwd(x, delta, A, B, C, D, maps=None, nthreads=0) -> y (float64)
+states(abar, bx) -> h   the recurrences alone on given Abar, Bx (one map)
+max_threads()           OpenMP thread count the oracle uses by default
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm2d_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libssm2d_oracle.so")
+
+_lib = None
+
+
+def build(out_path: str = LIB_PATH, src_path: str = _SRC, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-std=c99", *extra_flags, src_path, "-o", out_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def load(path: str = LIB_PATH):
+    """Load a compiled oracle library (default: the in-tree one)."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.oracle_ssm2d_fwd_maps_f64.argtypes = [dp] * 7 + [i64] * 5 + [
+        ctypes.POINTER(i64), i64, ctypes.c_int]
+    lib.oracle_ssm2d_fwd_maps_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_states_f64.argtypes = [dp, dp, dp, i64, i64]
+    lib.oracle_ssm2d_states_f64.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"oracle library {LIB_PATH} is not built; run __graft_entry__.build()")
+        _lib = load(LIB_PATH)
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None):
+    """y = 2D selective scan forward in fp64.
+
+    x, delta: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
+    [batch][d_state][H][W]; D: [d_inner]. With ``maps`` (flat indices
+    b*d_inner+d), returns y for those maps only, shape [len(maps)][H][W];
+    otherwise the full [batch][d_inner][H][W].
+    """
+    lib = lib or _get()
+    x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))
+    batch, d_inner, H, W = x.shape
+    d_state = A.shape[1]
+    assert delta.shape == x.shape
+    assert A.shape == (d_inner, d_state) and D.shape == (d_inner,)
+    assert B.shape == (batch, d_state, H, W) and C.shape == B.shape
+    if maps is None:
+        y = np.empty((batch, d_inner, H, W), dtype=np.float64)
+        mp, nm = None, batch * d_inner
+    else:
+        m = np.ascontiguousarray(maps, dtype=np.int64)
+        y = np.empty((m.size, H, W), dtype=np.float64)
+        mp, nm = m.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), m.size
+    s = lib.oracle_ssm2d_fwd_maps_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(y), batch, d_inner, d_state, H, W,
+                                      mp, nm, int(nthreads))
+    if s != 0:
+        raise RuntimeError(f"oracle failed with status {s}")
+    return y
+
+
+def states(abar, bx, lib=None):
+    """h for one state map from given Abar [H][W] and Bx [H][W] (fp64)."""
+    lib = lib or _get()
+    abar, bx = _f64(abar), _f64(bx)
+    H, W = abar.shape
+    h = np.empty((H, W), dtype=np.float64)
+    s = lib.oracle_ssm2d_states_f64(_ptr(abar), _ptr(bx), _ptr(h), H, W)
+    if s != 0:
+        raise RuntimeError(f"oracle failed with status {s}")
+    return h
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or _get()).oracle_max_threads())

@@ -1,0 +1,150 @@
+/*
+ * fp64 CPU oracle for the 2DMamba 2D selective scan (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no source with the GPU kernels.
+ *
+ * What it computes, per batch b, channel d, state n and cell (i, j) of an
+ * H x W map (row-major, j fastest):
+ *
+ *   discretisation      Abar = exp(delta * A[d,n]),  Bx = delta * B[b,n,i,j] * x
+ *       (the pages name Abar and Bbar without defining them; this is the
+ *        zero-order-hold A / Euler B reading used by Mamba)
+ *   horizontal scan     hh[i,j] = Abar[i,j] * hh[i,j-1] + Bx[i,j],  hh[i,-1] = 0
+ *       (juejin.cn "2DMamba 精读", section 5(1) 横向扫描)
+ *   vertical scan       h[i,j]  = Abar[i,j] * h[i-1,j]  + hh[i,j],  h[-1,j] = 0
+ *       (same page, section 5(2) 纵向扫描; it scans the horizontal results,
+ *        papernotes.org "2DMamba", 关键设计: 2D选择性SSM架构)
+ *   output              y[i,j]  = sum_n C[b,n,i,j] * h[i,j] + D[d] * x[i,j]
+ *       (juejin.cn section 5, 最终输出 y = C h; the D x skip term is the
+ *        Mamba convention and is added here)
+ *
+ * Every step is executed literally, in the order written, in double precision,
+ * one state map at a time. There is no blocking, fusion or reordering.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* The two recurrences on one (b, d, n) state map.
+ * abar, bx: [H][W] inputs; h: [H][W] output. hh_row: scratch of length W. */
+static void scan_state_map(const double *abar, const double *bx, double *h,
+                           double *hh_row, int64_t H, int64_t W)
+{
+    for (int64_t i = 0; i < H; ++i) {
+        /* horizontal recurrence along row i, left to right, zero start */
+        double carry = 0.0;
+        for (int64_t j = 0; j < W; ++j) {
+            carry = abar[i * W + j] * carry + bx[i * W + j];
+            hh_row[j] = carry;
+        }
+        /* vertical recurrence down each column, over the horizontal results */
+        for (int64_t j = 0; j < W; ++j) {
+            double up = (i > 0) ? h[(i - 1) * W + j] : 0.0;
+            h[i * W + j] = abar[i * W + j] * up + hh_row[j];
+        }
+    }
+}
+
+/* Internal entry: the recurrences alone, on caller-supplied Abar and Bx.
+ * abar, bx, h: [H][W] doubles. Returns 0, or 2 on a bad size. */
+int oracle_ssm2d_states_f64(const double *abar, const double *bx, double *h,
+                            int64_t H, int64_t W)
+{
+    if (H < 0 || W < 0) return 2;
+    if (H == 0 || W == 0) return 0;
+    double *hh_row = (double *)malloc((size_t)W * sizeof(double));
+    if (!hh_row) return 6;
+    scan_state_map(abar, bx, h, hh_row, H, W);
+    free(hh_row);
+    return 0;
+}
+
+/* One (b, d) map: y_map[H][W]. */
+static int forward_one_map(const double *x, const double *delta, const double *A,
+                           const double *B, const double *C, const double *D,
+                           double *y_map, int64_t b, int64_t d, int64_t d_inner,
+                           int64_t d_state, int64_t H, int64_t W)
+{
+    const int64_t L = H * W;
+    const double *xm = x + (b * d_inner + d) * L;
+    const double *dm = delta + (b * d_inner + d) * L;
+    double *abar = (double *)malloc((size_t)L * sizeof(double));
+    double *bx = (double *)malloc((size_t)L * sizeof(double));
+    double *h = (double *)malloc((size_t)L * sizeof(double));
+    double *hh_row = (double *)malloc((size_t)W * sizeof(double));
+    if (!abar || !bx || !h || !hh_row) {
+        free(abar); free(bx); free(h); free(hh_row);
+        return 6;
+    }
+    for (int64_t p = 0; p < L; ++p) y_map[p] = 0.0;
+    for (int64_t n = 0; n < d_state; ++n) {
+        const double a = A[d * d_state + n];
+        const double *Bn = B + (b * d_state + n) * L;
+        const double *Cn = C + (b * d_state + n) * L;
+        for (int64_t p = 0; p < L; ++p) {
+            abar[p] = exp(dm[p] * a);
+            bx[p] = dm[p] * Bn[p] * xm[p];
+        }
+        scan_state_map(abar, bx, h, hh_row, H, W);
+        for (int64_t p = 0; p < L; ++p) y_map[p] += Cn[p] * h[p];
+    }
+    for (int64_t p = 0; p < L; ++p) y_map[p] += D[d] * xm[p];
+    free(abar); free(bx); free(h); free(hh_row);
+    return 0;
+}
+
+/* Forward pass over a list of (b, d) maps.
+ *
+ * x, delta: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
+ * [batch][d_state][H][W]; D: [d_inner]. maps: n_maps flat indices
+ * m = b * d_inner + d (NULL = all maps in order). y: [n_maps][H][W].
+ * nthreads: OpenMP threads (<= 0: runtime default).
+ * Returns 0 on success, 2 on a bad size or map index, 6 on allocation failure.
+ */
+int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double *A,
+                              const double *B, const double *C, const double *D,
+                              double *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                              int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
+                              int nthreads)
+{
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
+    const int64_t total = batch * d_inner;
+    if (maps == NULL) n_maps = total;
+    if (n_maps < 0) return 2;
+    for (int64_t k = 0; maps != NULL && k < n_maps; ++k)
+        if (maps[k] < 0 || maps[k] >= total) return 2;
+    if (n_maps == 0 || H == 0 || W == 0) return 0;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t k = 0; k < n_maps; ++k) {
+        const int64_t m = maps ? maps[k] : k;
+        int s = forward_one_map(x, delta, A, B, C, D, y + k * H * W, m / d_inner,
+                                m % d_inner, d_inner, d_state, H, W);
+        if (s != 0) {
+#pragma omp atomic write
+            status = s;
+        }
+    }
+    return status;
+}
+
+/* Number of threads the OpenMP runtime would use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
