@@ -1,0 +1,104 @@
+/*
+ * ssm2d.h — C ABI of the MI355X (gfx950) 2D selective scan library, libssm2d.so.
+ *
+ * The operation is the forward pass of the 2DMamba 2D selective scan
+ * (arXiv 2412.00678). For batch b, channel d < d_inner, state n < d_state and
+ * cell (i, j) of an H x W map:
+ *
+ *   Abar = exp(delta * A[d,n]),   Bx = delta * B[b,n,i,j] * x[b,d,i,j]
+ *   hh[i,j] = Abar * hh[i,j-1] + Bx          (horizontal scan, left to right)
+ *   h[i,j]  = Abar * h[i-1,j]  + hh[i,j]     (vertical scan over the horizontal results)
+ *   y[b,d,i,j] = sum_n C[b,n,i,j] * h[i,j] + D[d] * x[b,d,i,j]
+ *
+ * with zero state before the first column and above the first row.
+ * Passages: juejin.cn "2DMamba 精读" section 5 (横向扫描, 纵向扫描, final output
+ * y = C h); papernotes.org "2DMamba" 关键设计, items 2D选择性SSM架构 (row scans are
+ * 1D Mamba, the vertical scan runs over the horizontal results) and 硬件感知2D并行
+ * 扫描算子 (state dims reduced on chip, only the aggregate written back). The
+ * pages name Abar and Bbar without defining them: this library uses the
+ * zero-order-hold A and Euler B of Mamba. The D x skip term is the Mamba
+ * convention (the pages' output is y = C h).
+ *
+ * Layout: every tensor is dense row-major (C order), W fastest:
+ *   x, delta, y : [batch][d_inner][H][W]
+ *   B, C        : [batch][d_state][H][W]   (input dependent, shared by all d)
+ *   A           : [d_inner][d_state]       float32
+ *   D           : [d_inner]                float32
+ * All pointers are DEVICE pointers on the current HIP device, allocated and
+ * owned by the caller, 16-byte aligned. y must not alias any input. The library
+ * keeps no pointer after the call returns.
+ *
+ * Asynchrony: a call validates its arguments on the host, enqueues its kernels
+ * on `stream` (hipStream_t; NULL = the null stream) and returns without waiting.
+ * Launch errors are reported as SSM2D_ERR_HIP. The library keeps an internal
+ * workspace per (device, stream), zero-initialised when created; calls on the
+ * same stream are ordered, calls on different streams use different workspaces.
+ *
+ * Errors: every function returns a status and never throws or aborts.
+ *   batch, d_inner, d_state, H or W < 0          -> SSM2D_ERR_BAD_DIM
+ *   batch, d_inner, H or W == 0                  -> SSM2D_OK, nothing is launched
+ *   d_state == 0                                 -> valid: y = D x
+ *   d_state > SSM2D_MAX_STATE                    -> SSM2D_ERR_UNSUPPORTED
+ *   H or W > SSM2D_MAX_SIDE, or a tensor of 2^31 or more elements
+ *                                                -> SSM2D_ERR_UNSUPPORTED
+ *   any NULL pointer when there is work          -> SSM2D_ERR_NULLPTR
+ *   any pointer not 16-byte aligned              -> SSM2D_ERR_MISALIGNED
+ *   workspace allocation failure                 -> SSM2D_ERR_NOMEM
+ * NaN and Inf inputs are not checked; they propagate.
+ */
+#ifndef SSM2D_H
+#define SSM2D_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM2D_MAX_STATE 64
+#define SSM2D_MAX_SIDE 65535
+
+typedef enum {
+    SSM2D_OK = 0,
+    SSM2D_ERR_NULLPTR = 1,
+    SSM2D_ERR_BAD_DIM = 2,
+    SSM2D_ERR_UNSUPPORTED = 3,
+    SSM2D_ERR_MISALIGNED = 4,
+    SSM2D_ERR_HIP = 5,
+    SSM2D_ERR_NOMEM = 6,
+    SSM2D_ERR_DEVICE_TIMEOUT = 7
+} ssm2d_status;
+
+/* fp32 forward: x, delta, B, C, y are float32; A, D float32; state fp32. */
+int ssm2d_scan_fwd(const float *x, const float *delta, const float *A, const float *B,
+                   const float *C, const float *D, float *y, int64_t batch, int64_t d_inner,
+                   int64_t d_state, int64_t H, int64_t W, void *stream);
+
+/* bf16 forward: x, delta, B, C, y are bfloat16 (raw uint16 bits); A, D float32;
+ * the state and all arithmetic are fp32; y is rounded to bf16 (nearest-even). */
+int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                        const uint16_t *B, const uint16_t *C, const float *D, uint16_t *y,
+                        int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                        void *stream);
+
+/* Static description of a status code. Never NULL. */
+const char *ssm2d_status_string(int status);
+
+/* Waits for `stream`, then returns and clears the device-side error word of
+ * that stream's workspace: SSM2D_OK, or SSM2D_ERR_DEVICE_TIMEOUT if a kernel
+ * gave up waiting for a neighbouring tile's carries (its output is then
+ * invalid). Returns SSM2D_ERR_HIP if the wait fails. */
+int ssm2d_sync_check(void *stream);
+
+/* Test hook: bound on the polls a kernel makes while waiting for carries
+ * (0 = default, about one second). A tiny bound forces the timeout path. */
+int ssm2d_set_spin_limit(int64_t polls);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int ssm2d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM2D_H */

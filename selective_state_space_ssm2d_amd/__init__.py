@@ -1,0 +1,143 @@
+"""MI355X (gfx950) 2D selective scan — Python binding of libssm2d.so.
+
+This module only marshals arguments: it checks tensors, passes their device
+pointers and the current HIP stream to the C ABI declared in
+``include/ssm2d.h``, and turns status codes into exceptions. Every step of the
+scan runs in the library's HIP kernels. PyTorch supplies device memory and
+streams only. There is no fallback: if the library is missing the call fails.
+
+    y = scan_fwd(x, delta, A, B, C, D)
+
+x, delta: [batch, d_inner, H, W]; B, C: [batch, d_state, H, W]; all four
+float32 or all four bfloat16. A: [d_inner, d_state] float32; D: [d_inner]
+float32. y has the dtype of x. All tensors on the current CUDA (HIP) device,
+contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "status_string",
+    "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm2d.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm2d.h")
+
+OK, ERR_NULLPTR, ERR_BAD_DIM, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NOMEM, ERR_DEVICE_TIMEOUT = range(8)
+
+_lib = None
+
+
+class Ssm2dError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libssm2d.so and declare the C signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
+        f.restype = ctypes.c_int
+    lib.ssm2d_status_string.argtypes = [ctypes.c_int]
+    lib.ssm2d_status_string.restype = ctypes.c_char_p
+    lib.ssm2d_sync_check.argtypes = [vp]
+    lib.ssm2d_sync_check.restype = ctypes.c_int
+    lib.ssm2d_set_spin_limit.argtypes = [i64]
+    lib.ssm2d_set_spin_limit.restype = ctypes.c_int
+    lib.ssm2d_version.argtypes = []
+    lib.ssm2d_version.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def exported_names(header: str = HEADER_PATH):
+    """Function names the header declares (for the symbol-export check)."""
+    with open(header) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(ssm2d_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().ssm2d_status_string(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def sync_check(stream=None) -> None:
+    """Wait for the stream; raise if a kernel reported a device-side timeout."""
+    s = load_library().ssm2d_sync_check(_stream_handle(stream))
+    if s != OK:
+        raise Ssm2dError(s, "ssm2d_sync_check")
+
+
+def set_spin_limit(polls: int) -> None:
+    load_library().ssm2d_set_spin_limit(int(polls))
+
+
+def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
+    """y = 2D selective scan forward (see module docstring)."""
+    import torch
+
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x and B must be 4-D")
+    batch, d_inner, H, W = x.shape
+    d_state = B.shape[1]
+    if delta.shape != x.shape:
+        raise ValueError("delta must have the shape of x")
+    if B.shape != (batch, d_state, H, W) or C.shape != B.shape:
+        raise ValueError("B and C must be [batch, d_state, H, W]")
+    if A.shape != (d_inner, d_state) or D.shape != (d_inner,):
+        raise ValueError("A must be [d_inner, d_state] and D [d_inner]")
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    for name, t in (("delta", delta), ("B", B), ("C", C)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must have the dtype of x")
+    for name, t in (("A", A), ("D", D)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    tensors = [x, delta, A, B, C, D]
+    if y is None:
+        y = torch.empty_like(x)
+    elif y.shape != x.shape or y.dtype != dt:
+        raise ValueError("y must match x in shape and dtype")
+    tensors.append(y)
+    dev = x.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    fn = lib.ssm2d_scan_fwd if dt == torch.float32 else lib.ssm2d_scan_fwd_bf16
+    with torch.cuda.device(dev):
+        s = fn(*(ctypes.c_void_p(t.data_ptr()) for t in tensors), batch, d_inner, d_state, H, W,
+               _stream_handle(stream))
+    if s != OK:
+        raise Ssm2dError(s, fn.__name__)
+    return y

@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ssm2d.h declares, and validates arguments before any
+HIP call (so these paths return their documented status codes here)."""
+import ctypes
+import os
+
+import pytest
+
+import selective_state_space_ssm2d_amd as pkg
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkg.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return pkg.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = pkg.exported_names()
+    assert "ssm2d_scan_fwd" in names and "ssm2d_scan_fwd_bf16" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        text = lib.ssm2d_status_string(s)
+        assert text and text != b"unknown status", s
+    assert lib.ssm2d_status_string(99) == b"unknown status"
+    assert lib.ssm2d_version() >= 100
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or returns first
+
+
+def _call(lib, dims, ptrs=None, bf16=False):
+    ptrs = ptrs if ptrs is not None else [FAKE] * 7
+    fn = lib.ssm2d_scan_fwd_bf16 if bf16 else lib.ssm2d_scan_fwd
+    return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_negative_dims(lib, bf16):
+    for k in range(5):
+        dims = [1, 2, 3, 4, 5]
+        dims[k] = -1
+        assert _call(lib, dims, bf16=bf16) == pkg.ERR_BAD_DIM
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_zero_sizes_are_noops(lib, bf16):
+    # nothing is launched, so even null pointers are fine
+    for dims in ([0, 2, 3, 4, 5], [1, 0, 3, 4, 5], [1, 2, 3, 0, 5], [1, 2, 3, 4, 0]):
+        assert _call(lib, dims, ptrs=[0] * 7, bf16=bf16) == pkg.OK
+
+
+def test_unsupported_sizes(lib):
+    assert _call(lib, [1, 2, 65, 4, 5]) == pkg.ERR_UNSUPPORTED
+    assert _call(lib, [1, 2, 4, 65536, 5]) == pkg.ERR_UNSUPPORTED
+    assert _call(lib, [1 << 16, 1 << 16, 4, 2, 1]) == pkg.ERR_UNSUPPORTED
+
+
+def test_null_pointers(lib):
+    for k in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[k] = 0
+        assert _call(lib, [1, 2, 3, 4, 5], ptrs) == pkg.ERR_NULLPTR, k
+    # with d_state == 0, A, B and C are not read
+    ptrs = [FAKE, FAKE, 0, 0, 0, FAKE, FAKE]
+    assert _call(lib, [1, 2, 0, 4, 5], ptrs) != pkg.ERR_NULLPTR
+
+
+def test_misaligned(lib):
+    for k in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[k] = FAKE + 4
+        assert _call(lib, [1, 2, 3, 4, 5], ptrs) == pkg.ERR_MISALIGNED, k
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 3, 4)
+    B = torch.zeros(1, 5, 3, 4)
+    A, D = torch.zeros(2, 5), torch.zeros(2)
+    with pytest.raises(ValueError):
+        pkg.scan_fwd(x, x, A, B[:, :, :2], B, D)
+    with pytest.raises(TypeError):
+        pkg.scan_fwd(x.double(), x.double(), A, B.double(), B.double(), D)
+    with pytest.raises(ValueError):  # CPU tensors are refused: no host fallback
+        pkg.scan_fwd(x, x, A, B, B, D)
