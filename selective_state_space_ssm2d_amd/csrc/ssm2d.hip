@@ -8,21 +8,30 @@
 //
 // Work decomposition (gfx950-specific; the pages' CUDA tiling is prior art):
 //   * One wave = 64 lanes = 16 channels d x 4 state groups g. All lanes of a
-//     wave sit on the same cell at the same time, so B and C (shared by all
-//     channels) are broadcast loads, and x / delta are 16 contiguous row
-//     segments. Each lane keeps NPL states (n = g*NPL + k).
+//     wave work on the same cell at the same time, so B and C (shared by all
+//     channels) and x / delta (one row segment per channel) arrive together.
+//     Each lane keeps NPL states (n = g*NPL + k).
 //   * A lane walks a strip of K columns from the top row to the bottom row.
 //     Along a row it runs the horizontal recurrence sequentially; the vertical
-//     state of its K columns stays in registers. Nothing is padded to the
-//     wavefront width: a map needs only ceil(W/K) strips.
-//   * The horizontal carry (hh at the strip's right edge, per row) flows to the
-//     next strip. Strips of one (batch, channel block) form a chain: waves of a
-//     workgroup hand carries on through an LDS ring, workgroups through a
-//     global buffer with epoch-tagged progress counters. A strip only waits
-//     for the row it is about to process, so the chain runs as a pipeline.
-//   * Workgroups take tickets from an atomic counter; ticket order puts every
-//     producer before its consumer, so a waiting workgroup's producer is
-//     always resident or done.
+//     state of its K columns stays in registers. Only the strip's last
+//     columns are masked: nothing is padded to the wavefront width.
+//   * Inputs: a wave's whole input for one row (x and delta of 16 channels,
+//     B and C of 4*NPL states, K cells each) is a packet of 16-byte chunks,
+//     one coalesced load per lane. Packets are prefetched P rows ahead into a
+//     register ring and staged through a per-wave LDS packet buffer, from
+//     which each lane reads its operands (B and C reads are broadcasts).
+//   * The horizontal carry (hh at the strip's right edge, per row) flows to
+//     the next strip. Strips of one (batch, channel block) form a chain:
+//     waves of a workgroup hand carries on through an LDS ring, workgroups
+//     through tagged 64-bit words (epoch, row | value) written and polled with
+//     relaxed device-scope atomics, so no cache flush or invalidate is needed.
+//     A strip only waits for the row it is about to process: the chain is a
+//     pipeline, one row deep per strip.
+//   * Multi-workgroup chains take tickets from an atomic counter; ticket order
+//     puts every producer before its consumer, so a waiting workgroup's
+//     producer is resident or done. A bounded global ring with back-pressure
+//     is used only when the whole grid is co-resident; otherwise every row has
+//     its own slot and nothing ever waits on a consumer.
 //   * The sum over n: each lane holds K partial sums over its NPL states; two
 //     permlane swaps (32- and 16-lane) transpose-reduce them across the 4 state
 //     groups, leaving each lane with K/4 finished cells.
@@ -42,73 +51,110 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kGroups = 4;                 // state groups per wave
+constexpr int kGroups = 4;                     // state groups per wave
 constexpr int kChanPerWave = kWave / kGroups;  // channels per wave
-constexpr int kMaxStrips = 8;              // waves (strips) per workgroup
+constexpr int kMaxWaves = 8;                   // waves per workgroup (strips + courier)
+constexpr int kCourierBatch = 4;               // rows a courier moves per poll
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct Workspace {
-    unsigned int *ticket;        // [1] next ticket
-    unsigned int *done;          // [1] finished workgroups (last one resets both)
-    unsigned int *err;           // [1] device error word
-    unsigned long long *prog;    // [n_chains * groups] epoch<<32 | rows published
-    float *carry;                // [n_chains][groups-1][H][NPL][64]
-    void *zeros;                 // zero page: max(H*W) elements of 4 bytes
-};
 
 struct Params {
     const void *x, *delta, *B, *C;
     const float *A, *D;
     void *y;
-    const void *zeros;
+    const void *zeros;                 // zero page, >= H*W*4 bytes
+    void *sink;                        // write target of masked-off output lanes
     unsigned int *ticket, *done, *err;
-    unsigned long long *prog;
-    float *carry;
+    unsigned long long *gring;         // [n_bound][qg][NPL][64] tagged carries
+    unsigned long long *cons;          // [n_bound] consumer progress: epoch<<32 | rows
     int batch, d_inner, d_state, H, W;
     int nstrips, s_local, groups, n_dblk, n_chains, total_wg;
-    int ring_rows;     // LDS ring depth between waves
-    int publish_rows;  // rows between global progress updates
+    int ring_rows;                     // LDS ring depth between waves
+    int qg;                            // global ring depth (== H: no reuse)
+    int use_ticket;                    // chains span workgroups
+    int xcd_remap;                     // spread chains over XCDs in contiguous blocks
     unsigned int epoch;
     long long spin_limit;
-    int vec_ok;        // W % 4 == 0: strips can use vector loads
 };
 
-// Load N consecutive elements starting at p (fp32 or bf16 bits) into floats.
-// `valid` < N masks the tail with zeros. `vec` allows 16-byte loads (fp32) or
-// 8/16-byte loads (bf16), which needs N % 4 == 0 and a 16-byte aligned row.
-template <int N> __device__ __forceinline__ void load_row(const float *p, float (&v)[N], int valid, bool vec)
+template <typename T> struct ChunkOf;
+template <> struct ChunkOf<float> { using type = float4; };      // 4 fp32
+template <> struct ChunkOf<uint16_t> { using type = uint2; };    // 4 bf16
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// One 4-element chunk, read as 4/ALIGN unconditional loads of ALIGN elements.
+// Sub-loads that fall past the end of a row were pointed at the zero page when
+// the pointers were set up, so no load needs a mask.
+template <int ALIGN> struct Sub;
+template <> struct Sub<4> { using f = float4; using h = uint2; };
+template <> struct Sub<2> { using f = float2; using h = unsigned; };
+template <> struct Sub<1> { using f = float; using h = uint16_t; };
+
+template <int ALIGN>
+__device__ __forceinline__ float4 load_chunk(const float *const (&sp)[4 / ALIGN], long off)
 {
-    if constexpr (N % 4 == 0) {
-        if (vec && valid == N) {
-#pragma unroll
-            for (int q = 0; q < N / 4; ++q) {
-                float4 t = reinterpret_cast<const float4 *>(p)[q];
-                v[4 * q + 0] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-            }
-            return;
-        }
+    float4 v;
+    if constexpr (ALIGN == 4) {
+        v = *reinterpret_cast<const float4 *>(sp[0] + off);
+    } else if constexpr (ALIGN == 2) {
+        float2 a = *reinterpret_cast<const float2 *>(sp[0] + off);
+        float2 b = *reinterpret_cast<const float2 *>(sp[1] + off);
+        v.x = a.x; v.y = a.y; v.z = b.x; v.w = b.y;
+    } else {
+        v.x = sp[0][off]; v.y = sp[1][off]; v.z = sp[2][off]; v.w = sp[3][off];
     }
-#pragma unroll
-    for (int c = 0; c < N; ++c) v[c] = (c < valid) ? p[c] : 0.0f;
+    return v;
 }
 
-template <int N> __device__ __forceinline__ void load_row(const uint16_t *p, float (&v)[N], int valid, bool vec)
+template <int ALIGN>
+__device__ __forceinline__ uint2 load_chunk(const uint16_t *const (&sp)[4 / ALIGN], long off)
 {
-    if constexpr (N % 4 == 0) {
-        if (vec && valid == N) {
-#pragma unroll
-            for (int q = 0; q < N / 4; ++q) {
-                uint2 t = reinterpret_cast<const uint2 *>(p)[q];
-                v[4 * q + 0] = __uint_as_float(t.x << 16);
-                v[4 * q + 1] = __uint_as_float(t.x & 0xffff0000u);
-                v[4 * q + 2] = __uint_as_float(t.y << 16);
-                v[4 * q + 3] = __uint_as_float(t.y & 0xffff0000u);
-            }
-            return;
-        }
+    uint2 v;
+    if constexpr (ALIGN == 4) {
+        v = *reinterpret_cast<const uint2 *>(sp[0] + off);
+    } else if constexpr (ALIGN == 2) {
+        v.x = *reinterpret_cast<const unsigned *>(sp[0] + off);
+        v.y = *reinterpret_cast<const unsigned *>(sp[1] + off);
+    } else {
+        v.x = static_cast<unsigned>(sp[0][off]) | (static_cast<unsigned>(sp[1][off]) << 16);
+        v.y = static_cast<unsigned>(sp[2][off]) | (static_cast<unsigned>(sp[3][off]) << 16);
     }
+    return v;
+}
+
+// N consecutive packet elements (N % 4 == 0) starting at element offset `off`.
+template <int N>
+__device__ __forceinline__ void read_packet(const float *pk, int off, float (&v)[N])
+{
 #pragma unroll
-    for (int c = 0; c < N; ++c) v[c] = (c < valid) ? __uint_as_float(static_cast<unsigned>(p[c]) << 16) : 0.0f;
+    for (int q = 0; q < N / 4; ++q) {
+        float4 t = *reinterpret_cast<const float4 *>(pk + off + 4 * q);
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+}
+template <int N>
+__device__ __forceinline__ void read_packet(const uint16_t *pk, int off, float (&v)[N])
+{
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        uint2 t = *reinterpret_cast<const uint2 *>(pk + off + 4 * q);
+        v[4 * q] = bf16_lo(t.x); v[4 * q + 1] = bf16_hi(t.x);
+        v[4 * q + 2] = bf16_lo(t.y); v[4 * q + 3] = bf16_hi(t.y);
+    }
+}
+// N elements one by one.
+template <int N>
+__device__ __forceinline__ void read_packet_scalar(const float *pk, int off, float (&v)[N])
+{
+#pragma unroll
+    for (int c = 0; c < N; ++c) v[c] = pk[off + c];
+}
+template <int N>
+__device__ __forceinline__ void read_packet_scalar(const uint16_t *pk, int off, float (&v)[N])
+{
+#pragma unroll
+    for (int c = 0; c < N; ++c) v[c] = __uint_as_float(static_cast<unsigned>(pk[off + c]) << 16);
 }
 
 __device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
@@ -149,81 +195,229 @@ __device__ __forceinline__ void reduce_groups(const float (&p)[K], float (&out)[
 
 __device__ __forceinline__ void sleep_a_bit() { __builtin_amdgcn_s_sleep(2); }
 
-template <typename T, int K, int NPL>
-__global__ __launch_bounds__(kWave * kMaxStrips) void scan2d_fwd_kernel(Params p)
+__device__ __forceinline__ unsigned long long ld_relaxed(const unsigned long long *p)
 {
-    static_assert(K % kGroups == 0, "strip width must split over the 4 state groups");
-    extern __shared__ float ring[];  // [s_local-1][ring_rows][64][NPL]
-    __shared__ int s_done[kMaxStrips];
-    __shared__ int s_used[kMaxStrips];
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NPL> constexpr int passes_for(int K) { return ((32 + 8 * NPL) * (K / 4) + kWave - 1) / kWave; }
+template <int NPL> constexpr int prefetch_rows(int K) { return passes_for<NPL>(K) == 1 ? 4 : 2; }
+
+template <typename T, int K, int NPL, int ALIGN>
+__global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
+{
+    static_assert(K % kGroups == 0 && K % 4 == 0, "strip width must be a multiple of 4");
+    using Chunk = typename ChunkOf<T>::type;
+    constexpr int KO = K / kGroups;                   // finished cells per lane and row
+    constexpr int SEG_X = 0, SEG_DT = 16, SEG_B = 32, SEG_C = 32 + 4 * NPL;
+    constexpr int SEGROWS = 32 + 8 * NPL;             // packet rows of K elements
+    constexpr int CPR = K / 4;                        // chunks per packet row
+    constexpr int NCHUNK = SEGROWS * CPR;
+    constexpr int PASSES = passes_for<NPL>(K);
+    constexpr int P = prefetch_rows<NPL>(K);          // rows per prefetch buffer
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_done[kMaxWaves + 1];   // rows published into LDS ring b
+    __shared__ int s_used[kMaxWaves + 1];   // rows consumed from LDS ring b
     __shared__ unsigned int s_ticket;
 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    if (threadIdx.x == 0)
+    if (p.use_ticket && threadIdx.x == 0)
         s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x < kMaxStrips) {
+    if (threadIdx.x <= kMaxWaves) {
         s_done[threadIdx.x] = 0;
         s_used[threadIdx.x] = 0;
     }
     __syncthreads();
 
-    const int ticket = static_cast<int>(s_ticket);
-    const int chain = ticket % p.n_chains;
-    const int grp = ticket / p.n_chains;
+    int wg;
+    if (p.use_ticket) {
+        wg = static_cast<int>(s_ticket);
+    } else if (p.xcd_remap) {
+        // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+        // contiguous run of chains so chains sharing a batch entry (and its
+        // B, C) share that XCD's L2.
+        const int per = p.total_wg / 8;
+        wg = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    } else {
+        wg = blockIdx.x;
+    }
+    const int chain = wg % p.n_chains;
+    const int grp = wg / p.n_chains;
     const int b = chain / p.n_dblk;
     const int dblk = chain % p.n_dblk;
-    const int strip = grp * p.s_local + wave;
     const int H = p.H, W = p.W;
+    const int RM = p.ring_rows - 1;                   // ring depth is a power of two
+    const long ring_floats = static_cast<long>(p.ring_rows) * kWave * NPL;
+    float *lring = reinterpret_cast<float *>(smem + static_cast<long>(p.s_local) * NCHUNK * sizeof(Chunk));
 
-    if (strip < p.nstrips) {
+    if (wave == p.s_local) {
+        // ---------------- courier: global ring <-> LDS rings 0 and s_local
+        const bool in_act = grp > 0;
+        const bool out_act = (grp + 1) * p.s_local < p.nstrips;
+        const long nb_per_chain = p.groups - 1;
+        const long bound_in = chain * nb_per_chain + (grp - 1);
+        const long bound_out = chain * nb_per_chain + grp;
+        const long gstride = static_cast<long>(p.qg) * NPL * kWave;
+        const unsigned long long *gin = p.gring + bound_in * gstride + lane;
+        unsigned long long *gout = p.gring + bound_out * gstride + lane;
+        float *ring0 = lring;
+        const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
+        const unsigned int etag = p.epoch << 16;
+        const unsigned long long ctag = static_cast<unsigned long long>(p.epoch) << 32;
+        int in_next = 0, out_next = 0, cons_seen = 0;
+        long idle = 0;
+        bool timed_out = false;
+        while ((in_act && in_next < H) || (out_act && out_next < H)) {
+            bool progress = false;
+            if (in_act && in_next < H) {
+                const int used0 = __hip_atomic_load(&s_used[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int nb = min(min(kCourierBatch, H - in_next), used0 + p.ring_rows - in_next);
+                if (nb > 0) {
+                    unsigned long long w[kCourierBatch][NPL];
+#pragma unroll
+                    for (int r = 0; r < kCourierBatch; ++r)
+                        if (r < nb)
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k)
+                                w[r][k] = ld_relaxed(gin + (static_cast<long>((in_next + r) % p.qg) * NPL + k) * kWave);
+                    int v = 0;
+#pragma unroll
+                    for (int r = 0; r < kCourierBatch; ++r) {
+                        if (r < nb && v == r) {
+                            const unsigned long long want = static_cast<unsigned long long>(etag | static_cast<unsigned>(in_next + r)) << 32;
+                            bool ok = true;
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k) ok = ok && ((w[r][k] & 0xffffffff00000000ull) == want);
+                            if (__all(ok)) {
+                                float *dst = ring0 + (static_cast<long>((in_next + r) & RM) * kWave + lane) * NPL;
+#pragma unroll
+                                for (int k = 0; k < NPL; ++k) dst[k] = __uint_as_float(static_cast<unsigned>(w[r][k] & 0xffffffffu));
+                                v = r + 1;
+                            }
+                        }
+                    }
+                    if (v > 0) {
+                        in_next += v;
+                        __hip_atomic_store(&s_done[0], in_next, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
+                        progress = true;
+                    }
+                }
+            }
+            if (out_act && out_next < H) {
+                const int avail = __hip_atomic_load(&s_done[p.s_local], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                int nb = min(kCourierBatch, avail - out_next);
+                if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
+                    const unsigned long long v = ld_relaxed(p.cons + bound_out);
+                    if ((v & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(v & 0xffffffffu);
+                    nb = min(nb, cons_seen + p.qg - out_next);
+                }
+                if (nb > 0) {
+#pragma unroll
+                    for (int r = 0; r < kCourierBatch; ++r) {
+                        if (r < nb) {
+                            const int row = out_next + r;
+                            const float *src_c = ringS + (static_cast<long>(row & RM) * kWave + lane) * NPL;
+                            const unsigned long long tagw = static_cast<unsigned long long>(etag | static_cast<unsigned>(row)) << 32;
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k)
+                                st_relaxed(gout + (static_cast<long>(row % p.qg) * NPL + k) * kWave,
+                                           tagw | __float_as_uint(src_c[k]));
+                        }
+                    }
+                    out_next += nb;
+                    __hip_atomic_store(&s_used[p.s_local], out_next, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    progress = true;
+                }
+            }
+            if (progress) {
+                idle = 0;
+            } else {
+                if (++idle > p.spin_limit) { timed_out = true; break; }
+                sleep_a_bit();
+            }
+        }
+        if (timed_out) {
+            atomicOr(p.err, 1u);
+            // let the compute waves of this workgroup run to the end
+            __hip_atomic_store(&s_done[0], H, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&s_used[p.s_local], H, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    } else if (grp * p.s_local + wave < p.nstrips) {
+        // ---------------- compute wave: one strip
+        const int strip = grp * p.s_local + wave;
         const int j0 = strip * K;
         const int valid = min(K, W - j0);
-        const bool vec = p.vec_ok != 0;
         const int g = lane / kChanPerWave;
-        const int d = dblk * kChanPerWave + lane % kChanPerWave;
+        const int dl = lane % kChanPerWave;
+        const int d = dblk * kChanPerWave + dl;
         const bool d_ok = d < p.d_inner;
         const long HW = static_cast<long>(H) * W;
         const T *zeros = static_cast<const T *>(p.zeros);
+        T *packet = reinterpret_cast<T *>(smem) + static_cast<long>(wave) * NCHUNK * 4;
 
-        // Channel rows (zero page for channels past d_inner).
-        const T *xrow = d_ok ? static_cast<const T *>(p.x) + (static_cast<long>(b) * p.d_inner + d) * HW + j0 : zeros;
-        const T *drow = d_ok ? static_cast<const T *>(p.delta) + (static_cast<long>(b) * p.d_inner + d) * HW + j0 : zeros;
-        T *yrow = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (d_ok ? d : 0)) * HW + j0;
-        const T *Brow[NPL];
-        const T *Crow[NPL];
+        // Chunk sources of this lane: packet row r, chunk q of that row, split
+        // into 4/ALIGN sub-loads; a sub-load past the row end reads the zero page.
+        constexpr int NSUB = 4 / ALIGN;
+        const T *src[PASSES][NSUB];
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+            const int c = pp * kWave + lane;
+            const int r = c / CPR, q = c % CPR;
+            const T *base = zeros;
+            if (c < NCHUNK) {
+                if (r < SEG_DT) {
+                    const int dd = dblk * kChanPerWave + r;
+                    if (dd < p.d_inner) base = static_cast<const T *>(p.x) + (static_cast<long>(b) * p.d_inner + dd) * HW;
+                } else if (r < SEG_B) {
+                    const int dd = dblk * kChanPerWave + r - SEG_DT;
+                    if (dd < p.d_inner) base = static_cast<const T *>(p.delta) + (static_cast<long>(b) * p.d_inner + dd) * HW;
+                } else if (r < SEG_C) {
+                    const int n = r - SEG_B;
+                    if (n < p.d_state) base = static_cast<const T *>(p.B) + (static_cast<long>(b) * p.d_state + n) * HW;
+                } else {
+                    const int n = r - SEG_C;
+                    if (n < p.d_state) base = static_cast<const T *>(p.C) + (static_cast<long>(b) * p.d_state + n) * HW;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < NSUB; ++e) {
+                const int col = j0 + 4 * q + e * ALIGN;
+                src[pp][e] = ((col + ALIGN <= W) ? base : zeros) + col;
+            }
+        }
+
         float Ap[NPL];
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
             const int n = g * NPL + k;
-            const bool n_ok = n < p.d_state;
-            Brow[k] = n_ok ? static_cast<const T *>(p.B) + (static_cast<long>(b) * p.d_state + n) * HW + j0 : zeros;
-            Crow[k] = n_ok ? static_cast<const T *>(p.C) + (static_cast<long>(b) * p.d_state + n) * HW + j0 : zeros;
-            Ap[k] = (n_ok && d_ok) ? p.A[d * p.d_state + n] * kLog2e : 0.0f;
+            Ap[k] = (n < p.d_state && d_ok) ? p.A[d * p.d_state + n] * kLog2e : 0.0f;
         }
         const float Dd = d_ok ? p.D[d] : 0.0f;
-        // Cells this lane finishes after the group reduction.
-        constexpr int KO = K / kGroups;
-        const int c_out = g * KO;
+        const int c_out = g * KO;  // first of this lane's finished cells
+        // Output cells of this lane; cells outside the map go to the sink.
+        T *ydst[KO];
+        long ystep[KO];
+#pragma unroll
+        for (int c = 0; c < KO; ++c) {
+            const bool ok = d_ok && (c_out + c < valid);
+            ydst[c] = ok ? static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + d) * HW + j0 + c_out + c
+                         : static_cast<T *>(p.sink) + lane * KO + c;
+            ystep[c] = ok ? W : 0;
+        }
 
-        // Neighbours in the chain.
         const bool has_left = strip > 0;
-        const bool left_in_lds = has_left && wave > 0;
         const bool has_right = strip + 1 < p.nstrips;
-        const bool right_in_lds = has_right && wave + 1 < p.s_local;
-        const bool right_global = has_right && !right_in_lds;
-        const int R = p.ring_rows;
-        float *ring_in = ring + static_cast<long>(wave - 1) * R * kWave * NPL;
-        float *ring_out = ring + static_cast<long>(wave) * R * kWave * NPL;
-        unsigned long long *prog_in = p.prog + static_cast<long>(chain) * p.groups + (grp - 1);
-        unsigned long long *prog_out = p.prog + static_cast<long>(chain) * p.groups + grp;
-        const long carry_stride = static_cast<long>(H) * NPL * kWave;  // one boundary
-        const float *gin = p.carry + (static_cast<long>(chain) * (p.groups - 1) + (grp - 1)) * carry_stride;
-        float *gout = p.carry + (static_cast<long>(chain) * (p.groups - 1) + grp) * carry_stride;
-        const unsigned long long tag = static_cast<unsigned long long>(p.epoch) << 32;
-
-        int avail = 0;      // rows the left neighbour has published (as seen)
-        int room = R;       // rows this wave may publish before the ring is full
+        const float *ring_in = lring + static_cast<long>(wave) * ring_floats;
+        float *ring_out = lring + static_cast<long>(wave + 1) * ring_floats;
+        int avail = 0;      // rows the left neighbour has published, as seen
+        int room = 0;       // rows this wave may publish, as seen
         bool timed_out = false;
 
         float hv[K][NPL];
@@ -232,53 +426,39 @@ __global__ __launch_bounds__(kWave * kMaxStrips) void scan2d_fwd_kernel(Params p
 #pragma unroll
             for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
 
-        for (int i = 0; i < H; ++i) {
-            const long roff = static_cast<long>(i) * W;
-            // ---- inputs of row i (independent of the carry: issue first)
+        auto do_row = [&](const int i, const Chunk (&cb)[PASSES]) {
+            // ---- stage row i's packet and read this lane's operands
+#pragma unroll
+            for (int pp = 0; pp < PASSES; ++pp)
+                if (pp * kWave + lane < NCHUNK) reinterpret_cast<Chunk *>(packet)[pp * kWave + lane] = cb[pp];
             float xv[K], dv[K], Bv[NPL][K], Cv[NPL][K], xo[KO];
-            load_row<K>(xrow + roff, xv, valid, vec);
-            load_row<K>(drow + roff, dv, valid, vec);
+            read_packet<K>(packet, (SEG_X + dl) * K, xv);
+            read_packet<K>(packet, (SEG_DT + dl) * K, dv);
 #pragma unroll
             for (int k = 0; k < NPL; ++k) {
-                load_row<K>(Brow[k] + roff, Bv[k], valid, vec);
-                load_row<K>(Crow[k] + roff, Cv[k], valid, vec);
+                read_packet<K>(packet, (SEG_B + g * NPL + k) * K, Bv[k]);
+                read_packet<K>(packet, (SEG_C + g * NPL + k) * K, Cv[k]);
             }
-            load_row<KO>(xrow + roff + c_out, xo, valid - c_out, false);
+            read_packet_scalar<KO>(packet, (SEG_X + dl) * K + c_out, xo);
 
             // ---- left carry of row i
             float hh[NPL];
             if (!has_left) {
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
-            } else if (left_in_lds) {
+            } else {
                 if (i >= avail && !timed_out) {
                     long spins = 0;
-                    while ((avail = __hip_atomic_load(&s_done[wave - 1], __ATOMIC_ACQUIRE,
+                    while ((avail = __hip_atomic_load(&s_done[wave], __ATOMIC_ACQUIRE,
                                                       __HIP_MEMORY_SCOPE_WORKGROUP)) <= i) {
                         if (++spins > p.spin_limit) { timed_out = true; break; }
                         sleep_a_bit();
                     }
                 }
-                const float *src = ring_in + (static_cast<long>(i % R) * kWave + lane) * NPL;
+                const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) hh[k] = src[k];
-                __hip_atomic_store(&s_used[wave - 1], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            } else {
-                if (i >= avail && !timed_out) {
-                    long spins = 0;
-                    for (;;) {
-                        unsigned long long v = __hip_atomic_load(prog_in, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((v & 0xffffffff00000000ull) == tag) {
-                            avail = static_cast<int>(v & 0xffffffffu);
-                            if (avail > i) break;
-                        }
-                        if (++spins > p.spin_limit) { timed_out = true; break; }
-                        sleep_a_bit();
-                    }
-                }
-                const float *src = gin + static_cast<long>(i) * NPL * kWave + lane;
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) hh[k] = src[k * kWave];
+                for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
+                __hip_atomic_store(&s_used[wave], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
 
             // ---- the scan over this row's K cells
@@ -299,48 +479,67 @@ __global__ __launch_bounds__(kWave * kMaxStrips) void scan2d_fwd_kernel(Params p
             }
 
             // ---- hand the right-edge carry on
-            if (right_in_lds) {
+            if (has_right) {
                 if (i >= room && !timed_out) {
                     long spins = 0;
                     int used;
-                    while ((used = __hip_atomic_load(&s_used[wave], __ATOMIC_ACQUIRE,
-                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) + R <= i) {
+                    while ((used = __hip_atomic_load(&s_used[wave + 1], __ATOMIC_ACQUIRE,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) + p.ring_rows <= i) {
                         if (++spins > p.spin_limit) { timed_out = true; break; }
                         sleep_a_bit();
                     }
-                    room = used + R;
+                    room = used + p.ring_rows;
                 }
-                float *dst = ring_out + (static_cast<long>(i % R) * kWave + lane) * NPL;
+                float *dst = ring_out + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) dst[k] = hh[k];
-                __hip_atomic_store(&s_done[wave], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            } else if (right_global) {
-                float *dst = gout + static_cast<long>(i) * NPL * kWave + lane;
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) dst[k * kWave] = hh[k];
-                if ((i + 1) % p.publish_rows == 0 || i + 1 == H)
-                    __hip_atomic_store(prog_out, tag | static_cast<unsigned long long>(i + 1),
-                                       __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&s_done[wave + 1], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
 
             // ---- sum over the state groups, skip term, store
             float out[KO];
             reduce_groups<K>(part, out);
-            if (d_ok) {
 #pragma unroll
-                for (int c = 0; c < KO; ++c)
-                    if (c_out + c < valid) store_elem(yrow + roff + c_out + c, out[c] + Dd * xo[c]);
-            }
+            for (int c = 0; c < KO; ++c) store_elem(ydst[c] + static_cast<long>(i) * ystep[c], out[c] + Dd * xo[c]);
+        };
+
+        // Two prefetch buffers of P rows: while one buffer's rows are
+        // computed, the other's loads are in flight.
+        Chunk bufA[P][PASSES], bufB[P][PASSES];
+#pragma unroll
+        for (int s = 0; s < P; ++s)
+#pragma unroll
+            for (int pp = 0; pp < PASSES; ++pp)
+                bufA[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(s, H - 1)) * W);
+        for (int i0 = 0; i0 < H; i0 += 2 * P) {
+#pragma unroll
+            for (int s = 0; s < P; ++s)
+#pragma unroll
+                for (int pp = 0; pp < PASSES; ++pp)
+                    bufB[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(i0 + P + s, H - 1)) * W);
+#pragma unroll
+            for (int s = 0; s < P; ++s)
+                if (i0 + s < H) do_row(i0 + s, bufA[s]);
+#pragma unroll
+            for (int s = 0; s < P; ++s)
+#pragma unroll
+                for (int pp = 0; pp < PASSES; ++pp)
+                    bufA[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(i0 + 2 * P + s, H - 1)) * W);
+#pragma unroll
+            for (int s = 0; s < P; ++s)
+                if (i0 + P + s < H) do_row(i0 + P + s, bufB[s]);
         }
         if (timed_out) atomicOr(p.err, 1u);
     }
 
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned int old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (old + 1 == static_cast<unsigned int>(p.total_wg)) {
-            __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.use_ticket) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned int old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == static_cast<unsigned int>(p.total_wg)) {
+                __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -348,7 +547,7 @@ __global__ __launch_bounds__(kWave * kMaxStrips) void scan2d_fwd_kernel(Params p
 // ---------------------------------------------------------------- host side
 
 struct Plan {
-    int K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, publish_rows;
+    int K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
 };
 
 int env_int(const char *name, int dflt)
@@ -363,36 +562,50 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     int npl = 1;
     while (npl * kGroups < d_state) npl *= 2;
     pl.npl = npl;
-    pl.K = 4;
-    pl.K = env_int("SSM2D_STRIP", pl.K);
+    pl.K = env_int("SSM2D_STRIP", 4);
     if (pl.K != 4 && pl.K != 8) pl.K = 4;
-    if (npl == 16) pl.K = 4;
+    if (npl >= 8 || W % 4 != 0) pl.K = 4;
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     pl.n_dblk = static_cast<int>((d_inner + kChanPerWave - 1) / kChanPerWave);
     pl.n_chains = static_cast<int>(batch) * pl.n_dblk;
-    // Enough workgroups to cover the chip; otherwise keep a whole chain in
-    // one workgroup so the carries stay in LDS.
-    int want_wg = 512;
-    int groups = (pl.n_chains >= want_wg) ? 1 : (want_wg + pl.n_chains - 1) / pl.n_chains;
-    int s_local = (pl.nstrips + groups - 1) / groups;
-    if (s_local < 1) s_local = 1;
-    if (s_local > kMaxStrips) s_local = kMaxStrips;
+    // Enough workgroups to cover the chip (256 CUs). With that many chains,
+    // and a chain short enough for one workgroup, carries stay in LDS.
+    // Otherwise chains are cut into groups of s_local strips linked by a
+    // courier wave (so at most kMaxWaves - 1 strips per workgroup).
+    const int want_wg = 256;
+    int s_local;
+    if (pl.n_chains >= want_wg && pl.nstrips <= kMaxWaves) {
+        s_local = pl.nstrips;
+    } else {
+        const int groups = (pl.n_chains >= want_wg) ? 1 : (want_wg + pl.n_chains - 1) / pl.n_chains;
+        s_local = (pl.nstrips + groups - 1) / groups;
+        if (s_local < 4) s_local = 4;
+    }
     s_local = env_int("SSM2D_WAVES", s_local);
     if (s_local < 1) s_local = 1;
-    if (s_local > kMaxStrips) s_local = kMaxStrips;
     if (s_local > pl.nstrips) s_local = pl.nstrips;
+    if (s_local > kMaxWaves) s_local = kMaxWaves;
+    if (s_local < pl.nstrips && s_local > kMaxWaves - 1) s_local = kMaxWaves - 1;
     pl.s_local = s_local;
     pl.groups = (pl.nstrips + s_local - 1) / s_local;
     pl.total_wg = pl.n_chains * pl.groups;
-    pl.ring_rows = (npl <= 4) ? 8 : (npl == 8 ? 4 : 2);
-    pl.publish_rows = env_int("SSM2D_PUBLISH", 2);
-    if (pl.publish_rows < 1) pl.publish_rows = 1;
+    // LDS ring depth: a power of two, at least 2, the rings within ~48 KB.
+    const long row_bytes = static_cast<long>(kWave) * npl * 4;
+    int R = 8;
+    while (R > 2 && (s_local + 1) * R * row_bytes > 48 * 1024) R /= 2;
+    pl.ring_rows = R;
+    pl.qg = static_cast<int>(H);
     return pl;
 }
 
+constexpr size_t kHeadBytes = 256;   // ticket, done, err
+constexpr size_t kSinkBytes = 4096;  // >= 64 lanes x 8 cells x 4 bytes
+
 struct WsEntry {
-    Workspace ws{};
-    size_t carry_bytes = 0, zero_bytes = 0, prog_count = 0;
+    unsigned int *head = nullptr;          // ticket, done, err, then cons[]
+    unsigned long long *gring = nullptr;
+    void *zeros = nullptr;
+    size_t gring_bytes = 0, zero_bytes = 0, cons_count = 0;
     unsigned int epoch = 0;
 };
 
@@ -402,67 +615,126 @@ long long g_spin_limit = 0;
 
 void free_ws(WsEntry &e)
 {
-    if (e.ws.ticket) (void)hipFree(e.ws.ticket);
-    if (e.ws.carry) (void)hipFree(e.ws.carry);
-    if (e.ws.zeros) (void)hipFree(e.ws.zeros);
+    if (e.head) (void)hipFree(e.head);
+    if (e.gring) (void)hipFree(e.gring);
+    if (e.zeros) (void)hipFree(e.zeros);
     e = WsEntry{};
 }
 
 // Workspace for (device, stream), grown when needed. Growth waits for the
-// stream so that no in-flight kernel still uses the old buffers.
-int get_ws(int dev, void *stream, size_t carry_bytes, size_t zero_bytes, size_t prog_count, WsEntry **out)
+// stream so that no in-flight kernel still uses the old buffers. Fresh
+// buffers are zeroed; tags are never zero, so no stale word matches.
+int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t cons_count, WsEntry **out)
 {
     WsEntry &e = g_ws[{dev, stream}];
-    if (e.ws.ticket && carry_bytes <= e.carry_bytes && zero_bytes <= e.zero_bytes && prog_count <= e.prog_count) {
+    if (e.head && gring_bytes <= e.gring_bytes && zero_bytes <= e.zero_bytes && cons_count <= e.cons_count) {
         *out = &e;
         return SSM2D_OK;
     }
-    if (e.ws.ticket) {
+    unsigned int epoch = e.epoch;
+    if (e.head) {
         if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SSM2D_ERR_HIP;
         free_ws(e);
     }
-    size_t cb = carry_bytes < 256 ? 256 : carry_bytes;
+    size_t gb = gring_bytes < 256 ? 256 : gring_bytes;
     size_t zb = zero_bytes < 256 ? 256 : zero_bytes;
-    size_t pc = prog_count < 1 ? 1 : prog_count;
-    size_t head = 256 + pc * sizeof(unsigned long long);
-    void *h = nullptr, *c = nullptr, *z = nullptr;
-    if (hipMalloc(&h, head) != hipSuccess || hipMalloc(&c, cb) != hipSuccess || hipMalloc(&z, zb) != hipSuccess) {
+    size_t cc = cons_count < 1 ? 1 : cons_count;
+    size_t head = kHeadBytes + kSinkBytes + cc * sizeof(unsigned long long);
+    void *h = nullptr, *g = nullptr, *z = nullptr;
+    if (hipMalloc(&h, head) != hipSuccess || hipMalloc(&g, gb) != hipSuccess || hipMalloc(&z, zb) != hipSuccess) {
         if (h) (void)hipFree(h);
-        if (c) (void)hipFree(c);
+        if (g) (void)hipFree(g);
         (void)hipGetLastError();
         return SSM2D_ERR_NOMEM;
     }
-    if (hipMemset(h, 0, head) != hipSuccess || hipMemset(z, 0, zb) != hipSuccess) return SSM2D_ERR_HIP;
-    e.ws.ticket = static_cast<unsigned int *>(h);
-    e.ws.done = e.ws.ticket + 1;
-    e.ws.err = e.ws.ticket + 2;
-    e.ws.prog = reinterpret_cast<unsigned long long *>(static_cast<char *>(h) + 256);
-    e.ws.carry = static_cast<float *>(c);
-    e.ws.zeros = z;
-    e.carry_bytes = cb;
+    if (hipMemset(h, 0, head) != hipSuccess || hipMemset(g, 0, gb) != hipSuccess ||
+        hipMemset(z, 0, zb) != hipSuccess)
+        return SSM2D_ERR_HIP;
+    e.head = static_cast<unsigned int *>(h);
+    e.gring = static_cast<unsigned long long *>(g);
+    e.zeros = z;
+    e.gring_bytes = gb;
     e.zero_bytes = zb;
-    e.prog_count = pc;
-    e.epoch = 0;
+    e.cons_count = cc;
+    e.epoch = epoch;
     *out = &e;
     return SSM2D_OK;
 }
 
-template <typename T, int K, int NPL>
-hipError_t launch(const Params &prm, const Plan &pl, hipStream_t stream)
+int device_cus(int dev)
 {
-    size_t lds = static_cast<size_t>(pl.s_local > 1 ? pl.s_local - 1 : 0) * pl.ring_rows * kWave * NPL * sizeof(float);
-    hipLaunchKernelGGL((scan2d_fwd_kernel<T, K, NPL>), dim3(pl.total_wg), dim3(kWave * pl.s_local), lds, stream, prm);
-    return hipGetLastError();
+    static std::map<int, int> cache;
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev] = n;
+    return n;
 }
 
-template <typename T>
-hipError_t dispatch(const Params &prm, const Plan &pl, hipStream_t stream)
+int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 1 : 0)); }
+
+template <typename T, int K, int NPL>
+size_t lds_bytes(const Plan &pl)
 {
-#define SSM2D_CASE(KK, NN) if (pl.K == KK && pl.npl == NN) return launch<T, KK, NN>(prm, pl, stream);
-    SSM2D_CASE(4, 1) SSM2D_CASE(4, 2) SSM2D_CASE(4, 4) SSM2D_CASE(4, 8) SSM2D_CASE(4, 16)
-    SSM2D_CASE(8, 1) SSM2D_CASE(8, 2) SSM2D_CASE(8, 4) SSM2D_CASE(8, 8)
-#undef SSM2D_CASE
-    return hipErrorInvalidValue;
+    using Chunk = typename ChunkOf<T>::type;
+    const size_t nchunk = static_cast<size_t>(32 + 8 * NPL) * (K / 4);
+    return static_cast<size_t>(pl.s_local) * nchunk * sizeof(Chunk) +
+           static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
+}
+
+// Global ring depth: bounded (with back-pressure) only if the whole grid is
+// co-resident, so that a producer never waits on a consumer that cannot run.
+template <typename T, int K, int NPL, int ALIGN>
+int choose_qg(const Plan &pl, int dev, int H)
+{
+    if (pl.groups <= 1) return H;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN>, block_threads(pl),
+                                                     lds_bytes<T, K, NPL>(pl)) != hipSuccess) {
+        (void)hipGetLastError();
+        return H;
+    }
+    const long resident = static_cast<long>(per_cu) * device_cus(dev);
+    const int qg = env_int("SSM2D_RING", 32);
+    if (resident >= pl.total_wg && qg >= 8 && qg < H) return qg;
+    return H;
+}
+
+template <typename T, int K, int NPL, int ALIGN>
+int run(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+        int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
+{
+    pl.qg = choose_qg<T, K, NPL, ALIGN>(pl, dev, H);
+    const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
+    const size_t gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
+    const size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
+    WsEntry *e = nullptr;
+    int st = get_ws(dev, stream, gring_bytes, zero_bytes, static_cast<size_t>(n_bound > 0 ? n_bound : 1), &e);
+    if (st != SSM2D_OK) return st;
+    e->epoch = (e->epoch + 1) & 0xffffu;
+    if (e->epoch == 0) e->epoch = 1;  // tags are (epoch << 16 | row); zero never matches
+
+    Params prm{};
+    prm.x = x; prm.delta = delta;
+    prm.B = d_state ? static_cast<const void *>(B) : e->zeros;
+    prm.C = d_state ? static_cast<const void *>(C) : e->zeros;
+    prm.A = A; prm.D = D; prm.y = y; prm.zeros = e->zeros;
+    prm.ticket = e->head; prm.done = e->head + 1; prm.err = e->head + 2;
+    prm.sink = reinterpret_cast<char *>(e->head) + kHeadBytes;
+    prm.cons = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(e->head) + kHeadBytes + kSinkBytes);
+    prm.gring = e->gring;
+    prm.batch = batch; prm.d_inner = d_inner; prm.d_state = d_state; prm.H = H; prm.W = W;
+    prm.nstrips = pl.nstrips; prm.s_local = pl.s_local; prm.groups = pl.groups; prm.n_dblk = pl.n_dblk;
+    prm.n_chains = pl.n_chains; prm.total_wg = pl.total_wg; prm.ring_rows = pl.ring_rows; prm.qg = pl.qg;
+    prm.use_ticket = pl.groups > 1 ? 1 : 0;
+    prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
+    prm.epoch = e->epoch;
+    prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
+    const size_t lds = lds_bytes<T, K, NPL>(pl);
+    scan2d_fwd_kernel<T, K, NPL, ALIGN><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
+                                   static_cast<hipStream_t>(stream)>>>(prm);
+    return hipGetLastError() == hipSuccess ? SSM2D_OK : SSM2D_ERR_HIP;
 }
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -486,28 +758,18 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SSM2D_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mutex);
-    const size_t carry_bytes = static_cast<size_t>(pl.n_chains) * (pl.groups - 1) * H * pl.npl * kWave * sizeof(float);
-    const size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
-    WsEntry *e = nullptr;
-    int st = get_ws(dev, stream, carry_bytes, zero_bytes, static_cast<size_t>(pl.n_chains) * pl.groups, &e);
-    if (st != SSM2D_OK) return st;
-    e->epoch += 1;
-    if (e->epoch == 0) e->epoch = 1;  // 0 marks never-written progress counters
-
-    Params prm{};
-    prm.x = x; prm.delta = delta; prm.B = d_state ? B : e->ws.zeros; prm.C = d_state ? C : e->ws.zeros;
-    prm.A = A; prm.D = D; prm.y = y; prm.zeros = e->ws.zeros;
-    prm.ticket = e->ws.ticket; prm.done = e->ws.done; prm.err = e->ws.err;
-    prm.prog = e->ws.prog; prm.carry = e->ws.carry;
-    prm.batch = static_cast<int>(batch); prm.d_inner = static_cast<int>(d_inner);
-    prm.d_state = static_cast<int>(d_state); prm.H = static_cast<int>(H); prm.W = static_cast<int>(W);
-    prm.nstrips = pl.nstrips; prm.s_local = pl.s_local; prm.groups = pl.groups; prm.n_dblk = pl.n_dblk;
-    prm.n_chains = pl.n_chains; prm.total_wg = pl.total_wg; prm.ring_rows = pl.ring_rows;
-    prm.publish_rows = pl.publish_rows; prm.epoch = e->epoch;
-    prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
-    prm.vec_ok = (W % 4 == 0) ? 1 : 0;
-    hipError_t err = dispatch<T>(prm, pl, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? SSM2D_OK : SSM2D_ERR_HIP;
+    const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
+    const int hi = static_cast<int>(H), wi = static_cast<int>(W);
+    const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
+#define SSM2D_CASE(KK, NN, AL) \
+    if (pl.K == KK && pl.npl == NN && align == AL) \
+        return run<T, KK, NN, AL>(x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream);
+    SSM2D_CASE(4, 1, 4) SSM2D_CASE(4, 2, 4) SSM2D_CASE(4, 4, 4) SSM2D_CASE(4, 8, 4) SSM2D_CASE(4, 16, 4)
+    SSM2D_CASE(8, 1, 4) SSM2D_CASE(8, 2, 4) SSM2D_CASE(8, 4, 4)
+    SSM2D_CASE(4, 1, 2) SSM2D_CASE(4, 2, 2) SSM2D_CASE(4, 4, 2) SSM2D_CASE(4, 8, 2) SSM2D_CASE(4, 16, 2)
+    SSM2D_CASE(4, 1, 1) SSM2D_CASE(4, 2, 1) SSM2D_CASE(4, 4, 1) SSM2D_CASE(4, 8, 1) SSM2D_CASE(4, 16, 1)
+#undef SSM2D_CASE
+    return SSM2D_ERR_UNSUPPORTED;
 }
 
 }  // namespace
@@ -550,12 +812,12 @@ int ssm2d_sync_check(void *stream)
     if (hipGetDevice(&dev) != hipSuccess) return SSM2D_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mutex);
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || !it->second.ws.err) return SSM2D_OK;
+    if (it == g_ws.end() || !it->second.head) return SSM2D_OK;
     unsigned int v = 0;
-    if (hipMemcpy(&v, it->second.ws.err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SSM2D_ERR_HIP;
+    if (hipMemcpy(&v, it->second.head + 2, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SSM2D_ERR_HIP;
     if (v != 0) {
         unsigned int z = 0;
-        if (hipMemcpy(it->second.ws.err, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return SSM2D_ERR_HIP;
+        if (hipMemcpy(it->second.head + 2, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return SSM2D_ERR_HIP;
         return SSM2D_ERR_DEVICE_TIMEOUT;
     }
     return SSM2D_OK;
@@ -568,6 +830,6 @@ int ssm2d_set_spin_limit(int64_t polls)
     return SSM2D_OK;
 }
 
-int ssm2d_version(void) { return 100; }
+int ssm2d_version(void) { return 200; }
 
 }  // extern "C"
