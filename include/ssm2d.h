@@ -94,6 +94,10 @@ int ssm2d_sync_check(void *stream);
  * (0 = default, about one second). A tiny bound forces the timeout path. */
 int ssm2d_set_spin_limit(int64_t polls);
 
+/* Text of the last HIP runtime error behind an SSM2D_ERR_HIP status
+ * ("no error" if there was none). Static storage; never NULL. */
+const char *ssm2d_last_hip_error(void);
+
 /* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
 int ssm2d_version(void);
 

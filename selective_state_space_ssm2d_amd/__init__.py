@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssm2d_set_spin_limit.restype = ctypes.c_int
     lib.ssm2d_version.argtypes = []
     lib.ssm2d_version.restype = ctypes.c_int
+    lib.ssm2d_last_hip_error.argtypes = []
+    lib.ssm2d_last_hip_error.restype = ctypes.c_char_p
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -138,6 +140,8 @@ def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
     with torch.cuda.device(dev):
         s = fn(*(ctypes.c_void_p(t.data_ptr()) for t in tensors), batch, d_inner, d_state, H, W,
                _stream_handle(stream))
+    if s == ERR_HIP:
+        raise Ssm2dError(s, f"{fn.__name__} ({lib.ssm2d_last_hip_error().decode()})")
     if s != OK:
         raise Ssm2dError(s, fn.__name__)
     return y

@@ -39,6 +39,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -54,7 +55,7 @@ constexpr int kWave = 64;
 constexpr int kGroups = 4;                     // state groups per wave
 constexpr int kChanPerWave = kWave / kGroups;  // channels per wave
 constexpr int kMaxWaves = 8;                   // waves per workgroup (strips + courier)
-constexpr int kCourierBatch = 4;               // rows a courier moves per poll
+constexpr int kCourierBatch = 4;               // rows a courier requests per poll
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Params {
@@ -195,6 +196,45 @@ __device__ __forceinline__ void reduce_groups(const float (&p)[K], float (&out)[
 
 __device__ __forceinline__ void sleep_a_bit() { __builtin_amdgcn_s_sleep(2); }
 
+// Wave-uniform read of an LDS progress counter (kept in a scalar register so
+// the waits below compile to scalar branches, not exec-mask juggling).
+__device__ __forceinline__ int lds_counter(const int *c)
+{
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ void lds_publish(int *c, int v)
+{
+    __hip_atomic_store(c, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Relaxed LDS counter access. A wave's LDS accesses execute in order, so a
+// counter written after a ring slot (or read before it) orders the two without
+// a hardware wait; signal_fence() keeps the compiler from reordering them.
+__device__ __forceinline__ int lds_peek(const int *c)
+{
+    return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_poke(int *c, int v)
+{
+    __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void signal_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// Polls counter *c until it exceeds `need` (returns the value seen), or
+// until `limit` polls have failed (sets `timed_out`).
+__device__ __forceinline__ int wait_counter_above(const int *c, int need, long long limit, bool &timed_out)
+{
+    long long spins = 0;
+    int v;
+    while ((v = lds_counter(c)) <= need) {
+        if (++spins > limit) {
+            timed_out = true;
+            break;
+        }
+        sleep_a_bit();
+    }
+    return v;
+}
+
 __device__ __forceinline__ unsigned long long ld_relaxed(const unsigned long long *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -225,7 +265,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
     __shared__ int s_used[kMaxWaves + 1];   // rows consumed from LDS ring b
     __shared__ unsigned int s_ticket;
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     if (p.use_ticket && threadIdx.x == 0)
         s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
         while ((in_act && in_next < H) || (out_act && out_next < H)) {
             bool progress = false;
             if (in_act && in_next < H) {
-                const int used0 = __hip_atomic_load(&s_used[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int used0 = lds_counter(&s_used[0]);
                 const int nb = min(min(kCourierBatch, H - in_next), used0 + p.ring_rows - in_next);
                 if (nb > 0) {
                     unsigned long long w[kCourierBatch][NPL];
@@ -304,14 +344,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
                     }
                     if (v > 0) {
                         in_next += v;
-                        __hip_atomic_store(&s_done[0], in_next, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        lds_publish(&s_done[0], in_next);
                         if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
                         progress = true;
                     }
                 }
             }
             if (out_act && out_next < H) {
-                const int avail = __hip_atomic_load(&s_done[p.s_local], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int avail = lds_counter(&s_done[p.s_local]);
                 int nb = min(kCourierBatch, avail - out_next);
                 if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
                     const unsigned long long v = ld_relaxed(p.cons + bound_out);
@@ -332,7 +372,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
                         }
                     }
                     out_next += nb;
-                    __hip_atomic_store(&s_used[p.s_local], out_next, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    lds_publish(&s_used[p.s_local], out_next);
                     progress = true;
                 }
             }
@@ -402,8 +442,9 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
         const float Dd = d_ok ? p.D[d] : 0.0f;
         const int c_out = g * KO;  // first of this lane's finished cells
         // Output cells of this lane; cells outside the map go to the sink.
+        // The pointers advance one row per processed row.
         T *ydst[KO];
-        long ystep[KO];
+        int ystep[KO];
 #pragma unroll
         for (int c = 0; c < KO; ++c) {
             const bool ok = d_ok && (c_out + c < valid);
@@ -441,90 +482,117 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
             }
             read_packet_scalar<KO>(packet, (SEG_X + dl) * K + c_out, xo);
 
-            // ---- left carry of row i
+            // ---- left carry of row i: the counter and the ring slot are read
+            // together (LDS executes a wave's accesses in order, and the
+            // producer writes the slot before the counter), before the
+            // carry-independent work below, so their latency overlaps it.
             float hh[NPL];
-            if (!has_left) {
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
-            } else {
-                if (i >= avail && !timed_out) {
-                    long spins = 0;
-                    while ((avail = __hip_atomic_load(&s_done[wave], __ATOMIC_ACQUIRE,
-                                                      __HIP_MEMORY_SCOPE_WORKGROUP)) <= i) {
-                        if (++spins > p.spin_limit) { timed_out = true; break; }
-                        sleep_a_bit();
-                    }
-                }
+            int seen = 0;
+            if (has_left) {
+                seen = lds_peek(&s_done[wave]);
+                signal_fence();
                 const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
-                __hip_atomic_store(&s_used[wave], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
             }
 
-            // ---- the scan over this row's K cells
-            float part[K];
+            // ---- carry-independent work: decay factors and inputs of the row
+            float av[K][NPL], bx[K][NPL];
 #pragma unroll
             for (int c = 0; c < K; ++c) {
-                const float dt = dv[c];
-                const float dx = dt * xv[c];
-                float acc = 0.0f;
+                const float dx = dv[c] * xv[c];
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) {
-                    const float a = __builtin_amdgcn_exp2f(dt * Ap[k]);
-                    hh[k] = __builtin_fmaf(a, hh[k], dx * Bv[k][c]);
-                    hv[c][k] = __builtin_fmaf(a, hv[c][k], hh[k]);
-                    acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                    av[c][k] = __builtin_amdgcn_exp2f(dv[c] * Ap[k]);
+                    bx[c][k] = dx * Bv[k][c];
                 }
-                part[c] = acc;
             }
 
-            // ---- hand the right-edge carry on
-            if (has_right) {
-                if (i >= room && !timed_out) {
-                    long spins = 0;
-                    int used;
-                    while ((used = __hip_atomic_load(&s_used[wave + 1], __ATOMIC_ACQUIRE,
-                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) + p.ring_rows <= i) {
-                        if (++spins > p.spin_limit) { timed_out = true; break; }
-                        sleep_a_bit();
-                    }
-                    room = used + p.ring_rows;
+            if (has_left) {
+                if (__builtin_amdgcn_readfirstlane(seen) <= i && !timed_out) {
+                    // not published yet: poll, then read the slot again
+                    wait_counter_above(&s_done[wave], i, p.spin_limit, timed_out);
+                    signal_fence();
+                    const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
                 }
+            }
+
+            // ---- horizontal recurrence along the row, then hand the carry on
+            float hc[K][NPL];
+#pragma unroll
+            for (int c = 0; c < K; ++c)
+#pragma unroll
+                for (int k = 0; k < NPL; ++k) {
+                    hh[k] = __builtin_fmaf(av[c][k], hh[k], bx[c][k]);
+                    hc[c][k] = hh[k];
+                }
+            if (has_right) {
+                if (i >= room && !timed_out)
+                    room = wait_counter_above(&s_used[wave + 1], i - p.ring_rows, p.spin_limit, timed_out) + p.ring_rows;
                 float *dst = ring_out + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) dst[k] = hh[k];
-                __hip_atomic_store(&s_done[wave + 1], i + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                signal_fence();
+                lds_poke(&s_done[wave + 1], i + 1);
+            }
+            if (has_left) lds_poke(&s_used[wave], i + 1);
+
+            // ---- vertical recurrence and the sum over this lane's states
+            float part[K];
+#pragma unroll
+            for (int c = 0; c < K; ++c) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < NPL; ++k) {
+                    hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
+                    acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                }
+                part[c] = acc;
             }
 
             // ---- sum over the state groups, skip term, store
             float out[KO];
             reduce_groups<K>(part, out);
 #pragma unroll
-            for (int c = 0; c < KO; ++c) store_elem(ydst[c] + static_cast<long>(i) * ystep[c], out[c] + Dd * xo[c]);
+            for (int c = 0; c < KO; ++c) {
+                store_elem(ydst[c], out[c] + Dd * xo[c]);
+                ydst[c] += ystep[c];
+            }
         };
 
         // Two prefetch buffers of P rows: while one buffer's rows are
-        // computed, the other's loads are in flight.
+        // computed, the other's loads are in flight. Full blocks of 2P rows
+        // run without per-row guards (a guard would make the compiler copy
+        // the register-resident state at every row); the last, partial block
+        // runs guarded.
         Chunk bufA[P][PASSES], bufB[P][PASSES];
-#pragma unroll
-        for (int s = 0; s < P; ++s)
-#pragma unroll
-            for (int pp = 0; pp < PASSES; ++pp)
-                bufA[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(s, H - 1)) * W);
-        for (int i0 = 0; i0 < H; i0 += 2 * P) {
+        auto load_rows = [&](Chunk (&buf)[P][PASSES], const int first) {
 #pragma unroll
             for (int s = 0; s < P; ++s)
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp)
-                    bufB[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(i0 + P + s, H - 1)) * W);
+                    buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s, H - 1)) * W);
+        };
+        load_rows(bufA, 0);
+        int i0 = 0;
+        for (; i0 + 2 * P <= H; i0 += 2 * P) {
+            load_rows(bufB, i0 + P);
+#pragma unroll
+            for (int s = 0; s < P; ++s) do_row(i0 + s, bufA[s]);
+            load_rows(bufA, i0 + 2 * P);
+#pragma unroll
+            for (int s = 0; s < P; ++s) do_row(i0 + P + s, bufB[s]);
+        }
+        if (i0 < H) {
+            load_rows(bufB, i0 + P);
 #pragma unroll
             for (int s = 0; s < P; ++s)
                 if (i0 + s < H) do_row(i0 + s, bufA[s]);
-#pragma unroll
-            for (int s = 0; s < P; ++s)
-#pragma unroll
-                for (int pp = 0; pp < PASSES; ++pp)
-                    bufA[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(i0 + 2 * P + s, H - 1)) * W);
 #pragma unroll
             for (int s = 0; s < P; ++s)
                 if (i0 + P + s < H) do_row(i0 + P + s, bufB[s]);
@@ -589,10 +657,12 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     pl.s_local = s_local;
     pl.groups = (pl.nstrips + s_local - 1) / s_local;
     pl.total_wg = pl.n_chains * pl.groups;
-    // LDS ring depth: a power of two, at least 2, the rings within ~48 KB.
+    // LDS ring depth: a power of two, at least 2 (and at least a courier
+    // batch), with all rings of a workgroup within ~48 KB.
     const long row_bytes = static_cast<long>(kWave) * npl * 4;
+    const long budget = 48 * 1024;
     int R = 8;
-    while (R > 2 && (s_local + 1) * R * row_bytes > 48 * 1024) R /= 2;
+    while (R > 2 && (s_local + 1) * R * row_bytes > budget) R /= 2;
     pl.ring_rows = R;
     pl.qg = static_cast<int>(H);
     return pl;
@@ -610,6 +680,19 @@ struct WsEntry {
 };
 
 std::mutex g_mutex;
+std::atomic<int> g_last_hip_error{hipSuccess};
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip_error.store(static_cast<int>(e));
+    return SSM2D_ERR_HIP;
+}
+
+#define SSM2D_HIP_TRY(call)                               \
+    do {                                                  \
+        const hipError_t e_ = (call);                     \
+        if (e_ != hipSuccess) return hip_fail(e_);        \
+    } while (0)
 std::map<std::pair<int, void *>, WsEntry> g_ws;
 long long g_spin_limit = 0;
 
@@ -633,7 +716,7 @@ int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t 
     }
     unsigned int epoch = e.epoch;
     if (e.head) {
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SSM2D_ERR_HIP;
+        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
         free_ws(e);
     }
     size_t gb = gring_bytes < 256 ? 256 : gring_bytes;
@@ -647,9 +730,9 @@ int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t 
         (void)hipGetLastError();
         return SSM2D_ERR_NOMEM;
     }
-    if (hipMemset(h, 0, head) != hipSuccess || hipMemset(g, 0, gb) != hipSuccess ||
-        hipMemset(z, 0, zb) != hipSuccess)
-        return SSM2D_ERR_HIP;
+    SSM2D_HIP_TRY(hipMemset(h, 0, head));
+    SSM2D_HIP_TRY(hipMemset(g, 0, gb));
+    SSM2D_HIP_TRY(hipMemset(z, 0, zb));
     e.head = static_cast<unsigned int *>(h);
     e.gring = static_cast<unsigned long long *>(g);
     e.zeros = z;
@@ -734,7 +817,8 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     const size_t lds = lds_bytes<T, K, NPL>(pl);
     scan2d_fwd_kernel<T, K, NPL, ALIGN><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
                                    static_cast<hipStream_t>(stream)>>>(prm);
-    return hipGetLastError() == hipSuccess ? SSM2D_OK : SSM2D_ERR_HIP;
+    const hipError_t err = hipGetLastError();
+    return err == hipSuccess ? SSM2D_OK : hip_fail(err);
 }
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -756,7 +840,7 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 
     const Plan pl = make_plan(batch, d_inner, d_state, H, W);
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SSM2D_ERR_HIP;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(g_mutex);
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
@@ -807,17 +891,17 @@ const char *ssm2d_status_string(int status)
 
 int ssm2d_sync_check(void *stream)
 {
-    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SSM2D_ERR_HIP;
+    SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SSM2D_ERR_HIP;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(g_mutex);
     auto it = g_ws.find({dev, stream});
     if (it == g_ws.end() || !it->second.head) return SSM2D_OK;
     unsigned int v = 0;
-    if (hipMemcpy(&v, it->second.head + 2, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SSM2D_ERR_HIP;
+    SSM2D_HIP_TRY(hipMemcpy(&v, it->second.head + 2, sizeof(v), hipMemcpyDeviceToHost));
     if (v != 0) {
         unsigned int z = 0;
-        if (hipMemcpy(it->second.head + 2, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return SSM2D_ERR_HIP;
+        SSM2D_HIP_TRY(hipMemcpy(it->second.head + 2, &z, sizeof(z), hipMemcpyHostToDevice));
         return SSM2D_ERR_DEVICE_TIMEOUT;
     }
     return SSM2D_OK;
@@ -831,5 +915,10 @@ int ssm2d_set_spin_limit(int64_t polls)
 }
 
 int ssm2d_version(void) { return 200; }
+
+const char *ssm2d_last_hip_error(void)
+{
+    return hipGetErrorString(static_cast<hipError_t>(g_last_hip_error.load()));
+}
 
 }  // extern "C"
