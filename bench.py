@@ -13,6 +13,9 @@ consecutive steps exceeds the 256 MB Infinity Cache: every step reads HBM.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -40,6 +43,68 @@ def algorithmic_bytes(wl) -> int:
     return E * 3 * s + wl.batch * wl.d_state * wl.H * wl.W * 2 * s + wl.d_inner * wl.d_state * 4 + wl.d_inner * 4
 
 
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_ssm2d_amd", "csrc", "ssm2d.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def copy_probe(mb: int, steps: int) -> None:
+    """A plain device-to-device copy of known size, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+
+    n = mb * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mb": mb, "steps": steps}))
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str):
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} under {run_dir}")
+    v = sorted(vals.values())
+    return v[len(v) // 2]  # median over dispatches
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                copy_mb: int) -> None:
+    """Turns four rocprofv3 --pmc runs (scan FETCH_SIZE, scan WRITE_SIZE, copy
+    FETCH_SIZE, copy WRITE_SIZE; KiB per dispatch) into calibrated HBM bytes
+    per launch of the scan kernel: profiles/traffic_<workload>.json."""
+    copy_bytes = copy_mb * 1024 * 1024
+    cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy") * 1024.0
+    cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy") * 1024.0
+    sf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "scan2d_fwd_kernel") * 1024.0
+    sw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "scan2d_fwd_kernel") * 1024.0
+    kf, kw = copy_bytes / cf, copy_bytes / cw
+    rec = {
+        "workload": workload,
+        "kernel": "scan2d_fwd_kernel",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "copy_probe_bytes": copy_bytes,
+        "copy_fetch_counter_bytes": cf, "copy_write_counter_bytes": cw,
+        "fetch_scale": kf, "write_scale": kw,
+        "scan_fetch_counter_bytes": sf, "scan_write_counter_bytes": sw,
+        "fetch_bytes_per_launch": sf * kf, "write_bytes_per_launch": sw * kw,
+        "bytes_per_launch": sf * kf + sw * kw,
+    }
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,7 +113,18 @@ def main():
     ap.add_argument("--workload", default="gigapixel_wsi")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-maps", type=int, default=0, help="oracle sample size in (b,d) maps (0 = all)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("SCAN_FETCH", "SCAN_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output directories")
+    ap.add_argument("--copy-mb", type=int, default=512)
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary, copy_mb=args.copy_mb)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -110,11 +186,15 @@ def main():
     flops = E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
     tflops = flops / (kmean * 1e-3) / 1e12
 
+    # HBM bytes per launch from the committed counter summary, only while it
+    # describes the kernel as it is now
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
 
     cpu = None
     if not args.no_cpu_baseline:

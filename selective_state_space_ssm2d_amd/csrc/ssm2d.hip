@@ -54,7 +54,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kGroups = 4;                     // state groups per wave
 constexpr int kChanPerWave = kWave / kGroups;  // channels per wave
-constexpr int kMaxWaves = 8;                   // waves per workgroup (strips + courier)
+constexpr int kMaxWaves = 8;                   // waves per workgroup (strips + couriers)
 constexpr int kCourierBatch = 4;               // rows a courier requests per poll
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -296,28 +296,27 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
     const long ring_floats = static_cast<long>(p.ring_rows) * kWave * NPL;
     float *lring = reinterpret_cast<float *>(smem + static_cast<long>(p.s_local) * NCHUNK * sizeof(Chunk));
 
-    if (wave == p.s_local) {
-        // ---------------- courier: global ring <-> LDS rings 0 and s_local
-        const bool in_act = grp > 0;
-        const bool out_act = (grp + 1) * p.s_local < p.nstrips;
+    if (wave >= p.s_local) {
+        // ---------------- couriers between the global ring and the LDS rings.
+        // Wave s_local brings the left workgroup's carries into LDS ring 0;
+        // wave s_local + 1 sends LDS ring s_local to the right workgroup. They
+        // are separate waves so that waiting for loads never also waits for
+        // the write-through of stores (one counter tracks both).
         const long nb_per_chain = p.groups - 1;
-        const long bound_in = chain * nb_per_chain + (grp - 1);
-        const long bound_out = chain * nb_per_chain + grp;
         const long gstride = static_cast<long>(p.qg) * NPL * kWave;
-        const unsigned long long *gin = p.gring + bound_in * gstride + lane;
-        unsigned long long *gout = p.gring + bound_out * gstride + lane;
-        float *ring0 = lring;
-        const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
         const unsigned int etag = p.epoch << 16;
         const unsigned long long ctag = static_cast<unsigned long long>(p.epoch) << 32;
-        int in_next = 0, out_next = 0, cons_seen = 0;
         long idle = 0;
         bool timed_out = false;
-        while ((in_act && in_next < H) || (out_act && out_next < H)) {
-            bool progress = false;
-            if (in_act && in_next < H) {
+        if (wave == p.s_local && grp > 0) {
+            const long bound_in = chain * nb_per_chain + (grp - 1);
+            const unsigned long long *gin = p.gring + bound_in * gstride + lane;
+            float *ring0 = lring;
+            int in_next = 0;
+            while (in_next < H) {
                 const int used0 = lds_counter(&s_used[0]);
                 const int nb = min(min(kCourierBatch, H - in_next), used0 + p.ring_rows - in_next);
+                int v = 0;
                 if (nb > 0) {
                     unsigned long long w[kCourierBatch][NPL];
 #pragma unroll
@@ -326,7 +325,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
 #pragma unroll
                             for (int k = 0; k < NPL; ++k)
                                 w[r][k] = ld_relaxed(gin + (static_cast<long>((in_next + r) % p.qg) * NPL + k) * kWave);
-                    int v = 0;
 #pragma unroll
                     for (int r = 0; r < kCourierBatch; ++r) {
                         if (r < nb && v == r) {
@@ -342,20 +340,29 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
                             }
                         }
                     }
-                    if (v > 0) {
-                        in_next += v;
-                        lds_publish(&s_done[0], in_next);
-                        if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
-                        progress = true;
-                    }
+                }
+                if (v > 0) {
+                    in_next += v;
+                    lds_publish(&s_done[0], in_next);
+                    if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
+                    idle = 0;
+                } else {
+                    if (++idle > p.spin_limit) { timed_out = true; break; }
+                    sleep_a_bit();
                 }
             }
-            if (out_act && out_next < H) {
+            if (timed_out) lds_publish(&s_done[0], H);  // let wave 0 run to the end
+        } else if (wave == p.s_local + 1 && (grp + 1) * p.s_local < p.nstrips) {
+            const long bound_out = chain * nb_per_chain + grp;
+            unsigned long long *gout = p.gring + bound_out * gstride + lane;
+            const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
+            int out_next = 0, cons_seen = 0;
+            while (out_next < H) {
                 const int avail = lds_counter(&s_done[p.s_local]);
                 int nb = min(kCourierBatch, avail - out_next);
                 if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
-                    const unsigned long long v = ld_relaxed(p.cons + bound_out);
-                    if ((v & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(v & 0xffffffffu);
+                    const unsigned long long c = ld_relaxed(p.cons + bound_out);
+                    if ((c & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(c & 0xffffffffu);
                     nb = min(nb, cons_seen + p.qg - out_next);
                 }
                 if (nb > 0) {
@@ -373,22 +380,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
                     }
                     out_next += nb;
                     lds_publish(&s_used[p.s_local], out_next);
-                    progress = true;
+                    idle = 0;
+                } else {
+                    if (++idle > p.spin_limit) { timed_out = true; break; }
+                    sleep_a_bit();
                 }
             }
-            if (progress) {
-                idle = 0;
-            } else {
-                if (++idle > p.spin_limit) { timed_out = true; break; }
-                sleep_a_bit();
-            }
+            if (timed_out) lds_publish(&s_used[p.s_local], H);  // let the last wave run to the end
         }
-        if (timed_out) {
-            atomicOr(p.err, 1u);
-            // let the compute waves of this workgroup run to the end
-            __hip_atomic_store(&s_done[0], H, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_store(&s_used[p.s_local], H, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
+        if (timed_out) atomicOr(p.err, 1u);
     } else if (grp * p.s_local + wave < p.nstrips) {
         // ---------------- compute wave: one strip
         const int strip = grp * p.s_local + wave;
@@ -630,17 +630,20 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     int npl = 1;
     while (npl * kGroups < d_state) npl *= 2;
     pl.npl = npl;
-    pl.K = env_int("SSM2D_STRIP", 4);
-    if (pl.K != 4 && pl.K != 8) pl.K = 4;
-    if (npl >= 8 || W % 4 != 0) pl.K = 4;
-    pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     pl.n_dblk = static_cast<int>((d_inner + kChanPerWave - 1) / kChanPerWave);
     pl.n_chains = static_cast<int>(batch) * pl.n_dblk;
     // Enough workgroups to cover the chip (256 CUs). With that many chains,
-    // and a chain short enough for one workgroup, carries stay in LDS.
-    // Otherwise chains are cut into groups of s_local strips linked by a
-    // courier wave (so at most kMaxWaves - 1 strips per workgroup).
+    // keep each chain in one workgroup (its carries stay in LDS), widening the
+    // strips to 8 columns if that makes the chain fit. Otherwise chains are cut
+    // into groups of s_local strips linked by two courier waves (so at most
+    // kMaxWaves - 2 strips per workgroup).
     const int want_wg = 256;
+    const bool wide_ok = npl <= 4 && W % 4 == 0;
+    pl.K = 4;
+    if (pl.n_chains >= want_wg && (W + 3) / 4 > kMaxWaves && wide_ok && (W + 7) / 8 <= kMaxWaves) pl.K = 8;
+    const int kenv = env_int("SSM2D_STRIP", 0);
+    if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
+    pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;
     if (pl.n_chains >= want_wg && pl.nstrips <= kMaxWaves) {
         s_local = pl.nstrips;
@@ -653,7 +656,7 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     if (s_local < 1) s_local = 1;
     if (s_local > pl.nstrips) s_local = pl.nstrips;
     if (s_local > kMaxWaves) s_local = kMaxWaves;
-    if (s_local < pl.nstrips && s_local > kMaxWaves - 1) s_local = kMaxWaves - 1;
+    if (s_local < pl.nstrips && s_local > kMaxWaves - 2) s_local = kMaxWaves - 2;  // room for 2 couriers
     pl.s_local = s_local;
     pl.groups = (pl.nstrips + s_local - 1) / s_local;
     pl.total_wg = pl.n_chains * pl.groups;
@@ -755,7 +758,7 @@ int device_cus(int dev)
     return n;
 }
 
-int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 1 : 0)); }
+int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 2 : 0)); }
 
 template <typename T, int K, int NPL>
 size_t lds_bytes(const Plan &pl)
