@@ -11,7 +11,7 @@
  *   y[b,d,i,j] = sum_n C[b,n,i,j] * h[i,j] + D[d] * x[b,d,i,j]
  *
  * with zero state before the first column and above the first row.
- * Passages: juejin.cn "2DMamba 精读" section 5 (横向扫描, 纵向扫描, final output
+ * Passages: juejin.cn "2DMamba 精读", part 四 section 5 (横向扫描, 纵向扫描, final output
  * y = C h); papernotes.org "2DMamba" 关键设计, items 2D选择性SSM架构 (row scans are
  * 1D Mamba, the vertical scan runs over the horizontal results) and 硬件感知2D并行
  * 扫描算子 (state dims reduced on chip, only the aggregate written back). The

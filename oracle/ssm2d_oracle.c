@@ -12,12 +12,12 @@
  *       (the pages name Abar and Bbar without defining them; this is the
  *        zero-order-hold A / Euler B reading used by Mamba)
  *   horizontal scan     hh[i,j] = Abar[i,j] * hh[i,j-1] + Bx[i,j],  hh[i,-1] = 0
- *       (juejin.cn "2DMamba 精读", section 5(1) 横向扫描)
+ *       (juejin.cn "2DMamba 精读", part 四 section 5, 横向扫描)
  *   vertical scan       h[i,j]  = Abar[i,j] * h[i-1,j]  + hh[i,j],  h[-1,j] = 0
  *       (same page, section 5(2) 纵向扫描; it scans the horizontal results,
  *        papernotes.org "2DMamba", 关键设计: 2D选择性SSM架构)
  *   output              y[i,j]  = sum_n C[b,n,i,j] * h[i,j] + D[d] * x[i,j]
- *       (juejin.cn section 5, 最终输出 y = C h; the D x skip term is the
+ *       (juejin.cn "2DMamba 精读", part 四 section 5, 最终输出 y = C h; the D x skip term is the
  *        Mamba convention and is added here)
  *
  * Every step is executed literally, in the order written, in double precision,

@@ -1,6 +1,6 @@
 // libssm2d: 2DMamba 2D selective scan (forward) for MI355X / gfx950.
 //
-// Method (juejin.cn "2DMamba 精读" section 5; papernotes.org "2DMamba" 关键设计):
+// Method (juejin.cn "2DMamba 精读", part 四 section 5; papernotes.org "2DMamba" 关键设计):
 //   Abar = exp(delta*A), Bx = delta*B*x
 //   hh[i,j] = Abar*hh[i,j-1] + Bx         horizontal scan, zero before column 0
 //   h[i,j]  = Abar*h[i-1,j]  + hh[i,j]    vertical scan of the horizontal results

@@ -7,7 +7,7 @@ Sources (page titles; sections):
     form h[i,j] = sum_{i'<=i, j'<=j} Abar^{(i-i')+(j-j')} Bbar x[i',j'] (a
     simplified form, exact for a position-independent Abar); the 3x3 example
     (decay Abar^4 in 2D versus Abar^8 raster-flattened).
-  * juejin.cn "2DMamba 精读" section 5: the horizontal recurrence, the vertical
+  * juejin.cn "2DMamba 精读", part 四 section 5: the horizontal recurrence, the vertical
     recurrence, y = C h; section 博士阶段 3: the same closed form and the
     upper-left support of the state.
   * Each check names the property it pins. ``ALL_PINS`` lists all of
