@@ -105,6 +105,66 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
     print(json.dumps(rec))
 
 
+def cpu_baseline(wl, t, keys, seconds: float):
+    """Times the oracle as it is (fp64, OpenMP over maps, all host threads) on
+    a bounded sample of the workload's (b, d) maps: calls over consecutive maps
+    (all of them per call if a pass is short) repeat until about `seconds` of
+    wall time have passed; a first untimed call over one map per thread sizes
+    the calls."""
+    import oracle
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    nmaps = wl.batch * wl.d_inner
+    threads = oracle.max_threads()
+    ins = [np.ascontiguousarray(t[k], dtype=np.float64) for k in keys]  # the oracle's input type
+    first = np.arange(min(threads, nmaps))
+    c0 = time.perf_counter()
+    oracle.fwd(*ins, maps=first)
+    t_first = max(time.perf_counter() - c0, 1e-6)
+    per_map = t_first / first.size
+    chunk = nmaps if per_map * nmaps <= seconds / 2 else max(first.size, int(seconds / 4 / per_map))
+    done, k = 0, 0
+    c0 = time.perf_counter()
+    while True:
+        sel = (np.arange(chunk) + k) % nmaps
+        oracle.fwd(*ins, maps=sel)
+        done += sel.size
+        k = (k + chunk) % nmaps
+        cw = time.perf_counter() - c0
+        if cw >= seconds:
+            break
+    n_el = done * wl.H * wl.W
+    return {"value": n_el / cw, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} (b,d) map scans ({nmaps} maps in the workload) of {wl.name} "
+                      f"({wl.H}x{wl.W}, d_state {wl.d_state}), fp64, {cw:.1f} s wall on {threads} threads"}
+
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
+             "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
+
+
+def trace_summary(workload: str, run_dir: str) -> None:
+    """Writes profiles/kernel_stats_<workload>.txt from the kernel statistics of
+    a rocprofv3 --kernel-trace --stats run of this benchmark."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && {TRACE_CMD.format(w=workload)}",
+             f"# kernel source sha256[:16] {kernel_source_hash()}",
+             "# name | calls | total ns | average ns | min ns | max ns | percent"]
+    for r in rows:
+        short = r["Name"].replace("(anonymous namespace)::", "").removeprefix("void ").split("(")[0][:110]
+        lines.append(f"{short} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.1f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
+    out = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,13 +172,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gigapixel_wsi")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-maps", type=int, default=0, help="oracle sample size in (b,d) maps (0 = all)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("SCAN_FETCH", "SCAN_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output directories")
     ap.add_argument("--copy-mb", type=int, default=512)
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.workload, args.trace_summary)
+        return
     if args.pmc_summary:
         pmc_summary(args.workload, *args.pmc_summary, copy_mb=args.copy_mb)
         return
@@ -198,19 +263,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-
-        if not os.path.exists(oracle.LIB_PATH):
-            oracle.build()
-        nmaps = wl.batch * wl.d_inner
-        sel = np.arange(nmaps if args.cpu_maps <= 0 else min(args.cpu_maps, nmaps))
-        threads = oracle.max_threads()
-        c0 = time.perf_counter()
-        oracle.fwd(*(t[k] for k in keys), maps=sel)
-        cw = time.perf_counter() - c0
-        cpu = {"value": sel.size * wl.H * wl.W / cw, "unit": "elements/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{sel.size} of {nmaps} (b,d) maps of {wl.name}, fp64, {cw:.2f} s wall"}
+        cpu = cpu_baseline(wl, t, keys, args.cpu_seconds)
 
     rec = {
         "metric": METRIC,

@@ -45,6 +45,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "ssm2d.h"
@@ -52,10 +53,12 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kGroups = 4;                     // state groups per wave
-constexpr int kChanPerWave = kWave / kGroups;  // channels per wave
-constexpr int kMaxWaves = 8;                   // waves per workgroup (strips + couriers)
+constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + couriers)
+// Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
+// small (8 state groups, K * NPL <= 16), else 8, which leaves a wave 256 VGPRs.
+constexpr int max_waves(int K, int NPL, int G) { return (G == 8 && K * NPL <= 16) ? 10 : 8; }
 constexpr int kCourierBatch = 4;               // rows a courier requests per poll
+constexpr int kSpinPolls = 64;                  // polls of an LDS counter before sleeping between polls
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Params {
@@ -184,14 +187,43 @@ __device__ __forceinline__ float perm_sum16(float a, float b)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int K>
-__device__ __forceinline__ void reduce_groups(const float (&p)[K], float (&out)[K / 4])
+// Lane value of the lane 8 places away in the same 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ float row_ror8(float v)
 {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+// Sum over the G state groups of a wave. Lane l holds partial sums p[0..K) of
+// K cells; state group g = l / (64 / G). Each halving level pairs groups that
+// are 32, 16 (and, for G = 8, 8) lanes apart and keeps half of the cells on
+// each side, so lanes end with K / G finished cells: cells [g*K/G, (g+1)*K/G).
+// For G = 8 and K = 4 the last level cannot halve: both lanes of a pair end
+// with the full sum of cell g / 2.
+template <int K, int G>
+__device__ __forceinline__ void reduce_groups(const float (&p)[K], float (&out)[(K / G) > 0 ? K / G : 1], int g)
+{
+    static_assert(G == 4 || G == 8, "4 or 8 state groups");
     float q[K / 2];
 #pragma unroll
     for (int c = 0; c < K / 2; ++c) q[c] = perm_sum32(p[c], p[c + K / 2]);
+    float r[K / 4];
 #pragma unroll
-    for (int c = 0; c < K / 4; ++c) out[c] = perm_sum16(q[c], q[c + K / 4]);
+    for (int c = 0; c < K / 4; ++c) r[c] = perm_sum16(q[c], q[c + K / 4]);
+    if constexpr (G == 4) {
+#pragma unroll
+        for (int c = 0; c < K / 4; ++c) out[c] = r[c];
+    } else if constexpr (K / 4 == 1) {
+        out[0] = r[0] + row_ror8(r[0]);
+    } else {
+        // even groups keep the first half of their cells, odd groups the second
+        const bool odd = (g & 1) != 0;
+#pragma unroll
+        for (int c = 0; c < K / 8; ++c) {
+            const float send = odd ? r[c] : r[c + K / 8];
+            const float keep = odd ? r[c + K / 8] : r[c];
+            out[c] = keep + row_ror8(send);
+        }
+    }
 }
 
 __device__ __forceinline__ void sleep_a_bit() { __builtin_amdgcn_s_sleep(2); }
@@ -244,21 +276,24 @@ __device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long 
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NPL> constexpr int passes_for(int K) { return ((32 + 8 * NPL) * (K / 4) + kWave - 1) / kWave; }
-template <int NPL> constexpr int prefetch_rows(int K) { return passes_for<NPL>(K) == 1 ? 4 : 2; }
+// Packet rows of a wave: x and delta of 64/G channels, B and C of G*NPL states.
+template <int NPL, int G> constexpr int packet_rows() { return 2 * (kWave / G) + 2 * G * NPL; }
+template <int NPL, int G> constexpr int passes_for(int K) { return (packet_rows<NPL, G>() * (K / 4) + kWave - 1) / kWave; }
+template <int NPL, int G> constexpr int prefetch_rows(int K) { return passes_for<NPL, G>(K) == 1 ? 4 : 2; }
 
-template <typename T, int K, int NPL, int ALIGN>
-__global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
+template <typename T, int K, int NPL, int ALIGN, int G>
+__global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kernel(Params p)
 {
-    static_assert(K % kGroups == 0 && K % 4 == 0, "strip width must be a multiple of 4");
+    static_assert(K % 4 == 0, "strip width must be a multiple of 4");
     using Chunk = typename ChunkOf<T>::type;
-    constexpr int KO = K / kGroups;                   // finished cells per lane and row
-    constexpr int SEG_X = 0, SEG_DT = 16, SEG_B = 32, SEG_C = 32 + 4 * NPL;
-    constexpr int SEGROWS = 32 + 8 * NPL;             // packet rows of K elements
+    constexpr int CPW = kWave / G;                    // channels per wave
+    constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
+    constexpr int SEG_X = 0, SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
+    constexpr int SEGROWS = packet_rows<NPL, G>();    // packet rows of K elements
     constexpr int CPR = K / 4;                        // chunks per packet row
     constexpr int NCHUNK = SEGROWS * CPR;
-    constexpr int PASSES = passes_for<NPL>(K);
-    constexpr int P = prefetch_rows<NPL>(K);          // rows per prefetch buffer
+    constexpr int PASSES = passes_for<NPL, G>(K);
+    constexpr int P = prefetch_rows<NPL, G>(K);       // rows per prefetch buffer
 
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_done[kMaxWaves + 1];   // rows published into LDS ring b
@@ -294,7 +329,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
     const int H = p.H, W = p.W;
     const int RM = p.ring_rows - 1;                   // ring depth is a power of two
     const long ring_floats = static_cast<long>(p.ring_rows) * kWave * NPL;
-    float *lring = reinterpret_cast<float *>(smem + static_cast<long>(p.s_local) * NCHUNK * sizeof(Chunk));
+    float *lring = reinterpret_cast<float *>(smem + static_cast<long>(p.s_local) * 2 * PASSES * kWave * sizeof(Chunk));
 
     if (wave >= p.s_local) {
         // ---------------- couriers between the global ring and the LDS rings.
@@ -394,13 +429,16 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
         const int strip = grp * p.s_local + wave;
         const int j0 = strip * K;
         const int valid = min(K, W - j0);
-        const int g = lane / kChanPerWave;
-        const int dl = lane % kChanPerWave;
-        const int d = dblk * kChanPerWave + dl;
+        const int g = lane / CPW;
+        const int dl = lane % CPW;
+        const int d = dblk * CPW + dl;
         const bool d_ok = d < p.d_inner;
         const long HW = static_cast<long>(H) * W;
         const T *zeros = static_cast<const T *>(p.zeros);
-        T *packet = reinterpret_cast<T *>(smem) + static_cast<long>(wave) * NCHUNK * 4;
+        // Two packet buffers of PASSES x 64 chunks (chunks past NCHUNK are
+        // padding, so every lane stores its chunk without a mask): row i is
+        // read from buffer i % 2 while row i + 1 is staged into the other.
+        T *packets = reinterpret_cast<T *>(smem) + static_cast<long>(wave) * 2 * PASSES * kWave * 4;
 
         // Chunk sources of this lane: packet row r, chunk q of that row, split
         // into 4/ALIGN sub-loads; a sub-load past the row end reads the zero page.
@@ -413,10 +451,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
             const T *base = zeros;
             if (c < NCHUNK) {
                 if (r < SEG_DT) {
-                    const int dd = dblk * kChanPerWave + r;
+                    const int dd = dblk * CPW + r;
                     if (dd < p.d_inner) base = static_cast<const T *>(p.x) + (static_cast<long>(b) * p.d_inner + dd) * HW;
                 } else if (r < SEG_B) {
-                    const int dd = dblk * kChanPerWave + r - SEG_DT;
+                    const int dd = dblk * CPW + r - SEG_DT;
                     if (dd < p.d_inner) base = static_cast<const T *>(p.delta) + (static_cast<long>(b) * p.d_inner + dd) * HW;
                 } else if (r < SEG_C) {
                     const int n = r - SEG_B;
@@ -440,14 +478,17 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
             Ap[k] = (n < p.d_state && d_ok) ? p.A[d * p.d_state + n] * kLog2e : 0.0f;
         }
         const float Dd = d_ok ? p.D[d] : 0.0f;
-        const int c_out = g * KO;  // first of this lane's finished cells
+        // First of this lane's finished cells (for G = 8 and K = 4 the two
+        // lanes of a pair hold the same cell and the odd one does not store).
+        const int c_out = (K >= G) ? g * KO : g / 2;
+        const bool storer = (K >= G) || (g % 2 == 0);
         // Output cells of this lane; cells outside the map go to the sink.
         // The pointers advance one row per processed row.
         T *ydst[KO];
         int ystep[KO];
 #pragma unroll
         for (int c = 0; c < KO; ++c) {
-            const bool ok = d_ok && (c_out + c < valid);
+            const bool ok = d_ok && storer && (c_out + c < valid);
             ydst[c] = ok ? static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + d) * HW + j0 + c_out + c
                          : static_cast<T *>(p.sink) + lane * KO + c;
             ystep[c] = ok ? W : 0;
@@ -457,8 +498,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
         const bool has_right = strip + 1 < p.nstrips;
         const float *ring_in = lring + static_cast<long>(wave) * ring_floats;
         float *ring_out = lring + static_cast<long>(wave + 1) * ring_floats;
-        int avail = 0;      // rows the left neighbour has published, as seen
-        int room = 0;       // rows this wave may publish, as seen
         bool timed_out = false;
 
         float hv[K][NPL];
@@ -467,135 +506,202 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
 #pragma unroll
             for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
 
-        auto do_row = [&](const int i, const Chunk (&cb)[PASSES]) {
-            // ---- stage row i's packet and read this lane's operands
+        // x and delta of one row: read one row ahead, they start the row's
+        // arithmetic. B, C and the skip input are read when the row starts.
+        struct Ops {
+            float xv[K], dv[K];
+        };
+        // Stage a row's packet in LDS buffer `buf` and issue the reads of this
+        // lane's x and delta (their latency hides behind the current row).
+        auto stage = [&](const Chunk (&cb)[PASSES], const int buf, Ops &o) {
+            T *pk = packets + buf * PASSES * kWave * 4;
 #pragma unroll
-            for (int pp = 0; pp < PASSES; ++pp)
-                if (pp * kWave + lane < NCHUNK) reinterpret_cast<Chunk *>(packet)[pp * kWave + lane] = cb[pp];
-            float xv[K], dv[K], Bv[NPL][K], Cv[NPL][K], xo[KO];
-            read_packet<K>(packet, (SEG_X + dl) * K, xv);
-            read_packet<K>(packet, (SEG_DT + dl) * K, dv);
-#pragma unroll
-            for (int k = 0; k < NPL; ++k) {
-                read_packet<K>(packet, (SEG_B + g * NPL + k) * K, Bv[k]);
-                read_packet<K>(packet, (SEG_C + g * NPL + k) * K, Cv[k]);
-            }
-            read_packet_scalar<KO>(packet, (SEG_X + dl) * K + c_out, xo);
+            for (int pp = 0; pp < PASSES; ++pp) reinterpret_cast<Chunk *>(pk)[pp * kWave + lane] = cb[pp];
+            read_packet<K>(pk, (SEG_X + dl) * K, o.xv);
+            read_packet<K>(pk, (SEG_DT + dl) * K, o.dv);
+        };
 
-            // ---- left carry of row i: the counter and the ring slot are read
-            // together (LDS executes a wave's accesses in order, and the
-            // producer writes the slot before the counter), before the
-            // carry-independent work below, so their latency overlaps it.
-            float hh[NPL];
-            int seen = 0;
-            if (has_left) {
-                seen = lds_peek(&s_done[wave]);
-                signal_fence();
-                const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
-            } else {
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
-            }
+        // Rows of the strip, with the code for the strip's neighbours fixed at
+        // compile time (LEFT: a strip to the left sends carries; RIGHT: one to
+        // the right takes them).
+        auto strip_rows = [&](auto left_tag, auto right_tag) {
+            constexpr bool LEFT = decltype(left_tag)::value;
+            constexpr bool RIGHT = decltype(right_tag)::value;
+            int room = 0;  // rows this wave may publish, as seen
 
-            // ---- carry-independent work: decay factors and inputs of the row
-            float av[K][NPL], bx[K][NPL];
+            // Row i from packet buffer i % 2 and operands `o`; row i+1's
+            // packet `nb` is staged (and its x, delta read into `on`) first,
+            // so that LDS traffic overlaps this row's arithmetic.
+            auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on) {
+                const T *pk = packets + (i % 2) * PASSES * kWave * 4;
+                float Bv[NPL][K], Cv[NPL][K], xo[KO];
 #pragma unroll
-            for (int c = 0; c < K; ++c) {
-                const float dx = dv[c] * xv[c];
+                for (int k = 0; k < NPL; ++k) read_packet<K>(pk, (SEG_B + g * NPL + k) * K, Bv[k]);
+                stage(nb, (i + 1) % 2, on);
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) {
-                    av[c][k] = __builtin_amdgcn_exp2f(dv[c] * Ap[k]);
-                    bx[c][k] = dx * Bv[k][c];
-                }
-            }
+                for (int k = 0; k < NPL; ++k) read_packet<K>(pk, (SEG_C + g * NPL + k) * K, Cv[k]);
+                read_packet_scalar<KO>(pk, (SEG_X + dl) * K + c_out, xo);
 
-            if (has_left) {
-                if (__builtin_amdgcn_readfirstlane(seen) <= i && !timed_out) {
-                    // not published yet: poll, then read the slot again
-                    wait_counter_above(&s_done[wave], i, p.spin_limit, timed_out);
+                // ---- left carry of row i: the counter and the ring slot are
+                // read together (LDS executes a wave's accesses in order, and
+                // the producer writes the slot before the counter), before the
+                // carry-independent work below, so their latency overlaps it.
+                float hh[NPL];
+                int seen = 0;
+                if constexpr (LEFT) {
+                    seen = lds_peek(&s_done[wave]);
                     signal_fence();
                     const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
                 }
-            }
 
-            // ---- horizontal recurrence along the row, then hand the carry on
-            float hc[K][NPL];
+                // ---- carry-independent work: decay factors and inputs of the row
+                float av[K][NPL], bx[K][NPL];
 #pragma unroll
-            for (int c = 0; c < K; ++c)
+                for (int c = 0; c < K; ++c) {
+                    const float dx = o.dv[c] * o.xv[c];
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) {
-                    hh[k] = __builtin_fmaf(av[c][k], hh[k], bx[c][k]);
-                    hc[c][k] = hh[k];
+                    for (int k = 0; k < NPL; ++k) {
+                        av[c][k] = __builtin_amdgcn_exp2f(o.dv[c] * Ap[k]);
+                        bx[c][k] = dx * Bv[k][c];
+                    }
                 }
-            if (has_right) {
-                if (i >= room && !timed_out)
-                    room = wait_counter_above(&s_used[wave + 1], i - p.ring_rows, p.spin_limit, timed_out) + p.ring_rows;
-                float *dst = ring_out + (static_cast<long>(i & RM) * kWave + lane) * NPL;
+                // Pin that work here, ahead of the wait below: left to itself
+                // the compiler sinks it past the wait, onto the carry's
+                // critical path.
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) dst[k] = hh[k];
-                signal_fence();
-                lds_poke(&s_done[wave + 1], i + 1);
-            }
-            if (has_left) lds_poke(&s_used[wave], i + 1);
+                for (int c = 0; c < K; ++c)
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(av[c][k]), "+v"(bx[c][k]));
 
-            // ---- vertical recurrence and the sum over this lane's states
-            float part[K];
-#pragma unroll
-            for (int c = 0; c < K; ++c) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int k = 0; k < NPL; ++k) {
-                    hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
-                    acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                // room in the right ring for row i (rarely short; checked here,
+                // off the carry's critical path)
+                if constexpr (RIGHT) {
+                    if (i >= room && !timed_out)
+                        room = wait_counter_above(&s_used[wave + 1], i - p.ring_rows, p.spin_limit, timed_out) +
+                               p.ring_rows;
                 }
-                part[c] = acc;
-            }
 
-            // ---- sum over the state groups, skip term, store
-            float out[KO];
-            reduce_groups<K>(part, out);
+                if constexpr (LEFT) {
+                    if (__builtin_amdgcn_readfirstlane(seen) <= i && !timed_out) {
+                        // Not published yet: poll. Each poll reads the counter
+                        // and then the slot, back to back, so the poll that sees
+                        // row i published has already fetched its carry (one
+                        // LDS round trip per poll). Short waits spin; long ones
+                        // sleep between polls.
+                        const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
+                        long long spins = 0;
+                        while (true) {
+                            const int v = lds_peek(&s_done[wave]);
+                            signal_fence();
+                            float t[NPL];
 #pragma unroll
-            for (int c = 0; c < KO; ++c) {
-                store_elem(ydst[c], out[c] + Dd * xo[c]);
-                ydst[c] += ystep[c];
+                            for (int k = 0; k < NPL; ++k) t[k] = src_c[k];
+                            if (__builtin_amdgcn_readfirstlane(v) > i) {
+#pragma unroll
+                                for (int k = 0; k < NPL; ++k) hh[k] = t[k];
+                                break;
+                            }
+                            if (++spins > p.spin_limit) {
+                                timed_out = true;
+                                break;
+                            }
+                            if (spins > kSpinPolls) sleep_a_bit();
+                        }
+                    }
+                }
+
+                // ---- horizontal recurrence along the row, then hand the carry on
+                float hc[K][NPL];
+#pragma unroll
+                for (int c = 0; c < K; ++c)
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        hh[k] = __builtin_fmaf(av[c][k], hh[k], bx[c][k]);
+                        hc[c][k] = hh[k];
+                    }
+                if constexpr (RIGHT) {
+                    float *dst = ring_out + (static_cast<long>(i & RM) * kWave + lane) * NPL;
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) dst[k] = hh[k];
+                    signal_fence();
+                    lds_poke(&s_done[wave + 1], i + 1);
+                }
+                if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
+
+                // ---- vertical recurrence and the sum over this lane's states
+                float part[K];
+#pragma unroll
+                for (int c = 0; c < K; ++c) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
+                        acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                    }
+                    part[c] = acc;
+                }
+
+                // ---- sum over the state groups, skip term, store
+                float out[KO];
+                reduce_groups<K, G>(part, out, g);
+#pragma unroll
+                for (int c = 0; c < KO; ++c) {
+                    store_elem(ydst[c], out[c] + Dd * xo[c]);
+                    ydst[c] += ystep[c];
+                }
+            };
+
+            // Two prefetch buffers of P rows: while one buffer's rows are
+            // computed, the other's loads are in flight. Operands alternate
+            // between two register sets, row by row. Full blocks of 2P rows run
+            // without per-row guards (a guard would make the compiler copy the
+            // register-resident state at every row); the last, partial block
+            // runs guarded. Rows past the map's end are never computed; their
+            // loads read the last row again.
+            Chunk bufA[P][PASSES], bufB[P][PASSES];
+            Ops ops[2];
+            auto load_rows = [&](Chunk (&buf)[P][PASSES], const int first) {
+#pragma unroll
+                for (int s = 0; s < P; ++s)
+#pragma unroll
+                    for (int pp = 0; pp < PASSES; ++pp)
+                        buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s, H - 1)) * W);
+            };
+            load_rows(bufA, 0);
+            load_rows(bufB, P);
+            stage(bufA[0], 0, ops[0]);
+            int i0 = 0;
+            for (; i0 + 2 * P <= H; i0 += 2 * P) {
+#pragma unroll
+                for (int s = 0; s < P; ++s)
+                    do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2]);
+                load_rows(bufA, i0 + 2 * P);
+#pragma unroll
+                for (int s = 0; s < P; ++s)
+                    do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2]);
+                load_rows(bufB, i0 + 3 * P);
+            }
+            if (i0 < H) {
+#pragma unroll
+                for (int s = 0; s < P; ++s)
+                    if (i0 + s < H) do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2]);
+#pragma unroll
+                for (int s = 0; s < P; ++s)
+                    if (i0 + P + s < H)
+                        do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2]);
             }
         };
-
-        // Two prefetch buffers of P rows: while one buffer's rows are
-        // computed, the other's loads are in flight. Full blocks of 2P rows
-        // run without per-row guards (a guard would make the compiler copy
-        // the register-resident state at every row); the last, partial block
-        // runs guarded.
-        Chunk bufA[P][PASSES], bufB[P][PASSES];
-        auto load_rows = [&](Chunk (&buf)[P][PASSES], const int first) {
-#pragma unroll
-            for (int s = 0; s < P; ++s)
-#pragma unroll
-                for (int pp = 0; pp < PASSES; ++pp)
-                    buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s, H - 1)) * W);
-        };
-        load_rows(bufA, 0);
-        int i0 = 0;
-        for (; i0 + 2 * P <= H; i0 += 2 * P) {
-            load_rows(bufB, i0 + P);
-#pragma unroll
-            for (int s = 0; s < P; ++s) do_row(i0 + s, bufA[s]);
-            load_rows(bufA, i0 + 2 * P);
-#pragma unroll
-            for (int s = 0; s < P; ++s) do_row(i0 + P + s, bufB[s]);
-        }
-        if (i0 < H) {
-            load_rows(bufB, i0 + P);
-#pragma unroll
-            for (int s = 0; s < P; ++s)
-                if (i0 + s < H) do_row(i0 + s, bufA[s]);
-#pragma unroll
-            for (int s = 0; s < P; ++s)
-                if (i0 + P + s < H) do_row(i0 + P + s, bufB[s]);
+        if (has_left) {
+            if (has_right) strip_rows(std::true_type{}, std::true_type{});
+            else strip_rows(std::true_type{}, std::false_type{});
+        } else {
+            if (has_right) strip_rows(std::false_type{}, std::true_type{});
+            else strip_rows(std::false_type{}, std::false_type{});
         }
         if (timed_out) atomicOr(p.err, 1u);
     }
@@ -615,7 +721,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan2d_fwd_kernel(Params p)
 // ---------------------------------------------------------------- host side
 
 struct Plan {
-    int K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
+    int G, K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
 };
 
 int env_int(const char *name, int dflt)
@@ -627,25 +733,39 @@ int env_int(const char *name, int dflt)
 Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W)
 {
     Plan pl{};
+    const int want_wg = 256;  // enough workgroups to cover the chip's CUs
+    // Layout: 4 state groups per wave (16 channels) unless the map has more
+    // than 4 states and too few (batch, channel-block) chains to give every CU
+    // a chain of its own. Then 8 groups (8 channels, half the states per lane)
+    // double the chains, halve the workgroups each chain spans, and put two
+    // compute waves on each SIMD. Above 32 states a lane of a 4-group layout
+    // would hold 16 states, more than its registers: 8 groups then too.
+    const int64_t chains4 = batch * ((d_inner + 15) / 16);
+    int G = (d_state > 32 || (d_state > 4 && chains4 < want_wg)) ? 8 : 4;
+    const int genv = env_int("SSM2D_GROUPS", 0);
+    if (genv == 8 || (genv == 4 && d_state <= 32)) G = genv;
+    pl.G = G;
     int npl = 1;
-    while (npl * kGroups < d_state) npl *= 2;
+    while (npl * G < d_state) npl *= 2;
     pl.npl = npl;
-    pl.n_dblk = static_cast<int>((d_inner + kChanPerWave - 1) / kChanPerWave);
+    const int cpw = kWave / G;
+    pl.n_dblk = static_cast<int>((d_inner + cpw - 1) / cpw);
     pl.n_chains = static_cast<int>(batch) * pl.n_dblk;
-    // Enough workgroups to cover the chip (256 CUs). With that many chains,
-    // keep each chain in one workgroup (its carries stay in LDS), widening the
-    // strips to 8 columns if that makes the chain fit. Otherwise chains are cut
-    // into groups of s_local strips linked by two courier waves (so at most
-    // kMaxWaves - 2 strips per workgroup).
-    const int want_wg = 256;
+    // With that many chains, keep each chain in one workgroup (its carries
+    // stay in LDS), widening the strips to 8 columns if that makes the chain
+    // fit. Otherwise chains are cut into groups of s_local strips linked by two
+    // courier waves (so at most maxw - 2 strips per workgroup).
     const bool wide_ok = npl <= 4 && W % 4 == 0;
     pl.K = 4;
-    if (pl.n_chains >= want_wg && (W + 3) / 4 > kMaxWaves && wide_ok && (W + 7) / 8 <= kMaxWaves) pl.K = 8;
+    if (pl.n_chains >= want_wg && (W + 3) / 4 > max_waves(4, npl, G) && wide_ok &&
+        (W + 7) / 8 <= max_waves(8, npl, G))
+        pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
+    const int maxw = max_waves(pl.K, npl, G);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;
-    if (pl.n_chains >= want_wg && pl.nstrips <= kMaxWaves) {
+    if (pl.n_chains >= want_wg && pl.nstrips <= maxw) {
         s_local = pl.nstrips;
     } else {
         const int groups = (pl.n_chains >= want_wg) ? 1 : (want_wg + pl.n_chains - 1) / pl.n_chains;
@@ -655,8 +775,8 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     s_local = env_int("SSM2D_WAVES", s_local);
     if (s_local < 1) s_local = 1;
     if (s_local > pl.nstrips) s_local = pl.nstrips;
-    if (s_local > kMaxWaves) s_local = kMaxWaves;
-    if (s_local < pl.nstrips && s_local > kMaxWaves - 2) s_local = kMaxWaves - 2;  // room for 2 couriers
+    if (s_local > maxw) s_local = maxw;
+    if (s_local < pl.nstrips && s_local > maxw - 2) s_local = maxw - 2;  // room for 2 couriers
     pl.s_local = s_local;
     pl.groups = (pl.nstrips + s_local - 1) / s_local;
     pl.total_wg = pl.n_chains * pl.groups;
@@ -760,24 +880,24 @@ int device_cus(int dev)
 
 int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 2 : 0)); }
 
-template <typename T, int K, int NPL>
+template <typename T, int K, int NPL, int G>
 size_t lds_bytes(const Plan &pl)
 {
     using Chunk = typename ChunkOf<T>::type;
-    const size_t nchunk = static_cast<size_t>(32 + 8 * NPL) * (K / 4);
-    return static_cast<size_t>(pl.s_local) * nchunk * sizeof(Chunk) +
+    const size_t chunks = 2 * static_cast<size_t>(passes_for<NPL, G>(K)) * kWave;  // per wave: 2 padded buffers
+    return static_cast<size_t>(pl.s_local) * chunks * sizeof(Chunk) +
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
 
 // Global ring depth: bounded (with back-pressure) only if the whole grid is
 // co-resident, so that a producer never waits on a consumer that cannot run.
-template <typename T, int K, int NPL, int ALIGN>
+template <typename T, int K, int NPL, int ALIGN, int G>
 int choose_qg(const Plan &pl, int dev, int H)
 {
     if (pl.groups <= 1) return H;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN>, block_threads(pl),
-                                                     lds_bytes<T, K, NPL>(pl)) != hipSuccess) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G>, block_threads(pl),
+                                                     lds_bytes<T, K, NPL, G>(pl)) != hipSuccess) {
         (void)hipGetLastError();
         return H;
     }
@@ -787,11 +907,11 @@ int choose_qg(const Plan &pl, int dev, int H)
     return H;
 }
 
-template <typename T, int K, int NPL, int ALIGN>
+template <typename T, int K, int NPL, int ALIGN, int G>
 int run(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
         int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
 {
-    pl.qg = choose_qg<T, K, NPL, ALIGN>(pl, dev, H);
+    pl.qg = choose_qg<T, K, NPL, ALIGN, G>(pl, dev, H);
     const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
     const size_t gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
     const size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
@@ -817,8 +937,8 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     prm.epoch = e->epoch;
     prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
-    const size_t lds = lds_bytes<T, K, NPL>(pl);
-    scan2d_fwd_kernel<T, K, NPL, ALIGN><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
+    const size_t lds = lds_bytes<T, K, NPL, G>(pl);
+    scan2d_fwd_kernel<T, K, NPL, ALIGN, G><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
                                    static_cast<hipStream_t>(stream)>>>(prm);
     const hipError_t err = hipGetLastError();
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
@@ -848,13 +968,17 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
-#define SSM2D_CASE(KK, NN, AL) \
-    if (pl.K == KK && pl.npl == NN && align == AL) \
-        return run<T, KK, NN, AL>(x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream);
-    SSM2D_CASE(4, 1, 4) SSM2D_CASE(4, 2, 4) SSM2D_CASE(4, 4, 4) SSM2D_CASE(4, 8, 4) SSM2D_CASE(4, 16, 4)
-    SSM2D_CASE(8, 1, 4) SSM2D_CASE(8, 2, 4) SSM2D_CASE(8, 4, 4)
-    SSM2D_CASE(4, 1, 2) SSM2D_CASE(4, 2, 2) SSM2D_CASE(4, 4, 2) SSM2D_CASE(4, 8, 2) SSM2D_CASE(4, 16, 2)
-    SSM2D_CASE(4, 1, 1) SSM2D_CASE(4, 2, 1) SSM2D_CASE(4, 4, 1) SSM2D_CASE(4, 8, 1) SSM2D_CASE(4, 16, 1)
+#define SSM2D_CASE(GG, KK, NN, AL) \
+    if (pl.G == GG && pl.K == KK && pl.npl == NN && align == AL) \
+        return run<T, KK, NN, AL, GG>(x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream);
+    SSM2D_CASE(4, 4, 1, 4) SSM2D_CASE(4, 4, 2, 4) SSM2D_CASE(4, 4, 4, 4) SSM2D_CASE(4, 4, 8, 4)
+    SSM2D_CASE(4, 8, 1, 4) SSM2D_CASE(4, 8, 2, 4) SSM2D_CASE(4, 8, 4, 4)
+    SSM2D_CASE(4, 4, 1, 2) SSM2D_CASE(4, 4, 2, 2) SSM2D_CASE(4, 4, 4, 2) SSM2D_CASE(4, 4, 8, 2)
+    SSM2D_CASE(4, 4, 1, 1) SSM2D_CASE(4, 4, 2, 1) SSM2D_CASE(4, 4, 4, 1) SSM2D_CASE(4, 4, 8, 1)
+    SSM2D_CASE(8, 4, 1, 4) SSM2D_CASE(8, 4, 2, 4) SSM2D_CASE(8, 4, 4, 4) SSM2D_CASE(8, 4, 8, 4)
+    SSM2D_CASE(8, 8, 1, 4) SSM2D_CASE(8, 8, 2, 4) SSM2D_CASE(8, 8, 4, 4)
+    SSM2D_CASE(8, 4, 1, 2) SSM2D_CASE(8, 4, 2, 2) SSM2D_CASE(8, 4, 4, 2) SSM2D_CASE(8, 4, 8, 2)
+    SSM2D_CASE(8, 4, 1, 1) SSM2D_CASE(8, 4, 2, 1) SSM2D_CASE(8, 4, 4, 1) SSM2D_CASE(8, 4, 8, 1)
 #undef SSM2D_CASE
     return SSM2D_ERR_UNSUPPORTED;
 }

@@ -90,23 +90,43 @@ SHAPES = [
 ]
 
 
+def _seed(shape):
+    return sum((i + 1) * v for i, v in enumerate(shape)) % 1000
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_random_shapes(shape, dtype):
-    _say(f"shape {shape} {dtype}")
-    t = make_random_inputs(*shape, seed=hash(shape) % 1000, dtype=dtype)
+@pytest.mark.parametrize("groups", ["4", "8"])
+def test_random_shapes(shape, dtype, groups, monkeypatch):
+    """Both lane layouts: 16 channels x 4 state groups and 8 x 8 per wave."""
+    monkeypatch.setenv("SSM2D_GROUPS", groups)
+    _say(f"shape {shape} {dtype} groups={groups}")
+    t = make_random_inputs(*shape, seed=_seed(shape), dtype=dtype)
     y = as_f64(run_gpu(t, dtype))
-    check(y, ref_of(t), dtype, f"{shape} {dtype}")
+    check(y, ref_of(t), dtype, f"{shape} {dtype} groups={groups}")
 
 
-@pytest.mark.parametrize("waves", ["1", "2", "3"])
-def test_multi_workgroup_chains(waves, monkeypatch):
+@pytest.mark.parametrize("groups", ["4", "8"])
+@pytest.mark.parametrize("shape", [(2, 16, 16, 19, 64), (1, 24, 8, 7, 40), (1, 8, 4, 9, 16)])
+def test_wide_strips(shape, groups, monkeypatch):
+    """8-column strips (each lane keeps 8 cells per row)."""
+    monkeypatch.setenv("SSM2D_GROUPS", groups)
+    monkeypatch.setenv("SSM2D_STRIP", "8")
+    _say(f"wide strips {shape} groups={groups}")
+    t = make_random_inputs(*shape, seed=_seed(shape))
+    check(as_f64(run_gpu(t, "f32")), ref_of(t), "f32", f"K=8 {shape} groups={groups}")
+
+
+@pytest.mark.parametrize("groups", ["4", "8"])
+@pytest.mark.parametrize("waves", ["1", "2", "3", "8"])
+def test_multi_workgroup_chains(waves, groups, monkeypatch):
     """Force short workgroups so strip carries cross workgroups (global path)."""
     monkeypatch.setenv("SSM2D_WAVES", waves)
-    for shape in ((1, 16, 16, 33, 80), (2, 20, 4, 9, 52)):
-        _say(f"chains waves={waves} shape {shape}")
-        t = make_random_inputs(*shape, seed=3)
-        check(as_f64(run_gpu(t, "f32")), ref_of(t), "f32", f"waves={waves} {shape}")
+    monkeypatch.setenv("SSM2D_GROUPS", groups)
+    for shape, dtype in (((1, 16, 16, 33, 80), "f32"), ((2, 20, 4, 9, 52), "f32"), ((1, 8, 16, 21, 132), "bf16")):
+        _say(f"chains waves={waves} groups={groups} shape {shape} {dtype}")
+        t = make_random_inputs(*shape, seed=3, dtype=dtype)
+        check(as_f64(run_gpu(t, dtype)), ref_of(t), dtype, f"waves={waves} groups={groups} {shape}")
 
 
 def test_special_cases_through_gpu():
