@@ -76,6 +76,7 @@ struct Params {
     int qg;                            // global ring depth (== H: no reuse)
     int use_ticket;                    // chains span workgroups
     int xcd_remap;                     // spread chains over XCDs in contiguous blocks
+    int vec_store;                     // gather each channel's cells and store whole chunks
     unsigned int epoch;
     long long spin_limit;
 };
@@ -162,14 +163,8 @@ __device__ __forceinline__ void read_packet_scalar(const uint16_t *pk, int off, 
 }
 
 __device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_elem(uint16_t *p, float v)
-{
-    unsigned u = __float_as_uint(v);
-    unsigned r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) r = (u >> 16) | 0x40u;          // quiet NaN
-    else r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                       // nearest even
-    *p = static_cast<uint16_t>(r);
-}
+__device__ __forceinline__ unsigned bf16_bits(float v);
+__device__ __forceinline__ void store_elem(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
 
 __device__ __forceinline__ float perm_sum32(float a, float b)
 {
@@ -223,6 +218,97 @@ __device__ __forceinline__ void reduce_groups(const float (&p)[K], float (&out)[
             const float keep = odd ? r[c + K / 8] : r[c];
             out[c] = keep + row_ror8(send);
         }
+    }
+}
+
+// Value of `x` held by the lane in 16-lane row r (0..3) at the same position
+// within its row, delivered to the lanes of row 0.
+__device__ __forceinline__ float from_row(float x, int r)
+{
+    if (r == 0) return x;
+    if (r == 1) return __uint_as_float(__builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)[1]);
+    const float x2 = __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)[1]);
+    if (r == 2) return x2;
+    return __uint_as_float(__builtin_amdgcn_permlane16_swap(__float_as_uint(x2), __float_as_uint(x2), false, false)[1]);
+}
+
+__device__ __forceinline__ unsigned bf16_bits(float v)
+{
+    const unsigned u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                    // nearest even
+}
+__device__ __forceinline__ unsigned row_word(unsigned w, int r) { return __float_as_uint(from_row(__uint_as_float(w), r)); }
+
+// Whole-row store of a strip. After reduce_groups the K finished cells of a
+// channel sit in the four 16-lane rows (KO per lane). They are converted to the
+// output type first (bf16 cells packed in pairs where a lane holds two), then
+// collected, in column order, in the channel's lane of row 0 (lane < 64 / G),
+// which stores them as whole chunks: K floats, or K bf16 values.
+template <int K, int G>
+__device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
+{
+    constexpr int KO = (K / G) > 0 ? K / G : 1;
+    float cells[K];
+    if constexpr (G == 4) {
+        // row r = group r holds cells [r*KO, (r+1)*KO)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < KO; ++c) cells[r * KO + c] = from_row(v[c], r);
+    } else if constexpr (K == 4) {
+        // row r holds cell r (twice: groups 2r and 2r+1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cells[r] = from_row(v[0], r);
+    } else {
+        // K = 8: in row r, lanes 0-7 (group 2r) hold cell 2r and lanes 8-15
+        // (group 2r+1) cell 2r+1, which comes over 8 lanes.
+        static_assert(K == 8, "8-group layout stores 4- or 8-column strips");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            cells[2 * r] = from_row(v[0], r);
+            cells[2 * r + 1] = row_ror8(cells[2 * r]);
+        }
+    }
+    if (storer) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+            *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(cells[4 * q], cells[4 * q + 1], cells[4 * q + 2], cells[4 * q + 3]);
+    }
+}
+template <int K, int G>
+__device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
+{
+    constexpr int KO = (K / G) > 0 ? K / G : 1;
+    unsigned words[K / 2];  // two bf16 cells per word, column order
+    if constexpr (G == 4 && KO >= 2) {
+        unsigned w[KO / 2];
+#pragma unroll
+        for (int c = 0; c < KO / 2; ++c) w[c] = bf16_bits(v[2 * c]) | (bf16_bits(v[2 * c + 1]) << 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < KO / 2; ++c) words[r * KO / 2 + c] = row_word(w[c], r);
+    } else if constexpr (K == 4) {
+        // one cell per lane: rows 0..3 hold cells 0..3
+        const unsigned h = bf16_bits(v[0]);
+        unsigned t[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = row_word(h, r);
+        words[0] = t[0] | (t[1] << 16);
+        words[1] = t[2] | (t[3] << 16);
+    } else {
+        static_assert(G == 8 && K == 8, "bf16 row store layouts");
+        const unsigned h = bf16_bits(v[0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const unsigned t = row_word(h, r);
+            words[r] = t | (__float_as_uint(row_ror8(__uint_as_float(t))) << 16);
+        }
+    }
+    if (storer) {
+        if constexpr (K == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(words[0], words[1]);
+        else *reinterpret_cast<uint4 *>(p) = make_uint4(words[0], words[1], words[2], words[3]);
     }
 }
 
@@ -493,6 +579,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                          : static_cast<T *>(p.sink) + lane * KO + c;
             ystep[c] = ok ? W : 0;
         }
+        // Whole-strip stores: with 4-aligned rows and a full strip, each
+        // channel's cells are gathered into one lane of row 0 and stored as
+        // chunks; other strips store cell by cell.
+        const bool vec_store = (ALIGN == 4) && (valid == K) && p.vec_store;
+        const bool vec_lane = (lane < CPW) && d_ok;
+        T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + j0;
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -650,9 +742,16 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 float out[KO];
                 reduce_groups<K, G>(part, out, g);
 #pragma unroll
-                for (int c = 0; c < KO; ++c) {
-                    store_elem(ydst[c], out[c] + Dd * xo[c]);
-                    ydst[c] += ystep[c];
+                for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
+                if (vec_store) {
+                    store_row<K, G>(yvec, out, vec_lane);
+                    yvec += W;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < KO; ++c) {
+                        store_elem(ydst[c], out[c]);
+                        ydst[c] += ystep[c];
+                    }
                 }
             };
 
@@ -936,6 +1035,7 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     prm.epoch = e->epoch;
+    prm.vec_store = env_int("SSM2D_VECSTORE", 1);
     prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
     const size_t lds = lds_bytes<T, K, NPL, G>(pl);
     scan2d_fwd_kernel<T, K, NPL, ALIGN, G><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
