@@ -43,12 +43,18 @@ def algorithmic_bytes(wl) -> int:
     return E * 3 * s + wl.batch * wl.d_state * wl.H * wl.W * 2 * s + wl.d_inner * wl.d_state * 4 + wl.d_inner * 4
 
 
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_ssm2d_amd", "csrc", "ssm2d.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "selective_state_space_ssm2d_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the library's HIP sources (counter summaries are only valid for
+    the kernel they were taken on)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def copy_probe(mb: int, steps: int) -> None:

@@ -1,12 +1,19 @@
-"""Build step for libssm2d.so (gfx950). Used by ``__graft_entry__.build()``."""
+"""Build step for libssm2d.so (gfx950). Used by ``__graft_entry__.build()``.
+
+The kernel instances are split over several translation units (one per input
+type and lane layout) that hipcc compiles in parallel; the objects are then
+linked into one shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "ssm2d.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["ssm2d.hip", "scan2d_f32_g4.hip", "scan2d_f32_g8.hip", "scan2d_bf16_g4.hip", "scan2d_bf16_g8.hip"]
 LIB = os.path.join(PKG, "libssm2d.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -14,13 +21,31 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fPIC", "-shared",
+    # single-lane LDS counter updates stay single instructions
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    "-fPIC",
 ]
 
 
 def build(out_path: str = LIB) -> str:
-    cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", out_path]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    with tempfile.TemporaryDirectory(prefix="ssm2d_build_") as tmp:
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        errors = []
+        for src, pr in procs:
+            out, _ = pr.communicate()
+            if pr.returncode != 0:
+                errors.append(f"{src}:\n{out}")
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp_out = out_path + ".tmp"
+        cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
+        os.replace(tmp_out, out_path)
     return out_path

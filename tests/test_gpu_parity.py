@@ -129,6 +129,26 @@ def test_multi_workgroup_chains(waves, groups, monkeypatch):
         check(as_f64(run_gpu(t, dtype)), ref_of(t), dtype, f"waves={waves} groups={groups} {shape}")
 
 
+COOP_SHAPES = [
+    # tall maps (H >= 128, W % 4 == 0) cut into several workgroups per chain:
+    # the workgroup shares one ring of input rows (cooperative loads)
+    ((1, 16, 16, 160, 96), None), ((1, 8, 40, 130, 68), None), ((2, 24, 4, 128, 44), "3"),
+    ((1, 16, 16, 131, 64), "8"), ((1, 8, 8, 200, 36), "5"),
+]
+
+
+@pytest.mark.parametrize("case", COOP_SHAPES, ids=[str(c) for c in COOP_SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cooperative_row_ring(case, dtype, monkeypatch):
+    shape, waves = case
+    monkeypatch.setenv("SSM2D_GROUPS", "8")
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    _say(f"row ring {shape} waves={waves} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape), dtype=dtype)
+    check(as_f64(run_gpu(t, dtype)), ref_of(t), dtype, f"row ring {shape} waves={waves}")
+
+
 def test_special_cases_through_gpu():
     # constant delta (position-independent Abar), A = 0 (Abar = 1), d_state = 0
     t = make_random_inputs(1, 16, 16, 20, 24, seed=5, delta_mode="const")
