@@ -567,7 +567,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 const int rem = cw % (nact * CPR);
                 jc = (grp * p.s_local + rem / CPR) * K;
                 q = rem % CPR;
-                wpos[pp] = (rem / CPR) * (NCHUNK + 1) + r * CPR + q;
+                // padding lanes (c >= NCHUNK) write the strip's unused pad chunk
+                wpos[pp] = (c < NCHUNK) ? (rem / CPR) * (NCHUNK + 1) + r * CPR + q : wave * (NCHUNK + 1) + NCHUNK;
             }
             const T *base = zeros;
             if (c < NCHUNK) {
@@ -599,6 +600,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             Ap[k] = (n < p.d_state && d_ok) ? p.A[d * p.d_state + n] * kLog2e : 0.0f;
         }
         const float Dd = d_ok ? p.D[d] : 0.0f;
+        // Wait for these loads here, once: used inside the row loop they
+        // would make the compiler wait for every load in flight (the row
+        // prefetches too) at each use, since it cannot tell at the loop head
+        // whether they have completed.
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) asm volatile("" ::"v"(Ap[k]));
+        asm volatile("" ::"v"(Dd));
         // First of this lane's finished cells (for G = 8 and K = 4 the two
         // lanes of a pair hold the same cell and the odd one does not store).
         const int c_out = (K >= G) ? g * KO : g / 2;
@@ -681,8 +689,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 T *slot = row_base(tw);
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp)
-                    if ((pp + 1) * kWave <= NCHUNK || pp * kWave + lane < NCHUNK)
-                        reinterpret_cast<Chunk *>(slot)[wpos[pp]] = cb[pp];
+                    reinterpret_cast<Chunk *>(slot)[wpos[pp]] = cb[pp];
                 signal_fence();
                 if (lane == 0)
                     __hip_atomic_fetch_add(&s_arrive[tw & slot_mask], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -871,10 +878,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 for (int s = 0; s < P; ++s)
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        // lanes past the packet's end load nothing (their
-                        // chunk only fills padding)
-                        if ((pp + 1) * kWave <= NCHUNK || pp * kWave + lane < NCHUNK)
-                            buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s + (COOP ? XA : 0), H - 1)) * W);
+                        buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s + (COOP ? XA : 0), H - 1)) * W);
             };
             if constexpr (COOP) {
                 // shares of rows 0 .. XA-1; row XA's comes from bufA[0] below
@@ -882,13 +886,11 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     Chunk c0[PASSES];
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        if ((pp + 1) * kWave <= NCHUNK || pp * kWave + lane < NCHUNK)
-                            c0[pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(t, H - 1)) * W);
+                        c0[pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(t, H - 1)) * W);
                     T *slot = row_base(t);
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        if ((pp + 1) * kWave <= NCHUNK || pp * kWave + lane < NCHUNK)
-                            reinterpret_cast<Chunk *>(slot)[wpos[pp]] = c0[pp];
+                        reinterpret_cast<Chunk *>(slot)[wpos[pp]] = c0[pp];
                     signal_fence();
                     if (lane == 0)
                         __hip_atomic_fetch_add(&s_arrive[t & slot_mask], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
