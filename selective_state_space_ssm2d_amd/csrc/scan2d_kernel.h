@@ -830,6 +830,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     for (int k = 0; k < NPL; ++k) dst[k] = hh[k];
                     signal_fence();
                     lds_poke(&s_done[wave + 1], i + 1);
+                    // keep the vertical step below from being scheduled ahead
+                    // of the publish: it would sit on the carry's path
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
 
