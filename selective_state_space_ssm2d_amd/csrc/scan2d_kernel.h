@@ -801,6 +801,11 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                             float t[NPL];
 #pragma unroll
                             for (int k = 0; k < NPL; ++k) t[k] = src_c[k];
+                            // issue the slot read with the counter read (left
+                            // alone, the compiler reads the slot only after the
+                            // check: a second round trip on the carry's path)
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(t[k]));
                             if (__builtin_amdgcn_readfirstlane(v) > i) {
 #pragma unroll
                                 for (int k = 0; k < NPL; ++k) hh[k] = t[k];

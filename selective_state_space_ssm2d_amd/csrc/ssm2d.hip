@@ -67,7 +67,9 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     const long row_bytes = static_cast<long>(kWave) * npl * 4;
     const long budget = 48 * 1024;
     int R = 8;
-    while (R > 2 && (s_local + 1) * R * row_bytes > budget) R /= 2;
+    const int renv = env_int("SSM2D_LDSRING", 0);
+    if (renv == 4 || renv == 16 || renv == 32) R = renv;
+    while (R > 2 && (s_local + 1) * R * row_bytes > budget * (R > 8 ? 2 : 1)) R /= 2;
     pl.ring_rows = R;
     pl.qg = static_cast<int>(H);
     return pl;
