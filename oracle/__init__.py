@@ -11,8 +11,10 @@ and the passages they follow). This module only marshals numpy arrays.
 Functions
 ---------
 build()                 compile ssm2d_oracle.c into libssm2d_oracle.so (gcc)
-fwd(x, delta, A, B, C, D, maps=None, nthreads=0) -> y (float64)
-states(abar, bx) -> h   the recurrences alone on given Abar, Bx (one map)
+fwd(x, delta, A, B, C, D, maps=None, nthreads=0, flip_h=False, flip_w=False,
+    vertical_first=False) -> y (float64)
+states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
+                        the recurrences alone on given Abar, Bx (one map)
 max_threads()           OpenMP thread count the oracle uses by default
 """
 from __future__ import annotations
@@ -48,6 +50,11 @@ def load(path: str = LIB_PATH):
     lib.oracle_ssm2d_fwd_maps_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_states_f64.argtypes = [dp, dp, dp, i64, i64]
     lib.oracle_ssm2d_states_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_fwd_ex_f64.argtypes = [dp] * 7 + [i64] * 5 + [
+        ctypes.POINTER(i64), i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_ssm2d_fwd_ex_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_states_ex_f64.argtypes = [dp, dp, dp, i64, i64, ctypes.c_int]
+    lib.oracle_ssm2d_states_ex_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -71,14 +78,22 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None):
+def _flags(flip_h, flip_w, vertical_first):
+    return (1 if flip_h else 0) | (2 if flip_w else 0) | (4 if vertical_first else 0)
+
+
+def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, flip_w=False,
+        vertical_first=False):
     """y = 2D selective scan forward in fp64.
 
     x, delta: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
     [batch][d_state][H][W]; D: [d_inner]. With ``maps`` (flat indices
     b*d_inner+d), returns y for those maps only, shape [len(maps)][H][W];
-    otherwise the full [batch][d_inner][H][W].
+    otherwise the full [batch][d_inner][H][W]. flip_h / flip_w scan rows
+    bottom to top / columns right to left; vertical_first runs the column
+    recurrence before the row recurrence.
     """
+    flags = _flags(flip_h, flip_w, vertical_first)
     lib = lib or _get()
     x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))
     batch, d_inner, H, W = x.shape
@@ -93,21 +108,30 @@ def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None):
         m = np.ascontiguousarray(maps, dtype=np.int64)
         y = np.empty((m.size, H, W), dtype=np.float64)
         mp, nm = m.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), m.size
-    s = lib.oracle_ssm2d_fwd_maps_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                      _ptr(D), _ptr(y), batch, d_inner, d_state, H, W,
-                                      mp, nm, int(nthreads))
+    if flags == 0:
+        s = lib.oracle_ssm2d_fwd_maps_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(y), batch, d_inner, d_state, H, W,
+                                          mp, nm, int(nthreads))
+    else:
+        s = lib.oracle_ssm2d_fwd_ex_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                        _ptr(D), _ptr(y), batch, d_inner, d_state, H, W,
+                                        mp, nm, int(nthreads), flags)
     if s != 0:
         raise RuntimeError(f"oracle failed with status {s}")
     return y
 
 
-def states(abar, bx, lib=None):
+def states(abar, bx, lib=None, flip_h=False, flip_w=False, vertical_first=False):
     """h for one state map from given Abar [H][W] and Bx [H][W] (fp64)."""
     lib = lib or _get()
     abar, bx = _f64(abar), _f64(bx)
     H, W = abar.shape
     h = np.empty((H, W), dtype=np.float64)
-    s = lib.oracle_ssm2d_states_f64(_ptr(abar), _ptr(bx), _ptr(h), H, W)
+    flags = _flags(flip_h, flip_w, vertical_first)
+    if flags == 0:
+        s = lib.oracle_ssm2d_states_f64(_ptr(abar), _ptr(bx), _ptr(h), H, W)
+    else:
+        s = lib.oracle_ssm2d_states_ex_f64(_ptr(abar), _ptr(bx), _ptr(h), H, W, flags)
     if s != 0:
         raise RuntimeError(f"oracle failed with status {s}")
     return h

@@ -51,6 +51,74 @@ static void scan_state_map(const double *abar, const double *bx, double *h,
     }
 }
 
+/* The same two recurrences in another scan direction or order.
+ *
+ * The pages' scan runs left to right, then top to bottom, and leaves both
+ * the reverse scans and the vertical-then-horizontal order as variants: the
+ * papernotes.org page (消融实验要点) finds the two orders nearly equal, its
+ * 局限与展望 notes that the upper-left scan needs a reverse scan for full
+ * context, and the juejin.cn page (part 七, section 4) lists bidirectional and
+ * four-quadrant 2D propagation. Read plainly, a flipped axis scans from the
+ * other end, with zero state before the first cell in scan order; the
+ * vertical-first order runs the column recurrence on Bx and the row
+ * recurrence over its results.
+ *
+ *   flip_h: rows bottom to top; flip_w: columns right to left;
+ *   vfirst: v[i,j] = Abar[i,j] v[i-1,j] + Bx[i,j] (column scan first),
+ *           h[i,j] = Abar[i,j] h[i,j-1] + v[i,j]  (row scan of the results)
+ * ("i-1", "j-1" meaning the previous cell in scan order). tmp: H*W scratch. */
+static void scan_state_map_dir(const double *abar, const double *bx, double *h, double *tmp,
+                               int64_t H, int64_t W, int flip_h, int flip_w, int vfirst)
+{
+    for (int64_t si = 0; si < H; ++si) {
+        const int64_t i = flip_h ? H - 1 - si : si;      /* row in scan order */
+        const int64_t ip = flip_h ? i + 1 : i - 1;        /* previous row in scan order */
+        if (!vfirst) {
+            double carry = 0.0;                           /* row recurrence first */
+            for (int64_t sj = 0; sj < W; ++sj) {
+                const int64_t j = flip_w ? W - 1 - sj : sj;
+                carry = abar[i * W + j] * carry + bx[i * W + j];
+                tmp[i * W + j] = carry;
+            }
+            for (int64_t j = 0; j < W; ++j) {
+                const double prev = (si > 0) ? h[ip * W + j] : 0.0;
+                h[i * W + j] = abar[i * W + j] * prev + tmp[i * W + j];
+            }
+        } else {
+            for (int64_t j = 0; j < W; ++j) {             /* column recurrence first */
+                const double prev = (si > 0) ? tmp[ip * W + j] : 0.0;
+                tmp[i * W + j] = abar[i * W + j] * prev + bx[i * W + j];
+            }
+            double carry = 0.0;
+            for (int64_t sj = 0; sj < W; ++sj) {
+                const int64_t j = flip_w ? W - 1 - sj : sj;
+                carry = abar[i * W + j] * carry + tmp[i * W + j];
+                h[i * W + j] = carry;
+            }
+        }
+    }
+}
+
+/* Direction / order flags of the variant entries (bit values). */
+#define ORACLE_FLIP_H 1
+#define ORACLE_FLIP_W 2
+#define ORACLE_VFIRST 4
+
+/* Internal entry: the recurrences in the direction and order `flags` selects,
+ * on caller-supplied Abar and Bx ([H][W] doubles). Returns 0, 2 or 6. */
+int oracle_ssm2d_states_ex_f64(const double *abar, const double *bx, double *h,
+                               int64_t H, int64_t W, int flags)
+{
+    if (H < 0 || W < 0) return 2;
+    if (H == 0 || W == 0) return 0;
+    double *tmp = (double *)malloc((size_t)(H * W) * sizeof(double));
+    if (!tmp) return 6;
+    scan_state_map_dir(abar, bx, h, tmp, H, W, (flags & ORACLE_FLIP_H) != 0,
+                       (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0);
+    free(tmp);
+    return 0;
+}
+
 /* Internal entry: the recurrences alone, on caller-supplied Abar and Bx.
  * abar, bx, h: [H][W] doubles. Returns 0, or 2 on a bad size. */
 int oracle_ssm2d_states_f64(const double *abar, const double *bx, double *h,
@@ -69,7 +137,7 @@ int oracle_ssm2d_states_f64(const double *abar, const double *bx, double *h,
 static int forward_one_map(const double *x, const double *delta, const double *A,
                            const double *B, const double *C, const double *D,
                            double *y_map, int64_t b, int64_t d, int64_t d_inner,
-                           int64_t d_state, int64_t H, int64_t W)
+                           int64_t d_state, int64_t H, int64_t W, int flags)
 {
     const int64_t L = H * W;
     const double *xm = x + (b * d_inner + d) * L;
@@ -77,7 +145,7 @@ static int forward_one_map(const double *x, const double *delta, const double *A
     double *abar = (double *)malloc((size_t)L * sizeof(double));
     double *bx = (double *)malloc((size_t)L * sizeof(double));
     double *h = (double *)malloc((size_t)L * sizeof(double));
-    double *hh_row = (double *)malloc((size_t)W * sizeof(double));
+    double *hh_row = (double *)malloc((size_t)(flags ? L : W) * sizeof(double));
     if (!abar || !bx || !h || !hh_row) {
         free(abar); free(bx); free(h); free(hh_row);
         return 6;
@@ -91,7 +159,9 @@ static int forward_one_map(const double *x, const double *delta, const double *A
             abar[p] = exp(dm[p] * a);
             bx[p] = dm[p] * Bn[p] * xm[p];
         }
-        scan_state_map(abar, bx, h, hh_row, H, W);
+        if (flags == 0) scan_state_map(abar, bx, h, hh_row, H, W);
+        else scan_state_map_dir(abar, bx, h, hh_row, H, W, (flags & ORACLE_FLIP_H) != 0,
+                                (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0);
         for (int64_t p = 0; p < L; ++p) y_map[p] += Cn[p] * h[p];
     }
     for (int64_t p = 0; p < L; ++p) y_map[p] += D[d] * xm[p];
@@ -107,11 +177,10 @@ static int forward_one_map(const double *x, const double *delta, const double *A
  * nthreads: OpenMP threads (<= 0: runtime default).
  * Returns 0 on success, 2 on a bad size or map index, 6 on allocation failure.
  */
-int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double *A,
-                              const double *B, const double *C, const double *D,
-                              double *y, int64_t batch, int64_t d_inner, int64_t d_state,
-                              int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
-                              int nthreads)
+static int fwd_maps(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, double *y, int64_t batch, int64_t d_inner,
+                    int64_t d_state, int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
+                    int nthreads, int flags)
 {
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
     const int64_t total = batch * d_inner;
@@ -130,13 +199,36 @@ int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double
     for (int64_t k = 0; k < n_maps; ++k) {
         const int64_t m = maps ? maps[k] : k;
         int s = forward_one_map(x, delta, A, B, C, D, y + k * H * W, m / d_inner,
-                                m % d_inner, d_inner, d_state, H, W);
+                                m % d_inner, d_inner, d_state, H, W, flags);
         if (s != 0) {
 #pragma omp atomic write
             status = s;
         }
     }
     return status;
+}
+
+int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double *A,
+                              const double *B, const double *C, const double *D,
+                              double *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                              int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
+                              int nthreads)
+{
+    return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
+                    nthreads, 0);
+}
+
+/* The forward pass in the direction / order `flags` selects (ORACLE_FLIP_H,
+ * ORACLE_FLIP_W, ORACLE_VFIRST); otherwise as oracle_ssm2d_fwd_maps_f64. */
+int oracle_ssm2d_fwd_ex_f64(const double *x, const double *delta, const double *A,
+                            const double *B, const double *C, const double *D,
+                            double *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                            int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
+                            int nthreads, int flags)
+{
+    if (flags < 0 || flags > 7) return 2;
+    return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
+                    nthreads, flags);
 }
 
 /* Number of threads the OpenMP runtime would use (1 without OpenMP). */

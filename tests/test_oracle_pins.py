@@ -271,6 +271,107 @@ def pin_map_independence(lib):
     assert np.array_equal(ys, y.reshape(12, 5, 6)[sel])
 
 
+# ---------------------------------------------------------------- P12-P14 directions and order
+# The variants (papernotes.org 消融实验要点: horizontal-then-vertical versus
+# vertical-then-horizontal; 局限与展望: a reverse scan for full context;
+# juejin.cn part 七 section 4: bidirectional and four-quadrant propagation).
+def _path_exact(abar, bx, flip_h, flip_w, vfirst):
+    """Exact rational h for any scan direction and order, by unrolling the
+    recurrences by hand. In scan coordinates (rows and columns counted from
+    the scan's starting corner) a source reaches a target in its quadrant;
+    the horizontal-first order moves along the source's row and then down the
+    target's column, the vertical-first order down the source's column and
+    then along the target's row, multiplying the Abar values entered."""
+    H, W = len(abar), len(abar[0])
+    row = (lambda u: H - 1 - u) if flip_h else (lambda u: u)   # scan row -> map row
+    col = (lambda v: W - 1 - v) if flip_w else (lambda v: v)
+    a = lambda u, v: abar[row(u)][col(v)]
+    h = [[Fraction(0)] * W for _ in range(H)]
+    for u in range(H):
+        for v in range(W):
+            tot = Fraction(0)
+            for up in range(u + 1):
+                for vp in range(v + 1):
+                    w = Fraction(1)
+                    if not vfirst:
+                        for k in range(vp + 1, v + 1):
+                            w *= a(up, k)
+                        for m in range(up + 1, u + 1):
+                            w *= a(m, v)
+                    else:
+                        for m in range(up + 1, u + 1):
+                            w *= a(m, vp)
+                        for k in range(vp + 1, v + 1):
+                            w *= a(u, k)
+                    tot += w * bx[row(up)][col(vp)]
+            h[row(u)][col(v)] = tot
+    return h
+
+
+def pin_directions_bruteforce(lib):
+    """All eight (flip rows, flip columns, order) variants on tiny grids with
+    selective Abar, against exact rationals."""
+    rng = np.random.default_rng(11)
+    for (H, W) in ((3, 3), (2, 4), (4, 2), (1, 4), (3, 1)):
+        abar = rng.uniform(0.05, 1.2, size=(H, W))
+        bx = rng.standard_normal((H, W))
+        fa = [[Fraction(float(v)) for v in r] for r in abar]
+        fb = [[Fraction(float(v)) for v in r] for r in bx]
+        for fh in (False, True):
+            for fw in (False, True):
+                for vf in (False, True):
+                    h = oracle.states(abar, bx, lib=lib, flip_h=fh, flip_w=fw, vertical_first=vf)
+                    exact = _path_exact(fa, fb, fh, fw, vf)
+                    scale = Fraction(max(1.0, float(np.max(np.abs(h)))))
+                    for i in range(H):
+                        for j in range(W):
+                            assert abs(Fraction(float(h[i, j])) - exact[i][j]) <= Fraction(1, 10 ** 14) * scale, \
+                                (H, W, fh, fw, vf, i, j)
+
+
+def pin_directions_reduce_to_1d(lib):
+    """One row: the scan is 1D Mamba along the row, in reverse when the
+    columns are flipped (order and row flips change nothing). One column:
+    likewise along the column."""
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 1, 23, 12)
+    for fh in (False, True):
+        for fw in (False, True):
+            for vf in (False, True):
+                y = oracle.fwd(x, dt, A, B, C, D, lib=lib, flip_h=fh, flip_w=fw, vertical_first=vf)
+                sl = slice(None, None, -1) if fw else slice(None)
+                ref = _mamba_1d(x[:, :, 0, sl], dt[:, :, 0, sl], A, B[:, :, 0, sl], C[:, :, 0, sl], D)
+                _close(y[:, :, 0, sl], ref, 1e-13, f"H=1 flips {fh},{fw} vf {vf}")
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 19, 1, 13)
+    for fh in (False, True):
+        for vf in (False, True):
+            y = oracle.fwd(x, dt, A, B, C, D, lib=lib, flip_h=fh, vertical_first=vf)
+            sl = slice(None, None, -1) if fh else slice(None)
+            ref = _mamba_1d(x[:, :, sl, 0], dt[:, :, sl, 0], A, B[:, :, sl, 0], C[:, :, sl, 0], D)
+            _close(y[:, :, sl, 0], ref, 1e-13, f"W=1 flip {fh} vf {vf}")
+
+
+def pin_order_closed_form(lib):
+    """Constant delta: both orders reach the Manhattan-power double sum (the
+    closed form is symmetric in the two axes), here for the lower-right
+    starting corner."""
+    H, W, N = 6, 5, 3
+    x, dt, A, B, C, D = _inputs(1, 2, N, H, W, 14, delta_mode="const")
+    for vf in (False, True):
+        y = oracle.fwd(x, dt, A, B, C, D, lib=lib, flip_h=True, flip_w=True, vertical_first=vf)
+        for d in range(2):
+            acc = D[d] * x[0, d]
+            for n in range(N):
+                a = np.exp(dt[0, d, 0, 0] * A[d, n])
+                bx = dt[0, d] * B[0, n] * x[0, d]
+                h = np.zeros((H, W))
+                for i in range(H):
+                    for j in range(W):
+                        h[i, j] = sum(a ** ((ip - i) + (jp - j)) * bx[ip, jp]
+                                      for ip in range(i, H) for jp in range(j, W))
+                acc = acc + C[0, n] * h
+            _close(y[0, d], acc, 1e-12, f"closed form, lower-right corner, vf={vf}")
+
+
 ALL_PINS = [
     pin_closed_form_constant_delta,
     pin_worked_example_3x3,
@@ -283,6 +384,9 @@ ALL_PINS = [
     pin_upper_left_support,
     pin_transpose_symmetry,
     pin_map_independence,
+    pin_directions_bruteforce,
+    pin_directions_reduce_to_1d,
+    pin_order_closed_form,
 ]
 
 
@@ -324,6 +428,12 @@ MUTANTS = {
     "vertical carry taken from the left neighbour":
         ("double up = (i > 0) ? h[(i - 1) * W + j] : 0.0;",
          "double up = (j > 0) ? h[i * W + j - 1] : 0.0;"),
+    "vertical-first column step drops Abar":
+        ("tmp[i * W + j] = abar[i * W + j] * prev + bx[i * W + j];", "tmp[i * W + j] = prev + bx[i * W + j];"),
+    "flipped columns scanned left to right":
+        ("const int64_t j = flip_w ? W - 1 - sj : sj;", "const int64_t j = sj;"),
+    "vertical-first row scan adds Bx":
+        ("carry = abar[i * W + j] * carry + tmp[i * W + j];", "carry = abar[i * W + j] * carry + bx[i * W + j];"),
 }
 
 
@@ -334,7 +444,7 @@ def test_pins_catch_planted_mistakes(tmp_path):
     for name, (old, new) in MUTANTS.items():
         assert src.count(old) >= 1, f"mutation site missing: {name}"
         path = tmp_path / (str(abs(hash(name))) + ".c")
-        path.write_text(src.replace(old, new))
+        path.write_text(src.replace(old, new, 1))
         lib_path = str(tmp_path / (str(abs(hash(name))) + ".so"))
         oracle.build(out_path=lib_path, src_path=str(path))
         lib = oracle.load(lib_path)
