@@ -66,7 +66,8 @@ typedef enum {
     SSM2D_ERR_MISALIGNED = 4,
     SSM2D_ERR_HIP = 5,
     SSM2D_ERR_NOMEM = 6,
-    SSM2D_ERR_DEVICE_TIMEOUT = 7
+    SSM2D_ERR_DEVICE_TIMEOUT = 7,
+    SSM2D_ERR_BAD_FLAGS = 8
 } ssm2d_status;
 
 /* fp32 forward: x, delta, B, C, y are float32; A, D float32; state fp32. */
@@ -80,6 +81,58 @@ int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
                         const uint16_t *B, const uint16_t *C, const float *D, uint16_t *y,
                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
                         void *stream);
+
+/* ---- Scan direction, scan order and multi-direction sums ----------------
+ *
+ * The scan above starts at the upper-left corner: a cell sees the cells above
+ * and to its left. The pages leave other directions and the other order as
+ * variants: the papernotes.org page finds the vertical-then-horizontal order
+ * about as good (消融实验要点) and notes that full context needs a reverse scan
+ * from the lower right (局限与展望); the juejin.cn page (part 七, section 4)
+ * lists bidirectional and four-quadrant 2D propagation. Read plainly:
+ *
+ *   SSM2D_FLIP_H          rows run bottom to top (h[i,j] takes h[i+1,j])
+ *   SSM2D_FLIP_W          columns run right to left (hh[i,j] takes hh[i,j+1])
+ *   SSM2D_VERTICAL_FIRST  v[i,j] = Abar v[i-1,j] + Bx   (column scan first)
+ *                         h[i,j] = Abar h[i,j-1] + v[i,j] (row scan of its results)
+ *                         ("i-1", "j-1": the previous cell in scan order)
+ *   SSM2D_ACCUMULATE      y += result, instead of y = result
+ *   SSM2D_FOUR_WAY        result = the sum of the four scans from the four
+ *                         corners (no flip, FLIP_H, FLIP_W, both), each in the
+ *                         order VERTICAL_FIRST selects, plus D x once
+ *
+ * State starts at zero before the first row and column in scan order. */
+#define SSM2D_FLIP_H 1u
+#define SSM2D_FLIP_W 2u
+#define SSM2D_VERTICAL_FIRST 4u
+#define SSM2D_ACCUMULATE 8u
+#define SSM2D_FOUR_WAY 16u
+
+/* Forward pass in the direction and order `flags` selects (an OR of the bits
+ * above; 0 gives ssm2d_scan_fwd). Arguments, layout, ownership, asynchrony and
+ * errors as for ssm2d_scan_fwd, and also:
+ *   D may be NULL: no skip term (as D = 0).
+ *   SSM2D_ACCUMULATE reads y: y must hold valid values. The additions are
+ *     returnless hardware atomics, one per cell and call, so the result is
+ *     y + result rounded once (fp32), deterministic for calls on one stream;
+ *     fp32 denormal sums may be flushed to zero.
+ *   bf16: y + bf16(result), rounded to bf16 (two roundings).
+ *   SSM2D_FOUR_WAY enqueues four kernels on `stream`, the last three
+ *     accumulating; with SSM2D_ACCUMULATE the first accumulates too.
+ *   Unknown bits, or SSM2D_FOUR_WAY with SSM2D_FLIP_H or SSM2D_FLIP_W
+ *                                                -> SSM2D_ERR_BAD_FLAGS
+ *     (checked first, before the sizes).
+ * Right-to-left and vertical-first scans run 4-column strips with 8 state
+ * groups per wave whatever the shape. */
+int ssm2d_scan_fwd_ex(const float *x, const float *delta, const float *A, const float *B,
+                      const float *C, const float *D, float *y, int64_t batch, int64_t d_inner,
+                      int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
+
+/* bf16 variant of ssm2d_scan_fwd_ex: types as for ssm2d_scan_fwd_bf16. */
+int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                           const uint16_t *B, const uint16_t *C, const float *D, uint16_t *y,
+                           int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                           uint32_t flags, void *stream);
 
 /* Static description of a status code. Never NULL. */
 const char *ssm2d_status_string(int status);

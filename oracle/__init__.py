@@ -12,7 +12,7 @@ Functions
 ---------
 build()                 compile ssm2d_oracle.c into libssm2d_oracle.so (gcc)
 fwd(x, delta, A, B, C, D, maps=None, nthreads=0, flip_h=False, flip_w=False,
-    vertical_first=False) -> y (float64)
+    vertical_first=False, four_way=False) -> y (float64)
 states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
                         the recurrences alone on given Abar, Bx (one map)
 max_threads()           OpenMP thread count the oracle uses by default
@@ -83,7 +83,7 @@ def _flags(flip_h, flip_w, vertical_first):
 
 
 def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, flip_w=False,
-        vertical_first=False):
+        vertical_first=False, four_way=False):
     """y = 2D selective scan forward in fp64.
 
     x, delta: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
@@ -91,8 +91,20 @@ def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, fli
     b*d_inner+d), returns y for those maps only, shape [len(maps)][H][W];
     otherwise the full [batch][d_inner][H][W]. flip_h / flip_w scan rows
     bottom to top / columns right to left; vertical_first runs the column
-    recurrence before the row recurrence.
+    recurrence before the row recurrence. four_way sums the scans from the
+    four corners (the four-quadrant propagation of the juejin.cn page, part 七
+    section 4) with the D x term counted once; D may be None (no skip term).
     """
+    if D is None:
+        D = np.zeros(np.shape(A)[0])
+    if four_way:
+        assert not (flip_h or flip_w)
+        zero = np.zeros_like(_f64(D))
+        y = fwd(x, delta, A, B, C, D, maps, nthreads, lib, vertical_first=vertical_first)
+        for fh, fw in ((True, False), (False, True), (True, True)):
+            y = y + fwd(x, delta, A, B, C, zero, maps, nthreads, lib, flip_h=fh, flip_w=fw,
+                        vertical_first=vertical_first)
+        return y
     flags = _flags(flip_h, flip_w, vertical_first)
     lib = lib or _get()
     x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))

@@ -7,11 +7,14 @@ scan runs in the library's HIP kernels. PyTorch supplies device memory and
 streams only. There is no fallback: if the library is missing the call fails.
 
     y = scan_fwd(x, delta, A, B, C, D)
+    y = scan_fwd_ex(x, delta, A, B, C, D, flip_h=..., flip_w=..., vertical_first=...,
+                    accumulate=..., four_way=...)
 
 x, delta: [batch, d_inner, H, W]; B, C: [batch, d_state, H, W]; all four
 float32 or all four bfloat16. A: [d_inner, d_state] float32; D: [d_inner]
-float32. y has the dtype of x. All tensors on the current CUDA (HIP) device,
-contiguous.
+float32 (``scan_fwd_ex``: or None, no skip term). y has the dtype of x. All
+tensors on the current CUDA (HIP) device, contiguous. ``scan_fwd_ex`` selects
+the scan direction and order, and multi-direction sums (SSM2D_* flags).
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import os
 import re
 
 __all__ = [
-    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "status_string",
+    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "status_string",
     "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
 ]
 
@@ -28,7 +31,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm2d.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm2d.h")
 
-OK, ERR_NULLPTR, ERR_BAD_DIM, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NOMEM, ERR_DEVICE_TIMEOUT = range(8)
+(OK, ERR_NULLPTR, ERR_BAD_DIM, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NOMEM, ERR_DEVICE_TIMEOUT,
+ ERR_BAD_FLAGS) = range(9)
+FLIP_H, FLIP_W, VERTICAL_FIRST, ACCUMULATE, FOUR_WAY = 1, 2, 4, 8, 16
 
 _lib = None
 
@@ -51,6 +56,10 @@ def load_library(path: str = LIB_PATH):
     for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
+        f.restype = ctypes.c_int
+    for name in ("ssm2d_scan_fwd_ex", "ssm2d_scan_fwd_ex_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 7 + [i64] * 5 + [ctypes.c_uint32, vp]
         f.restype = ctypes.c_int
     lib.ssm2d_status_string.argtypes = [ctypes.c_int]
     lib.ssm2d_status_string.restype = ctypes.c_char_p
@@ -100,11 +109,9 @@ def set_spin_limit(polls: int) -> None:
     load_library().ssm2d_set_spin_limit(int(polls))
 
 
-def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
-    """y = 2D selective scan forward (see module docstring)."""
+def _check(x, delta, A, B, C, D, y, need_d):
     import torch
 
-    lib = load_library()
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x and B must be 4-D")
     batch, d_inner, H, W = x.shape
@@ -113,7 +120,9 @@ def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
         raise ValueError("delta must have the shape of x")
     if B.shape != (batch, d_state, H, W) or C.shape != B.shape:
         raise ValueError("B and C must be [batch, d_state, H, W]")
-    if A.shape != (d_inner, d_state) or D.shape != (d_inner,):
+    if D is None and need_d:
+        raise ValueError("D is required")
+    if A.shape != (d_inner, d_state) or (D is not None and D.shape != (d_inner,)):
         raise ValueError("A must be [d_inner, d_state] and D [d_inner]")
     dt = x.dtype
     if dt not in (torch.float32, torch.bfloat16):
@@ -122,26 +131,64 @@ def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
         if t.dtype != dt:
             raise TypeError(f"{name} must have the dtype of x")
     for name, t in (("A", A), ("D", D)):
-        if t.dtype != torch.float32:
+        if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
-    tensors = [x, delta, A, B, C, D]
     if y is None:
         y = torch.empty_like(x)
     elif y.shape != x.shape or y.dtype != dt:
         raise ValueError("y must match x in shape and dtype")
-    tensors.append(y)
     dev = x.device
-    for t in tensors:
+    for t in (x, delta, A, B, C, D, y):
+        if t is None:
+            continue
         if t.device != dev or dev.type != "cuda":
             raise ValueError("all tensors must be on the same GPU device")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    fn = lib.ssm2d_scan_fwd if dt == torch.float32 else lib.ssm2d_scan_fwd_bf16
+    return y, (batch, d_inner, d_state, H, W)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else None)
+
+
+def _call(fn, lib, dev, args):
+    import torch
+
     with torch.cuda.device(dev):
-        s = fn(*(ctypes.c_void_p(t.data_ptr()) for t in tensors), batch, d_inner, d_state, H, W,
-               _stream_handle(stream))
+        s = fn(*args)
     if s == ERR_HIP:
         raise Ssm2dError(s, f"{fn.__name__} ({lib.ssm2d_last_hip_error().decode()})")
     if s != OK:
         raise Ssm2dError(s, fn.__name__)
+
+
+def scan_fwd(x, delta, A, B, C, D, y=None, stream=None):
+    """y = 2D selective scan forward (see module docstring)."""
+    import torch
+
+    lib = load_library()
+    y, dims = _check(x, delta, A, B, C, D, y, need_d=True)
+    fn = lib.ssm2d_scan_fwd if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_bf16
+    _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, y)] + [*dims, _stream_handle(stream)])
+    return y
+
+
+def scan_fwd_ex(x, delta, A, B, C, D=None, y=None, *, flip_h=False, flip_w=False, vertical_first=False,
+                accumulate=False, four_way=False, flags=None, stream=None):
+    """2D selective scan forward in another direction / order (include/ssm2d.h,
+    ssm2d_scan_fwd_ex). With ``accumulate`` the result is added to ``y``, which
+    must then be given. ``flags`` (an int of SSM2D_* bits) overrides the
+    keyword switches and is passed through unchecked."""
+    import torch
+
+    lib = load_library()
+    if accumulate and y is None:
+        raise ValueError("accumulate needs y")
+    y, dims = _check(x, delta, A, B, C, D, y, need_d=False)
+    if flags is None:
+        flags = ((FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
+                 | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0))
+    fn = lib.ssm2d_scan_fwd_ex if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_ex_bf16
+    _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, y)] + [*dims, int(flags), _stream_handle(stream)])
     return y

@@ -13,7 +13,9 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["ssm2d.hip", "scan2d_f32_g4.hip", "scan2d_f32_g8.hip", "scan2d_bf16_g4.hip", "scan2d_bf16_g8.hip"]
+# one translation unit per (input type, lane layout or mode)
+_VARIANTS = ("g4", "g8", "flipw", "vfirst", "flipw_vfirst", "acc", "flipw_acc", "vfirst_acc", "flipw_vfirst_acc")
+SOURCES = ["ssm2d.hip"] + [f"scan2d_{t}_{v}.hip" for t in ("f32", "bf16") for v in _VARIANTS]
 LIB = os.path.join(PKG, "libssm2d.so")
 INCLUDE = os.path.join(ROOT, "include")
 

@@ -83,6 +83,7 @@ struct Params {
     int vec_store;                     // gather each channel's cells and store whole chunks
     int coop_slots;                    // rows in the workgroup's shared row ring (cooperative loads)
     int coop_shift;                    // log2 of coop_slots
+    int flip_h;                        // rows in scan order run bottom to top
     unsigned int epoch;
     long long spin_limit;
 };
@@ -135,42 +136,62 @@ __device__ __forceinline__ uint2 load_chunk(const uint16_t *const (&sp)[4 / ALIG
 }
 
 // N consecutive packet elements (N % 4 == 0) starting at element offset `off`.
-template <int N>
+// REV: each chunk holds its 4 cells in reverse order (rows scanned right to
+// left are loaded in memory order), so element m of a chunk is cell 3 - m.
+template <int N, bool REV = false>
 __device__ __forceinline__ void read_packet(const float *pk, int off, float (&v)[N])
 {
+    constexpr int X = REV ? 3 : 0;
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
         float4 t = *reinterpret_cast<const float4 *>(pk + off + 4 * q);
-        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        v[4 * q + (0 ^ X)] = t.x; v[4 * q + (1 ^ X)] = t.y; v[4 * q + (2 ^ X)] = t.z; v[4 * q + (3 ^ X)] = t.w;
     }
 }
-template <int N>
+template <int N, bool REV = false>
 __device__ __forceinline__ void read_packet(const uint16_t *pk, int off, float (&v)[N])
 {
+    constexpr int X = REV ? 3 : 0;
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
         uint2 t = *reinterpret_cast<const uint2 *>(pk + off + 4 * q);
-        v[4 * q] = bf16_lo(t.x); v[4 * q + 1] = bf16_hi(t.x);
-        v[4 * q + 2] = bf16_lo(t.y); v[4 * q + 3] = bf16_hi(t.y);
+        v[4 * q + (0 ^ X)] = bf16_lo(t.x); v[4 * q + (1 ^ X)] = bf16_hi(t.x);
+        v[4 * q + (2 ^ X)] = bf16_lo(t.y); v[4 * q + (3 ^ X)] = bf16_hi(t.y);
     }
 }
-// N elements one by one.
-template <int N>
-__device__ __forceinline__ void read_packet_scalar(const float *pk, int off, float (&v)[N])
+// Cells c0 .. c0+N-1 of a packet row one by one (chunk order as above).
+template <int N, bool REV = false>
+__device__ __forceinline__ void read_packet_scalar(const float *pk, int off, int c0, float (&v)[N])
 {
 #pragma unroll
-    for (int c = 0; c < N; ++c) v[c] = pk[off + c];
+    for (int c = 0; c < N; ++c) v[c] = pk[off + (REV ? ((c0 + c) ^ 3) : (c0 + c))];
 }
-template <int N>
-__device__ __forceinline__ void read_packet_scalar(const uint16_t *pk, int off, float (&v)[N])
+template <int N, bool REV = false>
+__device__ __forceinline__ void read_packet_scalar(const uint16_t *pk, int off, int c0, float (&v)[N])
 {
 #pragma unroll
-    for (int c = 0; c < N; ++c) v[c] = __uint_as_float(static_cast<unsigned>(pk[off + c]) << 16);
+    for (int c = 0; c < N; ++c)
+        v[c] = __uint_as_float(static_cast<unsigned>(pk[off + (REV ? ((c0 + c) ^ 3) : (c0 + c))]) << 16);
 }
 
 __device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
 __device__ __forceinline__ unsigned bf16_bits(float v);
 __device__ __forceinline__ void store_elem(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
+
+// y += v with a returnless hardware atomic: nothing waits for it, and each cell
+// has one writer per call, so the sum is y + v rounded once (for bf16: v is
+// rounded to bf16 first, then the sum; the other half of the 32-bit word gets
+// -0, which leaves every value, -0 included, unchanged).
+__device__ __forceinline__ void add_elem(float *p, float v) { (void)unsafeAtomicAdd(p, v); }
+__device__ __forceinline__ void add_elem(uint16_t *p, float v)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const unsigned h = bf16_bits(v);
+    const unsigned w = (a & 2u) ? ((h << 16) | 0x8000u) : (h | 0x80000000u);
+    __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<__attribute__((address_space(1))) bf16x2 *>(a & ~uintptr_t{3}),
+                                               __builtin_bit_cast(bf16x2, w));
+}
 
 __device__ __forceinline__ float perm_sum32(float a, float b)
 {
@@ -251,7 +272,7 @@ __device__ __forceinline__ unsigned row_word(unsigned w, int r) { return __float
 // output type first (bf16 cells packed in pairs where a lane holds two), then
 // collected, in column order, in the channel's lane of row 0 (lane < 64 / G),
 // which stores them as whole chunks: K floats, or K bf16 values.
-template <int K, int G>
+template <int K, int G, bool REV = false>
 __device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
 {
     constexpr int KO = (K / G) > 0 ? K / G : 1;
@@ -277,12 +298,18 @@ __device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0
         }
     }
     if (storer) {
+        // REV: the strip's columns run right to left in memory
 #pragma unroll
-        for (int q = 0; q < K / 4; ++q)
-            *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(cells[4 * q], cells[4 * q + 1], cells[4 * q + 2], cells[4 * q + 3]);
+        for (int q = 0; q < K / 4; ++q) {
+            if constexpr (REV)
+                *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(cells[K - 1 - 4 * q], cells[K - 2 - 4 * q],
+                                                                     cells[K - 3 - 4 * q], cells[K - 4 - 4 * q]);
+            else
+                *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(cells[4 * q], cells[4 * q + 1], cells[4 * q + 2], cells[4 * q + 3]);
+        }
     }
 }
-template <int K, int G>
+template <int K, int G, bool REV = false>
 __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
 {
     constexpr int KO = (K / G) > 0 ? K / G : 1;
@@ -311,6 +338,14 @@ __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) 
             const unsigned t = row_word(h, r);
             words[r] = t | (__float_as_uint(row_ror8(__uint_as_float(t))) << 16);
         }
+    }
+    if constexpr (REV) {
+        // columns right to left in memory: word order reversed, halves swapped
+        unsigned t[K / 2];
+#pragma unroll
+        for (int c = 0; c < K / 2; ++c) t[c] = (words[K / 2 - 1 - c] >> 16) | (words[K / 2 - 1 - c] << 16);
+#pragma unroll
+        for (int c = 0; c < K / 2; ++c) words[c] = t[c];
     }
     if (storer) {
         if constexpr (K == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(words[0], words[1]);
@@ -373,10 +408,21 @@ template <int NPL, int G> constexpr int packet_rows() { return 2 * (kWave / G) +
 template <int NPL, int G> constexpr int passes_for(int K) { return (packet_rows<NPL, G>() * (K / 4) + kWave - 1) / kWave; }
 template <int NPL, int G> constexpr int prefetch_rows(int K) { return passes_for<NPL, G>(K) == 1 ? 4 : 2; }
 
-template <typename T, int K, int NPL, int ALIGN, int G, bool COOP>
+// MODE bits (fixed at compile time): kModeFlipW scans rows right to left,
+// kModeVFirst runs the column recurrence before the row recurrence,
+// kModeAccumulate adds the result to y instead of storing it.
+constexpr int kModeFlipW = 1;
+constexpr int kModeVFirst = 2;
+constexpr int kModeAccumulate = 4;
+
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kernel(Params p)
 {
     static_assert(K % 4 == 0, "strip width must be a multiple of 4");
+    constexpr bool FW = (MODE & kModeFlipW) != 0;
+    constexpr bool VF = (MODE & kModeVFirst) != 0;
+    constexpr bool ACC = (MODE & kModeAccumulate) != 0;
+    static_assert(!(COOP && FW), "cooperative loads keep columns in memory order");
     using Chunk = typename ChunkOf<T>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
     constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
@@ -534,6 +580,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
         const int d = dblk * CPW + dl;
         const bool d_ok = d < p.d_inner;
         const long HW = static_cast<long>(H) * W;
+        // Rows in scan order: the map's rows top to bottom, or bottom to top.
+        // Row t of the scan sits at row0 + t * rs.
+        const int rs = p.flip_h ? -W : W;  // |W| <= 65535
+        const long row0 = p.flip_h ? HW - W : 0;
         const T *zeros = static_cast<const T *>(p.zeros);
         // Two packet buffers of PASSES x 64 chunks (chunks past NCHUNK are
         // padding, so every lane stores its chunk without a mask): row i is
@@ -553,6 +603,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
 
         // Chunk sources of this lane: packet row r, chunk q of that row, split
         // into 4/ALIGN sub-loads; a sub-load past the row end reads the zero page.
+        // Scanning right to left, cell u of the scan is memory column W-1-u:
+        // a chunk of cells u..u+3 is loaded as memory columns W-4-u..W-1-u,
+        // in memory order (the packet reads reverse it).
         constexpr int NSUB = 4 / ALIGN;
         const T *src[PASSES][NSUB];
         int wpos[PASSES];  // ring-row chunk this lane's share chunk goes to
@@ -588,8 +641,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             }
 #pragma unroll
             for (int e = 0; e < NSUB; ++e) {
-                const int col = jc + 4 * q + e * ALIGN;
-                src[pp][e] = ((col + ALIGN <= W) ? base : zeros) + col;
+                if constexpr (FW) {
+                    const int col = W - jc - 4 * q - 4 + e * ALIGN;
+                    src[pp][e] = (col >= 0 ? base + col : zeros) + row0;
+                } else {
+                    const int col = jc + 4 * q + e * ALIGN;
+                    src[pp][e] = ((col + ALIGN <= W) ? base : zeros) + col + row0;
+                }
             }
         }
 
@@ -614,20 +672,22 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
         // Output cells of this lane; cells outside the map go to the sink.
         // The pointers advance one row per processed row.
         T *ydst[KO];
-        int ystep[KO];
+        long ystep[KO];
 #pragma unroll
         for (int c = 0; c < KO; ++c) {
             const bool ok = d_ok && storer && (c_out + c < valid);
-            ydst[c] = ok ? static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + d) * HW + j0 + c_out + c
+            const int u = j0 + c_out + c;  // column in scan order
+            ydst[c] = ok ? static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + d) * HW + row0 + (FW ? W - 1 - u : u)
                          : static_cast<T *>(p.sink) + lane * KO + c;
-            ystep[c] = ok ? W : 0;
+            ystep[c] = ok ? rs : 0;
         }
         // Whole-strip stores: with 4-aligned rows and a full strip, each
         // channel's cells are gathered into one lane of row 0 and stored as
-        // chunks; other strips store cell by cell.
-        const bool vec_store = (ALIGN == 4) && (valid == K) && p.vec_store;
+        // chunks; other strips, and accumulating calls, store cell by cell.
+        const bool vec_store = !ACC && (ALIGN == 4) && (valid == K) && p.vec_store;
         const bool vec_lane = (lane < CPW) && d_ok;
-        T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + j0;
+        T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + row0 +
+                  (FW ? W - j0 - K : j0);
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -697,15 +757,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 const int v = lds_peek(&s_arrive[t & slot_mask]);
                 signal_fence();
                 const T *pk = row_base(t);
-                read_packet<K>(pk, off_x, o.xv);
-                read_packet<K>(pk, off_dt, o.dv);
+                read_packet<K, FW>(pk, off_x, o.xv);
+                read_packet<K, FW>(pk, off_dt, o.dv);
                 return v;
             } else {
                 T *pk = row_base(t);
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp) reinterpret_cast<Chunk *>(pk)[pp * kWave + lane] = cb[pp];
-                read_packet<K>(pk, off_x, o.xv);
-                read_packet<K>(pk, off_dt, o.dv);
+                read_packet<K, FW>(pk, off_x, o.xv);
+                read_packet<K, FW>(pk, off_dt, o.dv);
                 return 0;
             }
         };
@@ -715,8 +775,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 if (__builtin_amdgcn_readfirstlane(seen_count) < need && !timed_out) {
                     wait_count(&s_arrive[t & slot_mask], need);
                     const T *pk = row_base(t);
-                    read_packet<K>(pk, off_x, o.xv);
-                    read_packet<K>(pk, off_dt, o.dv);
+                    read_packet<K, FW>(pk, off_x, o.xv);
+                    read_packet<K, FW>(pk, off_dt, o.dv);
                 }
             }
         };
@@ -736,11 +796,11 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 const T *pk = row_base(i);
                 float Bv[NPL][K], Cv[NPL][K], xo[KO];
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) read_packet<K>(pk, off_b[k], Bv[k]);
+                for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_b[k], Bv[k]);
                 const int next_count = stage(nb, i + 1, on);
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) read_packet<K>(pk, off_c[k], Cv[k]);
-                read_packet_scalar<KO>(pk, off_x + c_out, xo);
+                for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_c[k], Cv[k]);
+                read_packet_scalar<KO, FW>(pk, off_x, c_out, xo);
 
                 // ---- left carry of row i: the counter and the ring slot are
                 // read together (LDS executes a wave's accesses in order, and
@@ -769,6 +829,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                         av[c][k] = __builtin_amdgcn_exp2f(o.dv[c] * Ap[k]);
                         bx[c][k] = dx * Bv[k][c];
                     }
+                }
+                // Column recurrence first (vertical-first order): it needs no
+                // carry, so it joins the carry-independent work, and the row
+                // recurrence below runs over its results.
+                if constexpr (VF) {
+#pragma unroll
+                    for (int c = 0; c < K; ++c)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) bx[c][k] = hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], bx[c][k]);
                 }
                 // Pin that work here, ahead of the wait below: left to itself
                 // the compiler sinks it past the wait, onto the carry's
@@ -841,15 +910,20 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
 
-                // ---- vertical recurrence and the sum over this lane's states
+                // ---- vertical recurrence (unless it ran first) and the sum
+                // over this lane's states
                 float part[K];
 #pragma unroll
                 for (int c = 0; c < K; ++c) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) {
-                        hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
-                        acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                        if constexpr (VF) {
+                            acc = __builtin_fmaf(Cv[k][c], hc[c][k], acc);
+                        } else {
+                            hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
+                            acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                        }
                     }
                     part[c] = acc;
                 }
@@ -859,9 +933,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 reduce_groups<K, G>(part, out, g);
 #pragma unroll
                 for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
-                if (vec_store) {
-                    store_row<K, G>(yvec, out, vec_lane);
-                    yvec += W;
+                if constexpr (ACC) {
+#pragma unroll
+                    for (int c = 0; c < KO; ++c) {
+                        add_elem(ydst[c], out[c]);
+                        ydst[c] += ystep[c];
+                    }
+                } else if (vec_store) {
+                    store_row<K, G, FW>(yvec, out, vec_lane);
+                    yvec += rs;
                 } else {
 #pragma unroll
                     for (int c = 0; c < KO; ++c) {
@@ -886,7 +966,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 for (int s = 0; s < P; ++s)
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s + (COOP ? XA : 0), H - 1)) * W);
+                        buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s + (COOP ? XA : 0), H - 1)) * rs);
             };
             if constexpr (COOP) {
                 // shares of rows 0 .. XA-1; row XA's comes from bufA[0] below
@@ -894,7 +974,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     Chunk c0[PASSES];
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        c0[pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(t, H - 1)) * W);
+                        c0[pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(t, H - 1)) * rs);
                     T *slot = row_base(t);
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
@@ -956,6 +1036,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
 struct Plan {
     int G, K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
     int coop_slots;  // rows of the shared row ring with cooperative loads, 0 = per-wave packets
+    int mode;        // kModeFlipW | kModeVFirst | kModeAccumulate
+    int flip_h;      // rows bottom to top
 };
 
 int env_int(const char *name, int dflt);
@@ -991,12 +1073,12 @@ size_t lds_bytes(const Plan &pl)
 
 // Global ring depth: bounded (with back-pressure) only if the whole grid is
 // co-resident, so that a producer never waits on a consumer that cannot run.
-template <typename T, int K, int NPL, int ALIGN, int G, bool COOP>
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 int choose_qg(const Plan &pl, int dev, int H)
 {
     if (pl.groups <= 1) return H;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP>, block_threads(pl),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE>, block_threads(pl),
                                                      lds_bytes<T, K, NPL, G>(pl)) != hipSuccess) {
         (void)hipGetLastError();
         return H;
@@ -1007,15 +1089,17 @@ int choose_qg(const Plan &pl, int dev, int H)
     return H;
 }
 
-template <typename T, int K, int NPL, int ALIGN, int G, bool COOP>
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 int run(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
         int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
 {
     if (!COOP) pl.coop_slots = 0;
-    pl.qg = choose_qg<T, K, NPL, ALIGN, G, COOP>(pl, dev, H);
+    pl.qg = choose_qg<T, K, NPL, ALIGN, G, COOP, MODE>(pl, dev, H);
     const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
     const size_t gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
-    const size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
+    // zero page: whole rows of any input type, and a zero D (no skip term)
+    size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
+    if (zero_bytes < static_cast<size_t>(d_inner) * 4 + 64) zero_bytes = static_cast<size_t>(d_inner) * 4 + 64;
     WsEntry *e = nullptr;
     int st = get_ws(dev, stream, gring_bytes, zero_bytes, static_cast<size_t>(n_bound > 0 ? n_bound : 1), &e);
     if (st != SSM2D_OK) return st;
@@ -1026,7 +1110,7 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.x = x; prm.delta = delta;
     prm.B = d_state ? static_cast<const void *>(B) : e->zeros;
     prm.C = d_state ? static_cast<const void *>(C) : e->zeros;
-    prm.A = A; prm.D = D; prm.y = y; prm.zeros = e->zeros;
+    prm.A = A; prm.D = D ? D : static_cast<const float *>(e->zeros); prm.y = y; prm.zeros = e->zeros;
     prm.ticket = e->head; prm.done = e->head + 1; prm.err = e->head + 2;
     prm.sink = reinterpret_cast<char *>(e->head) + kHeadBytes;
     prm.cons = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(e->head) + kHeadBytes + kSinkBytes);
@@ -1038,15 +1122,34 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     prm.epoch = e->epoch;
     prm.vec_store = env_int("SSM2D_VECSTORE", 1);
+    prm.flip_h = pl.flip_h;
     prm.coop_slots = pl.coop_slots > 0 ? pl.coop_slots : 2;
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;
     prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
     const size_t lds = lds_bytes<T, K, NPL, G>(pl);
-    scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
+    scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
                                    static_cast<hipStream_t>(stream)>>>(prm);
     const hipError_t err = hipGetLastError();
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
+}
+
+// Launch of a right-to-left, vertical-first and / or accumulating scan: 8 state groups,
+// 4-column strips, per-wave packets, align 4 or 1. Instantiated by one
+// translation unit per (input type, mode).
+template <typename T, int MODE>
+int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
+                  int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream, int align)
+{
+    if (pl.G != 8 || pl.K != 4 || pl.coop_slots != 0) return SSM2D_ERR_UNSUPPORTED;
+    const int al = align == 4 ? 4 : 1;
+#define SSM2D_MODE_CASE(NN, AL)    \
+    if (pl.npl == NN && al == AL) \
+        return run<T, 4, NN, AL, 8, false, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    SSM2D_MODE_CASE(1, 4) SSM2D_MODE_CASE(2, 4) SSM2D_MODE_CASE(4, 4) SSM2D_MODE_CASE(8, 4)
+    SSM2D_MODE_CASE(1, 1) SSM2D_MODE_CASE(2, 1) SSM2D_MODE_CASE(4, 1) SSM2D_MODE_CASE(8, 1)
+#undef SSM2D_MODE_CASE
+    return SSM2D_ERR_UNSUPPORTED;
 }
 
 // Launch for a plan: one translation unit per (input type, state-group
@@ -1058,6 +1161,19 @@ SSM2D_DISPATCH_DECL(float, dispatch_g4)
 SSM2D_DISPATCH_DECL(float, dispatch_g8)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g4)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
+// The other modes (8 state groups, 4-column strips, per-wave packets; align 2
+// is served by the align-1 kernels), one translation unit per (type, mode).
+#define SSM2D_MODE_DECLS(TT)                         \
+    SSM2D_DISPATCH_DECL(TT, dispatch_flipw)          \
+    SSM2D_DISPATCH_DECL(TT, dispatch_vfirst)         \
+    SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst)   \
+    SSM2D_DISPATCH_DECL(TT, dispatch_acc)            \
+    SSM2D_DISPATCH_DECL(TT, dispatch_flipw_acc)      \
+    SSM2D_DISPATCH_DECL(TT, dispatch_vfirst_acc)     \
+    SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst_acc)
+SSM2D_MODE_DECLS(float)
+SSM2D_MODE_DECLS(uint16_t)
+#undef SSM2D_MODE_DECLS
 #undef SSM2D_DISPATCH_DECL
 
 }  // namespace ssm2d_impl

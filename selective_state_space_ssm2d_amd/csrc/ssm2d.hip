@@ -1,7 +1,7 @@
 // libssm2d: 2DMamba 2D selective scan (forward) for MI355X / gfx950 -- host
 // side: argument checks, the work plan, per-stream workspaces and the C ABI
 // declared in include/ssm2d.h. The kernel is in scan2d_kernel.h; its instances
-// are compiled in scan2d_{f32,bf16}_{g4,g8}.hip.
+// are compiled in scan2d_{f32,bf16}_*.hip.
 #include "scan2d_kernel.h"
 
 namespace ssm2d_impl {
@@ -12,9 +12,10 @@ int env_int(const char *name, int dflt)
     return (s && *s) ? std::atoi(s) : dflt;
 }
 
-Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W)
+Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode)
 {
     Plan pl{};
+    pl.mode = mode;
     const int want_wg = 256;  // enough workgroups to cover the chip's CUs
     // Layout: 4 state groups per wave (16 channels) unless the map has more
     // than 4 states and too few (batch, channel-block) chains to give every CU
@@ -26,6 +27,7 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     int G = (d_state > 32 || (d_state > 4 && chains4 < want_wg)) ? 8 : 4;
     const int genv = env_int("SSM2D_GROUPS", 0);
     if (genv == 8 || (genv == 4 && d_state <= 32)) G = genv;
+    if (mode != 0) G = 8;  // the kernels of the other modes use 8 groups
     pl.G = G;
     int npl = 1;
     while (npl * G < d_state) npl *= 2;
@@ -37,13 +39,14 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     // stay in LDS), widening the strips to 8 columns if that makes the chain
     // fit. Otherwise chains are cut into groups of s_local strips linked by two
     // courier waves (so at most maxw - 2 strips per workgroup).
-    const bool wide_ok = npl <= 4 && W % 4 == 0;
+    const bool wide_ok = npl <= 4 && W % 4 == 0 && mode == 0;
     pl.K = 4;
     if (pl.n_chains >= want_wg && (W + 3) / 4 > max_waves(4, npl, G) && wide_ok &&
         (W + 7) / 8 <= max_waves(8, npl, G))
         pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
+    if (mode != 0) pl.K = 4;
     const int maxw = max_waves(pl.K, npl, G);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;
@@ -158,27 +161,14 @@ namespace {
 
 using namespace ssm2d_impl;
 
-bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }  // NULL passes
 
 template <typename T>
-int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
-             int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, void *stream)
+int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
+           int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream)
 {
-    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
-    if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
-    if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t{1} << 31) - 1;
-    if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim)
-        return SSM2D_ERR_UNSUPPORTED;
-    if (!x || !delta || !D || !y || (d_state > 0 && (!A || !B || !C))) return SSM2D_ERR_NULLPTR;
-    if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) ||
-        (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
-        return SSM2D_ERR_MISALIGNED;
-
-    Plan pl = make_plan(batch, d_inner, d_state, H, W);
-    int dev = 0;
-    SSM2D_HIP_TRY(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lock(g_mutex);
+    Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
+    pl.flip_h = flip_h;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
@@ -186,15 +176,69 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     // rows, when a workgroup holds part of a chain of a tall map (short maps
     // do not repay the ring's start-up), if the row ring fits.
     pl.coop_slots = 0;
-    if (pl.G == 8 && pl.K == 4 && align == 4 && pl.groups > 1 && H >= 128 && env_int("SSM2D_COOP", 1)) {
+    if (mode == 0 && pl.G == 8 && pl.K == 4 && align == 4 && pl.groups > 1 && H >= 128 && env_int("SSM2D_COOP", 1)) {
         using Chunk = typename ChunkOf<T>::type;
         const size_t nchunk = static_cast<size_t>(16 + 16 * pl.npl);
         const size_t rings = static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * pl.npl * 4;
         for (int slots = kMaxSlots; slots >= 8 && pl.coop_slots == 0; slots /= 2)
             if (static_cast<size_t>(pl.s_local) * slots * (nchunk + 1) * sizeof(Chunk) + rings <= 144 * 1024) pl.coop_slots = slots;
     }
-if (pl.G == 8) return dispatch_g8(x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align);
-    return dispatch_g4(x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align);
+#define SSM2D_ARGS x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align
+    constexpr int FW = kModeFlipW, VF = kModeVFirst, AC = kModeAccumulate;
+    switch (mode) {
+    case 0: return pl.G == 8 ? dispatch_g8(SSM2D_ARGS) : dispatch_g4(SSM2D_ARGS);
+    case FW: return dispatch_flipw(SSM2D_ARGS);
+    case VF: return dispatch_vfirst(SSM2D_ARGS);
+    case FW | VF: return dispatch_flipw_vfirst(SSM2D_ARGS);
+    case AC: return dispatch_acc(SSM2D_ARGS);
+    case FW | AC: return dispatch_flipw_acc(SSM2D_ARGS);
+    case VF | AC: return dispatch_vfirst_acc(SSM2D_ARGS);
+    case FW | VF | AC: return dispatch_flipw_vfirst_acc(SSM2D_ARGS);
+    default: return SSM2D_ERR_UNSUPPORTED;
+    }
+#undef SSM2D_ARGS
+}
+
+constexpr unsigned kKnownFlags = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST | SSM2D_ACCUMULATE | SSM2D_FOUR_WAY;
+
+// `extended`: the flag-taking entry points, where D may be NULL (no skip term).
+template <typename T>
+int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
+             int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
+             void *stream)
+{
+    if ((flags & ~kKnownFlags) != 0) return SSM2D_ERR_BAD_FLAGS;
+    if ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))) return SSM2D_ERR_BAD_FLAGS;
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
+    if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
+    if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t{1} << 31) - 1;
+    if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim)
+        return SSM2D_ERR_UNSUPPORTED;
+    if (!x || !delta || (!D && !extended) || !y || (d_state > 0 && (!A || !B || !C))) return SSM2D_ERR_NULLPTR;
+    if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) ||
+        (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
+        return SSM2D_ERR_MISALIGNED;
+
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(g_mutex);
+    const int vf = (flags & SSM2D_VERTICAL_FIRST) ? kModeVFirst : 0;
+    const int acc = (flags & SSM2D_ACCUMULATE) ? kModeAccumulate : 0;
+    if (!(flags & SSM2D_FOUR_WAY)) {
+        const int mode = ((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc;
+        return launch(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, mode, (flags & SSM2D_FLIP_H) ? 1 : 0,
+                      dev, stream);
+    }
+    // Four scans, one per starting corner, summed into y in stream order; the
+    // skip term is added once, by the first.
+    for (int q = 0; q < 4; ++q) {
+        const int mode = ((q & 2) ? kModeFlipW : 0) | vf | (q == 0 ? acc : kModeAccumulate);
+        const int st = launch(x, delta, A, B, C, q == 0 ? D : nullptr, y, batch, d_inner, d_state, H, W, mode,
+                              q & 1, dev, stream);
+        if (st != SSM2D_OK) return st;
+    }
+    return SSM2D_OK;
 }
 
 }  // namespace
@@ -205,14 +249,28 @@ int ssm2d_scan_fwd(const float *x, const float *delta, const float *A, const flo
                    const float *D, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
                    int64_t W, void *stream)
 {
-    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, stream);
+    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, 0u, false, stream);
 }
 
 int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
                         const uint16_t *C, const float *D, uint16_t *y, int64_t batch, int64_t d_inner,
                         int64_t d_state, int64_t H, int64_t W, void *stream)
 {
-    return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, stream);
+    return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, 0u, false, stream);
+}
+
+int ssm2d_scan_fwd_ex(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                      const float *D, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                      int64_t W, uint32_t flags, void *stream)
+{
+    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream);
+}
+
+int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
+                           const uint16_t *C, const float *D, uint16_t *y, int64_t batch, int64_t d_inner,
+                           int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+{
+    return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream);
 }
 
 const char *ssm2d_status_string(int status)
@@ -226,6 +284,7 @@ const char *ssm2d_status_string(int status)
     case SSM2D_ERR_HIP: return "HIP runtime error";
     case SSM2D_ERR_NOMEM: return "workspace allocation failed";
     case SSM2D_ERR_DEVICE_TIMEOUT: return "kernel timed out waiting for a neighbouring strip's carries";
+    case SSM2D_ERR_BAD_FLAGS: return "unknown flag bits, or SSM2D_FOUR_WAY with a flip flag";
     default: return "unknown status";
     }
 }
@@ -255,7 +314,7 @@ int ssm2d_set_spin_limit(int64_t polls)
     return SSM2D_OK;
 }
 
-int ssm2d_version(void) { return 200; }
+int ssm2d_version(void) { return 300; }
 
 const char *ssm2d_last_hip_error(void)
 {

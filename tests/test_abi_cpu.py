@@ -26,11 +26,11 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         text = lib.ssm2d_status_string(s)
         assert text and text != b"unknown status", s
     assert lib.ssm2d_status_string(99) == b"unknown status"
-    assert lib.ssm2d_version() >= 100
+    assert lib.ssm2d_version() >= 300
 
 
 FAKE = 0x10000  # never dereferenced: validation fails or returns first
@@ -80,6 +80,44 @@ def test_misaligned(lib):
         assert _call(lib, [1, 2, 3, 4, 5], ptrs) == pkg.ERR_MISALIGNED, k
 
 
+def _call_ex(lib, dims, flags, ptrs=None, bf16=False):
+    ptrs = ptrs if ptrs is not None else [FAKE] * 7
+    fn = lib.ssm2d_scan_fwd_ex_bf16 if bf16 else lib.ssm2d_scan_fwd_ex
+    return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_ex_flag_validation(lib, bf16):
+    # unknown bits, and a four-way sum with a flip, are refused before anything else
+    for flags in (32, 1 << 31, pkg.FOUR_WAY | pkg.FLIP_H, pkg.FOUR_WAY | pkg.FLIP_W):
+        assert _call_ex(lib, [1, 2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_FLAGS, flags
+        assert _call_ex(lib, [-1, 2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_FLAGS, flags
+    # valid flags reach the usual checks
+    for flags in range(32):
+        if flags & pkg.FOUR_WAY and flags & (pkg.FLIP_H | pkg.FLIP_W):
+            continue
+        assert _call_ex(lib, [1, -2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_DIM, flags
+        assert _call_ex(lib, [1, 2, 3, 0, 5], flags, ptrs=[0] * 7, bf16=bf16) == pkg.OK, flags
+        assert _call_ex(lib, [1, 2, 65, 4, 5], flags, bf16=bf16) == pkg.ERR_UNSUPPORTED, flags
+
+
+def test_ex_null_and_misaligned(lib):
+    # D may be NULL in the flag-taking entry points (no skip term) ...
+    ptrs = [FAKE] * 7
+    ptrs[5] = 0
+    assert _call_ex(lib, [1, 2, 3, 4, 5], 0, ptrs) not in (pkg.ERR_NULLPTR, pkg.ERR_MISALIGNED)
+    # ... but not in the plain one
+    assert _call(lib, [1, 2, 3, 4, 5], ptrs) == pkg.ERR_NULLPTR
+    for k in (0, 1, 2, 3, 4, 6):
+        ptrs = [FAKE] * 7
+        ptrs[k] = 0
+        assert _call_ex(lib, [1, 2, 3, 4, 5], pkg.FLIP_W, ptrs) == pkg.ERR_NULLPTR, k
+    for k in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[k] = FAKE + 8
+        assert _call_ex(lib, [1, 2, 3, 4, 5], pkg.VERTICAL_FIRST, ptrs) == pkg.ERR_MISALIGNED, k
+
+
 def test_python_binding_rejects_bad_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 3, 4)
@@ -91,3 +129,9 @@ def test_python_binding_rejects_bad_tensors():
         pkg.scan_fwd(x.double(), x.double(), A, B.double(), B.double(), D)
     with pytest.raises(ValueError):  # CPU tensors are refused: no host fallback
         pkg.scan_fwd(x, x, A, B, B, D)
+    with pytest.raises(ValueError):
+        pkg.scan_fwd_ex(x, x, A, B, B, None, flip_w=True)
+    with pytest.raises(ValueError):  # accumulating needs an output to add to
+        pkg.scan_fwd_ex(x, x, A, B, B, D, accumulate=True)
+    with pytest.raises(ValueError):  # the plain entry point needs D
+        pkg.scan_fwd(x, x, A, B, B, None)

@@ -372,6 +372,66 @@ def pin_order_closed_form(lib):
             _close(y[0, d], acc, 1e-12, f"closed form, lower-right corner, vf={vf}")
 
 
+def pin_flip_equivariance(lib):
+    """Scanning from another corner is scanning the mirrored map from the
+    upper-left corner and mirroring the result back."""
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 6, 7, 15)
+    for vf in (False, True):
+        for fh in (False, True):
+            for fw in (False, True):
+                ax = tuple(a for a, f in ((2, fh), (3, fw)) if f)
+                fl = (lambda a: np.ascontiguousarray(np.flip(a, ax))) if ax else (lambda a: a)
+                y = oracle.fwd(x, dt, A, B, C, D, lib=lib, flip_h=fh, flip_w=fw, vertical_first=vf)
+                ym = oracle.fwd(fl(x), fl(dt), A, fl(B), fl(C), D, lib=lib, vertical_first=vf)
+                _close(y, fl(ym), 1e-14, f"mirror, flips {fh},{fw} vf {vf}")
+
+
+def pin_vfirst_is_transposed_scan(lib):
+    """Column scan first, then row scan, is the horizontal-first scan of the
+    transposed map, transposed back (in every direction)."""
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 2, 3))
+    x, dt, A, B, C, D = _inputs(1, 3, 4, 5, 8, 20)
+    for fh in (False, True):
+        for fw in (False, True):
+            y = oracle.fwd(x, dt, A, B, C, D, lib=lib, flip_h=fh, flip_w=fw, vertical_first=True)
+            yt = oracle.fwd(tr(x), tr(dt), A, tr(B), tr(C), D, lib=lib, flip_h=fw, flip_w=fh)
+            _close(y, tr(yt), 1e-14, f"vertical-first as transpose, flips {fh},{fw}")
+
+
+def pin_four_way_no_decay(lib):
+    """Abar = 0 (delta*A far below the exp underflow): each scan keeps only
+    the cell's own input, so the four-corner sum is 4 C Bx + D x."""
+    x, dt, A, B, C, D = _inputs(1, 2, 3, 4, 5, 21)
+    A = np.full_like(A, -1e6)
+    for vf in (False, True):
+        y = oracle.fwd(x, dt, A, B, C, D, lib=lib, four_way=True, vertical_first=vf)
+        ref = D[None, :, None, None] * x + 4 * np.einsum("bnhw,bdhw->bdhw", C * B, dt * x)
+        _close(y, ref, 1e-14, f"four-way, no decay, vf={vf}")
+        y0 = oracle.fwd(x, dt, A, B, C, None, lib=lib, four_way=True, vertical_first=vf)
+        _close(y0, ref - D[None, :, None, None] * x, 1e-14, "four-way without skip term")
+
+
+def pin_four_way_closed_form(lib):
+    """Constant delta: the four-corner sum reaches every cell of the map with
+    decay Abar^(Manhattan distance); cells sharing the target's row or column
+    lie in two of the quadrants and the target itself in all four."""
+    H, W, N = 5, 6, 2
+    x, dt, A, B, C, D = _inputs(1, 2, N, H, W, 22, delta_mode="const")
+    y = oracle.fwd(x, dt, A, B, C, D, lib=lib, four_way=True)
+    for d in range(2):
+        acc = D[d] * x[0, d]
+        for n in range(N):
+            a = np.exp(dt[0, d, 0, 0] * A[d, n])
+            bx = dt[0, d] * B[0, n] * x[0, d]
+            h = np.zeros((H, W))
+            for i in range(H):
+                for j in range(W):
+                    h[i, j] = sum((1 + (ip == i)) * (1 + (jp == j)) * a ** (abs(ip - i) + abs(jp - j)) * bx[ip, jp]
+                                  for ip in range(H) for jp in range(W))
+            acc = acc + C[0, n] * h
+        _close(y[0, d], acc, 1e-12, "four-way closed form")
+
+
 ALL_PINS = [
     pin_closed_form_constant_delta,
     pin_worked_example_3x3,
@@ -387,6 +447,10 @@ ALL_PINS = [
     pin_directions_bruteforce,
     pin_directions_reduce_to_1d,
     pin_order_closed_form,
+    pin_flip_equivariance,
+    pin_vfirst_is_transposed_scan,
+    pin_four_way_no_decay,
+    pin_four_way_closed_form,
 ]
 
 
