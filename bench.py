@@ -3,7 +3,12 @@
 One step = one ssm2d_scan_fwd call over one batch of the workload (inputs
 resident in HBM). Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant V]
+
+--variant times another direction / order through ssm2d_scan_fwd_ex instead:
+flip_hw (from the lower-right corner), vfirst (vertical-first order), four_way
+(sum of the four corner scans: four launches per step, the last three adding
+into y), four_way_vfirst.
 
 Workload (default): the giga-pixel WSI grid, batch 1, d_inner 128, d_state 16,
 H x W = 384 x 512, fp32, 60 % blob-shaped pad cells. Inputs are seeded and
@@ -37,10 +42,27 @@ SLOTS_PER_ELEM_STATE = 7
 METRIC = "2D-scan elements/s (B·D·H·W) + % of MI355X peak HBM GB/s"
 
 
-def algorithmic_bytes(wl) -> int:
+def algorithmic_bytes(wl, accumulate=False) -> int:
+    """Compulsory HBM bytes of one launch: x, delta, B, C, A, D read, y written
+    (and read too, when the launch adds into y)."""
     s = 2 if wl.dtype == "bf16" else 4
     E = wl.elements
-    return E * 3 * s + wl.batch * wl.d_state * wl.H * wl.W * 2 * s + wl.d_inner * wl.d_state * 4 + wl.d_inner * 4
+    return (E * (4 if accumulate else 3) * s + wl.batch * wl.d_state * wl.H * wl.W * 2 * s
+            + wl.d_inner * wl.d_state * 4 + wl.d_inner * 4)
+
+
+# variant -> (ssm2d_scan_fwd_ex keywords, launches per step); None: ssm2d_scan_fwd
+VARIANTS = {
+    "fwd": (None, 1),
+    "flip_hw": (dict(flip_h=True, flip_w=True), 1),
+    "vfirst": (dict(vertical_first=True), 1),
+    "four_way": (dict(four_way=True), 4),
+    "four_way_vfirst": (dict(four_way=True, vertical_first=True), 4),
+}
+
+
+def _tag(workload: str, variant: str) -> str:
+    return workload if variant == "fwd" else f"{workload}_{variant}"
 
 
 KERNEL_SRC_DIR = os.path.join(ROOT, "selective_state_space_ssm2d_amd", "csrc")
@@ -84,10 +106,10 @@ def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str):
 
 
 def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
-                copy_mb: int) -> None:
+                copy_mb: int, variant: str = "fwd") -> None:
     """Turns four rocprofv3 --pmc runs (scan FETCH_SIZE, scan WRITE_SIZE, copy
     FETCH_SIZE, copy WRITE_SIZE; KiB per dispatch) into calibrated HBM bytes
-    per launch of the scan kernel: profiles/traffic_<workload>.json."""
+    per launch of the scan kernel: profiles/traffic_<workload>[_<variant>].json."""
     copy_bytes = copy_mb * 1024 * 1024
     cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy") * 1024.0
     cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy") * 1024.0
@@ -96,6 +118,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
     kf, kw = copy_bytes / cf, copy_bytes / cw
     rec = {
         "workload": workload,
+        "variant": variant,
         "kernel": "scan2d_fwd_kernel",
         "kernel_source_sha256_16": kernel_source_hash(),
         "copy_probe_bytes": copy_bytes,
@@ -105,13 +128,13 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
         "fetch_bytes_per_launch": sf * kf, "write_bytes_per_launch": sw * kw,
         "bytes_per_launch": sf * kf + sw * kw,
     }
-    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    out = os.path.join(ROOT, "profiles", f"traffic_{_tag(workload, variant)}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def cpu_baseline(wl, t, keys, seconds: float):
+def cpu_baseline(wl, t, keys, seconds: float, kw=None):
     """Times the oracle as it is (fp64, OpenMP over maps, all host threads) on
     a bounded sample of the workload's (b, d) maps: calls over consecutive maps
     (all of them per call if a pass is short) repeat until about `seconds` of
@@ -126,7 +149,7 @@ def cpu_baseline(wl, t, keys, seconds: float):
     ins = [np.ascontiguousarray(t[k], dtype=np.float64) for k in keys]  # the oracle's input type
     first = np.arange(min(threads, nmaps))
     c0 = time.perf_counter()
-    oracle.fwd(*ins, maps=first)
+    oracle.fwd(*ins, maps=first, **(kw or {}))
     t_first = max(time.perf_counter() - c0, 1e-6)
     per_map = t_first / first.size
     chunk = nmaps if per_map * nmaps <= seconds / 2 else max(first.size, int(seconds / 4 / per_map))
@@ -134,38 +157,40 @@ def cpu_baseline(wl, t, keys, seconds: float):
     c0 = time.perf_counter()
     while True:
         sel = (np.arange(chunk) + k) % nmaps
-        oracle.fwd(*ins, maps=sel)
+        oracle.fwd(*ins, maps=sel, **(kw or {}))
         done += sel.size
         k = (k + chunk) % nmaps
         cw = time.perf_counter() - c0
         if cw >= seconds:
             break
     n_el = done * wl.H * wl.W
+    what = "map scans" if not kw else f"map scans ({', '.join(sorted(kw))})"
     return {"value": n_el / cw, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} (b,d) map scans ({nmaps} maps in the workload) of {wl.name} "
+            "sample": f"{done} (b,d) {what} ({nmaps} maps in the workload) of {wl.name} "
                       f"({wl.H}x{wl.W}, d_state {wl.d_state}), fp64, {cw:.1f} s wall on {threads} threads"}
 
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
-             "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
+             "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline{v}")
 
 
-def trace_summary(workload: str, run_dir: str) -> None:
-    """Writes profiles/kernel_stats_<workload>.txt from the kernel statistics of
-    a rocprofv3 --kernel-trace --stats run of this benchmark."""
+def trace_summary(workload: str, run_dir: str, variant: str = "fwd") -> None:
+    """Writes profiles/kernel_stats_<workload>[_<variant>].txt from the kernel
+    statistics of a rocprofv3 --kernel-trace --stats run of this benchmark."""
     files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {run_dir}")
     rows = list(csv.DictReader(open(files[0])))
-    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
-             f"# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && {TRACE_CMD.format(w=workload)}",
+    vopt = "" if variant == "fwd" else f" --variant {variant}"
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}, variant {variant}",
+             f"# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && {TRACE_CMD.format(w=workload, v=vopt)}",
              f"# kernel source sha256[:16] {kernel_source_hash()}",
              "# name | calls | total ns | average ns | min ns | max ns | percent"]
     for r in rows:
         short = r["Name"].replace("(anonymous namespace)::", "").removeprefix("void ").split("(")[0][:110]
         lines.append(f"{short} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.1f} | "
                      f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
-    out = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+    out = os.path.join(ROOT, "profiles", f"kernel_stats_{_tag(workload, variant)}.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -177,6 +202,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gigapixel_wsi")
+    ap.add_argument("--variant", default="fwd", choices=sorted(VARIANTS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -188,10 +214,10 @@ def main():
                     help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.workload, args.trace_summary)
+        trace_summary(args.workload, args.trace_summary, args.variant)
         return
     if args.pmc_summary:
-        pmc_summary(args.workload, *args.pmc_summary, copy_mb=args.copy_mb)
+        pmc_summary(args.workload, *args.pmc_summary, copy_mb=args.copy_mb, variant=args.variant)
         return
     if args.copy_probe:
         copy_probe(args.copy_probe, max(1, args.steps))
@@ -225,15 +251,21 @@ def main():
                 out.append(torch.from_numpy(np.ascontiguousarray(t[k])).to(dev))
         return out
 
+    kw, launches = VARIANTS[args.variant]
     abytes = algorithmic_bytes(wl)
     ncopies = max(2, int(np.ceil(768e6 / abytes)))
     sets = [upload() for _ in range(ncopies)]
-    ys = [torch.empty_like(s[0]) for s in sets]
+    ys = [torch.zeros_like(s[0]) for s in sets]
+
+    def step(k):
+        if kw is None:
+            pkg.scan_fwd(*sets[k], y=ys[k])
+        else:
+            pkg.scan_fwd_ex(*sets[k], y=ys[k], **kw)
 
     stream = torch.cuda.current_stream()
     for w in range(args.warmup):
-        k = w % ncopies
-        pkg.scan_fwd(*sets[k], y=ys[k])
+        step(w % ncopies)
     pkg.sync_check()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -243,7 +275,7 @@ def main():
     for s in range(args.steps):
         k = s % ncopies
         starts[s].record(stream)
-        pkg.scan_fwd(*sets[k], y=ys[k])
+        step(k)
         ends[s].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -252,15 +284,16 @@ def main():
     ms_step = wall * 1e3 / args.steps
     E = wl.elements
     value = E / (ms_step * 1e-3)
-    kmean = float(np.mean(kern_ms))
-    gbs = abytes / (kmean * 1e-3) / 1e9
-    flops = E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
+    kmean = float(np.mean(kern_ms))        # one step: `launches` kernels back to back
+    step_bytes = abytes if launches == 1 else abytes + (launches - 1) * algorithmic_bytes(wl, accumulate=True)
+    gbs = step_bytes / (kmean * 1e-3) / 1e9
+    flops = launches * E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
     tflops = flops / (kmean * 1e-3) / 1e12
 
     # HBM bytes per launch from the committed counter summary, only while it
     # describes the kernel as it is now
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{_tag(wl.name, args.variant)}.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
@@ -269,7 +302,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, t, keys, args.cpu_seconds)
+        cpu = cpu_baseline(wl, t, keys, args.cpu_seconds, kw)
 
     rec = {
         "metric": METRIC,
@@ -286,13 +319,14 @@ def main():
         "data": "synthetic (seeded; shapes and pad structure of the workload, no dataset)",
         "config": {"workload": wl.name, "batch": wl.batch, "d_inner": wl.d_inner, "d_state": wl.d_state,
                    "H": wl.H, "W": wl.W, "pad": wl.pad, "pad_cells": wl.pad_cells,
-                   "input_copies_cycled": ncopies},
+                   "input_copies_cycled": ncopies, "variant": args.variant, "launches_per_step": launches},
         "roofline": {"bound": "alu", "achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
-                     "kernel": "scan2d_fwd_kernel", "kernel_ms_mean": kmean,
-                     "kernel_ms_median": float(np.median(kern_ms)), "kernel_ms_min": float(np.min(kern_ms))},
+                     "kernel": "scan2d_fwd_kernel", "kernel_ms_mean": kmean / launches,
+                     "kernel_ms_median": float(np.median(kern_ms)) / launches,
+                     "kernel_ms_min": float(np.min(kern_ms)) / launches},
         "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "algorithmic_bytes": abytes},
+                "algorithmic_bytes": step_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

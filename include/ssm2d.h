@@ -112,11 +112,9 @@ int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
  * above; 0 gives ssm2d_scan_fwd). Arguments, layout, ownership, asynchrony and
  * errors as for ssm2d_scan_fwd, and also:
  *   D may be NULL: no skip term (as D = 0).
- *   SSM2D_ACCUMULATE reads y: y must hold valid values. The additions are
- *     returnless hardware atomics, one per cell and call, so the result is
- *     y + result rounded once (fp32), deterministic for calls on one stream;
- *     fp32 denormal sums may be flushed to zero.
- *   bf16: y + bf16(result), rounded to bf16 (two roundings).
+ *   SSM2D_ACCUMULATE reads y: y must hold valid values. Each cell of y is
+ *     read and rewritten by one thread, so the result is y + result computed
+ *     in fp32 and rounded once to y's type; deterministic.
  *   SSM2D_FOUR_WAY enqueues four kernels on `stream`, the last three
  *     accumulating; with SSM2D_ACCUMULATE the first accumulates too.
  *   Unknown bits, or SSM2D_FOUR_WAY with SSM2D_FLIP_H or SSM2D_FLIP_W

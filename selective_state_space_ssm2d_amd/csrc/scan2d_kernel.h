@@ -178,20 +178,8 @@ __device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
 __device__ __forceinline__ unsigned bf16_bits(float v);
 __device__ __forceinline__ void store_elem(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
 
-// y += v with a returnless hardware atomic: nothing waits for it, and each cell
-// has one writer per call, so the sum is y + v rounded once (for bf16: v is
-// rounded to bf16 first, then the sum; the other half of the 32-bit word gets
-// -0, which leaves every value, -0 included, unchanged).
-__device__ __forceinline__ void add_elem(float *p, float v) { (void)unsafeAtomicAdd(p, v); }
-__device__ __forceinline__ void add_elem(uint16_t *p, float v)
-{
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const unsigned h = bf16_bits(v);
-    const unsigned w = (a & 2u) ? ((h << 16) | 0x8000u) : (h | 0x80000000u);
-    __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<__attribute__((address_space(1))) bf16x2 *>(a & ~uintptr_t{3}),
-                                               __builtin_bit_cast(bf16x2, w));
-}
+__device__ __forceinline__ float elem_value(float v) { return v; }
+__device__ __forceinline__ float elem_value(uint16_t v) { return __uint_as_float(static_cast<unsigned>(v) << 16); }
 
 __device__ __forceinline__ float perm_sum32(float a, float b)
 {
@@ -681,6 +669,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                          : static_cast<T *>(p.sink) + lane * KO + c;
             ystep[c] = ok ? rs : 0;
         }
+        T *ybase[KO];  // row 0 of the scan (accumulating calls read y there)
+#pragma unroll
+        for (int c = 0; c < KO; ++c) ybase[c] = ydst[c];
         // Whole-strip stores: with 4-aligned rows and a full strip, each
         // channel's cells are gathered into one lane of row 0 and stored as
         // chunks; other strips, and accumulating calls, store cell by cell.
@@ -792,7 +783,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             // Row i from packet buffer i % 2 and operands `o`; row i+1's
             // packet `nb` is staged (and its x, delta read into `on`) first,
             // so that LDS traffic overlaps this row's arithmetic.
-            auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on) {
+            auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on, const T (&yo)[KO]) {
                 const T *pk = row_base(i);
                 float Bv[NPL][K], Cv[NPL][K], xo[KO];
 #pragma unroll
@@ -934,9 +925,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
 #pragma unroll
                 for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
                 if constexpr (ACC) {
+                    // y of this row was read with the row's inputs
 #pragma unroll
                     for (int c = 0; c < KO; ++c) {
-                        add_elem(ydst[c], out[c]);
+                        store_elem(ydst[c], elem_value(yo[c]) + out[c]);
                         ydst[c] += ystep[c];
                     }
                 } else if (vec_store) {
@@ -959,14 +951,23 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             // register-resident state at every row); the last, partial block
             // runs guarded. Rows past the map's end are never computed; their
             // loads read the last row again.
+            // Accumulating into y: each row's y cells are read with its inputs
+            // (yoA / yoB, loaded with bufA / bufB), added to the result and
+            // written back by the same lane, so no other wave touches them.
             Chunk bufA[P][PASSES], bufB[P][PASSES];
+            T yoA[P][KO], yoB[P][KO];
             Ops ops[2];
-            auto load_rows = [&](Chunk (&buf)[P][PASSES], const int first) {
+            auto load_rows = [&](Chunk (&buf)[P][PASSES], T (&yo)[P][KO], const int first) {
 #pragma unroll
-                for (int s = 0; s < P; ++s)
+                for (int s = 0; s < P; ++s) {
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
                         buf[s][pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(first + s + (COOP ? XA : 0), H - 1)) * rs);
+                    if constexpr (ACC) {
+#pragma unroll
+                        for (int c = 0; c < KO; ++c) yo[s][c] = ybase[c][static_cast<long>(min(first + s, H - 1)) * ystep[c]];
+                    }
+                }
             };
             if constexpr (COOP) {
                 // shares of rows 0 .. XA-1; row XA's comes from bufA[0] below
@@ -985,28 +986,28 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     signal_fence();
                 }
             }
-            load_rows(bufA, 0);
-            load_rows(bufB, P);
+            load_rows(bufA, yoA, 0);
+            load_rows(bufB, yoB, P);
             confirm(0, stage(bufA[0], 0, ops[0]), ops[0]);
             int i0 = 0;
             for (; i0 + 2 * P <= H; i0 += 2 * P) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2]);
-                load_rows(bufA, i0 + 2 * P);
+                    do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s]);
+                load_rows(bufA, yoA, i0 + 2 * P);
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2]);
-                load_rows(bufB, i0 + 3 * P);
+                    do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2], yoB[s]);
+                load_rows(bufB, yoB, i0 + 3 * P);
             }
             if (i0 < H) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    if (i0 + s < H) do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2]);
+                    if (i0 + s < H) do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s]);
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     if (i0 + P + s < H)
-                        do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2]);
+                        do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2], yoB[s]);
             }
         };
         if (has_left) {

@@ -106,11 +106,11 @@ def test_accumulate(shape, dtype, kw):
 
 
 def check_sum(got, ref, terms, dtype, what):
-    """bf16 multi-direction sums: y is rounded to bf16 after each of the four
-    scans (each result is rounded to bf16, then the running sum), so the
-    rounding error scales with the terms' magnitudes, not the sum's: the bar
-    is taken relative to 1 + sum_k |y_k| (y_k: the per-scan results, the skip
-    term counted with the first)."""
+    """bf16 multi-direction sums: the running sum in y is rounded to bf16
+    after each of the four scans, so the rounding error scales with the
+    partial sums, bounded by the terms' magnitudes, not with the final sum:
+    the bar is taken relative to 1 + sum_k |y_k| (y_k: the per-scan results,
+    the skip term counted with the first)."""
     if dtype != "bf16":
         return check(got, ref, dtype, what)
     scale = 1.0 + sum(np.abs(t) for t in terms)
