@@ -15,6 +15,7 @@ fwd(x, delta, A, B, C, D, maps=None, nthreads=0, flip_h=False, flip_w=False,
     vertical_first=False, four_way=False) -> y (float64)
 states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
                         the recurrences alone on given Abar, Bx (one map)
+bwd(x, delta, A, B, C, D, dy) -> dict of dx, ddelta, dA, dB, dC, dD (float64)
 max_threads()           OpenMP thread count the oracle uses by default
 """
 from __future__ import annotations
@@ -55,6 +56,8 @@ def load(path: str = LIB_PATH):
     lib.oracle_ssm2d_fwd_ex_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_states_ex_f64.argtypes = [dp, dp, dp, i64, i64, ctypes.c_int]
     lib.oracle_ssm2d_states_ex_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_bwd_f64.argtypes = [dp] * 13 + [i64] * 5 + [ctypes.c_int]
+    lib.oracle_ssm2d_bwd_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -147,6 +150,26 @@ def states(abar, bx, lib=None, flip_h=False, flip_w=False, vertical_first=False)
     if s != 0:
         raise RuntimeError(f"oracle failed with status {s}")
     return h
+
+
+def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None):
+    """Gradients of the forward pass (fp64) for upstream gradient dy (shape of
+    y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input."""
+    lib = lib or _get()
+    x, delta, A, B, C, D, dy = map(_f64, (x, delta, A, B, C, D, dy))
+    batch, d_inner, H, W = x.shape
+    d_state = A.shape[1]
+    assert delta.shape == x.shape and dy.shape == x.shape
+    assert A.shape == (d_inner, d_state) and D.shape == (d_inner,)
+    assert B.shape == (batch, d_state, H, W) and C.shape == B.shape
+    out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty_like(A),
+           "dB": np.empty_like(B), "dC": np.empty_like(C), "dD": np.empty_like(D)}
+    s = lib.oracle_ssm2d_bwd_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+                                 *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")),
+                                 batch, d_inner, d_state, H, W, int(nthreads))
+    if s != 0:
+        raise RuntimeError(f"oracle failed with status {s}")
+    return out
 
 
 def max_threads(lib=None) -> int:

@@ -1,5 +1,5 @@
 /*
- * fp64 CPU oracle for the 2DMamba 2D selective scan (forward).
+ * fp64 CPU oracle for the 2DMamba 2D selective scan (forward and backward).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
@@ -229,6 +229,144 @@ int oracle_ssm2d_fwd_ex_f64(const double *x, const double *delta, const double *
     if (flags < 0 || flags > 7) return 2;
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
                     nthreads, flags);
+}
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Gradients of a scalar loss L through the forward pass above, given
+ * dy = dL/dy. The pages describe training but not the backward pass; this is
+ * reverse-mode differentiation of the forward steps, taken in reverse order,
+ * in fp64 (pinned against finite differences of the forward pass). Per
+ * (b, d, n) map, with a = Abar, u = Bx:
+ *
+ *   y  <- h  : g_h[i,j]  = dy[i,j] C[i,j] + a[i+1,j] g_h[i+1,j]   (h[i,j] also feeds h[i+1,j])
+ *   h  <- hh : g_hh[i,j] = g_h[i,j] + a[i,j+1] g_hh[i,j+1]        (hh[i,j] also feeds hh[i,j+1])
+ *   a        : g_a[i,j]  = g_hh[i,j] hh[i,j-1] + g_h[i,j] h[i-1,j]
+ *   u        : g_u[i,j]  = g_hh[i,j]
+ *   a = exp(delta A), u = delta B x:
+ *     d delta += g_a A a + g_u B x      dA[d,n] += g_a delta a
+ *     dB[b,n] += g_u delta x            dx      += g_u delta B
+ *     dC[b,n] += dy h
+ *   skip term: dx += dy D[d],  dD[d] += dy x
+ * (terms with index -1 or beyond the map are zero). */
+static void backward_one_map(const double *xm, const double *dm, double a_dn, const double *Bn,
+                             const double *Cn, const double *dym, double *dxm, double *ddm,
+                             double *dBn, double *dCn, double *dA_dn, int64_t H, int64_t W,
+                             double *a, double *u, double *hh, double *h, double *gh, double *ghh)
+{
+    const int64_t L = H * W;
+    for (int64_t p = 0; p < L; ++p) {
+        a[p] = exp(dm[p] * a_dn);
+        u[p] = dm[p] * Bn[p] * xm[p];
+    }
+    /* forward states, kept whole */
+    for (int64_t i = 0; i < H; ++i) {
+        for (int64_t j = 0; j < W; ++j) {
+            const double left = (j > 0) ? hh[i * W + j - 1] : 0.0;
+            hh[i * W + j] = a[i * W + j] * left + u[i * W + j];
+        }
+        for (int64_t j = 0; j < W; ++j) {
+            const double up = (i > 0) ? h[(i - 1) * W + j] : 0.0;
+            h[i * W + j] = a[i * W + j] * up + hh[i * W + j];
+        }
+    }
+    /* adjoint of the vertical scan: bottom to top */
+    for (int64_t i = H - 1; i >= 0; --i)
+        for (int64_t j = 0; j < W; ++j) {
+            const double below = (i + 1 < H) ? a[(i + 1) * W + j] * gh[(i + 1) * W + j] : 0.0;
+            gh[i * W + j] = dym[i * W + j] * Cn[i * W + j] + below;
+        }
+    /* adjoint of the horizontal scan: right to left along each row */
+    for (int64_t i = 0; i < H; ++i)
+        for (int64_t j = W - 1; j >= 0; --j) {
+            const double right = (j + 1 < W) ? a[i * W + j + 1] * ghh[i * W + j + 1] : 0.0;
+            ghh[i * W + j] = gh[i * W + j] + right;
+        }
+    /* local derivatives */
+    double dA_sum = 0.0;
+    for (int64_t i = 0; i < H; ++i)
+        for (int64_t j = 0; j < W; ++j) {
+            const int64_t p = i * W + j;
+            const double left = (j > 0) ? hh[p - 1] : 0.0;
+            const double up = (i > 0) ? h[p - W] : 0.0;
+            const double g_a = ghh[p] * left + gh[p] * up;
+            const double g_u = ghh[p];
+            ddm[p] += g_a * a_dn * a[p] + g_u * Bn[p] * xm[p];
+            dA_sum += g_a * dm[p] * a[p];
+            dBn[p] += g_u * dm[p] * xm[p];
+            dxm[p] += g_u * dm[p] * Bn[p];
+            dCn[p] += dym[p] * h[p];
+        }
+    *dA_dn += dA_sum;
+}
+
+/* Internal entry: gradients of the forward pass. Inputs as for the forward
+ * (x, delta, dy: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
+ * [batch][d_state][H][W]; D: [d_inner]); outputs dx, ddelta, dA, dB, dC, dD
+ * of the same shapes, overwritten. OpenMP over batch entries; the per-entry
+ * dA and dD parts are added in batch order, so results do not depend on the
+ * thread count. Returns 0, 2 on a bad size, 6 on allocation failure. */
+int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, const double *B,
+                         const double *C, const double *D, const double *dy, double *dx,
+                         double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                         int nthreads)
+{
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
+    const int64_t L = H * W;
+    memset(dx, 0, (size_t)(batch * d_inner * L) * sizeof(double));
+    memset(ddelta, 0, (size_t)(batch * d_inner * L) * sizeof(double));
+    memset(dA, 0, (size_t)(d_inner * d_state) * sizeof(double));
+    memset(dB, 0, (size_t)(batch * d_state * L) * sizeof(double));
+    memset(dC, 0, (size_t)(batch * d_state * L) * sizeof(double));
+    memset(dD, 0, (size_t)d_inner * sizeof(double));
+    if (batch == 0 || d_inner == 0 || L == 0) return 0;
+    /* per batch entry: dA and dD parts, added in order at the end */
+    double *dA_b = (double *)calloc((size_t)(batch * d_inner * d_state) + 1, sizeof(double));
+    double *dD_b = (double *)calloc((size_t)(batch * d_inner) + 1, sizeof(double));
+    if (!dA_b || !dD_b) {
+        free(dA_b); free(dD_b);
+        return 6;
+    }
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t b = 0; b < batch; ++b) {
+        double *buf = (double *)malloc((size_t)(6 * L) * sizeof(double));
+        if (!buf) {
+#pragma omp atomic write
+            status = 6;
+            continue;
+        }
+        for (int64_t d = 0; d < d_inner; ++d) {
+            const int64_t m = (b * d_inner + d) * L;
+            for (int64_t n = 0; n < d_state; ++n) {
+                const int64_t q = (b * d_state + n) * L;
+                backward_one_map(x + m, delta + m, A[d * d_state + n], B + q, C + q, dy + m,
+                                 dx + m, ddelta + m, dB + q, dC + q,
+                                 dA_b + (b * d_inner + d) * d_state + n, H, W,
+                                 buf, buf + L, buf + 2 * L, buf + 3 * L, buf + 4 * L, buf + 5 * L);
+            }
+            double s = 0.0;
+            for (int64_t p = 0; p < L; ++p) {
+                dx[m + p] += dy[m + p] * D[d];
+                s += dy[m + p] * x[m + p];
+            }
+            dD_b[b * d_inner + d] = s;
+        }
+        free(buf);
+    }
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < d_inner; ++d) {
+            dD[d] += dD_b[b * d_inner + d];
+            for (int64_t n = 0; n < d_state; ++n)
+                dA[d * d_state + n] += dA_b[(b * d_inner + d) * d_state + n];
+        }
+    free(dA_b);
+    free(dD_b);
+    return status;
 }
 
 /* Number of threads the OpenMP runtime would use (1 without OpenMP). */

@@ -1,0 +1,141 @@
+"""Pins for the oracle's backward pass (gradients of the forward scan).
+
+The pages describe training of the models built on the scan but not its
+backward pass; the oracle's backward is reverse-mode differentiation of its
+forward. It is pinned here against things that do not share its derivation:
+central finite differences of the (separately pinned) forward pass, the
+closed form with no decay (Abar = 0), and the skip-only case (d_state = 0).
+A mutation check plants mistakes in the adjoint recurrences and the local
+derivatives and checks that some pin fails for each.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_ssm2d_amd.inputs import make_random_inputs
+
+KEYS = ("x", "delta", "A", "B", "C", "D")
+GRAD = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD"}
+
+
+def _inputs(b, d, n, H, W, seed, **kw):
+    t = make_random_inputs(b, d, n, H, W, seed=seed, **kw)
+    return {k: t[k].astype(np.float64) for k in KEYS}
+
+
+def _loss(ins, dy, lib):
+    y = oracle.fwd(*(ins[k] for k in KEYS), lib=lib)
+    return float(np.sum(y * dy))
+
+
+def pin_finite_differences(lib):
+    """Every gradient element against a central difference of
+    L = sum(dy * y) computed with the forward pass (step 1e-6, relative)."""
+    for shape, seed in (((2, 3, 3, 4, 5), 31), ((1, 2, 2, 1, 6), 32), ((1, 2, 3, 5, 1), 33)):
+        ins = _inputs(*shape, seed)
+        dy = np.random.default_rng(seed).standard_normal(ins["x"].shape)
+        g = oracle.bwd(*(ins[k] for k in KEYS), dy, lib=lib)
+        for k in KEYS:
+            base = ins[k]
+            fd = np.empty_like(base)
+            for idx in np.ndindex(base.shape):
+                h = 1e-6 * max(1.0, abs(base[idx]))
+                orig = base[idx]
+                base[idx] = orig + h
+                lp = _loss(ins, dy, lib)
+                base[idx] = orig - h
+                lm = _loss(ins, dy, lib)
+                base[idx] = orig
+                fd[idx] = (lp - lm) / (2 * h)
+            err = np.max(np.abs(g[GRAD[k]] - fd) / (1.0 + np.abs(fd)))
+            assert err < 1e-6, f"{GRAD[k]} vs finite differences {shape}: {err:.2e}"
+
+
+def pin_no_decay_closed_form(lib):
+    """Abar = 0 (delta*A far below the exp underflow): y = sum_n C delta B x
+    + D x, whose gradients are written out directly; dA = 0 since the decay
+    and its derivative vanish."""
+    ins = _inputs(2, 3, 4, 3, 5, 34)
+    ins["A"] = np.full_like(ins["A"], -1e6)
+    dy = np.random.default_rng(34).standard_normal(ins["x"].shape)
+    x, dt, B, C, D = ins["x"], ins["delta"], ins["B"], ins["C"], ins["D"]
+    g = oracle.bwd(*(ins[k] for k in KEYS), dy, lib=lib)
+    CB = np.einsum("bnhw,bnhw->bhw", C, B)[:, None]
+    ref = {
+        "dx": dy * (dt * CB + D[None, :, None, None]),
+        "ddelta": dy * x * CB,
+        "dB": np.einsum("bdhw,bnhw->bnhw", dy * dt * x, C),
+        "dC": np.einsum("bdhw,bnhw->bnhw", dy * dt * x, B),
+        "dD": np.einsum("bdhw,bdhw->d", dy, x),
+        "dA": np.zeros_like(ins["A"]),
+    }
+    for k, v in ref.items():
+        err = np.max(np.abs(g[k] - v) / (1.0 + np.abs(v)))
+        assert err < 1e-13, f"{k}, no decay: {err:.2e}"
+
+
+def pin_skip_only(lib):
+    """d_state = 0: y = D x, so dx = dy D, dD = sum dy x, ddelta = 0."""
+    ins = _inputs(2, 3, 0, 4, 6, 35)
+    dy = np.random.default_rng(35).standard_normal(ins["x"].shape)
+    g = oracle.bwd(*(ins[k] for k in KEYS), dy, lib=lib)
+    assert np.allclose(g["dx"], dy * ins["D"][None, :, None, None], rtol=0, atol=1e-15)
+    assert np.allclose(g["dD"], np.einsum("bdhw,bdhw->d", dy, ins["x"]), rtol=1e-14, atol=1e-14)
+    assert np.all(g["ddelta"] == 0)
+    assert g["dA"].size == 0 and g["dB"].size == 0 and g["dC"].size == 0
+
+
+BWD_PINS = [pin_finite_differences, pin_no_decay_closed_form, pin_skip_only]
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda f: f.__name__)
+def test_bwd_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+def test_bwd_thread_count_does_not_change_results(oracle_lib):
+    ins = _inputs(3, 4, 5, 6, 7, 36)
+    dy = np.random.default_rng(36).standard_normal(ins["x"].shape)
+    g1 = oracle.bwd(*(ins[k] for k in KEYS), dy, nthreads=1)
+    g3 = oracle.bwd(*(ins[k] for k in KEYS), dy, nthreads=3)
+    for k in g1:
+        assert np.array_equal(g1[k], g3[k]), k
+
+
+BWD_MUTANTS = {
+    "vertical adjoint uses Abar of its own row":
+        ("a[(i + 1) * W + j] * gh[(i + 1) * W + j]", "a[i * W + j] * gh[(i + 1) * W + j]"),
+    "horizontal adjoint drops the vertical adjoint":
+        ("ghh[i * W + j] = gh[i * W + j] + right;", "ghh[i * W + j] = right;"),
+    "decay derivative misses the vertical path":
+        ("const double g_a = ghh[p] * left + gh[p] * up;", "const double g_a = ghh[p] * left;"),
+    "dA misses the factor Abar":
+        ("dA_sum += g_a * dm[p] * a[p];", "dA_sum += g_a * dm[p];"),
+    "dB without delta":
+        ("dBn[p] += g_u * dm[p] * xm[p];", "dBn[p] += g_u * xm[p];"),
+    "dC from the horizontal state":
+        ("dCn[p] += dym[p] * h[p];", "dCn[p] += dym[p] * hh[p];"),
+    "dx skip term dropped":
+        ("dx[m + p] += dy[m + p] * D[d];", "(void)D;"),
+    "ddelta misses the input path":
+        ("ddm[p] += g_a * a_dn * a[p] + g_u * Bn[p] * xm[p];", "ddm[p] += g_a * a_dn * a[p];"),
+}
+
+
+def test_bwd_pins_catch_planted_mistakes(tmp_path):
+    with open(oracle._SRC) as f:
+        src = f.read()
+    for name, (old, new) in BWD_MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site missing or ambiguous: {name}"
+        path = tmp_path / (str(abs(hash(name))) + ".c")
+        path.write_text(src.replace(old, new))
+        lib_path = str(tmp_path / (str(abs(hash(name))) + ".so"))
+        oracle.build(out_path=lib_path, src_path=str(path))
+        lib = oracle.load(lib_path)
+        caught = []
+        for pin in BWD_PINS:
+            try:
+                pin(lib)
+            except (AssertionError, RuntimeError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin caught the planted mistake: {name}"
