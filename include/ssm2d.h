@@ -56,6 +56,7 @@ extern "C" {
 #endif
 
 #define SSM2D_MAX_STATE 64
+#define SSM2D_MAX_STATE_BWD 32
 #define SSM2D_MAX_SIDE 65535
 
 typedef enum {
@@ -131,6 +132,49 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
                            const uint16_t *B, const uint16_t *C, const float *D, uint16_t *y,
                            int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
                            uint32_t flags, void *stream);
+
+/* ---- Backward pass -------------------------------------------------------
+ *
+ * Gradients of a scalar loss through ssm2d_scan_fwd, given dy = dL/dy. The
+ * pages train models built on the scan but do not describe its backward pass;
+ * this is the plain derivative of the forward above. Per (b, d, n), with
+ * a = Abar, u = Bx, and terms outside the map zero:
+ *
+ *   g_h[i,j]  = dy[b,d,i,j] C[b,n,i,j] + a[i+1,j] g_h[i+1,j]   (bottom to top)
+ *   g_hh[i,j] = g_h[i,j] + a[i,j+1] g_hh[i,j+1]                 (right to left)
+ *   g_a       = g_hh[i,j] hh[i,j-1] + g_h[i,j] h[i-1,j]
+ *   ddelta = sum_n (g_a A a + g_hh B x)      dx = sum_n g_hh delta B + dy D
+ *   dA[d,n] = sum_{b,i,j} g_a delta a        dB[b,n] = sum_d g_hh delta x
+ *   dC[b,n] = sum_d dy h                     dD[d] = sum_{b,i,j} dy x
+ *
+ * Inputs x, delta, A, B, C, D as for ssm2d_scan_fwd; dy like y. Outputs (all
+ * overwritten, none may alias an input or another output): dx, ddelta like x;
+ * dA like A; dB, dC like B; dD like D. Device pointers, 16-byte aligned.
+ * Three kernels are enqueued on `stream`: the forward again, storing every
+ * state h; the adjoint scans with the local derivatives; the sums of dB and
+ * dC over channel blocks. The library keeps a workspace per (device, stream)
+ * of 4 * batch * d_inner * d_state * H * ld + 8 * ceil(d_inner / 8) * batch *
+ * d_state * H * ld bytes, ld = W rounded up to a multiple of 4 (grown when
+ * needed, kept until the process ends). dA and dD are accumulated with
+ * atomics, so their last bits may differ from run to run; every other output
+ * is deterministic.
+ * Errors as for ssm2d_scan_fwd (with d_state == 0, A, B, C, dA, dB and dC
+ * are not touched and may be NULL), plus: d_state > SSM2D_MAX_STATE_BWD ->
+ * SSM2D_ERR_UNSUPPORTED. d_inner == 0: nothing to do. batch, H or W == 0:
+ * dA and dD are zeroed, nothing else is touched. */
+int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B,
+                   const float *C, const float *D, const float *dy, float *dx, float *ddelta,
+                   float *dA, float *dB, float *dC, float *dD, int64_t batch, int64_t d_inner,
+                   int64_t d_state, int64_t H, int64_t W, void *stream);
+
+/* bf16 backward: x, delta, B, C, dy, dx, ddelta, dB, dC are bfloat16 (raw
+ * uint16 bits, outputs rounded to nearest even); A, D, dA, dD float32; the
+ * stored states and all arithmetic fp32. */
+int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                        const uint16_t *B, const uint16_t *C, const float *D, const uint16_t *dy,
+                        uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB, uint16_t *dC,
+                        float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                        int64_t W, void *stream);
 
 /* Static description of a status code. Never NULL. */
 const char *ssm2d_status_string(int status);

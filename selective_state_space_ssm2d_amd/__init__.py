@@ -9,6 +9,7 @@ streams only. There is no fallback: if the library is missing the call fails.
     y = scan_fwd(x, delta, A, B, C, D)
     y = scan_fwd_ex(x, delta, A, B, C, D, flip_h=..., flip_w=..., vertical_first=...,
                     accumulate=..., four_way=...)
+    g = scan_bwd(x, delta, A, B, C, D, dy)   # dict: dx, ddelta, dA, dB, dC, dD
 
 x, delta: [batch, d_inner, H, W]; B, C: [batch, d_state, H, W]; all four
 float32 or all four bfloat16. A: [d_inner, d_state] float32; D: [d_inner]
@@ -23,7 +24,7 @@ import os
 import re
 
 __all__ = [
-    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "status_string",
+    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_bwd", "status_string",
     "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
 ]
 
@@ -56,6 +57,10 @@ def load_library(path: str = LIB_PATH):
     for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
+        f.restype = ctypes.c_int
+    for name in ("ssm2d_scan_bwd", "ssm2d_scan_bwd_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 13 + [i64] * 5 + [vp]
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_fwd_ex", "ssm2d_scan_fwd_ex_bf16"):
         f = getattr(lib, name)
@@ -192,3 +197,30 @@ def scan_fwd_ex(x, delta, A, B, C, D=None, y=None, *, flip_h=False, flip_w=False
     fn = lib.ssm2d_scan_fwd_ex if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_ex_bf16
     _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, y)] + [*dims, int(flags), _stream_handle(stream)])
     return y
+
+
+def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None):
+    """Gradients of the forward scan for upstream gradient dy (include/ssm2d.h,
+    ssm2d_scan_bwd). Returns a dict dx, ddelta, dA, dB, dC, dD; ``out`` may
+    supply any of them (shapes and dtypes as the inputs they belong to)."""
+    import torch
+
+    lib = load_library()
+    _check(x, delta, A, B, C, D, None, need_d=True)
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
+        raise ValueError("dy must match x in shape, dtype and device, and be contiguous")
+    batch, d_inner, H, W = x.shape
+    d_state = B.shape[1]
+    like = {"dx": x, "ddelta": delta, "dA": A, "dB": B, "dC": C, "dD": D}
+    g = {}
+    for k, ref in like.items():
+        t = (out or {}).get(k)
+        if t is None:
+            t = torch.empty_like(ref)
+        elif t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+            raise ValueError(f"{k} must match its input in shape, dtype and device, and be contiguous")
+        g[k] = t
+    fn = lib.ssm2d_scan_bwd if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_bf16
+    args = [_ptr(t) for t in (x, delta, A, B, C, D, dy)] + [_ptr(g[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")]
+    _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, _stream_handle(stream)])
+    return g

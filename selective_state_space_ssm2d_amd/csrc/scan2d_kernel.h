@@ -42,6 +42,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
@@ -57,9 +58,27 @@ namespace ssm2d_impl {
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + couriers)
+
+// Kernel modes (bits, fixed at compile time):
+//   kModeFlipW       rows are scanned right to left
+//   kModeVFirst      the column recurrence runs before the row recurrence
+//   kModeAccumulate  the result is added to y instead of stored
+//   kModeStates      forward pass that writes every state h and no y
+//   kModeBackward    adjoint pass of the backward (with kModeFlipW and rows
+//                    bottom to top): gradients from the stored states
+constexpr int kModeFlipW = 1;
+constexpr int kModeVFirst = 2;
+constexpr int kModeAccumulate = 4;
+constexpr int kModeStates = 8;
+constexpr int kModeBackward = 16;
+
 // Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
-// small (8 state groups, K * NPL <= 16), else 8, which leaves a wave 256 VGPRs.
-constexpr int max_waves(int K, int NPL, int G) { return (G == 8 && K * NPL <= 16) ? 10 : 8; }
+// small (8 state groups, K * NPL <= 16, not the backward passes), else 8,
+// which leaves a wave 256 VGPRs.
+constexpr int max_waves(int K, int NPL, int G, int MODE = 0)
+{
+    return (G == 8 && K * NPL <= 16 && !(MODE & (kModeBackward | kModeStates))) ? 10 : 8;
+}
 constexpr int kCourierBatch = 4;               // rows a courier requests per poll
 constexpr int kMaxSlots = 16;                   // rows of a workgroup's shared row ring
 constexpr int kSpinPolls = 64;                  // polls of an LDS counter before sleeping between polls
@@ -84,6 +103,16 @@ struct Params {
     int coop_slots;                    // rows in the workgroup's shared row ring (cooperative loads)
     int coop_shift;                    // log2 of coop_slots
     int flip_h;                        // rows in scan order run bottom to top
+    // stored states (kModeStates writes, kModeBackward reads): fp32
+    // [batch][d_inner][d_state][H][ld], cell (i, j) at i * ld + pad + j
+    float *states;
+    int states_ld, states_pad;
+    // backward: upstream gradient, outputs, per-channel-block partial sums of
+    // dB and dC ([n_dblk][batch][d_state][H][ld], padded like the states)
+    const void *dy;
+    void *ddelta;                      // dx goes to y
+    float *dBp, *dCp, *dA, *dD;
+    long part_stride;                  // elements per channel block of dBp / dCp
     unsigned int epoch;
     long long spin_limit;
 };
@@ -201,6 +230,21 @@ __device__ __forceinline__ float perm_sum16(float a, float b)
 __device__ __forceinline__ float row_ror8(float v)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+// Sum over the 8 lanes of an aligned group of 8 (the 8 channels that share a
+// state group in the 8-group layout); every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    return v;
+}
+
+__device__ __forceinline__ float chunk_elem(const float4 &v, int m)
+{
+    return m == 0 ? v.x : (m == 1 ? v.y : (m == 2 ? v.z : v.w));
 }
 
 // Sum over the G state groups of a wave. Lane l holds partial sums p[0..K) of
@@ -392,34 +436,37 @@ __device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long 
 }
 
 // Packet rows of a wave: x and delta of 64/G channels, B and C of G*NPL states.
-template <int NPL, int G> constexpr int packet_rows() { return 2 * (kWave / G) + 2 * G * NPL; }
-template <int NPL, int G> constexpr int passes_for(int K) { return (packet_rows<NPL, G>() * (K / 4) + kWave - 1) / kWave; }
-template <int NPL, int G> constexpr int prefetch_rows(int K) { return passes_for<NPL, G>(K) == 1 ? 4 : 2; }
+// The backward's packet also carries dy (64/G more rows).
+template <int NPL, int G, int MODE = 0>
+constexpr int packet_rows() { return 2 * (kWave / G) + 2 * G * NPL + ((MODE & kModeBackward) ? kWave / G : 0); }
+template <int NPL, int G, int MODE = 0>
+constexpr int passes_for(int K) { return (packet_rows<NPL, G, MODE>() * (K / 4) + kWave - 1) / kWave; }
+template <int NPL, int G, int MODE = 0>
+constexpr int prefetch_rows(int K) { return (passes_for<NPL, G, MODE>(K) == 1 && !(MODE & kModeBackward)) ? 4 : 2; }
 
-// MODE bits (fixed at compile time): kModeFlipW scans rows right to left,
-// kModeVFirst runs the column recurrence before the row recurrence,
-// kModeAccumulate adds the result to y instead of storing it.
-constexpr int kModeFlipW = 1;
-constexpr int kModeVFirst = 2;
-constexpr int kModeAccumulate = 4;
 
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
-__global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kernel(Params p)
+__global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd_kernel(Params p)
 {
     static_assert(K % 4 == 0, "strip width must be a multiple of 4");
     constexpr bool FW = (MODE & kModeFlipW) != 0;
     constexpr bool VF = (MODE & kModeVFirst) != 0;
     constexpr bool ACC = (MODE & kModeAccumulate) != 0;
+    constexpr bool STATES = (MODE & kModeStates) != 0;
+    constexpr bool BWD = (MODE & kModeBackward) != 0;
+    static_assert(!BWD || (FW && !VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
+    static_assert(!STATES || (!FW && !VF && !ACC && !COOP), "stored states: forward order only");
     static_assert(!(COOP && FW), "cooperative loads keep columns in memory order");
     using Chunk = typename ChunkOf<T>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
     constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
     constexpr int SEG_X = 0, SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
-    constexpr int SEGROWS = packet_rows<NPL, G>();    // packet rows of K elements
+    constexpr int SEG_DY = SEG_C + G * NPL;           // backward only
+    constexpr int SEGROWS = packet_rows<NPL, G, MODE>();  // packet rows of K elements
     constexpr int CPR = K / 4;                        // chunks per packet row
     constexpr int NCHUNK = SEGROWS * CPR;
-    constexpr int PASSES = passes_for<NPL, G>(K);
-    constexpr int P = prefetch_rows<NPL, G>(K);       // rows per prefetch buffer
+    constexpr int PASSES = passes_for<NPL, G, MODE>(K);
+    constexpr int P = prefetch_rows<NPL, G, MODE>(K);  // rows per prefetch buffer
 
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_done[kMaxWaves + 1];   // rows published into LDS ring b
@@ -622,9 +669,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 } else if (r < SEG_C) {
                     const int n = r - SEG_B;
                     if (n < p.d_state) base = static_cast<const T *>(p.B) + (static_cast<long>(b) * p.d_state + n) * HW;
-                } else {
+                } else if (r < SEG_DY) {
                     const int n = r - SEG_C;
                     if (n < p.d_state) base = static_cast<const T *>(p.C) + (static_cast<long>(b) * p.d_state + n) * HW;
+                } else {
+                    const int dd = dblk * CPW + r - SEG_DY;
+                    if (dd < p.d_inner) base = static_cast<const T *>(p.dy) + (static_cast<long>(b) * p.d_inner + dd) * HW;
                 }
             }
 #pragma unroll
@@ -653,6 +703,51 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
 #pragma unroll
         for (int k = 0; k < NPL; ++k) asm volatile("" ::"v"(Ap[k]));
         asm volatile("" ::"v"(Dd));
+        // Backward: A itself (d delta takes g_a A Abar).
+        float At[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) At[k] = 0.0f;
+        if constexpr (BWD) {
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) {
+                const int n = g * NPL + k;
+                At[k] = (n < p.d_state && d_ok) ? p.A[d * p.d_state + n] : 0.0f;
+                asm volatile("" ::"v"(At[k]));
+            }
+        }
+        // Stored states of this lane's NPL states (row-major, padded rows of
+        // states_ld with the map starting at column states_pad, so that a
+        // right-to-left strip's 4 cells are one aligned chunk). The forward
+        // writes its strip's cells of each row; the backward reads, for scan
+        // row t, the chunk of memory row H-1-t (rows past the map read zeros).
+        // Partial sums of dB and dC have the same layout per channel block.
+        const int sld = p.states_ld;
+        float *hdst[NPL];
+        const float *hsrc[NPL];
+        float *pdb[NPL], *pdc[NPL];
+        bool hok[NPL];
+        long hstep[NPL];
+        const float *zeros_f = static_cast<const float *>(p.zeros);
+        if constexpr (STATES || BWD) {
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) {
+                const int n = g * NPL + k;
+                hok[k] = d_ok && n < p.d_state;
+                const long map = (static_cast<long>(b) * p.d_inner + d) * p.d_state + n;
+                float *base = p.states + map * H * sld + p.states_pad;
+                if constexpr (STATES) {
+                    hdst[k] = hok[k] ? base + j0 : nullptr;
+                } else {
+                    hsrc[k] = hok[k] ? base + static_cast<long>(H - 1) * sld + (W - j0 - 4) : zeros_f;
+                    hstep[k] = hok[k] ? -static_cast<long>(sld) : 0;
+                    const long part = dblk * p.part_stride + ((static_cast<long>(b) * p.d_state + (n < p.d_state ? n : 0)) * H + (H - 1)) * sld +
+                                      p.states_pad + (W - j0 - 4);
+                    pdb[k] = p.dBp + part;
+                    pdc[k] = p.dCp + part;
+                }
+            }
+        }
+        const bool part_lane = (dl == 0);  // stores the channel-block sums of its state group
         // First of this lane's finished cells (for G = 8 and K = 4 the two
         // lanes of a pair hold the same cell and the odd one does not store).
         const int c_out = (K >= G) ? g * KO : g / 2;
@@ -679,6 +774,18 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
         const bool vec_lane = (lane < CPW) && d_ok;
         T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + row0 +
                   (FW ? W - j0 - K : j0);
+        // Backward: d delta goes where dx goes, in its own tensor.
+        T *ddst[KO];
+        T *dvec = yvec;
+        if constexpr (BWD) {
+#pragma unroll
+            for (int c = 0; c < KO; ++c)
+                ddst[c] = (ystep[c] != 0) ? static_cast<T *>(p.ddelta) + (ydst[c] - static_cast<T *>(p.y)) : ydst[c];
+            dvec = static_cast<T *>(p.ddelta) + (yvec - static_cast<T *>(p.y));
+        }
+        float dAacc[NPL], dDacc = 0.0f;  // backward: this lane's parts of dA and dD
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) dAacc[k] = 0.0f;
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -699,7 +806,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             else return packets + (t % 2) * PASSES * kWave * 4;
         };
         auto roff = [&](const int r) { return COOP ? wave * (NCHUNK + 1) * 4 + r * K : r * K; };
-        const int off_x = roff(SEG_X + dl), off_dt = roff(SEG_DT + dl);
+        const int off_x = roff(SEG_X + dl), off_dt = roff(SEG_DT + dl), off_dy = roff(SEG_DY + dl);
         int off_b[NPL], off_c[NPL];
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
@@ -783,15 +890,20 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             // Row i from packet buffer i % 2 and operands `o`; row i+1's
             // packet `nb` is staged (and its x, delta read into `on`) first,
             // so that LDS traffic overlaps this row's arithmetic.
-            auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on, const T (&yo)[KO]) {
+            auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on, const T (&yo)[KO],
+                              const float4 (&hcur)[NPL], const float4 (&hnext)[NPL]) {
                 const T *pk = row_base(i);
-                float Bv[NPL][K], Cv[NPL][K], xo[KO];
+                float Bv[NPL][K], Cv[NPL][K], xo[KO], dyv[K], dyo[KO];
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_b[k], Bv[k]);
                 const int next_count = stage(nb, i + 1, on);
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_c[k], Cv[k]);
                 read_packet_scalar<KO, FW>(pk, off_x, c_out, xo);
+                if constexpr (BWD) {
+                    read_packet<K, FW>(pk, off_dy, dyv);
+                    read_packet_scalar<KO, FW>(pk, off_dy, c_out, dyo);
+                }
 
                 // ---- left carry of row i: the counter and the ring slot are
                 // read together (LDS executes a wave's accesses in order, and
@@ -829,6 +941,21 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     for (int c = 0; c < K; ++c)
 #pragma unroll
                         for (int k = 0; k < NPL; ++k) bx[c][k] = hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], bx[c][k]);
+                }
+                // Backward: the adjoint of the vertical scan runs first and
+                // needs no carry: g_h = dy C + (Abar g_h) of the row below,
+                // kept pre-multiplied in hv. The carried adjoint of the row
+                // scan then adds Abar g_hh of the cell to the right.
+                float gh[K][NPL];
+                if constexpr (BWD) {
+#pragma unroll
+                    for (int c = 0; c < K; ++c)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            gh[c][k] = __builtin_fmaf(dyv[c], Cv[k][c], hv[c][k]);
+                            hv[c][k] = av[c][k] * gh[c][k];
+                            asm volatile("" : "+v"(gh[c][k]), "+v"(hv[c][k]));
+                        }
                 }
                 // Pin that work here, ahead of the wait below: left to itself
                 // the compiler sinks it past the wait, onto the carry's
@@ -886,8 +1013,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 for (int c = 0; c < K; ++c)
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) {
-                        hh[k] = __builtin_fmaf(av[c][k], hh[k], bx[c][k]);
-                        hc[c][k] = hh[k];
+                        if constexpr (BWD) {
+                            // g_hh = g_h + carry; carry' = Abar g_hh = Abar g_h + Abar carry
+                            hc[c][k] = gh[c][k] + hh[k];
+                            hh[k] = __builtin_fmaf(av[c][k], hh[k], hv[c][k]);
+                        } else {
+                            hh[k] = __builtin_fmaf(av[c][k], hh[k], bx[c][k]);
+                            hc[c][k] = hh[k];
+                        }
                     }
                 if constexpr (RIGHT) {
                     float *dst = ring_out + (static_cast<long>(i & RM) * kWave + lane) * NPL;
@@ -901,44 +1034,120 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
 
-                // ---- vertical recurrence (unless it ran first) and the sum
-                // over this lane's states
-                float part[K];
+                if constexpr (BWD) {
+                    // ---- local derivatives. With hh = h - Abar h(row above)
+                    // and u = Bx, the decay's adjoint times Abar is
+                    // g_a Abar = g_hh (hh - u) + g_h (h - hh).
+                    float ddp[K], dxp[K], dBv[NPL][K], dCv[NPL][K];
 #pragma unroll
-                for (int c = 0; c < K; ++c) {
-                    float acc = 0.0f;
+                    for (int c = 0; c < K; ++c) {
+                        float sdd = 0.0f, sdx = 0.0f;
 #pragma unroll
-                    for (int k = 0; k < NPL; ++k) {
-                        if constexpr (VF) {
-                            acc = __builtin_fmaf(Cv[k][c], hc[c][k], acc);
-                        } else {
-                            hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
-                            acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                        for (int k = 0; k < NPL; ++k) {
+                            const float hcu = chunk_elem(hcur[k], 3 - c);   // chunks hold cells in memory order
+                            const float hab = chunk_elem(hnext[k], 3 - c);
+                            const float hhv = __builtin_fmaf(-av[c][k], hab, hcu);
+                            const float gaa = hc[c][k] * (hhv - bx[c][k]) + gh[c][k] * (hcu - hhv);
+                            const float gb = hc[c][k] * Bv[k][c];
+                            sdd = __builtin_fmaf(gaa, At[k], sdd);
+                            sdd = __builtin_fmaf(gb, o.xv[c], sdd);
+                            sdx = __builtin_fmaf(gb, o.dv[c], sdx);
+                            dBv[k][c] = hc[c][k] * (o.dv[c] * o.xv[c]);
+                            dCv[k][c] = dyv[c] * hcu;
+                            dAacc[k] = __builtin_fmaf(gaa, o.dv[c], dAacc[k]);
+                        }
+                        ddp[c] = sdd;
+                        dxp[c] = sdx;
+                        dDacc = __builtin_fmaf(dyv[c], o.xv[c], dDacc);
+                    }
+                    // sums over the state groups; dx takes the skip term's dy D
+                    float ddo[KO], dxo[KO];
+                    reduce_groups<K, G>(ddp, ddo, g);
+                    reduce_groups<K, G>(dxp, dxo, g);
+#pragma unroll
+                    for (int c = 0; c < KO; ++c) dxo[c] = __builtin_fmaf(Dd, dyo[c], dxo[c]);
+                    if (vec_store) {
+                        store_row<K, G, FW>(yvec, dxo, vec_lane);
+                        store_row<K, G, FW>(dvec, ddo, vec_lane);
+                        yvec += rs;
+                        dvec += rs;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < KO; ++c) {
+                            store_elem(ydst[c], dxo[c]);
+                            store_elem(ddst[c], ddo[c]);
+                            ydst[c] += ystep[c];
+                            ddst[c] += ystep[c];
                         }
                     }
-                    part[c] = acc;
-                }
-
-                // ---- sum over the state groups, skip term, store
-                float out[KO];
-                reduce_groups<K, G>(part, out, g);
+                    // dB and dC: sums over the wave's 8 channels of a state
+                    // group, one partial per channel block (summed later)
+                    const long prow = static_cast<long>(i) * sld;
 #pragma unroll
-                for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
-                if constexpr (ACC) {
-                    // y of this row was read with the row's inputs
+                    for (int k = 0; k < NPL; ++k) {
+                        float sb[K], sc[K];
 #pragma unroll
-                    for (int c = 0; c < KO; ++c) {
-                        store_elem(ydst[c], elem_value(yo[c]) + out[c]);
-                        ydst[c] += ystep[c];
+                        for (int c = 0; c < K; ++c) {
+                            sb[c] = sum8(dBv[k][c]);
+                            sc[c] = sum8(dCv[k][c]);
+                        }
+                        if (part_lane && hok[k]) {
+                            *reinterpret_cast<float4 *>(pdb[k] - prow) = make_float4(sb[3], sb[2], sb[1], sb[0]);
+                            *reinterpret_cast<float4 *>(pdc[k] - prow) = make_float4(sc[3], sc[2], sc[1], sc[0]);
+                        }
                     }
-                } else if (vec_store) {
-                    store_row<K, G, FW>(yvec, out, vec_lane);
-                    yvec += rs;
                 } else {
+                    // ---- vertical recurrence (unless it ran first) and the sum
+                    // over this lane's states
+                    float part[K];
 #pragma unroll
-                    for (int c = 0; c < KO; ++c) {
-                        store_elem(ydst[c], out[c]);
-                        ydst[c] += ystep[c];
+                    for (int c = 0; c < K; ++c) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            if constexpr (VF) {
+                                acc = __builtin_fmaf(Cv[k][c], hc[c][k], acc);
+                            } else {
+                                hv[c][k] = __builtin_fmaf(av[c][k], hv[c][k], hc[c][k]);
+                                acc = __builtin_fmaf(Cv[k][c], hv[c][k], acc);
+                            }
+                        }
+                        part[c] = acc;
+                    }
+
+                    if constexpr (STATES) {
+                        // every state of the strip's valid cells, this row
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k)
+                            if (hok[k]) {
+                                float *dst = hdst[k] + static_cast<long>(i) * sld;
+#pragma unroll
+                                for (int c = 0; c < K; ++c)
+                                    if (c < valid) dst[c] = hv[c][k];
+                            }
+                    } else {
+                        // ---- sum over the state groups, skip term, store
+                        float out[KO];
+                        reduce_groups<K, G>(part, out, g);
+#pragma unroll
+                        for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
+                        if constexpr (ACC) {
+                            // y of this row was read with the row's inputs
+#pragma unroll
+                            for (int c = 0; c < KO; ++c) {
+                                store_elem(ydst[c], elem_value(yo[c]) + out[c]);
+                                ydst[c] += ystep[c];
+                            }
+                        } else if (vec_store) {
+                            store_row<K, G, FW>(yvec, out, vec_lane);
+                            yvec += rs;
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < KO; ++c) {
+                                store_elem(ydst[c], out[c]);
+                                ydst[c] += ystep[c];
+                            }
+                        }
                     }
                 }
                 confirm(i + 1, next_count, on);
@@ -954,10 +1163,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
             // Accumulating into y: each row's y cells are read with its inputs
             // (yoA / yoB, loaded with bufA / bufB), added to the result and
             // written back by the same lane, so no other wave touches them.
+            // Backward: each row's stored states (hbA / hbB), read likewise;
+            // a row needs its own and the next scan row's.
             Chunk bufA[P][PASSES], bufB[P][PASSES];
             T yoA[P][KO], yoB[P][KO];
+            float4 hbA[P][NPL], hbB[P][NPL];
             Ops ops[2];
-            auto load_rows = [&](Chunk (&buf)[P][PASSES], T (&yo)[P][KO], const int first) {
+            auto load_rows = [&](Chunk (&buf)[P][PASSES], T (&yo)[P][KO], float4 (&hb)[P][NPL], const int first) {
 #pragma unroll
                 for (int s = 0; s < P; ++s) {
 #pragma unroll
@@ -966,6 +1178,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     if constexpr (ACC) {
 #pragma unroll
                         for (int c = 0; c < KO; ++c) yo[s][c] = ybase[c][static_cast<long>(min(first + s, H - 1)) * ystep[c]];
+                    }
+                    if constexpr (BWD) {
+                        const int t = first + s;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k)
+                            hb[s][k] = *reinterpret_cast<const float4 *>(t < H ? hsrc[k] + t * hstep[k] : zeros_f);
                     }
                 }
             };
@@ -986,28 +1204,34 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
                     signal_fence();
                 }
             }
-            load_rows(bufA, yoA, 0);
-            load_rows(bufB, yoB, P);
+            load_rows(bufA, yoA, hbA, 0);
+            load_rows(bufB, yoB, hbB, P);
             confirm(0, stage(bufA[0], 0, ops[0]), ops[0]);
             int i0 = 0;
             for (; i0 + 2 * P <= H; i0 += 2 * P) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s]);
-                load_rows(bufA, yoA, i0 + 2 * P);
+                    do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s], hbA[s],
+                           s + 1 < P ? hbA[s + 1] : hbB[0]);
+                load_rows(bufA, yoA, hbA, i0 + 2 * P);
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2], yoB[s]);
-                load_rows(bufB, yoB, i0 + 3 * P);
+                    do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2], yoB[s],
+                           hbB[s], s + 1 < P ? hbB[s + 1] : hbA[0]);
+                load_rows(bufB, yoB, hbB, i0 + 3 * P);
             }
             if (i0 < H) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
-                    if (i0 + s < H) do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s]);
+                    if (i0 + s < H)
+                        do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s], hbA[s],
+                               s + 1 < P ? hbA[s + 1] : hbB[0]);
+                // (the last slot here is never a map row: i0 + 2P > H)
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     if (i0 + P + s < H)
-                        do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2], yoB[s]);
+                        do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2], yoB[s],
+                               hbB[s], s + 1 < P ? hbB[s + 1] : hbB[s]);
             }
         };
         if (has_left) {
@@ -1016,6 +1240,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
         } else {
             if (has_right) strip_rows(std::false_type{}, std::true_type{});
             else strip_rows(std::false_type{}, std::false_type{});
+        }
+        if constexpr (BWD) {
+            // this strip's parts of dA (every state of the lane) and dD (one
+            // lane per channel)
+#pragma unroll
+            for (int k = 0; k < NPL; ++k)
+                if (hok[k]) (void)unsafeAtomicAdd(p.dA + d * p.d_state + g * NPL + k, dAacc[k]);
+            if (d_ok && g == 0) (void)unsafeAtomicAdd(p.dD + d, dDacc);
         }
         if (timed_out) atomicOr(p.err, 1u);
     }
@@ -1034,11 +1266,23 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G)) void scan2d_fwd_kerne
 
 // ---------------------------------------------------------------- host side
 
+// Buffers of the two backward passes (the stored states and the partial sums
+// of dB and dC live in a library workspace; the rest are the caller's).
+struct BwdArgs {
+    float *states;
+    int ld, pad;
+    const void *dy;
+    void *ddelta;
+    float *dBp, *dCp, *dA, *dD;
+    long part_stride;
+};
+
 struct Plan {
     int G, K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
     int coop_slots;  // rows of the shared row ring with cooperative loads, 0 = per-wave packets
-    int mode;        // kModeFlipW | kModeVFirst | kModeAccumulate
+    int mode;        // kMode* bits
     int flip_h;      // rows bottom to top
+    const BwdArgs *bw;  // stored-state and backward passes
 };
 
 int env_int(const char *name, int dflt);
@@ -1061,13 +1305,13 @@ int device_cus(int dev);
 
 inline int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 2 : 0)); }
 
-template <typename T, int K, int NPL, int G>
+template <typename T, int K, int NPL, int G, int MODE>
 size_t lds_bytes(const Plan &pl)
 {
     using Chunk = typename ChunkOf<T>::type;
-    const size_t nchunk = static_cast<size_t>(packet_rows<NPL, G>()) * (K / 4);
-    const size_t chunks = pl.coop_slots > 0 ? pl.coop_slots * (nchunk + 1)                            // ring rows
-                                            : 2 * static_cast<size_t>(passes_for<NPL, G>(K)) * kWave;  // 2 padded packets
+    const size_t nchunk = static_cast<size_t>(packet_rows<NPL, G, MODE>()) * (K / 4);
+    const size_t chunks = pl.coop_slots > 0 ? pl.coop_slots * (nchunk + 1)                                  // ring rows
+                                            : 2 * static_cast<size_t>(passes_for<NPL, G, MODE>(K)) * kWave;  // 2 padded packets
     return static_cast<size_t>(pl.s_local) * chunks * sizeof(Chunk) +
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
@@ -1080,7 +1324,7 @@ int choose_qg(const Plan &pl, int dev, int H)
     if (pl.groups <= 1) return H;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE>, block_threads(pl),
-                                                     lds_bytes<T, K, NPL, G>(pl)) != hipSuccess) {
+                                                     lds_bytes<T, K, NPL, G, MODE>(pl)) != hipSuccess) {
         (void)hipGetLastError();
         return H;
     }
@@ -1124,11 +1368,23 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.epoch = e->epoch;
     prm.vec_store = env_int("SSM2D_VECSTORE", 1);
     prm.flip_h = pl.flip_h;
+    if (pl.bw) {
+        prm.states = pl.bw->states;
+        prm.states_ld = pl.bw->ld;
+        prm.states_pad = pl.bw->pad;
+        prm.dy = pl.bw->dy;
+        prm.ddelta = pl.bw->ddelta;
+        prm.dBp = pl.bw->dBp;
+        prm.dCp = pl.bw->dCp;
+        prm.dA = pl.bw->dA;
+        prm.dD = pl.bw->dD;
+        prm.part_stride = pl.bw->part_stride;
+    }
     prm.coop_slots = pl.coop_slots > 0 ? pl.coop_slots : 2;
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;
     prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
-    const size_t lds = lds_bytes<T, K, NPL, G>(pl);
+    const size_t lds = lds_bytes<T, K, NPL, G, MODE>(pl);
     scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
                                    static_cast<hipStream_t>(stream)>>>(prm);
     const hipError_t err = hipGetLastError();
@@ -1143,12 +1399,16 @@ int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const 
                   int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream, int align)
 {
     if (pl.G != 8 || pl.K != 4 || pl.coop_slots != 0) return SSM2D_ERR_UNSUPPORTED;
+    if ((MODE & (kModeStates | kModeBackward)) && !pl.bw) return SSM2D_ERR_UNSUPPORTED;
     const int al = align == 4 ? 4 : 1;
 #define SSM2D_MODE_CASE(NN, AL)    \
     if (pl.npl == NN && al == AL) \
         return run<T, 4, NN, AL, 8, false, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
-    SSM2D_MODE_CASE(1, 4) SSM2D_MODE_CASE(2, 4) SSM2D_MODE_CASE(4, 4) SSM2D_MODE_CASE(8, 4)
-    SSM2D_MODE_CASE(1, 1) SSM2D_MODE_CASE(2, 1) SSM2D_MODE_CASE(4, 1) SSM2D_MODE_CASE(8, 1)
+    SSM2D_MODE_CASE(1, 4) SSM2D_MODE_CASE(2, 4) SSM2D_MODE_CASE(4, 4)
+    SSM2D_MODE_CASE(1, 1) SSM2D_MODE_CASE(2, 1) SSM2D_MODE_CASE(4, 1)
+    if constexpr (!(MODE & kModeBackward)) {  // the backward keeps at most 4 states per lane (d_state <= 32)
+        SSM2D_MODE_CASE(8, 4) SSM2D_MODE_CASE(8, 1)
+    }
 #undef SSM2D_MODE_CASE
     return SSM2D_ERR_UNSUPPORTED;
 }
@@ -1171,7 +1431,9 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
     SSM2D_DISPATCH_DECL(TT, dispatch_acc)            \
     SSM2D_DISPATCH_DECL(TT, dispatch_flipw_acc)      \
     SSM2D_DISPATCH_DECL(TT, dispatch_vfirst_acc)     \
-    SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst_acc)
+    SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst_acc) \
+    SSM2D_DISPATCH_DECL(TT, dispatch_states)           \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd)
 SSM2D_MODE_DECLS(float)
 SSM2D_MODE_DECLS(uint16_t)
 #undef SSM2D_MODE_DECLS

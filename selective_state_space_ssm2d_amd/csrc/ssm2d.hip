@@ -41,13 +41,13 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     // courier waves (so at most maxw - 2 strips per workgroup).
     const bool wide_ok = npl <= 4 && W % 4 == 0 && mode == 0;
     pl.K = 4;
-    if (pl.n_chains >= want_wg && (W + 3) / 4 > max_waves(4, npl, G) && wide_ok &&
-        (W + 7) / 8 <= max_waves(8, npl, G))
+    if (pl.n_chains >= want_wg && (W + 3) / 4 > max_waves(4, npl, G, mode) && wide_ok &&
+        (W + 7) / 8 <= max_waves(8, npl, G, mode))
         pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
     if (mode != 0) pl.K = 4;
-    const int maxw = max_waves(pl.K, npl, G);
+    const int maxw = max_waves(pl.K, npl, G, mode);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;
     if (pl.n_chains >= want_wg && pl.nstrips <= maxw) {
@@ -142,6 +142,74 @@ int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t 
     e.epoch = epoch;
     *out = &e;
     return SSM2D_OK;
+}
+
+// ---------------------------------------------------------------- backward
+
+// Backward workspace per (device, stream): the stored states and the
+// per-channel-block partial sums of dB and dC. Grown when needed (after
+// waiting for the stream); zeroed when allocated.
+struct BwdWs {
+    void *buf = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, void *>, BwdWs> g_bwd_ws;
+
+int get_bwd_ws(int dev, void *stream, size_t bytes, void **out)
+{
+    BwdWs &e = g_bwd_ws[{dev, stream}];
+    if (e.buf && bytes <= e.bytes) {
+        *out = e.buf;
+        return SSM2D_OK;
+    }
+    if (e.buf) {
+        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+        (void)hipFree(e.buf);
+        e = BwdWs{};
+    }
+    void *b = nullptr;
+    if (hipMalloc(&b, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return SSM2D_ERR_NOMEM;
+    }
+    SSM2D_HIP_TRY(hipMemset(b, 0, bytes));
+    e.buf = b;
+    e.bytes = bytes;
+    *out = b;
+    return SSM2D_OK;
+}
+
+// Zeroes dA, dD and the pad columns of the stored states (a shape change can
+// leave another call's values there; the backward reads them for the cells
+// past the map's edge).
+__global__ void bwd_prepare_kernel(float *dA, long n_a, float *dD, long n_d, float *states, long rows, int ld, int pad)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t < n_a) dA[t] = 0.0f;
+    if (t < n_d) dD[t] = 0.0f;
+    if (t < rows)
+        for (int c = 0; c < pad; ++c) states[t * ld + c] = 0.0f;
+}
+
+__device__ __forceinline__ void put(float *p, float v) { *p = v; }
+__device__ __forceinline__ void put(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
+
+// dB, dC = sums of the channel blocks' partials (padded rows) -> dense output.
+template <typename T>
+__global__ void bwd_reduce_kernel(const float *dBp, const float *dCp, long part_stride, int n_dblk, T *dB, T *dC,
+                                  long total, int W, int ld, int pad)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const long row = t / W;
+    const long src = row * ld + pad + (t - row * W);
+    float sb = 0.0f, sc = 0.0f;
+    for (int k = 0; k < n_dblk; ++k) {
+        sb += dBp[k * part_stride + src];
+        sc += dCp[k * part_stride + src];
+    }
+    put(dB + t, sb);
+    put(dC + t, sc);
 }
 
 int device_cus(int dev)
@@ -241,6 +309,90 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     return SSM2D_OK;
 }
 
+template <typename T>
+int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
+             T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+             int64_t W, void *stream)
+{
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
+    if (d_inner == 0) return SSM2D_OK;
+    if (d_state > SSM2D_MAX_STATE_BWD || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t{1} << 31) - 1;
+    const int64_t ld = (W + 3) / 4 * 4, pad = ld - W;
+    const int64_t n_dblk = (d_inner + 7) / 8;
+    if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim ||
+        batch * d_inner * d_state * H * ld > lim || n_dblk * batch * d_state * H * ld > lim)
+        return SSM2D_ERR_UNSUPPORTED;
+    const bool work = batch > 0 && H > 0 && W > 0;
+    if ((!dA && d_state > 0) || !dD || (work && (!x || !delta || !D || !dy || !dx || !ddelta)) ||
+        (work && d_state > 0 && (!A || !B || !C || !dB || !dC)))
+        return SSM2D_ERR_NULLPTR;
+    if (misaligned(x) || misaligned(delta) || misaligned(A) || misaligned(B) || misaligned(C) || misaligned(D) ||
+        misaligned(dy) || misaligned(dx) || misaligned(ddelta) || misaligned(dA) || misaligned(dB) || misaligned(dC) ||
+        misaligned(dD))
+        return SSM2D_ERR_MISALIGNED;
+
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(g_mutex);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const long rows = work ? batch * d_inner * d_state * H : 0;
+    const size_t state_elems = static_cast<size_t>(rows) * ld;
+    const long part_stride = batch * d_state * H * ld;
+    const size_t part_elems = static_cast<size_t>(n_dblk) * part_stride;
+    void *ws = nullptr;
+    if (work) {
+        const int st = get_bwd_ws(dev, stream, (state_elems + 2 * part_elems) * sizeof(float) + 256, &ws);
+        if (st != SSM2D_OK) return st;
+    }
+    float *states = static_cast<float *>(ws);
+    {
+        const long n = std::max<long>(std::max<long>(d_inner * d_state, d_inner), pad ? rows : 0);
+        bwd_prepare_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(
+            dA, d_inner * d_state, dD, d_inner, states, pad ? rows : 0, static_cast<int>(ld), static_cast<int>(pad));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (!work) return SSM2D_OK;
+
+    BwdArgs bw{};
+    bw.states = states;
+    bw.ld = static_cast<int>(ld);
+    bw.pad = static_cast<int>(pad);
+    bw.dy = dy;
+    bw.ddelta = ddelta;
+    bw.dBp = states + state_elems;
+    bw.dCp = bw.dBp + part_elems;
+    bw.dA = dA;
+    bw.dD = dD;
+    bw.part_stride = part_stride;
+    const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
+    const int hi = static_cast<int>(H), wi = static_cast<int>(W);
+    const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
+    // 1. the forward pass again, storing every state
+    Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates);
+    pf.bw = &bw;
+    int st = dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
+    if (st != SSM2D_OK) return st;
+    // 2. the adjoint scans from the lower-right corner, with every local derivative
+    Plan pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward);
+    pb.flip_h = 1;
+    pb.bw = &bw;
+    if (pb.n_dblk != n_dblk) return SSM2D_ERR_UNSUPPORTED;
+    st = dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    if (st != SSM2D_OK) return st;
+    // 3. dB and dC: sums over the channel blocks
+    if (d_state > 0) {
+        const long total = batch * d_state * H * W;
+        bwd_reduce_kernel<T><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+            bw.dBp, bw.dCp, part_stride, static_cast<int>(n_dblk), dB, dC, total, wi, static_cast<int>(ld),
+            static_cast<int>(pad));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SSM2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,6 +423,22 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
                            int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
     return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream);
+}
+
+int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                   const float *D, const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                   float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, void *stream)
+{
+    return scan_bwd<float>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W, stream);
+}
+
+int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
+                        const uint16_t *C, const float *D, const uint16_t *dy, uint16_t *dx, uint16_t *ddelta,
+                        float *dA, uint16_t *dB, uint16_t *dC, float *dD, int64_t batch, int64_t d_inner,
+                        int64_t d_state, int64_t H, int64_t W, void *stream)
+{
+    return scan_bwd<uint16_t>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                              stream);
 }
 
 const char *ssm2d_status_string(int status)

@@ -118,6 +118,34 @@ def test_ex_null_and_misaligned(lib):
         assert _call_ex(lib, [1, 2, 3, 4, 5], pkg.VERTICAL_FIRST, ptrs) == pkg.ERR_MISALIGNED, k
 
 
+def _call_bwd(lib, dims, ptrs=None, bf16=False):
+    ptrs = ptrs if ptrs is not None else [FAKE] * 13
+    fn = lib.ssm2d_scan_bwd_bf16 if bf16 else lib.ssm2d_scan_bwd
+    return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_bwd_validation(lib, bf16):
+    for k in range(5):
+        dims = [1, 2, 3, 4, 5]
+        dims[k] = -1
+        assert _call_bwd(lib, dims, bf16=bf16) == pkg.ERR_BAD_DIM
+    assert _call_bwd(lib, [1, 2, 33, 4, 5], bf16=bf16) == pkg.ERR_UNSUPPORTED   # d_state > 32
+    assert _call_bwd(lib, [1, 2, 4, 65536, 5], bf16=bf16) == pkg.ERR_UNSUPPORTED
+    assert _call_bwd(lib, [1, 0, 3, 4, 5], ptrs=[0] * 13, bf16=bf16) == pkg.OK  # d_inner = 0: nothing
+    # with d_state = 0, A, B, C, dA, dB, dC may be NULL
+    ptrs = [FAKE] * 13
+    for k in (2, 3, 4, 9, 10, 11):
+        ptrs[k] = 0
+    assert _call_bwd(lib, [1, 2, 0, 4, 5], ptrs, bf16=bf16) not in (pkg.ERR_NULLPTR, pkg.ERR_MISALIGNED)
+    for k in range(13):
+        ptrs = [FAKE] * 13
+        ptrs[k] = 0
+        assert _call_bwd(lib, [1, 2, 3, 4, 5], ptrs, bf16=bf16) == pkg.ERR_NULLPTR, k
+        ptrs[k] = FAKE + 4
+        assert _call_bwd(lib, [1, 2, 3, 4, 5], ptrs, bf16=bf16) == pkg.ERR_MISALIGNED, k
+
+
 def test_python_binding_rejects_bad_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 3, 4)

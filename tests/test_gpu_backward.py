@@ -1,0 +1,123 @@
+"""GPU parity of the backward pass (ssm2d_scan_bwd / _bf16) against the fp64
+oracle's backward, gradient by gradient, on the same seeded inputs.
+
+Bars. Elementwise gradients (dx, d delta) and the channel sums dB, dC:
+max |g - g_ref| <= tol (1 + |g_ref|). The parameter gradients dA and dD are
+sums over every cell of the batch, whose fp32 rounding grows with the number
+of terms: their bar is tol (1 + |g_ref|) with the cell count folded in as
+tol = 1e-4 * max(1, sqrt(cells / 4096)). tol = 1e-4 for fp32 inputs, 2e-2 for
+bf16 inputs and outputs (fp32 state and arithmetic).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_ssm2d_amd as pkg
+from selective_state_space_ssm2d_amd.inputs import (WORKLOADS, bf16_bits_from_f32, f32_from_bf16_bits,
+                                                    make_inputs, make_random_inputs)
+from test_gpu_parity import KEYS, _say, _seed, _setup, as_f64, to_dev  # noqa: F401 (_setup: fixture)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dx", "ddelta", "dA", "dB", "dC", "dD")
+
+
+def make_dy(t, dtype, seed):
+    """Seeded upstream gradient with the shape of y; for bf16 the exact bf16
+    values (the oracle sees what the kernel sees)."""
+    dy = np.random.default_rng(seed).standard_normal(t["x"].shape).astype(np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits_from_f32(dy)
+        return f32_from_bf16_bits(bits), torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return dy, torch.from_numpy(dy).cuda()
+
+
+def run_bwd(t, dtype, dy_dev):
+    args = to_dev(t, dtype)
+    g = pkg.scan_bwd(*args, dy_dev)
+    pkg.sync_check()
+    return {k: as_f64(v) for k, v in g.items()}
+
+
+def check_grads(got, ref, dtype, cells, what):
+    for k in NAMES:
+        tol = TOL[dtype]
+        if k in ("dA", "dD"):
+            tol = tol * max(1.0, np.sqrt(cells / 4096.0))
+        g, r = got[k], ref[k]
+        assert g.shape == r.shape, (k, g.shape, r.shape)
+        if g.size == 0:
+            continue
+        err = float(np.max(np.abs(g - r) / (1.0 + np.abs(r))))
+        _say(f"  {what} {k}: max |err|/(1+|g|) = {err:.3e} (bar {tol:.1e})")
+        assert np.all(np.isfinite(g)), (what, k)
+        assert err <= tol, (what, k)
+
+
+BWD_SHAPES = [
+    # batch, d_inner, d_state, H, W: one cell, one row, one column, ragged
+    # tails (W % 4 = 1, 2, 3), several strips / channel blocks / batch entries,
+    # 32 states, odd state counts
+    (1, 1, 1, 1, 1), (1, 3, 4, 1, 37), (2, 5, 4, 29, 1), (1, 17, 8, 13, 7),
+    (1, 9, 16, 14, 30), (2, 16, 16, 21, 64), (1, 12, 16, 10, 66), (1, 8, 32, 9, 21),
+    (3, 20, 3, 7, 45), (1, 24, 5, 33, 19),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=[str(s) for s in BWD_SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward(shape, dtype):
+    _say(f"backward {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 11, dtype=dtype)
+    dy, dy_dev = make_dy(t, dtype, _seed(shape) + 12)
+    got = run_bwd(t, dtype, dy_dev)
+    ref = oracle.bwd(*(t[k] for k in KEYS), dy)
+    check_grads(got, ref, dtype, shape[0] * shape[3] * shape[4], f"{shape} {dtype}")
+
+
+@pytest.mark.parametrize("waves", ["1", "2", "3"])
+def test_backward_multi_workgroup_chains(waves, monkeypatch):
+    """Adjoint carries crossing workgroups (right to left)."""
+    monkeypatch.setenv("SSM2D_WAVES", waves)
+    for shape, dtype in (((1, 16, 16, 33, 80), "f32"), ((1, 8, 16, 21, 130), "bf16")):
+        _say(f"backward chains waves={waves} {shape} {dtype}")
+        t = make_random_inputs(*shape, seed=5, dtype=dtype)
+        dy, dy_dev = make_dy(t, dtype, 6)
+        got = run_bwd(t, dtype, dy_dev)
+        check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), dtype, shape[0] * shape[3] * shape[4],
+                    f"waves={waves} {shape}")
+
+
+def test_backward_special_cases():
+    # no states: dx = dy D, dD = sum dy x; empty maps: dA, dD zeroed
+    t = make_random_inputs(2, 8, 0, 5, 8, seed=7)
+    dy, dy_dev = make_dy(t, "f32", 8)
+    got = run_bwd(t, "f32", dy_dev)
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 80, "d_state=0")
+    x = torch.zeros(1, 4, 0, 8, device="cuda")
+    B = torch.zeros(1, 3, 0, 8, device="cuda")
+    out = {"dA": torch.full((4, 3), 7.0, device="cuda"), "dD": torch.full((4,), 7.0, device="cuda")}
+    g = pkg.scan_bwd(x, x, torch.zeros(4, 3, device="cuda"), B, B, torch.zeros(4, device="cuda"), x, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0)
+
+
+def test_backward_repeated_calls_and_shape_changes():
+    """The workspace is reused and regrown; a smaller ragged call after a larger
+    one (stale pad columns) is still exact to the bar."""
+    for shape in ((1, 16, 16, 19, 64), (1, 9, 8, 17, 13), (1, 16, 16, 19, 64)):
+        t = make_random_inputs(*shape, seed=_seed(shape))
+        dy, dy_dev = make_dy(t, "f32", 9)
+        got = run_bwd(t, "f32", dy_dev)
+        check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", shape[3] * shape[4], f"repeat {shape}")
+
+
+def test_backward_full_wsi_mil():
+    """The WSI-MIL workload at full size (every gradient element)."""
+    wl = next(w for w in WORKLOADS if w.name == "wsi_mil")
+    t = make_inputs(wl, seed=0)
+    dy, dy_dev = make_dy(t, wl.dtype, 10)
+    got = run_bwd(t, wl.dtype, dy_dev)
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), wl.dtype, wl.batch * wl.H * wl.W, "wsi_mil")
