@@ -8,7 +8,8 @@ resident in HBM). Prints one JSON line.
 --variant times another direction / order through ssm2d_scan_fwd_ex instead:
 flip_hw (from the lower-right corner), vfirst (vertical-first order), four_way
 (sum of the four corner scans: four launches per step, the last three adding
-into y), four_way_vfirst.
+into y), four_way_vfirst; or bwd, the backward pass (ssm2d_scan_bwd: the
+stored-state forward, the adjoint scan and the channel sums per step).
 
 Workload (default): the giga-pixel WSI grid, batch 1, d_inner 128, d_state 16,
 H x W = 384 x 512, fp32, 60 % blob-shaped pad cells. Inputs are seeded and
@@ -38,6 +39,11 @@ ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
 # Algorithmic ALU work per (element, state): 2 mul + 3 FMA + 1 exp2, and exp2
 # issues at half rate on gfx950 (2 slots), so 7 slots = 14 FMA-equivalent flops.
 SLOTS_PER_ELEM_STATE = 7
+# Backward per (element, state): the forward's 7 to recompute the states, then
+# 22 for the adjoint: Abar (1 mul + exp2 = 3), u (1), g_h and its carry (2),
+# the carried g_hh (2), hh (1), g_a Abar (4), g_hh B (1), d delta (2), dx (1),
+# dB and dC terms (2), dA (1), and the sums over channels for dB, dC (2).
+SLOTS_PER_ELEM_STATE_BWD = 7 + 22
 
 METRIC = "2D-scan elements/s (B·D·H·W) + % of MI355X peak HBM GB/s"
 
@@ -51,6 +57,14 @@ def algorithmic_bytes(wl, accumulate=False) -> int:
             + wl.d_inner * wl.d_state * 4 + wl.d_inner * 4)
 
 
+def algorithmic_bytes_bwd(wl) -> int:
+    """Compulsory HBM bytes of the backward: x, delta, dy, B, C, A, D read;
+    dx, d delta, dB, dC, dA, dD written (the stored states are not counted)."""
+    s = 2 if wl.dtype == "bf16" else 4
+    bnhw = wl.batch * wl.d_state * wl.H * wl.W
+    return wl.elements * 5 * s + bnhw * 4 * s + 2 * (wl.d_inner * wl.d_state * 4 + wl.d_inner * 4)
+
+
 # variant -> (ssm2d_scan_fwd_ex keywords, launches per step); None: ssm2d_scan_fwd
 VARIANTS = {
     "fwd": (None, 1),
@@ -58,6 +72,7 @@ VARIANTS = {
     "vfirst": (dict(vertical_first=True), 1),
     "four_way": (dict(four_way=True), 4),
     "four_way_vfirst": (dict(four_way=True, vertical_first=True), 4),
+    "bwd": ("bwd", 3),
 }
 
 
@@ -170,6 +185,41 @@ def cpu_baseline(wl, t, keys, seconds: float, kw=None):
                       f"({wl.H}x{wl.W}, d_state {wl.d_state}), fp64, {cw:.1f} s wall on {threads} threads"}
 
 
+def cpu_baseline_bwd(wl, t, keys, seconds: float):
+    """Times the oracle's backward (fp64, OpenMP over batch entries) on the
+    workload's first k channels (all batch entries and cells), k doubling from
+    one until a call takes about `seconds` / 4, then repeated until `seconds`."""
+    import oracle
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    ins = [np.ascontiguousarray(t[k], dtype=np.float64) for k in keys]
+    dy = np.random.default_rng(1).standard_normal(ins[0].shape)
+
+    def call(k):
+        sl = [ins[0][:, :k], ins[1][:, :k], ins[2][:k], ins[3], ins[4], ins[5][:k], dy[:, :k]]
+        c0 = time.perf_counter()
+        oracle.bwd(*sl)
+        return time.perf_counter() - c0
+
+    k = 1
+    while True:
+        dt = call(k)
+        if dt >= seconds / 4 or k >= wl.d_inner:
+            break
+        k = min(wl.d_inner, 2 * k)
+    done, total = 0, 0.0
+    while total < seconds:
+        total += call(k)
+        done += k
+    n_el = done * wl.batch * wl.H * wl.W
+    threads = min(oracle.max_threads(), wl.batch)
+    return {"value": n_el / total, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"backward of {done} channel maps in calls of {k} channels x {wl.batch} batch "
+                      f"({wl.d_inner} channels in the workload) of {wl.name} ({wl.H}x{wl.W}, d_state {wl.d_state}), "
+                      f"fp64, {total:.1f} s wall, OpenMP over the {wl.batch} batch entries"}
+
+
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
              "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline{v}")
 
@@ -256,10 +306,18 @@ def main():
     ncopies = max(2, int(np.ceil(768e6 / abytes)))
     sets = [upload() for _ in range(ncopies)]
     ys = [torch.zeros_like(s[0]) for s in sets]
+    if kw == "bwd":
+        gen = torch.Generator(device="cpu").manual_seed(1)
+        dys = [torch.randn(s[0].shape, generator=gen).to(dev, s[0].dtype) for s in sets]
+        outs = [{"dx": torch.empty_like(s[0]), "ddelta": torch.empty_like(s[1]), "dA": torch.empty_like(s[2]),
+                 "dB": torch.empty_like(s[3]), "dC": torch.empty_like(s[4]), "dD": torch.empty_like(s[5])}
+                for s in sets]
 
     def step(k):
         if kw is None:
             pkg.scan_fwd(*sets[k], y=ys[k])
+        elif kw == "bwd":
+            pkg.scan_bwd(*sets[k], dys[k], out=outs[k])
         else:
             pkg.scan_fwd_ex(*sets[k], y=ys[k], **kw)
 
@@ -285,9 +343,15 @@ def main():
     E = wl.elements
     value = E / (ms_step * 1e-3)
     kmean = float(np.mean(kern_ms))        # one step: `launches` kernels back to back
-    step_bytes = abytes if launches == 1 else abytes + (launches - 1) * algorithmic_bytes(wl, accumulate=True)
+    if kw == "bwd":
+        # reads x, delta, B, C, dy, A, D; writes dx, d delta, dB, dC, dA, dD
+        step_bytes = algorithmic_bytes_bwd(wl)
+        flops = E * wl.d_state * SLOTS_PER_ELEM_STATE_BWD * 2
+        launches = 1  # roofline figures below are per step (three kernels)
+    else:
+        step_bytes = abytes if launches == 1 else abytes + (launches - 1) * algorithmic_bytes(wl, accumulate=True)
+        flops = launches * E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
     gbs = step_bytes / (kmean * 1e-3) / 1e9
-    flops = launches * E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
     tflops = flops / (kmean * 1e-3) / 1e12
 
     # HBM bytes per launch from the committed counter summary, only while it
@@ -302,7 +366,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, t, keys, args.cpu_seconds, kw)
+        cpu = cpu_baseline_bwd(wl, t, keys, args.cpu_seconds) if kw == "bwd" else \
+            cpu_baseline(wl, t, keys, args.cpu_seconds, kw)
 
     rec = {
         "metric": METRIC,

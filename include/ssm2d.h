@@ -153,9 +153,10 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
  * Three kernels are enqueued on `stream`: the forward again, storing every
  * state h; the adjoint scans with the local derivatives; the sums of dB and
  * dC over channel blocks. The library keeps a workspace per (device, stream)
- * of 4 * batch * d_inner * d_state * H * ld + 8 * ceil(d_inner / 8) * batch *
- * d_state * H * ld bytes, ld = W rounded up to a multiple of 4 (grown when
- * needed, kept until the process ends). dA and dD are accumulated with
+ * of 4 * ceil(d_inner / 8) * batch * 4 * ceil(W / 4) * H * (64 npl + 2 d_state)
+ * bytes, npl = d_state / 8 rounded up to a power of two (the stored states, 4
+ * bytes per state and cell at d_state = 8 npl, plus the sums over 8-channel
+ * blocks for dB and dC; grown when needed, kept until the process ends). dA and dD are accumulated with
  * atomics, so their last bits may differ from run to run; every other output
  * is deterministic.
  * Errors as for ssm2d_scan_fwd (with d_state == 0, A, B, C, dA, dB and dC

@@ -103,16 +103,20 @@ struct Params {
     int coop_slots;                    // rows in the workgroup's shared row ring (cooperative loads)
     int coop_shift;                    // log2 of coop_slots
     int flip_h;                        // rows in scan order run bottom to top
-    // stored states (kModeStates writes, kModeBackward reads): fp32
-    // [batch][d_inner][d_state][H][ld], cell (i, j) at i * ld + pad + j
+    // Stored states (kModeStates writes, kModeBackward reads), fp32, as the
+    // waves hold them: one tile per (chain, strip, row) of NPL x 64 lanes x 4
+    // cells, [chain][strip][row][k][lane][cell]. Strips are counted from the
+    // left over the map padded on the left by `states_pad` columns (to a
+    // multiple of 4), so the right-to-left backward meets the same strips.
     float *states;
-    int states_ld, states_pad;
-    // backward: upstream gradient, outputs, per-channel-block partial sums of
-    // dB and dC ([n_dblk][batch][d_state][H][ld], padded like the states)
+    int states_pad;
+    // backward: upstream gradient, d delta (dx goes to y), and the sums of dB
+    // and dC over each wave's 8 channels, [channel block][batch][d_state][H][ld]
+    // (rows of ld = 4 * nstrips columns, the map starting at states_pad)
     const void *dy;
-    void *ddelta;                      // dx goes to y
+    void *ddelta;
     float *dBp, *dCp, *dA, *dD;
-    long part_stride;                  // elements per channel block of dBp / dCp
+    long part_stride;                  // floats per channel block
     unsigned int epoch;
     long long spin_limit;
 };
@@ -236,9 +240,11 @@ __device__ __forceinline__ float row_ror8(float v)
 // state group in the 8-group layout); every lane of the group gets the sum.
 __device__ __forceinline__ float sum8(float v)
 {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    // every lane has a source lane here, so bound_ctrl (zero for lanes
+    // without one) changes nothing and lets the move fold into the add
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, true));  // row_half_mirror
     return v;
 }
 
@@ -683,8 +689,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     const int col = W - jc - 4 * q - 4 + e * ALIGN;
                     src[pp][e] = (col >= 0 ? base + col : zeros) + row0;
                 } else {
-                    const int col = jc + 4 * q + e * ALIGN;
-                    src[pp][e] = ((col + ALIGN <= W) ? base : zeros) + col + row0;
+                    // (the stored-state pass counts strips over the map padded
+                    // on the left: columns below 0 read zeros)
+                    const int col = jc + 4 * q + e * ALIGN - (STATES ? p.states_pad : 0);
+                    src[pp][e] = (col >= 0 && col + ALIGN <= W) ? base + col + row0 : zeros + row0;
                 }
             }
         }
@@ -715,39 +723,27 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 asm volatile("" ::"v"(At[k]));
             }
         }
-        // Stored states of this lane's NPL states (row-major, padded rows of
-        // states_ld with the map starting at column states_pad, so that a
-        // right-to-left strip's 4 cells are one aligned chunk). The forward
-        // writes its strip's cells of each row; the backward reads, for scan
-        // row t, the chunk of memory row H-1-t (rows past the map read zeros).
-        // Partial sums of dB and dC have the same layout per channel block.
-        const int sld = p.states_ld;
-        float *hdst[NPL];
-        const float *hsrc[NPL];
-        float *pdb[NPL], *pdc[NPL];
-        bool hok[NPL];
-        long hstep[NPL];
+        // Stored-state tiles: the forward writes its strip's tile of each row
+        // (whole 1 KB blocks per state slot, every lane, no masks: lanes and
+        // cells outside the map hold exact zeros); the backward's strip s and
+        // scan row t read the forward's strip nstrips-1-s, row H-1-t (its
+        // cells in reverse order); rows past the map read the zero page.
+        constexpr long TILE = static_cast<long>(NPL) * kWave * 4;   // floats per (chain, strip, row)
+        const int fstrip = BWD ? p.nstrips - 1 - strip : strip;     // strip in the forward's numbering
+        const long tile0 = (static_cast<long>(chain) * p.nstrips + fstrip) * H;  // tile of row 0
+        float *hrow = p.states + tile0 * TILE + lane * 4;            // + row * TILE + k * 256
+        const float *hlast = p.states + (tile0 + H - 1) * TILE + lane * 4;
+        // backward: 8-channel sums of dB, dC for this lane's group, memory row
+        // H-1 - t, the strip's 4 cells at padded column 4 * fstrip
+        const long pld = 4L * p.nstrips;
+        const long part0 = dblk * p.part_stride + ((static_cast<long>(b) * p.d_state + g * NPL) * H + (H - 1)) * pld + 4L * fstrip;
+        float *pbrow = p.dBp + part0;
+        float *pcrow = p.dCp + part0;
         const float *zeros_f = static_cast<const float *>(p.zeros);
-        if constexpr (STATES || BWD) {
+        bool hok[NPL];
 #pragma unroll
-            for (int k = 0; k < NPL; ++k) {
-                const int n = g * NPL + k;
-                hok[k] = d_ok && n < p.d_state;
-                const long map = (static_cast<long>(b) * p.d_inner + d) * p.d_state + n;
-                float *base = p.states + map * H * sld + p.states_pad;
-                if constexpr (STATES) {
-                    hdst[k] = hok[k] ? base + j0 : nullptr;
-                } else {
-                    hsrc[k] = hok[k] ? base + static_cast<long>(H - 1) * sld + (W - j0 - 4) : zeros_f;
-                    hstep[k] = hok[k] ? -static_cast<long>(sld) : 0;
-                    const long part = dblk * p.part_stride + ((static_cast<long>(b) * p.d_state + (n < p.d_state ? n : 0)) * H + (H - 1)) * sld +
-                                      p.states_pad + (W - j0 - 4);
-                    pdb[k] = p.dBp + part;
-                    pdc[k] = p.dCp + part;
-                }
-            }
-        }
-        const bool part_lane = (dl == 0);  // stores the channel-block sums of its state group
+        for (int k = 0; k < NPL; ++k) hok[k] = d_ok && (g * NPL + k < p.d_state);
+        const bool part_lane = (dl == 0);  // stores the 8-channel sums of its state group
         // First of this lane's finished cells (for G = 8 and K = 4 the two
         // lanes of a pair hold the same cell and the odd one does not store).
         const int c_out = (K >= G) ? g * KO : g / 2;
@@ -774,14 +770,16 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         const bool vec_lane = (lane < CPW) && d_ok;
         T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + row0 +
                   (FW ? W - j0 - K : j0);
-        // Backward: d delta goes where dx goes, in its own tensor.
-        T *ddst[KO];
-        T *dvec = yvec;
+        // Backward: d delta goes where dx goes, in its own tensor: the same
+        // addresses moved by the distance between the two tensors (zero for
+        // lanes writing the sink). Offsets keep the stores on global pointers.
+        long ddoff[KO], dvoff = 0;
         if constexpr (BWD) {
+            const long dist = static_cast<long>(reinterpret_cast<uintptr_t>(p.ddelta) - reinterpret_cast<uintptr_t>(p.y)) /
+                              static_cast<long>(sizeof(T));
 #pragma unroll
-            for (int c = 0; c < KO; ++c)
-                ddst[c] = (ystep[c] != 0) ? static_cast<T *>(p.ddelta) + (ydst[c] - static_cast<T *>(p.y)) : ydst[c];
-            dvec = static_cast<T *>(p.ddelta) + (yvec - static_cast<T *>(p.y));
+            for (int c = 0; c < KO; ++c) ddoff[c] = (ystep[c] != 0) ? dist : 0;
+            dvoff = dist;
         }
         float dAacc[NPL], dDacc = 0.0f;  // backward: this lane's parts of dA and dD
 #pragma unroll
@@ -1068,21 +1066,20 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     for (int c = 0; c < KO; ++c) dxo[c] = __builtin_fmaf(Dd, dyo[c], dxo[c]);
                     if (vec_store) {
                         store_row<K, G, FW>(yvec, dxo, vec_lane);
-                        store_row<K, G, FW>(dvec, ddo, vec_lane);
+                        store_row<K, G, FW>(yvec + dvoff, ddo, vec_lane);
                         yvec += rs;
-                        dvec += rs;
                     } else {
 #pragma unroll
                         for (int c = 0; c < KO; ++c) {
                             store_elem(ydst[c], dxo[c]);
-                            store_elem(ddst[c], ddo[c]);
+                            store_elem(ydst[c] + ddoff[c], ddo[c]);
                             ydst[c] += ystep[c];
-                            ddst[c] += ystep[c];
                         }
                     }
                     // dB and dC: sums over the wave's 8 channels of a state
-                    // group, one partial per channel block (summed later)
-                    const long prow = static_cast<long>(i) * sld;
+                    // group (the sum over channel blocks comes later), cells
+                    // in memory order
+                    const long prow = static_cast<long>(i) * pld;
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) {
                         float sb[K], sc[K];
@@ -1092,8 +1089,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                             sc[c] = sum8(dCv[k][c]);
                         }
                         if (part_lane && hok[k]) {
-                            *reinterpret_cast<float4 *>(pdb[k] - prow) = make_float4(sb[3], sb[2], sb[1], sb[0]);
-                            *reinterpret_cast<float4 *>(pdc[k] - prow) = make_float4(sc[3], sc[2], sc[1], sc[0]);
+                            const long off = static_cast<long>(k) * H * pld - prow;
+                            *reinterpret_cast<float4 *>(pbrow + off) = make_float4(sb[3], sb[2], sb[1], sb[0]);
+                            *reinterpret_cast<float4 *>(pcrow + off) = make_float4(sc[3], sc[2], sc[1], sc[0]);
                         }
                     }
                 } else {
@@ -1116,15 +1114,11 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     }
 
                     if constexpr (STATES) {
-                        // every state of the strip's valid cells, this row
+                        // the wave's tile of this row
 #pragma unroll
                         for (int k = 0; k < NPL; ++k)
-                            if (hok[k]) {
-                                float *dst = hdst[k] + static_cast<long>(i) * sld;
-#pragma unroll
-                                for (int c = 0; c < K; ++c)
-                                    if (c < valid) dst[c] = hv[c][k];
-                            }
+                            *reinterpret_cast<float4 *>(hrow + static_cast<long>(i) * TILE + k * kWave * 4) =
+                                make_float4(hv[0][k], hv[1][k], hv[2][k], hv[3][k]);
                     } else {
                         // ---- sum over the state groups, skip term, store
                         float out[KO];
@@ -1183,7 +1177,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                         const int t = first + s;
 #pragma unroll
                         for (int k = 0; k < NPL; ++k)
-                            hb[s][k] = *reinterpret_cast<const float4 *>(t < H ? hsrc[k] + t * hstep[k] : zeros_f);
+                            hb[s][k] = *reinterpret_cast<const float4 *>(
+                                t < H ? hlast - static_cast<long>(t) * TILE + k * kWave * 4 : zeros_f);
                     }
                 }
             };
@@ -1270,7 +1265,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 // of dB and dC live in a library workspace; the rest are the caller's).
 struct BwdArgs {
     float *states;
-    int ld, pad;
+    int pad;
     const void *dy;
     void *ddelta;
     float *dBp, *dCp, *dA, *dD;
@@ -1370,7 +1365,6 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.flip_h = pl.flip_h;
     if (pl.bw) {
         prm.states = pl.bw->states;
-        prm.states_ld = pl.bw->ld;
         prm.states_pad = pl.bw->pad;
         prm.dy = pl.bw->dy;
         prm.ddelta = pl.bw->ddelta;

@@ -179,22 +179,20 @@ int get_bwd_ws(int dev, void *stream, size_t bytes, void **out)
     return SSM2D_OK;
 }
 
-// Zeroes dA, dD and the pad columns of the stored states (a shape change can
-// leave another call's values there; the backward reads them for the cells
-// past the map's edge).
-__global__ void bwd_prepare_kernel(float *dA, long n_a, float *dD, long n_d, float *states, long rows, int ld, int pad)
+// Zeroes dA and dD (the backward adds into them).
+__global__ void bwd_prepare_kernel(float *dA, long n_a, float *dD, long n_d)
 {
     const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t < n_a) dA[t] = 0.0f;
     if (t < n_d) dD[t] = 0.0f;
-    if (t < rows)
-        for (int c = 0; c < pad; ++c) states[t * ld + c] = 0.0f;
 }
 
 __device__ __forceinline__ void put(float *p, float v) { *p = v; }
 __device__ __forceinline__ void put(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
 
-// dB, dC = sums of the channel blocks' partials (padded rows) -> dense output.
+// dB, dC [batch][d_state][H][W] = sums over the channel blocks of the
+// backward's 8-channel sums ([channel block][batch][d_state][H][ld], the map
+// starting at column pad of each row).
 template <typename T>
 __global__ void bwd_reduce_kernel(const float *dBp, const float *dCp, long part_stride, int n_dblk, T *dB, T *dC,
                                   long total, int W, int ld, int pad)
@@ -202,11 +200,11 @@ __global__ void bwd_reduce_kernel(const float *dBp, const float *dCp, long part_
     const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= total) return;
     const long row = t / W;
-    const long src = row * ld + pad + (t - row * W);
+    long idx = row * ld + pad + (t - row * W);
     float sb = 0.0f, sc = 0.0f;
-    for (int k = 0; k < n_dblk; ++k) {
-        sb += dBp[k * part_stride + src];
-        sc += dCp[k * part_stride + src];
+    for (int q = 0; q < n_dblk; ++q, idx += part_stride) {
+        sb += dBp[idx];
+        sc += dCp[idx];
     }
     put(dB + t, sb);
     put(dC + t, sc);
@@ -318,10 +316,12 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (d_inner == 0) return SSM2D_OK;
     if (d_state > SSM2D_MAX_STATE_BWD || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
     const int64_t lim = (int64_t{1} << 31) - 1;
-    const int64_t ld = (W + 3) / 4 * 4, pad = ld - W;
+    const int64_t nstrips = (W + 3) / 4, pad = 4 * nstrips - W;
     const int64_t n_dblk = (d_inner + 7) / 8;
-    if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim ||
-        batch * d_inner * d_state * H * ld > lim || n_dblk * batch * d_state * H * ld > lim)
+    int64_t npl = 1;
+    while (npl * 8 < d_state) npl *= 2;
+    const int64_t tiles = batch * n_dblk * nstrips * H;  // (chain, strip, row)
+    if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim)
         return SSM2D_ERR_UNSUPPORTED;
     const bool work = batch > 0 && H > 0 && W > 0;
     if ((!dA && d_state > 0) || !dD || (work && (!x || !delta || !D || !dy || !dx || !ddelta)) ||
@@ -336,10 +336,9 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(g_mutex);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const long rows = work ? batch * d_inner * d_state * H : 0;
-    const size_t state_elems = static_cast<size_t>(rows) * ld;
-    const long part_stride = batch * d_state * H * ld;
-    const size_t part_elems = static_cast<size_t>(n_dblk) * part_stride;
+    const size_t state_elems = work ? static_cast<size_t>(tiles) * npl * kWave * 4 : 0;
+    const long part_stride = batch * d_state * H * 4 * nstrips;  // floats per channel block
+    const size_t part_elems = work ? static_cast<size_t>(n_dblk) * part_stride : 0;
     void *ws = nullptr;
     if (work) {
         const int st = get_bwd_ws(dev, stream, (state_elems + 2 * part_elems) * sizeof(float) + 256, &ws);
@@ -347,9 +346,9 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     }
     float *states = static_cast<float *>(ws);
     {
-        const long n = std::max<long>(std::max<long>(d_inner * d_state, d_inner), pad ? rows : 0);
-        bwd_prepare_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(
-            dA, d_inner * d_state, dD, d_inner, states, pad ? rows : 0, static_cast<int>(ld), static_cast<int>(pad));
+        const long n = std::max<long>(d_inner * d_state, d_inner);
+        bwd_prepare_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(dA, d_inner * d_state,
+                                                                                            dD, d_inner);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
     }
@@ -357,7 +356,6 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 
     BwdArgs bw{};
     bw.states = states;
-    bw.ld = static_cast<int>(ld);
     bw.pad = static_cast<int>(pad);
     bw.dy = dy;
     bw.ddelta = ddelta;
@@ -372,20 +370,21 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     // 1. the forward pass again, storing every state
     Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates);
     pf.bw = &bw;
+    if (pf.npl != npl || pf.n_dblk != n_dblk || pf.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     int st = dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 2. the adjoint scans from the lower-right corner, with every local derivative
     Plan pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward);
     pb.flip_h = 1;
     pb.bw = &bw;
-    if (pb.n_dblk != n_dblk) return SSM2D_ERR_UNSUPPORTED;
+    if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     st = dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 3. dB and dC: sums over the channel blocks
     if (d_state > 0) {
         const long total = batch * d_state * H * W;
         bwd_reduce_kernel<T><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
-            bw.dBp, bw.dCp, part_stride, static_cast<int>(n_dblk), dB, dC, total, wi, static_cast<int>(ld),
+            bw.dBp, bw.dCp, part_stride, static_cast<int>(n_dblk), dB, dC, total, wi, static_cast<int>(4 * nstrips),
             static_cast<int>(pad));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
