@@ -108,6 +108,7 @@ int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
 #define SSM2D_VERTICAL_FIRST 4u
 #define SSM2D_ACCUMULATE 8u
 #define SSM2D_FOUR_WAY 16u
+#define SSM2D_DELTA_SOFTPLUS 32u
 
 /* Forward pass in the direction and order `flags` selects (an OR of the bits
  * above; 0 gives ssm2d_scan_fwd). Arguments, layout, ownership, asynchrony and
@@ -118,7 +119,8 @@ int ssm2d_scan_fwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
  *     in fp32 and rounded once to y's type; deterministic.
  *   SSM2D_FOUR_WAY enqueues four kernels on `stream`, the last three
  *     accumulating; with SSM2D_ACCUMULATE the first accumulates too.
- *   Unknown bits, or SSM2D_FOUR_WAY with SSM2D_FLIP_H or SSM2D_FLIP_W
+ *   Unknown bits (SSM2D_DELTA_SOFTPLUS is accepted and applies softplus to
+ *   delta), or SSM2D_FOUR_WAY with SSM2D_FLIP_H or SSM2D_FLIP_W
  *                                                -> SSM2D_ERR_BAD_FLAGS
  *     (checked first, before the sizes).
  * Right-to-left and vertical-first scans run 4-column strips with 8 state
@@ -132,6 +134,35 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
                            const uint16_t *B, const uint16_t *C, const float *D, uint16_t *y,
                            int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
                            uint32_t flags, void *stream);
+
+/* ---- Mamba selective-scan options -----------------------------------------
+ *
+ * The pages name Mamba's selective_scan_fn as the operator the 2D scan
+ * extends. Its options around the scan, for the 2D scan:
+ *   step size  delta' = delta + delta_bias[d] (delta_bias may be NULL: 0),
+ *              then softplus(delta') = log(1 + e^delta') if SSM2D_DELTA_SOFTPLUS;
+ *              computed in fp32 by a separate pass and stored in the input
+ *              type (bf16 inputs: delta' is rounded to bf16, nearest even)
+ *              in a library workspace of batch*d_inner*H*W elements per
+ *              (device, stream); the scan then runs on delta';
+ *   gate       y = (sum_n C h + D x) * SiLU(z), SiLU(z) = z / (1 + e^-z), z
+ *              shaped like x in x's type (z may be NULL: no gate).
+ * Arguments otherwise as for ssm2d_scan_fwd_ex, with the same flags (and
+ * SSM2D_DELTA_SOFTPLUS). The gate applies to this call's result: with
+ * SSM2D_FOUR_WAY it multiplies the four-corner sum (one more pass over y);
+ * a gate with SSM2D_ACCUMULATE -> SSM2D_ERR_BAD_FLAGS. Gated single scans use
+ * 8 state groups and 4-column strips, with the gate fused into the store. */
+int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B,
+                         const float *C, const float *D, const float *z, const float *delta_bias,
+                         float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                         int64_t W, uint32_t flags, void *stream);
+
+/* bf16 variant: x, delta, B, C, z, y bfloat16 bits; A, D, delta_bias float32. */
+int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                              const uint16_t *B, const uint16_t *C, const float *D,
+                              const uint16_t *z, const float *delta_bias, uint16_t *y,
+                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                              int64_t W, uint32_t flags, void *stream);
 
 /* ---- Backward pass -------------------------------------------------------
  *

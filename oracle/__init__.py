@@ -16,6 +16,8 @@ fwd(x, delta, A, B, C, D, maps=None, nthreads=0, flip_h=False, flip_w=False,
 states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
                         the recurrences alone on given Abar, Bx (one map)
 bwd(x, delta, A, B, C, D, dy) -> dict of dx, ddelta, dA, dB, dC, dD (float64)
+fwd_mamba(x, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=False, ...)
+                        the scan with Mamba's step-size bias / softplus and SiLU(z) gating
 max_threads()           OpenMP thread count the oracle uses by default
 """
 from __future__ import annotations
@@ -150,6 +152,44 @@ def states(abar, bx, lib=None, flip_h=False, flip_w=False, vertical_first=False)
     if s != 0:
         raise RuntimeError(f"oracle failed with status {s}")
     return h
+
+
+def softplus(v):
+    """log(1 + e^v) in fp64, without overflow for large v."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.where(v > 0, v + np.log1p(np.exp(-np.abs(v))), np.log1p(np.exp(v)))
+
+
+def silu(z):
+    """z * sigmoid(z) in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, delta_round=None,
+              maps=None, lib=None, **dirs):
+    """The Mamba selective-scan operator's options around the 2D scan: the
+    step size is delta + delta_bias[d] (bias per channel), passed through
+    softplus when asked, and the output is gated by SiLU(z), z shaped like x
+    (Mamba's selective_scan_fn options; the 2DMamba pages name that entry point
+    as the op they extend). ``delta_round`` (a function) is applied to the
+    effective step size before the scan, for inputs that store it rounded.
+    ``dirs``: flip_h, flip_w, vertical_first, four_way as for fwd."""
+    dt = np.asarray(delta, dtype=np.float64)
+    if delta_bias is not None:
+        dt = dt + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
+    if delta_softplus:
+        dt = softplus(dt)
+    if delta_round is not None:
+        dt = delta_round(dt)
+    y = fwd(x, dt, A, B, C, D, maps=maps, lib=lib, **dirs)
+    if z is not None:
+        g = silu(z)
+        if maps is not None:
+            b_, d_, H, W = np.shape(x)
+            g = g.reshape(b_ * d_, H, W)[np.asarray(maps)]
+        y = y * g
+    return y
 
 
 def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None):

@@ -9,6 +9,7 @@ streams only. There is no fallback: if the library is missing the call fails.
     y = scan_fwd(x, delta, A, B, C, D)
     y = scan_fwd_ex(x, delta, A, B, C, D, flip_h=..., flip_w=..., vertical_first=...,
                     accumulate=..., four_way=...)
+    y = scan_fwd_mamba(x, delta, A, B, C, D, z=..., delta_bias=..., delta_softplus=...)
     g = scan_bwd(x, delta, A, B, C, D, dy)   # dict: dx, ddelta, dA, dB, dC, dD
 
 x, delta: [batch, d_inner, H, W]; B, C: [batch, d_state, H, W]; all four
@@ -24,7 +25,8 @@ import os
 import re
 
 __all__ = [
-    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_bwd", "status_string",
+    "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_fwd_mamba", "scan_bwd",
+    "status_string",
     "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
 ]
 
@@ -34,7 +36,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm2d.h")
 
 (OK, ERR_NULLPTR, ERR_BAD_DIM, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NOMEM, ERR_DEVICE_TIMEOUT,
  ERR_BAD_FLAGS) = range(9)
-FLIP_H, FLIP_W, VERTICAL_FIRST, ACCUMULATE, FOUR_WAY = 1, 2, 4, 8, 16
+FLIP_H, FLIP_W, VERTICAL_FIRST, ACCUMULATE, FOUR_WAY, DELTA_SOFTPLUS = 1, 2, 4, 8, 16, 32
 
 _lib = None
 
@@ -57,6 +59,10 @@ def load_library(path: str = LIB_PATH):
     for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
+        f.restype = ctypes.c_int
+    for name in ("ssm2d_scan_fwd_mamba", "ssm2d_scan_fwd_mamba_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_uint32, vp]
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_bwd", "ssm2d_scan_bwd_bf16"):
         f = getattr(lib, name)
@@ -196,6 +202,31 @@ def scan_fwd_ex(x, delta, A, B, C, D=None, y=None, *, flip_h=False, flip_w=False
                  | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0))
     fn = lib.ssm2d_scan_fwd_ex if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_ex_bf16
     _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, y)] + [*dims, int(flags), _stream_handle(stream)])
+    return y
+
+
+def scan_fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, y=None, *, delta_softplus=False,
+                   flip_h=False, flip_w=False, vertical_first=False, four_way=False, accumulate=False, stream=None):
+    """The 2D scan with Mamba's operator options (include/ssm2d.h,
+    ssm2d_scan_fwd_mamba): step size delta + delta_bias[d], optionally through
+    softplus, and the output gated by SiLU(z)."""
+    import torch
+
+    lib = load_library()
+    if accumulate and y is None:
+        raise ValueError("accumulate needs y")
+    y, dims = _check(x, delta, A, B, C, D, y, need_d=False)
+    if z is not None and (z.shape != x.shape or z.dtype != x.dtype or z.device != x.device or not z.is_contiguous()):
+        raise ValueError("z must match x in shape, dtype and device, and be contiguous")
+    if delta_bias is not None and (delta_bias.shape != (dims[1],) or delta_bias.dtype != torch.float32
+                                   or delta_bias.device != x.device):
+        raise ValueError("delta_bias must be float32 [d_inner] on x's device")
+    flags = ((FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
+             | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0)
+             | (DELTA_SOFTPLUS if delta_softplus else 0))
+    fn = lib.ssm2d_scan_fwd_mamba if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_mamba_bf16
+    _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, y)]
+          + [*dims, flags, _stream_handle(stream)])
     return y
 
 

@@ -1,0 +1,24 @@
+// libssm2d: kernel instances for fp32 inputs with the output gated by SiLU(z).
+#include "scan2d_kernel.h"
+
+namespace ssm2d_impl {
+
+// gated
+int dispatch_gate(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                  const float *D, float *y, int batch, int d_inner, int d_state, int H, int W,
+                  const Plan &pl, int dev, void *stream, int align)
+{
+    constexpr int kMode = kModeGate;
+    return dispatch_mode<float, kMode>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream, align);
+}
+
+// gated, vertical-first
+int dispatch_gate_vfirst(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                         const float *D, float *y, int batch, int d_inner, int d_state, int H, int W,
+                         const Plan &pl, int dev, void *stream, int align)
+{
+    constexpr int kMode = kModeGate | kModeVFirst;
+    return dispatch_mode<float, kMode>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream, align);
+}
+
+}  // namespace ssm2d_impl

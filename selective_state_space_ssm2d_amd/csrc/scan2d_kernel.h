@@ -66,11 +66,13 @@ constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + 
 //   kModeStates      forward pass that writes every state h and no y
 //   kModeBackward    adjoint pass of the backward (with kModeFlipW and rows
 //                    bottom to top): gradients from the stored states
+//   kModeGate        the result is multiplied by SiLU(z) before it is stored
 constexpr int kModeFlipW = 1;
 constexpr int kModeVFirst = 2;
 constexpr int kModeAccumulate = 4;
 constexpr int kModeStates = 8;
 constexpr int kModeBackward = 16;
+constexpr int kModeGate = 32;
 
 // Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
 // small (8 state groups, K * NPL <= 16, not the backward passes), else 8,
@@ -117,6 +119,7 @@ struct Params {
     void *ddelta;
     float *dBp, *dCp, *dA, *dD;
     long part_stride;                  // floats per channel block
+    const void *z;                     // gate input, shaped like y (kModeGate)
     unsigned int epoch;
     long long spin_limit;
 };
@@ -460,6 +463,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool ACC = (MODE & kModeAccumulate) != 0;
     constexpr bool STATES = (MODE & kModeStates) != 0;
     constexpr bool BWD = (MODE & kModeBackward) != 0;
+    constexpr bool GATE = (MODE & kModeGate) != 0;
+    static_assert(!GATE || (!ACC && !STATES && !BWD && !COOP), "gate: plain output only");
     static_assert(!BWD || (FW && !VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
     static_assert(!STATES || (!FW && !VF && !ACC && !COOP), "stored states: forward order only");
     static_assert(!(COOP && FW), "cooperative loads keep columns in memory order");
@@ -780,6 +785,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 #pragma unroll
             for (int c = 0; c < KO; ++c) ddoff[c] = (ystep[c] != 0) ? dist : 0;
             dvoff = dist;
+        }
+        // Gate: z of this lane's output cells, at the same place in its tensor
+        // (offset zero for lanes writing the sink, which read it instead).
+        long zoff[KO];
+        if constexpr (GATE) {
+            const long dist = static_cast<long>(reinterpret_cast<uintptr_t>(p.z) - reinterpret_cast<uintptr_t>(p.y)) /
+                              static_cast<long>(sizeof(T));
+#pragma unroll
+            for (int c = 0; c < KO; ++c) zoff[c] = (ystep[c] != 0) ? dist : 0;
         }
         float dAacc[NPL], dDacc = 0.0f;  // backward: this lane's parts of dA and dD
 #pragma unroll
@@ -1125,6 +1139,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                         reduce_groups<K, G>(part, out, g);
 #pragma unroll
                         for (int c = 0; c < KO; ++c) out[c] += Dd * xo[c];
+                        if constexpr (GATE) {
+                            // times SiLU(z) = z / (1 + e^-z); z of this row was read with its inputs
+#pragma unroll
+                            for (int c = 0; c < KO; ++c) {
+                                const float zf = elem_value(yo[c]);
+                                out[c] *= zf * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zf * kLog2e));
+                            }
+                        }
                         if constexpr (ACC) {
                             // y of this row was read with the row's inputs
 #pragma unroll
@@ -1157,6 +1179,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             // Accumulating into y: each row's y cells are read with its inputs
             // (yoA / yoB, loaded with bufA / bufB), added to the result and
             // written back by the same lane, so no other wave touches them.
+            // Gated: yoA / yoB hold z of those cells instead.
             // Backward: each row's stored states (hbA / hbB), read likewise;
             // a row needs its own and the next scan row's.
             Chunk bufA[P][PASSES], bufB[P][PASSES];
@@ -1172,6 +1195,11 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     if constexpr (ACC) {
 #pragma unroll
                         for (int c = 0; c < KO; ++c) yo[s][c] = ybase[c][static_cast<long>(min(first + s, H - 1)) * ystep[c]];
+                    }
+                    if constexpr (GATE) {
+#pragma unroll
+                        for (int c = 0; c < KO; ++c)
+                            yo[s][c] = ybase[c][zoff[c] + static_cast<long>(min(first + s, H - 1)) * ystep[c]];
                     }
                     if constexpr (BWD) {
                         const int t = first + s;
@@ -1278,6 +1306,7 @@ struct Plan {
     int mode;        // kMode* bits
     int flip_h;      // rows bottom to top
     const BwdArgs *bw;  // stored-state and backward passes
+    const void *z;   // gate input (kModeGate)
 };
 
 int env_int(const char *name, int dflt);
@@ -1374,6 +1403,7 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
         prm.dD = pl.bw->dD;
         prm.part_stride = pl.bw->part_stride;
     }
+    prm.z = pl.z;
     prm.coop_slots = pl.coop_slots > 0 ? pl.coop_slots : 2;
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;
@@ -1394,6 +1424,7 @@ int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const 
 {
     if (pl.G != 8 || pl.K != 4 || pl.coop_slots != 0) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & (kModeStates | kModeBackward)) && !pl.bw) return SSM2D_ERR_UNSUPPORTED;
+    if ((MODE & kModeGate) && !pl.z) return SSM2D_ERR_UNSUPPORTED;
     const int al = align == 4 ? 4 : 1;
 #define SSM2D_MODE_CASE(NN, AL)    \
     if (pl.npl == NN && al == AL) \
@@ -1427,7 +1458,11 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
     SSM2D_DISPATCH_DECL(TT, dispatch_vfirst_acc)     \
     SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst_acc) \
     SSM2D_DISPATCH_DECL(TT, dispatch_states)           \
-    SSM2D_DISPATCH_DECL(TT, dispatch_bwd)
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd)              \
+    SSM2D_DISPATCH_DECL(TT, dispatch_gate)             \
+    SSM2D_DISPATCH_DECL(TT, dispatch_gate_vfirst)      \
+    SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw)       \
+    SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw_vfirst)
 SSM2D_MODE_DECLS(float)
 SSM2D_MODE_DECLS(uint16_t)
 #undef SSM2D_MODE_DECLS

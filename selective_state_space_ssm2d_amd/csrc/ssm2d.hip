@@ -210,6 +210,61 @@ __global__ void bwd_reduce_kernel(const float *dBp, const float *dCp, long part_
     put(dC + t, sc);
 }
 
+// ---------------------------------------------------------------- Mamba-op options
+
+// Scratch per (device, stream, slot), grown when needed; not zeroed.
+std::map<std::pair<std::pair<int, void *>, int>, BwdWs> g_aux_ws;
+
+int get_aux_ws(int dev, void *stream, int slot, size_t bytes, void **out)
+{
+    BwdWs &e = g_aux_ws[{{dev, stream}, slot}];
+    if (e.buf && bytes <= e.bytes) {
+        *out = e.buf;
+        return SSM2D_OK;
+    }
+    if (e.buf) {
+        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+        (void)hipFree(e.buf);
+        e = BwdWs{};
+    }
+    void *b = nullptr;
+    if (hipMalloc(&b, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return SSM2D_ERR_NOMEM;
+    }
+    e.buf = b;
+    e.bytes = bytes;
+    *out = b;
+    return SSM2D_OK;
+}
+
+__device__ __forceinline__ float get(const float *p) { return *p; }
+__device__ __forceinline__ float get(const uint16_t *p) { return __uint_as_float(static_cast<unsigned>(*p) << 16); }
+
+// Step size of the scan: delta + bias[d], through softplus if asked, computed
+// in fp32 and stored in the input type. softplus(v) = max(v, 0) + log1p(e^-|v|).
+template <typename T>
+__global__ void delta_prep_kernel(const T *delta, const float *bias, T *out, long total, long hw, int d_inner,
+                                  int use_softplus)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    float v = get(delta + t);
+    if (bias) v += bias[(t / hw) % d_inner];
+    if (use_softplus) v = fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+    put(out + t, v);
+}
+
+// y *= SiLU(z) = z / (1 + e^-z), for outputs summed over several launches.
+template <typename T>
+__global__ void gate_kernel(T *y, const T *z, long total)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const float zf = get(z + t);
+    put(y + t, get(y + t) * (zf / (1.0f + expf(-zf))));
+}
+
 int device_cus(int dev)
 {
     static std::map<int, int> cache;
@@ -231,10 +286,12 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
-           int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream)
+           int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
+           const T *z = nullptr)
 {
     Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
     pl.flip_h = flip_h;
+    pl.z = z;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
@@ -260,21 +317,28 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     case FW | AC: return dispatch_flipw_acc(SSM2D_ARGS);
     case VF | AC: return dispatch_vfirst_acc(SSM2D_ARGS);
     case FW | VF | AC: return dispatch_flipw_vfirst_acc(SSM2D_ARGS);
+    case kModeGate: return dispatch_gate(SSM2D_ARGS);
+    case kModeGate | VF: return dispatch_gate_vfirst(SSM2D_ARGS);
+    case kModeGate | FW: return dispatch_gate_flipw(SSM2D_ARGS);
+    case kModeGate | FW | VF: return dispatch_gate_flipw_vfirst(SSM2D_ARGS);
     default: return SSM2D_ERR_UNSUPPORTED;
     }
 #undef SSM2D_ARGS
 }
 
-constexpr unsigned kKnownFlags = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST | SSM2D_ACCUMULATE | SSM2D_FOUR_WAY;
+constexpr unsigned kKnownFlags = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST | SSM2D_ACCUMULATE | SSM2D_FOUR_WAY |
+                                 SSM2D_DELTA_SOFTPLUS;
 
 // `extended`: the flag-taking entry points, where D may be NULL (no skip term).
+// z (gate) and delta_bias come with the Mamba-option entry points only.
 template <typename T>
 int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
-             void *stream)
+             void *stream, const T *z = nullptr, const float *delta_bias = nullptr)
 {
     if ((flags & ~kKnownFlags) != 0) return SSM2D_ERR_BAD_FLAGS;
     if ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))) return SSM2D_ERR_BAD_FLAGS;
+    if (z && (flags & SSM2D_ACCUMULATE)) return SSM2D_ERR_BAD_FLAGS;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
     if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
@@ -282,19 +346,36 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim)
         return SSM2D_ERR_UNSUPPORTED;
     if (!x || !delta || (!D && !extended) || !y || (d_state > 0 && (!A || !B || !C))) return SSM2D_ERR_NULLPTR;
-    if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) ||
-        (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
+    if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) || misaligned(z) ||
+        misaligned(delta_bias) || (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
         return SSM2D_ERR_MISALIGNED;
 
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(g_mutex);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const long total = batch * d_inner * H * W;
+    const unsigned nblk = static_cast<unsigned>((total + 255) / 256);
+    if (delta_bias || (flags & SSM2D_DELTA_SOFTPLUS)) {
+        // the scan's step size, prepared once (an HBM-bound pass; done inside
+        // the scan it would cost every state group of every channel the
+        // softplus of its cells)
+        void *buf = nullptr;
+        const int st = get_aux_ws(dev, stream, 0, static_cast<size_t>(total) * sizeof(T) + 256, &buf);
+        if (st != SSM2D_OK) return st;
+        delta_prep_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, static_cast<T *>(buf), total, H * W,
+                                                                static_cast<int>(d_inner),
+                                                                (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+        delta = static_cast<const T *>(buf);
+    }
     const int vf = (flags & SSM2D_VERTICAL_FIRST) ? kModeVFirst : 0;
     const int acc = (flags & SSM2D_ACCUMULATE) ? kModeAccumulate : 0;
     if (!(flags & SSM2D_FOUR_WAY)) {
-        const int mode = ((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc;
+        const int mode = ((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc | (z ? kModeGate : 0);
         return launch(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, mode, (flags & SSM2D_FLIP_H) ? 1 : 0,
-                      dev, stream);
+                      dev, stream, z);
     }
     // Four scans, one per starting corner, summed into y in stream order; the
     // skip term is added once, by the first.
@@ -303,6 +384,12 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         const int st = launch(x, delta, A, B, C, q == 0 ? D : nullptr, y, batch, d_inner, d_state, H, W, mode,
                               q & 1, dev, stream);
         if (st != SSM2D_OK) return st;
+    }
+    if (z) {
+        // the gate is linear in y: applied once to the sum
+        gate_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(y, z, total);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
     }
     return SSM2D_OK;
 }
@@ -424,6 +511,22 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
     return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream);
 }
 
+int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                         const float *D, const float *z, const float *delta_bias, float *y, int64_t batch,
+                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+{
+    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z, delta_bias);
+}
+
+int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
+                              const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
+                              uint16_t *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                              uint32_t flags, void *stream)
+{
+    return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z,
+                              delta_bias);
+}
+
 int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B, const float *C,
                    const float *D, const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
                    float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, void *stream)
@@ -451,7 +554,7 @@ const char *ssm2d_status_string(int status)
     case SSM2D_ERR_HIP: return "HIP runtime error";
     case SSM2D_ERR_NOMEM: return "workspace allocation failed";
     case SSM2D_ERR_DEVICE_TIMEOUT: return "kernel timed out waiting for a neighbouring strip's carries";
-    case SSM2D_ERR_BAD_FLAGS: return "unknown flag bits, or SSM2D_FOUR_WAY with a flip flag";
+    case SSM2D_ERR_BAD_FLAGS: return "unknown flag bits, SSM2D_FOUR_WAY with a flip flag, or a gate with SSM2D_ACCUMULATE";
     default: return "unknown status";
     }
 }

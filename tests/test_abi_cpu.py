@@ -89,16 +89,45 @@ def _call_ex(lib, dims, flags, ptrs=None, bf16=False):
 @pytest.mark.parametrize("bf16", [False, True])
 def test_ex_flag_validation(lib, bf16):
     # unknown bits, and a four-way sum with a flip, are refused before anything else
-    for flags in (32, 1 << 31, pkg.FOUR_WAY | pkg.FLIP_H, pkg.FOUR_WAY | pkg.FLIP_W):
+    for flags in (64, 1 << 31, pkg.FOUR_WAY | pkg.FLIP_H, pkg.FOUR_WAY | pkg.FLIP_W):
         assert _call_ex(lib, [1, 2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_FLAGS, flags
         assert _call_ex(lib, [-1, 2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_FLAGS, flags
     # valid flags reach the usual checks
-    for flags in range(32):
+    for flags in range(64):
         if flags & pkg.FOUR_WAY and flags & (pkg.FLIP_H | pkg.FLIP_W):
             continue
         assert _call_ex(lib, [1, -2, 3, 4, 5], flags, bf16=bf16) == pkg.ERR_BAD_DIM, flags
         assert _call_ex(lib, [1, 2, 3, 0, 5], flags, ptrs=[0] * 7, bf16=bf16) == pkg.OK, flags
         assert _call_ex(lib, [1, 2, 65, 4, 5], flags, bf16=bf16) == pkg.ERR_UNSUPPORTED, flags
+
+
+def _call_mamba(lib, dims, flags, ptrs=None, bf16=False):
+    ptrs = ptrs if ptrs is not None else [FAKE] * 9
+    fn = lib.ssm2d_scan_fwd_mamba_bf16 if bf16 else lib.ssm2d_scan_fwd_mamba
+    return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_mamba_entry_validation(lib, bf16):
+    # a gate cannot be combined with accumulation; unknown bits are refused
+    assert _call_mamba(lib, [1, 2, 3, 4, 5], pkg.ACCUMULATE, bf16=bf16) == pkg.ERR_BAD_FLAGS
+    assert _call_mamba(lib, [1, 2, 3, 4, 5], 64, bf16=bf16) == pkg.ERR_BAD_FLAGS
+    ptrs = [FAKE] * 9
+    ptrs[6] = 0  # no gate: accumulation is fine
+    assert _call_mamba(lib, [1, 2, 3, 4, 5], pkg.ACCUMULATE, ptrs, bf16=bf16) not in (pkg.ERR_BAD_FLAGS, pkg.ERR_NULLPTR)
+    # z, delta_bias and D are optional; the others are not
+    ptrs = [FAKE] * 9
+    ptrs[5] = ptrs[6] = ptrs[7] = 0
+    assert _call_mamba(lib, [1, 2, 3, 4, 5], pkg.DELTA_SOFTPLUS, ptrs, bf16=bf16) not in (pkg.ERR_NULLPTR,
+                                                                                         pkg.ERR_MISALIGNED)
+    for k in (0, 1, 2, 3, 4, 8):
+        ptrs = [FAKE] * 9
+        ptrs[k] = 0
+        assert _call_mamba(lib, [1, 2, 3, 4, 5], 0, ptrs, bf16=bf16) == pkg.ERR_NULLPTR, k
+    for k in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[k] = FAKE + 4
+        assert _call_mamba(lib, [1, 2, 3, 4, 5], 0, ptrs, bf16=bf16) == pkg.ERR_MISALIGNED, k
 
 
 def test_ex_null_and_misaligned(lib):

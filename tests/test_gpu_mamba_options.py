@@ -1,0 +1,116 @@
+"""GPU parity of the Mamba-option entry points (ssm2d_scan_fwd_mamba / _bf16):
+step size delta + delta_bias[d] through softplus, and SiLU(z) gating, against
+the oracle's fwd_mamba on the same seeded inputs. Bars as for the forward
+scan: 1e-4 (1 + |y_ref|) for fp32 and 2e-2 (1 + |y_ref|) for bf16; for the
+bf16 step size the oracle rounds softplus(delta + bias) to bf16 like the
+library (computed in fp32, rounded to nearest even)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_ssm2d_amd as pkg
+from selective_state_space_ssm2d_amd.inputs import bf16_bits_from_f32, f32_from_bf16_bits, make_random_inputs
+from test_gpu_parity import KEYS, _say, _seed, _setup, as_f64, check, to_dev  # noqa: F401 (_setup: fixture)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _tensor(a, dtype):
+    """Seeded fp32 draws as device tensors, and the exact values the kernel sees."""
+    a = np.asarray(a, dtype=np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits_from_f32(a)
+        return f32_from_bf16_bits(bits).astype(np.float64), torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return a.astype(np.float64), torch.from_numpy(a).cuda()
+
+
+def _round_like(dtype):
+    if dtype == "bf16":
+        return lambda v: f32_from_bf16_bits(bf16_bits_from_f32(np.asarray(v, dtype=np.float32))).astype(np.float64)
+    return lambda v: np.asarray(v, dtype=np.float32).astype(np.float64)
+
+
+SHAPES = [(1, 16, 16, 19, 64), (2, 9, 8, 11, 23), (1, 8, 4, 1, 30), (1, 5, 16, 27, 1)]
+
+
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)), ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_gate(shape, dtype, d):
+    fh, fw, vf = d
+    _say(f"gate {shape} {dtype} {d}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 21, dtype=dtype)
+    z, z_dev = _tensor(np.random.default_rng(_seed(shape)).standard_normal(t["x"].shape) * 2, dtype)
+    args = to_dev(t, dtype)
+    y = pkg.scan_fwd_mamba(*args, z=z_dev, flip_h=fh, flip_w=fw, vertical_first=vf)
+    pkg.sync_check()
+    ref = oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, flip_h=fh, flip_w=fw, vertical_first=vf)
+    check(as_f64(y), ref, dtype, f"gate {shape} {d}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+@pytest.mark.parametrize("opts", [dict(bias=True, sp=True), dict(bias=False, sp=True), dict(bias=True, sp=False)],
+                         ids=str)
+def test_step_size(shape, dtype, opts):
+    """Raw step sizes of either sign, with the per-channel bias and softplus."""
+    _say(f"step size {opts} {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 22, dtype=dtype)
+    rng = np.random.default_rng(_seed(shape) + 23)
+    raw, raw_dev = _tensor(rng.standard_normal(t["x"].shape) - 0.5, dtype)
+    bias = (rng.standard_normal(shape[1]) * 0.5).astype(np.float32) if opts["bias"] else None
+    if not opts["sp"]:
+        # no softplus: keep the step positive (a negative step makes Abar > 1
+        # and the recurrences expanding, outside what the bars are derived for)
+        raw, raw_dev = _tensor(np.abs(raw) + 0.05, dtype)
+        bias = None if bias is None else np.abs(bias)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    y = pkg.scan_fwd_mamba(*args, delta_bias=None if bias is None else torch.from_numpy(bias).cuda(),
+                           delta_softplus=opts["sp"])
+    pkg.sync_check()
+    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], delta_bias=bias, delta_softplus=opts["sp"],
+                           delta_round=_round_like(dtype))
+    check(as_f64(y), ref, dtype, f"step size {opts} {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_everything_together(dtype, monkeypatch):
+    """Bias, softplus, gate and the four-corner sum, no skip term; then a
+    gated single scan across workgroup chains."""
+    shape = (1, 16, 16, 21, 44)
+    t = make_random_inputs(*shape, seed=24, dtype=dtype)
+    rng = np.random.default_rng(25)
+    raw, raw_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    z, z_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    bias = (rng.standard_normal(shape[1]) * 0.3).astype(np.float32)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    args[5] = None
+    y = pkg.scan_fwd_mamba(*args, z=z_dev, delta_bias=torch.from_numpy(bias).cuda(), delta_softplus=True,
+                           four_way=True)
+    pkg.sync_check()
+    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], None, z=z, delta_bias=bias, delta_softplus=True,
+                           delta_round=_round_like(dtype), four_way=True)
+    got = as_f64(y)
+    if dtype == "bf16":
+        # the four-corner sum is rounded to bf16 after each scan: bar against the terms
+        terms = [oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], None, delta_bias=bias, delta_softplus=True,
+                                  delta_round=_round_like(dtype), flip_h=fh, flip_w=fw)
+                 for fh, fw in ((False, False), (True, False), (False, True), (True, True))]
+        scale = 1.0 + np.abs(oracle.silu(z)) * sum(np.abs(v) for v in terms)
+        err = float(np.max(np.abs(got - ref) / scale))
+        _say(f"  everything bf16: {err:.3e}")
+        assert err <= 2e-2
+    else:
+        check(got, ref, dtype, "everything together")
+    monkeypatch.setenv("SSM2D_WAVES", "2")
+    shape = (1, 8, 16, 17, 60)
+    t = make_random_inputs(*shape, seed=26, dtype=dtype)
+    z, z_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, flip_w=True)
+    pkg.sync_check()
+    check(as_f64(y), oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, flip_w=True), dtype, "gated chains")

@@ -519,3 +519,30 @@ def test_pins_catch_planted_mistakes(tmp_path):
             except (AssertionError, RuntimeError):
                 caught.append(pin.__name__)
         assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# ---------------------------------------------------------------- Mamba-op options
+def test_mamba_options_pins(oracle_lib):
+    """softplus and SiLU against their definitions at points the mathematics
+    fixes; step-size bias and softplus that cancel reproduce the plain scan;
+    gating is elementwise (and zero where z = 0)."""
+    assert oracle.softplus(0.0) == np.log(2.0)
+    assert abs(oracle.softplus(50.0) - 50.0) < 1e-15 and oracle.softplus(-50.0) == np.log1p(np.exp(-50.0))
+    assert abs(oracle.softplus(np.log(np.expm1(0.7))) - 0.7) < 1e-15
+    assert oracle.silu(0.0) == 0.0 and abs(oracle.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 5, 6, 40)
+    y = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib)
+    bias = np.array([0.3, -0.2, 0.1])
+    # softplus(v + bias) with v = log(expm1(dt)) - bias is dt again
+    v = np.log(np.expm1(dt)) - bias[None, :, None, None]
+    y2 = oracle.fwd_mamba(x, v, A, B, C, D, delta_bias=bias, delta_softplus=True, lib=oracle_lib)
+    _close(y2, y, 1e-12, "bias + softplus that cancel")
+    z = np.random.default_rng(40).standard_normal(x.shape)
+    z[0, 1, 2, :] = 0.0
+    yg = oracle.fwd_mamba(x, dt, A, B, C, D, z=z, lib=oracle_lib)
+    _close(yg, y * z / (1 + np.exp(-z)), 1e-15, "gating")
+    assert np.all(yg[0, 1, 2, :] == 0.0)
+    # the four-corner sum is gated as a whole (the gate is linear in y)
+    y4 = oracle.fwd_mamba(x, dt, A, B, C, D, z=z, four_way=True, lib=oracle_lib)
+    _close(y4, oracle.fwd(x, dt, A, B, C, D, four_way=True, lib=oracle_lib) * oracle.silu(z), 1e-14, "gated four-way")
