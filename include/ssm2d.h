@@ -146,23 +146,34 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
  *              in a library workspace of batch*d_inner*H*W elements per
  *              (device, stream); the scan then runs on delta';
  *   gate       y = (sum_n C h + D x) * SiLU(z), SiLU(z) = z / (1 + e^-z), z
- *              shaped like x in x's type (z may be NULL: no gate).
+ *              shaped like x in x's type (z may be NULL: no gate);
+ *   carried    h_init (may be NULL: zeros): per (b, d, n) and column, the
+ *   states     vertical state before the first row in scan order (h, or v for
+ *              SSM2D_VERTICAL_FIRST); h_last (may be NULL): the same state
+ *              after the last row; both float32 [batch][d_inner][d_state][W].
+ *              A map scanned in bands of rows, each band passed the previous
+ *              band's h_last as h_init, gives the scan of the whole map (Mamba's
+ *              last-state return, for maps processed in pieces).
  * Arguments otherwise as for ssm2d_scan_fwd_ex, with the same flags (and
  * SSM2D_DELTA_SOFTPLUS). The gate applies to this call's result: with
  * SSM2D_FOUR_WAY it multiplies the four-corner sum (one more pass over y);
- * a gate with SSM2D_ACCUMULATE -> SSM2D_ERR_BAD_FLAGS. Gated single scans use
- * 8 state groups and 4-column strips, with the gate fused into the store. */
+ * a gate with SSM2D_ACCUMULATE, or carried states with SSM2D_FOUR_WAY
+ * -> SSM2D_ERR_BAD_FLAGS. Gated single scans use 8 state groups and 4-column
+ * strips, with the gate fused into the store. h_last is written only by a
+ * kernel that did not time out (see ssm2d_sync_check). */
 int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B,
                          const float *C, const float *D, const float *z, const float *delta_bias,
-                         float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-                         int64_t W, uint32_t flags, void *stream);
+                         const float *h_init, float *h_last, float *y, int64_t batch,
+                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
+                         void *stream);
 
-/* bf16 variant: x, delta, B, C, z, y bfloat16 bits; A, D, delta_bias float32. */
+/* bf16 variant: x, delta, B, C, z, y bfloat16 bits; A, D, delta_bias, h_init,
+ * h_last float32. */
 int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
                               const uint16_t *B, const uint16_t *C, const float *D,
-                              const uint16_t *z, const float *delta_bias, uint16_t *y,
-                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-                              int64_t W, uint32_t flags, void *stream);
+                              const uint16_t *z, const float *delta_bias, const float *h_init,
+                              float *h_last, uint16_t *y, int64_t batch, int64_t d_inner,
+                              int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
 
 /* ---- Backward pass -------------------------------------------------------
  *

@@ -68,8 +68,14 @@ static void scan_state_map(const double *abar, const double *bx, double *h,
  *           h[i,j] = Abar[i,j] h[i,j-1] + v[i,j]  (row scan of the results)
  * ("i-1", "j-1" meaning the previous cell in scan order). tmp: H*W scratch. */
 static void scan_state_map_dir(const double *abar, const double *bx, double *h, double *tmp,
-                               int64_t H, int64_t W, int flip_h, int flip_w, int vfirst)
+                               int64_t H, int64_t W, int flip_h, int flip_w, int vfirst,
+                               const double *h0, double *hl)
 {
+    /* h0 (may be NULL: zeros): the carried vertical state before the first
+     * row in scan order, by column (h for the horizontal-first order, v for
+     * vertical-first); hl (may be NULL): the same state after the last row.
+     * Scanning a map in bands of rows, each band's h0 the previous band's hl,
+     * gives the scan of the whole map. */
     for (int64_t si = 0; si < H; ++si) {
         const int64_t i = flip_h ? H - 1 - si : si;      /* row in scan order */
         const int64_t ip = flip_h ? i + 1 : i - 1;        /* previous row in scan order */
@@ -81,12 +87,12 @@ static void scan_state_map_dir(const double *abar, const double *bx, double *h, 
                 tmp[i * W + j] = carry;
             }
             for (int64_t j = 0; j < W; ++j) {
-                const double prev = (si > 0) ? h[ip * W + j] : 0.0;
+                const double prev = (si > 0) ? h[ip * W + j] : (h0 ? h0[j] : 0.0);
                 h[i * W + j] = abar[i * W + j] * prev + tmp[i * W + j];
             }
         } else {
             for (int64_t j = 0; j < W; ++j) {             /* column recurrence first */
-                const double prev = (si > 0) ? tmp[ip * W + j] : 0.0;
+                const double prev = (si > 0) ? tmp[ip * W + j] : (h0 ? h0[j] : 0.0);
                 tmp[i * W + j] = abar[i * W + j] * prev + bx[i * W + j];
             }
             double carry = 0.0;
@@ -96,6 +102,10 @@ static void scan_state_map_dir(const double *abar, const double *bx, double *h, 
                 h[i * W + j] = carry;
             }
         }
+    }
+    if (hl) {
+        const int64_t last = flip_h ? 0 : H - 1;  /* last row in scan order */
+        for (int64_t j = 0; j < W; ++j) hl[j] = vfirst ? tmp[last * W + j] : h[last * W + j];
     }
 }
 
@@ -114,7 +124,7 @@ int oracle_ssm2d_states_ex_f64(const double *abar, const double *bx, double *h,
     double *tmp = (double *)malloc((size_t)(H * W) * sizeof(double));
     if (!tmp) return 6;
     scan_state_map_dir(abar, bx, h, tmp, H, W, (flags & ORACLE_FLIP_H) != 0,
-                       (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0);
+                       (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0, NULL, NULL);
     free(tmp);
     return 0;
 }
@@ -137,15 +147,18 @@ int oracle_ssm2d_states_f64(const double *abar, const double *bx, double *h,
 static int forward_one_map(const double *x, const double *delta, const double *A,
                            const double *B, const double *C, const double *D,
                            double *y_map, int64_t b, int64_t d, int64_t d_inner,
-                           int64_t d_state, int64_t H, int64_t W, int flags)
+                           int64_t d_state, int64_t H, int64_t W, int flags,
+                           const double *h0m, double *hlm)
 {
+    /* h0m, hlm (may be NULL): carried vertical states [d_state][W] of this map */
+    const int carries = (h0m != NULL) || (hlm != NULL);
     const int64_t L = H * W;
     const double *xm = x + (b * d_inner + d) * L;
     const double *dm = delta + (b * d_inner + d) * L;
     double *abar = (double *)malloc((size_t)L * sizeof(double));
     double *bx = (double *)malloc((size_t)L * sizeof(double));
     double *h = (double *)malloc((size_t)L * sizeof(double));
-    double *hh_row = (double *)malloc((size_t)(flags ? L : W) * sizeof(double));
+    double *hh_row = (double *)malloc((size_t)((flags || carries) ? L : W) * sizeof(double));
     if (!abar || !bx || !h || !hh_row) {
         free(abar); free(bx); free(h); free(hh_row);
         return 6;
@@ -159,9 +172,10 @@ static int forward_one_map(const double *x, const double *delta, const double *A
             abar[p] = exp(dm[p] * a);
             bx[p] = dm[p] * Bn[p] * xm[p];
         }
-        if (flags == 0) scan_state_map(abar, bx, h, hh_row, H, W);
+        if (flags == 0 && !carries) scan_state_map(abar, bx, h, hh_row, H, W);
         else scan_state_map_dir(abar, bx, h, hh_row, H, W, (flags & ORACLE_FLIP_H) != 0,
-                                (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0);
+                                (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0,
+                                h0m ? h0m + n * W : NULL, hlm ? hlm + n * W : NULL);
         for (int64_t p = 0; p < L; ++p) y_map[p] += Cn[p] * h[p];
     }
     for (int64_t p = 0; p < L; ++p) y_map[p] += D[d] * xm[p];
@@ -180,7 +194,7 @@ static int forward_one_map(const double *x, const double *delta, const double *A
 static int fwd_maps(const double *x, const double *delta, const double *A, const double *B,
                     const double *C, const double *D, double *y, int64_t batch, int64_t d_inner,
                     int64_t d_state, int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
-                    int nthreads, int flags)
+                    int nthreads, int flags, const double *h0, double *hl)
 {
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
     const int64_t total = batch * d_inner;
@@ -199,7 +213,8 @@ static int fwd_maps(const double *x, const double *delta, const double *A, const
     for (int64_t k = 0; k < n_maps; ++k) {
         const int64_t m = maps ? maps[k] : k;
         int s = forward_one_map(x, delta, A, B, C, D, y + k * H * W, m / d_inner,
-                                m % d_inner, d_inner, d_state, H, W, flags);
+                                m % d_inner, d_inner, d_state, H, W, flags,
+                                h0 ? h0 + m * d_state * W : NULL, hl ? hl + m * d_state * W : NULL);
         if (s != 0) {
 #pragma omp atomic write
             status = s;
@@ -215,7 +230,7 @@ int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double
                               int nthreads)
 {
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
-                    nthreads, 0);
+                    nthreads, 0, NULL, NULL);
 }
 
 /* The forward pass in the direction / order `flags` selects (ORACLE_FLIP_H,
@@ -228,7 +243,22 @@ int oracle_ssm2d_fwd_ex_f64(const double *x, const double *delta, const double *
 {
     if (flags < 0 || flags > 7) return 2;
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
-                    nthreads, flags);
+                    nthreads, flags, NULL, NULL);
+}
+
+/* The forward pass with carried vertical states (all maps): h0 (may be NULL)
+ * holds, per (b, d, n) and column, the state before the first row in scan
+ * order, hl (may be NULL) receives the state after the last row; both
+ * [batch][d_inner][d_state][W]. Otherwise as oracle_ssm2d_fwd_ex_f64. */
+int oracle_ssm2d_fwd_carry_f64(const double *x, const double *delta, const double *A,
+                               const double *B, const double *C, const double *D,
+                               double *y, const double *h0, double *hl, int64_t batch,
+                               int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                               int nthreads, int flags)
+{
+    if (flags < 0 || flags > 7) return 2;
+    return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, NULL, 0,
+                    nthreads, flags, h0, hl);
 }
 
 /* ---------------------------------------------------------------- backward

@@ -62,7 +62,7 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_fwd_mamba", "ssm2d_scan_fwd_mamba_bf16"):
         f = getattr(lib, name)
-        f.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_uint32, vp]
+        f.argtypes = [vp] * 11 + [i64] * 5 + [ctypes.c_uint32, vp]
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_bwd", "ssm2d_scan_bwd_bf16"):
         f = getattr(lib, name)
@@ -206,10 +206,13 @@ def scan_fwd_ex(x, delta, A, B, C, D=None, y=None, *, flip_h=False, flip_w=False
 
 
 def scan_fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, y=None, *, delta_softplus=False,
-                   flip_h=False, flip_w=False, vertical_first=False, four_way=False, accumulate=False, stream=None):
+                   h_init=None, h_last=None, return_last_state=False, flip_h=False, flip_w=False,
+                   vertical_first=False, four_way=False, accumulate=False, stream=None):
     """The 2D scan with Mamba's operator options (include/ssm2d.h,
     ssm2d_scan_fwd_mamba): step size delta + delta_bias[d], optionally through
-    softplus, and the output gated by SiLU(z)."""
+    softplus, the output gated by SiLU(z), and carried vertical states
+    (h_init in, h_last out; float32 [batch, d_inner, d_state, W]). With
+    return_last_state, returns (y, h_last)."""
     import torch
 
     lib = load_library()
@@ -221,13 +224,20 @@ def scan_fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, y=None, *
     if delta_bias is not None and (delta_bias.shape != (dims[1],) or delta_bias.dtype != torch.float32
                                    or delta_bias.device != x.device):
         raise ValueError("delta_bias must be float32 [d_inner] on x's device")
+    cshape = (dims[0], dims[1], dims[2], dims[4])
+    if return_last_state and h_last is None:
+        h_last = torch.empty(cshape, dtype=torch.float32, device=x.device)
+    for name, t in (("h_init", h_init), ("h_last", h_last)):
+        if t is not None and (t.shape != cshape or t.dtype != torch.float32 or t.device != x.device
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [batch, d_inner, d_state, W] on x's device")
     flags = ((FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
              | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0)
              | (DELTA_SOFTPLUS if delta_softplus else 0))
     fn = lib.ssm2d_scan_fwd_mamba if x.dtype == torch.float32 else lib.ssm2d_scan_fwd_mamba_bf16
-    _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, y)]
+    _call(fn, lib, x.device, [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, h_init, h_last, y)]
           + [*dims, flags, _stream_handle(stream)])
-    return y
+    return (y, h_last) if return_last_state else y
 
 
 def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None):

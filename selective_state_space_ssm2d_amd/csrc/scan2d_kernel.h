@@ -120,6 +120,10 @@ struct Params {
     float *dBp, *dCp, *dA, *dD;
     long part_stride;                  // floats per channel block
     const void *z;                     // gate input, shaped like y (kModeGate)
+    // carried vertical states, fp32 [batch][d_inner][d_state][W] (may be
+    // null): before the first row in scan order, and after the last row
+    const float *h_init;
+    float *h_last;
     unsigned int epoch;
     long long spin_limit;
 };
@@ -810,6 +814,29 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         for (int c = 0; c < K; ++c)
 #pragma unroll
             for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
+        // Carried vertical state (a band of rows continuing a scan): the
+        // register state of the strip's columns starts from h_init and is
+        // written to h_last after the last row.
+        auto carry_index = [&](const int c, const int k, long &idx) -> bool {
+            const int n = g * NPL + k, u = j0 + c;
+            idx = ((static_cast<long>(b) * p.d_inner + d) * p.d_state + n) * W + (FW ? W - 1 - u : u);
+            return d_ok && n < p.d_state && u < W;
+        };
+        if constexpr (!STATES && !BWD) {
+            if (p.h_init) {
+#pragma unroll
+                for (int c = 0; c < K; ++c)
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        long idx;
+                        if (carry_index(c, k, idx)) hv[c][k] = p.h_init[idx];
+                    }
+#pragma unroll
+                for (int c = 0; c < K; ++c)
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(hv[c][k]));  // loaded before the row loop
+            }
+        }
 
         // Operands of row t live at row_base(t) + roff(packet row).
         const int slot_mask = p.coop_slots - 1;
@@ -1264,6 +1291,17 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             if (has_right) strip_rows(std::false_type{}, std::true_type{});
             else strip_rows(std::false_type{}, std::false_type{});
         }
+        if constexpr (!STATES && !BWD) {
+            if (p.h_last && !timed_out) {
+#pragma unroll
+                for (int c = 0; c < K; ++c)
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        long idx;
+                        if (carry_index(c, k, idx)) p.h_last[idx] = hv[c][k];
+                    }
+            }
+        }
         if constexpr (BWD) {
             // this strip's parts of dA (every state of the lane) and dD (one
             // lane per channel)
@@ -1307,6 +1345,8 @@ struct Plan {
     int flip_h;      // rows bottom to top
     const BwdArgs *bw;  // stored-state and backward passes
     const void *z;   // gate input (kModeGate)
+    const float *h_init;  // carried vertical states in / out (may be null)
+    float *h_last;
 };
 
 int env_int(const char *name, int dflt);
@@ -1404,6 +1444,8 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
         prm.part_stride = pl.bw->part_stride;
     }
     prm.z = pl.z;
+    prm.h_init = pl.h_init;
+    prm.h_last = pl.h_last;
     prm.coop_slots = pl.coop_slots > 0 ? pl.coop_slots : 2;
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;

@@ -287,11 +287,13 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
-           const T *z = nullptr)
+           const T *z = nullptr, const float *h_init = nullptr, float *h_last = nullptr)
 {
     Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
     pl.flip_h = flip_h;
     pl.z = z;
+    pl.h_init = h_init;
+    pl.h_last = h_last;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
@@ -334,11 +336,13 @@ constexpr unsigned kKnownFlags = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FI
 template <typename T>
 int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
-             void *stream, const T *z = nullptr, const float *delta_bias = nullptr)
+             void *stream, const T *z = nullptr, const float *delta_bias = nullptr, const float *h_init = nullptr,
+             float *h_last = nullptr)
 {
     if ((flags & ~kKnownFlags) != 0) return SSM2D_ERR_BAD_FLAGS;
     if ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))) return SSM2D_ERR_BAD_FLAGS;
     if (z && (flags & SSM2D_ACCUMULATE)) return SSM2D_ERR_BAD_FLAGS;
+    if ((h_init || h_last) && (flags & SSM2D_FOUR_WAY)) return SSM2D_ERR_BAD_FLAGS;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
     if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
@@ -347,7 +351,8 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         return SSM2D_ERR_UNSUPPORTED;
     if (!x || !delta || (!D && !extended) || !y || (d_state > 0 && (!A || !B || !C))) return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) || misaligned(z) ||
-        misaligned(delta_bias) || (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
+        misaligned(delta_bias) || misaligned(h_init) || misaligned(h_last) ||
+        (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
         return SSM2D_ERR_MISALIGNED;
 
     int dev = 0;
@@ -375,7 +380,7 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (!(flags & SSM2D_FOUR_WAY)) {
         const int mode = ((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc | (z ? kModeGate : 0);
         return launch(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, mode, (flags & SSM2D_FLIP_H) ? 1 : 0,
-                      dev, stream, z);
+                      dev, stream, z, h_init, h_last);
     }
     // Four scans, one per starting corner, summed into y in stream order; the
     // skip term is added once, by the first.
@@ -512,19 +517,21 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
 }
 
 int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
-                         const float *D, const float *z, const float *delta_bias, float *y, int64_t batch,
-                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+                         const float *D, const float *z, const float *delta_bias, const float *h_init,
+                         float *h_last, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                         int64_t W, uint32_t flags, void *stream)
 {
-    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z, delta_bias);
+    return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z, delta_bias,
+                           h_init, h_last);
 }
 
 int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
                               const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
-                              uint16_t *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                              uint32_t flags, void *stream)
+                              const float *h_init, float *h_last, uint16_t *y, int64_t batch, int64_t d_inner,
+                              int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
     return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z,
-                              delta_bias);
+                              delta_bias, h_init, h_last);
 }
 
 int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B, const float *C,
@@ -554,7 +561,8 @@ const char *ssm2d_status_string(int status)
     case SSM2D_ERR_HIP: return "HIP runtime error";
     case SSM2D_ERR_NOMEM: return "workspace allocation failed";
     case SSM2D_ERR_DEVICE_TIMEOUT: return "kernel timed out waiting for a neighbouring strip's carries";
-    case SSM2D_ERR_BAD_FLAGS: return "unknown flag bits, SSM2D_FOUR_WAY with a flip flag, or a gate with SSM2D_ACCUMULATE";
+    case SSM2D_ERR_BAD_FLAGS:
+        return "unknown flag bits, SSM2D_FOUR_WAY with a flip flag or carried states, or a gate with SSM2D_ACCUMULATE";
     default: return "unknown status";
     }
 }

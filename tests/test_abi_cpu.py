@@ -103,6 +103,7 @@ def test_ex_flag_validation(lib, bf16):
 
 def _call_mamba(lib, dims, flags, ptrs=None, bf16=False):
     ptrs = ptrs if ptrs is not None else [FAKE] * 9
+    ptrs = ptrs[:8] + [0, 0] + ptrs[8:]  # no carried states
     fn = lib.ssm2d_scan_fwd_mamba_bf16 if bf16 else lib.ssm2d_scan_fwd_mamba
     return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
 
@@ -128,6 +129,14 @@ def test_mamba_entry_validation(lib, bf16):
         ptrs = [FAKE] * 9
         ptrs[k] = FAKE + 4
         assert _call_mamba(lib, [1, 2, 3, 4, 5], 0, ptrs, bf16=bf16) == pkg.ERR_MISALIGNED, k
+    # carried states: optional, aligned, not with the four-corner sum
+    fn = lib.ssm2d_scan_fwd_mamba_bf16 if bf16 else lib.ssm2d_scan_fwd_mamba
+    base = [FAKE] * 6 + [0, 0]
+    call = lambda hi, hl, flags: fn(*(ctypes.c_void_p(p) for p in base + [hi, hl, FAKE]), 1, 2, 3, 4, 5, flags, None)
+    assert call(FAKE, FAKE, pkg.FOUR_WAY) == pkg.ERR_BAD_FLAGS
+    assert call(FAKE + 4, 0, 0) == pkg.ERR_MISALIGNED and call(0, FAKE + 4, 0) == pkg.ERR_MISALIGNED
+    assert call(FAKE, FAKE, pkg.FLIP_H | pkg.VERTICAL_FIRST) not in (pkg.ERR_BAD_FLAGS, pkg.ERR_MISALIGNED,
+                                                                     pkg.ERR_NULLPTR)
 
 
 def test_ex_null_and_misaligned(lib):

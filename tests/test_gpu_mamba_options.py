@@ -114,3 +114,45 @@ def test_everything_together(dtype, monkeypatch):
     y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, flip_w=True)
     pkg.sync_check()
     check(as_f64(y), oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, flip_w=True), dtype, "gated chains")
+
+
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)), ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [((1, 16, 16, 9, 64), None), ((2, 9, 8, 7, 23), None), ((1, 8, 16, 13, 90), "2")],
+                         ids=str)
+def test_carried_states(case, dtype, d, monkeypatch):
+    """A seeded h_init and the returned h_last against the oracle, in every
+    direction and order (and across workgroup chains)."""
+    shape, waves = case
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    _say(f"carried states {shape} {dtype} {d} waves={waves}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 27, dtype=dtype)
+    b, di, n, H, W = shape
+    h0 = np.random.default_rng(_seed(shape) + 28).standard_normal((b, di, n, W)).astype(np.float32)
+    y, hl = pkg.scan_fwd_mamba(*to_dev(t, dtype), h_init=torch.from_numpy(h0).cuda(), return_last_state=True, **kw)
+    pkg.sync_check()
+    ref_y, ref_hl = oracle.fwd(*(t[k] for k in KEYS), h_init=h0, return_last=True, **kw)
+    check(as_f64(y), ref_y, dtype, f"carried y {shape} {d}")
+    check(hl.double().cpu().numpy(), ref_hl, "f32", f"h_last {shape} {d}")
+
+
+@pytest.mark.parametrize("vf", [False, True])
+def test_bands_equal_whole_map(vf):
+    """Two bands of rows with the carried state in between give the whole
+    map's scan (GPU against GPU, and the whole against the oracle)."""
+    t = make_random_inputs(1, 16, 16, 40, 64, seed=29)
+    args = to_dev(t, "f32")
+    y = pkg.scan_fwd_mamba(*args, vertical_first=vf)
+    band = lambda a, r: a[:, :, r].contiguous()
+    r1, r2 = slice(0, 17), slice(17, 40)
+    a1 = [band(args[0], r1), band(args[1], r1), args[2], band(args[3], r1), band(args[4], r1), args[5]]
+    a2 = [band(args[0], r2), band(args[1], r2), args[2], band(args[3], r2), band(args[4], r2), args[5]]
+    y1, h1 = pkg.scan_fwd_mamba(*a1, vertical_first=vf, return_last_state=True)
+    y2 = pkg.scan_fwd_mamba(*a2, vertical_first=vf, h_init=h1)
+    pkg.sync_check()
+    full = as_f64(y)
+    check(full, oracle.fwd(*(t[k] for k in KEYS), vertical_first=vf), "f32", "whole map")
+    check(np.concatenate([as_f64(y1), as_f64(y2)], axis=2), full, "f32", "bands vs whole")

@@ -546,3 +546,27 @@ def test_mamba_options_pins(oracle_lib):
     # the four-corner sum is gated as a whole (the gate is linear in y)
     y4 = oracle.fwd_mamba(x, dt, A, B, C, D, z=z, four_way=True, lib=oracle_lib)
     _close(y4, oracle.fwd(x, dt, A, B, C, D, four_way=True, lib=oracle_lib) * oracle.silu(z), 1e-14, "gated four-way")
+
+
+def test_carried_states_pin(oracle_lib):
+    """Scanning a map in two bands of rows, the second band starting from the
+    first band's last vertical state, gives the whole map's scan (every
+    direction and order); a band starting from zeros is the plain scan."""
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 9, 7, 41)
+    for fh in (False, True):
+        for fw in (False, True):
+            for vf in (False, True):
+                kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+                y = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, **kw)
+                rows = [slice(0, 4), slice(4, 9)]
+                if fh:
+                    rows = rows[::-1]  # scan order: bottom band first
+                band = lambda a, r: np.ascontiguousarray(a[:, :, r])
+                y1, h1 = oracle.fwd(band(x, rows[0]), band(dt, rows[0]), A, band(B, rows[0]), band(C, rows[0]), D,
+                                    lib=oracle_lib, return_last=True, **kw)
+                y2 = oracle.fwd(band(x, rows[1]), band(dt, rows[1]), A, band(B, rows[1]), band(C, rows[1]), D,
+                                lib=oracle_lib, h_init=h1, **kw)
+                _close(y1, y[:, :, rows[0]], 1e-13, f"first band {kw}")
+                _close(y2, y[:, :, rows[1]], 1e-12, f"second band from carried state {kw}")
+                y0 = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, h_init=np.zeros_like(h1), **kw)
+                _close(y0, y, 1e-15, f"zero carried state {kw}")
