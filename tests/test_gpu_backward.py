@@ -121,3 +121,15 @@ def test_backward_full_wsi_mil():
     dy, dy_dev = make_dy(t, wl.dtype, 10)
     got = run_bwd(t, wl.dtype, dy_dev)
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), wl.dtype, wl.batch * wl.H * wl.W, "wsi_mil")
+
+
+@pytest.mark.parametrize("name", ["vmamba_t_s1", "grid14", "gigapixel_wsi"])
+def test_backward_full_workloads(name):
+    """The other workloads at full size, in the launch configuration the
+    benchmark times: every gradient element against the oracle."""
+    wl = next(w for w in WORKLOADS if w.name == name)
+    _say(f"backward full size {name}")
+    t = make_inputs(wl, seed=0)
+    dy, dy_dev = make_dy(t, wl.dtype, 13)
+    got = run_bwd(t, wl.dtype, dy_dev)
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), wl.dtype, wl.batch * wl.H * wl.W, name)

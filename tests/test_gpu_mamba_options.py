@@ -156,3 +156,26 @@ def test_bands_equal_whole_map(vf):
     full = as_f64(y)
     check(full, oracle.fwd(*(t[k] for k in KEYS), vertical_first=vf), "f32", "whole map")
     check(np.concatenate([as_f64(y1), as_f64(y2)], axis=2), full, "f32", "bands vs whole")
+
+
+@pytest.mark.parametrize("name", ["vmamba_t_s1", "gigapixel_wsi"])
+def test_options_full_size_sampled(name):
+    """Full workload sizes with bias, softplus and the gate; sampled maps."""
+    from selective_state_space_ssm2d_amd.inputs import WORKLOADS, make_inputs
+
+    wl = next(w for w in WORKLOADS if w.name == name)
+    dtype = wl.dtype
+    t = make_inputs(wl, seed=0)
+    rng = np.random.default_rng(30)
+    raw, raw_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    z, z_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    bias = (rng.standard_normal(wl.d_inner) * 0.3).astype(np.float32)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    y = pkg.scan_fwd_mamba(*args, z=z_dev, delta_bias=torch.from_numpy(bias).cuda(), delta_softplus=True)
+    pkg.sync_check()
+    nmaps = wl.batch * wl.d_inner
+    maps = np.unique(np.array([0, 7, nmaps // 2, nmaps - 1]))
+    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], z=z, delta_bias=bias, delta_softplus=True,
+                           delta_round=_round_like(dtype), maps=maps)
+    check(as_f64(y).reshape(nmaps, wl.H, wl.W)[maps], ref, dtype, f"{name} options, maps {maps.tolist()}")
