@@ -75,11 +75,15 @@ constexpr int kModeBackward = 16;
 constexpr int kModeGate = 32;
 
 // Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
-// small (8 state groups, K * NPL <= 16, not the backward passes), else 8,
-// which leaves a wave 256 VGPRs.
+// small (8 state groups, K * NPL <= 16; K * NPL <= 8 for the stored-state
+// pass; never for the adjoint pass), else 8, which leaves a wave 256 VGPRs.
+// A chain cut into more workgroups than the chip holds at once waits for the
+// first ones to finish, so the larger workgroup pays even at lower occupancy.
 constexpr int max_waves(int K, int NPL, int G, int MODE = 0)
 {
-    return (G == 8 && K * NPL <= 16 && !(MODE & (kModeBackward | kModeStates))) ? 10 : 8;
+    if (MODE & kModeBackward) return 8;
+    if (MODE & kModeStates) return (G == 8 && K * NPL <= 8) ? 10 : 8;
+    return (G == 8 && K * NPL <= 16) ? 10 : 8;
 }
 constexpr int kCourierBatch = 4;               // rows a courier requests per poll
 constexpr int kMaxSlots = 16;                   // rows of a workgroup's shared row ring
