@@ -36,6 +36,11 @@
 //   * The sum over n: each lane holds K partial sums over its NPL states; two
 //     permlane swaps (32- and 16-lane) transpose-reduce them across the 4 state
 //     groups, leaving each lane with K/4 finished cells.
+// Modes (compile time, kMode* below) reuse this structure for the other scan
+// directions and orders (pages: papernotes 消融实验要点 and 局限与展望; juejin
+// part 七 section 4), for accumulating and gated outputs (Mamba's operator
+// options), and for the backward pass: a forward that stores every state and
+// an adjoint pass that scans right to left and bottom to top.
 // No MFMA: the scan is not a dense contraction.
 
 #pragma once

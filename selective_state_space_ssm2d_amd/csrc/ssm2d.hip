@@ -1,7 +1,9 @@
-// libssm2d: 2DMamba 2D selective scan (forward) for MI355X / gfx950 -- host
-// side: argument checks, the work plan, per-stream workspaces and the C ABI
-// declared in include/ssm2d.h. The kernel is in scan2d_kernel.h; its instances
-// are compiled in scan2d_{f32,bf16}_*.hip.
+// libssm2d: 2DMamba 2D selective scan for MI355X / gfx950 -- host side:
+// argument checks, the work plan, per-stream workspaces, the small elementwise
+// kernels around the scan (step-size preparation, gating of summed outputs,
+// the backward's zeroing and channel sums) and the C ABI declared in
+// include/ssm2d.h. The scan kernel is in scan2d_kernel.h; its instances are
+// compiled in scan2d_{f32,bf16}_*.hip.
 #include "scan2d_kernel.h"
 
 namespace ssm2d_impl {
