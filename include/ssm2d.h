@@ -236,6 +236,17 @@ int ssm2d_set_spin_limit(int64_t polls);
  * ("no error" if there was none). Static storage; never NULL. */
 const char *ssm2d_last_hip_error(void);
 
+/* Test and tuning hooks (environment variables, read at each call; integers).
+ * They change how the work is laid out, never what is computed:
+ *   SSM2D_GROUPS=4|8     state groups per wave (default: by shape)
+ *   SSM2D_STRIP=4|8      columns per strip (default: by shape)
+ *   SSM2D_WAVES=n        strips per workgroup (forces chains across workgroups)
+ *   SSM2D_COOP=0         per-wave input packets instead of the shared row ring
+ *   SSM2D_VECSTORE=0     cell-by-cell output stores
+ *   SSM2D_RING=n         depth of the global carry ring when the grid is co-resident
+ *   SSM2D_LDSRING=4|16|32  depth of the LDS carry rings
+ *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD */
+
 /* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
 int ssm2d_version(void);
 
