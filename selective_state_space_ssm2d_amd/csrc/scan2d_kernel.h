@@ -477,10 +477,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool STATES = (MODE & kModeStates) != 0;
     constexpr bool BWD = (MODE & kModeBackward) != 0;
     constexpr bool GATE = (MODE & kModeGate) != 0;
-    static_assert(!GATE || (!ACC && !STATES && !BWD && !COOP), "gate: plain output only");
+    static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
     static_assert(!BWD || (FW && !VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
-    static_assert(!STATES || (!FW && !VF && !ACC && !COOP), "stored states: forward order only");
-    static_assert(!(COOP && FW), "cooperative loads keep columns in memory order");
+    static_assert(!STATES || (!FW && !VF && !ACC), "stored states: forward order only");
     using Chunk = typename ChunkOf<T>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
     constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
@@ -1473,9 +1472,20 @@ template <typename T, int MODE>
 int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
                   int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream, int align)
 {
-    if (pl.G != 8 || pl.K != 4 || pl.coop_slots != 0) return SSM2D_ERR_UNSUPPORTED;
+    if (pl.G != 8 || pl.K != 4) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & (kModeStates | kModeBackward)) && !pl.bw) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & kModeGate) && !pl.z) return SSM2D_ERR_UNSUPPORTED;
+    if (pl.coop_slots != 0) {
+        // the shared row ring (tall maps cut into several workgroups per chain)
+        if constexpr (!(MODE & kModeBackward)) {
+            if (align != 4) return SSM2D_ERR_UNSUPPORTED;
+#define SSM2D_MODE_COOP(NN) \
+    if (pl.npl == NN) return run<T, 4, NN, 4, 8, true, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+            SSM2D_MODE_COOP(1) SSM2D_MODE_COOP(2) SSM2D_MODE_COOP(4) SSM2D_MODE_COOP(8)
+#undef SSM2D_MODE_COOP
+        }
+        return SSM2D_ERR_UNSUPPORTED;
+    }
     const int al = align == 4 ? 4 : 1;
 #define SSM2D_MODE_CASE(NN, AL)    \
     if (pl.npl == NN && al == AL) \

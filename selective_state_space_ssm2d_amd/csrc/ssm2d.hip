@@ -286,6 +286,25 @@ using namespace ssm2d_impl;
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }  // NULL passes
 
+// Cooperative loads (a shared ring of input rows per workgroup): 8-group
+// layouts with 4-column strips and 4-aligned rows, when a workgroup holds part
+// of a chain of a tall map (short maps do not repay the ring's start-up), if
+// the row ring fits; not for the adjoint pass.
+template <typename T>
+void choose_coop(Plan &pl, int64_t H, int align)
+{
+    pl.coop_slots = 0;
+    if ((pl.mode & kModeBackward) || pl.G != 8 || pl.K != 4 || align != 4 || pl.groups <= 1 || H < 128 ||
+        !env_int("SSM2D_COOP", 1))
+        return;
+    using Chunk = typename ChunkOf<T>::type;
+    const size_t nchunk = static_cast<size_t>(16 + 16 * pl.npl);
+    const size_t rings = static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * pl.npl * 4;
+    for (int slots = kMaxSlots; slots >= 8 && pl.coop_slots == 0; slots /= 2)
+        if (static_cast<size_t>(pl.s_local) * slots * (nchunk + 1) * sizeof(Chunk) + rings <= 144 * 1024)
+            pl.coop_slots = slots;
+}
+
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
@@ -299,17 +318,7 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
-    // Cooperative loads: 8-group layouts with 4-column strips and 4-aligned
-    // rows, when a workgroup holds part of a chain of a tall map (short maps
-    // do not repay the ring's start-up), if the row ring fits.
-    pl.coop_slots = 0;
-    if (mode == 0 && pl.G == 8 && pl.K == 4 && align == 4 && pl.groups > 1 && H >= 128 && env_int("SSM2D_COOP", 1)) {
-        using Chunk = typename ChunkOf<T>::type;
-        const size_t nchunk = static_cast<size_t>(16 + 16 * pl.npl);
-        const size_t rings = static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * pl.npl * 4;
-        for (int slots = kMaxSlots; slots >= 8 && pl.coop_slots == 0; slots /= 2)
-            if (static_cast<size_t>(pl.s_local) * slots * (nchunk + 1) * sizeof(Chunk) + rings <= 144 * 1024) pl.coop_slots = slots;
-    }
+    choose_coop<T>(pl, H, align);
 #define SSM2D_ARGS x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align
     constexpr int FW = kModeFlipW, VF = kModeVFirst, AC = kModeAccumulate;
     switch (mode) {
@@ -464,6 +473,7 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     // 1. the forward pass again, storing every state
     Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates);
     pf.bw = &bw;
+    choose_coop<T>(pf, H, align);
     if (pf.npl != npl || pf.n_dblk != n_dblk || pf.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     int st = dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
     if (st != SSM2D_OK) return st;

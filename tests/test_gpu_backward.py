@@ -133,3 +133,12 @@ def test_backward_full_workloads(name):
     dy, dy_dev = make_dy(t, wl.dtype, 13)
     got = run_bwd(t, wl.dtype, dy_dev)
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), wl.dtype, wl.batch * wl.H * wl.W, name)
+
+
+def test_backward_tall_map():
+    """A tall map: the stored-state pass uses the shared row ring."""
+    shape = (1, 16, 16, 160, 96)
+    t = make_random_inputs(*shape, seed=32)
+    dy, dy_dev = make_dy(t, "f32", 33)
+    got = run_bwd(t, "f32", dy_dev)
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 160 * 96, "tall map")

@@ -202,3 +202,30 @@ def test_full_size_sampled(case):
         check_sum(got, ref, terms, wl.dtype, f"{name} {kw} maps {maps.tolist()}")
     else:
         check(got, ref, wl.dtype, f"{name} {kw} maps {maps.tolist()}")
+
+
+TALL = [((1, 16, 16, 160, 96), None), ((1, 8, 8, 200, 36), "5")]
+
+
+@pytest.mark.parametrize("d", DIRS, ids=_name)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", TALL, ids=str)
+def test_directions_shared_row_ring(case, d, dtype, monkeypatch):
+    """Tall maps whose chains span workgroups use the workgroup's shared row
+    ring in every direction and order; also accumulated, and four-corner."""
+    shape, waves = case
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    _say(f"row ring {_name(d)} {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 3, dtype=dtype)
+    ref = ref_ex(t, **kw)
+    check(as_f64(run_ex(t, dtype, **kw)), ref, dtype, f"row ring {_name(d)} {shape}")
+    if dtype == "f32":
+        y0 = np.random.default_rng(6).standard_normal(t["x"].shape).astype(np.float32)
+        got = as_f64(run_ex(t, dtype, y=torch.from_numpy(y0).cuda(), accumulate=True, **kw))
+        check(got, y0 + ref, dtype, f"row ring accumulate {_name(d)} {shape}")
+        if not (fh or fw):
+            check(as_f64(run_ex(t, dtype, four_way=True, vertical_first=vf)),
+                  ref_ex(t, four_way=True, vertical_first=vf), dtype, f"row ring four-way {shape}")

@@ -179,3 +179,14 @@ def test_options_full_size_sampled(name):
     ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], z=z, delta_bias=bias, delta_softplus=True,
                            delta_round=_round_like(dtype), maps=maps)
     check(as_f64(y).reshape(nmaps, wl.H, wl.W)[maps], ref, dtype, f"{name} options, maps {maps.tolist()}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_shared_row_ring(dtype):
+    """A gated scan of a tall map (the shared row ring), right to left."""
+    shape = (1, 16, 16, 160, 96)
+    t = make_random_inputs(*shape, seed=31, dtype=dtype)
+    z, z_dev = _tensor(np.random.default_rng(31).standard_normal(t["x"].shape), dtype)
+    y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, flip_w=True)
+    pkg.sync_check()
+    check(as_f64(y), oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, flip_w=True), dtype, "gated row ring")
