@@ -21,12 +21,14 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     const int want_wg = 256;  // enough workgroups to cover the chip's CUs
     // Layout: 4 state groups per wave (16 channels) unless the map has more
     // than 4 states and too few (batch, channel-block) chains to give every CU
-    // a chain of its own. Then 8 groups (8 channels, half the states per lane)
-    // double the chains, halve the workgroups each chain spans, and put two
-    // compute waves on each SIMD. Above 32 states a lane of a 4-group layout
-    // would hold 16 states, more than its registers: 8 groups then too.
+    // two chains. Then 8 groups (8 channels, half the states per lane) double
+    // the chains, halve the workgroups each chain spans, and put two compute
+    // waves on each SIMD; with between one and two chains per CU they also
+    // even out the last round of workgroups (VMamba stage 1: 384 chains of
+    // 16 channels, 768 of 8). Above 32 states a lane of a 4-group layout would
+    // hold 16 states, more than its registers: 8 groups then too.
     const int64_t chains4 = batch * ((d_inner + 15) / 16);
-    int G = (d_state > 32 || (d_state > 4 && chains4 < want_wg)) ? 8 : 4;
+    int G = (d_state > 32 || (d_state > 4 && chains4 < 2 * want_wg)) ? 8 : 4;
     const int genv = env_int("SSM2D_GROUPS", 0);
     if (genv == 8 || (genv == 4 && d_state <= 32)) G = genv;
     if (mode != 0) G = 8;  // the kernels of the other modes use 8 groups
