@@ -142,3 +142,28 @@ def test_backward_tall_map():
     dy, dy_dev = make_dy(t, "f32", 33)
     got = run_bwd(t, "f32", dy_dev)
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 160 * 96, "tall map")
+
+
+def test_backward_timeout_path_reports_and_recovers(monkeypatch):
+    """A tiny bound on the kernels' own carry waits: the three backward
+    kernels still exit, the error word reports the timeout, and the next
+    call is exact again."""
+    monkeypatch.setenv("SSM2D_WAVES", "1")
+    t = make_random_inputs(1, 16, 16, 64, 128, seed=34)
+    dy, dy_dev = make_dy(t, "f32", 35)
+    args = to_dev(t, "f32")
+    pkg.set_spin_limit(1)
+    try:
+        pkg.scan_bwd(*args, dy_dev)
+        try:
+            pkg.sync_check()
+            timed_out = False
+        except pkg.Ssm2dError as e:
+            assert e.status == pkg.ERR_DEVICE_TIMEOUT
+            timed_out = True
+        _say(f"  forced wait bound (backward): timed_out={timed_out}")
+    finally:
+        pkg.set_spin_limit(0)
+    pkg.sync_check()
+    got = run_bwd(t, "f32", dy_dev)
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 64 * 128, "after timeout")

@@ -229,3 +229,23 @@ def test_directions_shared_row_ring(case, d, dtype, monkeypatch):
         if not (fh or fw):
             check(as_f64(run_ex(t, dtype, four_way=True, vertical_first=vf)),
                   ref_ex(t, four_way=True, vertical_first=vf), dtype, f"row ring four-way {shape}")
+
+
+def test_timeout_path_right_to_left(monkeypatch):
+    """The bounded carry waits of the right-to-left kernels: a tiny bound
+    ends every kernel, is reported, and the next call is exact."""
+    monkeypatch.setenv("SSM2D_WAVES", "1")
+    t = make_random_inputs(1, 16, 16, 64, 128, seed=36)
+    pkg.set_spin_limit(1)
+    try:
+        run = lambda: pkg.scan_fwd_ex(*to_dev(t, "f32"), flip_w=True, vertical_first=True)
+        run()
+        try:
+            pkg.sync_check()
+        except pkg.Ssm2dError as e:
+            assert e.status == pkg.ERR_DEVICE_TIMEOUT
+    finally:
+        pkg.set_spin_limit(0)
+    pkg.sync_check()
+    check(as_f64(run_ex(t, "f32", flip_w=True, vertical_first=True)),
+          ref_ex(t, flip_w=True, vertical_first=True), "f32", "after timeout")
