@@ -219,6 +219,35 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
                         float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
                         int64_t W, void *stream);
 
+/* Backward of ssm2d_scan_fwd_mamba (single upper-left scan; flags: 0 or
+ * SSM2D_DELTA_SOFTPLUS): the gradients of ssm2d_scan_bwd, with ddelta taken
+ * with respect to the raw delta, plus dz (shaped like z; required when z is
+ * given) and ddelta_bias (float32 [d_inner], may be NULL; requires
+ * delta_bias). By the chain rule around ssm2d_scan_bwd: the gate gives
+ * dz = dy * y * SiLU'(z) and passes dy * SiLU(z) on (y = the ungated scan,
+ * recomputed); the step size passes d delta' back through softplus
+ * (times sigmoid(delta + bias)) and sums it over cells for the bias.
+ * Elementwise passes run around the backward's three kernels; scratch of
+ * up to three tensors shaped like x per (device, stream). ddelta_bias is
+ * accumulated with atomics (last bits may vary between runs). Other flags
+ * -> SSM2D_ERR_BAD_FLAGS; errors otherwise as for ssm2d_scan_bwd. */
+int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B,
+                         const float *C, const float *D, const float *z, const float *delta_bias,
+                         const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                         float *dD, float *dz, float *ddelta_bias, int64_t batch, int64_t d_inner,
+                         int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
+
+/* bf16 variant: x, delta, B, C, z, dy, dx, ddelta, dB, dC, dz bfloat16 bits; the
+ * recomputed scan output and dy * SiLU(z) are held in bf16 as well (rounded to
+ * nearest even), the prepared step size as in ssm2d_scan_fwd_mamba_bf16. */
+int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                              const uint16_t *B, const uint16_t *C, const float *D,
+                              const uint16_t *z, const float *delta_bias, const uint16_t *dy,
+                              uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
+                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias,
+                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                              int64_t W, uint32_t flags, void *stream);
+
 /* Static description of a status code. Never NULL. */
 const char *ssm2d_status_string(int status);
 

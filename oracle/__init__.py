@@ -18,6 +18,8 @@ states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
 bwd(x, delta, A, B, C, D, dy) -> dict of dx, ddelta, dA, dB, dC, dD (float64)
 fwd_mamba(x, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=False, ...)
                         the scan with Mamba's step-size bias / softplus and SiLU(z) gating
+bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False)
+                        its gradients (bwd's dict plus dz, ddelta_bias)
 max_threads()           OpenMP thread count the oracle uses by default
 """
 from __future__ import annotations
@@ -212,6 +214,43 @@ def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus
             g = g.reshape(b_ * d_, H, W)[np.asarray(maps)]
         y = y * g
     return y
+
+
+def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, delta_round=None,
+              dy_round=None, lib=None):
+    """Gradients of fwd_mamba (step-size bias and softplus, SiLU(z) gate) for
+    upstream dy, by the chain rule around the scan's backward: the gate gives
+    dz = dy * y_scan * SiLU'(z) and hands dy * SiLU(z) to the scan; the step
+    size hands d delta' back through softplus (its derivative is the logistic
+    sigmoid) and sums it over cells for the bias. ``delta_round`` as in
+    fwd_mamba (applied to the effective step size; its derivative is taken as
+    1); ``dy_round`` likewise to the gated upstream gradient handed to the
+    scan, for outputs that store it rounded. Returns the dict of bwd plus dz
+    and ddelta_bias where they apply."""
+    raw = np.asarray(delta, dtype=np.float64)
+    pre = raw if delta_bias is None else raw + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
+    dt = softplus(pre) if delta_softplus else pre
+    if delta_round is not None:
+        dt = delta_round(dt)
+    dyf = np.asarray(dy, dtype=np.float64)
+    out = {}
+    if z is not None:
+        zf = np.asarray(z, dtype=np.float64)
+        sig = 1.0 / (1.0 + np.exp(-zf))
+        y_scan = fwd(x, dt, A, B, C, D, lib=lib)
+        out["dz"] = dyf * y_scan * sig * (1.0 + zf * (1.0 - sig))
+        dyf = dyf * zf * sig
+        if dy_round is not None:
+            dyf = dy_round(dyf)
+    g = bwd(x, dt, A, B, C, D, dyf, lib=lib)
+    dd = g["ddelta"]
+    if delta_softplus:
+        dd = dd / (1.0 + np.exp(-pre))
+    g["ddelta"] = dd
+    if delta_bias is not None:
+        out["ddelta_bias"] = dd.sum(axis=(0, 2, 3))
+    g.update(out)
+    return g
 
 
 def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None):

@@ -26,6 +26,7 @@ import re
 
 __all__ = [
     "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_fwd_mamba", "scan_bwd",
+    "scan_bwd_mamba",
     "status_string",
     "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
 ]
@@ -63,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     for name in ("ssm2d_scan_fwd_mamba", "ssm2d_scan_fwd_mamba_bf16"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 11 + [i64] * 5 + [ctypes.c_uint32, vp]
+        f.restype = ctypes.c_int
+    for name in ("ssm2d_scan_bwd_mamba", "ssm2d_scan_bwd_mamba_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 17 + [i64] * 5 + [ctypes.c_uint32, vp]
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_bwd", "ssm2d_scan_bwd_bf16"):
         f = getattr(lib, name)
@@ -264,4 +269,35 @@ def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None):
     fn = lib.ssm2d_scan_bwd if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_bf16
     args = [_ptr(t) for t in (x, delta, A, B, C, D, dy)] + [_ptr(g[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")]
     _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, _stream_handle(stream)])
+    return g
+
+
+def scan_bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, *, delta_softplus=False, stream=None):
+    """Gradients of scan_fwd_mamba (include/ssm2d.h, ssm2d_scan_bwd_mamba):
+    scan_bwd's dict with ddelta taken with respect to the raw delta, plus dz
+    (when z is given) and ddelta_bias (when delta_bias is given)."""
+    import torch
+
+    lib = load_library()
+    _check(x, delta, A, B, C, D, None, need_d=True)
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
+        raise ValueError("dy must match x in shape, dtype and device, and be contiguous")
+    if z is not None and (z.shape != x.shape or z.dtype != x.dtype or z.device != x.device or not z.is_contiguous()):
+        raise ValueError("z must match x in shape, dtype and device, and be contiguous")
+    batch, d_inner, H, W = x.shape
+    if delta_bias is not None and (delta_bias.shape != (d_inner,) or delta_bias.dtype != torch.float32
+                                   or delta_bias.device != x.device):
+        raise ValueError("delta_bias must be float32 [d_inner] on x's device")
+    d_state = B.shape[1]
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(delta), "dA": torch.empty_like(A),
+         "dB": torch.empty_like(B), "dC": torch.empty_like(C), "dD": torch.empty_like(D)}
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty_like(delta_bias)
+    fn = lib.ssm2d_scan_bwd_mamba if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_mamba_bf16
+    args = [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, dy)] + \
+        [_ptr(g.get(k)) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")]
+    _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, DELTA_SOFTPLUS if delta_softplus else 0,
+                                     _stream_handle(stream)])
     return g

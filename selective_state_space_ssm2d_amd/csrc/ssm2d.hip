@@ -269,6 +269,56 @@ __global__ void gate_kernel(T *y, const T *z, long total)
     put(y + t, get(y + t) * (zf / (1.0f + expf(-zf))));
 }
 
+// Backward of the gate: dz = dy * y * SiLU'(z), and the scan's upstream
+// gradient dy * SiLU(z); SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
+template <typename T>
+__global__ void gate_bwd_kernel(const T *dy, const T *y, const T *z, T *dz, T *dys, long total)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const float zf = get(z + t), g = get(dy + t);
+    const float sg = 1.0f / (1.0f + expf(-zf));
+    put(dz + t, g * get(y + t) * sg * (1.0f + zf * (1.0f - sg)));
+    put(dys + t, g * zf * sg);
+}
+
+// Backward of the step-size preparation, one block per (batch, channel) map:
+// d delta = d delta' * sigmoid(delta + bias[d]) with softplus (else
+// unchanged), and d bias[d] += the map's sum of d delta.
+template <typename T>
+__global__ void step_bwd_kernel(T *ddelta, const T *delta, const float *bias, float *dbias, long hw, int d_inner,
+                                int use_softplus)
+{
+    __shared__ float part[256];
+    const long map = blockIdx.x;
+    const int d = static_cast<int>(map % d_inner);
+    const float bd = bias ? bias[d] : 0.0f;
+    float acc = 0.0f;
+    for (long p = threadIdx.x; p < hw; p += blockDim.x) {
+        const long t = map * hw + p;
+        float g = get(ddelta + t);
+        if (use_softplus) {
+            g *= 1.0f / (1.0f + expf(-(get(delta + t) + bd)));
+            put(ddelta + t, g);
+        }
+        acc += g;
+    }
+    if (!dbias) return;
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w /= 2) {
+        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) (void)unsafeAtomicAdd(dbias + d, part[0]);
+}
+
+__global__ void zero_kernel(float *p, long n)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t < n) p[t] = 0.0f;
+}
+
 int device_cus(int dev)
 {
     static std::map<int, int> cache;
@@ -498,6 +548,74 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     return SSM2D_OK;
 }
 
+// Backward of the Mamba-option forward: the chain rule around scan_bwd (the
+// gate and the step-size preparation are elementwise).
+template <typename T>
+int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *z,
+                   const float *delta_bias, const T *dy, T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, T *dz,
+                   float *ddelta_bias, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                   unsigned flags, void *stream)
+{
+    if ((flags & ~SSM2D_DELTA_SOFTPLUS) != 0) return SSM2D_ERR_BAD_FLAGS;
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
+    if (d_inner == 0) return SSM2D_OK;
+    if ((z && !dz) || (ddelta_bias && !delta_bias)) return SSM2D_ERR_NULLPTR;
+    if (misaligned(z) || misaligned(dz) || misaligned(delta_bias) || misaligned(ddelta_bias)) return SSM2D_ERR_MISALIGNED;
+    const bool prep = delta_bias || (flags & SSM2D_DELTA_SOFTPLUS);
+    const long total = batch * d_inner * H * W;
+    const unsigned nblk = static_cast<unsigned>((total + 255) / 256);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    if (ddelta_bias) {
+        zero_kernel<<<dim3(static_cast<unsigned>((d_inner + 255) / 256)), dim3(256), 0, s>>>(ddelta_bias, d_inner);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (total == 0 || d_state > SSM2D_MAX_STATE_BWD)  // the backward reports sizes and zeroes dA, dD
+        return scan_bwd<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                           stream);
+    if (!x || !delta || !dy || !dx || !ddelta) return SSM2D_ERR_NULLPTR;
+    void *ws1 = nullptr, *ws2 = nullptr, *ws3 = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        const size_t bytes = static_cast<size_t>(total) * sizeof(T) + 256;
+        int st = prep ? get_aux_ws(dev, stream, 0, bytes, &ws1) : SSM2D_OK;
+        if (st == SSM2D_OK && z) st = get_aux_ws(dev, stream, 1, bytes, &ws2);
+        if (st == SSM2D_OK && z) st = get_aux_ws(dev, stream, 2, bytes, &ws3);
+        if (st != SSM2D_OK) return st;
+        if (prep) {
+            delta_prep_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, static_cast<T *>(ws1), total,
+                                                                    H * W, static_cast<int>(d_inner),
+                                                                    (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    }
+    const T *dstep = prep ? static_cast<const T *>(ws1) : delta;
+    const T *g = dy;
+    if (z) {
+        // the ungated scan output, then dz and the scan's upstream gradient
+        T *y0 = static_cast<T *>(ws2);
+        int st = scan_fwd<T>(x, dstep, A, B, C, D, y0, batch, d_inner, d_state, H, W, 0u, false, stream);
+        if (st != SSM2D_OK) return st;
+        gate_bwd_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(dy, y0, z, dz, static_cast<T *>(ws3), total);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+        g = static_cast<const T *>(ws3);
+    }
+    int st = scan_bwd<T>(x, dstep, A, B, C, D, g, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W, stream);
+    if (st != SSM2D_OK) return st;
+    if ((flags & SSM2D_DELTA_SOFTPLUS) || ddelta_bias) {
+        step_bwd_kernel<T><<<dim3(static_cast<unsigned>(batch * d_inner)), dim3(256), 0, s>>>(
+            ddelta, delta, delta_bias, ddelta_bias, H * W, static_cast<int>(d_inner),
+            (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SSM2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -562,6 +680,26 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
 {
     return scan_bwd<uint16_t>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
                               stream);
+}
+
+int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                         const float *D, const float *z, const float *delta_bias, const float *dy, float *dx,
+                         float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
+                         void *stream)
+{
+    return scan_bwd_mamba<float>(x, delta, A, B, C, D, z, delta_bias, dy, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                                 batch, d_inner, d_state, H, W, flags, stream);
+}
+
+int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
+                              const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
+                              const uint16_t *dy, uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
+                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias, int64_t batch,
+                              int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+{
+    return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, z, delta_bias, dy, dx, ddelta, dA, dB, dC, dD, dz,
+                                    ddelta_bias, batch, d_inner, d_state, H, W, flags, stream);
 }
 
 const char *ssm2d_status_string(int status)

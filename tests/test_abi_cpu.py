@@ -184,6 +184,25 @@ def test_bwd_validation(lib, bf16):
         assert _call_bwd(lib, [1, 2, 3, 4, 5], ptrs, bf16=bf16) == pkg.ERR_MISALIGNED, k
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_bwd_mamba_validation(lib, bf16):
+    fn = lib.ssm2d_scan_bwd_mamba_bf16 if bf16 else lib.ssm2d_scan_bwd_mamba
+    call = lambda ptrs, dims, flags: fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
+    full = [FAKE] * 17
+    assert call(full, [1, 2, 3, 4, 5], pkg.FLIP_H) == pkg.ERR_BAD_FLAGS  # directions: not in the backward
+    assert call(full, [1, -2, 3, 4, 5], 0) == pkg.ERR_BAD_DIM
+    assert call([0] * 17, [1, 0, 3, 4, 5], 0) == pkg.OK                   # d_inner = 0: nothing to do
+    no_dz = list(full)
+    no_dz[15] = 0
+    assert call(no_dz, [1, 2, 3, 4, 5], 0) == pkg.ERR_NULLPTR             # z given, dz missing
+    no_bias = list(full)
+    no_bias[7] = 0
+    assert call(no_bias, [1, 2, 3, 4, 5], 0) == pkg.ERR_NULLPTR           # d bias asked without a bias
+    odd = list(full)
+    odd[6] = FAKE + 4
+    assert call(odd, [1, 2, 3, 4, 5], 0) == pkg.ERR_MISALIGNED
+
+
 def test_python_binding_rejects_bad_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 2, 3, 4)

@@ -167,3 +167,56 @@ def test_backward_timeout_path_reports_and_recovers(monkeypatch):
     pkg.sync_check()
     got = run_bwd(t, "f32", dy_dev)
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 64 * 128, "after timeout")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("opts", [dict(gate=True, bias=True, sp=True), dict(gate=True, bias=False, sp=False),
+                                  dict(gate=False, bias=True, sp=True), dict(gate=False, bias=False, sp=True)],
+                         ids=str)
+def test_backward_mamba_options(opts, dtype):
+    """Gradients of the gated scan with the step-size bias and softplus,
+    including dz and d bias, against the oracle's chain rule (itself pinned by
+    finite differences)."""
+    from selective_state_space_ssm2d_amd.inputs import bf16_bits_from_f32, f32_from_bf16_bits
+
+    shape = (2, 12, 16, 17, 30)
+    t = make_random_inputs(*shape, seed=38, dtype=dtype)
+    r = np.random.default_rng(38)
+
+    def dev(a):
+        a = np.asarray(a, dtype=np.float32)
+        if dtype == "bf16":
+            bits = bf16_bits_from_f32(a)
+            return f32_from_bf16_bits(bits).astype(np.float64), torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        return a.astype(np.float64), torch.from_numpy(a).cuda()
+
+    raw, raw_dev = dev(r.standard_normal(t["x"].shape) - 0.2) if opts["sp"] else dev(np.abs(r.standard_normal(t["x"].shape)) + 0.1)
+    z, z_dev = dev(r.standard_normal(t["x"].shape)) if opts["gate"] else (None, None)
+    bias = (np.abs(r.standard_normal(shape[1])) * 0.3).astype(np.float32) if opts["bias"] else None
+    dy, dy_dev = make_dy(t, dtype, 39)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    g = pkg.scan_bwd_mamba(*args, dy_dev, z=z_dev, delta_bias=None if bias is None else torch.from_numpy(bias).cuda(),
+                           delta_softplus=opts["sp"])
+    pkg.sync_check()
+    got = {k: v.double().cpu().numpy() for k, v in g.items()}
+    rnd = (lambda v: f32_from_bf16_bits(bf16_bits_from_f32(np.asarray(v, dtype=np.float32))).astype(np.float64)) \
+        if dtype == "bf16" else (lambda v: np.asarray(v, dtype=np.float32).astype(np.float64))
+    # the library hands the scan's backward dy * SiLU(z) in the input type
+    # (bf16: rounded to nearest even); the oracle takes the same values
+    ref = oracle.bwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], dy, z=z, delta_bias=bias,
+                           delta_softplus=opts["sp"], delta_round=rnd if (opts["sp"] or opts["bias"]) else None,
+                           dy_round=rnd if dtype == "bf16" else None)
+    cells = shape[0] * shape[3] * shape[4]
+    check_grads(got, ref, dtype, cells, f"options {opts}")
+    if "dz" in ref:
+        err = float(np.max(np.abs(got["dz"] - ref["dz"]) / (1.0 + np.abs(ref["dz"]))))
+        _say(f"  options {opts} dz: {err:.3e} (bar {TOL[dtype]:.1e})")
+        assert err <= TOL[dtype], "dz"
+    if "ddelta_bias" in ref:
+        # d bias[d] sums d delta over the channel's cells: its bar is the sum
+        # of the elementwise bars of those d delta values
+        bar = TOL[dtype] * np.sum(1.0 + np.abs(ref["ddelta"]), axis=(0, 2, 3))
+        worst = float(np.max(np.abs(got["ddelta_bias"] - ref["ddelta_bias"]) / bar))
+        _say(f"  options {opts} ddelta_bias: {worst:.3e} of the summed bar")
+        assert worst <= 1.0, "ddelta_bias"

@@ -139,3 +139,34 @@ def test_bwd_pins_catch_planted_mistakes(tmp_path):
             except (AssertionError, RuntimeError):
                 caught.append(pin.__name__)
         assert caught, f"no pin caught the planted mistake: {name}"
+
+
+def test_mamba_options_backward_finite_differences(oracle_lib):
+    """Gradients through the step-size bias, softplus and the SiLU(z) gate
+    against central finite differences of fwd_mamba."""
+    ins = _inputs(1, 3, 2, 3, 4, 37)
+    r = np.random.default_rng(37)
+    raw = r.standard_normal(ins["x"].shape) - 0.3
+    z = r.standard_normal(ins["x"].shape)
+    bias = r.standard_normal(3) * 0.4
+    dy = r.standard_normal(ins["x"].shape)
+    args = dict(z=z, delta_bias=bias, delta_softplus=True)
+
+    def loss(**over):
+        v = {"x": ins["x"], "delta": raw, "A": ins["A"], "B": ins["B"], "C": ins["C"], "D": ins["D"], **args}
+        v.update(over)
+        return float(np.sum(oracle.fwd_mamba(v["x"], v["delta"], v["A"], v["B"], v["C"], v["D"], z=v["z"],
+                                             delta_bias=v["delta_bias"], delta_softplus=True, lib=oracle_lib) * dy))
+
+    g = oracle.bwd_mamba(ins["x"], raw, ins["A"], ins["B"], ins["C"], ins["D"], dy, lib=oracle_lib, **args)
+    for name, base, key in (("delta", raw, "ddelta"), ("z", z, "dz"), ("delta_bias", bias, "ddelta_bias"),
+                            ("x", ins["x"], "dx"), ("A", ins["A"], "dA")):
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            h = 1e-6 * max(1.0, abs(base[idx]))
+            p, m = base.copy(), base.copy()
+            p[idx] += h
+            m[idx] -= h
+            fd[idx] = (loss(**{name: p}) - loss(**{name: m})) / (2 * h)
+        err = np.max(np.abs(g[key] - fd) / (1.0 + np.abs(fd)))
+        assert err < 1e-6, f"{key} vs finite differences: {err:.2e}"
