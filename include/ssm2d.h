@@ -137,8 +137,9 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
 
 /* ---- Mamba selective-scan options -----------------------------------------
  *
- * The pages name Mamba's selective_scan_fn as the operator the 2D scan
- * extends. Its options around the scan, for the 2D scan:
+ * The codewithpapers.app record of the paper lists selective_scan_fn (in the
+ * official code's pscan_2d.py) as the code's entry point: Mamba's operator
+ * of that name, whose options around the scan are, for the 2D scan:
  *   step size  delta' = delta + delta_bias[d] (delta_bias may be NULL: 0),
  *              then softplus(delta') = log(1 + e^delta') if SSM2D_DELTA_SOFTPLUS;
  *              computed in fp32 by a separate pass and stored in the input

@@ -195,8 +195,8 @@ def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus
     """The Mamba selective-scan operator's options around the 2D scan: the
     step size is delta + delta_bias[d] (bias per channel), passed through
     softplus when asked, and the output is gated by SiLU(z), z shaped like x
-    (Mamba's selective_scan_fn options; the 2DMamba pages name that entry point
-    as the op they extend). ``delta_round`` (a function) is applied to the
+    (Mamba's selective_scan_fn options; the codewithpapers.app record lists
+    that function as the official code's entry point). ``delta_round`` (a function) is applied to the
     effective step size before the scan, for inputs that store it rounded.
     ``dirs``: flip_h, flip_w, vertical_first, four_way as for fwd."""
     dt = np.asarray(delta, dtype=np.float64)
