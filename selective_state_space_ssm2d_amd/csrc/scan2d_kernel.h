@@ -72,12 +72,16 @@ constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + 
 //   kModeBackward    adjoint pass of the backward (with kModeFlipW and rows
 //                    bottom to top): gradients from the stored states
 //   kModeGate        the result is multiplied by SiLU(z) before it is stored
+//   kModeEdges       (with kModeBackward) chains cross workgroups without
+//                    courier waves: boundary strips use the global ring
+//                    themselves
 constexpr int kModeFlipW = 1;
 constexpr int kModeVFirst = 2;
 constexpr int kModeAccumulate = 4;
 constexpr int kModeStates = 8;
 constexpr int kModeBackward = 16;
 constexpr int kModeGate = 32;
+constexpr int kModeEdges = 64;
 
 // Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
 // small (8 state groups, K * NPL <= 16; K * NPL <= 8 for the stored-state
@@ -477,6 +481,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool STATES = (MODE & kModeStates) != 0;
     constexpr bool BWD = (MODE & kModeBackward) != 0;
     constexpr bool GATE = (MODE & kModeGate) != 0;
+    constexpr bool EDGES = (MODE & kModeEdges) != 0;
+    static_assert(!EDGES || BWD, "courier-free chains: adjoint pass only");
     static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
     static_assert(!BWD || (FW && !VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
     static_assert(!STATES || (!FW && !VF && !ACC), "stored states: forward order only");
@@ -929,9 +935,23 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // Rows of the strip, with the code for the strip's neighbours fixed at
         // compile time (LEFT: a strip to the left sends carries; RIGHT: one to
         // the right takes them).
+        // Carries between workgroups in the courier-free adjoint pass
+        // (kModeEdges: its 256-VGPR waves leave no room for couriers next to
+        // 8 strips): the workgroup's first strip reads the global ring
+        // itself, its last strip writes it. Every row has its own slot there
+        // (no reuse, so no back-pressure).
+        const unsigned int etag_c = p.epoch << 16;
+        const long gstride_c = static_cast<long>(p.qg) * NPL * kWave;
+        const unsigned long long *gin_c =
+            p.gring + (static_cast<long>(chain) * (p.groups - 1) + (grp > 0 ? grp - 1 : 0)) * gstride_c + lane;
+        unsigned long long *gout_c = p.gring + (static_cast<long>(chain) * (p.groups - 1) + grp) * gstride_c + lane;
+
+        // LK / RK: 0 no neighbour, 1 a strip of this workgroup (LDS ring),
+        // 2 a strip of another workgroup reached by this strip itself.
         auto strip_rows = [&](auto left_tag, auto right_tag) {
-            constexpr bool LEFT = decltype(left_tag)::value;
-            constexpr bool RIGHT = decltype(right_tag)::value;
+            constexpr int LK = decltype(left_tag)::value, RK = decltype(right_tag)::value;
+            constexpr bool LEFT = LK == 1, RIGHT = RK == 1;
+            constexpr bool LEFT_G = LK == 2, RIGHT_G = RK == 2;
             int room = 0;  // rows this wave may publish, as seen
 
             // Row i from packet buffer i % 2 and operands `o`; row i+1's
@@ -958,6 +978,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 // carry-independent work below, so their latency overlaps it.
                 float hh[NPL];
                 int seen = 0;
+                unsigned long long gw[NPL];
                 if constexpr (LEFT) {
                     seen = lds_peek(&s_done[wave]);
                     signal_fence();
@@ -967,6 +988,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 } else {
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
+                }
+                if constexpr (LEFT_G) {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) gw[k] = ld_relaxed(gin_c + (static_cast<long>(i) * NPL + k) * kWave);
                 }
 
                 // ---- carry-independent work: decay factors and inputs of the row
@@ -1054,6 +1079,28 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     }
                 }
 
+                if constexpr (LEFT_G) {
+                    // the tagged words of row i from the left workgroup's
+                    // last strip; polled again until every lane has them
+                    const unsigned long long want = static_cast<unsigned long long>(etag_c | static_cast<unsigned>(i)) << 32;
+                    long long spins = 0;
+                    while (!timed_out) {
+                        bool ok = true;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) ok = ok && ((gw[k] & 0xffffffff00000000ull) == want);
+                        if (__all(ok)) break;
+                        if (++spins > p.spin_limit) {
+                            timed_out = true;
+                            break;
+                        }
+                        if (spins > kSpinPolls) sleep_a_bit();
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) gw[k] = ld_relaxed(gin_c + (static_cast<long>(i) * NPL + k) * kWave);
+                    }
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) hh[k] = __uint_as_float(static_cast<unsigned>(gw[k] & 0xffffffffu));
+                }
+
                 // ---- horizontal recurrence along the row, then hand the carry on
                 float hc[K][NPL];
 #pragma unroll
@@ -1077,6 +1124,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     lds_poke(&s_done[wave + 1], i + 1);
                     // keep the vertical step below from being scheduled ahead
                     // of the publish: it would sit on the carry's path
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (RIGHT_G) {
+                    const unsigned long long tagw = static_cast<unsigned long long>(etag_c | static_cast<unsigned>(i)) << 32;
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k)
+                        st_relaxed(gout_c + (static_cast<long>(i) * NPL + k) * kWave, tagw | __float_as_uint(hh[k]));
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
@@ -1292,12 +1346,26 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                                hbB[s], s + 1 < P ? hbB[s + 1] : hbB[s]);
             }
         };
-        if (has_left) {
-            if (has_right) strip_rows(std::true_type{}, std::true_type{});
-            else strip_rows(std::true_type{}, std::false_type{});
+        using N0 = std::integral_constant<int, 0>;
+        using N1 = std::integral_constant<int, 1>;
+        using N2 = std::integral_constant<int, 2>;
+        if constexpr (EDGES) {
+            const int lk = !has_left ? 0 : (wave == 0 && grp > 0 ? 2 : 1);
+            const int rk = !has_right ? 0 : (wave == nact - 1 ? 2 : 1);
+            auto with_right = [&](auto lt) {
+                if (rk == 0) strip_rows(lt, N0{});
+                else if (rk == 1) strip_rows(lt, N1{});
+                else strip_rows(lt, N2{});
+            };
+            if (lk == 0) with_right(N0{});
+            else if (lk == 1) with_right(N1{});
+            else with_right(N2{});
+        } else if (has_left) {
+            if (has_right) strip_rows(N1{}, N1{});
+            else strip_rows(N1{}, N0{});
         } else {
-            if (has_right) strip_rows(std::false_type{}, std::true_type{});
-            else strip_rows(std::false_type{}, std::false_type{});
+            if (has_right) strip_rows(N0{}, N1{});
+            else strip_rows(N0{}, N0{});
         }
         if constexpr (!STATES && !BWD) {
             if (p.h_last && !timed_out) {
@@ -1375,7 +1443,13 @@ extern long long g_spin_limit;
 int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t cons_count, WsEntry **out);
 int device_cus(int dev);
 
-inline int block_threads(const Plan &pl) { return kWave * (pl.s_local + (pl.groups > 1 ? 2 : 0)); }
+// Two courier waves join the strips when a chain spans workgroups (not in
+// the courier-free adjoint pass, whose boundary strips reach the global ring
+// themselves).
+inline int block_threads(const Plan &pl)
+{
+    return kWave * (pl.s_local + ((pl.groups > 1 && !(pl.mode & kModeEdges)) ? 2 : 0));
+}
 
 template <typename T, int K, int NPL, int G, int MODE>
 size_t lds_bytes(const Plan &pl)
@@ -1393,7 +1467,7 @@ size_t lds_bytes(const Plan &pl)
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 int choose_qg(const Plan &pl, int dev, int H)
 {
-    if (pl.groups <= 1) return H;
+    if (pl.groups <= 1 || (pl.mode & kModeEdges)) return H;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE>, block_threads(pl),
                                                      lds_bytes<T, K, NPL, G, MODE>(pl)) != hipSuccess) {
@@ -1520,6 +1594,7 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
     SSM2D_DISPATCH_DECL(TT, dispatch_flipw_vfirst_acc) \
     SSM2D_DISPATCH_DECL(TT, dispatch_states)           \
     SSM2D_DISPATCH_DECL(TT, dispatch_bwd)              \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_edges)        \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate)             \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_vfirst)      \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw)       \

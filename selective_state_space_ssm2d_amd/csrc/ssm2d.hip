@@ -65,7 +65,8 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     if (s_local < 1) s_local = 1;
     if (s_local > pl.nstrips) s_local = pl.nstrips;
     if (s_local > maxw) s_local = maxw;
-    if (s_local < pl.nstrips && s_local > maxw - 2) s_local = maxw - 2;  // room for 2 couriers
+    if (s_local < pl.nstrips && s_local > maxw - 2 && !(mode & kModeEdges))
+        s_local = maxw - 2;  // room for 2 couriers (none in the courier-free adjoint pass)
     pl.s_local = s_local;
     pl.groups = (pl.nstrips + s_local - 1) / s_local;
     pl.total_wg = pl.n_chains * pl.groups;
@@ -530,11 +531,16 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     int st = dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 2. the adjoint scans from the lower-right corner, with every local derivative
+    // (chains cut into several workgroups: the courier-free kernels, which fit
+    // 8 strips per workgroup instead of 6)
     Plan pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward);
+    const bool edges = pb.groups > 1;
+    if (edges) pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward | kModeEdges);
     pb.flip_h = 1;
     pb.bw = &bw;
     if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
-    st = dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    st = edges ? dispatch_bwd_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
+               : dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 3. dB and dC: sums over the channel blocks
     if (d_state > 0) {
