@@ -211,6 +211,25 @@ int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const flo
                    float *dA, float *dB, float *dC, float *dD, int64_t batch, int64_t d_inner,
                    int64_t d_state, int64_t H, int64_t W, void *stream);
 
+/* Backward of ssm2d_scan_fwd_ex for the scan direction `flags` selects
+ * (SSM2D_FLIP_H, SSM2D_FLIP_W; 0 gives ssm2d_scan_bwd): the stored-state pass
+ * runs in the forward's direction, the adjoint from the opposite corner.
+ * SSM2D_VERTICAL_FIRST -> SSM2D_ERR_UNSUPPORTED; SSM2D_ACCUMULATE,
+ * SSM2D_FOUR_WAY, SSM2D_DELTA_SOFTPLUS or unknown bits -> SSM2D_ERR_BAD_FLAGS
+ * (a four-corner sum's gradient is the sum of the four directions'). Otherwise
+ * as ssm2d_scan_bwd. */
+int ssm2d_scan_bwd_ex(const float *x, const float *delta, const float *A, const float *B,
+                      const float *C, const float *D, const float *dy, float *dx, float *ddelta,
+                      float *dA, float *dB, float *dC, float *dD, int64_t batch, int64_t d_inner,
+                      int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
+
+/* bf16 variant of ssm2d_scan_bwd_ex: types as for ssm2d_scan_bwd_bf16. */
+int ssm2d_scan_bwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
+                           const uint16_t *B, const uint16_t *C, const float *D, const uint16_t *dy,
+                           uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB, uint16_t *dC,
+                           float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                           int64_t W, uint32_t flags, void *stream);
+
 /* bf16 backward: x, delta, B, C, dy, dx, ddelta, dB, dC are bfloat16 (raw
  * uint16 bits, outputs rounded to nearest even); A, D, dA, dD float32; the
  * stored states and all arithmetic fp32. */

@@ -253,9 +253,19 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
     return g
 
 
-def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None):
+def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False):
     """Gradients of the forward pass (fp64) for upstream gradient dy (shape of
-    y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input."""
+    y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input.
+    flip_h / flip_w: of the scan in that direction, which is the upper-left
+    scan of the mirrored map (a permutation of the cells), so its gradients
+    are the mirrored map's, mirrored back."""
+    if flip_h or flip_w:
+        ax = tuple(a for a, f in ((2, flip_h), (3, flip_w)) if f)
+        fl = lambda a: np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), ax))
+        g = bwd(fl(x), fl(delta), A, fl(B), fl(C), D, fl(dy), nthreads, lib)
+        for k in ("dx", "ddelta", "dB", "dC"):
+            g[k] = fl(g[k])
+        return g
     lib = lib or _get()
     x, delta, A, B, C, D, dy = map(_f64, (x, delta, A, B, C, D, dy))
     batch, d_inner, H, W = x.shape

@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [vp] * 13 + [i64] * 5 + [vp]
         f.restype = ctypes.c_int
+    for name in ("ssm2d_scan_bwd_ex", "ssm2d_scan_bwd_ex_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 13 + [i64] * 5 + [ctypes.c_uint32, vp]
+        f.restype = ctypes.c_int
     for name in ("ssm2d_scan_fwd_ex", "ssm2d_scan_fwd_ex_bf16"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 7 + [i64] * 5 + [ctypes.c_uint32, vp]
@@ -245,9 +249,10 @@ def scan_fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, y=None, *
     return (y, h_last) if return_last_state else y
 
 
-def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None):
+def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None, *, flip_h=False, flip_w=False):
     """Gradients of the forward scan for upstream gradient dy (include/ssm2d.h,
-    ssm2d_scan_bwd). Returns a dict dx, ddelta, dA, dB, dC, dD; ``out`` may
+    ssm2d_scan_bwd; with flip_h / flip_w, ssm2d_scan_bwd_ex for the scan in
+    that direction). Returns a dict dx, ddelta, dA, dB, dC, dD; ``out`` may
     supply any of them (shapes and dtypes as the inputs they belong to)."""
     import torch
 
@@ -266,9 +271,14 @@ def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None):
         elif t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
             raise ValueError(f"{k} must match its input in shape, dtype and device, and be contiguous")
         g[k] = t
-    fn = lib.ssm2d_scan_bwd if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_bf16
     args = [_ptr(t) for t in (x, delta, A, B, C, D, dy)] + [_ptr(g[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")]
-    _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, _stream_handle(stream)])
+    if flip_h or flip_w:
+        fn = lib.ssm2d_scan_bwd_ex if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_ex_bf16
+        flags = (FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0)
+        _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, flags, _stream_handle(stream)])
+    else:
+        fn = lib.ssm2d_scan_bwd if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_bf16
+        _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, _stream_handle(stream)])
     return g
 
 

@@ -1,0 +1,14 @@
+// libssm2d: kernel instances for fp32 inputs, adjoint pass of the backward of a right-to-left scan.
+#include "scan2d_kernel.h"
+
+namespace ssm2d_impl {
+
+int dispatch_bwd_ltr(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                     const float *D, float *y, int batch, int d_inner, int d_state, int H, int W,
+                     const Plan &pl, int dev, void *stream, int align)
+{
+    constexpr int kMode = kModeBackward;
+    return dispatch_mode<float, kMode>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream, align);
+}
+
+}  // namespace ssm2d_impl

@@ -484,8 +484,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool EDGES = (MODE & kModeEdges) != 0;
     static_assert(!EDGES || BWD, "courier-free chains: adjoint pass only");
     static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
-    static_assert(!BWD || (FW && !VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
-    static_assert(!STATES || (!FW && !VF && !ACC), "stored states: forward order only");
+    static_assert(!BWD || (!VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
+    static_assert(!STATES || (!VF && !ACC), "stored states: horizontal-first order");
     using Chunk = typename ChunkOf<T>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
     constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
@@ -708,12 +708,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             }
 #pragma unroll
             for (int e = 0; e < NSUB; ++e) {
+                // (the stored-state pass counts strips over the map padded to a
+                // multiple of 4 columns at the end it scans last: on the left
+                // scanning left to right, on the right scanning right to left;
+                // columns outside the map read zeros)
                 if constexpr (FW) {
-                    const int col = W - jc - 4 * q - 4 + e * ALIGN;
-                    src[pp][e] = (col >= 0 ? base + col : zeros) + row0;
+                    const int col = (STATES ? W + p.states_pad : W) - jc - 4 * q - 4 + e * ALIGN;
+                    src[pp][e] = (col >= 0 && col + ALIGN <= W) ? base + col + row0 : zeros + row0;
                 } else {
-                    // (the stored-state pass counts strips over the map padded
-                    // on the left: columns below 0 read zeros)
                     const int col = jc + 4 * q + e * ALIGN - (STATES ? p.states_pad : 0);
                     src[pp][e] = (col >= 0 && col + ALIGN <= W) ? base + col + row0 : zeros + row0;
                 }
@@ -758,8 +760,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         const float *hlast = p.states + (tile0 + H - 1) * TILE + lane * 4;
         // backward: 8-channel sums of dB, dC for this lane's group, memory row
         // H-1 - t, the strip's 4 cells at padded column 4 * fstrip
+        // (rows of 4 * nstrips columns: the map starts at states_pad when the
+        // adjoint runs right to left, at 0 when it runs left to right)
         const long pld = 4L * p.nstrips;
-        const long part0 = dblk * p.part_stride + ((static_cast<long>(b) * p.d_state + g * NPL) * H + (H - 1)) * pld + 4L * fstrip;
+        const long pcol = FW ? 4L * fstrip : 4L * strip;
+        const long prow0 = p.flip_h ? H - 1 : 0;  // memory row of scan row 0
+        const long part0 = dblk * p.part_stride + ((static_cast<long>(b) * p.d_state + g * NPL) * H + prow0) * pld + pcol;
         float *pbrow = p.dBp + part0;
         float *pcrow = p.dCp + part0;
         const float *zeros_f = static_cast<const float *>(p.zeros);
@@ -1182,7 +1188,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     // dB and dC: sums over the wave's 8 channels of a state
                     // group (the sum over channel blocks comes later), cells
                     // in memory order
-                    const long prow = static_cast<long>(i) * pld;
+                    const long prow = static_cast<long>(i) * (p.flip_h ? -pld : pld);
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) {
                         float sb[K], sc[K];
@@ -1192,9 +1198,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                             sc[c] = sum8(dCv[k][c]);
                         }
                         if (part_lane && hok[k]) {
-                            const long off = static_cast<long>(k) * H * pld - prow;
-                            *reinterpret_cast<float4 *>(pbrow + off) = make_float4(sb[3], sb[2], sb[1], sb[0]);
-                            *reinterpret_cast<float4 *>(pcrow + off) = make_float4(sc[3], sc[2], sc[1], sc[0]);
+                            const long off = static_cast<long>(k) * H * pld + prow;
+                            if constexpr (FW) {
+                                *reinterpret_cast<float4 *>(pbrow + off) = make_float4(sb[3], sb[2], sb[1], sb[0]);
+                                *reinterpret_cast<float4 *>(pcrow + off) = make_float4(sc[3], sc[2], sc[1], sc[0]);
+                            } else {
+                                *reinterpret_cast<float4 *>(pbrow + off) = make_float4(sb[0], sb[1], sb[2], sb[3]);
+                                *reinterpret_cast<float4 *>(pcrow + off) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+                            }
                         }
                     }
                 } else {
@@ -1595,6 +1606,9 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
     SSM2D_DISPATCH_DECL(TT, dispatch_states)           \
     SSM2D_DISPATCH_DECL(TT, dispatch_bwd)              \
     SSM2D_DISPATCH_DECL(TT, dispatch_bwd_edges)        \
+    SSM2D_DISPATCH_DECL(TT, dispatch_states_flipw)     \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_ltr)          \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_ltr_edges)    \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate)             \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_vfirst)      \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw)       \

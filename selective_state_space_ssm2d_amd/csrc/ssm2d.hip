@@ -463,11 +463,16 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     return SSM2D_OK;
 }
 
+// flags: SSM2D_FLIP_H / SSM2D_FLIP_W, the direction of the forward scan.
 template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-             int64_t W, void *stream)
+             int64_t W, void *stream, unsigned flags = 0)
 {
+    if ((flags & ~kKnownFlags) != 0 || (flags & (SSM2D_ACCUMULATE | SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
+        return SSM2D_ERR_BAD_FLAGS;
+    if (flags & SSM2D_VERTICAL_FIRST) return SSM2D_ERR_UNSUPPORTED;
+    const bool f_h = (flags & SSM2D_FLIP_H) != 0, f_w = (flags & SSM2D_FLIP_W) != 0;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (d_inner == 0) return SSM2D_OK;
     if (d_state > SSM2D_MAX_STATE_BWD || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
@@ -523,31 +528,40 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
-    // 1. the forward pass again, storing every state
-    Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates);
+    // 1. the forward pass again, in its direction, storing every state
+    Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates | (f_w ? kModeFlipW : 0));
     pf.bw = &bw;
+    pf.flip_h = f_h ? 1 : 0;
     choose_coop<T>(pf, H, align);
     if (pf.npl != npl || pf.n_dblk != n_dblk || pf.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
-    int st = dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
+    int st = f_w ? dispatch_states_flipw(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align)
+                 : dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
     if (st != SSM2D_OK) return st;
-    // 2. the adjoint scans from the lower-right corner, with every local derivative
-    // (chains cut into several workgroups: the courier-free kernels, which fit
-    // 8 strips per workgroup instead of 6)
-    Plan pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward);
+    // 2. the adjoint scans from the opposite corner, with every local
+    // derivative (chains cut into several workgroups: the courier-free
+    // kernels, which fit 8 strips per workgroup instead of 6)
+    const int bmode = kModeBackward | (f_w ? 0 : kModeFlipW);
+    Plan pb = make_plan(batch, d_inner, d_state, H, W, bmode);
     const bool edges = pb.groups > 1;
-    if (edges) pb = make_plan(batch, d_inner, d_state, H, W, kModeFlipW | kModeBackward | kModeEdges);
-    pb.flip_h = 1;
+    if (edges) pb = make_plan(batch, d_inner, d_state, H, W, bmode | kModeEdges);
+    pb.flip_h = f_h ? 0 : 1;
     pb.bw = &bw;
     if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
-    st = edges ? dispatch_bwd_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
-               : dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    if (f_w)
+        st = edges ? dispatch_bwd_ltr_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
+                   : dispatch_bwd_ltr(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    else
+        st = edges ? dispatch_bwd_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
+                   : dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 3. dB and dC: sums over the channel blocks
     if (d_state > 0) {
         const long total = batch * d_state * H * W;
+        // (the partial rows start at column pad when the adjoint ran right to
+        // left, at 0 when it ran left to right)
         bwd_reduce_kernel<T><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
             bw.dBp, bw.dCp, part_stride, static_cast<int>(n_dblk), dB, dC, total, wi, static_cast<int>(4 * nstrips),
-            static_cast<int>(pad));
+            f_w ? 0 : static_cast<int>(pad));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
     }
@@ -677,6 +691,24 @@ int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const flo
                    float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, void *stream)
 {
     return scan_bwd<float>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W, stream);
+}
+
+int ssm2d_scan_bwd_ex(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                      const float *D, const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                      float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
+                      void *stream)
+{
+    return scan_bwd<float>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W, stream,
+                           flags);
+}
+
+int ssm2d_scan_bwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
+                           const uint16_t *C, const float *D, const uint16_t *dy, uint16_t *dx, uint16_t *ddelta,
+                           float *dA, uint16_t *dB, uint16_t *dC, float *dD, int64_t batch, int64_t d_inner,
+                           int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+{
+    return scan_bwd<uint16_t>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                              stream, flags);
 }
 
 int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,

@@ -185,6 +185,18 @@ def test_bwd_validation(lib, bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
+def test_bwd_ex_validation(lib, bf16):
+    fn = lib.ssm2d_scan_bwd_ex_bf16 if bf16 else lib.ssm2d_scan_bwd_ex
+    call = lambda dims, flags, ptrs=None: fn(*(ctypes.c_void_p(p) for p in (ptrs or [FAKE] * 13)), *dims, flags, None)
+    for flags in (pkg.ACCUMULATE, pkg.FOUR_WAY, pkg.DELTA_SOFTPLUS, 128):
+        assert call([1, 2, 3, 4, 5], flags) == pkg.ERR_BAD_FLAGS, flags
+    assert call([1, 2, 3, 4, 5], pkg.VERTICAL_FIRST) == pkg.ERR_UNSUPPORTED
+    for flags in (pkg.FLIP_H, pkg.FLIP_W, pkg.FLIP_H | pkg.FLIP_W):
+        assert call([1, -2, 3, 4, 5], flags) == pkg.ERR_BAD_DIM
+        assert call([1, 0, 3, 4, 5], flags, [0] * 13) == pkg.OK
+
+
+@pytest.mark.parametrize("bf16", [False, True])
 def test_bwd_mamba_validation(lib, bf16):
     fn = lib.ssm2d_scan_bwd_mamba_bf16 if bf16 else lib.ssm2d_scan_bwd_mamba
     call = lambda ptrs, dims, flags: fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)

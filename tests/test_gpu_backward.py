@@ -220,3 +220,41 @@ def test_backward_mamba_options(opts, dtype):
         worst = float(np.max(np.abs(got["ddelta_bias"] - ref["ddelta_bias"]) / bar))
         _say(f"  options {opts} ddelta_bias: {worst:.3e} of the summed bar")
         assert worst <= 1.0, "ddelta_bias"
+
+
+FLIPS = [(True, False), (False, True), (True, True)]
+
+
+@pytest.mark.parametrize("fl", FLIPS, ids=lambda f: ("H" if f[0] else "-") + ("W" if f[1] else "-"))
+@pytest.mark.parametrize("shape", [(1, 3, 4, 1, 37), (2, 5, 4, 29, 1), (1, 17, 8, 13, 7), (1, 9, 16, 14, 30),
+                                   (2, 16, 16, 21, 64), (1, 8, 32, 9, 21)], ids=str)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_other_directions(shape, fl, dtype):
+    """The backward of the scans from the other corners (ssm2d_scan_bwd_ex)."""
+    fh, fw = fl
+    _say(f"backward flips {fl} {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 40, dtype=dtype)
+    dy, dy_dev = make_dy(t, dtype, _seed(shape) + 41)
+    g = pkg.scan_bwd(*to_dev(t, dtype), dy_dev, flip_h=fh, flip_w=fw)
+    pkg.sync_check()
+    got = {k: as_f64(v) for k, v in g.items()}
+    ref = oracle.bwd(*(t[k] for k in KEYS), dy, flip_h=fh, flip_w=fw)
+    check_grads(got, ref, dtype, shape[0] * shape[3] * shape[4], f"flips {fl} {shape}")
+
+
+@pytest.mark.parametrize("fl", FLIPS, ids=lambda f: ("H" if f[0] else "-") + ("W" if f[1] else "-"))
+@pytest.mark.parametrize("case", [((1, 16, 16, 33, 80), "1", "f32"), ((1, 8, 16, 21, 130), "3", "bf16"),
+                                  ((1, 16, 16, 160, 96), None, "f32")], ids=str)
+def test_backward_other_directions_chains(case, fl, monkeypatch):
+    """Other corners with chains across workgroups, and a tall map."""
+    shape, waves, dtype = case
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    fh, fw = fl
+    t = make_random_inputs(*shape, seed=43, dtype=dtype)
+    dy, dy_dev = make_dy(t, dtype, 44)
+    g = pkg.scan_bwd(*to_dev(t, dtype), dy_dev, flip_h=fh, flip_w=fw)
+    pkg.sync_check()
+    got = {k: as_f64(v) for k, v in g.items()}
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy, flip_h=fh, flip_w=fw), dtype,
+                shape[0] * shape[3] * shape[4], f"flips {fl} chains {case}")

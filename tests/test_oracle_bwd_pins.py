@@ -170,3 +170,30 @@ def test_mamba_options_backward_finite_differences(oracle_lib):
             fd[idx] = (loss(**{name: p}) - loss(**{name: m})) / (2 * h)
         err = np.max(np.abs(g[key] - fd) / (1.0 + np.abs(fd)))
         assert err < 1e-6, f"{key} vs finite differences: {err:.2e}"
+
+
+def test_flipped_backward_finite_differences(oracle_lib):
+    """The backward of the scans from the other corners against central
+    finite differences of those scans (x, delta, A, B)."""
+    ins = _inputs(1, 2, 2, 3, 4, 42)
+    dy = np.random.default_rng(42).standard_normal(ins["x"].shape)
+    for fh, fw in ((True, False), (False, True), (True, True)):
+        g = oracle.bwd(*(ins[k] for k in KEYS), dy, lib=oracle_lib, flip_h=fh, flip_w=fw)
+
+        def loss():
+            return float(np.sum(oracle.fwd(*(ins[k] for k in KEYS), lib=oracle_lib, flip_h=fh, flip_w=fw) * dy))
+
+        for k in ("x", "delta", "A", "B"):
+            base = ins[k]
+            fd = np.empty_like(base)
+            for idx in np.ndindex(base.shape):
+                h = 1e-6 * max(1.0, abs(base[idx]))
+                orig = base[idx]
+                base[idx] = orig + h
+                lp = loss()
+                base[idx] = orig - h
+                lm = loss()
+                base[idx] = orig
+                fd[idx] = (lp - lm) / (2 * h)
+            err = np.max(np.abs(g[GRAD[k]] - fd) / (1.0 + np.abs(fd)))
+            assert err < 1e-6, f"{GRAD[k]} flips {fh},{fw}: {err:.2e}"
