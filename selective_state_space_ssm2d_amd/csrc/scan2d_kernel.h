@@ -462,13 +462,15 @@ __device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long 
 }
 
 // Packet rows of a wave: x and delta of 64/G channels, B and C of G*NPL states.
-// The backward's packet also carries dy (64/G more rows).
+// The backward's packet also carries dy (64/G more rows). Its adjoint pass
+// prefetches one row per buffer: its rows are long enough to hide the loads,
+// and the registers saved keep it free of spills.
 template <int NPL, int G, int MODE = 0>
 constexpr int packet_rows() { return 2 * (kWave / G) + 2 * G * NPL + ((MODE & kModeBackward) ? kWave / G : 0); }
 template <int NPL, int G, int MODE = 0>
 constexpr int passes_for(int K) { return (packet_rows<NPL, G, MODE>() * (K / 4) + kWave - 1) / kWave; }
 template <int NPL, int G, int MODE = 0>
-constexpr int prefetch_rows(int K) { return (passes_for<NPL, G, MODE>(K) == 1 && !(MODE & kModeBackward)) ? 4 : 2; }
+constexpr int prefetch_rows(int K) { return (MODE & kModeBackward) ? 1 : (passes_for<NPL, G, MODE>(K) == 1 ? 4 : 2); }
 
 
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
