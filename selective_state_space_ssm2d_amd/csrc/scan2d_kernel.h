@@ -1525,7 +1525,13 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     prm.epoch = e->epoch;
-    prm.vec_store = env_int("SSM2D_VECSTORE", 1);
+    // Gathering a channel's cells into one lane pays for fp32 rows of 4-column
+    // strips (one 16-byte store instead of four 4-byte ones) and for the
+    // adjoint pass (two outputs a row). Otherwise, for 8-column strips and for
+    // 2-byte cells, the gather costs more VALU work than the scattered stores,
+    // which the memory system coalesces anyway.
+    prm.vec_store =
+        env_int("SSM2D_VECSTORE", ((sizeof(T) == 4 && pl.K == 4) || (MODE & kModeBackward)) ? 1 : 0);
     prm.flip_h = pl.flip_h;
     if (pl.bw) {
         prm.states = pl.bw->states;
