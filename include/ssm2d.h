@@ -292,9 +292,8 @@ const char *ssm2d_last_hip_error(void);
  *   SSM2D_WAVES=n        strips per workgroup (forces chains across workgroups)
  *   SSM2D_COOP=0         per-wave input packets instead of the shared row ring
  *   SSM2D_VECSTORE=0|1   cell-by-cell output stores, or each channel's cells
- *                        gathered into 16-byte stores (default: 1 for fp32
- *                        maps with 4-column strips and for the backward,
- *                        else 0)
+ *                        gathered into wider stores (default: 1 for 4-column
+ *                        strips, 0 for 8-column strips)
  *   SSM2D_RING=n         depth of the global carry ring when the grid is co-resident
  *   SSM2D_LDSRING=4|16|32  depth of the LDS carry rings
  *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD */

@@ -330,8 +330,39 @@ __device__ __forceinline__ unsigned row_word(unsigned w, int r) { return __float
 // output type first (bf16 cells packed in pairs where a lane holds two), then
 // collected, in column order, in the channel's lane of row 0 (lane < 64 / G),
 // which stores them as whole chunks: K floats, or K bf16 values.
+// Exception, 4-column strips (row r holds cell r, in 4 or 8 groups): one swap
+// of odd and even rows leaves cells 0, 1 in row 0 and cells 2, 3 in row 2, and
+// the channel's lane in each of those rows stores its two cells (pair_lane and
+// pair_offset say which lanes and where).
+template <int K, int G>
+constexpr bool pair_store() { return K == 4; }
+template <int K, int G>
+__device__ __forceinline__ int pair_lane(int lane) { return pair_store<K, G>() ? (lane & ~32) : lane; }
+template <int K, int G, bool REV>
+__device__ __forceinline__ int pair_offset(int lane)
+{
+    // columns left to right: row 2's pair is the chunk's second half;
+    // right to left: row 0's pair is
+    return (pair_store<K, G>() && ((lane >> 5) & 1) != (REV ? 1 : 0)) ? 2 : 0;
+}
+template <bool REV>
+__device__ __forceinline__ void store_pair(float *p, float v, bool storer)
+{
+    // after the swap, lo holds cells 0 and 2 in rows 0 and 2, hi cells 1 and 3
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float lo = __uint_as_float(s[0]), hi = __uint_as_float(s[1]);
+    if (storer) *reinterpret_cast<float2 *>(p) = REV ? make_float2(hi, lo) : make_float2(lo, hi);
+}
+template <bool REV>
+__device__ __forceinline__ void store_pair(uint16_t *p, float v, bool storer)
+{
+    // one cell per lane; pairs as for fp32, packed in one word
+    const unsigned h = bf16_bits(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+    if (storer) *reinterpret_cast<unsigned *>(p) = REV ? (s[1] | (s[0] << 16)) : (s[0] | (s[1] << 16));
+}
 template <int K, int G, bool REV = false>
-__device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
+__device__ __forceinline__ void store_chunks(float *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
 {
     constexpr int KO = (K / G) > 0 ? K / G : 1;
     float cells[K];
@@ -341,10 +372,6 @@ __device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < KO; ++c) cells[r * KO + c] = from_row(v[c], r);
-    } else if constexpr (K == 4) {
-        // row r holds cell r (twice: groups 2r and 2r+1)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cells[r] = from_row(v[0], r);
     } else {
         // K = 8: in row r, lanes 0-7 (group 2r) hold cell 2r and lanes 8-15
         // (group 2r+1) cell 2r+1, which comes over 8 lanes.
@@ -368,7 +395,7 @@ __device__ __forceinline__ void store_row(float *p, const float (&v)[(K / G) > 0
     }
 }
 template <int K, int G, bool REV = false>
-__device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
+__device__ __forceinline__ void store_chunks(uint16_t *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
 {
     constexpr int KO = (K / G) > 0 ? K / G : 1;
     unsigned words[K / 2];  // two bf16 cells per word, column order
@@ -380,14 +407,6 @@ __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) 
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < KO / 2; ++c) words[r * KO / 2 + c] = row_word(w[c], r);
-    } else if constexpr (K == 4) {
-        // one cell per lane: rows 0..3 hold cells 0..3
-        const unsigned h = bf16_bits(v[0]);
-        unsigned t[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] = row_word(h, r);
-        words[0] = t[0] | (t[1] << 16);
-        words[1] = t[2] | (t[3] << 16);
     } else {
         static_assert(G == 8 && K == 8, "bf16 row store layouts");
         const unsigned h = bf16_bits(v[0]);
@@ -405,10 +424,13 @@ __device__ __forceinline__ void store_row(uint16_t *p, const float (&v)[(K / G) 
 #pragma unroll
         for (int c = 0; c < K / 2; ++c) words[c] = t[c];
     }
-    if (storer) {
-        if constexpr (K == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(words[0], words[1]);
-        else *reinterpret_cast<uint4 *>(p) = make_uint4(words[0], words[1], words[2], words[3]);
-    }
+    if (storer) *reinterpret_cast<uint4 *>(p) = make_uint4(words[0], words[1], words[2], words[3]);
+}
+template <int K, int G, bool REV = false, typename T>
+__device__ __forceinline__ void store_row(T *p, const float (&v)[(K / G) > 0 ? K / G : 1], bool storer)
+{
+    if constexpr (pair_store<K, G>()) store_pair<REV>(p, v[0], storer);
+    else store_chunks<K, G, REV>(p, v, storer);
 }
 
 __device__ __forceinline__ void sleep_a_bit() { __builtin_amdgcn_s_sleep(2); }
@@ -798,9 +820,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // channel's cells are gathered into one lane of row 0 and stored as
         // chunks; other strips, and accumulating calls, store cell by cell.
         const bool vec_store = !ACC && (ALIGN == 4) && (valid == K) && p.vec_store;
-        const bool vec_lane = (lane < CPW) && d_ok;
+        const bool vec_lane = (pair_lane<K, G>(lane) < CPW) && d_ok;
         T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + row0 +
-                  (FW ? W - j0 - K : j0);
+                  (FW ? W - j0 - K : j0) + pair_offset<K, G, FW>(lane);
         // Backward: d delta goes where dx goes, in its own tensor: the same
         // addresses moved by the distance between the two tensors (zero for
         // lanes writing the sink). Offsets keep the stores on global pointers.
@@ -1525,13 +1547,10 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     prm.epoch = e->epoch;
-    // Gathering a channel's cells into one lane pays for fp32 rows of 4-column
-    // strips (one 16-byte store instead of four 4-byte ones) and for the
-    // adjoint pass (two outputs a row). Otherwise, for 8-column strips and for
-    // 2-byte cells, the gather costs more VALU work than the scattered stores,
-    // which the memory system coalesces anyway.
-    prm.vec_store =
-        env_int("SSM2D_VECSTORE", ((sizeof(T) == 4 && pl.K == 4) || (MODE & kModeBackward)) ? 1 : 0);
+    // Gathered stores pay for 4-column strips (one row swap, two cells a lane).
+    // Gathering the eight cells of an 8-column strip costs more VALU work than
+    // the scattered stores, which the memory system coalesces anyway.
+    prm.vec_store = env_int("SSM2D_VECSTORE", pl.K == 4 ? 1 : 0);
     prm.flip_h = pl.flip_h;
     if (pl.bw) {
         prm.states = pl.bw->states;

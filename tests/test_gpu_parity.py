@@ -117,6 +117,30 @@ def test_wide_strips(shape, groups, monkeypatch):
     check(as_f64(run_gpu(t, "f32")), ref_of(t), "f32", f"K=8 {shape} groups={groups}")
 
 
+@pytest.mark.parametrize("vec", ["0", "1"])
+@pytest.mark.parametrize("strip", ["4", "8"])
+@pytest.mark.parametrize("groups", ["4", "8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_store_forms(vec, strip, groups, dtype, monkeypatch):
+    """Both output store forms (one cell per lane, or a channel's cells
+    gathered into wider stores) for every strip width, lane layout and type,
+    scanning rows left to right and right to left (the other directions run
+    8 groups and 4-column strips). Rows are 4-aligned; with 8-column strips the
+    last strip is partial and stores its cells one by one."""
+    monkeypatch.setenv("SSM2D_VECSTORE", vec)
+    monkeypatch.setenv("SSM2D_STRIP", strip)
+    monkeypatch.setenv("SSM2D_GROUPS", groups)
+    shape = (2, 24, 16, 11, 44)
+    _say(f"store form vec={vec} K={strip} groups={groups} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape), dtype=dtype)
+    check(as_f64(run_gpu(t, dtype)), ref_of(t), dtype, f"vec={vec} K={strip} groups={groups}")
+    args = to_dev(t, dtype)
+    y = pkg.scan_fwd_ex(*args, flags=pkg.FLIP_W)
+    pkg.sync_check()
+    ref = oracle.fwd(*(t[k] for k in KEYS), flip_w=True)
+    check(as_f64(y), ref, dtype, f"flip_w vec={vec} K={strip} groups={groups}")
+
+
 @pytest.mark.parametrize("groups", ["4", "8"])
 @pytest.mark.parametrize("waves", ["1", "2", "3", "8"])
 def test_multi_workgroup_chains(waves, groups, monkeypatch):
