@@ -1577,14 +1577,15 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
 }
 
-// Launch of a right-to-left, vertical-first and / or accumulating scan: 8 state groups,
-// 4-column strips, per-wave packets, align 4 or 1. Instantiated by one
-// translation unit per (input type, mode).
+// Launch of a right-to-left, vertical-first, accumulating, gated, stored-state
+// or adjoint scan: 8 state groups; 4-column strips (per-wave packets, align 4
+// or 1, or the shared row ring) or, for the forward modes, 8-column strips
+// (align 4). Instantiated by one translation unit per (input type, mode).
 template <typename T, int MODE>
 int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
                   int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream, int align)
 {
-    if (pl.G != 8 || pl.K != 4) return SSM2D_ERR_UNSUPPORTED;
+    if (pl.G != 8 || (pl.K != 4 && pl.K != 8)) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & (kModeStates | kModeBackward)) && !pl.bw) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & kModeGate) && !pl.z) return SSM2D_ERR_UNSUPPORTED;
     if (pl.coop_slots != 0) {
@@ -1595,6 +1596,17 @@ int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const 
     if (pl.npl == NN) return run<T, 4, NN, 4, 8, true, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
             SSM2D_MODE_COOP(1) SSM2D_MODE_COOP(2) SSM2D_MODE_COOP(4) SSM2D_MODE_COOP(8)
 #undef SSM2D_MODE_COOP
+        }
+        return SSM2D_ERR_UNSUPPORTED;
+    }
+    if (pl.K == 8) {
+        // 8-column strips: rows of a multiple of 4 columns, at most 4 states a lane
+        if constexpr (!(MODE & (kModeStates | kModeBackward))) {
+            if (align != 4) return SSM2D_ERR_UNSUPPORTED;
+#define SSM2D_MODE_WIDE(NN) \
+    if (pl.npl == NN) return run<T, 8, NN, 4, 8, false, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+            SSM2D_MODE_WIDE(1) SSM2D_MODE_WIDE(2) SSM2D_MODE_WIDE(4)
+#undef SSM2D_MODE_WIDE
         }
         return SSM2D_ERR_UNSUPPORTED;
     }
@@ -1620,8 +1632,10 @@ SSM2D_DISPATCH_DECL(float, dispatch_g4)
 SSM2D_DISPATCH_DECL(float, dispatch_g8)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g4)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
-// The other modes (8 state groups, 4-column strips, per-wave packets; align 2
-// is served by the align-1 kernels), one translation unit per (type, mode).
+// The other modes (8 state groups; 4-column strips with per-wave packets or
+// the shared row ring, align 2 served by the align-1 kernels; 8-column strips
+// for the forward modes on rows of a multiple of 4 columns), one translation
+// unit per (type, mode).
 #define SSM2D_MODE_DECLS(TT)                         \
     SSM2D_DISPATCH_DECL(TT, dispatch_flipw)          \
     SSM2D_DISPATCH_DECL(TT, dispatch_vfirst)         \

@@ -43,14 +43,16 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     // stay in LDS), widening the strips to 8 columns if that makes the chain
     // fit. Otherwise chains are cut into groups of s_local strips linked by two
     // courier waves (so at most maxw - 2 strips per workgroup).
-    const bool wide_ok = npl <= 4 && W % 4 == 0 && mode == 0;
+    // 8-column strips: forward scans of any direction and order; the
+    // backward's passes keep 4-column strips (one tile layout)
+    const bool wide_ok = npl <= 4 && W % 4 == 0 && !(mode & (kModeStates | kModeBackward));
     pl.K = 4;
     if (pl.n_chains >= want_wg && (W + 3) / 4 > max_waves(4, npl, G, mode) && wide_ok &&
         (W + 7) / 8 <= max_waves(8, npl, G, mode))
         pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
-    if (mode != 0) pl.K = 4;
+    if (mode & (kModeStates | kModeBackward)) pl.K = 4;
     const int maxw = max_waves(pl.K, npl, G, mode);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;

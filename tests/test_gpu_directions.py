@@ -146,6 +146,38 @@ def test_four_way(shape, dtype, vf):
         check(y2, 2 * ref, dtype, f"four-way accumulated {shape}")
 
 
+WIDE_SHAPES = [(2, 24, 16, 9, 44), (1, 16, 8, 6, 40), (1, 8, 32, 5, 36)]
+
+
+@pytest.mark.parametrize("d", DIRS, ids=_name)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=str)
+def test_directions_wide_strips(shape, dtype, d, monkeypatch):
+    """8-column strips in every direction and order (1, 2 and 4 states a
+    lane; the last strip half full where W % 8 == 4), accumulated too."""
+    monkeypatch.setenv("SSM2D_STRIP", "8")
+    fh, fw, vf = d
+    _say(f"wide strips {_name(d)} {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 3, dtype=dtype)
+    ref = ref_ex(t, flip_h=fh, flip_w=fw, vertical_first=vf)
+    y = run_ex(t, dtype, flip_h=fh, flip_w=fw, vertical_first=vf)
+    check(as_f64(y), ref, dtype, f"K=8 {_name(d)} {shape}")
+    if dtype == "f32":
+        y2 = as_f64(run_ex(t, dtype, y=y, accumulate=True, flip_h=fh, flip_w=fw, vertical_first=vf))
+        check(y2, 2 * ref, dtype, f"K=8 accumulated {_name(d)} {shape}")
+
+
+@pytest.mark.parametrize("vf", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_four_way_wide_strips(dtype, vf, monkeypatch):
+    monkeypatch.setenv("SSM2D_STRIP", "8")
+    shape = WIDE_SHAPES[0]
+    _say(f"four-way wide strips vf={vf} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 4, dtype=dtype)
+    y = run_ex(t, dtype, four_way=True, vertical_first=vf)
+    check_sum(as_f64(y), ref_ex(t, four_way=True, vertical_first=vf), _terms(t, vf), dtype, f"four-way K=8 {shape}")
+
+
 def test_four_way_deterministic_and_in_bounds():
     t = make_random_inputs(2, 17, 16, 13, 21, seed=8)
     args = to_dev(t, "f32")

@@ -139,6 +139,31 @@ def test_carried_states(case, dtype, d, monkeypatch):
     check(hl.double().cpu().numpy(), ref_hl, "f32", f"h_last {shape} {d}")
 
 
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)), ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_and_carried_states_wide_strips(dtype, d, monkeypatch):
+    """8-column strips (the last one half full): gated output, and a seeded
+    h_init with the returned h_last, in every direction and order."""
+    monkeypatch.setenv("SSM2D_STRIP", "8")
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    shape = (2, 16, 16, 7, 44)
+    _say(f"wide strips gate / carried states {d} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 31, dtype=dtype)
+    rng = np.random.default_rng(_seed(shape) + 32)
+    z, z_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, **kw)
+    pkg.sync_check()
+    check(as_f64(y), oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, **kw), dtype, f"K=8 gated {d}")
+    b, di, n, H, W = shape
+    h0 = rng.standard_normal((b, di, n, W)).astype(np.float32)
+    y, hl = pkg.scan_fwd_mamba(*to_dev(t, dtype), h_init=torch.from_numpy(h0).cuda(), return_last_state=True, **kw)
+    pkg.sync_check()
+    ref_y, ref_hl = oracle.fwd(*(t[k] for k in KEYS), h_init=h0, return_last=True, **kw)
+    check(as_f64(y), ref_y, dtype, f"K=8 carried y {d}")
+    check(hl.double().cpu().numpy(), ref_hl, "f32", f"K=8 h_last {d}")
+
+
 @pytest.mark.parametrize("vf", [False, True])
 def test_bands_equal_whole_map(vf):
     """Two bands of rows with the carried state in between give the whole
