@@ -142,6 +142,10 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
         "scan_fetch_counter_bytes": sf, "scan_write_counter_bytes": sw,
         "fetch_bytes_per_launch": sf * kf, "write_bytes_per_launch": sw * kw,
         "bytes_per_launch": sf * kf + sw * kw,
+        "commands": ["cd /tmp && export TMPDIR=/tmp && cd <repo>"]
+        + [PMC_SCAN_CMD.format(c=c, w=workload, v="" if variant == "fwd" else f" --variant {variant}")
+           for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        + [PMC_COPY_CMD.format(c=c, mb=copy_mb) for c in ("FETCH_SIZE", "WRITE_SIZE")],
     }
     out = os.path.join(ROOT, "profiles", f"traffic_{_tag(workload, variant)}.json")
     with open(out, "w") as f:
@@ -222,6 +226,11 @@ def cpu_baseline_bwd(wl, t, keys, seconds: float):
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
              "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline{v}")
+# One counter per run (rocprofv3 does not split counters over passes).
+PMC_SCAN_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- "
+                "python bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline{v}")
+PMC_COPY_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- "
+                "python bench.py --copy-probe {mb} --steps 5")
 
 
 def trace_summary(workload: str, run_dir: str, variant: str = "fwd") -> None:
