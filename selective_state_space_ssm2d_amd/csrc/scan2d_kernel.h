@@ -97,6 +97,7 @@ constexpr int max_waves(int K, int NPL, int G, int MODE = 0)
 constexpr int kCourierBatch = 4;               // rows a courier requests per poll
 constexpr int kMaxSlots = 16;                   // rows of a workgroup's shared row ring
 constexpr int kSpinPolls = 64;                  // polls of an LDS counter before sleeping between polls
+constexpr int kSkipWaits = 1 << 30;             // above every row index and counter
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Params {
@@ -852,6 +853,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         const float *ring_in = lring + static_cast<long>(wave) * ring_floats;
         float *ring_out = lring + static_cast<long>(wave + 1) * ring_floats;
         bool timed_out = false;
+        // 0, or kSkipWaits once a wait has timed out: the per-row checks
+        // compare max(counter, skip) with the row, so later waits are skipped
+        // without a separate test of timed_out on the fast path.
+        int skip = 0;
 
         float hv[K][NPL];
 #pragma unroll
@@ -902,6 +907,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             while (__builtin_amdgcn_readfirstlane(lds_peek(c)) < need) {
                 if (++spins > p.spin_limit) {
                     timed_out = true;
+                    skip = kSkipWaits;
                     break;
                 }
                 if (spins > kSpinPolls) sleep_a_bit();
@@ -913,6 +919,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // arithmetic. B, C and the skip input are read when the row starts.
         struct Ops {
             float xv[K], dv[K];
+        };
+        auto read_ops = [&](const T *pk, Ops &o) {
+            read_packet<K, FW>(pk, off_x, o.xv);
+            read_packet<K, FW>(pk, off_dt, o.dv);
         };
         // Stage input for row t and issue the reads of this lane's x and delta
         // of row t (their latency hides behind the current row). Per-wave
@@ -937,27 +947,22 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 signal_fence();
                 const int v = lds_peek(&s_arrive[t & slot_mask]);
                 signal_fence();
-                const T *pk = row_base(t);
-                read_packet<K, FW>(pk, off_x, o.xv);
-                read_packet<K, FW>(pk, off_dt, o.dv);
+                read_ops(row_base(t), o);
                 return v;
             } else {
                 T *pk = row_base(t);
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp) reinterpret_cast<Chunk *>(pk)[pp * kWave + lane] = cb[pp];
-                read_packet<K, FW>(pk, off_x, o.xv);
-                read_packet<K, FW>(pk, off_dt, o.dv);
+                read_ops(pk, o);
                 return 0;
             }
         };
         auto confirm = [&](const int t, const int seen_count, Ops &o) {
             if constexpr (COOP) {
                 const int need = nact * ((t >> p.coop_shift) + 1);
-                if (__builtin_amdgcn_readfirstlane(seen_count) < need && !timed_out) {
+                if (max(__builtin_amdgcn_readfirstlane(seen_count), skip) < need) {
                     wait_count(&s_arrive[t & slot_mask], need);
-                    const T *pk = row_base(t);
-                    read_packet<K, FW>(pk, off_x, o.xv);
-                    read_packet<K, FW>(pk, off_dt, o.dv);
+                    read_ops(row_base(t), o);
                 }
             }
         };
@@ -1070,13 +1075,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 // room in the right ring for row i (rarely short; checked here,
                 // off the carry's critical path)
                 if constexpr (RIGHT) {
-                    if (i >= room && !timed_out)
+                    if (i >= max(room, skip)) {
                         room = wait_counter_above(&s_used[wave + 1], i - p.ring_rows, p.spin_limit, timed_out) +
                                p.ring_rows;
+                        if (timed_out) skip = kSkipWaits;
+                    }
                 }
 
                 if constexpr (LEFT) {
-                    if (__builtin_amdgcn_readfirstlane(seen) <= i && !timed_out) {
+                    if (max(__builtin_amdgcn_readfirstlane(seen), skip) <= i) {
                         // Not published yet: poll. Each poll reads the counter
                         // and then the slot, back to back, so the poll that sees
                         // row i published has already fetched its carry (one
@@ -1102,6 +1109,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                             }
                             if (++spins > p.spin_limit) {
                                 timed_out = true;
+                                skip = kSkipWaits;
                                 break;
                             }
                             if (spins > kSpinPolls) sleep_a_bit();
@@ -1121,6 +1129,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                         if (__all(ok)) break;
                         if (++spins > p.spin_limit) {
                             timed_out = true;
+                            skip = kSkipWaits;
                             break;
                         }
                         if (spins > kSpinPolls) sleep_a_bit();
