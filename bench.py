@@ -255,6 +255,106 @@ def trace_summary(workload: str, run_dir: str, variant: str = "fwd") -> None:
     print("\n".join(lines))
 
 
+SWEEP_CMD = "python bench.py --workload {w} --shape-sweep {spec}"
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_BRANCH SQ_INSTS_VMEM SQ_INSTS_SMEM "
+               "SQ_WAIT_INST_LDS",
+               "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+               "SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES")
+
+
+def shape_sweep(wl, spec: str, reps: int = 20) -> None:
+    """Mean kernel time of the forward over maps of the workload's batch,
+    channels and states at other heights and widths ("HxW,HxW,..."), and for
+    each width timed at two or more heights the least-squares fit
+    t = fixed + H * per_row: a chain's pipeline start-up and drain against
+    its steady row rate. Writes profiles/shape_sweep_<workload>.txt."""
+    import torch
+
+    import selective_state_space_ssm2d_amd as pkg
+    from selective_state_space_ssm2d_amd.inputs import make_random_inputs
+
+    pkg.load_library()
+    dev = torch.device("cuda:0")
+    shapes = [tuple(int(v) for v in hw.split("x")) for hw in spec.split(",")]
+    lines = [f"# forward kernel time vs map shape, batch {wl.batch}, d_inner {wl.d_inner}, d_state {wl.d_state}, "
+             f"{wl.dtype}; inputs: make_random_inputs(seed 0), no pad cells",
+             f"# command: {SWEEP_CMD.format(w=wl.name, spec=spec)}",
+             f"# kernel source sha256[:16] {kernel_source_hash()}",
+             "# H | W | mean us | min us"]
+    res = {}
+    for H, W in shapes:
+        t = make_random_inputs(wl.batch, wl.d_inner, wl.d_state, H, W, seed=0, dtype=wl.dtype)
+        args = []
+        for k in ("x", "delta", "A", "B", "C", "D"):
+            if wl.dtype == "bf16" and k in ("x", "delta", "B", "C"):
+                args.append(torch.from_numpy(t[k + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16))
+            else:
+                args.append(torch.from_numpy(np.ascontiguousarray(t[k])).to(dev))
+        y = torch.empty_like(args[0])
+        for _ in range(5):
+            pkg.scan_fwd(*args, y=y)
+        pkg.sync_check()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            pkg.scan_fwd(*args, y=y)
+            b.record()
+        torch.cuda.synchronize()
+        pkg.sync_check()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        res[(H, W)] = float(us.mean())
+        lines.append(f"{H} | {W} | {us.mean():.1f} | {us.min():.1f}")
+        print(lines[-1], flush=True)
+    lines.append("# W | fixed us | us per row (fit over the heights timed at that width)")
+    for W in sorted({w for _, w in shapes}):
+        hs = sorted(h for h, w in shapes if w == W)
+        if len(hs) >= 2:
+            slope, icpt = np.polyfit(hs, [res[(h, W)] for h in hs], 1)
+            lines.append(f"{W} | {icpt:.1f} | {slope:.3f}")
+    out = os.path.join(ROOT, "profiles", f"shape_sweep_{wl.name}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counter_table(workload: str, dirs) -> None:
+    """Per-dispatch SQ counters of the scan kernel (median over dispatches)
+    from rocprofv3 --pmc runs of this benchmark, one run per counter group:
+    profiles/sq_counters_<workload>.txt."""
+    lines = [f"# rocprofv3 SQ counters of scan2d_fwd_kernel, workload {workload} (median per dispatch; "
+             "totals over the chip's waves)",
+             f"# kernel source sha256[:16] {kernel_source_hash()}"]
+    for grp in SQ_COUNTERS:
+        lines.append("# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && timeout -s KILL 90 rocprofv3 --pmc "
+                     f"{grp} --output-format csv -d <dir> -o pmc -- python bench.py --workload {workload} "
+                     "--steps 3 --warmup 1 --no-cpu-baseline")
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = {}
+            for r in csv.DictReader(open(f)):
+                if "scan2d_fwd_kernel" in r["Kernel_Name"]:
+                    key = (r["Dispatch_Id"], r["Counter_Name"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            for (_, name), v in per.items():
+                vals.setdefault(name, []).append(v)
+    if not vals:
+        raise SystemExit("no scan2d_fwd_kernel counter rows under " + " ".join(dirs))
+    med = {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+    for k in sorted(med):
+        lines.append(f"{k} | {med[k]:.6g}")
+    if "SQ_WAVE_CYCLES" in med:
+        lines.append("# fractions of SQ_WAVE_CYCLES")
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS"):
+            if k in med:
+                lines.append(f"{k} | {med[k] / med['SQ_WAVE_CYCLES']:.3f}")
+    out = os.path.join(ROOT, "profiles", f"sq_counters_{workload}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,7 +371,14 @@ def main():
     ap.add_argument("--copy-mb", type=int, default=512)
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run")
+    ap.add_argument("--shape-sweep", metavar="HxW,...",
+                    help="time the forward at other map heights and widths (fill against row rate)")
+    ap.add_argument("--counter-table", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/sq_counters_<workload>.txt from rocprofv3 --pmc output directories")
     args = ap.parse_args()
+    if args.counter_table:
+        counter_table(args.workload, args.counter_table)
+        return
     if args.trace_summary:
         trace_summary(args.workload, args.trace_summary, args.variant)
         return
@@ -296,6 +403,9 @@ def main():
 
         __graft_entry__.build()
     pkg.load_library()
+    if args.shape_sweep:
+        shape_sweep(wl, args.shape_sweep)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t = make_inputs(wl, seed=0)
