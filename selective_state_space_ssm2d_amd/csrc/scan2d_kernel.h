@@ -1589,14 +1589,27 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
 // Launch of a right-to-left, vertical-first, accumulating, gated, stored-state
 // or adjoint scan: 8 state groups; 4-column strips (per-wave packets, align 4
 // or 1, or the shared row ring) or, for the forward modes, 8-column strips
-// (align 4). Instantiated by one translation unit per (input type, mode).
+// (align 4); and for the forward modes 4 state groups with 4 states a lane
+// (4-column strips, per-wave packets, align 4 or 2). Instantiated by one
+// translation unit per (input type, mode).
 template <typename T, int MODE>
 int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
                   int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream, int align)
 {
-    if (pl.G != 8 || (pl.K != 4 && pl.K != 8)) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & (kModeStates | kModeBackward)) && !pl.bw) return SSM2D_ERR_UNSUPPORTED;
     if ((MODE & kModeGate) && !pl.z) return SSM2D_ERR_UNSUPPORTED;
+    if (pl.G == 4) {
+        // 4 state groups (16 channels a wave, 4 states a lane) for the forward
+        // modes: 4-column strips, per-wave packets, rows of an even length
+        if constexpr (!(MODE & (kModeStates | kModeBackward))) {
+            if (pl.K == 4 && pl.npl == 4 && pl.coop_slots == 0) {
+                if (align == 4) return run<T, 4, 4, 4, 4, false, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+                if (align == 2) return run<T, 4, 4, 2, 4, false, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+            }
+        }
+        return SSM2D_ERR_UNSUPPORTED;
+    }
+    if (pl.G != 8 || (pl.K != 4 && pl.K != 8)) return SSM2D_ERR_UNSUPPORTED;
     if (pl.coop_slots != 0) {
         // the shared row ring (tall maps cut into several workgroups per chain)
         if constexpr (!(MODE & kModeBackward)) {

@@ -31,7 +31,15 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
     int G = (d_state > 32 || (d_state > 4 && chains4 < 2 * want_wg)) ? 8 : 4;
     const int genv = env_int("SSM2D_GROUPS", 0);
     if (genv == 8 || (genv == 4 && d_state <= 32)) G = genv;
-    if (mode != 0) G = 8;  // the kernels of the other modes use 8 groups
+    // The other modes use 8 groups, except the forward modes on maps whose
+    // chains fit one workgroup of 4-column strips (W <= 32) with 9 to 16
+    // states and rows of an even number of columns: there they have 4-group
+    // kernels too (4 states a lane, like the forward's).
+    if (mode != 0) {
+        const bool g4_ok = G == 4 && d_state > 8 && d_state <= 16 && W % 2 == 0 && (W + 3) / 4 <= max_waves(4, 4, 4) &&
+                           !(mode & (kModeStates | kModeBackward));
+        if (!g4_ok) G = 8;
+    }
     pl.G = G;
     int npl = 1;
     while (npl * G < d_state) npl *= 2;
@@ -52,7 +60,7 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
         pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
-    if (mode & (kModeStates | kModeBackward)) pl.K = 4;
+    if ((mode & (kModeStates | kModeBackward)) || (mode != 0 && G == 4)) pl.K = 4;
     const int maxw = max_waves(pl.K, npl, G, mode);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
     int s_local;

@@ -212,7 +212,7 @@ def test_lower_right_support_bitwise():
 
 
 FULL = [("gigapixel_wsi", dict(four_way=True)), ("vmamba_t_s1", dict(flip_w=True, vertical_first=True)),
-        ("wsi_mil", dict(flip_h=True, flip_w=True))]
+        ("wsi_mil", dict(flip_h=True, flip_w=True)), ("grid14", dict(four_way=True, vertical_first=True))]
 
 
 @pytest.mark.parametrize("case", FULL, ids=lambda c: f"{c[0]}-{c[1]}")
@@ -281,3 +281,53 @@ def test_timeout_path_right_to_left(monkeypatch):
     pkg.sync_check()
     check(as_f64(run_ex(t, "f32", flip_w=True, vertical_first=True)),
           ref_ex(t, flip_w=True, vertical_first=True), "f32", "after timeout")
+
+
+# 4 state groups (16 channels a wave, 4 states a lane) in the direction,
+# order, accumulating and gated kernels: used for maps of at most 32 columns,
+# an even number of them, 9 to 16 states and many chains (the 14 x 14 grid);
+# forced here by the layout hook for small shapes with a ragged channel block,
+# rows of 14 (8-byte loads) and of 32 columns (16-byte loads).
+G4_SHAPES = [(2, 24, 16, 9, 14), (1, 20, 12, 7, 32)]
+
+
+@pytest.mark.parametrize("d", DIRS, ids=_name)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", G4_SHAPES, ids=str)
+def test_directions_four_groups(shape, dtype, d, monkeypatch):
+    monkeypatch.setenv("SSM2D_GROUPS", "4")
+    fh, fw, vf = d
+    _say(f"4 groups {shape} {_name(d)} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 3, dtype=dtype)
+    got = as_f64(run_ex(t, dtype, flip_h=fh, flip_w=fw, vertical_first=vf))
+    check(got, ref_ex(t, flip_h=fh, flip_w=fw, vertical_first=vf), dtype, f"4 groups {shape} {_name(d)}")
+
+
+@pytest.mark.parametrize("vf", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", G4_SHAPES, ids=str)
+def test_four_way_four_groups(shape, dtype, vf, monkeypatch):
+    monkeypatch.setenv("SSM2D_GROUPS", "4")
+    _say(f"4 groups four-way {shape} vf={vf} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 4, dtype=dtype)
+    got = as_f64(run_ex(t, dtype, four_way=True, vertical_first=vf))
+    check_sum(got, ref_ex(t, four_way=True, vertical_first=vf), _terms(t, vf), dtype,
+              f"4 groups four-way {shape} vf={vf}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", G4_SHAPES, ids=str)
+def test_gate_four_groups(shape, dtype, monkeypatch):
+    monkeypatch.setenv("SSM2D_GROUPS", "4")
+    _say(f"4 groups gate {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 5, dtype=dtype)
+    z = np.random.default_rng(_seed(shape) + 6).standard_normal(t["x"].shape).astype(np.float32)
+    z_dev = torch.from_numpy(z).cuda()
+    if dtype == "bf16":
+        z_dev = z_dev.to(torch.bfloat16)
+        z = as_f64(z_dev).astype(np.float32)
+    for fw, vf in ((False, False), (True, True)):
+        y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, flip_w=fw, vertical_first=vf)
+        pkg.sync_check()
+        ref = oracle.fwd_mamba(*(t[k] for k in KEYS), z=z.astype(np.float64), flip_w=fw, vertical_first=vf)
+        check(as_f64(y), ref, dtype, f"4 groups gate {shape} flip_w={fw} vf={vf}")
