@@ -509,7 +509,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool EDGES = (MODE & kModeEdges) != 0;
     static_assert(!EDGES || BWD, "courier-free chains: adjoint pass only");
     static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
-    static_assert(!BWD || (!VF && !ACC && !STATES && K == 4 && G == 8 && !COOP), "backward: one layout");
+    static_assert(!BWD || (!VF && !ACC && !STATES && K == 4 && G == 8), "backward: one layout");
+    static_assert(!BWD || !COOP || EDGES, "backward with the shared row ring: courier-free chains only");
     static_assert(!STATES || (!VF && !ACC), "stored states: horizontal-first order");
     using Chunk = typename ChunkOf<T>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
@@ -1611,12 +1612,16 @@ int dispatch_mode(const T *x, const T *delta, const float *A, const T *B, const 
     }
     if (pl.G != 8 || (pl.K != 4 && pl.K != 8)) return SSM2D_ERR_UNSUPPORTED;
     if (pl.coop_slots != 0) {
-        // the shared row ring (tall maps cut into several workgroups per chain)
-        if constexpr (!(MODE & kModeBackward)) {
+        // the shared row ring (tall maps cut into several workgroups per chain;
+        // for the adjoint pass, its courier-free kernels)
+        if constexpr (!(MODE & kModeBackward) || (MODE & kModeEdges)) {
             if (align != 4) return SSM2D_ERR_UNSUPPORTED;
 #define SSM2D_MODE_COOP(NN) \
     if (pl.npl == NN) return run<T, 4, NN, 4, 8, true, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
-            SSM2D_MODE_COOP(1) SSM2D_MODE_COOP(2) SSM2D_MODE_COOP(4) SSM2D_MODE_COOP(8)
+            SSM2D_MODE_COOP(1) SSM2D_MODE_COOP(2) SSM2D_MODE_COOP(4)
+            if constexpr (!(MODE & kModeBackward)) {  // the backward keeps at most 4 states per lane
+                SSM2D_MODE_COOP(8)
+            }
 #undef SSM2D_MODE_COOP
         }
         return SSM2D_ERR_UNSUPPORTED;

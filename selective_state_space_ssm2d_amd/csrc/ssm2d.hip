@@ -352,16 +352,18 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // Cooperative loads (a shared ring of input rows per workgroup): 8-group
 // layouts with 4-column strips and 4-aligned rows, when a workgroup holds part
 // of a chain of a tall map (short maps do not repay the ring's start-up), if
-// the row ring fits; not for the adjoint pass.
+// the row ring fits; for the adjoint pass, with its courier-free chains.
 template <typename T>
 void choose_coop(Plan &pl, int64_t H, int align)
 {
     pl.coop_slots = 0;
-    if ((pl.mode & kModeBackward) || pl.G != 8 || pl.K != 4 || align != 4 || pl.groups <= 1 || H < 128 ||
-        !env_int("SSM2D_COOP", 1))
+    if (((pl.mode & kModeBackward) && !(pl.mode & kModeEdges)) || pl.G != 8 || pl.K != 4 || align != 4 ||
+        pl.groups <= 1 || H < 128 || !env_int("SSM2D_COOP", 1))
         return;
     using Chunk = typename ChunkOf<T>::type;
-    const size_t nchunk = static_cast<size_t>(16 + 16 * pl.npl);
+    // packet rows: x and delta of 8 channels, B and C of 8 * npl states, and
+    // dy of the 8 channels in the adjoint pass
+    const size_t nchunk = static_cast<size_t>(16 + 16 * pl.npl + ((pl.mode & kModeBackward) ? 8 : 0));
     const size_t rings = static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * pl.npl * 4;
     for (int slots = kMaxSlots; slots >= 8 && pl.coop_slots == 0; slots /= 2)
         if (static_cast<size_t>(pl.s_local) * slots * (nchunk + 1) * sizeof(Chunk) + rings <= 144 * 1024)
@@ -556,6 +558,7 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (edges) pb = make_plan(batch, d_inner, d_state, H, W, bmode | kModeEdges);
     pb.flip_h = f_h ? 0 : 1;
     pb.bw = &bw;
+    choose_coop<T>(pb, H, align);
     if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     if (f_w)
         st = edges ? dispatch_bwd_ltr_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)

@@ -244,9 +244,11 @@ def test_backward_other_directions(shape, fl, dtype):
 
 @pytest.mark.parametrize("fl", FLIPS, ids=lambda f: ("H" if f[0] else "-") + ("W" if f[1] else "-"))
 @pytest.mark.parametrize("case", [((1, 16, 16, 33, 80), "1", "f32"), ((1, 8, 16, 21, 130), "3", "bf16"),
-                                  ((1, 16, 16, 160, 96), None, "f32")], ids=str)
+                                  ((1, 16, 16, 160, 96), None, "f32"), ((1, 8, 16, 150, 64), None, "bf16")],
+                         ids=str)
 def test_backward_other_directions_chains(case, fl, monkeypatch):
-    """Other corners with chains across workgroups, and a tall map."""
+    """Other corners with chains across workgroups, and tall maps (the
+    stored-state pass and the adjoint pass both use the shared row ring)."""
     shape, waves, dtype = case
     if waves:
         monkeypatch.setenv("SSM2D_WAVES", waves)
