@@ -492,8 +492,18 @@ template <int NPL, int G, int MODE = 0>
 constexpr int packet_rows() { return 2 * (kWave / G) + 2 * G * NPL + ((MODE & kModeBackward) ? kWave / G : 0); }
 template <int NPL, int G, int MODE = 0>
 constexpr int passes_for(int K) { return (packet_rows<NPL, G, MODE>() * (K / 4) + kWave - 1) / kWave; }
-template <int NPL, int G, int MODE = 0>
-constexpr int prefetch_rows(int K) { return (MODE & kModeBackward) ? 1 : (passes_for<NPL, G, MODE>(K) == 1 ? 4 : 2); }
+// The stored-state pass with the shared row ring prefetches 8 rows per
+// buffer: its state stores share the in-order vector-memory counter with the
+// row loads, so a row's load is waited for only after every store issued
+// before it, and the longer distance lets those stores drain first. (With
+// per-wave packets the extra registers would spill.)
+template <int NPL, int G, int MODE = 0, bool COOP = false>
+constexpr int prefetch_rows(int K)
+{
+    if constexpr ((MODE & kModeBackward) != 0) return 1;
+    if (passes_for<NPL, G, MODE>(K) != 1) return 2;
+    return ((MODE & kModeStates) && COOP) ? 8 : 4;
+}
 
 
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
@@ -521,7 +531,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr int CPR = K / 4;                        // chunks per packet row
     constexpr int NCHUNK = SEGROWS * CPR;
     constexpr int PASSES = passes_for<NPL, G, MODE>(K);
-    constexpr int P = prefetch_rows<NPL, G, MODE>(K);  // rows per prefetch buffer
+    constexpr int P = prefetch_rows<NPL, G, MODE, COOP>(K);  // rows per prefetch buffer
 
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_done[kMaxWaves + 1];   // rows published into LDS ring b
