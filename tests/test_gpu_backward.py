@@ -135,13 +135,14 @@ def test_backward_full_workloads(name):
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), wl.dtype, wl.batch * wl.H * wl.W, name)
 
 
-def test_backward_tall_map():
-    """A tall map: the stored-state pass uses the shared row ring."""
-    shape = (1, 16, 16, 160, 96)
+@pytest.mark.parametrize("shape", [(1, 16, 16, 160, 96), (1, 8, 4, 140, 48), (1, 8, 32, 130, 64)], ids=str)
+def test_backward_tall_map(shape):
+    """Tall maps (1, 2 and 4 states a lane): the stored-state pass and the
+    adjoint pass use the shared row ring."""
     t = make_random_inputs(*shape, seed=32)
     dy, dy_dev = make_dy(t, "f32", 33)
     got = run_bwd(t, "f32", dy_dev)
-    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", 160 * 96, "tall map")
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy), "f32", shape[3] * shape[4], f"tall map {shape}")
 
 
 def test_backward_timeout_path_reports_and_recovers(monkeypatch):
@@ -244,7 +245,8 @@ def test_backward_other_directions(shape, fl, dtype):
 
 @pytest.mark.parametrize("fl", FLIPS, ids=lambda f: ("H" if f[0] else "-") + ("W" if f[1] else "-"))
 @pytest.mark.parametrize("case", [((1, 16, 16, 33, 80), "1", "f32"), ((1, 8, 16, 21, 130), "3", "bf16"),
-                                  ((1, 16, 16, 160, 96), None, "f32"), ((1, 8, 16, 150, 64), None, "bf16")],
+                                  ((1, 16, 16, 160, 96), None, "f32"), ((1, 8, 16, 150, 64), None, "bf16"),
+                                  ((1, 8, 4, 140, 48), None, "f32"), ((1, 8, 32, 130, 64), None, "f32")],
                          ids=str)
 def test_backward_other_directions_chains(case, fl, monkeypatch):
     """Other corners with chains across workgroups, and tall maps (the
