@@ -31,6 +31,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # Plain fp32 VALU issue rate (no packed fp32): 256 CU x 4 SIMD x 16 lanes x
@@ -121,7 +122,7 @@ def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str):
 
 
 def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
-                copy_mb: int, variant: str = "fwd") -> None:
+                copy_mb: int, variant: str = "fwd", out_dir: str = PROFILES) -> dict:
     """Turns four rocprofv3 --pmc runs (scan FETCH_SIZE, scan WRITE_SIZE, copy
     FETCH_SIZE, copy WRITE_SIZE; KiB per dispatch) into calibrated HBM bytes
     per launch of the scan kernel: profiles/traffic_<workload>[_<variant>].json."""
@@ -147,10 +148,11 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
            for c in ("FETCH_SIZE", "WRITE_SIZE")]
         + [PMC_COPY_CMD.format(c=c, mb=copy_mb) for c in ("FETCH_SIZE", "WRITE_SIZE")],
     }
-    out = os.path.join(ROOT, "profiles", f"traffic_{_tag(workload, variant)}.json")
+    out = os.path.join(out_dir, f"traffic_{_tag(workload, variant)}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+    return rec
 
 
 def cpu_baseline(wl, t, keys, seconds: float, kw=None):
@@ -233,7 +235,7 @@ PMC_COPY_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d 
                 "python bench.py --copy-probe {mb} --steps 5")
 
 
-def trace_summary(workload: str, run_dir: str, variant: str = "fwd") -> None:
+def trace_summary(workload: str, run_dir: str, variant: str = "fwd", out_dir: str = PROFILES) -> None:
     """Writes profiles/kernel_stats_<workload>[_<variant>].txt from the kernel
     statistics of a rocprofv3 --kernel-trace --stats run of this benchmark."""
     files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -249,7 +251,7 @@ def trace_summary(workload: str, run_dir: str, variant: str = "fwd") -> None:
         short = r["Name"].replace("(anonymous namespace)::", "").removeprefix("void ").split("(")[0][:110]
         lines.append(f"{short} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.1f} | "
                      f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
-    out = os.path.join(ROOT, "profiles", f"kernel_stats_{_tag(workload, variant)}.txt")
+    out = os.path.join(out_dir, f"kernel_stats_{_tag(workload, variant)}.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -311,13 +313,13 @@ def shape_sweep(wl, spec: str, reps: int = 20) -> None:
         if len(hs) >= 2:
             slope, icpt = np.polyfit(hs, [res[(h, W)] for h in hs], 1)
             lines.append(f"{W} | {icpt:.1f} | {slope:.3f}")
-    out = os.path.join(ROOT, "profiles", f"shape_sweep_{wl.name}.txt")
+    out = os.path.join(PROFILES, f"shape_sweep_{wl.name}.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def counter_table(workload: str, dirs) -> None:
+def counter_table(workload: str, dirs, out_dir: str = PROFILES) -> dict:
     """Per-dispatch SQ counters of the scan kernel (median over dispatches)
     from rocprofv3 --pmc runs of this benchmark, one run per counter group:
     profiles/sq_counters_<workload>.txt."""
@@ -349,10 +351,11 @@ def counter_table(workload: str, dirs) -> None:
                   "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS"):
             if k in med:
                 lines.append(f"{k} | {med[k] / med['SQ_WAVE_CYCLES']:.3f}")
-    out = os.path.join(ROOT, "profiles", f"sq_counters_{workload}.txt")
+    out = os.path.join(out_dir, f"sq_counters_{workload}.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    return med
 
 
 def main():
@@ -389,7 +392,7 @@ def main():
         copy_probe(args.copy_probe, max(1, args.steps))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
@@ -476,7 +479,7 @@ def main():
     # HBM bytes per launch from the committed counter summary, only while it
     # describes the kernel as it is now
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{_tag(wl.name, args.variant)}.json")
+    tpath = os.path.join(PROFILES, f"traffic_{_tag(wl.name, args.variant)}.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
