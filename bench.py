@@ -34,17 +34,22 @@ sys.path.insert(0, ROOT)
 PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-# Plain fp32 VALU issue rate (no packed fp32): 256 CU x 4 SIMD x 16 lanes x
-# 2.4 GHz = 39.3e12 slots/s; an FMA slot is 2 flops -> 78.6 TFLOP/s.
-ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
-# Algorithmic ALU work per (element, state): 2 mul + 3 FMA + 1 exp2, and exp2
-# issues at half rate on gfx950 (2 slots), so 7 slots = 14 FMA-equivalent flops.
-SLOTS_PER_ELEM_STATE = 7
-# Backward per (element, state): the forward's 7 to recompute the states, then
-# 22 for the adjoint: Abar (1 mul + exp2 = 3), u (1), g_h and its carry (2),
+# Secondary ALU view. The published fp32 vector peak is 157.3 TFLOP/s (256 CU
+# x 4 SIMD x 16 lanes x 2.4 GHz x 2 flops per FMA x 2 for packed fp32); this
+# library builds without packed fp32 instructions, so its issue ceiling is
+# half that: 39.3e12 VALU slots/s, 78.6 TFLOP/s counting an FMA as 2 flops.
+ALU_PEAK_TFLOPS = 157.3
+ALU_ISSUE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# Algorithmic work per (element, state): 1 exp2, 2 multiplies and 3 FMAs:
+# 6 VALU instructions (each counted as one issue slot), 9 flops (exp 1,
+# multiply 1, FMA 2).
+SLOTS_PER_ELEM_STATE = 6
+FLOPS_PER_ELEM_STATE = 9
+# Backward per (element, state): the forward's 6 to recompute the states, then
+# 21 for the adjoint: Abar (1 mul + exp2 = 2), u (1), g_h and its carry (2),
 # the carried g_hh (2), hh (1), g_a Abar (4), g_hh B (1), d delta (2), dx (1),
 # dB and dC terms (2), dA (1), and the sums over channels for dB, dC (2).
-SLOTS_PER_ELEM_STATE_BWD = 7 + 22
+SLOTS_PER_ELEM_STATE_BWD = 6 + 21
 
 METRIC = "2D-scan elements/s (B·D·H·W) + % of MI355X peak HBM GB/s"
 
@@ -468,13 +473,14 @@ def main():
     if kw == "bwd":
         # reads x, delta, B, C, dy, A, D; writes dx, d delta, dB, dC, dA, dD
         step_bytes = algorithmic_bytes_bwd(wl)
-        flops = E * wl.d_state * SLOTS_PER_ELEM_STATE_BWD * 2
+        slots = E * wl.d_state * SLOTS_PER_ELEM_STATE_BWD
         launches = 1  # roofline figures below are per step (three kernels)
     else:
         step_bytes = abytes if launches == 1 else abytes + (launches - 1) * algorithmic_bytes(wl, accumulate=True)
-        flops = launches * E * wl.d_state * SLOTS_PER_ELEM_STATE * 2
+        slots = launches * E * wl.d_state * SLOTS_PER_ELEM_STATE
     gbs = step_bytes / (kmean * 1e-3) / 1e9
-    tflops = flops / (kmean * 1e-3) / 1e12
+    tflops = slots * FLOPS_PER_ELEM_STATE / SLOTS_PER_ELEM_STATE / (kmean * 1e-3) / 1e12
+    issue_floor_ms = slots / ALU_ISSUE_SLOTS_PER_S * 1e3
 
     # HBM bytes per launch from the committed counter summary, only while it
     # describes the kernel as it is now
@@ -507,13 +513,15 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "d_inner": wl.d_inner, "d_state": wl.d_state,
                    "H": wl.H, "W": wl.W, "pad": wl.pad, "pad_cells": wl.pad_cells,
                    "input_copies_cycled": ncopies, "variant": args.variant, "launches_per_step": launches},
-        "roofline": {"bound": "alu", "achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": step_bytes,
                      "kernel": "scan2d_fwd_kernel", "kernel_ms_mean": kmean / launches,
                      "kernel_ms_median": float(np.median(kern_ms)) / launches,
                      "kernel_ms_min": float(np.min(kern_ms)) / launches},
-        "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "algorithmic_bytes": step_bytes},
+        "alu": {"achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / ALU_PEAK_TFLOPS,
+                "flops_per_elem_state": FLOPS_PER_ELEM_STATE,
+                "slots_per_elem_state": SLOTS_PER_ELEM_STATE_BWD if kw == "bwd" else SLOTS_PER_ELEM_STATE,
+                "issue_floor_ms": issue_floor_ms / launches, "issue_frac": issue_floor_ms / kmean},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

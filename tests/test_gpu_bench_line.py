@@ -30,12 +30,20 @@ def test_bench_line():
     roof = d["roofline"]
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in roof, k
-    assert roof["bound"] == "alu" and roof["unit"] == "TFLOP/s"
+    # the named bound of the scan: HBM, algorithmic bytes over the mean launch
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert 0.0 < roof["frac"] < 1.0
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-9)
-    # 7 issue slots (14 flops) per (element, state) over the mean launch time
-    assert roof["achieved"] == pytest.approx(elements * d["config"]["d_state"] * 14 / (roof["kernel_ms_mean"] * 1e-3)
-                                             / 1e12, rel=1e-6)
+    c = d["config"]
+    abytes = elements * 12 + c["batch"] * c["d_state"] * c["H"] * c["W"] * 8 + c["d_inner"] * (c["d_state"] + 1) * 4
+    assert roof["algorithmic_bytes"] == abytes
+    assert roof["achieved"] == pytest.approx(abytes / (roof["kernel_ms_mean"] * 1e-3) / 1e9, rel=1e-6)
+    assert roof["kernel_ms_mean"] <= d["ms_per_step"] * 1.05
+    # secondary ALU view: 9 flops per (element, state) against the published fp32 peak
+    alu = d["alu"]
+    assert alu["peak"] == 157.3 and alu["unit"] == "TFLOP/s"
+    assert alu["achieved"] == pytest.approx(elements * c["d_state"] * 9 / (roof["kernel_ms_mean"] * 1e-3) / 1e12,
+                                            rel=1e-6)
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "elements/s" and cpu["cores"] >= 1 and cpu["value"] > 0
     assert cpu["sample"]
