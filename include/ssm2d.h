@@ -31,8 +31,28 @@
  * Asynchrony: a call validates its arguments on the host, enqueues its kernels
  * on `stream` (hipStream_t; NULL = the null stream) and returns without waiting.
  * Launch errors are reported as SSM2D_ERR_HIP. The library keeps an internal
- * workspace per (device, stream), zero-initialised when created; calls on the
- * same stream are ordered, calls on different streams use different workspaces.
+ * workspace per (device, stream); calls on the same stream are ordered, calls
+ * on different streams use different workspaces. A workspace is allocated and
+ * grown in stream order (hipMallocAsync / hipFreeAsync on `stream`, zeroed by
+ * a kernel on `stream`): no call waits for the host, and a call whose
+ * workspace is already large enough allocates nothing. ssm2d_release_workspaces
+ * frees a stream's workspaces.
+ *
+ * Graph capture: once a call of the same kind and size has run on `stream`
+ * (so that nothing is allocated), the calls may be captured into a HIP graph
+ * and replayed. The carry words that link the tiles of one map carry a tag
+ * epoch kept in device memory and advanced by every launch, so replays and
+ * launches never take each other's words.
+ *
+ * Carry waits: when a map's chain of tiles spans several workgroups, a tile
+ * waits for its left neighbour's carries; with a bounded carry ring the
+ * producer also waits for its consumer. All workgroups of such a launch must
+ * be able to run at once; kernels of other streams or processes that hold the
+ * GPU's compute units can delay them. A wait gives up after a bound (about a
+ * second; ssm2d_set_spin_limit): the outputs from that point on are NaN, the
+ * next call on the same (device, stream) returns SSM2D_ERR_DEVICE_TIMEOUT
+ * without enqueueing anything (read from a host-visible flag, no wait), and
+ * ssm2d_sync_check reports it too.
  *
  * Errors: every function returns a status and never throws or aborts.
  *   batch, d_inner, d_state, H or W < 0          -> SSM2D_ERR_BAD_DIM
@@ -44,6 +64,8 @@
  *   any NULL pointer when there is work          -> SSM2D_ERR_NULLPTR
  *   any pointer not 16-byte aligned              -> SSM2D_ERR_MISALIGNED
  *   workspace allocation failure                 -> SSM2D_ERR_NOMEM
+ *   a kernel of an earlier call on this (device, stream) timed out
+ *                                                -> SSM2D_ERR_DEVICE_TIMEOUT
  * NaN and Inf inputs are not checked; they propagate.
  */
 #ifndef SSM2D_H
@@ -142,9 +164,8 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
  * of that name, whose options around the scan are, for the 2D scan:
  *   step size  delta' = delta + delta_bias[d] (delta_bias may be NULL: 0),
  *              then softplus(delta') = log(1 + e^delta') if SSM2D_DELTA_SOFTPLUS;
- *              computed in fp32 by a separate pass and stored in the input
- *              type (bf16 inputs: delta' is rounded to bf16, nearest even)
- *              in a library workspace of batch*d_inner*H*W elements per
+ *              computed in fp32 by a separate pass and kept in fp32 in a
+ *              library workspace of batch*d_inner*H*W elements per
  *              (device, stream); the scan then runs on delta';
  *   gate       y = (sum_n C h + D x) * SiLU(z), SiLU(z) = z / (1 + e^-z), z
  *              shaped like x in x's type (z may be NULL: no gate);
@@ -169,7 +190,12 @@ int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, con
                          void *stream);
 
 /* bf16 variant: x, delta, B, C, z, y bfloat16 bits; A, D, delta_bias, h_init,
- * h_last float32. */
+ * h_last float32. With a step-size bias or softplus, and for SSM2D_FOUR_WAY
+ * (also through ssm2d_scan_fwd_ex_bf16), x, B and C are widened to fp32
+ * (exactly) in library workspaces, the fp32 kernels compute the result in
+ * an fp32 workspace (the four scans summed there), and y is rounded to bf16
+ * once, after the gate: nothing between the inputs and y is rounded to bf16.
+ * A gated single scan without those options rounds once in its kernel. */
 int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
                               const uint16_t *B, const uint16_t *C, const float *D,
                               const uint16_t *z, const float *delta_bias, const float *h_init,
@@ -199,7 +225,8 @@ int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const fl
  * of 4 * ceil(d_inner / 8) * batch * 4 * ceil(W / 4) * H * (64 npl + 2 d_state)
  * bytes, npl = d_state / 8 rounded up to a power of two (the stored states, 4
  * bytes per state and cell at d_state = 8 npl, plus the sums over 8-channel
- * blocks for dB and dC; grown when needed, kept until the process ends). dA and dD are accumulated with
+ * blocks for dB and dC; grown when needed, kept until ssm2d_release_workspaces
+ * or the end of the process). dA and dD are accumulated with
  * atomics, so their last bits may differ from run to run; every other output
  * is deterministic.
  * Errors as for ssm2d_scan_fwd (with d_state == 0, A, B, C, dA, dB and dC
@@ -211,10 +238,14 @@ int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const flo
                    float *dA, float *dB, float *dC, float *dD, int64_t batch, int64_t d_inner,
                    int64_t d_state, int64_t H, int64_t W, void *stream);
 
-/* Backward of ssm2d_scan_fwd_ex for the scan direction `flags` selects
- * (SSM2D_FLIP_H, SSM2D_FLIP_W; 0 gives ssm2d_scan_bwd): the stored-state pass
- * runs in the forward's direction, the adjoint from the opposite corner.
- * SSM2D_VERTICAL_FIRST -> SSM2D_ERR_UNSUPPORTED; SSM2D_ACCUMULATE,
+/* Backward of ssm2d_scan_fwd_ex for the scan direction and order `flags`
+ * selects (SSM2D_FLIP_H, SSM2D_FLIP_W, SSM2D_VERTICAL_FIRST; 0 gives
+ * ssm2d_scan_bwd): the stored-state pass runs in the forward's direction, the
+ * adjoint from the opposite corner. The vertical-first scan is the
+ * horizontal-first scan of the transposed maps (the flips trading places): its
+ * backward transposes x, delta, dy, B and C into library workspaces (five
+ * tensors, and four for the transposed gradients), runs the horizontal-first
+ * backward and transposes dx, ddelta, dB and dC back. SSM2D_ACCUMULATE,
  * SSM2D_FOUR_WAY, SSM2D_DELTA_SOFTPLUS or unknown bits -> SSM2D_ERR_BAD_FLAGS
  * (a four-corner sum's gradient is the sum of the four directions'). Otherwise
  * as ssm2d_scan_bwd. */
@@ -257,9 +288,12 @@ int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, con
                          float *dD, float *dz, float *ddelta_bias, int64_t batch, int64_t d_inner,
                          int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
 
-/* bf16 variant: x, delta, B, C, z, dy, dx, ddelta, dB, dC, dz bfloat16 bits; the
- * recomputed scan output and dy * SiLU(z) are held in bf16 as well (rounded to
- * nearest even), the prepared step size as in ssm2d_scan_fwd_mamba_bf16. */
+/* bf16 variant: x, delta, B, C, z, dy, dx, ddelta, dB, dC, dz bfloat16 bits.
+ * With any option (z, delta_bias or softplus) every tensor the chain rule
+ * hands on (the prepared step size, the recomputed scan output, dy * SiLU(z))
+ * is kept in fp32, x, B and C are widened to fp32 (exactly) and the fp32
+ * backward runs on them; each gradient is rounded to bf16 once. Without
+ * options it is ssm2d_scan_bwd_bf16. */
 int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
                               const uint16_t *B, const uint16_t *C, const float *D,
                               const uint16_t *z, const float *delta_bias, const uint16_t *dy,
@@ -271,11 +305,28 @@ int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const fl
 /* Static description of a status code. Never NULL. */
 const char *ssm2d_status_string(int status);
 
-/* Waits for `stream`, then returns and clears the device-side error word of
- * that stream's workspace: SSM2D_OK, or SSM2D_ERR_DEVICE_TIMEOUT if a kernel
- * gave up waiting for a neighbouring tile's carries (its output is then
- * invalid). Returns SSM2D_ERR_HIP if the wait fails. */
+/* Waits for `stream`, then returns and clears the timeout records of that
+ * stream's workspace (the device error word and the host-visible flag): SSM2D_OK,
+ * or SSM2D_ERR_DEVICE_TIMEOUT if a kernel gave up waiting for a neighbouring
+ * tile's carries (its outputs from that point on are NaN). Returns
+ * SSM2D_ERR_HIP if the wait fails. */
 int ssm2d_sync_check(void *stream);
+
+/* Waits for `stream`, then frees every workspace the library keeps for
+ * (current device, stream): the scan's carry ring and zero page, the
+ * backward's stored states, the scratch tensors of the option, widening and
+ * transposition passes, and the host-visible timeout flag. A later call
+ * allocates them again. Returns SSM2D_OK, SSM2D_ERR_DEVICE_TIMEOUT if a
+ * timeout was still unreported (the workspaces are freed anyway), or
+ * SSM2D_ERR_HIP. */
+int ssm2d_release_workspaces(void *stream);
+
+/* Test hook: waits for `stream` and sets the stored carry-tag epoch of that
+ * stream's workspace (value modulo 65535; a launch tags with stored + 1 and
+ * advances it). Setting 65534 makes the next launch that uses the carry ring
+ * the last before the epoch wraps, when the ring is cleared. Returns
+ * SSM2D_ERR_UNSUPPORTED if the stream has no workspace yet. */
+int ssm2d_test_set_epoch(void *stream, uint32_t epoch);
 
 /* Test hook: bound on the polls a kernel makes while waiting for carries
  * (0 = default, about one second). A tiny bound forces the timeout path. */

@@ -15,7 +15,8 @@ fwd(x, delta, A, B, C, D, maps=None, nthreads=0, flip_h=False, flip_w=False,
     vertical_first=False, four_way=False) -> y (float64)
 states(abar, bx, flip_h=False, flip_w=False, vertical_first=False) -> h
                         the recurrences alone on given Abar, Bx (one map)
-bwd(x, delta, A, B, C, D, dy) -> dict of dx, ddelta, dA, dB, dC, dD (float64)
+bwd(x, delta, A, B, C, D, dy, flip_h=False, flip_w=False, vertical_first=False)
+                        -> dict of dx, ddelta, dA, dB, dC, dD (float64)
 fwd_mamba(x, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=False, ...)
                         the scan with Mamba's step-size bias / softplus and SiLU(z) gating
 bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False)
@@ -190,22 +191,19 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, delta_round=None,
+def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
               maps=None, lib=None, **dirs):
     """The Mamba selective-scan operator's options around the 2D scan: the
     step size is delta + delta_bias[d] (bias per channel), passed through
     softplus when asked, and the output is gated by SiLU(z), z shaped like x
     (Mamba's selective_scan_fn options; the codewithpapers.app record lists
-    that function as the official code's entry point). ``delta_round`` (a function) is applied to the
-    effective step size before the scan, for inputs that store it rounded.
+    that function as the official code's entry point). Everything in fp64.
     ``dirs``: flip_h, flip_w, vertical_first, four_way as for fwd."""
     dt = np.asarray(delta, dtype=np.float64)
     if delta_bias is not None:
         dt = dt + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
     if delta_softplus:
         dt = softplus(dt)
-    if delta_round is not None:
-        dt = delta_round(dt)
     y = fwd(x, dt, A, B, C, D, maps=maps, lib=lib, **dirs)
     if z is not None:
         g = silu(z)
@@ -216,22 +214,16 @@ def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus
     return y
 
 
-def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, delta_round=None,
-              dy_round=None, lib=None):
+def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, lib=None):
     """Gradients of fwd_mamba (step-size bias and softplus, SiLU(z) gate) for
     upstream dy, by the chain rule around the scan's backward: the gate gives
     dz = dy * y_scan * SiLU'(z) and hands dy * SiLU(z) to the scan; the step
     size hands d delta' back through softplus (its derivative is the logistic
-    sigmoid) and sums it over cells for the bias. ``delta_round`` as in
-    fwd_mamba (applied to the effective step size; its derivative is taken as
-    1); ``dy_round`` likewise to the gated upstream gradient handed to the
-    scan, for outputs that store it rounded. Returns the dict of bwd plus dz
-    and ddelta_bias where they apply."""
+    sigmoid) and sums it over cells for the bias. Everything in fp64.
+    Returns the dict of bwd plus dz and ddelta_bias where they apply."""
     raw = np.asarray(delta, dtype=np.float64)
     pre = raw if delta_bias is None else raw + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
     dt = softplus(pre) if delta_softplus else pre
-    if delta_round is not None:
-        dt = delta_round(dt)
     dyf = np.asarray(dy, dtype=np.float64)
     out = {}
     if z is not None:
@@ -240,8 +232,6 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
         y_scan = fwd(x, dt, A, B, C, D, lib=lib)
         out["dz"] = dyf * y_scan * sig * (1.0 + zf * (1.0 - sig))
         dyf = dyf * zf * sig
-        if dy_round is not None:
-            dyf = dy_round(dyf)
     g = bwd(x, dt, A, B, C, D, dyf, lib=lib)
     dd = g["ddelta"]
     if delta_softplus:
@@ -253,12 +243,23 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
     return g
 
 
-def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False):
+def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False, vertical_first=False):
     """Gradients of the forward pass (fp64) for upstream gradient dy (shape of
     y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input.
     flip_h / flip_w: of the scan in that direction, which is the upper-left
     scan of the mirrored map (a permutation of the cells), so its gradients
-    are the mirrored map's, mirrored back."""
+    are the mirrored map's, mirrored back. vertical_first: of the scan in the
+    other order, which is the horizontal-first scan of the transposed map
+    (cell (i, j) becomes (j, i); a flip of the rows becomes a flip of the
+    columns and the other way round), so its gradients are the transposed
+    map's, transposed back. Both identities are permutations of the cells;
+    the finite-difference pins check the results independently."""
+    if vertical_first:
+        tr = lambda a: np.ascontiguousarray(np.swapaxes(np.asarray(a, dtype=np.float64), 2, 3))
+        g = bwd(tr(x), tr(delta), A, tr(B), tr(C), D, tr(dy), nthreads, lib, flip_h=flip_w, flip_w=flip_h)
+        for k in ("dx", "ddelta", "dB", "dC"):
+            g[k] = tr(g[k])
+        return g
     if flip_h or flip_w:
         ax = tuple(a for a, f in ((2, flip_h), (3, flip_w)) if f)
         fl = lambda a: np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), ax))

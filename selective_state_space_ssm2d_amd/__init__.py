@@ -28,7 +28,7 @@ __all__ = [
     "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_fwd_mamba", "scan_bwd",
     "scan_bwd_mamba",
     "status_string",
-    "sync_check", "set_spin_limit", "exported_names", "Ssm2dError",
+    "sync_check", "set_spin_limit", "release_workspaces", "set_epoch_for_test", "exported_names", "Ssm2dError",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +87,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssm2d_sync_check.restype = ctypes.c_int
     lib.ssm2d_set_spin_limit.argtypes = [i64]
     lib.ssm2d_set_spin_limit.restype = ctypes.c_int
+    lib.ssm2d_release_workspaces.argtypes = [vp]
+    lib.ssm2d_release_workspaces.restype = ctypes.c_int
+    lib.ssm2d_test_set_epoch.argtypes = [vp, ctypes.c_uint32]
+    lib.ssm2d_test_set_epoch.restype = ctypes.c_int
     lib.ssm2d_version.argtypes = []
     lib.ssm2d_version.restype = ctypes.c_int
     lib.ssm2d_last_hip_error.argtypes = []
@@ -127,6 +131,21 @@ def sync_check(stream=None) -> None:
 
 def set_spin_limit(polls: int) -> None:
     load_library().ssm2d_set_spin_limit(int(polls))
+
+
+def release_workspaces(stream=None) -> None:
+    """Wait for the stream and free the library's workspaces for it (current
+    device); raise if a timeout was still unreported."""
+    s = load_library().ssm2d_release_workspaces(_stream_handle(stream))
+    if s != OK:
+        raise Ssm2dError(s, "ssm2d_release_workspaces")
+
+
+def set_epoch_for_test(epoch: int, stream=None) -> None:
+    """Test hook: set the stored carry-tag epoch of the stream's workspace."""
+    s = load_library().ssm2d_test_set_epoch(_stream_handle(stream), int(epoch))
+    if s != OK:
+        raise Ssm2dError(s, "ssm2d_test_set_epoch")
 
 
 def _check(x, delta, A, B, C, D, y, need_d):
@@ -249,11 +268,13 @@ def scan_fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, y=None, *
     return (y, h_last) if return_last_state else y
 
 
-def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None, *, flip_h=False, flip_w=False):
+def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None, *, flip_h=False, flip_w=False,
+             vertical_first=False):
     """Gradients of the forward scan for upstream gradient dy (include/ssm2d.h,
-    ssm2d_scan_bwd; with flip_h / flip_w, ssm2d_scan_bwd_ex for the scan in
-    that direction). Returns a dict dx, ddelta, dA, dB, dC, dD; ``out`` may
-    supply any of them (shapes and dtypes as the inputs they belong to)."""
+    ssm2d_scan_bwd; with flip_h / flip_w / vertical_first, ssm2d_scan_bwd_ex
+    for the scan in that direction and order). Returns a dict dx, ddelta, dA,
+    dB, dC, dD; ``out`` may supply any of them (shapes and dtypes as the
+    inputs they belong to)."""
     import torch
 
     lib = load_library()
@@ -272,9 +293,9 @@ def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None, *, flip_h=False, f
             raise ValueError(f"{k} must match its input in shape, dtype and device, and be contiguous")
         g[k] = t
     args = [_ptr(t) for t in (x, delta, A, B, C, D, dy)] + [_ptr(g[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")]
-    if flip_h or flip_w:
+    if flip_h or flip_w or vertical_first:
         fn = lib.ssm2d_scan_bwd_ex if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_ex_bf16
-        flags = (FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0)
+        flags = (FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
         _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, flags, _stream_handle(stream)])
     else:
         fn = lib.ssm2d_scan_bwd if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_bf16

@@ -107,8 +107,15 @@ struct Params {
     const void *zeros;                 // zero page, >= H*W*4 bytes
     void *sink;                        // write target of masked-off output lanes
     unsigned int *ticket, *done, *err;
+    // Tag epoch of the carry words, kept on the device so that every launch
+    // (a replayed graph's too) tags its words differently: each workgroup
+    // reads it at its start, the last one to finish advances it. Stored
+    // values run 0 .. 65534; a launch's tags use stored + 1.
+    unsigned int *epoch;
+    unsigned int *herr;                // host-visible timeout flag (may be null)
     unsigned long long *gring;         // [n_bound][qg][NPL][64] tagged carries
     unsigned long long *cons;          // [n_bound] consumer progress: epoch<<32 | rows
+    long gring_words, cons_words;      // cleared when the epoch wraps
     int batch, d_inner, d_state, H, W;
     int nstrips, s_local, groups, n_dblk, n_chains, total_wg;
     int ring_rows;                     // LDS ring depth between waves
@@ -138,9 +145,19 @@ struct Params {
     // null): before the first row in scan order, and after the last row
     const float *h_init;
     float *h_last;
-    unsigned int epoch;
     long long spin_limit;
 };
+
+constexpr unsigned int kEpochs = 65535;  // tag epochs 1 .. 65535 (zero never matches)
+
+// A wait that gave up: the device error word, and the host-visible flag that
+// the library's next call on this workspace reports.
+__device__ __forceinline__ void report_timeout(const Params &p)
+{
+    atomicOr(p.err, 1u);
+    if (p.herr) __hip_atomic_store(p.herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
 
 template <typename T> struct ChunkOf;
 template <> struct ChunkOf<float> { using type = float4; };      // 4 fp32
@@ -537,12 +554,18 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     __shared__ int s_done[kMaxWaves + 1];   // rows published into LDS ring b
     __shared__ int s_used[kMaxWaves + 1];   // rows consumed from LDS ring b
     __shared__ unsigned int s_ticket;
+    __shared__ unsigned int s_epoch;        // this launch's tag epoch, 1 .. kEpochs
+    __shared__ int s_last;                  // this workgroup finished last
     __shared__ int s_arrive[kMaxSlots];     // shares written into row-ring slot
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
-    if (p.use_ticket && threadIdx.x == 0)
+    if (p.use_ticket && threadIdx.x == 0) {
         s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // (the previous launch's last workgroup advanced it before that
+        // launch completed)
+        s_epoch = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % kEpochs + 1;
+    }
     if (threadIdx.x <= kMaxWaves) {
         s_done[threadIdx.x] = 0;
         s_used[threadIdx.x] = 0;
@@ -585,8 +608,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // the write-through of stores (one counter tracks both).
         const long nb_per_chain = p.groups - 1;
         const long gstride = static_cast<long>(p.qg) * NPL * kWave;
-        const unsigned int etag = p.epoch << 16;
-        const unsigned long long ctag = static_cast<unsigned long long>(p.epoch) << 32;
+        const unsigned int etag = s_epoch << 16;
+        const unsigned long long ctag = static_cast<unsigned long long>(s_epoch) << 32;
         long idle = 0;
         bool timed_out = false;
         if (wave == p.s_local && grp > 0) {
@@ -632,7 +655,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     sleep_a_bit();
                 }
             }
-            if (timed_out) lds_publish(&s_done[0], H);  // let wave 0 run to the end
+            if (timed_out) {
+                // Let wave 0 run to the end on NaN carries: every output it
+                // and the strips after it compute from here on is NaN.
+                for (long k = lane; k < static_cast<long>(p.ring_rows) * kWave * NPL; k += kWave) ring0[k] = quiet_nan();
+                lds_publish(&s_done[0], H);
+            }
         } else if (wave == p.s_local + 1 && (grp + 1) * p.s_local < p.nstrips) {
             const long bound_out = chain * nb_per_chain + grp;
             unsigned long long *gout = p.gring + bound_out * gstride + lane;
@@ -669,7 +697,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             }
             if (timed_out) lds_publish(&s_used[p.s_local], H);  // let the last wave run to the end
         }
-        if (timed_out) atomicOr(p.err, 1u);
+        if (timed_out) report_timeout(p);
     } else if (grp * p.s_local + wave < p.nstrips) {
         // ---------------- compute wave: one strip
         const int strip = grp * p.s_local + wave;
@@ -913,12 +941,21 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             off_c[k] = roff(SEG_C + g * NPL + k);
         }
         // Polls an LDS counter until it reaches `need` (bounded like every wait).
+        // A wait that gave up: later waits are skipped, and the decay
+        // exponents become NaN, so that every output this strip computes
+        // from here on (and, through its carries, the strips after it) is
+        // NaN instead of a plausible wrong value.
+        auto give_up = [&]() {
+            timed_out = true;
+            skip = kSkipWaits;
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) Ap[k] = quiet_nan();
+        };
         auto wait_count = [&](const int *c, const int need) {
             long long spins = 0;
             while (__builtin_amdgcn_readfirstlane(lds_peek(c)) < need) {
                 if (++spins > p.spin_limit) {
-                    timed_out = true;
-                    skip = kSkipWaits;
+                    give_up();
                     break;
                 }
                 if (spins > kSpinPolls) sleep_a_bit();
@@ -986,7 +1023,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // 8 strips): the workgroup's first strip reads the global ring
         // itself, its last strip writes it. Every row has its own slot there
         // (no reuse, so no back-pressure).
-        const unsigned int etag_c = p.epoch << 16;
+        const unsigned int etag_c = s_epoch << 16;  // (set when chains span workgroups)
         const long gstride_c = static_cast<long>(p.qg) * NPL * kWave;
         const unsigned long long *gin_c =
             p.gring + (static_cast<long>(chain) * (p.groups - 1) + (grp > 0 ? grp - 1 : 0)) * gstride_c + lane;
@@ -1089,7 +1126,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     if (i >= max(room, skip)) {
                         room = wait_counter_above(&s_used[wave + 1], i - p.ring_rows, p.spin_limit, timed_out) +
                                p.ring_rows;
-                        if (timed_out) skip = kSkipWaits;
+                        if (timed_out) give_up();
                     }
                 }
 
@@ -1119,8 +1156,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                                 break;
                             }
                             if (++spins > p.spin_limit) {
-                                timed_out = true;
-                                skip = kSkipWaits;
+                                give_up();
+#pragma unroll
+                                for (int k = 0; k < NPL; ++k) hh[k] = quiet_nan();
                                 break;
                             }
                             if (spins > kSpinPolls) sleep_a_bit();
@@ -1139,8 +1177,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                         for (int k = 0; k < NPL; ++k) ok = ok && ((gw[k] & 0xffffffff00000000ull) == want);
                         if (__all(ok)) break;
                         if (++spins > p.spin_limit) {
-                            timed_out = true;
-                            skip = kSkipWaits;
+                            give_up();
                             break;
                         }
                         if (spins > kSpinPolls) sleep_a_bit();
@@ -1148,7 +1185,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                         for (int k = 0; k < NPL; ++k) gw[k] = ld_relaxed(gin_c + (static_cast<long>(i) * NPL + k) * kWave);
                     }
 #pragma unroll
-                    for (int k = 0; k < NPL; ++k) hh[k] = __uint_as_float(static_cast<unsigned>(gw[k] & 0xffffffffu));
+                    for (int k = 0; k < NPL; ++k)
+                        hh[k] = timed_out ? quiet_nan() : __uint_as_float(static_cast<unsigned>(gw[k] & 0xffffffffu));
                 }
 
                 // ---- horizontal recurrence along the row, then hand the carry on
@@ -1441,17 +1479,33 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 if (hok[k]) (void)unsafeAtomicAdd(p.dA + d * p.d_state + g * NPL + k, dAacc[k]);
             if (d_ok && g == 0) (void)unsafeAtomicAdd(p.dD + d, dDacc);
         }
-        if (timed_out) atomicOr(p.err, 1u);
+        if (timed_out) report_timeout(p);
     }
 
     if (p.use_ticket) {
+        // The last workgroup to finish resets the tickets and advances the
+        // tag epoch for the next launch. When the epoch wraps, the next
+        // launch's tags repeat those of a launch 65535 launches back, whose
+        // words may still sit in slots nobody has rewritten since (another
+        // shape lays the ring out differently): every ring and consumer word
+        // is cleared first (zero never matches a tag).
         __syncthreads();
         if (threadIdx.x == 0) {
             unsigned int old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (old + 1 == static_cast<unsigned int>(p.total_wg)) {
+            s_last = (old + 1 == static_cast<unsigned int>(p.total_wg)) ? 1 : 0;
+            if (s_last) {
                 __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+        }
+        __syncthreads();
+        if (s_last) {
+            const unsigned int next = s_epoch % kEpochs;  // stored value of the next launch
+            if (next == 0) {
+                for (long k = threadIdx.x; k < p.gring_words; k += blockDim.x) st_relaxed(p.gring + k, 0ull);
+                for (long k = threadIdx.x; k < p.cons_words; k += blockDim.x) st_relaxed(p.cons + k, 0ull);
+            }
+            if (threadIdx.x == 0) __hip_atomic_store(p.epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -1482,21 +1536,33 @@ struct Plan {
 
 int env_int(const char *name, int dflt);
 
-constexpr size_t kHeadBytes = 256;   // ticket, done, err
+constexpr size_t kHeadBytes = 256;   // ticket, done, err, epoch
 constexpr size_t kSinkBytes = 4096;  // >= 64 lanes x 8 cells x 4 bytes
 
+// The scan's workspace: head words (ticket, done, err, epoch), the sink, the
+// consumer words cons[], the global carry ring and the zero page.
 struct WsEntry {
-    unsigned int *head = nullptr;          // ticket, done, err, then cons[]
+    unsigned int *head = nullptr;          // ticket, done, err, epoch, then the sink and cons[]
     unsigned long long *gring = nullptr;
     void *zeros = nullptr;
+    unsigned int *herr = nullptr;          // host-mapped timeout flag (null if unavailable)
     size_t gring_bytes = 0, zero_bytes = 0, cons_count = 0;
-    unsigned int epoch = 0;
 };
 
 int hip_fail(hipError_t e);
 extern long long g_spin_limit;
 int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t cons_count, WsEntry **out);
 int device_cus(int dev);
+
+// Sizes of the scan workspace a plan needs (the global ring, the zero page,
+// the consumer words).
+struct WsNeed {
+    size_t gring_bytes, zero_bytes, cons_count;
+};
+// The plan's launch, given its workspace.
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
+int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+                int d_inner, int d_state, int H, int W, const Plan &pl, const WsEntry &e, void *stream);
 
 // Two courier waves join the strips when a chain spans workgroups (not in
 // the courier-free adjoint pass, whose boundary strips reach the global ring
@@ -1535,38 +1601,55 @@ int choose_qg(const Plan &pl, int dev, int H)
     return H;
 }
 
+template <int NPL>
+WsNeed ws_need(const Plan &pl, int d_inner, int H, int W)
+{
+    const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
+    WsNeed n{};
+    n.gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
+    // zero page: whole rows of any input type, and a zero D (no skip term)
+    n.zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
+    if (n.zero_bytes < static_cast<size_t>(d_inner) * 4 + 64) n.zero_bytes = static_cast<size_t>(d_inner) * 4 + 64;
+    n.cons_count = static_cast<size_t>(n_bound > 0 ? n_bound : 1);
+    return n;
+}
+
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 int run(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
         int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
 {
     if (!COOP) pl.coop_slots = 0;
     pl.qg = choose_qg<T, K, NPL, ALIGN, G, COOP, MODE>(pl, dev, H);
-    const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
-    const size_t gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
-    // zero page: whole rows of any input type, and a zero D (no skip term)
-    size_t zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
-    if (zero_bytes < static_cast<size_t>(d_inner) * 4 + 64) zero_bytes = static_cast<size_t>(d_inner) * 4 + 64;
+    const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
     WsEntry *e = nullptr;
-    int st = get_ws(dev, stream, gring_bytes, zero_bytes, static_cast<size_t>(n_bound > 0 ? n_bound : 1), &e);
+    const int st = get_ws(dev, stream, need.gring_bytes, need.zero_bytes, need.cons_count, &e);
     if (st != SSM2D_OK) return st;
-    e->epoch = (e->epoch + 1) & 0xffffu;
-    if (e->epoch == 0) e->epoch = 1;  // tags are (epoch << 16 | row); zero never matches
+    return launch_plan<T, K, NPL, ALIGN, G, COOP, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, *e,
+                                                        stream);
+}
 
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
+int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+                int d_inner, int d_state, int H, int W, const Plan &pl, const WsEntry &ws, void *stream)
+{
+    const WsEntry *e = &ws;
     Params prm{};
     prm.x = x; prm.delta = delta;
     prm.B = d_state ? static_cast<const void *>(B) : e->zeros;
     prm.C = d_state ? static_cast<const void *>(C) : e->zeros;
     prm.A = A; prm.D = D ? D : static_cast<const float *>(e->zeros); prm.y = y; prm.zeros = e->zeros;
-    prm.ticket = e->head; prm.done = e->head + 1; prm.err = e->head + 2;
+    prm.ticket = e->head; prm.done = e->head + 1; prm.err = e->head + 2; prm.epoch = e->head + 3;
+    prm.herr = e->herr;
     prm.sink = reinterpret_cast<char *>(e->head) + kHeadBytes;
     prm.cons = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(e->head) + kHeadBytes + kSinkBytes);
     prm.gring = e->gring;
+    prm.gring_words = static_cast<long>(e->gring_bytes / sizeof(unsigned long long));
+    prm.cons_words = static_cast<long>(e->cons_count);
     prm.batch = batch; prm.d_inner = d_inner; prm.d_state = d_state; prm.H = H; prm.W = W;
     prm.nstrips = pl.nstrips; prm.s_local = pl.s_local; prm.groups = pl.groups; prm.n_dblk = pl.n_dblk;
     prm.n_chains = pl.n_chains; prm.total_wg = pl.total_wg; prm.ring_rows = pl.ring_rows; prm.qg = pl.qg;
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
-    prm.epoch = e->epoch;
     // Gathered stores pay for 4-column strips (one row swap, two cells a lane).
     // Gathering the eight cells of an 8-column strip costs more VALU work than
     // the scattered stores, which the memory system coalesces anyway.

@@ -94,7 +94,7 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
 }
 
 
-std::mutex g_mutex;
+std::recursive_mutex g_mutex;  // (entry points call one another on the widened bf16 paths)
 std::atomic<int> g_last_hip_error{hipSuccess};
 
 int hip_fail(hipError_t e)
@@ -111,87 +111,159 @@ int hip_fail(hipError_t e)
 std::map<std::pair<int, void *>, WsEntry> g_ws;
 long long g_spin_limit = 0;
 
-void free_ws(WsEntry &e)
+// Zeroes n16 16-byte words (a kernel rather than a memset node, so that a
+// caller capturing a graph records nothing the replays could misapply).
+__global__ void fill_zero_kernel(uint4 *p, long n16)
 {
-    if (e.head) (void)hipFree(e.head);
-    if (e.gring) (void)hipFree(e.gring);
-    if (e.zeros) (void)hipFree(e.zeros);
-    e = WsEntry{};
+    for (long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; t < n16;
+         t += static_cast<long>(gridDim.x) * blockDim.x)
+        p[t] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Workspace for (device, stream), grown when needed. Growth waits for the
-// stream so that no in-flight kernel still uses the old buffers. Fresh
-// buffers are zeroed; tags are never zero, so no stale word matches.
+int zero_async(void *p, size_t bytes, hipStream_t s)
+{
+    const long n16 = static_cast<long>((bytes + 15) / 16);
+    if (n16 == 0) return SSM2D_OK;
+    const long blocks = std::min<long>((n16 + 255) / 256, 4096);
+    fill_zero_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(static_cast<uint4 *>(p), n16);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSM2D_OK : hip_fail(e);
+}
+
+// Device memory in stream order: allocated and freed on the caller's stream
+// (no host wait; a buffer being replaced is released after the work queued
+// before it). Sizes are rounded up to 16 bytes.
+int alloc_async(void **p, size_t bytes, hipStream_t s)
+{
+    *p = nullptr;
+    if (hipMallocAsync(p, (bytes + 15) & ~size_t{15}, s) != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return SSM2D_ERR_NOMEM;
+    }
+    return SSM2D_OK;
+}
+void free_async(void *p, hipStream_t s)
+{
+    if (p) (void)hipFreeAsync(p, s);
+}
+
+void free_ws(WsEntry &e, hipStream_t s)
+{
+    free_async(e.head, s);
+    free_async(e.gring, s);
+    free_async(e.zeros, s);
+    unsigned int *herr = e.herr;
+    e = WsEntry{};
+    e.herr = herr;  // the flag stays with the (device, stream)
+}
+
+// Workspace for (device, stream), grown when needed: the old buffers are
+// released in stream order, the new ones zeroed by a kernel on the stream
+// (tags are never zero, so no zero word matches). The host-visible timeout
+// flag is pinned host memory, mapped for the device, allocated once.
 int get_ws(int dev, void *stream, size_t gring_bytes, size_t zero_bytes, size_t cons_count, WsEntry **out)
 {
     WsEntry &e = g_ws[{dev, stream}];
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!e.herr) {
+        void *h = nullptr;
+        if (hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess && h) {
+            std::memset(h, 0, 64);
+            e.herr = static_cast<unsigned int *>(h);
+        } else {
+            (void)hipGetLastError();  // no flag: timeouts are reported by ssm2d_sync_check only
+        }
+    }
     if (e.head && gring_bytes <= e.gring_bytes && zero_bytes <= e.zero_bytes && cons_count <= e.cons_count) {
         *out = &e;
         return SSM2D_OK;
     }
-    unsigned int epoch = e.epoch;
-    if (e.head) {
-        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-        free_ws(e);
-    }
-    size_t gb = gring_bytes < 256 ? 256 : gring_bytes;
-    size_t zb = zero_bytes < 256 ? 256 : zero_bytes;
-    size_t cc = cons_count < 1 ? 1 : cons_count;
+    if (e.head) free_ws(e, s);
+    size_t gb = std::max(gring_bytes, size_t{256});
+    size_t zb = std::max(zero_bytes, size_t{256});
+    size_t cc = std::max(cons_count, size_t{1});
     size_t head = kHeadBytes + kSinkBytes + cc * sizeof(unsigned long long);
     void *h = nullptr, *g = nullptr, *z = nullptr;
-    if (hipMalloc(&h, head) != hipSuccess || hipMalloc(&g, gb) != hipSuccess || hipMalloc(&z, zb) != hipSuccess) {
-        if (h) (void)hipFree(h);
-        if (g) (void)hipFree(g);
-        (void)hipGetLastError();
+    if (alloc_async(&h, head, s) != SSM2D_OK || alloc_async(&g, gb, s) != SSM2D_OK ||
+        alloc_async(&z, zb, s) != SSM2D_OK) {
+        free_async(h, s);
+        free_async(g, s);
         return SSM2D_ERR_NOMEM;
     }
-    SSM2D_HIP_TRY(hipMemset(h, 0, head));
-    SSM2D_HIP_TRY(hipMemset(g, 0, gb));
-    SSM2D_HIP_TRY(hipMemset(z, 0, zb));
+    int st = zero_async(h, head, s);
+    if (st == SSM2D_OK) st = zero_async(g, gb, s);
+    if (st == SSM2D_OK) st = zero_async(z, zb, s);
+    if (st != SSM2D_OK) {
+        free_async(h, s);
+        free_async(g, s);
+        free_async(z, s);
+        return st;
+    }
     e.head = static_cast<unsigned int *>(h);
     e.gring = static_cast<unsigned long long *>(g);
     e.zeros = z;
-    e.gring_bytes = gb;
+    e.gring_bytes = (gb / 8) * 8;
     e.zero_bytes = zb;
     e.cons_count = cc;
-    e.epoch = epoch;
     *out = &e;
     return SSM2D_OK;
 }
 
+// A timeout reported by a kernel of an earlier call on (device, stream)
+// (the host-mapped flag, read without waiting): consumed, and reported once.
+bool take_timeout_flag(int dev, void *stream)
+{
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.herr) return false;
+    unsigned int *f = it->second.herr;
+    if (__atomic_load_n(f, __ATOMIC_ACQUIRE) == 0u) return false;
+    __atomic_store_n(f, 0u, __ATOMIC_RELEASE);
+    return true;
+}
+
 // ---------------------------------------------------------------- backward
 
-// Backward workspace per (device, stream): the stored states and the
-// per-channel-block partial sums of dB and dC. Grown when needed (after
-// waiting for the stream); zeroed when allocated.
-struct BwdWs {
+// Buffers per (device, stream, slot) in stream order, grown when needed
+// (the old buffer is released after the work queued before it, the new one
+// optionally zeroed by a kernel on the stream). Slots: kSlotBwd holds the
+// backward's stored states and channel-block sums; the others are scratch
+// tensors of the option and widening passes.
+struct Buf {
     void *buf = nullptr;
     size_t bytes = 0;
 };
-std::map<std::pair<int, void *>, BwdWs> g_bwd_ws;
+std::map<std::pair<std::pair<int, void *>, int>, Buf> g_bufs;
+constexpr int kSlotBwd = -1;
 
-int get_bwd_ws(int dev, void *stream, size_t bytes, void **out)
+int get_buf(int dev, void *stream, int slot, size_t bytes, bool zero, void **out)
 {
-    BwdWs &e = g_bwd_ws[{dev, stream}];
+    Buf &e = g_bufs[{{dev, stream}, slot}];
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     if (e.buf && bytes <= e.bytes) {
         *out = e.buf;
         return SSM2D_OK;
     }
     if (e.buf) {
-        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-        (void)hipFree(e.buf);
-        e = BwdWs{};
+        free_async(e.buf, s);
+        e = Buf{};
     }
     void *b = nullptr;
-    if (hipMalloc(&b, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return SSM2D_ERR_NOMEM;
+    int st = alloc_async(&b, bytes, s);
+    if (st == SSM2D_OK && zero) st = zero_async(b, bytes, s);
+    if (st != SSM2D_OK) {
+        free_async(b, s);
+        return st;
     }
-    SSM2D_HIP_TRY(hipMemset(b, 0, bytes));
     e.buf = b;
     e.bytes = bytes;
     *out = b;
     return SSM2D_OK;
+}
+int get_bwd_ws(int dev, void *stream, size_t bytes, void **out) { return get_buf(dev, stream, kSlotBwd, bytes, true, out); }
+int get_aux_ws(int dev, void *stream, int slot, size_t bytes, void **out)
+{
+    return get_buf(dev, stream, slot, bytes, false, out);
 }
 
 // Zeroes dA and dD (the backward adds into them).
@@ -227,39 +299,14 @@ __global__ void bwd_reduce_kernel(const float *dBp, const float *dCp, long part_
 
 // ---------------------------------------------------------------- Mamba-op options
 
-// Scratch per (device, stream, slot), grown when needed; not zeroed.
-std::map<std::pair<std::pair<int, void *>, int>, BwdWs> g_aux_ws;
-
-int get_aux_ws(int dev, void *stream, int slot, size_t bytes, void **out)
-{
-    BwdWs &e = g_aux_ws[{{dev, stream}, slot}];
-    if (e.buf && bytes <= e.bytes) {
-        *out = e.buf;
-        return SSM2D_OK;
-    }
-    if (e.buf) {
-        SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-        (void)hipFree(e.buf);
-        e = BwdWs{};
-    }
-    void *b = nullptr;
-    if (hipMalloc(&b, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return SSM2D_ERR_NOMEM;
-    }
-    e.buf = b;
-    e.bytes = bytes;
-    *out = b;
-    return SSM2D_OK;
-}
-
 __device__ __forceinline__ float get(const float *p) { return *p; }
 __device__ __forceinline__ float get(const uint16_t *p) { return __uint_as_float(static_cast<unsigned>(*p) << 16); }
 
 // Step size of the scan: delta + bias[d], through softplus if asked, computed
-// in fp32 and stored in the input type. softplus(v) = max(v, 0) + log1p(e^-|v|).
-template <typename T>
-__global__ void delta_prep_kernel(const T *delta, const float *bias, T *out, long total, long hw, int d_inner,
+// in fp32 and stored as TO (the scan's input type, or fp32 for the widened
+// bf16 paths). softplus(v) = max(v, 0) + log1p(e^-|v|).
+template <typename TI, typename TO>
+__global__ void delta_prep_kernel(const TI *delta, const float *bias, TO *out, long total, long hw, int d_inner,
                                   int use_softplus)
 {
     const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -270,20 +317,32 @@ __global__ void delta_prep_kernel(const T *delta, const float *bias, T *out, lon
     put(out + t, v);
 }
 
-// y *= SiLU(z) = z / (1 + e^-z), for outputs summed over several launches.
-template <typename T>
-__global__ void gate_kernel(T *y, const T *z, long total)
+// bf16 -> fp32, exact.
+__global__ void widen_kernel(const uint16_t *in, float *out, long total)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t < total) out[t] = get(in + t);
+}
+
+// out = in * SiLU(z) (z may be null: no gate), rounded once to out's type.
+template <typename TI, typename TO>
+__global__ void gate_kernel(const TI *in, const TO *z, TO *out, long total)
 {
     const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= total) return;
-    const float zf = get(z + t);
-    put(y + t, get(y + t) * (zf / (1.0f + expf(-zf))));
+    float v = get(in + t);
+    if (z) {
+        const float zf = get(z + t);
+        v *= zf / (1.0f + expf(-zf));
+    }
+    put(out + t, v);
 }
 
 // Backward of the gate: dz = dy * y * SiLU'(z), and the scan's upstream
-// gradient dy * SiLU(z); SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
-template <typename T>
-__global__ void gate_bwd_kernel(const T *dy, const T *y, const T *z, T *dz, T *dys, long total)
+// gradient dy * SiLU(z) (held as TY: fp32 on the widened bf16 path);
+// SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
+template <typename T, typename TY>
+__global__ void gate_bwd_kernel(const T *dy, const TY *y, const T *z, T *dz, TY *dys, long total)
 {
     const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= total) return;
@@ -295,10 +354,11 @@ __global__ void gate_bwd_kernel(const T *dy, const T *y, const T *z, T *dz, T *d
 
 // Backward of the step-size preparation, one block per (batch, channel) map:
 // d delta = d delta' * sigmoid(delta + bias[d]) with softplus (else
-// unchanged), and d bias[d] += the map's sum of d delta.
-template <typename T>
-__global__ void step_bwd_kernel(T *ddelta, const T *delta, const float *bias, float *dbias, long hw, int d_inner,
-                                int use_softplus)
+// unchanged), read from gin (TG) and written to gout (T; may be gin), and
+// d bias[d] += the map's sum of d delta.
+template <typename TG, typename T>
+__global__ void step_bwd_kernel(const TG *gin, T *gout, const T *delta, const float *bias, float *dbias, long hw,
+                                int d_inner, int use_softplus)
 {
     __shared__ float part[256];
     const long map = blockIdx.x;
@@ -307,11 +367,9 @@ __global__ void step_bwd_kernel(T *ddelta, const T *delta, const float *bias, fl
     float acc = 0.0f;
     for (long p = threadIdx.x; p < hw; p += blockDim.x) {
         const long t = map * hw + p;
-        float g = get(ddelta + t);
-        if (use_softplus) {
-            g *= 1.0f / (1.0f + expf(-(get(delta + t) + bd)));
-            put(ddelta + t, g);
-        }
+        float g = get(gin + t);
+        if (use_softplus) g *= 1.0f / (1.0f + expf(-(get(delta + t) + bd)));
+        put(gout + t, g);
         acc += g;
     }
     if (!dbias) return;
@@ -322,6 +380,59 @@ __global__ void step_bwd_kernel(T *ddelta, const T *delta, const float *bias, fl
         __syncthreads();
     }
     if (threadIdx.x == 0) (void)unsafeAtomicAdd(dbias + d, part[0]);
+}
+
+// out[m][j][i] = in[m][i][j] for `maps` maps of H x W cells: 64 x 64 tiles
+// through LDS, so that both the reads and the writes run along rows.
+template <typename T>
+__global__ void transpose_kernel(const T *in, T *out, long maps, int H, int W)
+{
+    __shared__ T tile[64][65];
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;  // 256 threads: 64 x 4
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const long hw = static_cast<long>(H) * W;
+    for (long m = blockIdx.z; m < maps; m += gridDim.z) {
+        const T *src = in + m * hw;
+        T *dst = out + m * hw;
+        for (int r = ty; r < 64; r += 4) {
+            const int i = i0 + r, j = j0 + tx;
+            if (i < H && j < W) tile[r][tx] = src[static_cast<long>(i) * W + j];
+        }
+        __syncthreads();
+        for (int r = ty; r < 64; r += 4) {
+            const int j = j0 + r, i = i0 + tx;
+            if (j < W && i < H) dst[static_cast<long>(j) * H + i] = tile[tx][r];
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T>
+int transpose_maps(const T *in, T *out, long maps, long H, long W, hipStream_t s)
+{
+    if (maps == 0 || H == 0 || W == 0) return SSM2D_OK;
+    const dim3 grid(static_cast<unsigned>((W + 63) / 64), static_cast<unsigned>((H + 63) / 64),
+                    static_cast<unsigned>(std::min<long>(maps, 65535)));
+    transpose_kernel<T><<<grid, dim3(256), 0, s>>>(in, out, maps, static_cast<int>(H), static_cast<int>(W));
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSM2D_OK : hip_fail(e);
+}
+
+int widen(const uint16_t *in, float *out, long total, hipStream_t s)
+{
+    if (total == 0) return SSM2D_OK;
+    widen_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(in, out, total);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSM2D_OK : hip_fail(e);
+}
+
+template <typename TI, typename TO>
+int gate_or_round(const TI *in, const TO *z, TO *out, long total, hipStream_t s)
+{
+    if (total == 0) return SSM2D_OK;
+    gate_kernel<TI, TO><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(in, z, out, total);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSM2D_OK : hip_fail(e);
 }
 
 __global__ void zero_kernel(float *p, long n)
@@ -407,14 +518,66 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
 constexpr unsigned kKnownFlags = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST | SSM2D_ACCUMULATE | SSM2D_FOUR_WAY |
                                  SSM2D_DELTA_SOFTPLUS;
 
-// `extended`: the flag-taking entry points, where D may be NULL (no skip term).
-// z (gate) and delta_bias come with the Mamba-option entry points only.
+// Scratch slots of the widened bf16 paths (tensors shaped like x or B, fp32).
+enum : int {
+    kSlotStep = 0, kSlotY0 = 1, kSlotG = 2,
+    kSlotX32 = 3, kSlotD32 = 4, kSlotB32 = 5, kSlotC32 = 6, kSlotY32 = 7, kSlotG32 = 8,
+    kSlotDX32 = 9, kSlotDD32 = 10, kSlotDB32 = 11, kSlotDC32 = 12,
+    kSlotT0 = 13  // 13 .. 21: the transposed tensors of the vertical-first backward
+};
+
 template <typename T>
 int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
              void *stream, const T *z = nullptr, const float *delta_bias = nullptr, const float *h_init = nullptr,
-             float *h_last = nullptr)
+             float *h_last = nullptr);
+
+// bf16 calls whose result is more than one scan's rounded output (the
+// four-corner sums) or whose scan runs on a computed step size (bias,
+// softplus): x, B, C are widened to fp32 (exactly), the step size is computed
+// and kept in fp32, the fp32 scans produce the result in an fp32 tensor, and
+// that is rounded to bf16 once (times SiLU(z) when gated).
+int scan_fwd_widened(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B, const uint16_t *C,
+                     const float *D, uint16_t *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                     int64_t W, unsigned flags, void *stream, const uint16_t *z, const float *delta_bias,
+                     const float *h_init, float *h_last, int dev)
 {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const long total = batch * d_inner * H * W, tb = batch * d_state * H * W;
+    void *bx = nullptr, *bd = nullptr, *bb = nullptr, *bc = nullptr, *by = nullptr;
+    const size_t ebytes = static_cast<size_t>(total) * 4 + 256, bbytes = static_cast<size_t>(tb) * 4 + 256;
+    int st = get_aux_ws(dev, stream, kSlotX32, ebytes, &bx);
+    if (st == SSM2D_OK) st = get_aux_ws(dev, stream, kSlotD32, ebytes, &bd);
+    if (st == SSM2D_OK) st = get_aux_ws(dev, stream, kSlotB32, bbytes, &bb);
+    if (st == SSM2D_OK) st = get_aux_ws(dev, stream, kSlotC32, bbytes, &bc);
+    if (st == SSM2D_OK) st = get_aux_ws(dev, stream, kSlotY32, ebytes, &by);
+    if (st != SSM2D_OK) return st;
+    float *x32 = static_cast<float *>(bx), *d32 = static_cast<float *>(bd), *B32 = static_cast<float *>(bb);
+    float *C32 = static_cast<float *>(bc), *y32 = static_cast<float *>(by);
+    if ((st = widen(x, x32, total, s)) != SSM2D_OK) return st;
+    delta_prep_kernel<uint16_t, float><<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+        delta, delta_bias, d32, total, H * W, static_cast<int>(d_inner), (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+    if (d_state > 0) {
+        if ((st = widen(B, B32, tb, s)) != SSM2D_OK) return st;
+        if ((st = widen(C, C32, tb, s)) != SSM2D_OK) return st;
+    }
+    if ((flags & SSM2D_ACCUMULATE) && (st = widen(y, y32, total, s)) != SSM2D_OK) return st;
+    st = scan_fwd<float>(x32, d32, A, d_state ? B32 : nullptr, d_state ? C32 : nullptr, D, y32, batch, d_inner,
+                         d_state, H, W, flags & ~SSM2D_DELTA_SOFTPLUS, true, stream, nullptr, nullptr, h_init, h_last);
+    if (st != SSM2D_OK) return st;
+    return gate_or_round<float, uint16_t>(y32, z, y, total, s);
+}
+
+// Argument checks of the forward entry points (`extended`: the flag-taking
+// ones, where D may be NULL). SSM2D_OK with *work == false: nothing to do.
+template <typename T>
+int check_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *y,
+              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
+              const T *z, const float *delta_bias, const float *h_init, const float *h_last, bool *work)
+{
+    *work = false;
     if ((flags & ~kKnownFlags) != 0) return SSM2D_ERR_BAD_FLAGS;
     if ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))) return SSM2D_ERR_BAD_FLAGS;
     if (z && (flags & SSM2D_ACCUMULATE)) return SSM2D_ERR_BAD_FLAGS;
@@ -430,23 +593,44 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         misaligned(delta_bias) || misaligned(h_init) || misaligned(h_last) ||
         (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
         return SSM2D_ERR_MISALIGNED;
+    *work = true;
+    return SSM2D_OK;
+}
+
+// `extended`: the flag-taking entry points, where D may be NULL (no skip term).
+// z (gate) and delta_bias come with the Mamba-option entry points only.
+template <typename T>
+int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
+             int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
+             void *stream, const T *z, const float *delta_bias, const float *h_init, float *h_last)
+{
+    bool work = false;
+    const int chk = check_fwd(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, extended, z, delta_bias,
+                              h_init, h_last, &work);
+    if (chk != SSM2D_OK || !work) return chk;
 
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    if (take_timeout_flag(dev, stream)) return SSM2D_ERR_DEVICE_TIMEOUT;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        if ((flags & SSM2D_FOUR_WAY) || delta_bias || (flags & SSM2D_DELTA_SOFTPLUS))
+            return scan_fwd_widened(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, stream, z,
+                                    delta_bias, h_init, h_last, dev);
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const long total = batch * d_inner * H * W;
     const unsigned nblk = static_cast<unsigned>((total + 255) / 256);
     if (delta_bias || (flags & SSM2D_DELTA_SOFTPLUS)) {
-        // the scan's step size, prepared once (an HBM-bound pass; done inside
-        // the scan it would cost every state group of every channel the
-        // softplus of its cells)
+        // (fp32 only, see above) the scan's step size, prepared once (an
+        // HBM-bound pass; done inside the scan it would cost every state
+        // group of every channel the softplus of its cells)
         void *buf = nullptr;
-        const int st = get_aux_ws(dev, stream, 0, static_cast<size_t>(total) * sizeof(T) + 256, &buf);
+        const int st = get_aux_ws(dev, stream, kSlotStep, static_cast<size_t>(total) * sizeof(T) + 256, &buf);
         if (st != SSM2D_OK) return st;
-        delta_prep_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, static_cast<T *>(buf), total, H * W,
-                                                                static_cast<int>(d_inner),
-                                                                (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+        delta_prep_kernel<T, T><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, static_cast<T *>(buf), total,
+                                                                  H * W, static_cast<int>(d_inner),
+                                                                  (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
         delta = static_cast<const T *>(buf);
@@ -458,32 +642,76 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         return launch(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, mode, (flags & SSM2D_FLIP_H) ? 1 : 0,
                       dev, stream, z, h_init, h_last);
     }
-    // Four scans, one per starting corner, summed into y in stream order; the
-    // skip term is added once, by the first.
+    // (fp32 only) four scans, one per starting corner, summed into y in
+    // stream order; the skip term is added once, by the first.
     for (int q = 0; q < 4; ++q) {
         const int mode = ((q & 2) ? kModeFlipW : 0) | vf | (q == 0 ? acc : kModeAccumulate);
         const int st = launch(x, delta, A, B, C, q == 0 ? D : nullptr, y, batch, d_inner, d_state, H, W, mode,
                               q & 1, dev, stream);
         if (st != SSM2D_OK) return st;
     }
-    if (z) {
-        // the gate is linear in y: applied once to the sum
-        gate_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(y, z, total);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e);
+    // the gate is linear in y: applied once to the sum
+    if (z) return gate_or_round<T, T>(y, z, y, total, s);
+    return SSM2D_OK;
+}
+
+template <typename T>
+int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
+             T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+             int64_t W, void *stream, unsigned flags = 0);
+
+// Backward of the vertical-first order: that scan is the horizontal-first
+// scan of the transposed maps (the column recurrence becomes the row
+// recurrence), with the two flips trading places, so its gradients are the
+// transposed maps' gradients, transposed back. dA and dD need no transpose.
+template <typename T>
+int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy,
+                    T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner,
+                    int64_t d_state, int64_t H, int64_t W, void *stream, unsigned flags, int dev)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const long me = batch * d_inner, mb = batch * d_state;
+    const size_t eb = static_cast<size_t>(me * H * W) * sizeof(T) + 256, bb = static_cast<size_t>(mb * H * W) * sizeof(T) + 256;
+    void *buf[9] = {};
+    const size_t sizes[9] = {eb, eb, bb, bb, eb, eb, eb, bb, bb};
+    for (int k = 0; k < 9; ++k) {
+        const int st = get_aux_ws(dev, stream, kSlotT0 + k, sizes[k], &buf[k]);
+        if (st != SSM2D_OK) return st;
+    }
+    T *xt = static_cast<T *>(buf[0]), *dt = static_cast<T *>(buf[1]), *Bt = static_cast<T *>(buf[2]);
+    T *Ct = static_cast<T *>(buf[3]), *dyt = static_cast<T *>(buf[4]), *dxt = static_cast<T *>(buf[5]);
+    T *ddt = static_cast<T *>(buf[6]), *dBt = static_cast<T *>(buf[7]), *dCt = static_cast<T *>(buf[8]);
+    int st = SSM2D_OK;
+    if ((st = transpose_maps(x, xt, me, H, W, s)) != SSM2D_OK) return st;
+    if ((st = transpose_maps(delta, dt, me, H, W, s)) != SSM2D_OK) return st;
+    if ((st = transpose_maps(dy, dyt, me, H, W, s)) != SSM2D_OK) return st;
+    if (d_state > 0) {
+        if ((st = transpose_maps(B, Bt, mb, H, W, s)) != SSM2D_OK) return st;
+        if ((st = transpose_maps(C, Ct, mb, H, W, s)) != SSM2D_OK) return st;
+    }
+    const unsigned tflags = ((flags & SSM2D_FLIP_H) ? SSM2D_FLIP_W : 0u) | ((flags & SSM2D_FLIP_W) ? SSM2D_FLIP_H : 0u);
+    st = scan_bwd<T>(xt, dt, A, d_state ? Bt : nullptr, d_state ? Ct : nullptr, D, dyt, dxt, ddt, dA,
+                     d_state ? dBt : nullptr, d_state ? dCt : nullptr, dD, batch, d_inner, d_state, W, H, stream,
+                     tflags);
+    if (st != SSM2D_OK) return st;
+    if ((st = transpose_maps(dxt, dx, me, W, H, s)) != SSM2D_OK) return st;
+    if ((st = transpose_maps(ddt, ddelta, me, W, H, s)) != SSM2D_OK) return st;
+    if (d_state > 0) {
+        if ((st = transpose_maps(dBt, dB, mb, W, H, s)) != SSM2D_OK) return st;
+        if ((st = transpose_maps(dCt, dC, mb, W, H, s)) != SSM2D_OK) return st;
     }
     return SSM2D_OK;
 }
 
-// flags: SSM2D_FLIP_H / SSM2D_FLIP_W, the direction of the forward scan.
+// flags: SSM2D_FLIP_H / SSM2D_FLIP_W / SSM2D_VERTICAL_FIRST, the direction
+// and order of the forward scan.
 template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-             int64_t W, void *stream, unsigned flags = 0)
+             int64_t W, void *stream, unsigned flags)
 {
     if ((flags & ~kKnownFlags) != 0 || (flags & (SSM2D_ACCUMULATE | SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
         return SSM2D_ERR_BAD_FLAGS;
-    if (flags & SSM2D_VERTICAL_FIRST) return SSM2D_ERR_UNSUPPORTED;
     const bool f_h = (flags & SSM2D_FLIP_H) != 0, f_w = (flags & SSM2D_FLIP_W) != 0;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (d_inner == 0) return SSM2D_OK;
@@ -507,7 +735,11 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    if (take_timeout_flag(dev, stream)) return SSM2D_ERR_DEVICE_TIMEOUT;
+    if ((flags & SSM2D_VERTICAL_FIRST) && work)
+        return scan_bwd_vfirst<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                                  stream, flags, dev);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t state_elems = work ? static_cast<size_t>(tiles) * npl * kWave * 4 : 0;
     const long part_stride = batch * d_state * H * 4 * nstrips;  // floats per channel block
@@ -582,7 +814,11 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 }
 
 // Backward of the Mamba-option forward: the chain rule around scan_bwd (the
-// gate and the step-size preparation are elementwise).
+// gate and the step-size preparation are elementwise). fp32: the prepared
+// step size, the recomputed ungated output and the gated upstream gradient
+// are fp32 tensors. bf16 with any option: every tensor the chain rule hands
+// on is kept in fp32 (x, B, C widened exactly, the fp32 backward), and each
+// gradient is rounded to bf16 once.
 template <typename T>
 int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *z,
                    const float *delta_bias, const T *dy, T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, T *dz,
@@ -594,57 +830,104 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     if (d_inner == 0) return SSM2D_OK;
     if ((z && !dz) || (ddelta_bias && !delta_bias)) return SSM2D_ERR_NULLPTR;
     if (misaligned(z) || misaligned(dz) || misaligned(delta_bias) || misaligned(ddelta_bias)) return SSM2D_ERR_MISALIGNED;
-    const bool prep = delta_bias || (flags & SSM2D_DELTA_SOFTPLUS);
+    const bool softplus = (flags & SSM2D_DELTA_SOFTPLUS) != 0;
+    const bool prep = delta_bias || softplus;
     const long total = batch * d_inner * H * W;
     const unsigned nblk = static_cast<unsigned>((total + 255) / 256);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
     if (ddelta_bias) {
         zero_kernel<<<dim3(static_cast<unsigned>((d_inner + 255) / 256)), dim3(256), 0, s>>>(ddelta_bias, d_inner);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
     }
-    if (total == 0 || d_state > SSM2D_MAX_STATE_BWD)  // the backward reports sizes and zeroes dA, dD
+    if (total == 0 || d_state > SSM2D_MAX_STATE_BWD || (!prep && !z))  // the backward alone (it also reports sizes)
         return scan_bwd<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
                            stream);
-    if (!x || !delta || !dy || !dx || !ddelta) return SSM2D_ERR_NULLPTR;
-    void *ws1 = nullptr, *ws2 = nullptr, *ws3 = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_mutex);
-        const size_t bytes = static_cast<size_t>(total) * sizeof(T) + 256;
-        int st = prep ? get_aux_ws(dev, stream, 0, bytes, &ws1) : SSM2D_OK;
-        if (st == SSM2D_OK && z) st = get_aux_ws(dev, stream, 1, bytes, &ws2);
-        if (st == SSM2D_OK && z) st = get_aux_ws(dev, stream, 2, bytes, &ws3);
-        if (st != SSM2D_OK) return st;
-        if (prep) {
-            delta_prep_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, static_cast<T *>(ws1), total,
-                                                                    H * W, static_cast<int>(d_inner),
-                                                                    (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail(e);
-        }
-    }
-    const T *dstep = prep ? static_cast<const T *>(ws1) : delta;
-    const T *g = dy;
-    if (z) {
-        // the ungated scan output, then dz and the scan's upstream gradient
-        T *y0 = static_cast<T *>(ws2);
-        int st = scan_fwd<T>(x, dstep, A, B, C, D, y0, batch, d_inner, d_state, H, W, 0u, false, stream);
-        if (st != SSM2D_OK) return st;
-        gate_bwd_kernel<T><<<dim3(nblk), dim3(256), 0, s>>>(dy, y0, z, dz, static_cast<T *>(ws3), total);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e);
-        g = static_cast<const T *>(ws3);
-    }
-    int st = scan_bwd<T>(x, dstep, A, B, C, D, g, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W, stream);
+    if (!x || !delta || !dy || !dx || !ddelta || !D || (d_state > 0 && (!A || !B || !C || !dB || !dC || !dA)) || !dD)
+        return SSM2D_ERR_NULLPTR;
+    if (misaligned(x) || misaligned(delta) || misaligned(dy) || misaligned(dx) || misaligned(ddelta))
+        return SSM2D_ERR_MISALIGNED;
+    if (take_timeout_flag(dev, stream)) return SSM2D_ERR_DEVICE_TIMEOUT;
+    using TW = float;  // the working type of everything the chain rule hands on
+    constexpr bool WIDE = std::is_same<T, uint16_t>::value;
+    const long tb = batch * d_state * H * W;
+    const size_t eb = static_cast<size_t>(total) * 4 + 256, bb = static_cast<size_t>(tb) * 4 + 256;
+    auto buf = [&](int slot, size_t bytes, TW **out) {
+        void *v = nullptr;
+        const int st = get_aux_ws(dev, stream, slot, bytes, &v);
+        *out = static_cast<TW *>(v);
+        return st;
+    };
+    // inputs of the scan in the working type
+    const TW *xw, *Bw, *Cw;
+    TW *dstep = nullptr;
+    int st = buf(kSlotStep, eb, &dstep);
     if (st != SSM2D_OK) return st;
-    if ((flags & SSM2D_DELTA_SOFTPLUS) || ddelta_bias) {
-        step_bwd_kernel<T><<<dim3(static_cast<unsigned>(batch * d_inner)), dim3(256), 0, s>>>(
-            ddelta, delta, delta_bias, ddelta_bias, H * W, static_cast<int>(d_inner),
-            (flags & SSM2D_DELTA_SOFTPLUS) ? 1 : 0);
+    delta_prep_kernel<T, TW><<<dim3(nblk), dim3(256), 0, s>>>(delta, delta_bias, dstep, total, H * W,
+                                                               static_cast<int>(d_inner), softplus ? 1 : 0);
+    {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
+    }
+    if constexpr (WIDE) {
+        TW *x32, *B32, *C32;
+        if ((st = buf(kSlotX32, eb, &x32)) != SSM2D_OK || (st = buf(kSlotB32, bb, &B32)) != SSM2D_OK ||
+            (st = buf(kSlotC32, bb, &C32)) != SSM2D_OK)
+            return st;
+        if ((st = widen(x, x32, total, s)) != SSM2D_OK) return st;
+        if (d_state > 0 && ((st = widen(B, B32, tb, s)) != SSM2D_OK || (st = widen(C, C32, tb, s)) != SSM2D_OK))
+            return st;
+        xw = x32; Bw = B32; Cw = C32;
+    } else {
+        xw = x; Bw = B; Cw = C;
+    }
+    // upstream gradient of the scan
+    TW *g = nullptr;
+    if ((st = buf(kSlotG32, eb, &g)) != SSM2D_OK) return st;
+    if (z) {
+        // the ungated scan output, then dz and dy * SiLU(z)
+        TW *y0 = nullptr;
+        if ((st = buf(kSlotY0, eb, &y0)) != SSM2D_OK) return st;
+        st = scan_fwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, y0, batch, d_inner,
+                          d_state, H, W, 0u, false, stream);
+        if (st != SSM2D_OK) return st;
+        gate_bwd_kernel<T, TW><<<dim3(nblk), dim3(256), 0, s>>>(dy, y0, z, dz, g, total);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    } else if constexpr (WIDE) {
+        if ((st = widen(dy, g, total, s)) != SSM2D_OK) return st;
+    } else {
+        g = const_cast<TW *>(reinterpret_cast<const TW *>(dy));
+    }
+    // the scan's backward in the working type
+    TW *dxw, *ddw, *dBw, *dCw;
+    if constexpr (WIDE) {
+        if ((st = buf(kSlotDX32, eb, &dxw)) != SSM2D_OK || (st = buf(kSlotDD32, eb, &ddw)) != SSM2D_OK ||
+            (st = buf(kSlotDB32, bb, &dBw)) != SSM2D_OK || (st = buf(kSlotDC32, bb, &dCw)) != SSM2D_OK)
+            return st;
+    } else {
+        dxw = reinterpret_cast<TW *>(dx); ddw = reinterpret_cast<TW *>(ddelta);
+        dBw = reinterpret_cast<TW *>(dB); dCw = reinterpret_cast<TW *>(dC);
+    }
+    st = scan_bwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, g, dxw, ddw, dA,
+                      d_state ? dBw : nullptr, d_state ? dCw : nullptr, dD, batch, d_inner, d_state, H, W, stream);
+    if (st != SSM2D_OK) return st;
+    // d delta with respect to the raw step size, d bias (and the rounding)
+    if (prep || WIDE) {
+        step_bwd_kernel<TW, T><<<dim3(static_cast<unsigned>(batch * d_inner)), dim3(256), 0, s>>>(
+            ddw, ddelta, delta, delta_bias, ddelta_bias, H * W, static_cast<int>(d_inner), softplus ? 1 : 0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if constexpr (WIDE) {
+        if ((st = gate_or_round<TW, T>(dxw, nullptr, dx, total, s)) != SSM2D_OK) return st;
+        if (d_state > 0) {
+            if ((st = gate_or_round<TW, T>(dBw, nullptr, dB, tb, s)) != SSM2D_OK) return st;
+            if ((st = gate_or_round<TW, T>(dCw, nullptr, dC, tb, s)) != SSM2D_OK) return st;
+        }
     }
     return SSM2D_OK;
 }
@@ -775,27 +1058,78 @@ int ssm2d_sync_check(void *stream)
     SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    bool timeout = take_timeout_flag(dev, stream);
+    // the device error word, cleared here (a timeout counts from there only
+    // when the workspace has no host-visible flag, which reports it once by
+    // itself)
+    unsigned int *words[1] = {nullptr};
+    bool counts[1] = {false};
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || !it->second.head) return SSM2D_OK;
-    unsigned int v = 0;
-    SSM2D_HIP_TRY(hipMemcpy(&v, it->second.head + 2, sizeof(v), hipMemcpyDeviceToHost));
-    if (v != 0) {
-        unsigned int z = 0;
-        SSM2D_HIP_TRY(hipMemcpy(it->second.head + 2, &z, sizeof(z), hipMemcpyHostToDevice));
-        return SSM2D_ERR_DEVICE_TIMEOUT;
+    if (it != g_ws.end() && it->second.head) {
+        words[0] = it->second.head + 2;
+        counts[0] = it->second.herr == nullptr;
     }
+    for (int k = 0; k < 1; ++k) {
+        if (!words[k]) continue;
+        unsigned int v = 0;
+        SSM2D_HIP_TRY(hipMemcpy(&v, words[k], sizeof(v), hipMemcpyDeviceToHost));
+        if (v != 0) {
+            const unsigned int zero = 0;
+            SSM2D_HIP_TRY(hipMemcpy(words[k], &zero, sizeof(zero), hipMemcpyHostToDevice));
+            timeout = timeout || counts[k];
+        }
+    }
+    return timeout ? SSM2D_ERR_DEVICE_TIMEOUT : SSM2D_OK;
+}
+
+int ssm2d_release_workspaces(void *stream)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    SSM2D_HIP_TRY(hipStreamSynchronize(s));
+    const bool timeout = take_timeout_flag(dev, stream);
+    auto it = g_ws.find({dev, stream});
+    if (it != g_ws.end()) {
+        free_ws(it->second, s);
+        if (it->second.herr) (void)hipHostFree(it->second.herr);
+        g_ws.erase(it);
+    }
+    for (auto b = g_bufs.begin(); b != g_bufs.end();) {
+        if (b->first.first == std::make_pair(dev, stream)) {
+            free_async(b->second.buf, s);
+            b = g_bufs.erase(b);
+        } else {
+            ++b;
+        }
+    }
+    SSM2D_HIP_TRY(hipStreamSynchronize(s));
+    return timeout ? SSM2D_ERR_DEVICE_TIMEOUT : SSM2D_OK;
+}
+
+int ssm2d_test_set_epoch(void *stream, uint32_t epoch)
+{
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.head) return SSM2D_ERR_UNSUPPORTED;
+    SSM2D_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+    const unsigned int v = epoch % kEpochs;
+    SSM2D_HIP_TRY(hipMemcpy(it->second.head + 3, &v, sizeof(v), hipMemcpyHostToDevice));
     return SSM2D_OK;
 }
 
 int ssm2d_set_spin_limit(int64_t polls)
 {
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
     g_spin_limit = polls < 0 ? 0 : polls;
     return SSM2D_OK;
 }
 
-int ssm2d_version(void) { return 300; }
+int ssm2d_version(void) { return 400; }
 
 const char *ssm2d_last_hip_error(void)
 {

@@ -190,8 +190,8 @@ def test_bwd_ex_validation(lib, bf16):
     call = lambda dims, flags, ptrs=None: fn(*(ctypes.c_void_p(p) for p in (ptrs or [FAKE] * 13)), *dims, flags, None)
     for flags in (pkg.ACCUMULATE, pkg.FOUR_WAY, pkg.DELTA_SOFTPLUS, 128):
         assert call([1, 2, 3, 4, 5], flags) == pkg.ERR_BAD_FLAGS, flags
-    assert call([1, 2, 3, 4, 5], pkg.VERTICAL_FIRST) == pkg.ERR_UNSUPPORTED
-    for flags in (pkg.FLIP_H, pkg.FLIP_W, pkg.FLIP_H | pkg.FLIP_W):
+    for flags in (pkg.FLIP_H, pkg.FLIP_W, pkg.FLIP_H | pkg.FLIP_W, pkg.VERTICAL_FIRST,
+                  pkg.VERTICAL_FIRST | pkg.FLIP_H | pkg.FLIP_W):
         assert call([1, -2, 3, 4, 5], flags) == pkg.ERR_BAD_DIM
         assert call([1, 0, 3, 4, 5], flags, [0] * 13) == pkg.OK
 

@@ -201,13 +201,9 @@ def test_backward_mamba_options(opts, dtype):
                            delta_softplus=opts["sp"])
     pkg.sync_check()
     got = {k: v.double().cpu().numpy() for k, v in g.items()}
-    rnd = (lambda v: f32_from_bf16_bits(bf16_bits_from_f32(np.asarray(v, dtype=np.float32))).astype(np.float64)) \
-        if dtype == "bf16" else (lambda v: np.asarray(v, dtype=np.float32).astype(np.float64))
-    # the library hands the scan's backward dy * SiLU(z) in the input type
-    # (bf16: rounded to nearest even); the oracle takes the same values
+    # the oracle takes only the caller's inputs; every intermediate is fp64
     ref = oracle.bwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], dy, z=z, delta_bias=bias,
-                           delta_softplus=opts["sp"], delta_round=rnd if (opts["sp"] or opts["bias"]) else None,
-                           dy_round=rnd if dtype == "bf16" else None)
+                           delta_softplus=opts["sp"])
     cells = shape[0] * shape[3] * shape[4]
     check_grads(got, ref, dtype, cells, f"options {opts}")
     if "dz" in ref:
@@ -262,3 +258,38 @@ def test_backward_other_directions_chains(case, fl, monkeypatch):
     got = {k: as_f64(v) for k, v in g.items()}
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy, flip_h=fh, flip_w=fw), dtype,
                 shape[0] * shape[3] * shape[4], f"flips {fl} chains {case}")
+
+
+DIRS4 = [(False, False), (True, False), (False, True), (True, True)]
+
+
+@pytest.mark.parametrize("fl", DIRS4, ids=lambda f: "V" + ("H" if f[0] else "-") + ("W" if f[1] else "-"))
+@pytest.mark.parametrize("shape", [(1, 3, 4, 1, 37), (2, 5, 4, 29, 1), (1, 17, 8, 13, 7), (1, 9, 16, 14, 30),
+                                   (2, 16, 16, 21, 64), (1, 8, 32, 9, 21), (1, 8, 16, 70, 150)], ids=str)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_vertical_first(shape, fl, dtype):
+    """The backward of the vertical-first order in every direction
+    (ssm2d_scan_bwd_ex with SSM2D_VERTICAL_FIRST): non-square maps, ragged
+    sides, one row, one column, maps wider than a transpose tile."""
+    fh, fw = fl
+    _say(f"backward vertical-first flips {fl} {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 45, dtype=dtype)
+    dy, dy_dev = make_dy(t, dtype, _seed(shape) + 46)
+    g = pkg.scan_bwd(*to_dev(t, dtype), dy_dev, flip_h=fh, flip_w=fw, vertical_first=True)
+    pkg.sync_check()
+    got = {k: as_f64(v) for k, v in g.items()}
+    ref = oracle.bwd(*(t[k] for k in KEYS), dy, flip_h=fh, flip_w=fw, vertical_first=True)
+    check_grads(got, ref, dtype, shape[0] * shape[3] * shape[4], f"vertical-first {fl} {shape}")
+
+
+def test_backward_vertical_first_full_vmamba():
+    """VMamba stage 1 (bf16) at full size, vertical-first order: every
+    gradient element against the oracle."""
+    wl = next(w for w in WORKLOADS if w.name == "vmamba_t_s1")
+    t = make_inputs(wl, seed=0)
+    dy, dy_dev = make_dy(t, wl.dtype, 47)
+    g = pkg.scan_bwd(*to_dev(t, wl.dtype), dy_dev, vertical_first=True)
+    pkg.sync_check()
+    got = {k: as_f64(v) for k, v in g.items()}
+    check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy, vertical_first=True), wl.dtype,
+                wl.batch * wl.H * wl.W, "vmamba vertical-first")

@@ -1,9 +1,9 @@
 """GPU parity of the Mamba-option entry points (ssm2d_scan_fwd_mamba / _bf16):
 step size delta + delta_bias[d] through softplus, and SiLU(z) gating, against
 the oracle's fwd_mamba on the same seeded inputs. Bars as for the forward
-scan: 1e-4 (1 + |y_ref|) for fp32 and 2e-2 (1 + |y_ref|) for bf16; for the
-bf16 step size the oracle rounds softplus(delta + bias) to bf16 like the
-library (computed in fp32, rounded to nearest even)."""
+scan: 1e-4 (1 + |y_ref|) for fp32 and 2e-2 (1 + |y_ref|) for bf16. The oracle
+sees only the caller's inputs (fp64 copies of the exact values passed): the
+step size, the gate and the four-corner sums are computed in fp64 there."""
 import itertools
 
 import numpy as np
@@ -25,12 +25,6 @@ def _tensor(a, dtype):
         bits = bf16_bits_from_f32(a)
         return f32_from_bf16_bits(bits).astype(np.float64), torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
     return a.astype(np.float64), torch.from_numpy(a).cuda()
-
-
-def _round_like(dtype):
-    if dtype == "bf16":
-        return lambda v: f32_from_bf16_bits(bf16_bits_from_f32(np.asarray(v, dtype=np.float32))).astype(np.float64)
-    return lambda v: np.asarray(v, dtype=np.float32).astype(np.float64)
 
 
 SHAPES = [(1, 16, 16, 19, 64), (2, 9, 8, 11, 23), (1, 8, 4, 1, 30), (1, 5, 16, 27, 1)]
@@ -72,8 +66,7 @@ def test_step_size(shape, dtype, opts):
     y = pkg.scan_fwd_mamba(*args, delta_bias=None if bias is None else torch.from_numpy(bias).cuda(),
                            delta_softplus=opts["sp"])
     pkg.sync_check()
-    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], delta_bias=bias, delta_softplus=opts["sp"],
-                           delta_round=_round_like(dtype))
+    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], delta_bias=bias, delta_softplus=opts["sp"])
     check(as_f64(y), ref, dtype, f"step size {opts} {shape}")
 
 
@@ -94,19 +87,8 @@ def test_everything_together(dtype, monkeypatch):
                            four_way=True)
     pkg.sync_check()
     ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], None, z=z, delta_bias=bias, delta_softplus=True,
-                           delta_round=_round_like(dtype), four_way=True)
-    got = as_f64(y)
-    if dtype == "bf16":
-        # the four-corner sum is rounded to bf16 after each scan: bar against the terms
-        terms = [oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], None, delta_bias=bias, delta_softplus=True,
-                                  delta_round=_round_like(dtype), flip_h=fh, flip_w=fw)
-                 for fh, fw in ((False, False), (True, False), (False, True), (True, True))]
-        scale = 1.0 + np.abs(oracle.silu(z)) * sum(np.abs(v) for v in terms)
-        err = float(np.max(np.abs(got - ref) / scale))
-        _say(f"  everything bf16: {err:.3e}")
-        assert err <= 2e-2
-    else:
-        check(got, ref, dtype, "everything together")
+                           four_way=True)
+    check(as_f64(y), ref, dtype, "everything together")
     monkeypatch.setenv("SSM2D_WAVES", "2")
     shape = (1, 8, 16, 17, 60)
     t = make_random_inputs(*shape, seed=26, dtype=dtype)
@@ -201,8 +183,7 @@ def test_options_full_size_sampled(name):
     pkg.sync_check()
     nmaps = wl.batch * wl.d_inner
     maps = np.unique(np.array([0, 7, nmaps // 2, nmaps - 1]))
-    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], z=z, delta_bias=bias, delta_softplus=True,
-                           delta_round=_round_like(dtype), maps=maps)
+    ref = oracle.fwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], z=z, delta_bias=bias, delta_softplus=True, maps=maps)
     check(as_f64(y).reshape(nmaps, wl.H, wl.W)[maps], ref, dtype, f"{name} options, maps {maps.tolist()}")
 
 

@@ -197,3 +197,32 @@ def test_flipped_backward_finite_differences(oracle_lib):
                 fd[idx] = (lp - lm) / (2 * h)
             err = np.max(np.abs(g[GRAD[k]] - fd) / (1.0 + np.abs(fd)))
             assert err < 1e-6, f"{GRAD[k]} flips {fh},{fw}: {err:.2e}"
+
+
+def test_vertical_first_backward_finite_differences(oracle_lib):
+    """The backward of the vertical-first order, in all four directions,
+    against central finite differences of that forward (every input). The
+    map is not square, so a transposition taken the wrong way round fails."""
+    ins = _inputs(1, 2, 2, 3, 4, 43)
+    dy = np.random.default_rng(43).standard_normal(ins["x"].shape)
+    for fh, fw in ((False, False), (True, False), (False, True), (True, True)):
+        kw = dict(flip_h=fh, flip_w=fw, vertical_first=True)
+        g = oracle.bwd(*(ins[k] for k in KEYS), dy, lib=oracle_lib, **kw)
+
+        def loss():
+            return float(np.sum(oracle.fwd(*(ins[k] for k in KEYS), lib=oracle_lib, **kw) * dy))
+
+        for k in KEYS:
+            base = ins[k]
+            fd = np.empty_like(base)
+            for idx in np.ndindex(base.shape):
+                h = 1e-6 * max(1.0, abs(base[idx]))
+                orig = base[idx]
+                base[idx] = orig + h
+                lp = loss()
+                base[idx] = orig - h
+                lm = loss()
+                base[idx] = orig
+                fd[idx] = (lp - lm) / (2 * h)
+            err = np.max(np.abs(g[GRAD[k]] - fd) / (1.0 + np.abs(fd)))
+            assert err < 1e-6, f"{GRAD[k]} vertical-first flips {fh},{fw}: {err:.2e}"
