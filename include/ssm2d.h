@@ -66,6 +66,8 @@
  *   workspace allocation failure                 -> SSM2D_ERR_NOMEM
  *   a kernel of an earlier call on this (device, stream) timed out
  *                                                -> SSM2D_ERR_DEVICE_TIMEOUT
+ *   (ssm2d_scan_fwd_noalloc only) a workspace beyond its static array
+ *                                                -> SSM2D_ERR_TOO_LARGE
  * NaN and Inf inputs are not checked; they propagate.
  */
 #ifndef SSM2D_H
@@ -90,7 +92,8 @@ typedef enum {
     SSM2D_ERR_HIP = 5,
     SSM2D_ERR_NOMEM = 6,
     SSM2D_ERR_DEVICE_TIMEOUT = 7,
-    SSM2D_ERR_BAD_FLAGS = 8
+    SSM2D_ERR_BAD_FLAGS = 8,
+    SSM2D_ERR_TOO_LARGE = 9
 } ssm2d_status;
 
 /* fp32 forward: x, delta, B, C, y are float32; A, D float32; state fp32. */
@@ -302,11 +305,38 @@ int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const fl
                               int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
                               int64_t W, uint32_t flags, void *stream);
 
+/* ---- Forward without allocation -------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not record allocations, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, layout, results and errors as
+ * ssm2d_scan_fwd (fp32), and the same kernels, but the scan's workspace (head
+ * words, carry ring, zero page) is a static device array of 16 MiB that each
+ * GPU the library runs on holds until the process ends: this call allocates
+ * nothing, on the device or for the timeout flag. On the first call on a
+ * device the array's address is looked up (hipGetSymbolAddress) and the array
+ * is zeroed by a kernel on `stream`.
+ * Limits: the zero page holds 1 MiB (H * W <= 262128 cells) and the carry
+ * ring about 15 MiB (chains of tiles that span workgroups need
+ * n_chains * (workgroups per chain - 1) * ring rows * 8 bytes per state
+ * group slot; the giga-pixel map, 384 x 512 with 128 channels and 16 states,
+ * needs 7.5 MiB). A call whose plan exceeds them returns SSM2D_ERR_TOO_LARGE
+ * and enqueues nothing.
+ * Every call on a GPU shares that GPU's array, whose head words (tickets,
+ * tag epoch) carry over from call to call: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Timeouts show as NaN outputs and in ssm2d_sync_check (there is no
+ * host-visible flag). */
+int ssm2d_scan_fwd_noalloc(const float *x, const float *delta, const float *A, const float *B,
+                           const float *C, const float *D, float *y, int64_t batch, int64_t d_inner,
+                           int64_t d_state, int64_t H, int64_t W, void *stream);
+
 /* Static description of a status code. Never NULL. */
 const char *ssm2d_status_string(int status);
 
 /* Waits for `stream`, then returns and clears the timeout records of that
- * stream's workspace (the device error word and the host-visible flag): SSM2D_OK,
+ * stream's workspace (the device error word and the host-visible flag), and
+ * the error word of the device's ssm2d_scan_fwd_noalloc array: SSM2D_OK,
  * or SSM2D_ERR_DEVICE_TIMEOUT if a kernel gave up waiting for a neighbouring
  * tile's carries (its outputs from that point on are NaN). Returns
  * SSM2D_ERR_HIP if the wait fails. */

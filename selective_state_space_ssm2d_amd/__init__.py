@@ -36,7 +36,7 @@ LIB_PATH = os.path.join(_PKG, "libssm2d.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm2d.h")
 
 (OK, ERR_NULLPTR, ERR_BAD_DIM, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NOMEM, ERR_DEVICE_TIMEOUT,
- ERR_BAD_FLAGS) = range(9)
+ ERR_BAD_FLAGS, ERR_TOO_LARGE) = range(10)
 FLIP_H, FLIP_W, VERTICAL_FIRST, ACCUMULATE, FOUR_WAY, DELTA_SOFTPLUS = 1, 2, 4, 8, 16, 32
 
 _lib = None
@@ -57,7 +57,7 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
     lib = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16"):
+    for name in ("ssm2d_scan_fwd", "ssm2d_scan_fwd_bf16", "ssm2d_scan_fwd_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
         f.restype = ctypes.c_int

@@ -1532,6 +1532,9 @@ struct Plan {
     const void *z;   // gate input (kModeGate)
     const float *h_init;  // carried vertical states in / out (may be null)
     float *h_last;
+    // Workspace of fixed size to launch in (null: the per-(device, stream)
+    // workspace, grown as needed)
+    const struct WsEntry *fixed_ws;
 };
 
 int env_int(const char *name, int dflt);
@@ -1559,7 +1562,8 @@ int device_cus(int dev);
 struct WsNeed {
     size_t gring_bytes, zero_bytes, cons_count;
 };
-// The plan's launch, given its workspace.
+// The plan's launch, given its workspace (shared by the allocating entry
+// points and the one that runs in a static device array).
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
                 int d_inner, int d_state, int H, int W, const Plan &pl, const WsEntry &e, void *stream);
@@ -1621,6 +1625,14 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
     if (!COOP) pl.coop_slots = 0;
     pl.qg = choose_qg<T, K, NPL, ALIGN, G, COOP, MODE>(pl, dev, H);
     const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
+    if (pl.fixed_ws) {
+        // a workspace of fixed size (no allocation): the plan must fit it
+        if (need.gring_bytes > pl.fixed_ws->gring_bytes || need.zero_bytes > pl.fixed_ws->zero_bytes ||
+            need.cons_count > pl.fixed_ws->cons_count)
+            return SSM2D_ERR_TOO_LARGE;
+        return launch_plan<T, K, NPL, ALIGN, G, COOP, MODE>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl,
+                                                            *pl.fixed_ws, stream);
+    }
     WsEntry *e = nullptr;
     const int st = get_ws(dev, stream, need.gring_bytes, need.zero_bytes, need.cons_count, &e);
     if (st != SSM2D_OK) return st;

@@ -441,6 +441,47 @@ __global__ void zero_kernel(float *p, long n)
     if (t < n) p[t] = 0.0f;
 }
 
+// ---------------------------------------------------------------- static scratch
+
+// Workspace of ssm2d_scan_fwd_noalloc: a static device array (each GPU the
+// library runs on holds its own copy until the process ends). Its layout
+// follows the scan workspace: head words, sink and up to kScratchCons
+// consumer words; the zero page; the global carry ring in the rest.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+constexpr size_t kScratchHead = size_t{64} << 10;
+constexpr size_t kScratchZeros = size_t{1} << 20;
+constexpr size_t kScratchCons = (kScratchHead - kHeadBytes - kSinkBytes) / sizeof(unsigned long long);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::map<int, WsEntry> g_scratch;  // per device: views of that device's copy (its address from the runtime)
+
+// The scratch workspace of device `dev` (current). On the first call on a
+// device its address is looked up (the array's name is a host-side stand-in,
+// not a device address) and the array is zeroed on `s`.
+int scratch_ws(int dev, hipStream_t s, const WsEntry **out)
+{
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr) return SSM2D_ERR_HIP;
+        const int st = zero_async(ptr, kScratchBytes, s);
+        if (st != SSM2D_OK) return st;
+        WsEntry w{};
+        unsigned char *base = static_cast<unsigned char *>(ptr);
+        w.head = reinterpret_cast<unsigned int *>(base);
+        w.zeros = base + kScratchHead;
+        w.gring = reinterpret_cast<unsigned long long *>(base + kScratchHead + kScratchZeros);
+        w.gring_bytes = kScratchBytes - kScratchHead - kScratchZeros;
+        w.zero_bytes = kScratchZeros;
+        w.cons_count = kScratchCons;
+        w.herr = nullptr;  // (nothing is allocated: timeouts show as NaN outputs and in ssm2d_sync_check)
+        it = g_scratch.emplace(dev, w).first;
+    }
+    *out = &it->second;
+    return SSM2D_OK;
+}
+
 int device_cus(int dev)
 {
     static std::map<int, int> cache;
@@ -484,13 +525,15 @@ void choose_coop(Plan &pl, int64_t H, int align)
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
-           const T *z = nullptr, const float *h_init = nullptr, float *h_last = nullptr)
+           const T *z = nullptr, const float *h_init = nullptr, float *h_last = nullptr,
+           const WsEntry *fixed_ws = nullptr)
 {
     Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
     pl.flip_h = flip_h;
     pl.z = z;
     pl.h_init = h_init;
     pl.h_last = h_last;
+    pl.fixed_ws = fixed_ws;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
@@ -1049,8 +1092,27 @@ const char *ssm2d_status_string(int status)
     case SSM2D_ERR_DEVICE_TIMEOUT: return "kernel timed out waiting for a neighbouring strip's carries";
     case SSM2D_ERR_BAD_FLAGS:
         return "unknown flag bits, SSM2D_FOUR_WAY with a flip flag or carried states, or a gate with SSM2D_ACCUMULATE";
+    case SSM2D_ERR_TOO_LARGE: return "the call's workspace exceeds the static scratch of ssm2d_scan_fwd_noalloc";
     default: return "unknown status";
     }
+}
+
+int ssm2d_scan_fwd_noalloc(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                           const float *D, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                           int64_t W, void *stream)
+{
+    bool work = false;
+    const int chk = check_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, 0u, false, nullptr,
+                                     nullptr, nullptr, nullptr, &work);
+    if (chk != SSM2D_OK || !work) return chk;
+    int dev = 0;
+    SSM2D_HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::recursive_mutex> lock(g_mutex);
+    const WsEntry *ws = nullptr;
+    const int st = scratch_ws(dev, static_cast<hipStream_t>(stream), &ws);
+    if (st != SSM2D_OK) return st;
+    return launch<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, 0, 0, dev, stream, nullptr, nullptr,
+                         nullptr, ws);
 }
 
 int ssm2d_sync_check(void *stream)
@@ -1060,17 +1122,19 @@ int ssm2d_sync_check(void *stream)
     SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::recursive_mutex> lock(g_mutex);
     bool timeout = take_timeout_flag(dev, stream);
-    // the device error word, cleared here (a timeout counts from there only
-    // when the workspace has no host-visible flag, which reports it once by
-    // itself)
-    unsigned int *words[1] = {nullptr};
-    bool counts[1] = {false};
+    // device error words, cleared here: the stream's workspace (a timeout
+    // counts from there only when the workspace has no host-visible flag,
+    // which reports it once by itself), and the static scratch
+    unsigned int *words[2] = {nullptr, nullptr};
+    bool counts[2] = {false, true};
     auto it = g_ws.find({dev, stream});
     if (it != g_ws.end() && it->second.head) {
         words[0] = it->second.head + 2;
         counts[0] = it->second.herr == nullptr;
     }
-    for (int k = 0; k < 1; ++k) {
+    auto sc = g_scratch.find(dev);
+    if (sc != g_scratch.end()) words[1] = sc->second.head + 2;
+    for (int k = 0; k < 2; ++k) {
         if (!words[k]) continue;
         unsigned int v = 0;
         SSM2D_HIP_TRY(hipMemcpy(&v, words[k], sizeof(v), hipMemcpyDeviceToHost));

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         text = lib.ssm2d_status_string(s)
         assert text and text != b"unknown status", s
     assert lib.ssm2d_status_string(99) == b"unknown status"
