@@ -114,11 +114,37 @@ def copy_probe(mb: int, steps: int) -> None:
     print(json.dumps({"copy_probe_mb": mb, "steps": steps}))
 
 
-def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str):
+# The scan kernels: the general one and the two-rows-per-step forward of tall maps.
+SCAN_KERNELS = ("scan2d_fwd_kernel", "scan2d_fast_kernel")
+
+
+def is_scan_kernel(name: str) -> bool:
+    return any(k in name for k in SCAN_KERNELS)
+
+
+def kernel_name(wl, variant: str) -> str:
+    """The scan kernel a workload's launch runs: the two-rows-per-step forward
+    for the plain scan of tall maps whose chains span workgroups (8 state
+    groups, 4-column strips, rows of a multiple of 4 columns, at most 16
+    states), else the general kernel."""
+    if variant in ("fwd",) and wl.H >= 128 and wl.W % 4 == 0 and 4 < wl.d_state <= 16 and \
+            os.environ.get("SSM2D_FAST", "1") != "0":
+        chains4 = wl.batch * ((wl.d_inner + 15) // 16)
+        if chains4 < 512:  # 8 state groups; chains of one workgroup otherwise
+            chains8 = wl.batch * ((wl.d_inner + 7) // 8)
+            if chains8 < 256:
+                return "scan2d_fast_kernel"
+    return "scan2d_fwd_kernel"
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str, name_part):
+    """Median per dispatch of a counter over the kernels whose name contains
+    name_part (a string, or a tuple of alternatives)."""
+    parts = (name_part,) if isinstance(name_part, str) else tuple(name_part)
     vals = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            if any(q in r["Kernel_Name"] for q in parts) and r["Counter_Name"] == counter:
                 vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not vals:
         raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} under {run_dir}")
@@ -134,13 +160,13 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
     copy_bytes = copy_mb * 1024 * 1024
     cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy") * 1024.0
     cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy") * 1024.0
-    sf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "scan2d_fwd_kernel") * 1024.0
-    sw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "scan2d_fwd_kernel") * 1024.0
+    sf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", SCAN_KERNELS) * 1024.0
+    sw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", SCAN_KERNELS) * 1024.0
     kf, kw = copy_bytes / cf, copy_bytes / cw
     rec = {
         "workload": workload,
         "variant": variant,
-        "kernel": "scan2d_fwd_kernel",
+        "kernel": " / ".join(SCAN_KERNELS),
         "kernel_source_sha256_16": kernel_source_hash(),
         "copy_probe_bytes": copy_bytes,
         "copy_fetch_counter_bytes": cf, "copy_write_counter_bytes": cw,
@@ -328,7 +354,7 @@ def counter_table(workload: str, dirs, out_dir: str = PROFILES) -> dict:
     """Per-dispatch SQ counters of the scan kernel (median over dispatches)
     from rocprofv3 --pmc runs of this benchmark, one run per counter group:
     profiles/sq_counters_<workload>.txt."""
-    lines = [f"# rocprofv3 SQ counters of scan2d_fwd_kernel, workload {workload} (median per dispatch; "
+    lines = [f"# rocprofv3 SQ counters of the scan kernel, workload {workload} (median per dispatch; "
              "totals over the chip's waves)",
              f"# kernel source sha256[:16] {kernel_source_hash()}"]
     for grp in SQ_COUNTERS:
@@ -340,13 +366,13 @@ def counter_table(workload: str, dirs, out_dir: str = PROFILES) -> dict:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             per = {}
             for r in csv.DictReader(open(f)):
-                if "scan2d_fwd_kernel" in r["Kernel_Name"]:
+                if is_scan_kernel(r["Kernel_Name"]):
                     key = (r["Dispatch_Id"], r["Counter_Name"])
                     per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
             for (_, name), v in per.items():
                 vals.setdefault(name, []).append(v)
     if not vals:
-        raise SystemExit("no scan2d_fwd_kernel counter rows under " + " ".join(dirs))
+        raise SystemExit("no scan kernel counter rows under " + " ".join(dirs))
     med = {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
     for k in sorted(med):
         lines.append(f"{k} | {med[k]:.6g}")
@@ -515,7 +541,7 @@ def main():
                    "input_copies_cycled": ncopies, "variant": args.variant, "launches_per_step": launches},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": step_bytes,
-                     "kernel": "scan2d_fwd_kernel", "kernel_ms_mean": kmean / launches,
+                     "kernel": kernel_name(wl, args.variant), "kernel_ms_mean": kmean / launches,
                      "kernel_ms_median": float(np.median(kern_ms)) / launches,
                      "kernel_ms_min": float(np.min(kern_ms)) / launches},
         "alu": {"achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / ALU_PEAK_TFLOPS,

@@ -1,0 +1,560 @@
+// libssm2d: the plain forward scan of tall maps whose chains of strips are cut
+// into several workgroups (the giga-pixel layout), two rows per step.
+//
+// Method (juejin.cn "2DMamba 精读", part 四 section 5; papernotes.org "2DMamba" 关键设计):
+//   Abar = exp(delta*A), Bx = delta*B*x
+//   hh[i,j] = Abar*hh[i,j-1] + Bx         horizontal scan, zero before column 0
+//   h[i,j]  = Abar*h[i-1,j]  + hh[i,j]    vertical scan of the horizontal results
+//   y = sum_n C*h + D*x                   state dims reduced on chip, only y stored
+//
+// Same decomposition as the general kernel (scan2d_kernel.h): a wave is 64/G
+// channels x G state groups of NPL states, walking a strip of 4 columns down
+// the map; the strips of a chain pass the row carry on through LDS rings
+// inside a workgroup and through the couriers' tagged global words between
+// workgroups; the workgroup's strips load their input rows cooperatively, in
+// whole cache lines, into a shared ring of rows in LDS.
+//
+// What differs is the row loop, whose bookkeeping the general kernel pays
+// per row: here one step covers two rows. Both rows' carry-independent work
+// (decay factors, inputs) runs first; then one wait covers both rows' left
+// carries, the two horizontal chains (independent of each other) run side by
+// side, and one publish hands both carries on. The step loop is unrolled over
+// the input ring (8 steps, 16 rows) and the carry rings (4 steps), so every
+// LDS slot is a compile-time offset; the ring's arrival counts are per step;
+// the output stores have one layout (a full strip of 4 aligned columns).
+#pragma once
+
+#include "scan2d_kernel.h"
+
+namespace ssm2d_impl {
+
+constexpr int kFastSteps = 8;       // steps of the input ring (two rows each)
+constexpr int kFastAhead = 3;       // steps a wave writes its share ahead of processing
+constexpr int kFastPrefetch = 2;    // steps a share's loads are issued ahead of writing it
+constexpr int kFastCarryRows = 8;   // rows of each LDS carry ring
+constexpr int kFastStrips = 8;      // strips a workgroup can hold (with two couriers)
+
+// Input ring: the invariant that keeps a slot from being rewritten while it is
+// read. A wave reads step t only after every wave has written its share of
+// it, which each wave does kFastAhead steps before processing it: so no wave
+// is more than kFastAhead steps ahead of another. The fastest wave (at step f)
+// writes step f + kFastAhead; the slowest reads a step >= f - kFastAhead; the
+// two are 2 * kFastAhead < kFastSteps steps apart, so never in one slot.
+static_assert(2 * kFastAhead < kFastSteps, "input ring too shallow for the staging distance");
+static_assert(kFastPrefetch == 2, "two register sets of staged shares");
+
+// One chunk (4 elements) as a plain vector, which the compiler keeps in
+// registers across the unrolled steps.
+template <typename T> struct FastChunkOf;
+template <> struct FastChunkOf<float> { using type = float __attribute__((ext_vector_type(4))); };
+template <> struct FastChunkOf<uint16_t> { using type = unsigned __attribute__((ext_vector_type(2))); };
+
+template <typename T, int G, int NPL>
+struct FastShape {
+    using Chunk = typename FastChunkOf<T>::type;
+    static constexpr int CPW = kWave / G;                       // channels per wave
+    static constexpr int NCHUNK = 2 * CPW + 2 * G * NPL;        // packet rows: x, delta, B, C
+    static constexpr int PASSES = (NCHUNK + kWave - 1) / kWave;  // chunks a lane loads per row
+    static constexpr int PST = NCHUNK + 1;                      // chunks per strip packet (one pad chunk)
+    static constexpr int ROWC = kFastStrips * PST;              // chunks per ring row
+    static constexpr size_t ring_bytes = static_cast<size_t>(2 * kFastSteps) * ROWC * sizeof(Chunk);
+    static constexpr size_t carry_bytes = static_cast<size_t>(kFastStrips + 1) * kFastCarryRows * kWave * NPL * 4;
+    static constexpr size_t lds_bytes = ring_bytes + carry_bytes;
+};
+
+template <typename T, int G, int NPL>
+__global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(Params p)
+{
+    using Sh = FastShape<T, G, NPL>;
+    using Chunk = typename Sh::Chunk;
+    constexpr int CPW = Sh::CPW, NCHUNK = Sh::NCHUNK, PASSES = Sh::PASSES, PST = Sh::PST, ROWC = Sh::ROWC;
+    constexpr int SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
+    constexpr int CR = kFastCarryRows;
+    constexpr int KO = 4 / G > 0 ? 4 / G : 1;  // finished cells per lane and row (1)
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_done[kFastStrips + 1];   // rows published into LDS carry ring w
+    __shared__ int s_used[kFastStrips + 1];   // rows consumed from LDS carry ring w
+    __shared__ int s_arrive[kFastSteps];      // shares written into input-ring step slot
+    __shared__ unsigned int s_ticket, s_epoch;
+    __shared__ int s_last;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    if (threadIdx.x == 0) {
+        s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % kEpochs + 1;
+    }
+    if (threadIdx.x <= kFastStrips) {
+        s_done[threadIdx.x] = 0;
+        s_used[threadIdx.x] = 0;
+    }
+    if (threadIdx.x < kFastSteps) s_arrive[threadIdx.x] = 0;
+    __syncthreads();
+
+    // Tickets put every producer workgroup before its consumer (a waiting
+    // workgroup's producer is resident or done).
+    const int wg = static_cast<int>(s_ticket);
+    const int chain = wg % p.n_chains;
+    const int grp = wg / p.n_chains;
+    const int b = chain / p.n_dblk;
+    const int dblk = chain % p.n_dblk;
+    const int H = p.H, W = p.W;
+    const long ring_floats = static_cast<long>(CR) * kWave * NPL;
+    float *lring = reinterpret_cast<float *>(smem + Sh::ring_bytes);
+
+    if (wave >= p.s_local) {
+        courier_wave<NPL>(p, wave, lane, chain, grp, lring, s_done, s_used, s_epoch, ring_floats, CR - 1);
+    } else if (grp * p.s_local + wave < p.nstrips) {
+        // ---------------- compute wave: one strip of 4 columns
+        const int strip = grp * p.s_local + wave;
+        const int j0 = strip * 4;
+        const int nact = min(p.s_local, p.nstrips - grp * p.s_local);  // strips of this workgroup
+        const int g = lane / CPW;
+        const int dl = lane % CPW;
+        const int d = dblk * CPW + dl;
+        const bool d_ok = d < p.d_inner;
+        const long HW = static_cast<long>(H) * W;
+        // rows in scan order: top to bottom, or bottom to top (row t at row0 + t * rs)
+        const int rs = p.flip_h ? -W : W;
+        const long row0 = p.flip_h ? HW - W : 0;
+        const T *zeros = static_cast<const T *>(p.zeros);
+        T *ring = reinterpret_cast<T *>(smem);  // [16 rows][ROWC chunks of 4 elements]
+
+        // This lane's chunks of the workgroup's rows: wave w loads chunks
+        // [w NCHUNK, (w + 1) NCHUNK) of a row taken in column order (packet row
+        // r of strips 0 .. nact-1, then packet row r + 1, ...), so a load
+        // instruction reads whole cache lines, and writes each chunk into its
+        // strip's packet. Padding lanes read the zero page into their own pad
+        // chunk.
+        const T *src[PASSES];
+        int wdst[PASSES];
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+            const int c = pp * kWave + lane;
+            const T *base = zeros;
+            int dst = wave * PST + NCHUNK;
+            long col = 0;
+            if (c < NCHUNK) {
+                const int cw = wave * NCHUNK + c;
+                const int r = cw / nact, sj = cw % nact;
+                dst = sj * PST + r;
+                col = static_cast<long>(grp * p.s_local + sj) * 4;
+                if (r < SEG_DT) {
+                    const int dd = dblk * CPW + r;
+                    if (dd < p.d_inner) base = static_cast<const T *>(p.x) + (static_cast<long>(b) * p.d_inner + dd) * HW;
+                } else if (r < SEG_B) {
+                    const int dd = dblk * CPW + r - SEG_DT;
+                    if (dd < p.d_inner) base = static_cast<const T *>(p.delta) + (static_cast<long>(b) * p.d_inner + dd) * HW;
+                } else if (r < SEG_C) {
+                    const int n = r - SEG_B;
+                    if (n < p.d_state) base = static_cast<const T *>(p.B) + (static_cast<long>(b) * p.d_state + n) * HW;
+                } else {
+                    const int n = r - SEG_C;
+                    if (n < p.d_state) base = static_cast<const T *>(p.C) + (static_cast<long>(b) * p.d_state + n) * HW;
+                }
+            }
+            src[pp] = base + row0 + (base == zeros ? 0 : col);
+            wdst[pp] = dst;
+        }
+
+        float Ap[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const int n = g * NPL + k;
+            Ap[k] = (n < p.d_state && d_ok) ? p.A[d * p.d_state + n] * kLog2e : 0.0f;
+        }
+        const float Dd = d_ok ? p.D[d] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) asm volatile("" ::"v"(Ap[k]));
+        asm volatile("" ::"v"(Dd));
+
+        // Operand offsets (elements) of this lane in a ring row.
+        const int off_x = (wave * PST + dl) * 4;
+        const int off_dt = (wave * PST + SEG_DT + dl) * 4;
+        int off_b[NPL], off_c[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            off_b[k] = (wave * PST + SEG_B + g * NPL + k) * 4;
+            off_c[k] = (wave * PST + SEG_C + g * NPL + k) * 4;
+        }
+        // the finished cell of this lane after the sum over state groups, and
+        // the pair stores of a full strip (row r of the wave holds cell r; one
+        // swap of odd and even rows leaves cells 0, 1 in row 0 and 2, 3 in
+        // row 2, whose channel lanes store two cells each)
+        const int c_out = (4 >= G) ? g * KO : g / 2;
+        const int off_xo = off_x + c_out;
+        const bool storer = ((lane & ~32) < CPW) && d_ok;
+        T *yv = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (storer ? d : 0)) * HW + row0 + j0 +
+                (((lane >> 5) & 1) ? 2 : 0);
+
+        const bool has_left = strip > 0;
+        const bool has_right = strip + 1 < p.nstrips;
+        const float *ring_in = lring + static_cast<long>(wave) * ring_floats + lane * NPL;
+        float *ring_out = lring + static_cast<long>(wave + 1) * ring_floats + lane * NPL;
+        bool timed_out = false;
+        int skip = 0;  // kSkipWaits once a wait has given up: later waits pass at once
+
+        // A wait that gave up: later waits are skipped, and the decay
+        // exponents become NaN, so that every output this strip computes
+        // from here on (and, through its carries, the strips after it) is NaN.
+        auto give_up = [&]() __attribute__((always_inline)) {
+            timed_out = true;
+            skip = kSkipWaits;
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) Ap[k] = quiet_nan();
+        };
+        auto wait_count = [&](const int *c, const int need) __attribute__((always_inline)) {
+            long long spins = 0;
+            while (__builtin_amdgcn_readfirstlane(lds_peek(c)) < need) {
+                if (++spins > p.spin_limit) {
+                    give_up();
+                    break;
+                }
+                if (spins > kSpinPolls) sleep_a_bit();
+            }
+            signal_fence();
+        };
+
+        float hv[4][NPL];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
+
+        // Shares of two steps in flight: stg[s] holds the share of the step
+        // staged kFastPrefetch steps after it was loaded.
+        Chunk stg[2][2][PASSES];
+        auto load_step = [&](Chunk (&dst)[2][PASSES], const int first_row) __attribute__((always_inline)) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                for (int pp = 0; pp < PASSES; ++pp) {
+                    const long off = static_cast<long>(min(first_row + rr, H - 1)) * rs;
+                    dst[rr][pp] = *reinterpret_cast<const Chunk *>(src[pp] + off);
+                }
+        };
+        auto write_step = [&](const Chunk (&sh)[2][PASSES], const int slot) __attribute__((always_inline)) {
+            T *r0 = ring + static_cast<long>(2 * slot) * ROWC * 4;
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                for (int pp = 0; pp < PASSES; ++pp)
+                    reinterpret_cast<Chunk *>(r0 + static_cast<long>(rr) * ROWC * 4)[wdst[pp]] = sh[rr][pp];
+            signal_fence();
+            if (lane == 0) __hip_atomic_fetch_add(&s_arrive[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            signal_fence();
+        };
+
+        // Rows of the strip. LEFT: a strip (or the inbound courier) to the
+        // left sends carries into LDS ring `wave`; RIGHT: one to the right
+        // takes them from ring `wave + 1`.
+        auto strip_rows = [&](auto left_tag, auto right_tag) __attribute__((always_inline)) {
+            constexpr bool LEFT = decltype(left_tag)::value != 0;
+            constexpr bool RIGHT = decltype(right_tag)::value != 0;
+            int room = CR;  // rows this wave may publish, as last seen
+
+            // Step of rows i = i0 + 2J and i + 1; J fixes the ring slots.
+            // TAIL: the last, partial block of 16 rows (steps past the map
+            // are skipped, and a second row past it is not stored).
+            auto step = [&](const int i0, auto jt, auto tail_t) __attribute__((always_inline)) {
+                constexpr int J = decltype(jt)::value;
+                constexpr bool TAIL = decltype(tail_t)::value != 0;
+                const int i = i0 + 2 * J;
+                if constexpr (TAIL) {
+                    if (i >= H) return;
+                }
+                // ---- stage: this wave's share of step J + kFastAhead, loaded
+                // two steps ago; then the loads for two steps further on
+                constexpr int JS = (J + kFastAhead) % kFastSteps;
+                write_step(stg[J % 2], JS);
+                load_step(stg[J % 2], i + 2 * (kFastAhead + kFastPrefetch));
+
+                // ---- this step's rows (their arrival was confirmed at the end
+                // of the previous step), and the arrival count of the next
+                // step's, confirmed at the end of this one
+                const T *r0 = ring + static_cast<long>(2 * J) * ROWC * 4;
+                const T *r1 = r0 + static_cast<long>(ROWC) * 4;
+                float xv[2][4], dv[2][4], Bv[2][NPL][4], Cv[2][NPL][4], xo[2];
+                read_packet<4>(r0, off_x, xv[0]);
+                read_packet<4>(r0, off_dt, dv[0]);
+                read_packet<4>(r1, off_x, xv[1]);
+                read_packet<4>(r1, off_dt, dv[1]);
+#pragma unroll
+                for (int k = 0; k < NPL; ++k) {
+                    read_packet<4>(r0, off_b[k], Bv[0][k]);
+                    read_packet<4>(r1, off_b[k], Bv[1][k]);
+                    read_packet<4>(r0, off_c[k], Cv[0][k]);
+                    read_packet<4>(r1, off_c[k], Cv[1][k]);
+                }
+                xo[0] = elem_value(r0[off_xo]);
+                xo[1] = elem_value(r1[off_xo]);
+                constexpr int JN = (J + 1) % kFastSteps;
+                const int need_next = nact * (((i + 2) >> 4) + 1);
+                const int seen_next = lds_peek(&s_arrive[JN]);
+                // left carries of both rows (counter, then the two slots)
+                constexpr int C0 = (2 * J) % CR;
+                int seen_c = 0;
+                float hh[2][NPL];
+                if constexpr (LEFT) {
+                    seen_c = lds_peek(&s_done[wave]);
+                    signal_fence();
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        hh[0][k] = ring_in[C0 * kWave * NPL + k];
+                        hh[1][k] = ring_in[(C0 + 1) * kWave * NPL + k];
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) hh[0][k] = hh[1][k] = 0.0f;
+                }
+
+                // ---- carry-independent work of both rows
+                float av[2][4][NPL], bx[2][4][NPL];
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float dx = dv[rr][c] * xv[rr][c];
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            av[rr][c][k] = __builtin_amdgcn_exp2f(dv[rr][c] * Ap[k]);
+                            bx[rr][c][k] = dx * Bv[rr][k][c];
+                        }
+                    }
+                // keep that work ahead of the waits below (the compiler would
+                // sink it onto the carries' critical path)
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(av[rr][c][k]), "+v"(bx[rr][c][k]));
+
+                const int pub = TAIL ? min(i + 2, H) : i + 2;  // rows published after this step
+                // room in the right ring for both rows (rarely short)
+                if constexpr (RIGHT) {
+                    if (pub > max(room, skip)) {
+                        room = wait_counter_above(&s_used[wave + 1], pub - CR - 1, p.spin_limit, timed_out) + CR;
+                        if (timed_out) give_up();
+                    }
+                }
+                if constexpr (LEFT) {
+                    if (max(__builtin_amdgcn_readfirstlane(seen_c), skip) < pub) {
+                        // not both rows published yet: poll counter and slots
+                        // together (one LDS round trip per poll)
+                        long long spins = 0;
+                        while (true) {
+                            const int v = lds_peek(&s_done[wave]);
+                            signal_fence();
+                            float t0[NPL], t1[NPL];
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k) {
+                                t0[k] = ring_in[C0 * kWave * NPL + k];
+                                t1[k] = ring_in[(C0 + 1) * kWave * NPL + k];
+                            }
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(t0[k]), "+v"(t1[k]));
+                            if (__builtin_amdgcn_readfirstlane(v) >= pub) {
+#pragma unroll
+                                for (int k = 0; k < NPL; ++k) {
+                                    hh[0][k] = t0[k];
+                                    hh[1][k] = t1[k];
+                                }
+                                break;
+                            }
+                            if (++spins > p.spin_limit) {
+                                give_up();
+#pragma unroll
+                                for (int k = 0; k < NPL; ++k) hh[0][k] = hh[1][k] = quiet_nan();
+                                break;
+                            }
+                            if (spins > kSpinPolls) sleep_a_bit();
+                        }
+                    }
+                }
+
+                // ---- the two horizontal chains, then hand both carries on
+                float hc[2][4][NPL];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            hh[rr][k] = __builtin_fmaf(av[rr][c][k], hh[rr][k], bx[rr][c][k]);
+                            hc[rr][c][k] = hh[rr][k];
+                        }
+                if constexpr (RIGHT) {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) {
+                        ring_out[C0 * kWave * NPL + k] = hh[0][k];
+                        ring_out[(C0 + 1) * kWave * NPL + k] = hh[1][k];
+                    }
+                    signal_fence();
+                    lds_poke(&s_done[wave + 1], pub);
+                    // keep the vertical step below from being scheduled ahead
+                    // of the publish: it would sit on the carry's path
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (LEFT) lds_poke(&s_used[wave], pub);
+
+                // ---- vertical recurrence, sums over the lane's states and
+                // over the state groups, skip term, stores
+                float out[2][KO];
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    float part[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            hv[c][k] = __builtin_fmaf(av[rr][c][k], hv[c][k], hc[rr][c][k]);
+                            acc = __builtin_fmaf(Cv[rr][k][c], hv[c][k], acc);
+                        }
+                        part[c] = acc;
+                    }
+                    reduce_groups<4, G>(part, out[rr], g);
+                    out[rr][0] = __builtin_fmaf(Dd, xo[rr], out[rr][0]);
+                }
+                // pair stores of both rows (one swap of odd and even 16-lane
+                // rows each), under one mask
+                const long ro = static_cast<long>(i) * rs;
+                const bool second = !TAIL || i + 1 < H;
+                if constexpr (std::is_same<T, float>::value) {
+                    float lo[2], hi[2];
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(out[rr][0]),
+                                                                         __float_as_uint(out[rr][0]), false, false);
+                        lo[rr] = __uint_as_float(sw[0]);
+                        hi[rr] = __uint_as_float(sw[1]);
+                    }
+                    if (storer) {
+                        *reinterpret_cast<float2 *>(yv + ro) = make_float2(lo[0], hi[0]);
+                        if (second) *reinterpret_cast<float2 *>(yv + ro + rs) = make_float2(lo[1], hi[1]);
+                    }
+                } else {
+                    unsigned wv[2];
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const unsigned h = bf16_bits(out[rr][0]);
+                        const auto sw = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+                        wv[rr] = sw[0] | (sw[1] << 16);
+                    }
+                    if (storer) {
+                        *reinterpret_cast<unsigned *>(yv + ro) = wv[0];
+                        if (second) *reinterpret_cast<unsigned *>(yv + ro + rs) = wv[1];
+                    }
+                }
+                // the next step's rows in: every strip's share written
+                if (i + 2 < H && max(__builtin_amdgcn_readfirstlane(seen_next), skip) < need_next)
+                    wait_count(&s_arrive[JN], need_next);
+            };
+
+            // shares of the first kFastAhead steps, and the loads of the next two
+#pragma unroll
+            for (int s = 0; s < kFastAhead; ++s) {
+                load_step(stg[0], 2 * s);
+                write_step(stg[0], s);
+            }
+            load_step(stg[0], 2 * kFastAhead);
+            load_step(stg[1], 2 * kFastAhead + 2);
+            wait_count(&s_arrive[0], nact);  // the first step's rows
+            using I = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            int i0 = 0;
+            for (; i0 + 2 * kFastSteps <= H; i0 += 2 * kFastSteps) {
+                step(i0, std::integral_constant<int, 0>{}, I{});
+                step(i0, std::integral_constant<int, 1>{}, I{});
+                step(i0, std::integral_constant<int, 2>{}, I{});
+                step(i0, std::integral_constant<int, 3>{}, I{});
+                step(i0, std::integral_constant<int, 4>{}, I{});
+                step(i0, std::integral_constant<int, 5>{}, I{});
+                step(i0, std::integral_constant<int, 6>{}, I{});
+                step(i0, std::integral_constant<int, 7>{}, I{});
+            }
+            if (i0 < H) {
+                step(i0, std::integral_constant<int, 0>{}, I1{});
+                step(i0, std::integral_constant<int, 1>{}, I1{});
+                step(i0, std::integral_constant<int, 2>{}, I1{});
+                step(i0, std::integral_constant<int, 3>{}, I1{});
+                step(i0, std::integral_constant<int, 4>{}, I1{});
+                step(i0, std::integral_constant<int, 5>{}, I1{});
+                step(i0, std::integral_constant<int, 6>{}, I1{});
+                step(i0, std::integral_constant<int, 7>{}, I1{});
+            }
+        };
+        using N0 = std::integral_constant<int, 0>;
+        using N1 = std::integral_constant<int, 1>;
+        if (has_left) {
+            if (has_right) strip_rows(N1{}, N1{});
+            else strip_rows(N1{}, N0{});
+        } else {
+            if (has_right) strip_rows(N0{}, N1{});
+            else strip_rows(N0{}, N0{});
+        }
+        if (timed_out) report_timeout(p);
+    }
+
+    finish_launch(p, s_epoch, s_last);
+}
+
+// ---------------------------------------------------------------- host side
+
+// Launch for a plan of the shared-row-ring layout (8 state groups, 4-column
+// strips, rows of a multiple of 4 columns, chains across workgroups, at most
+// kFastStrips strips per workgroup) with 1 or 2 states a lane.
+template <typename T, int NPL>
+int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+             int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
+{
+    using Sh = FastShape<T, 8, NPL>;
+    pl.ring_rows = kFastCarryRows;
+    const int threads = kWave * (pl.s_local + 2);
+    // global ring depth: bounded (with back-pressure) only if the whole grid
+    // is co-resident, so that a producer never waits on a consumer that
+    // cannot run
+    pl.qg = H;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, 8, NPL>, threads, Sh::lds_bytes) ==
+        hipSuccess) {
+        const int qg = env_int("SSM2D_RING", 32);
+        if (static_cast<long>(per_cu) * device_cus(dev) >= pl.total_wg && qg >= 8 && qg < H) pl.qg = qg;
+    } else {
+        (void)hipGetLastError();
+    }
+    const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
+    const WsEntry *e = pl.fixed_ws;
+    if (e) {
+        if (need.gring_bytes > e->gring_bytes || need.zero_bytes > e->zero_bytes || need.cons_count > e->cons_count)
+            return SSM2D_ERR_TOO_LARGE;
+    } else {
+        WsEntry *w = nullptr;
+        const int st = get_ws(dev, stream, need.gring_bytes, need.zero_bytes, need.cons_count, &w);
+        if (st != SSM2D_OK) return st;
+        e = w;
+    }
+    const Params prm = make_params(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, *e);
+    scan2d_fast_kernel<T, 8, NPL><<<dim3(pl.total_wg), dim3(threads), Sh::lds_bytes, static_cast<hipStream_t>(stream)>>>(prm);
+    const hipError_t err = hipGetLastError();
+    return err == hipSuccess ? SSM2D_OK : hip_fail(err);
+}
+
+// The two-rows-per-step launch when the plan has its layout; kNoFastPath
+// otherwise (the general kernel then runs it).
+template <typename T>
+int dispatch_fast_impl(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
+                       int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream,
+                       int align)
+{
+    if (pl.mode != 0 || pl.G != 8 || pl.K != 4 || pl.coop_slots == 0 || pl.groups <= 1 ||
+        pl.s_local > kFastStrips || align != 4)
+        return kNoFastPath;
+    if (pl.npl == 1) return run_fast<T, 1>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    if (pl.npl == 2) return run_fast<T, 2>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    return kNoFastPath;
+}
+
+}  // namespace ssm2d_impl

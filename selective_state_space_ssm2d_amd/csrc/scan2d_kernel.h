@@ -523,6 +523,142 @@ constexpr int prefetch_rows(int K)
 }
 
 
+// End of a launch whose chains span workgroups: the last workgroup to
+// finish resets the tickets and advances the tag epoch for the next launch.
+// When the epoch wraps, the next launch's tags repeat those of a launch 65535
+// launches back, whose words may still sit in slots nobody has rewritten
+// since (another shape lays the ring out differently): every ring and
+// consumer word is cleared first (zero never matches a tag).
+__device__ __forceinline__ void finish_launch(const Params &p, const unsigned int s_epoch, int &s_last)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned int old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old + 1 == static_cast<unsigned int>(p.total_wg)) ? 1 : 0;
+        if (s_last) {
+            __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    if (s_last) {
+        const unsigned int next = s_epoch % kEpochs;  // stored value of the next launch
+        if (next == 0) {
+            for (long k = threadIdx.x; k < p.gring_words; k += blockDim.x) st_relaxed(p.gring + k, 0ull);
+            for (long k = threadIdx.x; k < p.cons_words; k += blockDim.x) st_relaxed(p.cons + k, 0ull);
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(p.epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Courier waves of a workgroup whose chain spans workgroups: wave s_local
+// brings the left workgroup's carries into LDS ring 0; wave s_local + 1 sends
+// LDS ring s_local to the right workgroup. They are separate waves so that
+// waiting for loads never also waits for the write-through of stores (one
+// counter tracks both). Carries between workgroups are tagged 64-bit words
+// (epoch << 16 | row, value) in the global ring, written and polled with
+// relaxed device-scope atomics; s_done / s_used are the LDS rings' published
+// and consumed row counts.
+template <int NPL>
+__device__ __forceinline__ void courier_wave(const Params &p, const int wave, const int lane, const int chain, const int grp,
+                             float *lring, int *s_done, int *s_used, const unsigned int s_epoch, const long ring_floats,
+                             const int RM)
+{
+    const int H = p.H;
+    const long nb_per_chain = p.groups - 1;
+    const long gstride = static_cast<long>(p.qg) * NPL * kWave;
+    const unsigned int etag = s_epoch << 16;
+    const unsigned long long ctag = static_cast<unsigned long long>(s_epoch) << 32;
+    long idle = 0;
+    bool timed_out = false;
+    if (wave == p.s_local && grp > 0) {
+        const long bound_in = chain * nb_per_chain + (grp - 1);
+        const unsigned long long *gin = p.gring + bound_in * gstride + lane;
+        float *ring0 = lring;
+        int in_next = 0;
+        while (in_next < H) {
+            const int used0 = lds_counter(&s_used[0]);
+            const int nb = min(min(kCourierBatch, H - in_next), used0 + p.ring_rows - in_next);
+            int v = 0;
+            if (nb > 0) {
+                unsigned long long w[kCourierBatch][NPL];
+#pragma unroll
+                for (int r = 0; r < kCourierBatch; ++r)
+                    if (r < nb)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k)
+                            w[r][k] = ld_relaxed(gin + (static_cast<long>((in_next + r) % p.qg) * NPL + k) * kWave);
+#pragma unroll
+                for (int r = 0; r < kCourierBatch; ++r) {
+                    if (r < nb && v == r) {
+                        const unsigned long long want = static_cast<unsigned long long>(etag | static_cast<unsigned>(in_next + r)) << 32;
+                        bool ok = true;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) ok = ok && ((w[r][k] & 0xffffffff00000000ull) == want);
+                        if (__all(ok)) {
+                            float *dst = ring0 + (static_cast<long>((in_next + r) & RM) * kWave + lane) * NPL;
+#pragma unroll
+                            for (int k = 0; k < NPL; ++k) dst[k] = __uint_as_float(static_cast<unsigned>(w[r][k] & 0xffffffffu));
+                            v = r + 1;
+                        }
+                    }
+                }
+            }
+            if (v > 0) {
+                in_next += v;
+                lds_publish(&s_done[0], in_next);
+                if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
+                idle = 0;
+            } else {
+                if (++idle > p.spin_limit) { timed_out = true; break; }
+                sleep_a_bit();
+            }
+        }
+        if (timed_out) {
+            // Let wave 0 run to the end on NaN carries: every output it
+            // and the strips after it compute from here on is NaN.
+            for (long k = lane; k < static_cast<long>(p.ring_rows) * kWave * NPL; k += kWave) ring0[k] = quiet_nan();
+            lds_publish(&s_done[0], H);
+        }
+    } else if (wave == p.s_local + 1 && (grp + 1) * p.s_local < p.nstrips) {
+        const long bound_out = chain * nb_per_chain + grp;
+        unsigned long long *gout = p.gring + bound_out * gstride + lane;
+        const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
+        int out_next = 0, cons_seen = 0;
+        while (out_next < H) {
+            const int avail = lds_counter(&s_done[p.s_local]);
+            int nb = min(kCourierBatch, avail - out_next);
+            if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
+                const unsigned long long c = ld_relaxed(p.cons + bound_out);
+                if ((c & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(c & 0xffffffffu);
+                nb = min(nb, cons_seen + p.qg - out_next);
+            }
+            if (nb > 0) {
+#pragma unroll
+                for (int r = 0; r < kCourierBatch; ++r) {
+                    if (r < nb) {
+                        const int row = out_next + r;
+                        const float *src_c = ringS + (static_cast<long>(row & RM) * kWave + lane) * NPL;
+                        const unsigned long long tagw = static_cast<unsigned long long>(etag | static_cast<unsigned>(row)) << 32;
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k)
+                            st_relaxed(gout + (static_cast<long>(row % p.qg) * NPL + k) * kWave,
+                                       tagw | __float_as_uint(src_c[k]));
+                    }
+                }
+                out_next += nb;
+                lds_publish(&s_used[p.s_local], out_next);
+                idle = 0;
+            } else {
+                if (++idle > p.spin_limit) { timed_out = true; break; }
+                sleep_a_bit();
+            }
+        }
+        if (timed_out) lds_publish(&s_used[p.s_local], H);  // let the last wave run to the end
+    }
+    if (timed_out) report_timeout(p);
+}
+
 template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
 __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd_kernel(Params p)
 {
@@ -601,103 +737,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     float *lring = reinterpret_cast<float *>(smem + in_bytes);
 
     if (wave >= p.s_local) {
-        // ---------------- couriers between the global ring and the LDS rings.
-        // Wave s_local brings the left workgroup's carries into LDS ring 0;
-        // wave s_local + 1 sends LDS ring s_local to the right workgroup. They
-        // are separate waves so that waiting for loads never also waits for
-        // the write-through of stores (one counter tracks both).
-        const long nb_per_chain = p.groups - 1;
-        const long gstride = static_cast<long>(p.qg) * NPL * kWave;
-        const unsigned int etag = s_epoch << 16;
-        const unsigned long long ctag = static_cast<unsigned long long>(s_epoch) << 32;
-        long idle = 0;
-        bool timed_out = false;
-        if (wave == p.s_local && grp > 0) {
-            const long bound_in = chain * nb_per_chain + (grp - 1);
-            const unsigned long long *gin = p.gring + bound_in * gstride + lane;
-            float *ring0 = lring;
-            int in_next = 0;
-            while (in_next < H) {
-                const int used0 = lds_counter(&s_used[0]);
-                const int nb = min(min(kCourierBatch, H - in_next), used0 + p.ring_rows - in_next);
-                int v = 0;
-                if (nb > 0) {
-                    unsigned long long w[kCourierBatch][NPL];
-#pragma unroll
-                    for (int r = 0; r < kCourierBatch; ++r)
-                        if (r < nb)
-#pragma unroll
-                            for (int k = 0; k < NPL; ++k)
-                                w[r][k] = ld_relaxed(gin + (static_cast<long>((in_next + r) % p.qg) * NPL + k) * kWave);
-#pragma unroll
-                    for (int r = 0; r < kCourierBatch; ++r) {
-                        if (r < nb && v == r) {
-                            const unsigned long long want = static_cast<unsigned long long>(etag | static_cast<unsigned>(in_next + r)) << 32;
-                            bool ok = true;
-#pragma unroll
-                            for (int k = 0; k < NPL; ++k) ok = ok && ((w[r][k] & 0xffffffff00000000ull) == want);
-                            if (__all(ok)) {
-                                float *dst = ring0 + (static_cast<long>((in_next + r) & RM) * kWave + lane) * NPL;
-#pragma unroll
-                                for (int k = 0; k < NPL; ++k) dst[k] = __uint_as_float(static_cast<unsigned>(w[r][k] & 0xffffffffu));
-                                v = r + 1;
-                            }
-                        }
-                    }
-                }
-                if (v > 0) {
-                    in_next += v;
-                    lds_publish(&s_done[0], in_next);
-                    if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
-                    idle = 0;
-                } else {
-                    if (++idle > p.spin_limit) { timed_out = true; break; }
-                    sleep_a_bit();
-                }
-            }
-            if (timed_out) {
-                // Let wave 0 run to the end on NaN carries: every output it
-                // and the strips after it compute from here on is NaN.
-                for (long k = lane; k < static_cast<long>(p.ring_rows) * kWave * NPL; k += kWave) ring0[k] = quiet_nan();
-                lds_publish(&s_done[0], H);
-            }
-        } else if (wave == p.s_local + 1 && (grp + 1) * p.s_local < p.nstrips) {
-            const long bound_out = chain * nb_per_chain + grp;
-            unsigned long long *gout = p.gring + bound_out * gstride + lane;
-            const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
-            int out_next = 0, cons_seen = 0;
-            while (out_next < H) {
-                const int avail = lds_counter(&s_done[p.s_local]);
-                int nb = min(kCourierBatch, avail - out_next);
-                if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
-                    const unsigned long long c = ld_relaxed(p.cons + bound_out);
-                    if ((c & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(c & 0xffffffffu);
-                    nb = min(nb, cons_seen + p.qg - out_next);
-                }
-                if (nb > 0) {
-#pragma unroll
-                    for (int r = 0; r < kCourierBatch; ++r) {
-                        if (r < nb) {
-                            const int row = out_next + r;
-                            const float *src_c = ringS + (static_cast<long>(row & RM) * kWave + lane) * NPL;
-                            const unsigned long long tagw = static_cast<unsigned long long>(etag | static_cast<unsigned>(row)) << 32;
-#pragma unroll
-                            for (int k = 0; k < NPL; ++k)
-                                st_relaxed(gout + (static_cast<long>(row % p.qg) * NPL + k) * kWave,
-                                           tagw | __float_as_uint(src_c[k]));
-                        }
-                    }
-                    out_next += nb;
-                    lds_publish(&s_used[p.s_local], out_next);
-                    idle = 0;
-                } else {
-                    if (++idle > p.spin_limit) { timed_out = true; break; }
-                    sleep_a_bit();
-                }
-            }
-            if (timed_out) lds_publish(&s_used[p.s_local], H);  // let the last wave run to the end
-        }
-        if (timed_out) report_timeout(p);
+        courier_wave<NPL>(p, wave, lane, chain, grp, lring, s_done, s_used, s_epoch, ring_floats, RM);
     } else if (grp * p.s_local + wave < p.nstrips) {
         // ---------------- compute wave: one strip
         const int strip = grp * p.s_local + wave;
@@ -1482,32 +1522,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         if (timed_out) report_timeout(p);
     }
 
-    if (p.use_ticket) {
-        // The last workgroup to finish resets the tickets and advances the
-        // tag epoch for the next launch. When the epoch wraps, the next
-        // launch's tags repeat those of a launch 65535 launches back, whose
-        // words may still sit in slots nobody has rewritten since (another
-        // shape lays the ring out differently): every ring and consumer word
-        // is cleared first (zero never matches a tag).
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            unsigned int old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (old + 1 == static_cast<unsigned int>(p.total_wg)) ? 1 : 0;
-            if (s_last) {
-                __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-        if (s_last) {
-            const unsigned int next = s_epoch % kEpochs;  // stored value of the next launch
-            if (next == 0) {
-                for (long k = threadIdx.x; k < p.gring_words; k += blockDim.x) st_relaxed(p.gring + k, 0ull);
-                for (long k = threadIdx.x; k < p.cons_words; k += blockDim.x) st_relaxed(p.cons + k, 0ull);
-            }
-            if (threadIdx.x == 0) __hip_atomic_store(p.epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (p.use_ticket) finish_launch(p, s_epoch, s_last);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1640,9 +1655,10 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
                                                         stream);
 }
 
-template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
-int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
-                int d_inner, int d_state, int H, int W, const Plan &pl, const WsEntry &ws, void *stream)
+// Kernel parameters of a plan and its workspace (shared by the kernels).
+inline Params make_params(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                          const float *D, void *y, int batch, int d_inner, int d_state, int H, int W, const Plan &pl,
+                          const WsEntry &ws)
 {
     const WsEntry *e = &ws;
     Params prm{};
@@ -1685,6 +1701,14 @@ int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T 
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;
     prm.spin_limit = g_spin_limit > 0 ? g_spin_limit : (1ll << 22);
+    return prm;
+}
+
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
+int launch_plan(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+                int d_inner, int d_state, int H, int W, const Plan &pl, const WsEntry &ws, void *stream)
+{
+    const Params prm = make_params(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, ws);
     const size_t lds = lds_bytes<T, K, NPL, G, MODE>(pl);
     scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE><<<dim3(pl.total_wg), dim3(block_threads(pl)), lds,
                                    static_cast<hipStream_t>(stream)>>>(prm);
@@ -1764,6 +1788,11 @@ SSM2D_DISPATCH_DECL(float, dispatch_g4)
 SSM2D_DISPATCH_DECL(float, dispatch_g8)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g4)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
+// The plain forward of tall maps, two rows per step (scan2d_fast.h), or
+// kNoFastPath when the plan is not of its layout.
+constexpr int kNoFastPath = -1;
+SSM2D_DISPATCH_DECL(float, dispatch_fast)
+SSM2D_DISPATCH_DECL(uint16_t, dispatch_fast)
 // The other modes (8 state groups; 4-column strips with per-wave packets or
 // the shared row ring, align 2 served by the align-1 kernels; 8-column strips
 // for the forward modes on rows of a multiple of 4 columns), one translation

@@ -1,0 +1,79 @@
+"""GPU parity of the two-rows-per-step forward (the plain scan of tall maps
+whose chains span workgroups: 8 state groups, 4-column strips, the shared
+input row ring) against the fp64 oracle, on the shapes that exercise its
+edges: the last, partial block of 16 rows and an odd last row; a last
+workgroup holding fewer strips; 1 and 2 states a lane with padded states and
+channels; several batch entries; bottom-to-top rows; bf16. Each case also
+runs the general kernel (SSM2D_FAST=0) on the same inputs.
+
+Bars: 1e-4 (1 + |y_ref|) for fp32 inputs, 2e-2 (1 + |y_ref|) for bf16.
+"""
+import numpy as np
+import pytest
+
+import selective_state_space_ssm2d_amd as pkg
+from selective_state_space_ssm2d_amd.inputs import make_random_inputs
+from test_gpu_parity import KEYS, _say, _setup, as_f64, check, ref_of, to_dev  # noqa: F401 (_setup: fixture)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# batch, d_inner, d_state, H, W (W % 4 == 0, H >= 128: the shared row ring)
+FAST_SHAPES = [
+    (1, 16, 16, 160, 96),    # 24 strips: whole blocks of 16 rows
+    (1, 8, 8, 200, 36),      # 1 state a lane; 9 strips (a last workgroup of 1 strip with 8 a group)
+    (1, 8, 16, 131, 64),     # odd H: a tail block ending on a single row
+    (2, 12, 12, 144, 100),   # padded channels (12 of 16) and states (12 of 16), two batch entries
+    (1, 24, 16, 129, 200),   # 50 strips, 2 + 1 chains of channels, H = 8 * 16 + 1
+    (1, 8, 5, 150, 124),     # 5 states (1 a lane, 3 padded), 31 strips
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("flip_h", [False, True])
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=str)
+def test_fast_path(shape, flip_h, dtype, monkeypatch):
+    _say(f"fast path {shape} flip_h={flip_h} {dtype}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 200 + flip_h, dtype=dtype)
+    args = to_dev(t, dtype)
+    ref = ref_of(t) if not flip_h else None
+    if flip_h:
+        import oracle
+
+        ref = oracle.fwd(*(t[k] for k in KEYS), flip_h=True)
+    y = pkg.scan_fwd_ex(*args, flip_h=flip_h)
+    pkg.sync_check()
+    check(as_f64(y), ref, dtype, f"fast {shape} flip_h={flip_h}")
+    monkeypatch.setenv("SSM2D_FAST", "0")
+    yg = pkg.scan_fwd_ex(*args, flip_h=flip_h)
+    pkg.sync_check()
+    check(as_f64(yg), ref, dtype, f"general {shape} flip_h={flip_h}")
+
+
+@pytest.mark.parametrize("waves", ["3", "5", "8"])
+def test_fast_path_workgroup_sizes(waves, monkeypatch):
+    """Strips per workgroup from 3 to 8 (more couriers, partial last groups)."""
+    monkeypatch.setenv("SSM2D_WAVES", waves)
+    shape = (1, 16, 16, 140, 120)
+    _say(f"fast path waves={waves} {shape}")
+    t = make_random_inputs(*shape, seed=230)
+    y = pkg.scan_fwd(*to_dev(t, "f32"))
+    pkg.sync_check()
+    check(as_f64(y), ref_of(t), "f32", f"fast waves={waves}")
+
+
+def test_fast_path_deterministic_and_guarded():
+    """Bitwise equal across runs; cells outside y untouched (guard bands)."""
+    shape = (1, 16, 16, 136, 64)
+    t = make_random_inputs(*shape, seed=231)
+    args = to_dev(t, "f32")
+    n = int(np.prod(t["x"].shape))
+    buf = torch.full((n + 2048,), 7.0, device="cuda")
+    y = buf[1024:1024 + n].view(t["x"].shape)
+    pkg.scan_fwd(*args, y=y)
+    y1 = y.clone()
+    pkg.scan_fwd(*args, y=y)
+    pkg.sync_check()
+    assert torch.equal(y, y1)
+    assert bool((buf[:1024] == 7.0).all()) and bool((buf[1024 + n:] == 7.0).all())
+    check(as_f64(y), ref_of(t), "f32", "fast guarded")
