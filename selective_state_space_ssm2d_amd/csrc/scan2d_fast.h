@@ -49,11 +49,15 @@ template <typename T> struct FastChunkOf;
 template <> struct FastChunkOf<float> { using type = float __attribute__((ext_vector_type(4))); };
 template <> struct FastChunkOf<uint16_t> { using type = unsigned __attribute__((ext_vector_type(2))); };
 
-template <typename T, int G, int NPL>
+// LDS a launch may take (with the kernel's few static words).
+constexpr size_t kFastLdsMax = 160 * 1024 - 256;
+
+template <typename T, int G, int NPL, int K>
 struct FastShape {
     using Chunk = typename FastChunkOf<T>::type;
     static constexpr int CPW = kWave / G;                       // channels per wave
-    static constexpr int NCHUNK = 2 * CPW + 2 * G * NPL;        // packet rows: x, delta, B, C
+    static constexpr int CPR = K / 4;                           // chunks per packet row of a strip
+    static constexpr int NCHUNK = (2 * CPW + 2 * G * NPL) * CPR;  // packet rows: x, delta, B, C
     static constexpr int PASSES = (NCHUNK + kWave - 1) / kWave;  // chunks a lane loads per row
     static constexpr int PST = NCHUNK + 1;                      // chunks per strip packet (one pad chunk)
     static constexpr int ROWC = kFastStrips * PST;              // chunks per ring row
@@ -62,15 +66,19 @@ struct FastShape {
     static constexpr size_t lds_bytes = ring_bytes + carry_bytes;
 };
 
-template <typename T, int G, int NPL>
-__global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(Params p)
+// CHAINED: chains cut into several workgroups (tickets, couriers); else one
+// workgroup holds a whole chain.
+template <typename T, int G, int NPL, int K, bool CHAINED>
+__global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void scan2d_fast_kernel(Params p)
 {
-    using Sh = FastShape<T, G, NPL>;
+    static_assert(K == 4 || K == 8, "4- or 8-column strips");
+    using Sh = FastShape<T, G, NPL, K>;
     using Chunk = typename Sh::Chunk;
-    constexpr int CPW = Sh::CPW, NCHUNK = Sh::NCHUNK, PASSES = Sh::PASSES, PST = Sh::PST, ROWC = Sh::ROWC;
+    constexpr int CPW = Sh::CPW, CPR = Sh::CPR, NCHUNK = Sh::NCHUNK, PASSES = Sh::PASSES, PST = Sh::PST,
+                  ROWC = Sh::ROWC;
     constexpr int SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
     constexpr int CR = kFastCarryRows;
-    constexpr int KO = 4 / G > 0 ? 4 / G : 1;  // finished cells per lane and row (1)
+    constexpr int KO = K / G > 0 ? K / G : 1;  // finished cells per lane and row
 
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_done[kFastStrips + 1];   // rows published into LDS carry ring w
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
-    if (threadIdx.x == 0) {
+    if (CHAINED && threadIdx.x == 0) {
         s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_epoch = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % kEpochs + 1;
     }
@@ -92,9 +100,19 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
     if (threadIdx.x < kFastSteps) s_arrive[threadIdx.x] = 0;
     __syncthreads();
 
-    // Tickets put every producer workgroup before its consumer (a waiting
-    // workgroup's producer is resident or done).
-    const int wg = static_cast<int>(s_ticket);
+    // Chained: tickets put every producer workgroup before its consumer (a
+    // waiting workgroup's producer is resident or done). Otherwise workgroups
+    // are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of
+    // chains, so chains sharing a batch entry (and its B, C) share its L2.
+    int wg;
+    if constexpr (CHAINED) {
+        wg = static_cast<int>(s_ticket);
+    } else if (p.xcd_remap) {
+        const int per = p.total_wg / 8;
+        wg = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    } else {
+        wg = blockIdx.x;
+    }
     const int chain = wg % p.n_chains;
     const int grp = wg / p.n_chains;
     const int b = chain / p.n_dblk;
@@ -104,11 +122,13 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
     float *lring = reinterpret_cast<float *>(smem + Sh::ring_bytes);
 
     if (wave >= p.s_local) {
-        courier_wave<NPL>(p, wave, lane, chain, grp, lring, s_done, s_used, s_epoch, ring_floats, CR - 1);
+        if constexpr (CHAINED)
+            courier_wave<NPL>(p, wave, lane, chain, grp, lring, s_done, s_used, s_epoch, ring_floats, CR - 1);
     } else if (grp * p.s_local + wave < p.nstrips) {
-        // ---------------- compute wave: one strip of 4 columns
+        // ---------------- compute wave: one strip of K columns
         const int strip = grp * p.s_local + wave;
-        const int j0 = strip * 4;
+        const int j0 = strip * K;
+        const int valid = min(K, W - j0);  // columns of the strip inside the map
         const int nact = min(p.s_local, p.nstrips - grp * p.s_local);  // strips of this workgroup
         const int g = lane / CPW;
         const int dl = lane % CPW;
@@ -125,8 +145,8 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
         // [w NCHUNK, (w + 1) NCHUNK) of a row taken in column order (packet row
         // r of strips 0 .. nact-1, then packet row r + 1, ...), so a load
         // instruction reads whole cache lines, and writes each chunk into its
-        // strip's packet. Padding lanes read the zero page into their own pad
-        // chunk.
+        // strip's packet. Padding lanes, and chunks past the row's end (the
+        // second half of a last 8-column strip), read the zero page.
         const T *src[PASSES];
         int wdst[PASSES];
 #pragma unroll
@@ -137,10 +157,13 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
             long col = 0;
             if (c < NCHUNK) {
                 const int cw = wave * NCHUNK + c;
-                const int r = cw / nact, sj = cw % nact;
-                dst = sj * PST + r;
-                col = static_cast<long>(grp * p.s_local + sj) * 4;
-                if (r < SEG_DT) {
+                const int r = cw / (nact * CPR), rem = cw % (nact * CPR);
+                const int sj = rem / CPR, q = rem % CPR;
+                dst = sj * PST + r * CPR + q;
+                col = static_cast<long>(grp * p.s_local + sj) * K + 4 * q;
+                if (col + 4 > W) {
+                    // past the row's end: zeros
+                } else if (r < SEG_DT) {
                     const int dd = dblk * CPW + r;
                     if (dd < p.d_inner) base = static_cast<const T *>(p.x) + (static_cast<long>(b) * p.d_inner + dd) * HW;
                 } else if (r < SEG_B) {
@@ -170,23 +193,28 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
         asm volatile("" ::"v"(Dd));
 
         // Operand offsets (elements) of this lane in a ring row.
-        const int off_x = (wave * PST + dl) * 4;
-        const int off_dt = (wave * PST + SEG_DT + dl) * 4;
+        const int off_x = (wave * PST + dl * CPR) * 4;
+        const int off_dt = (wave * PST + (SEG_DT + dl) * CPR) * 4;
         int off_b[NPL], off_c[NPL];
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
-            off_b[k] = (wave * PST + SEG_B + g * NPL + k) * 4;
-            off_c[k] = (wave * PST + SEG_C + g * NPL + k) * 4;
+            off_b[k] = (wave * PST + (SEG_B + g * NPL + k) * CPR) * 4;
+            off_c[k] = (wave * PST + (SEG_C + g * NPL + k) * CPR) * 4;
         }
-        // the finished cell of this lane after the sum over state groups, and
-        // the pair stores of a full strip (row r of the wave holds cell r; one
-        // swap of odd and even rows leaves cells 0, 1 in row 0 and 2, 3 in
-        // row 2, whose channel lanes store two cells each)
-        const int c_out = (4 >= G) ? g * KO : g / 2;
+        // The first finished cell of this lane after the sum over state
+        // groups (for G = 8 and K = 4 the two lanes of a pair hold the same
+        // cell). 4-column strips: pair stores (row r of the wave holds cell r;
+        // one swap of odd and even rows leaves cells 0, 1 in row 0 and 2, 3 in
+        // row 2, whose channel lanes store two cells each). 8-column strips:
+        // each lane stores its own KO cells.
+        const int c_out = (K >= G) ? g * KO : g / 2;
         const int off_xo = off_x + c_out;
-        const bool storer = ((lane & ~32) < CPW) && d_ok;
-        T *yv = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (storer ? d : 0)) * HW + row0 + j0 +
-                (((lane >> 5) & 1) ? 2 : 0);
+        const bool storer = K == 4 ? (((lane & ~32) < CPW) && d_ok) : d_ok;
+        T *yv = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (d_ok ? d : 0)) * HW + row0 + j0 +
+                (K == 4 ? (((lane >> 5) & 1) ? 2 : 0) : c_out);
+        bool cell_ok[KO];
+#pragma unroll
+        for (int c = 0; c < KO; ++c) cell_ok[c] = d_ok && c_out + c < valid;
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -216,9 +244,9 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
             signal_fence();
         };
 
-        float hv[4][NPL];
+        float hv[K][NPL];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < K; ++c)
 #pragma unroll
             for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
 
@@ -275,20 +303,23 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
                 // step's, confirmed at the end of this one
                 const T *r0 = ring + static_cast<long>(2 * J) * ROWC * 4;
                 const T *r1 = r0 + static_cast<long>(ROWC) * 4;
-                float xv[2][4], dv[2][4], Bv[2][NPL][4], Cv[2][NPL][4], xo[2];
-                read_packet<4>(r0, off_x, xv[0]);
-                read_packet<4>(r0, off_dt, dv[0]);
-                read_packet<4>(r1, off_x, xv[1]);
-                read_packet<4>(r1, off_dt, dv[1]);
+                float xv[2][K], dv[2][K], Bv[2][NPL][K], Cv[2][NPL][K], xo[2][KO];
+                read_packet<K>(r0, off_x, xv[0]);
+                read_packet<K>(r0, off_dt, dv[0]);
+                read_packet<K>(r1, off_x, xv[1]);
+                read_packet<K>(r1, off_dt, dv[1]);
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) {
-                    read_packet<4>(r0, off_b[k], Bv[0][k]);
-                    read_packet<4>(r1, off_b[k], Bv[1][k]);
-                    read_packet<4>(r0, off_c[k], Cv[0][k]);
-                    read_packet<4>(r1, off_c[k], Cv[1][k]);
+                    read_packet<K>(r0, off_b[k], Bv[0][k]);
+                    read_packet<K>(r1, off_b[k], Bv[1][k]);
+                    read_packet<K>(r0, off_c[k], Cv[0][k]);
+                    read_packet<K>(r1, off_c[k], Cv[1][k]);
                 }
-                xo[0] = elem_value(r0[off_xo]);
-                xo[1] = elem_value(r1[off_xo]);
+#pragma unroll
+                for (int c = 0; c < KO; ++c) {
+                    xo[0][c] = elem_value(r0[off_xo + c]);
+                    xo[1][c] = elem_value(r1[off_xo + c]);
+                }
                 constexpr int JN = (J + 1) % kFastSteps;
                 const int need_next = nact * (((i + 2) >> 4) + 1);
                 const int seen_next = lds_peek(&s_arrive[JN]);
@@ -310,11 +341,11 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
                 }
 
                 // ---- carry-independent work of both rows
-                float av[2][4][NPL], bx[2][4][NPL];
+                float av[2][K][NPL], bx[2][K][NPL];
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
+                    for (int c = 0; c < K; ++c) {
                         const float dx = dv[rr][c] * xv[rr][c];
 #pragma unroll
                         for (int k = 0; k < NPL; ++k) {
@@ -327,7 +358,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < K; ++c)
 #pragma unroll
                         for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(av[rr][c][k]), "+v"(bx[rr][c][k]));
 
@@ -375,9 +406,9 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
                 }
 
                 // ---- the two horizontal chains, then hand both carries on
-                float hc[2][4][NPL];
+                float hc[2][K][NPL];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < K; ++c)
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
@@ -404,9 +435,9 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
                 float out[2][KO];
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
-                    float part[4];
+                    float part[K];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
+                    for (int c = 0; c < K; ++c) {
                         float acc = 0.0f;
 #pragma unroll
                         for (int k = 0; k < NPL; ++k) {
@@ -415,14 +446,23 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
                         }
                         part[c] = acc;
                     }
-                    reduce_groups<4, G>(part, out[rr], g);
-                    out[rr][0] = __builtin_fmaf(Dd, xo[rr], out[rr][0]);
+                    reduce_groups<K, G>(part, out[rr], g);
+#pragma unroll
+                    for (int c = 0; c < KO; ++c) out[rr][c] = __builtin_fmaf(Dd, xo[rr][c], out[rr][c]);
                 }
                 // pair stores of both rows (one swap of odd and even 16-lane
                 // rows each), under one mask
                 const long ro = static_cast<long>(i) * rs;
                 const bool second = !TAIL || i + 1 < H;
-                if constexpr (std::is_same<T, float>::value) {
+                if constexpr (K == 8) {
+                    // each lane its own cells
+#pragma unroll
+                    for (int c = 0; c < KO; ++c)
+                        if (cell_ok[c]) {
+                            store_elem(yv + ro + c, out[0][c]);
+                            if (second) store_elem(yv + ro + rs + c, out[1][c]);
+                        }
+                } else if constexpr (std::is_same<T, float>::value) {
                     float lo[2], hi[2];
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr) {
@@ -498,7 +538,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
         if (timed_out) report_timeout(p);
     }
 
-    finish_launch(p, s_epoch, s_last);
+    if constexpr (CHAINED) finish_launch(p, s_epoch, s_last);
 }
 
 // ---------------------------------------------------------------- host side
@@ -506,24 +546,26 @@ __global__ __launch_bounds__(kWave * (kFastStrips + 2)) void scan2d_fast_kernel(
 // Launch for a plan of the shared-row-ring layout (8 state groups, 4-column
 // strips, rows of a multiple of 4 columns, chains across workgroups, at most
 // kFastStrips strips per workgroup) with 1 or 2 states a lane.
-template <typename T, int NPL>
+template <typename T, int G, int NPL, int K, bool CHAINED>
 int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
              int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
 {
-    using Sh = FastShape<T, 8, NPL>;
+    using Sh = FastShape<T, G, NPL, K>;
     pl.ring_rows = kFastCarryRows;
-    const int threads = kWave * (pl.s_local + 2);
-    // global ring depth: bounded (with back-pressure) only if the whole grid
-    // is co-resident, so that a producer never waits on a consumer that
-    // cannot run
+    const int threads = kWave * (pl.s_local + (CHAINED ? 2 : 0));
     pl.qg = H;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, 8, NPL>, threads, Sh::lds_bytes) ==
-        hipSuccess) {
-        const int qg = env_int("SSM2D_RING", 32);
-        if (static_cast<long>(per_cu) * device_cus(dev) >= pl.total_wg && qg >= 8 && qg < H) pl.qg = qg;
-    } else {
-        (void)hipGetLastError();
+    if constexpr (CHAINED) {
+        // global ring depth: bounded (with back-pressure) only if the whole
+        // grid is co-resident, so that a producer never waits on a consumer
+        // that cannot run
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, G, NPL, K, true>, threads,
+                                                         Sh::lds_bytes) == hipSuccess) {
+            const int qg = env_int("SSM2D_RING", 32);
+            if (static_cast<long>(per_cu) * device_cus(dev) >= pl.total_wg && qg >= 8 && qg < H) pl.qg = qg;
+        } else {
+            (void)hipGetLastError();
+        }
     }
     const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
     const WsEntry *e = pl.fixed_ws;
@@ -537,23 +579,50 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
         e = w;
     }
     const Params prm = make_params(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, *e);
-    scan2d_fast_kernel<T, 8, NPL><<<dim3(pl.total_wg), dim3(threads), Sh::lds_bytes, static_cast<hipStream_t>(stream)>>>(prm);
+    scan2d_fast_kernel<T, G, NPL, K, CHAINED>
+        <<<dim3(pl.total_wg), dim3(threads), Sh::lds_bytes, static_cast<hipStream_t>(stream)>>>(prm);
     const hipError_t err = hipGetLastError();
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
 }
 
-// The two-rows-per-step launch when the plan has its layout; kNoFastPath
-// otherwise (the general kernel then runs it).
+template <typename T, int G, int NPL, int K>
+int run_fast_layout(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
+                    int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream)
+{
+    if constexpr (FastShape<T, G, NPL, K>::lds_bytes > kFastLdsMax) {
+        return kNoFastPath;  // the input ring of this layout does not fit
+    } else {
+        // (8-column strips: chains of one workgroup only; the planner picks
+        // them only there, and with couriers their registers would spill)
+        if constexpr (K == 4) {
+            if (pl.groups > 1)
+                return run_fast<T, G, NPL, K, true>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev,
+                                                    stream);
+        } else {
+            if (pl.groups > 1) return kNoFastPath;
+        }
+        return run_fast<T, G, NPL, K, false>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    }
+}
+
+// The two-rows-per-step launch when the plan has one of its layouts (4 or 8
+// state groups with 1 or 2 states a lane, 4- or 8-column strips, rows of a
+// multiple of 4 columns, at most kFastStrips strips a workgroup, an input
+// ring that fits the LDS); kNoFastPath otherwise (the general kernel then
+// runs it).
 template <typename T>
 int dispatch_fast_impl(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
                        int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream,
                        int align)
 {
-    if (pl.mode != 0 || pl.G != 8 || pl.K != 4 || pl.coop_slots == 0 || pl.groups <= 1 ||
-        pl.s_local > kFastStrips || align != 4)
-        return kNoFastPath;
-    if (pl.npl == 1) return run_fast<T, 1>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
-    if (pl.npl == 2) return run_fast<T, 2>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    // Plain forward only: no direction or order bits, no carried states.
+    if (pl.mode != 0 || pl.h_init || pl.h_last || pl.s_local > kFastStrips || align != 4) return kNoFastPath;
+#define SSM2D_FAST_CASE(GG, NN, KK)                         \
+    if (pl.G == GG && pl.npl == NN && pl.K == KK)           \
+        return run_fast_layout<T, GG, NN, KK>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+    SSM2D_FAST_CASE(8, 1, 4) SSM2D_FAST_CASE(8, 2, 4) SSM2D_FAST_CASE(8, 1, 8) SSM2D_FAST_CASE(8, 2, 8)
+    SSM2D_FAST_CASE(4, 1, 4) SSM2D_FAST_CASE(4, 2, 4)
+#undef SSM2D_FAST_CASE
     return kNoFastPath;
 }
 

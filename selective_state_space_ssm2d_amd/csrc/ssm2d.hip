@@ -540,8 +540,8 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     choose_coop<T>(pl, H, align);
 #define SSM2D_ARGS x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align
     constexpr int FW = kModeFlipW, VF = kModeVFirst, AC = kModeAccumulate;
-    if (mode == 0 && pl.coop_slots > 0 && env_int("SSM2D_FAST", 1)) {
-        // the plain forward of a tall map: two rows per step
+    if (mode == 0 && env_int("SSM2D_FAST", 1)) {
+        // the plain forward: two rows per step, where the plan's layout has that kernel
         const int st = dispatch_fast(SSM2D_ARGS);
         if (st != kNoFastPath) return st;
     }

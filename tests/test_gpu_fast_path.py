@@ -1,10 +1,11 @@
-"""GPU parity of the two-rows-per-step forward (the plain scan of tall maps
-whose chains span workgroups: 8 state groups, 4-column strips, the shared
-input row ring) against the fp64 oracle, on the shapes that exercise its
-edges: the last, partial block of 16 rows and an odd last row; a last
-workgroup holding fewer strips; 1 and 2 states a lane with padded states and
-channels; several batch entries; bottom-to-top rows; bf16. Each case also
-runs the general kernel (SSM2D_FAST=0) on the same inputs.
+"""GPU parity of the two-rows-per-step forward (the plain scan with the
+workgroup's shared input row ring: 4 or 8 state groups with 1 or 2 states a
+lane, 4-column strips with chains in one or several workgroups, 8-column
+strips in one workgroup) against the fp64 oracle, on the shapes that exercise
+its edges: the last, partial block of 16 rows and an odd last row; a last
+workgroup holding fewer strips; a last 8-column strip half full; padded
+states and channels; several batch entries; bottom-to-top rows; bf16. Each
+case also runs the general kernel (SSM2D_FAST=0) on the same inputs.
 
 Bars: 1e-4 (1 + |y_ref|) for fp32 inputs, 2e-2 (1 + |y_ref|) for bf16.
 """
@@ -77,3 +78,34 @@ def test_fast_path_deterministic_and_guarded():
     assert torch.equal(y, y1)
     assert bool((buf[:1024] == 7.0).all()) and bool((buf[1024 + n:] == 7.0).all())
     check(as_f64(y), ref_of(t), "f32", "fast guarded")
+
+
+# Layouts the planner picks for many chains (one workgroup a chain):
+# 8-column strips (VMamba-like rows of 56 and 60 columns), 4-column strips,
+# 4 state groups with 1 and 2 states a lane; and a short map whose chains
+# span workgroups.
+LAYOUT_SHAPES = [
+    ((32, 64, 16, 20, 56), "bf16"),   # 8 groups, 2 states a lane, 8-column strips
+    ((32, 64, 16, 19, 60), "bf16"),   # the same, last strip half full, odd H
+    ((32, 64, 8, 18, 56), "f32"),     # 8-column strips, 1 state a lane, fp32
+    ((32, 64, 16, 21, 32), "f32"),    # 4-column strips in one workgroup
+    ((16, 256, 4, 12, 24), "f32"),    # 4 groups, 1 state a lane
+    ((32, 256, 8, 10, 24), "bf16"),   # 4 groups, 2 states a lane
+    ((1, 128, 16, 64, 80), "f32"),    # short map, chains across workgroups
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_SHAPES, ids=str)
+def test_fast_path_layouts(case, monkeypatch):
+    shape, dtype = case
+    _say(f"fast path layout {shape} {dtype}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 240, dtype=dtype)
+    args = to_dev(t, dtype)
+    ref = ref_of(t)
+    y = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    check(as_f64(y), ref, dtype, f"fast {shape}")
+    monkeypatch.setenv("SSM2D_FAST", "0")
+    yg = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    check(as_f64(yg), ref, dtype, f"general {shape}")
