@@ -123,18 +123,18 @@ def is_scan_kernel(name: str) -> bool:
 
 
 def kernel_name(wl, variant: str) -> str:
-    """The scan kernel a workload's launch runs: the two-rows-per-step forward
-    for the plain scan of tall maps whose chains span workgroups (8 state
-    groups, 4-column strips, rows of a multiple of 4 columns, at most 16
-    states), else the general kernel."""
-    if variant in ("fwd",) and wl.H >= 128 and wl.W % 4 == 0 and 4 < wl.d_state <= 16 and \
-            os.environ.get("SSM2D_FAST", "1") != "0":
-        chains4 = wl.batch * ((wl.d_inner + 15) // 16)
-        if chains4 < 512:  # 8 state groups; chains of one workgroup otherwise
-            chains8 = wl.batch * ((wl.d_inner + 7) // 8)
-            if chains8 < 256:
-                return "scan2d_fast_kernel"
-    return "scan2d_fwd_kernel"
+    """The scan kernel(s) a step of the workload launches, as the library plans
+    them (ssm2d_fwd_kernels): the two-rows-per-step forward, the general
+    kernel, or both joined by '+' (a four-corner sum can use both)."""
+    import selective_state_space_ssm2d_amd as pkg
+
+    kw, _ = VARIANTS[variant]
+    if kw == "bwd":
+        return "scan2d_fwd_kernel"  # the stored-state and adjoint passes
+    fast, general = pkg.fwd_kernels(wl.batch, wl.d_inner, wl.d_state, wl.H, wl.W, bf16=wl.dtype == "bf16",
+                                    **(kw or {}))
+    names = (["scan2d_fast_kernel"] if fast else []) + (["scan2d_fwd_kernel"] if general else [])
+    return "+".join(names)
 
 
 def _pmc_per_dispatch(run_dir: str, counter: str, name_part):

@@ -366,6 +366,18 @@ int ssm2d_set_spin_limit(int64_t polls);
  * ("no error" if there was none). Static storage; never NULL. */
 const char *ssm2d_last_hip_error(void);
 
+/* Which scan kernels a forward call with these sizes and flags (and no
+ * gate, delta bias or carried states) launches, as the call itself plans
+ * them (same environment, same device): *two_row = launches of the
+ * two-rows-per-step forward (the plain scan of rows of a multiple of 4
+ * columns whose layout has it), *general = launches of the general kernel.
+ * bf16 != 0: the bf16 entry points (their four-corner sums and softplus step
+ * sizes run fp32 kernels). No device work. Returns SSM2D_OK (both 0 for an
+ * empty call), or the status the call would return for bad flags or sizes,
+ * or SSM2D_ERR_NULLPTR for a null output. */
+int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                      uint32_t flags, int *two_row, int *general);
+
 /* Test and tuning hooks (environment variables, read at each call; integers).
  * They change how the work is laid out, never what is computed:
  *   SSM2D_GROUPS=4|8     state groups per wave (default: by shape)
@@ -377,7 +389,10 @@ const char *ssm2d_last_hip_error(void);
  *                        strips, 0 for 8-column strips)
  *   SSM2D_RING=n         depth of the global carry ring when the grid is co-resident
  *   SSM2D_LDSRING=4|16|32  depth of the LDS carry rings
- *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD */
+ *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD
+ *   SSM2D_FAST=0|1|2     the general kernel for every plain forward (0);
+ *                        the two-rows-per-step kernel for chains across
+ *                        workgroups (1, default); for every layout it has (2) */
 
 /* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
 int ssm2d_version(void);

@@ -28,7 +28,8 @@ __all__ = [
     "LIB_PATH", "HEADER_PATH", "load_library", "scan_fwd", "scan_fwd_ex", "scan_fwd_mamba", "scan_bwd",
     "scan_bwd_mamba",
     "status_string",
-    "sync_check", "set_spin_limit", "release_workspaces", "set_epoch_for_test", "exported_names", "Ssm2dError",
+    "sync_check", "set_spin_limit", "release_workspaces", "set_epoch_for_test", "fwd_kernels", "exported_names",
+    "Ssm2dError",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssm2d_release_workspaces.restype = ctypes.c_int
     lib.ssm2d_test_set_epoch.argtypes = [vp, ctypes.c_uint32]
     lib.ssm2d_test_set_epoch.restype = ctypes.c_int
+    lib.ssm2d_fwd_kernels.argtypes = [ctypes.c_int] + [i64] * 5 + [ctypes.c_uint32, vp, vp]
+    lib.ssm2d_fwd_kernels.restype = ctypes.c_int
     lib.ssm2d_version.argtypes = []
     lib.ssm2d_version.restype = ctypes.c_int
     lib.ssm2d_last_hip_error.argtypes = []
@@ -146,6 +149,22 @@ def set_epoch_for_test(epoch: int, stream=None) -> None:
     s = load_library().ssm2d_test_set_epoch(_stream_handle(stream), int(epoch))
     if s != OK:
         raise Ssm2dError(s, "ssm2d_test_set_epoch")
+
+
+def fwd_kernels(batch, d_inner, d_state, H, W, bf16=False, flip_h=False, flip_w=False, vertical_first=False,
+                accumulate=False, four_way=False, delta_softplus=False):
+    """(launches of the two-rows-per-step forward, launches of the general
+    kernel) that a forward call of these sizes and options makes (no gate,
+    delta bias or carried states). Host-side planning only: no GPU needed."""
+    flags = ((FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
+             | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0)
+             | (DELTA_SOFTPLUS if delta_softplus else 0))
+    fast, general = ctypes.c_int(0), ctypes.c_int(0)
+    s = load_library().ssm2d_fwd_kernels(int(bool(bf16)), batch, d_inner, d_state, H, W, flags,
+                                         ctypes.byref(fast), ctypes.byref(general))
+    if s != OK:
+        raise Ssm2dError(s, "ssm2d_fwd_kernels")
+    return fast.value, general.value
 
 
 def _check(x, delta, A, B, C, D, y, need_d):

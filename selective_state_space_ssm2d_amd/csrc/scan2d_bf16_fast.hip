@@ -11,4 +11,10 @@ int dispatch_fast(const uint16_t *x, const uint16_t *delta, const float *A, cons
     return dispatch_fast_impl<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream, align);
 }
 
+template <>
+bool fast_path_taken<uint16_t>(const Plan &pl, int align)
+{
+    return fast_path_taken_impl<uint16_t>(pl, align);
+}
+
 }  // namespace ssm2d_impl

@@ -11,4 +11,10 @@ int dispatch_fast(const float *x, const float *delta, const float *A, const floa
     return dispatch_fast_impl<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream, align);
 }
 
+template <>
+bool fast_path_taken<float>(const Plan &pl, int align)
+{
+    return fast_path_taken_impl<float>(pl, align);
+}
+
 }  // namespace ssm2d_impl

@@ -32,7 +32,8 @@ constexpr int kFastSteps = 8;       // steps of the input ring (two rows each)
 constexpr int kFastAhead = 3;       // steps a wave writes its share ahead of processing
 constexpr int kFastPrefetch = 2;    // steps a share's loads are issued ahead of writing it
 constexpr int kFastCarryRows = 8;   // rows of each LDS carry ring
-constexpr int kFastStrips = 8;      // strips a workgroup can hold (with two couriers)
+constexpr int kFastStrips = 8;      // strips a workgroup of a chain across workgroups holds (with two couriers)
+constexpr int kFastStripsOne = 16;  // strips a workgroup holding a whole chain can hold (light layouts)
 
 // Input ring: the invariant that keeps a slot from being rewritten while it is
 // read. A wave reads step t only after every wave has written its share of
@@ -60,29 +61,45 @@ struct FastShape {
     static constexpr int NCHUNK = (2 * CPW + 2 * G * NPL) * CPR;  // packet rows: x, delta, B, C
     static constexpr int PASSES = (NCHUNK + kWave - 1) / kWave;  // chunks a lane loads per row
     static constexpr int PST = NCHUNK + 1;                      // chunks per strip packet (one pad chunk)
-    static constexpr int ROWC = kFastStrips * PST;              // chunks per ring row
-    static constexpr size_t ring_bytes = static_cast<size_t>(2 * kFastSteps) * ROWC * sizeof(Chunk);
-    static constexpr size_t carry_bytes = static_cast<size_t>(kFastStrips + 1) * kFastCarryRows * kWave * NPL * 4;
-    static constexpr size_t lds_bytes = ring_bytes + carry_bytes;
+    static constexpr int SST = 2 * kFastSteps * PST + 1;        // chunks per strip's ring (its packets of 16 rows)
+    // LDS of a workgroup of s strips: the input ring (each strip's packets of
+    // 2 kFastSteps rows, strip-major, so that every offset within a strip's
+    // ring is a compile-time constant) and s + 1 carry rings.
+    static constexpr size_t ring_bytes(int s) { return static_cast<size_t>(s) * SST * sizeof(Chunk); }
+    static constexpr size_t carry_bytes(int s)
+    {
+        return static_cast<size_t>(s + 1) * kFastCarryRows * kWave * NPL * 4;
+    }
+    static constexpr size_t lds_bytes(int s) { return ring_bytes(s) + carry_bytes(s); }
+    // Strips a workgroup can hold: 8 (and two couriers) for chains across
+    // workgroups; 16 for a whole chain in the layouts light enough in
+    // registers for 16 waves a CU (4-column strips with 1 state a lane, or
+    // bf16 inputs), else 8.
+    static constexpr int max_strips(bool chained)
+    {
+        return chained ? kFastStrips : ((K == 4 && (NPL == 1 || sizeof(T) == 2)) ? kFastStripsOne : kFastStrips);
+    }
 };
 
 // CHAINED: chains cut into several workgroups (tickets, couriers); else one
 // workgroup holds a whole chain.
 template <typename T, int G, int NPL, int K, bool CHAINED>
-__global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void scan2d_fast_kernel(Params p)
+__global__ __launch_bounds__(kWave * (FastShape<T, G, NPL, K>::max_strips(CHAINED) + (CHAINED ? 2 : 0)))
+void scan2d_fast_kernel(Params p)
 {
     static_assert(K == 4 || K == 8, "4- or 8-column strips");
     using Sh = FastShape<T, G, NPL, K>;
     using Chunk = typename Sh::Chunk;
     constexpr int CPW = Sh::CPW, CPR = Sh::CPR, NCHUNK = Sh::NCHUNK, PASSES = Sh::PASSES, PST = Sh::PST,
-                  ROWC = Sh::ROWC;
+                  SST = Sh::SST;
+    constexpr int MAXS = Sh::max_strips(CHAINED);
     constexpr int SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
     constexpr int CR = kFastCarryRows;
     constexpr int KO = K / G > 0 ? K / G : 1;  // finished cells per lane and row
 
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_done[kFastStrips + 1];   // rows published into LDS carry ring w
-    __shared__ int s_used[kFastStrips + 1];   // rows consumed from LDS carry ring w
+    __shared__ int s_done[MAXS + 1];   // rows published into LDS carry ring w
+    __shared__ int s_used[MAXS + 1];   // rows consumed from LDS carry ring w
     __shared__ int s_arrive[kFastSteps];      // shares written into input-ring step slot
     __shared__ unsigned int s_ticket, s_epoch;
     __shared__ int s_last;
@@ -93,7 +110,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
         s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_epoch = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % kEpochs + 1;
     }
-    if (threadIdx.x <= kFastStrips) {
+    if (threadIdx.x <= MAXS) {
         s_done[threadIdx.x] = 0;
         s_used[threadIdx.x] = 0;
     }
@@ -119,7 +136,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
     const int dblk = chain % p.n_dblk;
     const int H = p.H, W = p.W;
     const long ring_floats = static_cast<long>(CR) * kWave * NPL;
-    float *lring = reinterpret_cast<float *>(smem + Sh::ring_bytes);
+    float *lring = reinterpret_cast<float *>(smem + Sh::ring_bytes(p.s_local));
 
     if (wave >= p.s_local) {
         if constexpr (CHAINED)
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
         const int rs = p.flip_h ? -W : W;
         const long row0 = p.flip_h ? HW - W : 0;
         const T *zeros = static_cast<const T *>(p.zeros);
-        T *ring = reinterpret_cast<T *>(smem);  // [16 rows][ROWC chunks of 4 elements]
+        T *ring = reinterpret_cast<T *>(smem);  // [strip][16 rows][PST chunks of 4 elements] (SST a strip)
 
         // This lane's chunks of the workgroup's rows: wave w loads chunks
         // [w NCHUNK, (w + 1) NCHUNK) of a row taken in column order (packet row
@@ -153,13 +170,13 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
         for (int pp = 0; pp < PASSES; ++pp) {
             const int c = pp * kWave + lane;
             const T *base = zeros;
-            int dst = wave * PST + NCHUNK;
+            int dst = wave * SST + NCHUNK;
             long col = 0;
             if (c < NCHUNK) {
                 const int cw = wave * NCHUNK + c;
                 const int r = cw / (nact * CPR), rem = cw % (nact * CPR);
                 const int sj = rem / CPR, q = rem % CPR;
-                dst = sj * PST + r * CPR + q;
+                dst = sj * SST + r * CPR + q;
                 col = static_cast<long>(grp * p.s_local + sj) * K + 4 * q;
                 if (col + 4 > W) {
                     // past the row's end: zeros
@@ -193,13 +210,13 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
         asm volatile("" ::"v"(Dd));
 
         // Operand offsets (elements) of this lane in a ring row.
-        const int off_x = (wave * PST + dl * CPR) * 4;
-        const int off_dt = (wave * PST + (SEG_DT + dl) * CPR) * 4;
+        const int off_x = (wave * SST + dl * CPR) * 4;
+        const int off_dt = (wave * SST + (SEG_DT + dl) * CPR) * 4;
         int off_b[NPL], off_c[NPL];
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
-            off_b[k] = (wave * PST + (SEG_B + g * NPL + k) * CPR) * 4;
-            off_c[k] = (wave * PST + (SEG_C + g * NPL + k) * CPR) * 4;
+            off_b[k] = (wave * SST + (SEG_B + g * NPL + k) * CPR) * 4;
+            off_c[k] = (wave * SST + (SEG_C + g * NPL + k) * CPR) * 4;
         }
         // The first finished cell of this lane after the sum over state
         // groups (for G = 8 and K = 4 the two lanes of a pair hold the same
@@ -263,12 +280,12 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
                 }
         };
         auto write_step = [&](const Chunk (&sh)[2][PASSES], const int slot) __attribute__((always_inline)) {
-            T *r0 = ring + static_cast<long>(2 * slot) * ROWC * 4;
+            T *r0 = ring + 2 * slot * PST * 4;
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp)
-                    reinterpret_cast<Chunk *>(r0 + static_cast<long>(rr) * ROWC * 4)[wdst[pp]] = sh[rr][pp];
+                    reinterpret_cast<Chunk *>(r0 + rr * PST * 4)[wdst[pp]] = sh[rr][pp];
             signal_fence();
             if (lane == 0) __hip_atomic_fetch_add(&s_arrive[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             signal_fence();
@@ -301,8 +318,8 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
                 // ---- this step's rows (their arrival was confirmed at the end
                 // of the previous step), and the arrival count of the next
                 // step's, confirmed at the end of this one
-                const T *r0 = ring + static_cast<long>(2 * J) * ROWC * 4;
-                const T *r1 = r0 + static_cast<long>(ROWC) * 4;
+                const T *r0 = ring + 2 * J * PST * 4;
+                const T *r1 = r0 + PST * 4;
                 float xv[2][K], dv[2][K], Bv[2][NPL][K], Cv[2][NPL][K], xo[2][KO];
                 read_packet<K>(r0, off_x, xv[0]);
                 read_packet<K>(r0, off_dt, dv[0]);
@@ -543,9 +560,8 @@ __global__ __launch_bounds__(kWave * (kFastStrips + (CHAINED ? 2 : 0))) void sca
 
 // ---------------------------------------------------------------- host side
 
-// Launch for a plan of the shared-row-ring layout (8 state groups, 4-column
-// strips, rows of a multiple of 4 columns, chains across workgroups, at most
-// kFastStrips strips per workgroup) with 1 or 2 states a lane.
+// Launch for a plan of one of the shared-row-ring layouts; CHAINED: the
+// chains span workgroups (tickets, couriers and the global carry ring).
 template <typename T, int G, int NPL, int K, bool CHAINED>
 int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
              int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
@@ -553,6 +569,7 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
     using Sh = FastShape<T, G, NPL, K>;
     pl.ring_rows = kFastCarryRows;
     const int threads = kWave * (pl.s_local + (CHAINED ? 2 : 0));
+    const size_t lds = Sh::lds_bytes(pl.s_local);
     pl.qg = H;
     if constexpr (CHAINED) {
         // global ring depth: bounded (with back-pressure) only if the whole
@@ -560,7 +577,7 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
         // that cannot run
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, G, NPL, K, true>, threads,
-                                                         Sh::lds_bytes) == hipSuccess) {
+                                                         lds) == hipSuccess) {
             const int qg = env_int("SSM2D_RING", 32);
             if (static_cast<long>(per_cu) * device_cus(dev) >= pl.total_wg && qg >= 8 && qg < H) pl.qg = qg;
         } else {
@@ -580,43 +597,61 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
     }
     const Params prm = make_params(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, *e);
     scan2d_fast_kernel<T, G, NPL, K, CHAINED>
-        <<<dim3(pl.total_wg), dim3(threads), Sh::lds_bytes, static_cast<hipStream_t>(stream)>>>(prm);
+        <<<dim3(pl.total_wg), dim3(threads), lds, static_cast<hipStream_t>(stream)>>>(prm);
     const hipError_t err = hipGetLastError();
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
+}
+
+// Whether a plan fits a layout's kernel: 8-column strips only for chains held
+// in one workgroup (with couriers their registers would spill), at most
+// max_strips strips a workgroup, LDS within the CU's.
+template <typename T, int G, int NPL, int K>
+bool fast_layout_ok(const Plan &pl)
+{
+    using Sh = FastShape<T, G, NPL, K>;
+    const bool chained = pl.groups > 1;
+    if (K == 8 && chained) return false;
+    return pl.s_local >= 1 && pl.s_local <= Sh::max_strips(chained) && Sh::lds_bytes(pl.s_local) <= kFastLdsMax;
 }
 
 template <typename T, int G, int NPL, int K>
 int run_fast_layout(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
                     int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream)
 {
-    if constexpr (FastShape<T, G, NPL, K>::lds_bytes > kFastLdsMax) {
-        return kNoFastPath;  // the input ring of this layout does not fit
+    if constexpr (K == 4) {
+        if (pl.groups > 1)
+            return run_fast<T, G, NPL, K, true>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev,
+                                                stream);
     } else {
-        // (8-column strips: chains of one workgroup only; the planner picks
-        // them only there, and with couriers their registers would spill)
-        if constexpr (K == 4) {
-            if (pl.groups > 1)
-                return run_fast<T, G, NPL, K, true>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev,
-                                                    stream);
-        } else {
-            if (pl.groups > 1) return kNoFastPath;
-        }
-        return run_fast<T, G, NPL, K, false>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
+        if (pl.groups > 1) return kNoFastPath;  // (no chained instance)
     }
+    return run_fast<T, G, NPL, K, false>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
 }
 
-// The two-rows-per-step launch when the plan has one of its layouts (4 or 8
-// state groups with 1 or 2 states a lane, 4- or 8-column strips, rows of a
-// multiple of 4 columns, at most kFastStrips strips a workgroup, an input
-// ring that fits the LDS); kNoFastPath otherwise (the general kernel then
-// runs it).
+// Whether a plan's launch is the two-rows-per-step kernel: the plain forward
+// (no direction or order bits, no carried states) of rows of a multiple of 4
+// columns, in a plan with one of its layouts (4 or 8 state groups with 1 or 2
+// states a lane, 4- or 8-column strips) that fast_layout_ok accepts.
+template <typename T>
+bool fast_path_taken_impl(const Plan &pl, int align)
+{
+    if (pl.mode != 0 || pl.h_init || pl.h_last || align != 4) return false;
+#define SSM2D_FAST_CASE(GG, NN, KK) \
+    if (pl.G == GG && pl.npl == NN && pl.K == KK) return fast_layout_ok<T, GG, NN, KK>(pl);
+    SSM2D_FAST_CASE(8, 1, 4) SSM2D_FAST_CASE(8, 2, 4) SSM2D_FAST_CASE(8, 1, 8) SSM2D_FAST_CASE(8, 2, 8)
+    SSM2D_FAST_CASE(4, 1, 4) SSM2D_FAST_CASE(4, 2, 4)
+#undef SSM2D_FAST_CASE
+    return false;
+}
+
+// The two-rows-per-step launch of a plan that fast_path_taken_impl accepts;
+// kNoFastPath otherwise (the general kernel then runs it).
 template <typename T>
 int dispatch_fast_impl(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
                        int batch, int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream,
                        int align)
 {
-    // Plain forward only: no direction or order bits, no carried states.
-    if (pl.mode != 0 || pl.h_init || pl.h_last || pl.s_local > kFastStrips || align != 4) return kNoFastPath;
+    if (!fast_path_taken_impl<T>(pl, align)) return kNoFastPath;
 #define SSM2D_FAST_CASE(GG, NN, KK)                         \
     if (pl.G == GG && pl.npl == NN && pl.K == KK)           \
         return run_fast_layout<T, GG, NN, KK>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);

@@ -1793,6 +1793,14 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
 constexpr int kNoFastPath = -1;
 SSM2D_DISPATCH_DECL(float, dispatch_fast)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_fast)
+// Whether dispatch_fast takes a plan (for inputs of type T; rows of a
+// multiple of `align` columns).
+template <typename T>
+bool fast_path_taken(const Plan &pl, int align);
+template <>
+bool fast_path_taken<float>(const Plan &pl, int align);
+template <>
+bool fast_path_taken<uint16_t>(const Plan &pl, int align);
 // The other modes (8 state groups; 4-column strips with per-wave packets or
 // the shared row ring, align 2 served by the align-1 kernels; 8-column strips
 // for the forward modes on rows of a multiple of 4 columns), one translation

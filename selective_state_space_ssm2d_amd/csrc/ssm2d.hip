@@ -522,6 +522,41 @@ void choose_coop(Plan &pl, int64_t H, int align)
             pl.coop_slots = slots;
 }
 
+// Rows of a multiple of 4, 2 or 1 columns (the widest vector loads a row takes).
+inline int row_align(int64_t W)
+{
+    return (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
+}
+
+// Whether a launch runs in the two-rows-per-step kernel; if so, pl becomes
+// its plan. By default that is the plain forward of plans whose chains span
+// workgroups (there it beats the general kernel: one handshake per two rows
+// against the couriers' and the shared ring's latencies). Chains held in one
+// workgroup stay on the general kernel, faster there as measured (VMamba
+// stage 1: 159 us against 168 us in 8-column and 174 us in 4-column strips);
+// SSM2D_FAST=2 runs them in the two-rows-per-step kernel too, trying first
+// a chain of up to 16 4-column strips where the general plan widens the
+// strips to 8 columns.
+template <typename T>
+bool takes_fast(Plan &pl, int64_t W, int align)
+{
+    const int fast = env_int("SSM2D_FAST", 1);
+    if (pl.mode != 0 || fast <= 0) return false;
+    if (pl.groups == 1 && fast < 2) return false;
+    if (pl.K == 8 && pl.groups == 1 && env_int("SSM2D_STRIP", 0) != 8) {
+        Plan p4 = pl;
+        p4.K = 4;
+        p4.nstrips = static_cast<int>((W + 3) / 4);
+        p4.s_local = p4.nstrips;
+        p4.total_wg = p4.n_chains;
+        if (fast_path_taken<T>(p4, align)) {
+            pl = p4;
+            return true;
+        }
+    }
+    return fast_path_taken<T>(pl, align);
+}
+
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
@@ -536,11 +571,11 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     pl.fixed_ws = fixed_ws;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
-    const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
+    const int align = row_align(W);
     choose_coop<T>(pl, H, align);
 #define SSM2D_ARGS x, delta, A, B, C, D, y, bi, di, ni, hi, wi, pl, dev, stream, align
     constexpr int FW = kModeFlipW, VF = kModeVFirst, AC = kModeAccumulate;
-    if (mode == 0 && env_int("SSM2D_FAST", 1)) {
+    if (takes_fast<T>(pl, W, align)) {
         // the plain forward: two rows per step, where the plan's layout has that kernel
         const int st = dispatch_fast(SSM2D_ARGS);
         if (st != kNoFastPath) return st;
@@ -980,9 +1015,47 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     return SSM2D_OK;
 }
 
+// Scan launches of a forward call (no gate, delta bias or carried states) in
+// each kernel, as scan_fwd and launch() plan them.
+template <typename T>
+void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags,
+                        int *two_row, int *general)
+{
+    const int vf = (flags & SSM2D_VERTICAL_FIRST) ? kModeVFirst : 0;
+    const int acc = (flags & SSM2D_ACCUMULATE) ? kModeAccumulate : 0;
+    const int n = (flags & SSM2D_FOUR_WAY) ? 4 : 1;
+    for (int q = 0; q < n; ++q) {
+        const int mode = (flags & SSM2D_FOUR_WAY)
+                             ? (((q & 2) ? kModeFlipW : 0) | vf | (q == 0 ? acc : kModeAccumulate))
+                             : (((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc);
+        Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
+        const int align = row_align(W);
+        choose_coop<T>(pl, H, align);
+        ++*(takes_fast<T>(pl, W, align) ? two_row : general);
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                      uint32_t flags, int *two_row, int *general)
+{
+    if (!two_row || !general) return SSM2D_ERR_NULLPTR;
+    *two_row = *general = 0;
+    if ((flags & ~kKnownFlags) != 0 || ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))))
+        return SSM2D_ERR_BAD_FLAGS;
+    if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
+    if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
+    if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
+    // bf16 four-corner sums and softplus step sizes run the fp32 kernels
+    if (bf16 && !(flags & (SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
+        count_fwd_launches<uint16_t>(batch, d_inner, d_state, H, W, flags, two_row, general);
+    else
+        count_fwd_launches<float>(batch, d_inner, d_state, H, W, flags, two_row, general);
+    return SSM2D_OK;
+}
 
 int ssm2d_scan_fwd(const float *x, const float *delta, const float *A, const float *B, const float *C,
                    const float *D, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
@@ -1198,7 +1271,7 @@ int ssm2d_set_spin_limit(int64_t polls)
     return SSM2D_OK;
 }
 
-int ssm2d_version(void) { return 400; }
+int ssm2d_version(void) { return 401; }
 
 const char *ssm2d_last_hip_error(void)
 {

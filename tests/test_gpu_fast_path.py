@@ -80,13 +80,17 @@ def test_fast_path_deterministic_and_guarded():
     check(as_f64(y), ref_of(t), "f32", "fast guarded")
 
 
-# Layouts the planner picks for many chains (one workgroup a chain):
-# 8-column strips (VMamba-like rows of 56 and 60 columns), 4-column strips,
-# 4 state groups with 1 and 2 states a lane; and a short map whose chains
-# span workgroups.
+# Layouts for many chains (one workgroup a chain; SSM2D_FAST=2): up to
+# 16 4-column strips a workgroup (VMamba-like rows of 56 and 60 columns in
+# bf16), 8-column strips where 4-column ones do not fit (LDS), 4 state groups
+# with 1 and 2 states a lane; and a short map whose chains span workgroups.
 LAYOUT_SHAPES = [
-    ((32, 64, 16, 20, 56), "bf16"),   # 8 groups, 2 states a lane, 8-column strips
-    ((32, 64, 16, 19, 60), "bf16"),   # the same, last strip half full, odd H
+    ((32, 64, 16, 20, 56), "bf16"),   # 8 groups, 2 states a lane, 14 4-column strips
+    ((32, 64, 16, 19, 60), "bf16"),   # 15 strips, odd H
+    ((32, 64, 16, 20, 64), "bf16"),   # 16 4-column strips exceed the LDS: 8-column strips
+    ((32, 64, 16, 17, 28), "f32"),    # fp32, 2 states a lane: 7 4-column strips (at most 8 there)
+    ((32, 64, 8, 20, 60), "f32"),     # fp32, 1 state a lane, 15 strips exceed the LDS: 8-column, half-full last
+    ((32, 64, 8, 13, 48), "f32"),     # fp32, 1 state a lane, 12 4-column strips
     ((32, 64, 8, 18, 56), "f32"),     # 8-column strips, 1 state a lane, fp32
     ((32, 64, 16, 21, 32), "f32"),    # 4-column strips in one workgroup
     ((16, 256, 4, 12, 24), "f32"),    # 4 groups, 1 state a lane
@@ -102,6 +106,8 @@ def test_fast_path_layouts(case, monkeypatch):
     t = make_random_inputs(*shape, seed=sum(shape) + 240, dtype=dtype)
     args = to_dev(t, dtype)
     ref = ref_of(t)
+    monkeypatch.setenv("SSM2D_FAST", "2")  # chains in one workgroup too
+    assert pkg.fwd_kernels(*shape, bf16=dtype == "bf16") == (1, 0)
     y = pkg.scan_fwd(*args)
     pkg.sync_check()
     check(as_f64(y), ref, dtype, f"fast {shape}")
