@@ -30,7 +30,10 @@ namespace ssm2d_impl {
 
 constexpr int kFastSteps = 8;       // steps of the input ring (two rows each)
 constexpr int kFastAhead = 3;       // steps a wave writes its share ahead of processing
-constexpr int kFastPrefetch = 2;    // steps a share's loads are issued ahead of writing it
+#ifndef SSM2D_FAST_PREFETCH
+#define SSM2D_FAST_PREFETCH 2
+#endif
+constexpr int kFastPrefetch = SSM2D_FAST_PREFETCH;    // steps a share's loads are issued ahead of writing it
 constexpr int kFastCarryRows = 8;   // rows of each LDS carry ring
 constexpr int kFastStrips = 8;      // strips a workgroup of a chain across workgroups holds (with two couriers)
 constexpr int kFastStripsOne = 16;  // strips a workgroup holding a whole chain can hold (light layouts)
@@ -42,7 +45,7 @@ constexpr int kFastStripsOne = 16;  // strips a workgroup holding a whole chain 
 // writes step f + kFastAhead; the slowest reads a step >= f - kFastAhead; the
 // two are 2 * kFastAhead < kFastSteps steps apart, so never in one slot.
 static_assert(2 * kFastAhead < kFastSteps, "input ring too shallow for the staging distance");
-static_assert(kFastPrefetch == 2, "two register sets of staged shares");
+static_assert(kFastSteps % kFastPrefetch == 0, "register sets of staged shares rotate with the unrolled steps");
 
 // One chunk (4 elements) as a plain vector, which the compiler keeps in
 // registers across the unrolled steps.
@@ -267,9 +270,9 @@ void scan2d_fast_kernel(Params p)
 #pragma unroll
             for (int k = 0; k < NPL; ++k) hv[c][k] = 0.0f;
 
-        // Shares of two steps in flight: stg[s] holds the share of the step
-        // staged kFastPrefetch steps after it was loaded.
-        Chunk stg[2][2][PASSES];
+        // Shares of kFastPrefetch steps in flight: stg[s] holds the share of
+        // the step staged kFastPrefetch steps after it was loaded.
+        Chunk stg[kFastPrefetch][2][PASSES];
         auto load_step = [&](Chunk (&dst)[2][PASSES], const int first_row) __attribute__((always_inline)) {
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr)
@@ -312,8 +315,8 @@ void scan2d_fast_kernel(Params p)
                 // ---- stage: this wave's share of step J + kFastAhead, loaded
                 // two steps ago; then the loads for two steps further on
                 constexpr int JS = (J + kFastAhead) % kFastSteps;
-                write_step(stg[J % 2], JS);
-                load_step(stg[J % 2], i + 2 * (kFastAhead + kFastPrefetch));
+                write_step(stg[J % kFastPrefetch], JS);
+                load_step(stg[J % kFastPrefetch], i + 2 * (kFastAhead + kFastPrefetch));
 
                 // ---- this step's rows (their arrival was confirmed at the end
                 // of the previous step), and the arrival count of the next
@@ -516,8 +519,8 @@ void scan2d_fast_kernel(Params p)
                 load_step(stg[0], 2 * s);
                 write_step(stg[0], s);
             }
-            load_step(stg[0], 2 * kFastAhead);
-            load_step(stg[1], 2 * kFastAhead + 2);
+#pragma unroll
+            for (int q = 0; q < kFastPrefetch; ++q) load_step(stg[q], 2 * (kFastAhead + q));
             wait_count(&s_arrive[0], nact);  // the first step's rows
             using I = std::integral_constant<int, 0>;
             using I1 = std::integral_constant<int, 1>;
