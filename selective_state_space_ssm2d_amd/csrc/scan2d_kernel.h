@@ -166,6 +166,23 @@ template <> struct ChunkOf<uint16_t> { using type = uint2; };    // 4 bf16
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Element type of the per-wave input packets in LDS: fp32 for both input
+// types. A bf16 chunk is widened (exactly) once, by the lane that stages
+// it, instead of by each of the lanes that read its elements (a B or C
+// element is read by every channel lane of its state group).
+template <typename T, bool COOP> struct PacketOf { using type = float; };
+template <> struct PacketOf<uint16_t, true> { using type = uint16_t; };  // (the shared row ring keeps bf16)
+__device__ __forceinline__ float4 to_packet(const float4 &c) { return c; }
+__device__ __forceinline__ float4 to_packet(uint2 c)
+{
+    // (widened here, where the chunk is staged: hoisted to where it is
+    // loaded, the widened chunks would double the prefetch buffers' registers)
+    asm volatile("" : "+v"(c.x), "+v"(c.y));
+    return make_float4(bf16_lo(c.x), bf16_hi(c.x), bf16_lo(c.y), bf16_hi(c.y));
+}
+__device__ __forceinline__ uint2 to_packet_ring(const uint2 &c) { return c; }
+__device__ __forceinline__ float4 to_packet_ring(const float4 &c) { return c; }
+
 // One 4-element chunk, read as 4/ALIGN unconditional loads of ALIGN elements.
 // Sub-loads that fall past the end of a row were pointed at the zero page when
 // the pointers were set up, so no load needs a mask.
@@ -676,6 +693,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     static_assert(!BWD || !COOP || EDGES, "backward with the shared row ring: courier-free chains only");
     static_assert(!STATES || (!VF && !ACC), "stored states: horizontal-first order");
     using Chunk = typename ChunkOf<T>::type;
+    using LT = typename PacketOf<T, COOP>::type;      // element type of the input rows in LDS
+    using LChunk = typename ChunkOf<LT>::type;
     constexpr int CPW = kWave / G;                    // channels per wave
     constexpr int KO = K / G > 0 ? K / G : 1;         // finished cells per lane and row
     constexpr int SEG_X = 0, SEG_DT = CPW, SEG_B = 2 * CPW, SEG_C = 2 * CPW + G * NPL;
@@ -732,8 +751,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     const long ring_floats = static_cast<long>(p.ring_rows) * kWave * NPL;
     // LDS: the input rows (per-wave packets, or the workgroup's row ring), then
     // the carry rings.
-    const long in_bytes = COOP ? static_cast<long>(p.coop_slots) * p.s_local * (NCHUNK + 1) * sizeof(Chunk)
-                               : static_cast<long>(p.s_local) * 2 * PASSES * kWave * sizeof(Chunk);
+    const long in_bytes = COOP ? static_cast<long>(p.coop_slots) * p.s_local * (NCHUNK + 1) * sizeof(LChunk)
+                               : static_cast<long>(p.s_local) * 2 * PASSES * kWave * sizeof(LChunk);
     float *lring = reinterpret_cast<float *>(smem + in_bytes);
 
     if (wave >= p.s_local) {
@@ -756,7 +775,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // Two packet buffers of PASSES x 64 chunks (chunks past NCHUNK are
         // padding, so every lane stores its chunk without a mask): row i is
         // read from buffer i % 2 while row i + 1 is staged into the other.
-        T *packets = reinterpret_cast<T *>(smem) + static_cast<long>(wave) * 2 * PASSES * kWave * 4;
+        LT *packets = reinterpret_cast<LT *>(smem) + static_cast<long>(wave) * 2 * PASSES * kWave * 4;
         // Cooperative loads: the workgroup's nact strips share one ring of
         // rows in LDS. A row of the ring holds every strip's packet (strip s
         // at chunk s * (NCHUNK + 1): the pad chunk spreads the strips over the
@@ -767,7 +786,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         const int nact = min(p.s_local, p.nstrips - grp * p.s_local);  // strips of this workgroup
         const int slot_elems = nact * (NCHUNK + 1) * 4;
         const int XA = p.coop_slots / 2 - 2;  // rows a share is written ahead of its first reader
-        T *ring_rows = reinterpret_cast<T *>(smem);
+        LT *ring_rows = reinterpret_cast<LT *>(smem);
 
         // Chunk sources of this lane: packet row r, chunk q of that row, split
         // into 4/ALIGN sub-loads; a sub-load past the row end reads the zero page.
@@ -968,7 +987,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 
         // Operands of row t live at row_base(t) + roff(packet row).
         const int slot_mask = p.coop_slots - 1;
-        auto row_base = [&](const int t) -> T * {
+        auto row_base = [&](const int t) -> LT * {
             if constexpr (COOP) return ring_rows + static_cast<long>(t & slot_mask) * slot_elems;
             else return packets + (t % 2) * PASSES * kWave * 4;
         };
@@ -1008,7 +1027,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         struct Ops {
             float xv[K], dv[K];
         };
-        auto read_ops = [&](const T *pk, Ops &o) {
+        auto read_ops = [&](const LT *pk, Ops &o) {
             read_packet<K, FW>(pk, off_x, o.xv);
             read_packet<K, FW>(pk, off_dt, o.dv);
         };
@@ -1025,10 +1044,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         auto stage = [&](const Chunk (&cb)[PASSES], const int t, Ops &o) -> int {
             if constexpr (COOP) {
                 const int tw = t + XA;
-                T *slot = row_base(tw);
+                LT *slot = row_base(tw);
 #pragma unroll
                 for (int pp = 0; pp < PASSES; ++pp)
-                    reinterpret_cast<Chunk *>(slot)[wpos[pp]] = cb[pp];
+                    reinterpret_cast<LChunk *>(slot)[wpos[pp]] = to_packet_ring(cb[pp]);
                 signal_fence();
                 if (lane == 0)
                     __hip_atomic_fetch_add(&s_arrive[tw & slot_mask], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1038,9 +1057,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 read_ops(row_base(t), o);
                 return v;
             } else {
-                T *pk = row_base(t);
+                LT *pk = row_base(t);
 #pragma unroll
-                for (int pp = 0; pp < PASSES; ++pp) reinterpret_cast<Chunk *>(pk)[pp * kWave + lane] = cb[pp];
+                for (int pp = 0; pp < PASSES; ++pp) reinterpret_cast<LChunk *>(pk)[pp * kWave + lane] = to_packet(cb[pp]);
                 read_ops(pk, o);
                 return 0;
             }
@@ -1082,7 +1101,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             // so that LDS traffic overlaps this row's arithmetic.
             auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on, const T (&yo)[KO],
                               const float4 (&hcur)[NPL], const float4 (&hnext)[NPL]) {
-                const T *pk = row_base(i);
+                const LT *pk = row_base(i);
                 float Bv[NPL][K], Cv[NPL][K], xo[KO], dyv[K], dyo[KO];
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_b[k], Bv[k]);
@@ -1439,10 +1458,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
                         c0[pp] = load_chunk<ALIGN>(src[pp], static_cast<long>(min(t, H - 1)) * rs);
-                    T *slot = row_base(t);
+                    LT *slot = row_base(t);
 #pragma unroll
                     for (int pp = 0; pp < PASSES; ++pp)
-                        reinterpret_cast<Chunk *>(slot)[wpos[pp]] = c0[pp];
+                        reinterpret_cast<LChunk *>(slot)[wpos[pp]] = to_packet_ring(c0[pp]);
                     signal_fence();
                     if (lane == 0)
                         __hip_atomic_fetch_add(&s_arrive[t & slot_mask], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1594,11 +1613,12 @@ inline int block_threads(const Plan &pl)
 template <typename T, int K, int NPL, int G, int MODE>
 size_t lds_bytes(const Plan &pl)
 {
-    using Chunk = typename ChunkOf<T>::type;
+    // the shared row ring keeps the input type; per-wave packets are fp32
+    const size_t chunk_bytes = pl.coop_slots > 0 ? sizeof(typename ChunkOf<T>::type) : sizeof(float4);
     const size_t nchunk = static_cast<size_t>(packet_rows<NPL, G, MODE>()) * (K / 4);
     const size_t chunks = pl.coop_slots > 0 ? pl.coop_slots * (nchunk + 1)                                  // ring rows
                                             : 2 * static_cast<size_t>(passes_for<NPL, G, MODE>(K)) * kWave;  // 2 padded packets
-    return static_cast<size_t>(pl.s_local) * chunks * sizeof(Chunk) +
+    return static_cast<size_t>(pl.s_local) * chunks * chunk_bytes +
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
 
