@@ -1106,8 +1106,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 #pragma unroll
                 for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_b[k], Bv[k]);
                 const int next_count = stage(nb, i + 1, on);
+                if constexpr (BWD) {
 #pragma unroll
-                for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_c[k], Cv[k]);
+                    for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_c[k], Cv[k]);
+                }
                 read_packet_scalar<KO, FW>(pk, off_x, c_out, xo);
                 if constexpr (BWD) {
                     read_packet<K, FW>(pk, off_dy, dyv);
@@ -1281,6 +1283,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
+                // C of the forward's row: read once the carry is handed on
+                // (needed only for the output sum; read with B, it held 16
+                // more registers across the carry wait and spilled)
+                if constexpr (!BWD) {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) read_packet<K, FW>(pk, off_c[k], Cv[k]);
+                }
 
                 if constexpr (BWD) {
                     // ---- local derivatives. With hh = h - Abar h(row above)
