@@ -63,6 +63,8 @@ def load(path: str = LIB_PATH):
     lib.oracle_ssm2d_states_ex_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_fwd_carry_f64.argtypes = [dp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_ssm2d_fwd_carry_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_fwd_tile_f64.argtypes = [dp] * 11 + [i64] * 5 + [ctypes.c_int, ctypes.c_int]
+    lib.oracle_ssm2d_fwd_tile_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_bwd_f64.argtypes = [dp] * 13 + [i64] * 5 + [ctypes.c_int]
     lib.oracle_ssm2d_bwd_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
@@ -93,7 +95,8 @@ def _flags(flip_h, flip_w, vertical_first):
 
 
 def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, flip_w=False,
-        vertical_first=False, four_way=False, h_init=None, return_last=False):
+        vertical_first=False, four_way=False, h_init=None, return_last=False, hh_init=None,
+        return_last_col=False):
     """y = 2D selective scan forward in fp64.
 
     x, delta: [batch][d_inner][H][W]; A: [d_inner][d_state]; B, C:
@@ -107,7 +110,12 @@ def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, fli
     h_init ([batch][d_inner][d_state][W], may be None) is the carried vertical
     state before the first row in scan order; return_last also returns the
     state after the last row (y, h_last): scanning a map in bands of rows
-    with these carries gives the scan of the whole map.
+    with these carries gives the scan of the whole map. hh_init
+    ([batch][d_inner][d_state][H], may be None) is the carried horizontal
+    state (the row recurrence's carry) before the first column in scan
+    order, by row; return_last_col also returns the state after the last
+    column: bands of columns, and tiles with both carries, compose likewise.
+    With both, the result is (y, h_last, hh_last).
     """
     if D is None:
         D = np.zeros(np.shape(A)[0])
@@ -121,22 +129,27 @@ def fwd(x, delta, A, B, C, D, maps=None, nthreads=0, lib=None, flip_h=False, fli
         return y
     flags = _flags(flip_h, flip_w, vertical_first)
     lib = lib or _get()
-    if h_init is not None or return_last:
+    if h_init is not None or return_last or hh_init is not None or return_last_col:
         assert maps is None and not four_way
         x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))
         batch, d_inner, H, W = x.shape
         d_state = A.shape[1]
         y = np.empty((batch, d_inner, H, W), dtype=np.float64)
         hl = np.empty((batch, d_inner, d_state, W), dtype=np.float64)
+        gl = np.empty((batch, d_inner, d_state, H), dtype=np.float64)
         h0 = None if h_init is None else _f64(h_init)
+        g0 = None if hh_init is None else _f64(hh_init)
         assert h0 is None or h0.shape == hl.shape
+        assert g0 is None or g0.shape == gl.shape
         null = ctypes.POINTER(ctypes.c_double)()
-        s = lib.oracle_ssm2d_fwd_carry_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
-                                           null if h0 is None else _ptr(h0), _ptr(hl), batch, d_inner, d_state,
-                                           H, W, int(nthreads), flags)
+        s = lib.oracle_ssm2d_fwd_tile_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                                          null if h0 is None else _ptr(h0), _ptr(hl),
+                                          null if g0 is None else _ptr(g0), _ptr(gl), batch, d_inner, d_state,
+                                          H, W, int(nthreads), flags)
         if s != 0:
             raise RuntimeError(f"oracle failed with status {s}")
-        return (y, hl) if return_last else y
+        out = (y,) + ((hl,) if return_last else ()) + ((gl,) if return_last_col else ())
+        return out if len(out) > 1 else y
     x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))
     batch, d_inner, H, W = x.shape
     d_state = A.shape[1]

@@ -69,23 +69,29 @@ static void scan_state_map(const double *abar, const double *bx, double *h,
  * ("i-1", "j-1" meaning the previous cell in scan order). tmp: H*W scratch. */
 static void scan_state_map_dir(const double *abar, const double *bx, double *h, double *tmp,
                                int64_t H, int64_t W, int flip_h, int flip_w, int vfirst,
-                               const double *h0, double *hl)
+                               const double *h0, double *hl, const double *g0, double *gl)
 {
     /* h0 (may be NULL: zeros): the carried vertical state before the first
      * row in scan order, by column (h for the horizontal-first order, v for
      * vertical-first); hl (may be NULL): the same state after the last row.
      * Scanning a map in bands of rows, each band's h0 the previous band's hl,
-     * gives the scan of the whole map. */
+     * gives the scan of the whole map.
+     * g0 (may be NULL: zeros): the carried horizontal state before the first
+     * column in scan order, by row (the row recurrence's carry: hh for the
+     * horizontal-first order, h for vertical-first); gl (may be NULL): the
+     * same state after the last column. Bands of columns compose the same
+     * way, and tiles with both carries too. */
     for (int64_t si = 0; si < H; ++si) {
         const int64_t i = flip_h ? H - 1 - si : si;      /* row in scan order */
         const int64_t ip = flip_h ? i + 1 : i - 1;        /* previous row in scan order */
         if (!vfirst) {
-            double carry = 0.0;                           /* row recurrence first */
+            double carry = g0 ? g0[i] : 0.0;              /* row recurrence first */
             for (int64_t sj = 0; sj < W; ++sj) {
                 const int64_t j = flip_w ? W - 1 - sj : sj;
                 carry = abar[i * W + j] * carry + bx[i * W + j];
                 tmp[i * W + j] = carry;
             }
+            if (gl) gl[i] = carry;
             for (int64_t j = 0; j < W; ++j) {
                 const double prev = (si > 0) ? h[ip * W + j] : (h0 ? h0[j] : 0.0);
                 h[i * W + j] = abar[i * W + j] * prev + tmp[i * W + j];
@@ -95,12 +101,13 @@ static void scan_state_map_dir(const double *abar, const double *bx, double *h, 
                 const double prev = (si > 0) ? tmp[ip * W + j] : (h0 ? h0[j] : 0.0);
                 tmp[i * W + j] = abar[i * W + j] * prev + bx[i * W + j];
             }
-            double carry = 0.0;
+            double carry = g0 ? g0[i] : 0.0;
             for (int64_t sj = 0; sj < W; ++sj) {
                 const int64_t j = flip_w ? W - 1 - sj : sj;
                 carry = abar[i * W + j] * carry + tmp[i * W + j];
                 h[i * W + j] = carry;
             }
+            if (gl) gl[i] = carry;
         }
     }
     if (hl) {
@@ -124,7 +131,7 @@ int oracle_ssm2d_states_ex_f64(const double *abar, const double *bx, double *h,
     double *tmp = (double *)malloc((size_t)(H * W) * sizeof(double));
     if (!tmp) return 6;
     scan_state_map_dir(abar, bx, h, tmp, H, W, (flags & ORACLE_FLIP_H) != 0,
-                       (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0, NULL, NULL);
+                       (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0, NULL, NULL, NULL, NULL);
     free(tmp);
     return 0;
 }
@@ -148,10 +155,11 @@ static int forward_one_map(const double *x, const double *delta, const double *A
                            const double *B, const double *C, const double *D,
                            double *y_map, int64_t b, int64_t d, int64_t d_inner,
                            int64_t d_state, int64_t H, int64_t W, int flags,
-                           const double *h0m, double *hlm)
+                           const double *h0m, double *hlm, const double *g0m, double *glm)
 {
-    /* h0m, hlm (may be NULL): carried vertical states [d_state][W] of this map */
-    const int carries = (h0m != NULL) || (hlm != NULL);
+    /* h0m, hlm (may be NULL): carried vertical states [d_state][W] of this map;
+     * g0m, glm (may be NULL): carried horizontal states [d_state][H] */
+    const int carries = (h0m != NULL) || (hlm != NULL) || (g0m != NULL) || (glm != NULL);
     const int64_t L = H * W;
     const double *xm = x + (b * d_inner + d) * L;
     const double *dm = delta + (b * d_inner + d) * L;
@@ -175,7 +183,8 @@ static int forward_one_map(const double *x, const double *delta, const double *A
         if (flags == 0 && !carries) scan_state_map(abar, bx, h, hh_row, H, W);
         else scan_state_map_dir(abar, bx, h, hh_row, H, W, (flags & ORACLE_FLIP_H) != 0,
                                 (flags & ORACLE_FLIP_W) != 0, (flags & ORACLE_VFIRST) != 0,
-                                h0m ? h0m + n * W : NULL, hlm ? hlm + n * W : NULL);
+                                h0m ? h0m + n * W : NULL, hlm ? hlm + n * W : NULL,
+                                g0m ? g0m + n * H : NULL, glm ? glm + n * H : NULL);
         for (int64_t p = 0; p < L; ++p) y_map[p] += Cn[p] * h[p];
     }
     for (int64_t p = 0; p < L; ++p) y_map[p] += D[d] * xm[p];
@@ -194,7 +203,8 @@ static int forward_one_map(const double *x, const double *delta, const double *A
 static int fwd_maps(const double *x, const double *delta, const double *A, const double *B,
                     const double *C, const double *D, double *y, int64_t batch, int64_t d_inner,
                     int64_t d_state, int64_t H, int64_t W, const int64_t *maps, int64_t n_maps,
-                    int nthreads, int flags, const double *h0, double *hl)
+                    int nthreads, int flags, const double *h0, double *hl, const double *g0,
+                    double *gl)
 {
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
     const int64_t total = batch * d_inner;
@@ -214,7 +224,8 @@ static int fwd_maps(const double *x, const double *delta, const double *A, const
         const int64_t m = maps ? maps[k] : k;
         int s = forward_one_map(x, delta, A, B, C, D, y + k * H * W, m / d_inner,
                                 m % d_inner, d_inner, d_state, H, W, flags,
-                                h0 ? h0 + m * d_state * W : NULL, hl ? hl + m * d_state * W : NULL);
+                                h0 ? h0 + m * d_state * W : NULL, hl ? hl + m * d_state * W : NULL,
+                                g0 ? g0 + m * d_state * H : NULL, gl ? gl + m * d_state * H : NULL);
         if (s != 0) {
 #pragma omp atomic write
             status = s;
@@ -230,7 +241,7 @@ int oracle_ssm2d_fwd_maps_f64(const double *x, const double *delta, const double
                               int nthreads)
 {
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
-                    nthreads, 0, NULL, NULL);
+                    nthreads, 0, NULL, NULL, NULL, NULL);
 }
 
 /* The forward pass in the direction / order `flags` selects (ORACLE_FLIP_H,
@@ -243,7 +254,7 @@ int oracle_ssm2d_fwd_ex_f64(const double *x, const double *delta, const double *
 {
     if (flags < 0 || flags > 7) return 2;
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, maps, n_maps,
-                    nthreads, flags, NULL, NULL);
+                    nthreads, flags, NULL, NULL, NULL, NULL);
 }
 
 /* The forward pass with carried vertical states (all maps): h0 (may be NULL)
@@ -258,7 +269,26 @@ int oracle_ssm2d_fwd_carry_f64(const double *x, const double *delta, const doubl
 {
     if (flags < 0 || flags > 7) return 2;
     return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, NULL, 0,
-                    nthreads, flags, h0, hl);
+                    nthreads, flags, h0, hl, NULL, NULL);
+}
+
+/* The forward pass of one tile of a larger map (all maps): h0 / hl as in
+ * oracle_ssm2d_fwd_carry_f64 ([batch][d_inner][d_state][W], the vertical
+ * state before the first / after the last row in scan order), g0 / gl
+ * ([batch][d_inner][d_state][H], the horizontal state before the first /
+ * after the last column in scan order, by row); any may be NULL (zeros in,
+ * nothing out). Scanning a map tile by tile in scan order, each tile taking
+ * the carries its upper and left neighbours (in scan order) hand out, gives
+ * the scan of the whole map. */
+int oracle_ssm2d_fwd_tile_f64(const double *x, const double *delta, const double *A,
+                              const double *B, const double *C, const double *D,
+                              double *y, const double *h0, double *hl, const double *g0,
+                              double *gl, int64_t batch, int64_t d_inner, int64_t d_state,
+                              int64_t H, int64_t W, int nthreads, int flags)
+{
+    if (flags < 0 || flags > 7) return 2;
+    return fwd_maps(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, NULL, 0,
+                    nthreads, flags, h0, hl, g0, gl);
 }
 
 /* ---------------------------------------------------------------- backward

@@ -570,3 +570,140 @@ def test_carried_states_pin(oracle_lib):
                 _close(y2, y[:, :, rows[1]], 1e-12, f"second band from carried state {kw}")
                 y0 = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, h_init=np.zeros_like(h1), **kw)
                 _close(y0, y, 1e-15, f"zero carried state {kw}")
+
+
+def pin_carried_horizontal_states(oracle_lib):
+    """Scanning a map in two bands of columns, the second band (in scan order)
+    starting each row from the first band's last horizontal state, gives the
+    whole map's scan, in every direction and order; a zero carried state is
+    the plain scan."""
+    x, dt, A, B, C, D = _inputs(2, 3, 4, 7, 9, 43)
+    for fh in (False, True):
+        for fw in (False, True):
+            for vf in (False, True):
+                kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+                y = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, **kw)
+                cols = [slice(0, 4), slice(4, 9)]
+                if fw:
+                    cols = cols[::-1]  # scan order: right band first
+                band = lambda a, c: np.ascontiguousarray(a[..., c])
+                y1, g1 = oracle.fwd(band(x, cols[0]), band(dt, cols[0]), A, band(B, cols[0]), band(C, cols[0]), D,
+                                    lib=oracle_lib, return_last_col=True, **kw)
+                y2 = oracle.fwd(band(x, cols[1]), band(dt, cols[1]), A, band(B, cols[1]), band(C, cols[1]), D,
+                                lib=oracle_lib, hh_init=g1, **kw)
+                _close(y1, y[..., cols[0]], 1e-13, f"first band {kw}")
+                _close(y2, y[..., cols[1]], 1e-12, f"second band from carried row state {kw}")
+                y0 = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, hh_init=np.zeros_like(g1), **kw)
+                _close(y0, y, 1e-15, f"zero carried row state {kw}")
+
+
+def pin_tiles_with_both_carries(oracle_lib):
+    """A 2 x 2 tiling: each tile scanned with the vertical state of the tile
+    before it in row scan order and the horizontal state of the tile before
+    it in column scan order gives the whole map's scan, and the outer tiles'
+    last states match the whole map's (every direction and order)."""
+    x, dt, A, B, C, D = _inputs(1, 2, 3, 8, 10, 44)
+    for fh in (False, True):
+        for fw in (False, True):
+            for vf in (False, True):
+                kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+                y, hl, gl = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, return_last=True, return_last_col=True,
+                                       **kw)
+                rows = [slice(0, 3), slice(3, 8)]
+                cols = [slice(0, 6), slice(6, 10)]
+                if fh:
+                    rows = rows[::-1]
+                if fw:
+                    cols = cols[::-1]
+                tile = lambda a, r, c: np.ascontiguousarray(a[:, :, r, c])
+                hcarry = {}   # column band -> vertical state handed down
+                gcarry = {}   # row band -> horizontal state handed across
+                for ri, r in enumerate(rows):
+                    for ci, c in enumerate(cols):
+                        yt, ht, gt = oracle.fwd(tile(x, r, c), tile(dt, r, c), A, tile(B, r, c), tile(C, r, c), D,
+                                                lib=oracle_lib, h_init=hcarry.get(ci), hh_init=gcarry.get(ri),
+                                                return_last=True, return_last_col=True, **kw)
+                        _close(yt, y[:, :, r, c], 1e-12, f"tile {ri},{ci} {kw}")
+                        hcarry[ci], gcarry[ri] = ht, gt
+                        if ri == 1:
+                            _close(ht, hl[..., c], 1e-12, f"last vertical state, tile {ri},{ci} {kw}")
+                        if ci == 1:
+                            _close(gt, gl[..., r], 1e-12, f"last horizontal state, tile {ri},{ci} {kw}")
+
+
+def pin_carried_horizontal_state_closed_form(oracle_lib):
+    """With x = 0 (no input) and no skip term, a horizontal state g carried
+    into row r alone enters before the first column's decay: in the
+    horizontal-first order hh[r, j] = (prod of Abar[r, 0..j]) g and
+    h[i, j] = (prod of Abar[r+1..i, j]) hh[r, j] below it; in the vertical-
+    first order h[r, j] = (prod of Abar[r, 0..j]) g on row r only. The last
+    horizontal state is (prod of Abar over the row) g. Written out here from
+    the inputs, independently of the oracle's recurrences."""
+    b, d, n, H, W = 1, 2, 3, 5, 6
+    x, dt, A, B, C, D = _inputs(b, d, n, H, W, 45)
+    x[:] = 0.0
+    D[:] = 0.0
+    r = 2
+    g = np.zeros((b, d, n, H))
+    g[:, :, :, r] = np.random.default_rng(7).standard_normal((b, d, n))
+    for vf in (False, True):
+        y, gl = oracle.fwd(x, dt, A, B, C, D, lib=oracle_lib, vertical_first=vf, hh_init=g, return_last_col=True)
+        ref = np.zeros_like(y)
+        ref_gl = np.zeros_like(gl)
+        for dd in range(d):
+            for k in range(n):
+                abar = np.exp(dt[0, dd] * A[dd, k])                       # [H][W]
+                hh_r = np.cumprod(abar[r]) * g[0, dd, k, r]                # row r
+                ref_gl[0, dd, k, r] = np.prod(abar[r]) * g[0, dd, k, r]
+                h = np.zeros((H, W))
+                h[r] = hh_r
+                if not vf:
+                    for i in range(r + 1, H):
+                        h[i] = abar[i] * h[i - 1]
+                ref[0, dd] += C[0, k] * h
+        _close(y, ref, 1e-14, f"injected row state, vertical_first={vf}")
+        _close(gl, ref_gl, 1e-14, f"last row state, vertical_first={vf}")
+
+
+CARRY_PINS = [pin_carried_horizontal_states, pin_tiles_with_both_carries, pin_carried_horizontal_state_closed_form]
+
+
+@pytest.mark.parametrize("pin", CARRY_PINS, ids=lambda f: f.__name__)
+def test_carry_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+CARRY_MUTANTS = {
+    "row state indexed by the row's place in scan order":
+        ("double carry = g0 ? g0[i] : 0.0;              /* row recurrence first */",
+         "double carry = g0 ? g0[si] : 0.0;"),
+    "last row state taken at the first column":
+        ("                tmp[i * W + j] = carry;\n            }\n            if (gl) gl[i] = carry;",
+         "                tmp[i * W + j] = carry;\n            }\n            if (gl) gl[i] = tmp[i * W + (flip_w ? W - 1 : 0)];"),
+    "vertical-first row scan ignores the carried state":
+        ("double carry = g0 ? g0[i] : 0.0;\n", "double carry = 0.0;\n"),
+    "vertical-first last row state from the column scan":
+        ("                h[i * W + j] = carry;\n            }\n            if (gl) gl[i] = carry;",
+         "                h[i * W + j] = carry;\n            }\n            if (gl) gl[i] = tmp[i * W + (flip_w ? 0 : W - 1)];"),
+}
+
+
+def test_carry_pins_catch_planted_mistakes(tmp_path):
+    """Each mistake planted in the carried-row-state code of a copy of the
+    oracle fails one of the carry pins."""
+    with open(oracle._SRC) as f:
+        src = f.read()
+    for name, (old, new) in CARRY_MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site missing or ambiguous: {name}"
+        path = tmp_path / (str(abs(hash(name))) + ".c")
+        path.write_text(src.replace(old, new, 1))
+        lib_path = str(tmp_path / (str(abs(hash(name))) + ".so"))
+        oracle.build(out_path=lib_path, src_path=str(path))
+        lib = oracle.load(lib_path)
+        caught = []
+        for pin in CARRY_PINS:
+            try:
+                pin(lib)
+            except (AssertionError, RuntimeError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin caught the planted mistake: {name}"
