@@ -179,21 +179,32 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
  *              A map scanned in bands of rows, each band passed the previous
  *              band's h_last as h_init, gives the scan of the whole map (Mamba's
  *              last-state return, for maps processed in pieces).
+ *   carried    hh_init (may be NULL: zeros): per (b, d, n) and row, the state
+ *   row states the row recurrence starts from, before the first column in
+ *              scan order (hh, or h for SSM2D_VERTICAL_FIRST); hh_last (may be
+ *              NULL): the row recurrence's state after the last column; both
+ *              float32 [batch][d_inner][d_state][H], indexed by memory row.
+ *              A map scanned in bands of columns, each band passed the
+ *              previous band's (in scan order) hh_last as hh_init, gives the
+ *              scan of the whole map; with h_init / h_last too, tiles compose
+ *              the same way (each tile taking the carries of its upper and
+ *              left neighbours in scan order).
  * Arguments otherwise as for ssm2d_scan_fwd_ex, with the same flags (and
  * SSM2D_DELTA_SOFTPLUS). The gate applies to this call's result: with
  * SSM2D_FOUR_WAY it multiplies the four-corner sum (one more pass over y);
- * a gate with SSM2D_ACCUMULATE, or carried states with SSM2D_FOUR_WAY
+ * a gate with SSM2D_ACCUMULATE, carried states with SSM2D_FOUR_WAY, or
+ * carried row states with a gate, SSM2D_ACCUMULATE or SSM2D_FOUR_WAY
  * -> SSM2D_ERR_BAD_FLAGS. Gated single scans use 8 state groups and 4-column
- * strips, with the gate fused into the store. h_last is written only by a
- * kernel that did not time out (see ssm2d_sync_check). */
+ * strips, with the gate fused into the store. h_last and hh_last are written
+ * only by kernels that did not time out (see ssm2d_sync_check). */
 int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B,
                          const float *C, const float *D, const float *z, const float *delta_bias,
-                         const float *h_init, float *h_last, float *y, int64_t batch,
-                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
-                         void *stream);
+                         const float *h_init, float *h_last, const float *hh_init, float *hh_last,
+                         float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                         int64_t W, uint32_t flags, void *stream);
 
 /* bf16 variant: x, delta, B, C, z, y bfloat16 bits; A, D, delta_bias, h_init,
- * h_last float32. With a step-size bias or softplus, and for SSM2D_FOUR_WAY
+ * h_last, hh_init, hh_last float32. With a step-size bias or softplus, and for SSM2D_FOUR_WAY
  * (also through ssm2d_scan_fwd_ex_bf16), x, B and C are widened to fp32
  * (exactly) in library workspaces, the fp32 kernels compute the result in
  * an fp32 workspace (the four scans summed there), and y is rounded to bf16
@@ -202,8 +213,9 @@ int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, con
 int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
                               const uint16_t *B, const uint16_t *C, const float *D,
                               const uint16_t *z, const float *delta_bias, const float *h_init,
-                              float *h_last, uint16_t *y, int64_t batch, int64_t d_inner,
-                              int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
+                              float *h_last, const float *hh_init, float *hh_last, uint16_t *y,
+                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                              uint32_t flags, void *stream);
 
 /* ---- Backward pass -------------------------------------------------------
  *

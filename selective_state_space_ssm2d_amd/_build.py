@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # one translation unit per (input type, lane layout or mode)
 _VARIANTS = ("g4", "g8", "flipw", "vfirst", "flipw_vfirst", "acc", "flipw_acc", "vfirst_acc", "flipw_vfirst_acc",
-             "states", "bwd", "bwd_edges", "states_flipw", "bwd_ltr", "bwd_ltr_edges", "gate", "gate_flipw", "fast")
+             "states", "bwd", "bwd_edges", "states_flipw", "bwd_ltr", "bwd_ltr_edges", "gate", "gate_flipw", "fast",
+             "rowc", "rowc_vfirst")
 SOURCES = ["ssm2d.hip"] + [f"scan2d_{t}_{v}.hip" for t in ("f32", "bf16") for v in _VARIANTS]
 LIB = os.path.join(PKG, "libssm2d.so")
 INCLUDE = os.path.join(ROOT, "include")

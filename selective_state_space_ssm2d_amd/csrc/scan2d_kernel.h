@@ -75,6 +75,10 @@ constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + 
 //   kModeEdges       (with kModeBackward) chains cross workgroups without
 //                    courier waves: boundary strips use the global ring
 //                    themselves
+//   kModeRowCarry    (forward, not accumulating or gated) carried horizontal
+//                    states: each row's recurrence starts from hh_init and
+//                    its state after the last column goes to hh_last (a band
+//                    of columns continuing a scan)
 constexpr int kModeFlipW = 1;
 constexpr int kModeVFirst = 2;
 constexpr int kModeAccumulate = 4;
@@ -82,6 +86,7 @@ constexpr int kModeStates = 8;
 constexpr int kModeBackward = 16;
 constexpr int kModeGate = 32;
 constexpr int kModeEdges = 64;
+constexpr int kModeRowCarry = 128;
 
 // Waves per workgroup: 10 (up to 3 per SIMD) when a lane's register state is
 // small (8 state groups, K * NPL <= 16; K * NPL <= 8 for the stored-state
@@ -145,6 +150,8 @@ struct Params {
     // null): before the first row in scan order, and after the last row
     const float *h_init;
     float *h_last;
+    const float *hh_init;              // carried horizontal states [b][d][n][H] (kModeRowCarry)
+    float *hh_last;
     long long spin_limit;
 };
 
@@ -687,7 +694,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool BWD = (MODE & kModeBackward) != 0;
     constexpr bool GATE = (MODE & kModeGate) != 0;
     constexpr bool EDGES = (MODE & kModeEdges) != 0;
+    constexpr bool RC = (MODE & kModeRowCarry) != 0;
     static_assert(!EDGES || BWD, "courier-free chains: adjoint pass only");
+    static_assert(!RC || (!ACC && !GATE && !STATES && !BWD), "carried row states: plain forward output only");
     static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
     static_assert(!BWD || (!VF && !ACC && !STATES && K == 4 && G == 8), "backward: one layout");
     static_assert(!BWD || !COOP || EDGES, "backward with the shared row ring: courier-free chains only");
@@ -969,6 +978,17 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             idx = ((static_cast<long>(b) * p.d_inner + d) * p.d_state + n) * W + (FW ? W - 1 - u : u);
             return d_ok && n < p.d_state && u < W;
         };
+        // Carried horizontal state of scan row t (kModeRowCarry): element
+        // [b][d][n][memory row] of hh_init / hh_last.
+        auto row_carry_index = [&](const int t, const int k, long &idx) -> bool {
+            const int n = g * NPL + k;
+            idx = ((static_cast<long>(b) * p.d_inner + d) * p.d_state + n) * H + (p.flip_h ? H - 1 - t : t);
+            return d_ok && n < p.d_state && t < H;
+        };
+        // the chain's first strip reads the rows' carried states, its last
+        // strip writes them (with the row's inputs / after the row's chain)
+        const bool rc_in = RC && p.hh_init && strip == 0;
+        const bool rc_out = RC && p.hh_last && strip + 1 == p.nstrips;
         if constexpr (!STATES && !BWD) {
             if (p.h_init) {
 #pragma unroll
@@ -1129,6 +1149,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     const float *src_c = ring_in + (static_cast<long>(i & RM) * kWave + lane) * NPL;
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
+                } else if constexpr (RC) {
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) hh[k] = hcur[k].x;  // the row's carried state (or 0)
                 } else {
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
@@ -1283,6 +1306,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (LEFT) lds_poke(&s_used[wave], i + 1);
+                if constexpr (RC && !RIGHT && !RIGHT_G) {
+                    if (rc_out && !timed_out) {
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            long idx;
+                            if (row_carry_index(i, k, idx)) p.hh_last[idx] = hh[k];
+                        }
+                    }
+                }
                 // C of the forward's row: read once the carry is handed on
                 // (needed only for the output sum; read with B, it held 16
                 // more registers across the carry wait and spilled)
@@ -1458,6 +1490,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                             hb[s][k] = *reinterpret_cast<const float4 *>(
                                 t < H ? hlast - static_cast<long>(t) * TILE + k * kWave * 4 : zeros_f);
                     }
+                    if constexpr (RC) {
+                        // (hb holds the row's carried horizontal state in .x)
+#pragma unroll
+                        for (int k = 0; k < NPL; ++k) {
+                            long idx;
+                            const bool ok = rc_in && row_carry_index(first + s, k, idx);
+                            hb[s][k] = make_float4(ok ? p.hh_init[idx] : 0.0f, 0.0f, 0.0f, 0.0f);
+                        }
+                    }
                 }
             };
             if constexpr (COOP) {
@@ -1575,6 +1616,8 @@ struct Plan {
     const void *z;   // gate input (kModeGate)
     const float *h_init;  // carried vertical states in / out (may be null)
     float *h_last;
+    const float *hh_init;  // carried horizontal states in / out (kModeRowCarry; may be null)
+    float *hh_last;
     // Workspace of fixed size to launch in (null: the per-(device, stream)
     // workspace, grown as needed)
     const struct WsEntry *fixed_ws;
@@ -1726,6 +1769,8 @@ inline Params make_params(const void *x, const void *delta, const float *A, cons
     prm.z = pl.z;
     prm.h_init = pl.h_init;
     prm.h_last = pl.h_last;
+    prm.hh_init = pl.hh_init;
+    prm.hh_last = pl.hh_last;
     prm.coop_slots = pl.coop_slots > 0 ? pl.coop_slots : 2;
     prm.coop_shift = 0;
     while ((1 << prm.coop_shift) < prm.coop_slots) ++prm.coop_shift;
@@ -1851,7 +1896,11 @@ bool fast_path_taken<uint16_t>(const Plan &pl, int align);
     SSM2D_DISPATCH_DECL(TT, dispatch_gate)             \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_vfirst)      \
     SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw)       \
-    SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw_vfirst)
+    SSM2D_DISPATCH_DECL(TT, dispatch_gate_flipw_vfirst) \
+    SSM2D_DISPATCH_DECL(TT, dispatch_rowc)             \
+    SSM2D_DISPATCH_DECL(TT, dispatch_rowc_flipw)       \
+    SSM2D_DISPATCH_DECL(TT, dispatch_rowc_vfirst)      \
+    SSM2D_DISPATCH_DECL(TT, dispatch_rowc_flipw_vfirst)
 SSM2D_MODE_DECLS(float)
 SSM2D_MODE_DECLS(uint16_t)
 #undef SSM2D_MODE_DECLS

@@ -561,13 +561,16 @@ template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
            const T *z = nullptr, const float *h_init = nullptr, float *h_last = nullptr,
-           const WsEntry *fixed_ws = nullptr)
+           const WsEntry *fixed_ws = nullptr, const float *hh_init = nullptr, float *hh_last = nullptr)
 {
+    if (hh_init || hh_last) mode |= kModeRowCarry;
     Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
     pl.flip_h = flip_h;
     pl.z = z;
     pl.h_init = h_init;
     pl.h_last = h_last;
+    pl.hh_init = hh_init;
+    pl.hh_last = hh_last;
     pl.fixed_ws = fixed_ws;
     const int bi = static_cast<int>(batch), di = static_cast<int>(d_inner), ni = static_cast<int>(d_state);
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
@@ -593,6 +596,10 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     case kModeGate | VF: return dispatch_gate_vfirst(SSM2D_ARGS);
     case kModeGate | FW: return dispatch_gate_flipw(SSM2D_ARGS);
     case kModeGate | FW | VF: return dispatch_gate_flipw_vfirst(SSM2D_ARGS);
+    case kModeRowCarry: return dispatch_rowc(SSM2D_ARGS);
+    case kModeRowCarry | FW: return dispatch_rowc_flipw(SSM2D_ARGS);
+    case kModeRowCarry | VF: return dispatch_rowc_vfirst(SSM2D_ARGS);
+    case kModeRowCarry | FW | VF: return dispatch_rowc_flipw_vfirst(SSM2D_ARGS);
     default: return SSM2D_ERR_UNSUPPORTED;
     }
 #undef SSM2D_ARGS
@@ -613,7 +620,7 @@ template <typename T>
 int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
              void *stream, const T *z = nullptr, const float *delta_bias = nullptr, const float *h_init = nullptr,
-             float *h_last = nullptr);
+             float *h_last = nullptr, const float *hh_init = nullptr, float *hh_last = nullptr);
 
 // bf16 calls whose result is more than one scan's rounded output (the
 // four-corner sums) or whose scan runs on a computed step size (bias,
@@ -623,7 +630,8 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 int scan_fwd_widened(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B, const uint16_t *C,
                      const float *D, uint16_t *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
                      int64_t W, unsigned flags, void *stream, const uint16_t *z, const float *delta_bias,
-                     const float *h_init, float *h_last, int dev)
+                     const float *h_init, float *h_last, int dev,
+                     const float *hh_init, float *hh_last)
 {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const long total = batch * d_inner * H * W, tb = batch * d_state * H * W;
@@ -648,7 +656,8 @@ int scan_fwd_widened(const uint16_t *x, const uint16_t *delta, const float *A, c
     }
     if ((flags & SSM2D_ACCUMULATE) && (st = widen(y, y32, total, s)) != SSM2D_OK) return st;
     st = scan_fwd<float>(x32, d32, A, d_state ? B32 : nullptr, d_state ? C32 : nullptr, D, y32, batch, d_inner,
-                         d_state, H, W, flags & ~SSM2D_DELTA_SOFTPLUS, true, stream, nullptr, nullptr, h_init, h_last);
+                         d_state, H, W, flags & ~SSM2D_DELTA_SOFTPLUS, true, stream, nullptr, nullptr, h_init, h_last,
+                         hh_init, hh_last);
     if (st != SSM2D_OK) return st;
     return gate_or_round<float, uint16_t>(y32, z, y, total, s);
 }
@@ -658,13 +667,16 @@ int scan_fwd_widened(const uint16_t *x, const uint16_t *delta, const float *A, c
 template <typename T>
 int check_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *y,
               int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
-              const T *z, const float *delta_bias, const float *h_init, const float *h_last, bool *work)
+              const T *z, const float *delta_bias, const float *h_init, const float *h_last, bool *work,
+              const float *hh_init = nullptr, const float *hh_last = nullptr)
 {
     *work = false;
     if ((flags & ~kKnownFlags) != 0) return SSM2D_ERR_BAD_FLAGS;
     if ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))) return SSM2D_ERR_BAD_FLAGS;
     if (z && (flags & SSM2D_ACCUMULATE)) return SSM2D_ERR_BAD_FLAGS;
     if ((h_init || h_last) && (flags & SSM2D_FOUR_WAY)) return SSM2D_ERR_BAD_FLAGS;
+    // carried horizontal states: plain (not accumulated, not gated) single scans
+    if ((hh_init || hh_last) && (z || (flags & (SSM2D_FOUR_WAY | SSM2D_ACCUMULATE)))) return SSM2D_ERR_BAD_FLAGS;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (batch == 0 || d_inner == 0 || H == 0 || W == 0) return SSM2D_OK;
     if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
@@ -673,7 +685,8 @@ int check_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C
         return SSM2D_ERR_UNSUPPORTED;
     if (!x || !delta || (!D && !extended) || !y || (d_state > 0 && (!A || !B || !C))) return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(D) || misaligned(y) || misaligned(z) ||
-        misaligned(delta_bias) || misaligned(h_init) || misaligned(h_last) ||
+        misaligned(delta_bias) || misaligned(h_init) || misaligned(h_last) || misaligned(hh_init) ||
+        misaligned(hh_last) ||
         (d_state > 0 && (misaligned(A) || misaligned(B) || misaligned(C))))
         return SSM2D_ERR_MISALIGNED;
     *work = true;
@@ -685,11 +698,12 @@ int check_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C
 template <typename T>
 int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y,
              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, bool extended,
-             void *stream, const T *z, const float *delta_bias, const float *h_init, float *h_last)
+             void *stream, const T *z, const float *delta_bias, const float *h_init, float *h_last,
+             const float *hh_init, float *hh_last)
 {
     bool work = false;
     const int chk = check_fwd(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, extended, z, delta_bias,
-                              h_init, h_last, &work);
+                              h_init, h_last, &work, hh_init, hh_last);
     if (chk != SSM2D_OK || !work) return chk;
 
     int dev = 0;
@@ -699,7 +713,7 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if constexpr (std::is_same<T, uint16_t>::value) {
         if ((flags & SSM2D_FOUR_WAY) || delta_bias || (flags & SSM2D_DELTA_SOFTPLUS))
             return scan_fwd_widened(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, stream, z,
-                                    delta_bias, h_init, h_last, dev);
+                                    delta_bias, h_init, h_last, dev, hh_init, hh_last);
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const long total = batch * d_inner * H * W;
@@ -723,7 +737,7 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (!(flags & SSM2D_FOUR_WAY)) {
         const int mode = ((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc | (z ? kModeGate : 0);
         return launch(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, mode, (flags & SSM2D_FLIP_H) ? 1 : 0,
-                      dev, stream, z, h_init, h_last);
+                      dev, stream, z, h_init, h_last, nullptr, hh_init, hh_last);
     }
     // (fp32 only) four scans, one per starting corner, summed into y in
     // stream order; the skip term is added once, by the first.
@@ -1087,20 +1101,21 @@ int ssm2d_scan_fwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
 
 int ssm2d_scan_fwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
                          const float *D, const float *z, const float *delta_bias, const float *h_init,
-                         float *h_last, float *y, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-                         int64_t W, uint32_t flags, void *stream)
+                         float *h_last, const float *hh_init, float *hh_last, float *y, int64_t batch,
+                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
     return scan_fwd<float>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z, delta_bias,
-                           h_init, h_last);
+                           h_init, h_last, hh_init, hh_last);
 }
 
 int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
                               const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
-                              const float *h_init, float *h_last, uint16_t *y, int64_t batch, int64_t d_inner,
-                              int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+                              const float *h_init, float *h_last, const float *hh_init, float *hh_last, uint16_t *y,
+                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
+                              void *stream)
 {
     return scan_fwd<uint16_t>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, flags, true, stream, z,
-                              delta_bias, h_init, h_last);
+                              delta_bias, h_init, h_last, hh_init, hh_last);
 }
 
 int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B, const float *C,

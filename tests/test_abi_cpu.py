@@ -103,7 +103,7 @@ def test_ex_flag_validation(lib, bf16):
 
 def _call_mamba(lib, dims, flags, ptrs=None, bf16=False):
     ptrs = ptrs if ptrs is not None else [FAKE] * 9
-    ptrs = ptrs[:8] + [0, 0] + ptrs[8:]  # no carried states
+    ptrs = ptrs[:8] + [0, 0, 0, 0] + ptrs[8:]  # no carried states
     fn = lib.ssm2d_scan_fwd_mamba_bf16 if bf16 else lib.ssm2d_scan_fwd_mamba
     return fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
 
@@ -132,11 +132,21 @@ def test_mamba_entry_validation(lib, bf16):
     # carried states: optional, aligned, not with the four-corner sum
     fn = lib.ssm2d_scan_fwd_mamba_bf16 if bf16 else lib.ssm2d_scan_fwd_mamba
     base = [FAKE] * 6 + [0, 0]
-    call = lambda hi, hl, flags: fn(*(ctypes.c_void_p(p) for p in base + [hi, hl, FAKE]), 1, 2, 3, 4, 5, flags, None)
+    call = lambda hi, hl, flags: fn(*(ctypes.c_void_p(p) for p in base + [hi, hl, 0, 0, FAKE]), 1, 2, 3, 4, 5, flags,
+                                    None)
     assert call(FAKE, FAKE, pkg.FOUR_WAY) == pkg.ERR_BAD_FLAGS
     assert call(FAKE + 4, 0, 0) == pkg.ERR_MISALIGNED and call(0, FAKE + 4, 0) == pkg.ERR_MISALIGNED
     assert call(FAKE, FAKE, pkg.FLIP_H | pkg.VERTICAL_FIRST) not in (pkg.ERR_BAD_FLAGS, pkg.ERR_MISALIGNED,
                                                                      pkg.ERR_NULLPTR)
+    # carried row states: optional, aligned, not with a gate, accumulation or the four-corner sum
+    rcall = lambda gi, gl, z, flags: fn(*(ctypes.c_void_p(p) for p in [FAKE] * 6 + [z, 0, 0, 0, gi, gl, FAKE]),
+                                        1, 2, 3, 4, 5, flags, None)
+    for flags in (pkg.FOUR_WAY, pkg.ACCUMULATE):
+        assert rcall(FAKE, 0, 0, flags) == pkg.ERR_BAD_FLAGS and rcall(0, FAKE, 0, flags) == pkg.ERR_BAD_FLAGS
+    assert rcall(FAKE, FAKE, FAKE, 0) == pkg.ERR_BAD_FLAGS  # gated
+    assert rcall(FAKE + 4, 0, 0, 0) == pkg.ERR_MISALIGNED and rcall(0, FAKE + 4, 0, 0) == pkg.ERR_MISALIGNED
+    assert rcall(FAKE, FAKE, 0, pkg.FLIP_H | pkg.FLIP_W | pkg.VERTICAL_FIRST | pkg.DELTA_SOFTPLUS) not in (
+        pkg.ERR_BAD_FLAGS, pkg.ERR_MISALIGNED, pkg.ERR_NULLPTR)
 
 
 def test_ex_null_and_misaligned(lib):

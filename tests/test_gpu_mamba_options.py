@@ -196,3 +196,100 @@ def test_gate_shared_row_ring(dtype):
     y = pkg.scan_fwd_mamba(*to_dev(t, dtype), z=z_dev, flip_w=True)
     pkg.sync_check()
     check(as_f64(y), oracle.fwd_mamba(*(t[k] for k in KEYS), z=z, flip_w=True), dtype, "gated row ring")
+
+
+# Carried row states (bands of columns): shapes with several strips and
+# channel blocks, ragged rows, chains across workgroups (forced 1- and
+# 2-strip workgroups), 8-column strips, one row and one column.
+ROW_CARRY_CASES = [((1, 16, 16, 9, 64), None), ((2, 9, 8, 7, 23), None), ((1, 8, 16, 13, 90), "2"),
+                   ((1, 16, 16, 6, 40), "1"), ((2, 16, 8, 5, 44), "K8"), ((1, 8, 4, 1, 30), None),
+                   ((1, 5, 16, 27, 1), None)]
+
+
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)), ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ROW_CARRY_CASES, ids=str)
+def test_carried_row_states(case, dtype, d, monkeypatch):
+    """A seeded hh_init (the row recurrence's state before the first column in
+    scan order) and the returned hh_last against the oracle, with h_init /
+    h_last too, in every direction and order."""
+    shape, opt = case
+    if opt == "K8":
+        monkeypatch.setenv("SSM2D_STRIP", "8")
+    elif opt:
+        monkeypatch.setenv("SSM2D_WAVES", opt)
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    _say(f"carried row states {shape} {opt} {dtype} {d}")
+    t = make_random_inputs(*shape, seed=_seed(shape) + 51, dtype=dtype)
+    b, di, n, H, W = shape
+    rng = np.random.default_rng(_seed(shape) + 52)
+    g0 = rng.standard_normal((b, di, n, H)).astype(np.float32)
+    h0 = rng.standard_normal((b, di, n, W)).astype(np.float32)
+    y, gl = pkg.scan_fwd_mamba(*to_dev(t, dtype), hh_init=torch.from_numpy(g0).cuda(), return_last_row_state=True,
+                               **kw)
+    pkg.sync_check()
+    ref_y, ref_gl = oracle.fwd(*(t[k] for k in KEYS), hh_init=g0, return_last_col=True, **kw)
+    check(as_f64(y), ref_y, dtype, f"row-carried y {shape} {d}")
+    check(gl.double().cpu().numpy(), ref_gl, "f32", f"hh_last {shape} {d}")
+    y, hl, gl = pkg.scan_fwd_mamba(*to_dev(t, dtype), h_init=torch.from_numpy(h0).cuda(),
+                                   hh_init=torch.from_numpy(g0).cuda(), return_last_state=True,
+                                   return_last_row_state=True, **kw)
+    pkg.sync_check()
+    ref_y, ref_hl, ref_gl = oracle.fwd(*(t[k] for k in KEYS), h_init=h0, hh_init=g0, return_last=True,
+                                       return_last_col=True, **kw)
+    check(as_f64(y), ref_y, dtype, f"tile y {shape} {d}")
+    check(hl.double().cpu().numpy(), ref_hl, "f32", f"tile h_last {shape} {d}")
+    check(gl.double().cpu().numpy(), ref_gl, "f32", f"tile hh_last {shape} {d}")
+
+
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)), ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+def test_tiles_equal_whole_map(d):
+    """A 2 x 2 tiling scanned tile by tile in scan order, each tile taking the
+    carries its neighbours handed out, gives the whole map's scan (GPU
+    against the oracle), in every direction and order."""
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    shape = (1, 16, 16, 37, 70)
+    t = make_random_inputs(*shape, seed=53)
+    args = to_dev(t, "f32")
+    ref = oracle.fwd(*(t[k] for k in KEYS), **kw)
+    rows = [slice(0, 15), slice(15, 37)]
+    cols = [slice(0, 28), slice(28, 70)]
+    if fh:
+        rows = rows[::-1]
+    if fw:
+        cols = cols[::-1]
+    tile = lambda a, r, c: a[:, :, r, c].contiguous()
+    hcarry, gcarry = {}, {}
+    for ri, r in enumerate(rows):
+        for ci, c in enumerate(cols):
+            a = [tile(args[0], r, c), tile(args[1], r, c), args[2], tile(args[3], r, c), tile(args[4], r, c), args[5]]
+            yt, ht, gt = pkg.scan_fwd_mamba(*a, h_init=hcarry.get(ci), hh_init=gcarry.get(ri), return_last_state=True,
+                                            return_last_row_state=True, **kw)
+            pkg.sync_check()
+            hcarry[ci], gcarry[ri] = ht, gt
+            check(as_f64(yt), ref[:, :, r, c], "f32", f"tile {ri},{ci} {d}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_carried_row_states_with_step_options(dtype):
+    """Carried row states with a step-size bias and softplus (the bf16 call
+    then runs the fp32 kernels on widened inputs)."""
+    shape = (2, 16, 16, 11, 36)
+    t = make_random_inputs(*shape, seed=54, dtype=dtype)
+    b, di, n, H, W = shape
+    rng = np.random.default_rng(55)
+    raw, raw_dev = _tensor(rng.standard_normal(t["x"].shape), dtype)
+    bias = rng.standard_normal(di).astype(np.float32) * 0.5
+    g0 = rng.standard_normal((b, di, n, H)).astype(np.float32)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    y, gl = pkg.scan_fwd_mamba(*args, delta_bias=torch.from_numpy(bias).cuda(), delta_softplus=True,
+                               hh_init=torch.from_numpy(g0).cuda(), return_last_row_state=True, flip_w=True)
+    pkg.sync_check()
+    dt = oracle.softplus(raw + bias[None, :, None, None].astype(np.float64))
+    ref_y, ref_gl = oracle.fwd(t["x"], dt, t["A"], t["B"], t["C"], t["D"], hh_init=g0, return_last_col=True,
+                               flip_w=True)
+    check(as_f64(y), ref_y, dtype, "row-carried y with step options")
+    check(gl.double().cpu().numpy(), ref_gl, "f32", "hh_last with step options")
