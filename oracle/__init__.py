@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH):
     lib.oracle_ssm2d_fwd_tile_f64.argtypes = [dp] * 11 + [i64] * 5 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_ssm2d_fwd_tile_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_bwd_f64.argtypes = [dp] * 13 + [i64] * 5 + [ctypes.c_int]
+    lib.oracle_ssm2d_bwd_carry_f64.argtypes = [dp] * 16 + [i64] * 5 + [ctypes.c_int]
+    lib.oracle_ssm2d_bwd_carry_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_bwd_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -256,7 +258,8 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
     return g
 
 
-def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False, vertical_first=False):
+def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False, vertical_first=False,
+        h_init=None, dh_last=None):
     """Gradients of the forward pass (fp64) for upstream gradient dy (shape of
     y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input.
     flip_h / flip_w: of the scan in that direction, which is the upper-left
@@ -266,8 +269,17 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
     (cell (i, j) becomes (j, i); a flip of the rows becomes a flip of the
     columns and the other way round), so its gradients are the transposed
     map's, transposed back. Both identities are permutations of the cells;
-    the finite-difference pins check the results independently."""
+    the finite-difference pins check the results independently.
+
+    h_init / dh_last ([batch][d_inner][d_state][W], may be None): the
+    backward of the forward with a carried vertical state h_init, for the
+    loss sum(dy * y) + sum(dh_last * h_last); the result then also holds
+    dh_init, shaped like h_init (horizontal-first order only: in the
+    vertical-first order the carried state is the transposed map's row
+    state)."""
+    carry = h_init is not None or dh_last is not None
     if vertical_first:
+        assert not carry, "carried states: horizontal-first order only"
         tr = lambda a: np.ascontiguousarray(np.swapaxes(np.asarray(a, dtype=np.float64), 2, 3))
         g = bwd(tr(x), tr(delta), A, tr(B), tr(C), D, tr(dy), nthreads, lib, flip_h=flip_w, flip_w=flip_h)
         for k in ("dx", "ddelta", "dB", "dC"):
@@ -276,9 +288,18 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
     if flip_h or flip_w:
         ax = tuple(a for a, f in ((2, flip_h), (3, flip_w)) if f)
         fl = lambda a: np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), ax))
-        g = bwd(fl(x), fl(delta), A, fl(B), fl(C), D, fl(dy), nthreads, lib)
+
+        def flc(a):  # carried states are per column: mirrored with the columns only
+            if a is None or not flip_w:
+                return a
+            return np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 3))
+
+        g = bwd(fl(x), fl(delta), A, fl(B), fl(C), D, fl(dy), nthreads, lib, h_init=flc(h_init),
+                dh_last=flc(dh_last))
         for k in ("dx", "ddelta", "dB", "dC"):
             g[k] = fl(g[k])
+        if "dh_init" in g:
+            g["dh_init"] = flc(g["dh_init"])
         return g
     lib = lib or _get()
     x, delta, A, B, C, D, dy = map(_f64, (x, delta, A, B, C, D, dy))
@@ -289,6 +310,20 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
     assert B.shape == (batch, d_state, H, W) and C.shape == B.shape
     out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty_like(A),
            "dB": np.empty_like(B), "dC": np.empty_like(C), "dD": np.empty_like(D)}
+    if carry:
+        cshape = (batch, d_inner, d_state, W)
+        h0 = None if h_init is None else _f64(h_init)
+        gl = None if dh_last is None else _f64(dh_last)
+        assert (h0 is None or h0.shape == cshape) and (gl is None or gl.shape == cshape)
+        out["dh_init"] = np.empty(cshape, dtype=np.float64)
+        null = ctypes.POINTER(ctypes.c_double)()
+        s = lib.oracle_ssm2d_bwd_carry_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+                                           null if h0 is None else _ptr(h0), null if gl is None else _ptr(gl),
+                                           *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")),
+                                           _ptr(out["dh_init"]), batch, d_inner, d_state, H, W, int(nthreads))
+        if s != 0:
+            raise RuntimeError(f"oracle failed with status {s}")
+        return out
     s = lib.oracle_ssm2d_bwd_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
                                  *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")),
                                  batch, d_inner, d_state, H, W, int(nthreads))

@@ -312,8 +312,13 @@ int oracle_ssm2d_fwd_tile_f64(const double *x, const double *delta, const double
 static void backward_one_map(const double *xm, const double *dm, double a_dn, const double *Bn,
                              const double *Cn, const double *dym, double *dxm, double *ddm,
                              double *dBn, double *dCn, double *dA_dn, int64_t H, int64_t W,
-                             double *a, double *u, double *hh, double *h, double *gh, double *ghh)
+                             double *a, double *u, double *hh, double *h, double *gh, double *ghh,
+                             const double *h0, const double *gl, double *dh0)
 {
+    /* h0 (may be NULL: zeros): the carried vertical state above row 0 ([W]);
+     * gl (may be NULL: zeros): dL/dh of the state after the last row, which
+     * the forward hands out (h of row H-1); dh0 (may be NULL): receives
+     * dL/dh0 = a[0,j] g_h[0,j], h0 entering row 0 through its decay. */
     const int64_t L = H * W;
     for (int64_t p = 0; p < L; ++p) {
         a[p] = exp(dm[p] * a_dn);
@@ -326,16 +331,19 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
             hh[i * W + j] = a[i * W + j] * left + u[i * W + j];
         }
         for (int64_t j = 0; j < W; ++j) {
-            const double up = (i > 0) ? h[(i - 1) * W + j] : 0.0;
+            const double up = (i > 0) ? h[(i - 1) * W + j] : (h0 ? h0[j] : 0.0);
             h[i * W + j] = a[i * W + j] * up + hh[i * W + j];
         }
     }
-    /* adjoint of the vertical scan: bottom to top */
+    /* adjoint of the vertical scan: bottom to top (the last row also feeds
+     * the handed-out state) */
     for (int64_t i = H - 1; i >= 0; --i)
         for (int64_t j = 0; j < W; ++j) {
-            const double below = (i + 1 < H) ? a[(i + 1) * W + j] * gh[(i + 1) * W + j] : 0.0;
+            const double below = (i + 1 < H) ? a[(i + 1) * W + j] * gh[(i + 1) * W + j] : (gl ? gl[j] : 0.0);
             gh[i * W + j] = dym[i * W + j] * Cn[i * W + j] + below;
         }
+    if (dh0)
+        for (int64_t j = 0; j < W; ++j) dh0[j] = (H > 0) ? a[j] * gh[j] : (gl ? gl[j] : 0.0);
     /* adjoint of the horizontal scan: right to left along each row */
     for (int64_t i = 0; i < H; ++i)
         for (int64_t j = W - 1; j >= 0; --j) {
@@ -348,7 +356,7 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
         for (int64_t j = 0; j < W; ++j) {
             const int64_t p = i * W + j;
             const double left = (j > 0) ? hh[p - 1] : 0.0;
-            const double up = (i > 0) ? h[p - W] : 0.0;
+            const double up = (i > 0) ? h[p - W] : (h0 ? h0[j] : 0.0);
             const double g_a = ghh[p] * left + gh[p] * up;
             const double g_u = ghh[p];
             ddm[p] += g_a * a_dn * a[p] + g_u * Bn[p] * xm[p];
@@ -366,11 +374,11 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
  * of the same shapes, overwritten. OpenMP over batch entries; the per-entry
  * dA and dD parts are added in batch order, so results do not depend on the
  * thread count. Returns 0, 2 on a bad size, 6 on allocation failure. */
-int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, const double *B,
-                         const double *C, const double *D, const double *dy, double *dx,
-                         double *ddelta, double *dA, double *dB, double *dC, double *dD,
-                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                         int nthreads)
+static int bwd_maps(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *dy, double *dx,
+                    double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                    int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                    int nthreads, const double *h0, const double *gl, double *dh0)
 {
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
     const int64_t L = H * W;
@@ -404,10 +412,12 @@ int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, 
             const int64_t m = (b * d_inner + d) * L;
             for (int64_t n = 0; n < d_state; ++n) {
                 const int64_t q = (b * d_state + n) * L;
+                const int64_t c = ((b * d_inner + d) * d_state + n) * W;  /* carried-state row */
                 backward_one_map(x + m, delta + m, A[d * d_state + n], B + q, C + q, dy + m,
                                  dx + m, ddelta + m, dB + q, dC + q,
                                  dA_b + (b * d_inner + d) * d_state + n, H, W,
-                                 buf, buf + L, buf + 2 * L, buf + 3 * L, buf + 4 * L, buf + 5 * L);
+                                 buf, buf + L, buf + 2 * L, buf + 3 * L, buf + 4 * L, buf + 5 * L,
+                                 h0 ? h0 + c : NULL, gl ? gl + c : NULL, dh0 ? dh0 + c : NULL);
             }
             double s = 0.0;
             for (int64_t p = 0; p < L; ++p) {
@@ -427,6 +437,35 @@ int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, 
     free(dA_b);
     free(dD_b);
     return status;
+}
+
+int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, const double *B,
+                         const double *C, const double *D, const double *dy, double *dx,
+                         double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                         int nthreads)
+{
+    return bwd_maps(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                    nthreads, NULL, NULL, NULL);
+}
+
+/* The backward pass of the forward with carried vertical states: h0 (may be
+ * NULL) the state above row 0 the forward started from, gl (may be NULL)
+ * dL/dh_last for the state it handed out after the last row, dh0 (may be
+ * NULL) receives dL/dh0; all [batch][d_inner][d_state][W]. Otherwise as
+ * oracle_ssm2d_bwd_f64. */
+int oracle_ssm2d_bwd_carry_f64(const double *x, const double *delta, const double *A, const double *B,
+                               const double *C, const double *D, const double *dy, const double *h0,
+                               const double *gl, double *dx, double *ddelta, double *dA, double *dB,
+                               double *dC, double *dD, double *dh0, int64_t batch, int64_t d_inner,
+                               int64_t d_state, int64_t H, int64_t W, int nthreads)
+{
+    if (dh0 && batch >= 0 && d_inner >= 0 && d_state >= 0 && W >= 0 && H == 0) {
+        /* no rows: the handed-out state is h0 itself */
+        for (int64_t k = 0; k < batch * d_inner * d_state * W; ++k) dh0[k] = gl ? gl[k] : 0.0;
+    }
+    return bwd_maps(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                    nthreads, h0, gl, dh0);
 }
 
 /* Number of threads the OpenMP runtime would use (1 without OpenMP). */

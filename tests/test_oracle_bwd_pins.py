@@ -226,3 +226,95 @@ def test_vertical_first_backward_finite_differences(oracle_lib):
                 fd[idx] = (lp - lm) / (2 * h)
             err = np.max(np.abs(g[GRAD[k]] - fd) / (1.0 + np.abs(fd)))
             assert err < 1e-6, f"{GRAD[k]} vertical-first flips {fh},{fw}: {err:.2e}"
+
+
+# ---------------------------------------------------------------- carried vertical states
+def pin_carried_state_finite_differences(lib):
+    """The backward of the forward with a carried vertical state, for the loss
+    L = sum(dy * y) + sum(g * h_last), in every corner: every gradient
+    element (h_init's too) against a central difference of L computed with
+    the forward pass."""
+    shape, seed = (1, 2, 3, 4, 5), 38
+    for fh in (False, True):
+        for fw in (False, True):
+            ins = _inputs(*shape, seed)
+            r = np.random.default_rng(seed + 2 * fh + fw)
+            b, d, n, H, W = shape
+            ins["h_init"] = r.standard_normal((b, d, n, W))
+            dy = r.standard_normal(ins["x"].shape)
+            gl = r.standard_normal((b, d, n, W))
+            kw = dict(flip_h=fh, flip_w=fw)
+
+            def loss():
+                y, hl = oracle.fwd(*(ins[k] for k in KEYS), h_init=ins["h_init"], return_last=True, lib=lib, **kw)
+                return float(np.sum(y * dy) + np.sum(hl * gl))
+
+            g = oracle.bwd(*(ins[k] for k in KEYS), dy, h_init=ins["h_init"], dh_last=gl, lib=lib, **kw)
+            for k, gk in list(GRAD.items()) + [("h_init", "dh_init")]:
+                base = ins[k]
+                fd = np.empty_like(base)
+                for idx in np.ndindex(base.shape):
+                    h = 1e-6 * max(1.0, abs(base[idx]))
+                    orig = base[idx]
+                    base[idx] = orig + h
+                    lp = loss()
+                    base[idx] = orig - h
+                    lm = loss()
+                    base[idx] = orig
+                    fd[idx] = (lp - lm) / (2 * h)
+                err = np.max(np.abs(g[gk] - fd) / (1.0 + np.abs(fd)))
+                assert err < 1e-6, f"{gk} vs finite differences, flips {kw}: {err:.2e}"
+
+
+def pin_carried_state_no_rows_of_decay(lib):
+    """A = 0 (Abar = 1, no decay): h_last = h_init + (the plain scan's last
+    row), so dL/dh_init = dh_last + the sum over each column of dy * C, the
+    vertical path from h_init reaching every row undamped; written out."""
+    ins = _inputs(1, 2, 3, 4, 5, 39)
+    ins["A"] = np.zeros_like(ins["A"])
+    r = np.random.default_rng(39)
+    h0 = r.standard_normal((1, 2, 3, 5))
+    dy = r.standard_normal(ins["x"].shape)
+    gl = r.standard_normal((1, 2, 3, 5))
+    g = oracle.bwd(*(ins[k] for k in KEYS), dy, h_init=h0, dh_last=gl, lib=lib)
+    ref = gl + np.einsum("bdhw,bnhw->bdnw", dy, ins["C"])
+    err = np.max(np.abs(g["dh_init"] - ref) / (1.0 + np.abs(ref)))
+    assert err < 1e-13, f"dh_init with no decay: {err:.2e}"
+
+
+CARRY_BWD_PINS = [pin_carried_state_finite_differences, pin_carried_state_no_rows_of_decay]
+
+
+@pytest.mark.parametrize("pin", CARRY_BWD_PINS, ids=lambda f: f.__name__)
+def test_carry_bwd_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+CARRY_BWD_MUTANTS = {
+    "dL/dh_last not fed into the vertical adjoint":
+        ("a[(i + 1) * W + j] * gh[(i + 1) * W + j] : (gl ? gl[j] : 0.0);",
+         "a[(i + 1) * W + j] * gh[(i + 1) * W + j] : 0.0;"),
+    "dh_init without the first row's decay":
+        ("dh0[j] = (H > 0) ? a[j] * gh[j] : (gl ? gl[j] : 0.0);", "dh0[j] = (H > 0) ? gh[j] : (gl ? gl[j] : 0.0);"),
+    "decay derivative ignores the carried state":
+        ("const double up = (i > 0) ? h[p - W] : (h0 ? h0[j] : 0.0);", "const double up = (i > 0) ? h[p - W] : 0.0;"),
+}
+
+
+def test_carry_bwd_pins_catch_planted_mistakes(tmp_path):
+    with open(oracle._SRC) as f:
+        src = f.read()
+    for name, (old, new) in CARRY_BWD_MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site missing or ambiguous: {name}"
+        path = tmp_path / (str(abs(hash(name))) + ".c")
+        path.write_text(src.replace(old, new))
+        lib_path = str(tmp_path / (str(abs(hash(name))) + ".so"))
+        oracle.build(out_path=lib_path, src_path=str(path))
+        lib = oracle.load(lib_path)
+        caught = []
+        for pin in CARRY_BWD_PINS:
+            try:
+                pin(lib)
+            except (AssertionError, RuntimeError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin caught the planted mistake: {name}"
