@@ -285,22 +285,31 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
                         float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
                         int64_t W, void *stream);
 
-/* Backward of ssm2d_scan_fwd_mamba (single upper-left scan; flags: 0 or
- * SSM2D_DELTA_SOFTPLUS): the gradients of ssm2d_scan_bwd, with ddelta taken
- * with respect to the raw delta, plus dz (shaped like z; required when z is
- * given) and ddelta_bias (float32 [d_inner], may be NULL; requires
- * delta_bias). By the chain rule around ssm2d_scan_bwd: the gate gives
- * dz = dy * y * SiLU'(z) and passes dy * SiLU(z) on (y = the ungated scan,
- * recomputed); the step size passes d delta' back through softplus
- * (times sigmoid(delta + bias)) and sums it over cells for the bias.
+/* Backward of ssm2d_scan_fwd_mamba (a single scan; flags: SSM2D_DELTA_SOFTPLUS
+ * and the direction and order flags SSM2D_FLIP_H, SSM2D_FLIP_W,
+ * SSM2D_VERTICAL_FIRST of the forward): the gradients of ssm2d_scan_bwd_ex,
+ * with ddelta taken with respect to the raw delta, plus dz (shaped like z;
+ * required when z is given) and ddelta_bias (float32 [d_inner], may be
+ * NULL; requires delta_bias). By the chain rule around the scan's backward:
+ * the gate gives dz = dy * y * SiLU'(z) and passes dy * SiLU(z) on (y = the
+ * ungated scan, recomputed); the step size passes d delta' back through
+ * softplus (times sigmoid(delta + bias)) and sums it over cells for the bias.
+ * Carried vertical states: h_init (may be NULL: zeros) the state the forward
+ * started from, dh_last (may be NULL: zeros) dL/dh_last for the state it
+ * handed out, dh_init (may be NULL: not computed) receives dL/dh_init; all
+ * float32 [batch][d_inner][d_state][W]. The vertical adjoint starts from
+ * dh_last and hands out dh_init = Abar(first row) g_h(first row); the first
+ * row's decay derivative uses h_init. Horizontal-first order only (with
+ * SSM2D_VERTICAL_FIRST -> SSM2D_ERR_UNSUPPORTED); no carried row states.
  * Elementwise passes run around the backward's three kernels; scratch of
  * up to three tensors shaped like x per (device, stream). ddelta_bias is
  * accumulated with atomics (last bits may vary between runs). Other flags
  * -> SSM2D_ERR_BAD_FLAGS; errors otherwise as for ssm2d_scan_bwd. */
 int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B,
                          const float *C, const float *D, const float *z, const float *delta_bias,
-                         const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
-                         float *dD, float *dz, float *ddelta_bias, int64_t batch, int64_t d_inner,
+                         const float *h_init, const float *dh_last, const float *dy, float *dx,
+                         float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
+                         float *ddelta_bias, float *dh_init, int64_t batch, int64_t d_inner,
                          int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
 
 /* bf16 variant: x, delta, B, C, z, dy, dx, ddelta, dB, dC, dz bfloat16 bits.
@@ -310,12 +319,12 @@ int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, con
  * backward runs on them; each gradient is rounded to bf16 once. Without
  * options it is ssm2d_scan_bwd_bf16. */
 int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
-                              const uint16_t *B, const uint16_t *C, const float *D,
-                              const uint16_t *z, const float *delta_bias, const uint16_t *dy,
-                              uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
-                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias,
-                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-                              int64_t W, uint32_t flags, void *stream);
+                              const uint16_t *B, const uint16_t *C, const float *D, const uint16_t *z,
+                              const float *delta_bias, const float *h_init, const float *dh_last,
+                              const uint16_t *dy, uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
+                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias, float *dh_init,
+                              int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                              uint32_t flags, void *stream);
 
 /* ---- Forward without allocation -------------------------------------------
  *

@@ -229,13 +229,16 @@ def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus
     return y
 
 
-def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, lib=None):
+def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, lib=None, h_init=None,
+              dh_last=None, **dirs):
     """Gradients of fwd_mamba (step-size bias and softplus, SiLU(z) gate) for
     upstream dy, by the chain rule around the scan's backward: the gate gives
     dz = dy * y_scan * SiLU'(z) and hands dy * SiLU(z) to the scan; the step
     size hands d delta' back through softplus (its derivative is the logistic
     sigmoid) and sums it over cells for the bias. Everything in fp64.
-    Returns the dict of bwd plus dz and ddelta_bias where they apply."""
+    Returns the dict of bwd plus dz and ddelta_bias where they apply.
+    h_init / dh_last and the direction keywords (flip_h, flip_w,
+    vertical_first) pass through to fwd and bwd (dh_init then in the dict)."""
     raw = np.asarray(delta, dtype=np.float64)
     pre = raw if delta_bias is None else raw + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
     dt = softplus(pre) if delta_softplus else pre
@@ -244,10 +247,10 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
     if z is not None:
         zf = np.asarray(z, dtype=np.float64)
         sig = 1.0 / (1.0 + np.exp(-zf))
-        y_scan = fwd(x, dt, A, B, C, D, lib=lib)
+        y_scan = fwd(x, dt, A, B, C, D, lib=lib, h_init=h_init, **dirs)
         out["dz"] = dyf * y_scan * sig * (1.0 + zf * (1.0 - sig))
         dyf = dyf * zf * sig
-    g = bwd(x, dt, A, B, C, D, dyf, lib=lib)
+    g = bwd(x, dt, A, B, C, D, dyf, lib=lib, h_init=h_init, dh_last=dh_last, **dirs)
     dd = g["ddelta"]
     if delta_softplus:
         dd = dd / (1.0 + np.exp(-pre))

@@ -882,12 +882,14 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         }
         // Stored-state tiles: the forward writes its strip's tile of each row
         // (whole 1 KB blocks per state slot, every lane, no masks: lanes and
-        // cells outside the map hold exact zeros); the backward's strip s and
-        // scan row t read the forward's strip nstrips-1-s, row H-1-t (its
-        // cells in reverse order); rows past the map read the zero page.
+        // cells outside the map hold exact zeros), and first a tile for row
+        // -1, the carried state above the map (zeros without one); the
+        // backward's strip s and scan row t read the forward's strip
+        // nstrips-1-s, row H-1-t (its cells in reverse order), row -1 at
+        // t = H; rows past that read the zero page.
         constexpr long TILE = static_cast<long>(NPL) * kWave * 4;   // floats per (chain, strip, row)
         const int fstrip = BWD ? p.nstrips - 1 - strip : strip;     // strip in the forward's numbering
-        const long tile0 = (static_cast<long>(chain) * p.nstrips + fstrip) * H;  // tile of row 0
+        const long tile0 = (static_cast<long>(chain) * p.nstrips + fstrip) * (H + 1) + 1;  // tile of row 0
         float *hrow = p.states + tile0 * TILE + lane * 4;            // + row * TILE + k * 256
         const float *hlast = p.states + (tile0 + H - 1) * TILE + lane * 4;
         // backward: 8-channel sums of dB, dC for this lane's group, memory row
@@ -973,10 +975,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // Carried vertical state (a band of rows continuing a scan): the
         // register state of the strip's columns starts from h_init and is
         // written to h_last after the last row.
+        // (the stored-state pass counts its strips over the map padded by
+        // states_pad columns at the end it scans last: column u of its scan is
+        // j0 + c - states_pad)
         auto carry_index = [&](const int c, const int k, long &idx) -> bool {
-            const int n = g * NPL + k, u = j0 + c;
+            const int n = g * NPL + k, u = j0 + c - (STATES ? p.states_pad : 0);
             idx = ((static_cast<long>(b) * p.d_inner + d) * p.d_state + n) * W + (FW ? W - 1 - u : u);
-            return d_ok && n < p.d_state && u < W;
+            return d_ok && n < p.d_state && u >= 0 && u < W;
         };
         // Carried horizontal state of scan row t (kModeRowCarry): element
         // [b][d][n][memory row] of hh_init / hh_last.
@@ -989,7 +994,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         // strip writes them (with the row's inputs / after the row's chain)
         const bool rc_in = RC && p.hh_init && strip == 0;
         const bool rc_out = RC && p.hh_last && strip + 1 == p.nstrips;
-        if constexpr (!STATES && !BWD) {
+        // (the adjoint pass: h_init is dL/dh_last, the carry its vertical
+        // adjoint starts from; h_last receives dL/dh_init, its final carry)
+        {
             if (p.h_init) {
 #pragma unroll
                 for (int c = 0; c < K; ++c)
@@ -1002,6 +1009,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                 for (int c = 0; c < K; ++c)
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) asm volatile("" : "+v"(hv[c][k]));  // loaded before the row loop
+            }
+            if constexpr (STATES) {
+                // row -1's tile: the carried state (or zeros)
+#pragma unroll
+                for (int k = 0; k < NPL; ++k)
+                    *reinterpret_cast<float4 *>(hrow - TILE + k * kWave * 4) =
+                        make_float4(hv[0][k], hv[1][k], hv[2][k], hv[3][k]);
             }
         }
 
@@ -1488,7 +1502,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 #pragma unroll
                         for (int k = 0; k < NPL; ++k)
                             hb[s][k] = *reinterpret_cast<const float4 *>(
-                                t < H ? hlast - static_cast<long>(t) * TILE + k * kWave * 4 : zeros_f);
+                                t <= H ? hlast - static_cast<long>(t) * TILE + k * kWave * 4 : zeros_f);
                     }
                     if constexpr (RC) {
                         // (hb holds the row's carried horizontal state in .x)
@@ -1569,7 +1583,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             if (has_right) strip_rows(N0{}, N1{});
             else strip_rows(N0{}, N0{});
         }
-        if constexpr (!STATES && !BWD) {
+        if constexpr (!STATES) {
             if (p.h_last && !timed_out) {
 #pragma unroll
                 for (int c = 0; c < K; ++c)

@@ -120,6 +120,13 @@ __global__ void fill_zero_kernel(uint4 *p, long n16)
         p[t] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// dst = src, or zeros where src is null (n floats).
+__global__ void copy_or_zero_kernel(const float *src, float *dst, long n)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t < n) dst[t] = src ? src[t] : 0.0f;
+}
+
 int zero_async(void *p, size_t bytes, hipStream_t s)
 {
     const long n16 = static_cast<long>((bytes + 15) / 16);
@@ -755,7 +762,8 @@ int scan_fwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-             int64_t W, void *stream, unsigned flags = 0);
+             int64_t W, void *stream, unsigned flags = 0, const float *h_init = nullptr, const float *dh_last = nullptr,
+             float *dh_init = nullptr);
 
 // Backward of the vertical-first order: that scan is the horizontal-first
 // scan of the transposed maps (the column recurrence becomes the row
@@ -801,11 +809,14 @@ int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, cons
 }
 
 // flags: SSM2D_FLIP_H / SSM2D_FLIP_W / SSM2D_VERTICAL_FIRST, the direction
-// and order of the forward scan.
+// and order of the forward scan. h_init (may be null): the carried vertical
+// state the forward started from; dh_last (may be null): dL/dh_last for the
+// state it handed out; dh_init (may be null): receives dL/dh_init (all
+// float32 [batch][d_inner][d_state][W]; horizontal-first order only).
 template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-             int64_t W, void *stream, unsigned flags)
+             int64_t W, void *stream, unsigned flags, const float *h_init, const float *dh_last, float *dh_init)
 {
     if ((flags & ~kKnownFlags) != 0 || (flags & (SSM2D_ACCUMULATE | SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
         return SSM2D_ERR_BAD_FLAGS;
@@ -818,7 +829,7 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const int64_t n_dblk = (d_inner + 7) / 8;
     int64_t npl = 1;
     while (npl * 8 < d_state) npl *= 2;
-    const int64_t tiles = batch * n_dblk * nstrips * H;  // (chain, strip, row)
+    const int64_t tiles = batch * n_dblk * nstrips * (H + 1);  // (chain, strip, row), rows -1 .. H-1
     if (batch * d_inner * H * W > lim || batch * d_state * H * W > lim || d_inner * d_state > lim)
         return SSM2D_ERR_UNSUPPORTED;
     const bool work = batch > 0 && H > 0 && W > 0;
@@ -827,13 +838,24 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(A) || misaligned(B) || misaligned(C) || misaligned(D) ||
         misaligned(dy) || misaligned(dx) || misaligned(ddelta) || misaligned(dA) || misaligned(dB) || misaligned(dC) ||
-        misaligned(dD))
+        misaligned(dD) || misaligned(h_init) || misaligned(dh_last) || misaligned(dh_init))
         return SSM2D_ERR_MISALIGNED;
+    const bool carry = h_init || dh_last || dh_init;
+    // (vertical-first: the carried state is the transposed map's row state)
+    if (carry && (flags & SSM2D_VERTICAL_FIRST)) return SSM2D_ERR_UNSUPPORTED;
 
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::recursive_mutex> lock(g_mutex);
     if (take_timeout_flag(dev, stream)) return SSM2D_ERR_DEVICE_TIMEOUT;
+    const hipStream_t s0 = static_cast<hipStream_t>(stream);
+    if (dh_init && batch > 0 && d_state > 0 && W > 0 && H == 0) {
+        // no rows: the handed-out state is h_init itself
+        const long n = batch * d_inner * d_state * W;
+        copy_or_zero_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s0>>>(dh_last, dh_init, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
     if ((flags & SSM2D_VERTICAL_FIRST) && work)
         return scan_bwd_vfirst<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
                                   stream, flags, dev);
@@ -873,6 +895,7 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates | (f_w ? kModeFlipW : 0));
     pf.bw = &bw;
     pf.flip_h = f_h ? 1 : 0;
+    pf.h_init = h_init;
     choose_coop<T>(pf, H, align);
     if (pf.npl != npl || pf.n_dblk != n_dblk || pf.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     int st = f_w ? dispatch_states_flipw(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align)
@@ -887,6 +910,8 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     if (edges) pb = make_plan(batch, d_inner, d_state, H, W, bmode | kModeEdges);
     pb.flip_h = f_h ? 0 : 1;
     pb.bw = &bw;
+    pb.h_init = dh_last;   // the vertical adjoint's carry in and out
+    pb.h_last = dh_init;
     choose_coop<T>(pb, H, align);
     if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
     if (f_w)
@@ -918,15 +943,21 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 // gradient is rounded to bf16 once.
 template <typename T>
 int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *z,
-                   const float *delta_bias, const T *dy, T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, T *dz,
-                   float *ddelta_bias, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                   unsigned flags, void *stream)
+                   const float *delta_bias, const float *h_init, const float *dh_last, const T *dy, T *dx, T *ddelta,
+                   float *dA, T *dB, T *dC, float *dD, T *dz, float *ddelta_bias, float *dh_init, int64_t batch,
+                   int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, void *stream)
 {
-    if ((flags & ~SSM2D_DELTA_SOFTPLUS) != 0) return SSM2D_ERR_BAD_FLAGS;
+    constexpr unsigned kDirs = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST;
+    if ((flags & ~(SSM2D_DELTA_SOFTPLUS | kDirs)) != 0) return SSM2D_ERR_BAD_FLAGS;
+    const unsigned dirs = flags & kDirs;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (d_inner == 0) return SSM2D_OK;
     if ((z && !dz) || (ddelta_bias && !delta_bias)) return SSM2D_ERR_NULLPTR;
-    if (misaligned(z) || misaligned(dz) || misaligned(delta_bias) || misaligned(ddelta_bias)) return SSM2D_ERR_MISALIGNED;
+    if (misaligned(z) || misaligned(dz) || misaligned(delta_bias) || misaligned(ddelta_bias) || misaligned(h_init) ||
+        misaligned(dh_last) || misaligned(dh_init))
+        return SSM2D_ERR_MISALIGNED;
+    // (vertical-first: the carried state is the transposed map's row state)
+    if ((h_init || dh_last || dh_init) && (dirs & SSM2D_VERTICAL_FIRST)) return SSM2D_ERR_UNSUPPORTED;
     const bool softplus = (flags & SSM2D_DELTA_SOFTPLUS) != 0;
     const bool prep = delta_bias || softplus;
     const long total = batch * d_inner * H * W;
@@ -942,7 +973,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     }
     if (total == 0 || d_state > SSM2D_MAX_STATE_BWD || (!prep && !z))  // the backward alone (it also reports sizes)
         return scan_bwd<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                           stream);
+                           stream, dirs, h_init, dh_last, dh_init);
     if (!x || !delta || !dy || !dx || !ddelta || !D || (d_state > 0 && (!A || !B || !C || !dB || !dC || !dA)) || !dD)
         return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(dy) || misaligned(dx) || misaligned(ddelta))
@@ -989,7 +1020,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
         TW *y0 = nullptr;
         if ((st = buf(kSlotY0, eb, &y0)) != SSM2D_OK) return st;
         st = scan_fwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, y0, batch, d_inner,
-                          d_state, H, W, 0u, false, stream);
+                          d_state, H, W, dirs, false, stream, nullptr, nullptr, h_init, nullptr);
         if (st != SSM2D_OK) return st;
         gate_bwd_kernel<T, TW><<<dim3(nblk), dim3(256), 0, s>>>(dy, y0, z, dz, g, total);
         const hipError_t e = hipGetLastError();
@@ -1010,7 +1041,8 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
         dBw = reinterpret_cast<TW *>(dB); dCw = reinterpret_cast<TW *>(dC);
     }
     st = scan_bwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, g, dxw, ddw, dA,
-                      d_state ? dBw : nullptr, d_state ? dCw : nullptr, dD, batch, d_inner, d_state, H, W, stream);
+                      d_state ? dBw : nullptr, d_state ? dCw : nullptr, dD, batch, d_inner, d_state, H, W, stream, dirs,
+                      h_init, dh_last, dh_init);
     if (st != SSM2D_OK) return st;
     // d delta with respect to the raw step size, d bias (and the rounding)
     if (prep || WIDE) {
@@ -1153,23 +1185,24 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
 }
 
 int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
-                         const float *D, const float *z, const float *delta_bias, const float *dy, float *dx,
-                         float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
-                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags,
-                         void *stream)
+                         const float *D, const float *z, const float *delta_bias, const float *h_init,
+                         const float *dh_last, const float *dy, float *dx, float *ddelta, float *dA, float *dB,
+                         float *dC, float *dD, float *dz, float *ddelta_bias, float *dh_init, int64_t batch,
+                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
-    return scan_bwd_mamba<float>(x, delta, A, B, C, D, z, delta_bias, dy, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
-                                 batch, d_inner, d_state, H, W, flags, stream);
+    return scan_bwd_mamba<float>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, dy, dx, ddelta, dA, dB, dC, dD,
+                                 dz, ddelta_bias, dh_init, batch, d_inner, d_state, H, W, flags, stream);
 }
 
 int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
                               const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
-                              const uint16_t *dy, uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
-                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias, int64_t batch,
-                              int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+                              const float *h_init, const float *dh_last, const uint16_t *dy, uint16_t *dx,
+                              uint16_t *ddelta, float *dA, uint16_t *dB, uint16_t *dC, float *dD, uint16_t *dz,
+                              float *ddelta_bias, float *dh_init, int64_t batch, int64_t d_inner, int64_t d_state,
+                              int64_t H, int64_t W, uint32_t flags, void *stream)
 {
-    return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, z, delta_bias, dy, dx, ddelta, dA, dB, dC, dD, dz,
-                                    ddelta_bias, batch, d_inner, d_state, H, W, flags, stream);
+    return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, dy, dx, ddelta, dA, dB, dC,
+                                    dD, dz, ddelta_bias, dh_init, batch, d_inner, d_state, H, W, flags, stream);
 }
 
 const char *ssm2d_status_string(int status)

@@ -293,3 +293,78 @@ def test_backward_vertical_first_full_vmamba():
     got = {k: as_f64(v) for k, v in g.items()}
     check_grads(got, oracle.bwd(*(t[k] for k in KEYS), dy, vertical_first=True), wl.dtype,
                 wl.batch * wl.H * wl.W, "vmamba vertical-first")
+
+
+# Carried vertical states (bands of rows): the forward started from h_init,
+# the loss also takes dh_last through h_last. Shapes: several strips and
+# channel blocks, ragged rows (W % 4 = 1, 3), one row, one column, chains
+# across workgroups (forced 1-strip workgroups: the courier-free adjoint),
+# and a tall map with the shared row ring.
+CARRY_CASES = [((1, 16, 16, 9, 64), None), ((2, 9, 8, 7, 23), None), ((1, 8, 16, 1, 29), None),
+               ((1, 5, 16, 27, 1), None), ((1, 16, 16, 13, 40), "1"), ((1, 16, 16, 140, 96), None)]
+
+
+@pytest.mark.parametrize("flips", [(False, False), (True, False), (False, True), (True, True)],
+                         ids=lambda f: "".join("HW"[i] if v else "-" for i, v in enumerate(f)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CARRY_CASES, ids=str)
+def test_carried_state_backward(case, dtype, flips, monkeypatch):
+    shape, waves = case
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    fh, fw = flips
+    _say(f"carried-state backward {shape} {dtype} flips={flips} waves={waves}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 61, dtype=dtype)
+    b, di, n, H, W = shape
+    r = np.random.default_rng(sum(shape) + 62)
+    h0 = r.standard_normal((b, di, n, W)).astype(np.float32)
+    gl = r.standard_normal((b, di, n, W)).astype(np.float32)
+    dy, dy_dev = make_dy(t, dtype, sum(shape) + 63)
+    g = pkg.scan_bwd_mamba(*to_dev(t, dtype), dy_dev, h_init=torch.from_numpy(h0).cuda(),
+                           dh_last=torch.from_numpy(gl).cuda(), flip_h=fh, flip_w=fw)
+    pkg.sync_check()
+    got = {k: v.double().cpu().numpy() for k, v in g.items()}
+    ref = oracle.bwd(*(t[k] for k in ("x", "delta", "A", "B", "C", "D")), dy, h_init=h0, dh_last=gl, flip_h=fh,
+                     flip_w=fw)
+    check_grads(got, ref, dtype, b * H * W, f"carried {shape} {flips}")
+    err = float(np.max(np.abs(got["dh_init"] - ref["dh_init"]) / (1.0 + np.abs(ref["dh_init"]))))
+    _say(f"  dh_init: {err:.3e}")
+    assert err <= TOL["f32"] * max(1.0, np.sqrt(H / 64.0)), "dh_init"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_carried_state_backward_with_options(dtype):
+    """Carried states with the gate, a step-size bias and softplus, scanned
+    from the lower-right corner."""
+    shape = (2, 12, 16, 11, 30)
+    t = make_random_inputs(*shape, seed=64, dtype=dtype)
+    b, di, n, H, W = shape
+    r = np.random.default_rng(64)
+
+    def dev(a):
+        a = np.asarray(a, dtype=np.float32)
+        if dtype == "bf16":
+            bits = bf16_bits_from_f32(a)
+            return f32_from_bf16_bits(bits).astype(np.float64), torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        return a.astype(np.float64), torch.from_numpy(a).cuda()
+
+    raw, raw_dev = dev(r.standard_normal(t["x"].shape) - 0.2)
+    z, z_dev = dev(r.standard_normal(t["x"].shape))
+    bias = (np.abs(r.standard_normal(di)) * 0.3).astype(np.float32)
+    h0 = r.standard_normal((b, di, n, W)).astype(np.float32)
+    gl = r.standard_normal((b, di, n, W)).astype(np.float32)
+    dy, dy_dev = make_dy(t, dtype, 65)
+    args = to_dev(t, dtype)
+    args[1] = raw_dev
+    g = pkg.scan_bwd_mamba(*args, dy_dev, z=z_dev, delta_bias=torch.from_numpy(bias).cuda(), delta_softplus=True,
+                           h_init=torch.from_numpy(h0).cuda(), dh_last=torch.from_numpy(gl).cuda(), flip_h=True,
+                           flip_w=True)
+    pkg.sync_check()
+    got = {k: v.double().cpu().numpy() for k, v in g.items()}
+    ref = oracle.bwd_mamba(t["x"], raw, t["A"], t["B"], t["C"], t["D"], dy, z=z, delta_bias=bias,
+                           delta_softplus=True, h_init=h0, dh_last=gl, flip_h=True, flip_w=True)
+    check_grads(got, ref, dtype, b * H * W, "carried with options")
+    for k in ("dz", "dh_init"):
+        err = float(np.max(np.abs(got[k] - ref[k]) / (1.0 + np.abs(ref[k]))))
+        _say(f"  {k}: {err:.3e}")
+        assert err <= TOL[dtype if k == "dz" else "f32"], k
