@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH):
     lib.oracle_ssm2d_bwd_f64.argtypes = [dp] * 13 + [i64] * 5 + [ctypes.c_int]
     lib.oracle_ssm2d_bwd_carry_f64.argtypes = [dp] * 16 + [i64] * 5 + [ctypes.c_int]
     lib.oracle_ssm2d_bwd_carry_f64.restype = ctypes.c_int
+    lib.oracle_ssm2d_bwd_tile_f64.argtypes = [dp] * 19 + [i64] * 5 + [ctypes.c_int]
+    lib.oracle_ssm2d_bwd_tile_f64.restype = ctypes.c_int
     lib.oracle_ssm2d_bwd_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -230,15 +232,16 @@ def fwd_mamba(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus
 
 
 def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=False, lib=None, h_init=None,
-              dh_last=None, **dirs):
+              dh_last=None, hh_init=None, dhh_last=None, **dirs):
     """Gradients of fwd_mamba (step-size bias and softplus, SiLU(z) gate) for
     upstream dy, by the chain rule around the scan's backward: the gate gives
     dz = dy * y_scan * SiLU'(z) and hands dy * SiLU(z) to the scan; the step
     size hands d delta' back through softplus (its derivative is the logistic
     sigmoid) and sums it over cells for the bias. Everything in fp64.
     Returns the dict of bwd plus dz and ddelta_bias where they apply.
-    h_init / dh_last and the direction keywords (flip_h, flip_w,
-    vertical_first) pass through to fwd and bwd (dh_init then in the dict)."""
+    h_init / dh_last, hh_init / dhh_last and the direction keywords (flip_h,
+    flip_w, vertical_first) pass through to fwd and bwd (dh_init, dhh_init
+    then in the dict)."""
     raw = np.asarray(delta, dtype=np.float64)
     pre = raw if delta_bias is None else raw + np.asarray(delta_bias, dtype=np.float64)[None, :, None, None]
     dt = softplus(pre) if delta_softplus else pre
@@ -247,10 +250,11 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
     if z is not None:
         zf = np.asarray(z, dtype=np.float64)
         sig = 1.0 / (1.0 + np.exp(-zf))
-        y_scan = fwd(x, dt, A, B, C, D, lib=lib, h_init=h_init, **dirs)
+        y_scan = fwd(x, dt, A, B, C, D, lib=lib, h_init=h_init, hh_init=hh_init, **dirs)
         out["dz"] = dyf * y_scan * sig * (1.0 + zf * (1.0 - sig))
         dyf = dyf * zf * sig
-    g = bwd(x, dt, A, B, C, D, dyf, lib=lib, h_init=h_init, dh_last=dh_last, **dirs)
+    g = bwd(x, dt, A, B, C, D, dyf, lib=lib, h_init=h_init, dh_last=dh_last, hh_init=hh_init, dhh_last=dhh_last,
+            **dirs)
     dd = g["ddelta"]
     if delta_softplus:
         dd = dd / (1.0 + np.exp(-pre))
@@ -262,7 +266,7 @@ def bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, delta_softplus=
 
 
 def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=False, vertical_first=False,
-        h_init=None, dh_last=None):
+        h_init=None, dh_last=None, hh_init=None, dhh_last=None):
     """Gradients of the forward pass (fp64) for upstream gradient dy (shape of
     y): returns dict dx, ddelta, dA, dB, dC, dD, each shaped like its input.
     flip_h / flip_w: of the scan in that direction, which is the upper-left
@@ -277,12 +281,19 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
     h_init / dh_last ([batch][d_inner][d_state][W], may be None): the
     backward of the forward with a carried vertical state h_init, for the
     loss sum(dy * y) + sum(dh_last * h_last); the result then also holds
-    dh_init, shaped like h_init (horizontal-first order only: in the
-    vertical-first order the carried state is the transposed map's row
-    state)."""
+    dh_init, shaped like h_init. hh_init / dhh_last ([batch][d_inner]
+    [d_state][H]): the same for the carried row state (dhh_init). In the
+    vertical-first order the two kinds trade places on the transposed map."""
     carry = h_init is not None or dh_last is not None
+    rcarry = hh_init is not None or dhh_last is not None
     if vertical_first:
-        assert not carry, "carried states: horizontal-first order only"
+        tr = lambda a: np.ascontiguousarray(np.swapaxes(np.asarray(a, dtype=np.float64), 2, 3))
+        g = bwd(tr(x), tr(delta), A, tr(B), tr(C), D, tr(dy), nthreads, lib, flip_h=flip_w, flip_w=flip_h,
+                h_init=hh_init, dh_last=dhh_last, hh_init=h_init, dhh_last=dh_last)
+        for k in ("dx", "ddelta", "dB", "dC"):
+            g[k] = tr(g[k])
+        g["dh_init"], g["dhh_init"] = g.pop("dhh_init", None), g.pop("dh_init", None)
+        return {k: v for k, v in g.items() if v is not None}
         tr = lambda a: np.ascontiguousarray(np.swapaxes(np.asarray(a, dtype=np.float64), 2, 3))
         g = bwd(tr(x), tr(delta), A, tr(B), tr(C), D, tr(dy), nthreads, lib, flip_h=flip_w, flip_w=flip_h)
         for k in ("dx", "ddelta", "dB", "dC"):
@@ -297,12 +308,19 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
                 return a
             return np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 3))
 
+        def flr(a):  # carried row states are per row: mirrored with the rows only
+            if a is None or not flip_h:
+                return a
+            return np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 3))
+
         g = bwd(fl(x), fl(delta), A, fl(B), fl(C), D, fl(dy), nthreads, lib, h_init=flc(h_init),
-                dh_last=flc(dh_last))
+                dh_last=flc(dh_last), hh_init=flr(hh_init), dhh_last=flr(dhh_last))
         for k in ("dx", "ddelta", "dB", "dC"):
             g[k] = fl(g[k])
         if "dh_init" in g:
             g["dh_init"] = flc(g["dh_init"])
+        if "dhh_init" in g:
+            g["dhh_init"] = flr(g["dhh_init"])
         return g
     lib = lib or _get()
     x, delta, A, B, C, D, dy = map(_f64, (x, delta, A, B, C, D, dy))
@@ -313,17 +331,25 @@ def bwd(x, delta, A, B, C, D, dy, nthreads=0, lib=None, flip_h=False, flip_w=Fal
     assert B.shape == (batch, d_state, H, W) and C.shape == B.shape
     out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty_like(A),
            "dB": np.empty_like(B), "dC": np.empty_like(C), "dD": np.empty_like(D)}
-    if carry:
-        cshape = (batch, d_inner, d_state, W)
+    if carry or rcarry:
+        cshape, rshape = (batch, d_inner, d_state, W), (batch, d_inner, d_state, H)
         h0 = None if h_init is None else _f64(h_init)
         gl = None if dh_last is None else _f64(dh_last)
+        g0 = None if hh_init is None else _f64(hh_init)
+        ggl = None if dhh_last is None else _f64(dhh_last)
         assert (h0 is None or h0.shape == cshape) and (gl is None or gl.shape == cshape)
-        out["dh_init"] = np.empty(cshape, dtype=np.float64)
+        assert (g0 is None or g0.shape == rshape) and (ggl is None or ggl.shape == rshape)
+        if carry:
+            out["dh_init"] = np.empty(cshape, dtype=np.float64)
+        if rcarry:
+            out["dhh_init"] = np.empty(rshape, dtype=np.float64)
         null = ctypes.POINTER(ctypes.c_double)()
-        s = lib.oracle_ssm2d_bwd_carry_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
-                                           null if h0 is None else _ptr(h0), null if gl is None else _ptr(gl),
-                                           *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")),
-                                           _ptr(out["dh_init"]), batch, d_inner, d_state, H, W, int(nthreads))
+        p = lambda a: null if a is None else _ptr(a)
+        s = lib.oracle_ssm2d_bwd_tile_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+                                          p(h0), p(gl), p(g0), p(ggl),
+                                          *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")),
+                                          p(out.get("dh_init")), p(out.get("dhh_init")), batch, d_inner, d_state,
+                                          H, W, int(nthreads))
         if s != 0:
             raise RuntimeError(f"oracle failed with status {s}")
         return out

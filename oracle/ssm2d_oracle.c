@@ -313,8 +313,12 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
                              const double *Cn, const double *dym, double *dxm, double *ddm,
                              double *dBn, double *dCn, double *dA_dn, int64_t H, int64_t W,
                              double *a, double *u, double *hh, double *h, double *gh, double *ghh,
-                             const double *h0, const double *gl, double *dh0)
+                             const double *h0, const double *gl, double *dh0,
+                             const double *g0, const double *ggl, double *dg0)
 {
+    /* g0, ggl, dg0 (may be NULL): the same for the carried row state ([H]):
+     * g0 the state left of column 0, ggl dL/dhh of the state after the last
+     * column (hh of column W-1), dg0 receives dL/dg0 = a[i,0] g_hh[i,0]. */
     /* h0 (may be NULL: zeros): the carried vertical state above row 0 ([W]);
      * gl (may be NULL: zeros): dL/dh of the state after the last row, which
      * the forward hands out (h of row H-1); dh0 (may be NULL): receives
@@ -327,7 +331,7 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
     /* forward states, kept whole */
     for (int64_t i = 0; i < H; ++i) {
         for (int64_t j = 0; j < W; ++j) {
-            const double left = (j > 0) ? hh[i * W + j - 1] : 0.0;
+            const double left = (j > 0) ? hh[i * W + j - 1] : (g0 ? g0[i] : 0.0);
             hh[i * W + j] = a[i * W + j] * left + u[i * W + j];
         }
         for (int64_t j = 0; j < W; ++j) {
@@ -344,18 +348,21 @@ static void backward_one_map(const double *xm, const double *dm, double a_dn, co
         }
     if (dh0)
         for (int64_t j = 0; j < W; ++j) dh0[j] = (H > 0) ? a[j] * gh[j] : (gl ? gl[j] : 0.0);
-    /* adjoint of the horizontal scan: right to left along each row */
-    for (int64_t i = 0; i < H; ++i)
+    /* adjoint of the horizontal scan: right to left along each row (the last
+     * column also feeds the handed-out row state) */
+    for (int64_t i = 0; i < H; ++i) {
         for (int64_t j = W - 1; j >= 0; --j) {
-            const double right = (j + 1 < W) ? a[i * W + j + 1] * ghh[i * W + j + 1] : 0.0;
+            const double right = (j + 1 < W) ? a[i * W + j + 1] * ghh[i * W + j + 1] : (ggl ? ggl[i] : 0.0);
             ghh[i * W + j] = gh[i * W + j] + right;
         }
+        if (dg0) dg0[i] = (W > 0) ? a[i * W] * ghh[i * W] : (ggl ? ggl[i] : 0.0);
+    }
     /* local derivatives */
     double dA_sum = 0.0;
     for (int64_t i = 0; i < H; ++i)
         for (int64_t j = 0; j < W; ++j) {
             const int64_t p = i * W + j;
-            const double left = (j > 0) ? hh[p - 1] : 0.0;
+            const double left = (j > 0) ? hh[p - 1] : (g0 ? g0[i] : 0.0);
             const double up = (i > 0) ? h[p - W] : (h0 ? h0[j] : 0.0);
             const double g_a = ghh[p] * left + gh[p] * up;
             const double g_u = ghh[p];
@@ -378,7 +385,8 @@ static int bwd_maps(const double *x, const double *delta, const double *A, const
                     const double *C, const double *D, const double *dy, double *dx,
                     double *ddelta, double *dA, double *dB, double *dC, double *dD,
                     int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                    int nthreads, const double *h0, const double *gl, double *dh0)
+                    int nthreads, const double *h0, const double *gl, double *dh0, const double *g0,
+                    const double *ggl, double *dg0)
 {
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return 2;
     const int64_t L = H * W;
@@ -412,12 +420,14 @@ static int bwd_maps(const double *x, const double *delta, const double *A, const
             const int64_t m = (b * d_inner + d) * L;
             for (int64_t n = 0; n < d_state; ++n) {
                 const int64_t q = (b * d_state + n) * L;
-                const int64_t c = ((b * d_inner + d) * d_state + n) * W;  /* carried-state row */
+                const int64_t c = ((b * d_inner + d) * d_state + n) * W;  /* carried-state rows */
+                const int64_t cr = ((b * d_inner + d) * d_state + n) * H;
                 backward_one_map(x + m, delta + m, A[d * d_state + n], B + q, C + q, dy + m,
                                  dx + m, ddelta + m, dB + q, dC + q,
                                  dA_b + (b * d_inner + d) * d_state + n, H, W,
                                  buf, buf + L, buf + 2 * L, buf + 3 * L, buf + 4 * L, buf + 5 * L,
-                                 h0 ? h0 + c : NULL, gl ? gl + c : NULL, dh0 ? dh0 + c : NULL);
+                                 h0 ? h0 + c : NULL, gl ? gl + c : NULL, dh0 ? dh0 + c : NULL,
+                                 g0 ? g0 + cr : NULL, ggl ? ggl + cr : NULL, dg0 ? dg0 + cr : NULL);
             }
             double s = 0.0;
             for (int64_t p = 0; p < L; ++p) {
@@ -446,7 +456,7 @@ int oracle_ssm2d_bwd_f64(const double *x, const double *delta, const double *A, 
                          int nthreads)
 {
     return bwd_maps(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                    nthreads, NULL, NULL, NULL);
+                    nthreads, NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /* The backward pass of the forward with carried vertical states: h0 (may be
@@ -465,7 +475,30 @@ int oracle_ssm2d_bwd_carry_f64(const double *x, const double *delta, const doubl
         for (int64_t k = 0; k < batch * d_inner * d_state * W; ++k) dh0[k] = gl ? gl[k] : 0.0;
     }
     return bwd_maps(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                    nthreads, h0, gl, dh0);
+                    nthreads, h0, gl, dh0, NULL, NULL, NULL);
+}
+
+/* The backward pass of a tile: carried vertical states as in
+ * oracle_ssm2d_bwd_carry_f64, and carried row states g0 (the state left of
+ * column 0 the forward started each row from), ggl (dL/dhh_last for the row
+ * state it handed out after the last column) and dg0 (receives dL/dg0), all
+ * three [batch][d_inner][d_state][H]; any may be NULL. */
+int oracle_ssm2d_bwd_tile_f64(const double *x, const double *delta, const double *A, const double *B,
+                              const double *C, const double *D, const double *dy, const double *h0,
+                              const double *gl, const double *g0, const double *ggl, double *dx,
+                              double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dh0,
+                              double *dg0, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                              int64_t W, int nthreads)
+{
+    if (batch >= 0 && d_inner >= 0 && d_state >= 0 && W >= 0 && H >= 0) {
+        /* no rows (or no columns): a handed-out state is the carried one itself */
+        if (dh0 && H == 0)
+            for (int64_t k = 0; k < batch * d_inner * d_state * W; ++k) dh0[k] = gl ? gl[k] : 0.0;
+        if (dg0 && W == 0)
+            for (int64_t k = 0; k < batch * d_inner * d_state * H; ++k) dg0[k] = ggl ? ggl[k] : 0.0;
+    }
+    return bwd_maps(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                    nthreads, h0, gl, dh0, g0, ggl, dg0);
 }
 
 /* Number of threads the OpenMP runtime would use (1 without OpenMP). */

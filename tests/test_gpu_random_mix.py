@@ -22,6 +22,7 @@ def _case(seed):
     kw = dict(flip_h=bool(r.random() < 0.5), flip_w=bool(r.random() < 0.5), vertical_first=bool(r.random() < 0.5))
     opts = dict(gate=bool(r.random() < 0.3), softplus=bool(r.random() < 0.3), carry=bool(r.random() < 0.3),
                 waves=str(int(r.integers(1, 4))) if r.random() < 0.3 else None)
+    opts["row_carry"] = bool(r.random() < 0.4) and not opts["gate"]  # (carried row states take no gate)
     return shape, dtype, kw, opts
 
 
@@ -33,7 +34,7 @@ def _dev(a, dtype):
     return a.astype(np.float64), torch.from_numpy(a).cuda()
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(60))
 def test_random_mix(seed, monkeypatch):
     shape, dtype, kw, opts = _case(seed)
     if opts["waves"]:
@@ -50,16 +51,28 @@ def test_random_mix(seed, monkeypatch):
         raw, args[1] = _dev(r.standard_normal(t["x"].shape), dtype)
     b, di, n, H, W = shape
     h0 = r.standard_normal((b, di, n, W)).astype(np.float32) if opts["carry"] else None
+    g0 = r.standard_normal((b, di, n, H)).astype(np.float32) if opts["row_carry"] else None
     res = pkg.scan_fwd_mamba(*args, z=zd, delta_softplus=opts["softplus"],
                              h_init=None if h0 is None else torch.from_numpy(h0).cuda(),
-                             return_last_state=opts["carry"], **kw)
+                             return_last_state=opts["carry"],
+                             hh_init=None if g0 is None else torch.from_numpy(g0).cuda(),
+                             return_last_row_state=opts["row_carry"], **kw)
     pkg.sync_check()
-    y, hl = res if opts["carry"] else (res, None)
+    res = res if isinstance(res, tuple) else (res,)
+    y = res[0]
+    hl = res[1] if opts["carry"] else None
+    gl = res[-1] if opts["row_carry"] else None
     # the oracle sees the caller's inputs only: the step size in fp64
     dt = oracle.softplus(raw) if opts["softplus"] else raw
-    if opts["carry"]:
-        ref, ref_hl = oracle.fwd(t["x"], dt, t["A"], t["B"], t["C"], t["D"], h_init=h0, return_last=True, **kw)
-        check(hl.double().cpu().numpy(), ref_hl, "f32", f"mix {seed} h_last")
+    if opts["carry"] or opts["row_carry"]:
+        out = oracle.fwd(t["x"], dt, t["A"], t["B"], t["C"], t["D"], h_init=h0, return_last=opts["carry"],
+                         hh_init=g0, return_last_col=opts["row_carry"], **kw)
+        out = out if isinstance(out, tuple) else (out,)
+        ref = out[0]
+        if opts["carry"]:
+            check(hl.double().cpu().numpy(), out[1], "f32", f"mix {seed} h_last")
+        if opts["row_carry"]:
+            check(gl.double().cpu().numpy(), out[-1], "f32", f"mix {seed} hh_last")
     else:
         ref = oracle.fwd(t["x"], dt, t["A"], t["B"], t["C"], t["D"], **kw)
     if z is not None:

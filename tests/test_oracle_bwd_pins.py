@@ -282,7 +282,50 @@ def pin_carried_state_no_rows_of_decay(lib):
     assert err < 1e-13, f"dh_init with no decay: {err:.2e}"
 
 
-CARRY_BWD_PINS = [pin_carried_state_finite_differences, pin_carried_state_no_rows_of_decay]
+def pin_tile_backward_finite_differences(lib):
+    """The backward of a tile (both carried states in, both last states out)
+    for L = sum(dy * y) + sum(g * h_last) + sum(gg * hh_last), in every
+    direction and order: every gradient element, dh_init's and dhh_init's
+    too, against a central difference of L computed with the forward pass."""
+    shape, seed = (1, 2, 2, 3, 4), 40
+    for fh in (False, True):
+        for fw in (False, True):
+            for vf in (False, True):
+                ins = _inputs(*shape, seed)
+                r = np.random.default_rng(seed + 4 * fh + 2 * fw + vf)
+                b, d, n, H, W = shape
+                ins["h_init"] = r.standard_normal((b, d, n, W))
+                ins["hh_init"] = r.standard_normal((b, d, n, H))
+                dy = r.standard_normal(ins["x"].shape)
+                gl = r.standard_normal((b, d, n, W))
+                ggl = r.standard_normal((b, d, n, H))
+                kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+
+                def loss():
+                    y, hl, gg = oracle.fwd(*(ins[k] for k in KEYS), h_init=ins["h_init"], hh_init=ins["hh_init"],
+                                           return_last=True, return_last_col=True, lib=lib, **kw)
+                    return float(np.sum(y * dy) + np.sum(hl * gl) + np.sum(gg * ggl))
+
+                g = oracle.bwd(*(ins[k] for k in KEYS), dy, h_init=ins["h_init"], dh_last=gl, hh_init=ins["hh_init"],
+                               dhh_last=ggl, lib=lib, **kw)
+                for k, gk in list(GRAD.items()) + [("h_init", "dh_init"), ("hh_init", "dhh_init")]:
+                    base = ins[k]
+                    fd = np.empty_like(base)
+                    for idx in np.ndindex(base.shape):
+                        h = 1e-6 * max(1.0, abs(base[idx]))
+                        orig = base[idx]
+                        base[idx] = orig + h
+                        lp = loss()
+                        base[idx] = orig - h
+                        lm = loss()
+                        base[idx] = orig
+                        fd[idx] = (lp - lm) / (2 * h)
+                    err = np.max(np.abs(g[gk] - fd) / (1.0 + np.abs(fd)))
+                    assert err < 1e-6, f"{gk} vs finite differences, {kw}: {err:.2e}"
+
+
+CARRY_BWD_PINS = [pin_carried_state_finite_differences, pin_carried_state_no_rows_of_decay,
+                  pin_tile_backward_finite_differences]
 
 
 @pytest.mark.parametrize("pin", CARRY_BWD_PINS, ids=lambda f: f.__name__)
@@ -298,6 +341,12 @@ CARRY_BWD_MUTANTS = {
         ("dh0[j] = (H > 0) ? a[j] * gh[j] : (gl ? gl[j] : 0.0);", "dh0[j] = (H > 0) ? gh[j] : (gl ? gl[j] : 0.0);"),
     "decay derivative ignores the carried state":
         ("const double up = (i > 0) ? h[p - W] : (h0 ? h0[j] : 0.0);", "const double up = (i > 0) ? h[p - W] : 0.0;"),
+    "dL/dhh_last not fed into the row adjoint":
+        ("a[i * W + j + 1] * ghh[i * W + j + 1] : (ggl ? ggl[i] : 0.0);", "a[i * W + j + 1] * ghh[i * W + j + 1] : 0.0;"),
+    "dhh_init without the first column's decay":
+        ("if (dg0) dg0[i] = (W > 0) ? a[i * W] * ghh[i * W] :", "if (dg0) dg0[i] = (W > 0) ? ghh[i * W] :"),
+    "decay derivative ignores the carried row state":
+        ("const double left = (j > 0) ? hh[p - 1] : (g0 ? g0[i] : 0.0);", "const double left = (j > 0) ? hh[p - 1] : 0.0;"),
 }
 
 
