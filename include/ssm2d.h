@@ -299,18 +299,22 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
  * handed out, dh_init (may be NULL: not computed) receives dL/dh_init; all
  * float32 [batch][d_inner][d_state][W]. The vertical adjoint starts from
  * dh_last and hands out dh_init = Abar(first row) g_h(first row); the first
- * row's decay derivative uses h_init. Horizontal-first order only (with
- * SSM2D_VERTICAL_FIRST -> SSM2D_ERR_UNSUPPORTED); no carried row states.
+ * row's decay derivative uses h_init. Carried row states likewise: hh_init,
+ * dhh_last, dhh_init, float32 [batch][d_inner][d_state][H] (the row
+ * adjoint starts from dhh_last and hands out Abar(first column) g_hh(first
+ * column)), so a tiled forward has a tiled backward. With
+ * SSM2D_VERTICAL_FIRST the two kinds trade places on the transposed map.
  * Elementwise passes run around the backward's three kernels; scratch of
  * up to three tensors shaped like x per (device, stream). ddelta_bias is
  * accumulated with atomics (last bits may vary between runs). Other flags
  * -> SSM2D_ERR_BAD_FLAGS; errors otherwise as for ssm2d_scan_bwd. */
 int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B,
                          const float *C, const float *D, const float *z, const float *delta_bias,
-                         const float *h_init, const float *dh_last, const float *dy, float *dx,
-                         float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
-                         float *ddelta_bias, float *dh_init, int64_t batch, int64_t d_inner,
-                         int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream);
+                         const float *h_init, const float *dh_last, const float *hh_init,
+                         const float *dhh_last, const float *dy, float *dx, float *ddelta, float *dA,
+                         float *dB, float *dC, float *dD, float *dz, float *ddelta_bias, float *dh_init,
+                         float *dhh_init, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
+                         int64_t W, uint32_t flags, void *stream);
 
 /* bf16 variant: x, delta, B, C, z, dy, dx, ddelta, dB, dC, dz bfloat16 bits.
  * With any option (z, delta_bias or softplus) every tensor the chain rule
@@ -321,8 +325,9 @@ int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, con
 int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A,
                               const uint16_t *B, const uint16_t *C, const float *D, const uint16_t *z,
                               const float *delta_bias, const float *h_init, const float *dh_last,
-                              const uint16_t *dy, uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB,
-                              uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias, float *dh_init,
+                              const float *hh_init, const float *dhh_last, const uint16_t *dy,
+                              uint16_t *dx, uint16_t *ddelta, float *dA, uint16_t *dB, uint16_t *dC,
+                              float *dD, uint16_t *dz, float *ddelta_bias, float *dh_init, float *dhh_init,
                               int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
                               uint32_t flags, void *stream);
 

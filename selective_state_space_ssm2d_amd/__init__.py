@@ -68,7 +68,7 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_bwd_mamba", "ssm2d_scan_bwd_mamba_bf16"):
         f = getattr(lib, name)
-        f.argtypes = [vp] * 20 + [i64] * 5 + [ctypes.c_uint32, vp]
+        f.argtypes = [vp] * 23 + [i64] * 5 + [ctypes.c_uint32, vp]
         f.restype = ctypes.c_int
     for name in ("ssm2d_scan_bwd", "ssm2d_scan_bwd_bf16"):
         f = getattr(lib, name)
@@ -332,12 +332,15 @@ def scan_bwd(x, delta, A, B, C, D, dy, out=None, stream=None, *, flip_h=False, f
 
 
 def scan_bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, *, delta_softplus=False, h_init=None,
-                   dh_last=None, flip_h=False, flip_w=False, vertical_first=False, stream=None):
+                   dh_last=None, hh_init=None, dhh_last=None, flip_h=False, flip_w=False, vertical_first=False,
+                   stream=None):
     """Gradients of scan_fwd_mamba (include/ssm2d.h, ssm2d_scan_bwd_mamba):
     scan_bwd's dict with ddelta taken with respect to the raw delta, plus dz
-    (when z is given), ddelta_bias (when delta_bias is given) and dh_init
+    (when z is given), ddelta_bias (when delta_bias is given), dh_init
     (when h_init or dh_last is given: the forward's carried vertical state
-    and dL/dh_last, float32 [batch, d_inner, d_state, W])."""
+    and dL/dh_last, float32 [batch, d_inner, d_state, W]) and dhh_init (when
+    hh_init or dhh_last is given: the carried row state and dL/dhh_last,
+    float32 [batch, d_inner, d_state, H])."""
     import torch
 
     lib = load_library()
@@ -357,17 +360,20 @@ def scan_bwd_mamba(x, delta, A, B, C, D, dy, z=None, delta_bias=None, *, delta_s
         g["dz"] = torch.empty_like(z)
     if delta_bias is not None:
         g["ddelta_bias"] = torch.empty_like(delta_bias)
-    cshape = (batch, d_inner, d_state, W)
-    for name, t in (("h_init", h_init), ("dh_last", dh_last)):
-        if t is not None and (t.shape != cshape or t.dtype != torch.float32 or t.device != x.device
+    cshape, rshape = (batch, d_inner, d_state, W), (batch, d_inner, d_state, H)
+    for name, t, shp, what in (("h_init", h_init, cshape, "W"), ("dh_last", dh_last, cshape, "W"),
+                               ("hh_init", hh_init, rshape, "H"), ("dhh_last", dhh_last, rshape, "H")):
+        if t is not None and (t.shape != shp or t.dtype != torch.float32 or t.device != x.device
                               or not t.is_contiguous()):
-            raise ValueError(f"{name} must be contiguous float32 [batch, d_inner, d_state, W] on x's device")
+            raise ValueError(f"{name} must be contiguous float32 [batch, d_inner, d_state, {what}] on x's device")
     if h_init is not None or dh_last is not None:
         g["dh_init"] = torch.empty(cshape, dtype=torch.float32, device=x.device)
+    if hh_init is not None or dhh_last is not None:
+        g["dhh_init"] = torch.empty(rshape, dtype=torch.float32, device=x.device)
     flags = ((DELTA_SOFTPLUS if delta_softplus else 0) | (FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0)
              | (VERTICAL_FIRST if vertical_first else 0))
     fn = lib.ssm2d_scan_bwd_mamba if x.dtype == torch.float32 else lib.ssm2d_scan_bwd_mamba_bf16
-    args = [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, dy)] + \
-        [_ptr(g.get(k)) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh_init")]
+    args = [_ptr(t) for t in (x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, hh_init, dhh_last, dy)] + \
+        [_ptr(g.get(k)) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh_init", "dhh_init")]
     _call(fn, lib, x.device, args + [batch, d_inner, d_state, H, W, flags, _stream_handle(stream)])
     return g

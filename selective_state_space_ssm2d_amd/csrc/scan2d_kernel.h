@@ -75,10 +75,11 @@ constexpr int kMaxWaves = 10;                  // waves per workgroup (strips + 
 //   kModeEdges       (with kModeBackward) chains cross workgroups without
 //                    courier waves: boundary strips use the global ring
 //                    themselves
-//   kModeRowCarry    (forward, not accumulating or gated) carried horizontal
-//                    states: each row's recurrence starts from hh_init and
-//                    its state after the last column goes to hh_last (a band
-//                    of columns continuing a scan)
+//   kModeRowCarry    (not accumulating or gated) carried horizontal states:
+//                    each row's recurrence starts from hh_init and its state
+//                    after the last column goes to hh_last (a band of columns
+//                    continuing a scan; in the adjoint pass dL/dhh_last in,
+//                    dL/dhh_init out)
 constexpr int kModeFlipW = 1;
 constexpr int kModeVFirst = 2;
 constexpr int kModeAccumulate = 4;
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     constexpr bool EDGES = (MODE & kModeEdges) != 0;
     constexpr bool RC = (MODE & kModeRowCarry) != 0;
     static_assert(!EDGES || BWD, "courier-free chains: adjoint pass only");
-    static_assert(!RC || (!ACC && !GATE && !STATES && !BWD), "carried row states: plain forward output only");
+    static_assert(!RC || (!ACC && !GATE), "carried row states: not accumulated or gated");
     static_assert(!GATE || (!ACC && !STATES && !BWD), "gate: plain output only");
     static_assert(!BWD || (!VF && !ACC && !STATES && K == 4 && G == 8), "backward: one layout");
     static_assert(!BWD || !COOP || EDGES, "backward with the shared row ring: courier-free chains only");
@@ -1134,7 +1135,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             // packet `nb` is staged (and its x, delta read into `on`) first,
             // so that LDS traffic overlaps this row's arithmetic.
             auto do_row = [&](const int i, const Ops &o, const Chunk (&nb)[PASSES], Ops &on, const T (&yo)[KO],
-                              const float4 (&hcur)[NPL], const float4 (&hnext)[NPL]) {
+                              const float4 (&hcur)[NPL], const float4 (&hnext)[NPL], const float (&rcur)[NPL]) {
                 const LT *pk = row_base(i);
                 float Bv[NPL][K], Cv[NPL][K], xo[KO], dyv[K], dyo[KO];
 #pragma unroll
@@ -1165,7 +1166,7 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     for (int k = 0; k < NPL; ++k) hh[k] = src_c[k];
                 } else if constexpr (RC) {
 #pragma unroll
-                    for (int k = 0; k < NPL; ++k) hh[k] = hcur[k].x;  // the row's carried state (or 0)
+                    for (int k = 0; k < NPL; ++k) hh[k] = rcur[k];  // the row's carried state (or 0)
                 } else {
 #pragma unroll
                     for (int k = 0; k < NPL; ++k) hh[k] = 0.0f;
@@ -1481,8 +1482,10 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             Chunk bufA[P][PASSES], bufB[P][PASSES];
             T yoA[P][KO], yoB[P][KO];
             float4 hbA[P][NPL], hbB[P][NPL];
+            float rcA[P][NPL], rcB[P][NPL];  // carried row states (kModeRowCarry)
             Ops ops[2];
-            auto load_rows = [&](Chunk (&buf)[P][PASSES], T (&yo)[P][KO], float4 (&hb)[P][NPL], const int first) {
+            auto load_rows = [&](Chunk (&buf)[P][PASSES], T (&yo)[P][KO], float4 (&hb)[P][NPL], float (&rc)[P][NPL],
+                                 const int first) {
 #pragma unroll
                 for (int s = 0; s < P; ++s) {
 #pragma unroll
@@ -1505,12 +1508,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                                 t <= H ? hlast - static_cast<long>(t) * TILE + k * kWave * 4 : zeros_f);
                     }
                     if constexpr (RC) {
-                        // (hb holds the row's carried horizontal state in .x)
+                        // the row's carried horizontal state (0 unless the chain's first strip)
 #pragma unroll
                         for (int k = 0; k < NPL; ++k) {
                             long idx;
                             const bool ok = rc_in && row_carry_index(first + s, k, idx);
-                            hb[s][k] = make_float4(ok ? p.hh_init[idx] : 0.0f, 0.0f, 0.0f, 0.0f);
+                            rc[s][k] = ok ? p.hh_init[idx] : 0.0f;
                         }
                     }
                 }
@@ -1532,34 +1535,34 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     signal_fence();
                 }
             }
-            load_rows(bufA, yoA, hbA, 0);
-            load_rows(bufB, yoB, hbB, P);
+            load_rows(bufA, yoA, hbA, rcA, 0);
+            load_rows(bufB, yoB, hbB, rcB, P);
             confirm(0, stage(bufA[0], 0, ops[0]), ops[0]);
             int i0 = 0;
             for (; i0 + 2 * P <= H; i0 += 2 * P) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s], hbA[s],
-                           s + 1 < P ? hbA[s + 1] : hbB[0]);
-                load_rows(bufA, yoA, hbA, i0 + 2 * P);
+                           s + 1 < P ? hbA[s + 1] : hbB[0], rcA[s]);
+                load_rows(bufA, yoA, hbA, rcA, i0 + 2 * P);
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufA[0], ops[(P + s + 1) % 2], yoB[s],
-                           hbB[s], s + 1 < P ? hbB[s + 1] : hbA[0]);
-                load_rows(bufB, yoB, hbB, i0 + 3 * P);
+                           hbB[s], s + 1 < P ? hbB[s + 1] : hbA[0], rcB[s]);
+                load_rows(bufB, yoB, hbB, rcB, i0 + 3 * P);
             }
             if (i0 < H) {
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     if (i0 + s < H)
                         do_row(i0 + s, ops[s % 2], s + 1 < P ? bufA[s + 1] : bufB[0], ops[(s + 1) % 2], yoA[s], hbA[s],
-                               s + 1 < P ? hbA[s + 1] : hbB[0]);
+                               s + 1 < P ? hbA[s + 1] : hbB[0], rcA[s]);
                 // (the last slot here is never a map row: i0 + 2P > H)
 #pragma unroll
                 for (int s = 0; s < P; ++s)
                     if (i0 + P + s < H)
                         do_row(i0 + P + s, ops[(P + s) % 2], s + 1 < P ? bufB[s + 1] : bufB[s], ops[(P + s + 1) % 2], yoB[s],
-                               hbB[s], s + 1 < P ? hbB[s + 1] : hbB[s]);
+                               hbB[s], s + 1 < P ? hbB[s + 1] : hbB[s], rcB[s]);
             }
         };
         using N0 = std::integral_constant<int, 0>;
@@ -1914,7 +1917,13 @@ bool fast_path_taken<uint16_t>(const Plan &pl, int align);
     SSM2D_DISPATCH_DECL(TT, dispatch_rowc)             \
     SSM2D_DISPATCH_DECL(TT, dispatch_rowc_flipw)       \
     SSM2D_DISPATCH_DECL(TT, dispatch_rowc_vfirst)      \
-    SSM2D_DISPATCH_DECL(TT, dispatch_rowc_flipw_vfirst)
+    SSM2D_DISPATCH_DECL(TT, dispatch_rowc_flipw_vfirst) \
+    SSM2D_DISPATCH_DECL(TT, dispatch_states_rowc)       \
+    SSM2D_DISPATCH_DECL(TT, dispatch_states_flipw_rowc) \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_rowc)          \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_edges_rowc)    \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_ltr_rowc)      \
+    SSM2D_DISPATCH_DECL(TT, dispatch_bwd_ltr_edges_rowc)
 SSM2D_MODE_DECLS(float)
 SSM2D_MODE_DECLS(uint16_t)
 #undef SSM2D_MODE_DECLS

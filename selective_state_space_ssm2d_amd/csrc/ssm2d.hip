@@ -763,16 +763,21 @@ template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
              int64_t W, void *stream, unsigned flags = 0, const float *h_init = nullptr, const float *dh_last = nullptr,
-             float *dh_init = nullptr);
+             float *dh_init = nullptr, const float *hh_init = nullptr, const float *dhh_last = nullptr,
+             float *dhh_init = nullptr);
 
 // Backward of the vertical-first order: that scan is the horizontal-first
 // scan of the transposed maps (the column recurrence becomes the row
 // recurrence), with the two flips trading places, so its gradients are the
 // transposed maps' gradients, transposed back. dA and dD need no transpose.
+// Carried states trade places there: the vertical-first scan's state carried
+// down its columns is the transposed map's row state, and the other way round
+// (both arrays keep their layout).
 template <typename T>
 int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy,
                     T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner,
-                    int64_t d_state, int64_t H, int64_t W, void *stream, unsigned flags, int dev)
+                    int64_t d_state, int64_t H, int64_t W, void *stream, unsigned flags, int dev, const float *h_init,
+                    const float *dh_last, float *dh_init, const float *hh_init, const float *dhh_last, float *dhh_init)
 {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const long me = batch * d_inner, mb = batch * d_state;
@@ -797,7 +802,7 @@ int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, cons
     const unsigned tflags = ((flags & SSM2D_FLIP_H) ? SSM2D_FLIP_W : 0u) | ((flags & SSM2D_FLIP_W) ? SSM2D_FLIP_H : 0u);
     st = scan_bwd<T>(xt, dt, A, d_state ? Bt : nullptr, d_state ? Ct : nullptr, D, dyt, dxt, ddt, dA,
                      d_state ? dBt : nullptr, d_state ? dCt : nullptr, dD, batch, d_inner, d_state, W, H, stream,
-                     tflags);
+                     tflags, hh_init, dhh_last, dhh_init, h_init, dh_last, dh_init);
     if (st != SSM2D_OK) return st;
     if ((st = transpose_maps(dxt, dx, me, W, H, s)) != SSM2D_OK) return st;
     if ((st = transpose_maps(ddt, ddelta, me, W, H, s)) != SSM2D_OK) return st;
@@ -812,11 +817,13 @@ int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, cons
 // and order of the forward scan. h_init (may be null): the carried vertical
 // state the forward started from; dh_last (may be null): dL/dh_last for the
 // state it handed out; dh_init (may be null): receives dL/dh_init (all
-// float32 [batch][d_inner][d_state][W]; horizontal-first order only).
+// float32 [batch][d_inner][d_state][W]); hh_init, dhh_last, dhh_init: the
+// same for the carried row state ([batch][d_inner][d_state][H]).
 template <typename T>
 int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *dy, T *dx,
              T *ddelta, float *dA, T *dB, T *dC, float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H,
-             int64_t W, void *stream, unsigned flags, const float *h_init, const float *dh_last, float *dh_init)
+             int64_t W, void *stream, unsigned flags, const float *h_init, const float *dh_last, float *dh_init,
+             const float *hh_init, const float *dhh_last, float *dhh_init)
 {
     if ((flags & ~kKnownFlags) != 0 || (flags & (SSM2D_ACCUMULATE | SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
         return SSM2D_ERR_BAD_FLAGS;
@@ -838,27 +845,34 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(A) || misaligned(B) || misaligned(C) || misaligned(D) ||
         misaligned(dy) || misaligned(dx) || misaligned(ddelta) || misaligned(dA) || misaligned(dB) || misaligned(dC) ||
-        misaligned(dD) || misaligned(h_init) || misaligned(dh_last) || misaligned(dh_init))
+        misaligned(dD) || misaligned(h_init) || misaligned(dh_last) || misaligned(dh_init) || misaligned(hh_init) ||
+        misaligned(dhh_last) || misaligned(dhh_init))
         return SSM2D_ERR_MISALIGNED;
-    const bool carry = h_init || dh_last || dh_init;
-    // (vertical-first: the carried state is the transposed map's row state)
-    if (carry && (flags & SSM2D_VERTICAL_FIRST)) return SSM2D_ERR_UNSUPPORTED;
+    const bool rcarry = hh_init || dhh_last || dhh_init;
 
     int dev = 0;
     SSM2D_HIP_TRY(hipGetDevice(&dev));
     std::lock_guard<std::recursive_mutex> lock(g_mutex);
     if (take_timeout_flag(dev, stream)) return SSM2D_ERR_DEVICE_TIMEOUT;
     const hipStream_t s0 = static_cast<hipStream_t>(stream);
-    if (dh_init && batch > 0 && d_state > 0 && W > 0 && H == 0) {
-        // no rows: the handed-out state is h_init itself
-        const long n = batch * d_inner * d_state * W;
-        copy_or_zero_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s0>>>(dh_last, dh_init, n);
+    // no rows (no columns): a handed-out state is the carried one itself
+    const bool vf = (flags & SSM2D_VERTICAL_FIRST) != 0;
+    float *cdst = vf ? dhh_init : dh_init, *rdst = vf ? dh_init : dhh_init;
+    const float *csrc = vf ? dhh_last : dh_last, *rsrc = vf ? dh_last : dhh_last;
+    const long cn = batch * d_inner * d_state * (vf ? H : W), rn = batch * d_inner * d_state * (vf ? W : H);
+    if (cdst && cn > 0 && (vf ? W : H) == 0) {
+        copy_or_zero_kernel<<<dim3(static_cast<unsigned>((cn + 255) / 256)), dim3(256), 0, s0>>>(csrc, cdst, cn);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
     }
-    if ((flags & SSM2D_VERTICAL_FIRST) && work)
+    if (rdst && rn > 0 && (vf ? H : W) == 0) {
+        copy_or_zero_kernel<<<dim3(static_cast<unsigned>((rn + 255) / 256)), dim3(256), 0, s0>>>(rsrc, rdst, rn);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (vf && work)
         return scan_bwd_vfirst<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                                  stream, flags, dev);
+                                  stream, flags, dev, h_init, dh_last, dh_init, hh_init, dhh_last, dhh_init);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t state_elems = work ? static_cast<size_t>(tiles) * npl * kWave * 4 : 0;
     const long part_stride = batch * d_state * H * 4 * nstrips;  // floats per channel block
@@ -892,19 +906,26 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const int hi = static_cast<int>(H), wi = static_cast<int>(W);
     const int align = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);
     // 1. the forward pass again, in its direction, storing every state
-    Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates | (f_w ? kModeFlipW : 0));
+    const int rc = rcarry ? kModeRowCarry : 0;
+    Plan pf = make_plan(batch, d_inner, d_state, H, W, kModeStates | (f_w ? kModeFlipW : 0) | rc);
     pf.bw = &bw;
     pf.flip_h = f_h ? 1 : 0;
     pf.h_init = h_init;
+    pf.hh_init = hh_init;
     choose_coop<T>(pf, H, align);
     if (pf.npl != npl || pf.n_dblk != n_dblk || pf.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
-    int st = f_w ? dispatch_states_flipw(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align)
+    int st;
+    if (rcarry)
+        st = f_w ? dispatch_states_flipw_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align)
+                 : dispatch_states_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
+    else
+        st = f_w ? dispatch_states_flipw(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align)
                  : dispatch_states(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pf, dev, stream, align);
     if (st != SSM2D_OK) return st;
     // 2. the adjoint scans from the opposite corner, with every local
     // derivative (chains cut into several workgroups: the courier-free
     // kernels, which fit 8 strips per workgroup instead of 6)
-    const int bmode = kModeBackward | (f_w ? 0 : kModeFlipW);
+    const int bmode = kModeBackward | (f_w ? 0 : kModeFlipW) | rc;
     Plan pb = make_plan(batch, d_inner, d_state, H, W, bmode);
     const bool edges = pb.groups > 1;
     if (edges) pb = make_plan(batch, d_inner, d_state, H, W, bmode | kModeEdges);
@@ -912,14 +933,24 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     pb.bw = &bw;
     pb.h_init = dh_last;   // the vertical adjoint's carry in and out
     pb.h_last = dh_init;
+    pb.hh_init = dhh_last;  // the row adjoint's carry in and out
+    pb.hh_last = dhh_init;
     choose_coop<T>(pb, H, align);
     if (pb.npl != npl || pb.n_dblk != n_dblk || pb.nstrips != nstrips) return SSM2D_ERR_UNSUPPORTED;
-    if (f_w)
+    if (rcarry) {
+        if (f_w)
+            st = edges ? dispatch_bwd_ltr_edges_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
+                       : dispatch_bwd_ltr_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+        else
+            st = edges ? dispatch_bwd_edges_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
+                       : dispatch_bwd_rowc(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    } else if (f_w) {
         st = edges ? dispatch_bwd_ltr_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
                    : dispatch_bwd_ltr(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
-    else
+    } else {
         st = edges ? dispatch_bwd_edges(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align)
                    : dispatch_bwd(x, delta, A, B, C, D, dx, bi, di, ni, hi, wi, pb, dev, stream, align);
+    }
     if (st != SSM2D_OK) return st;
     // 3. dB and dC: sums over the channel blocks
     if (d_state > 0) {
@@ -943,9 +974,10 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
 // gradient is rounded to bf16 once.
 template <typename T>
 int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, const T *z,
-                   const float *delta_bias, const float *h_init, const float *dh_last, const T *dy, T *dx, T *ddelta,
-                   float *dA, T *dB, T *dC, float *dD, T *dz, float *ddelta_bias, float *dh_init, int64_t batch,
-                   int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags, void *stream)
+                   const float *delta_bias, const float *h_init, const float *dh_last, const float *hh_init,
+                   const float *dhh_last, const T *dy, T *dx, T *ddelta, float *dA, T *dB, T *dC, float *dD, T *dz,
+                   float *ddelta_bias, float *dh_init, float *dhh_init, int64_t batch, int64_t d_inner,
+                   int64_t d_state, int64_t H, int64_t W, unsigned flags, void *stream)
 {
     constexpr unsigned kDirs = SSM2D_FLIP_H | SSM2D_FLIP_W | SSM2D_VERTICAL_FIRST;
     if ((flags & ~(SSM2D_DELTA_SOFTPLUS | kDirs)) != 0) return SSM2D_ERR_BAD_FLAGS;
@@ -954,10 +986,8 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     if (d_inner == 0) return SSM2D_OK;
     if ((z && !dz) || (ddelta_bias && !delta_bias)) return SSM2D_ERR_NULLPTR;
     if (misaligned(z) || misaligned(dz) || misaligned(delta_bias) || misaligned(ddelta_bias) || misaligned(h_init) ||
-        misaligned(dh_last) || misaligned(dh_init))
+        misaligned(dh_last) || misaligned(dh_init) || misaligned(hh_init) || misaligned(dhh_last) || misaligned(dhh_init))
         return SSM2D_ERR_MISALIGNED;
-    // (vertical-first: the carried state is the transposed map's row state)
-    if ((h_init || dh_last || dh_init) && (dirs & SSM2D_VERTICAL_FIRST)) return SSM2D_ERR_UNSUPPORTED;
     const bool softplus = (flags & SSM2D_DELTA_SOFTPLUS) != 0;
     const bool prep = delta_bias || softplus;
     const long total = batch * d_inner * H * W;
@@ -973,7 +1003,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     }
     if (total == 0 || d_state > SSM2D_MAX_STATE_BWD || (!prep && !z))  // the backward alone (it also reports sizes)
         return scan_bwd<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                           stream, dirs, h_init, dh_last, dh_init);
+                           stream, dirs, h_init, dh_last, dh_init, hh_init, dhh_last, dhh_init);
     if (!x || !delta || !dy || !dx || !ddelta || !D || (d_state > 0 && (!A || !B || !C || !dB || !dC || !dA)) || !dD)
         return SSM2D_ERR_NULLPTR;
     if (misaligned(x) || misaligned(delta) || misaligned(dy) || misaligned(dx) || misaligned(ddelta))
@@ -1020,7 +1050,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
         TW *y0 = nullptr;
         if ((st = buf(kSlotY0, eb, &y0)) != SSM2D_OK) return st;
         st = scan_fwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, y0, batch, d_inner,
-                          d_state, H, W, dirs, false, stream, nullptr, nullptr, h_init, nullptr);
+                          d_state, H, W, dirs, false, stream, nullptr, nullptr, h_init, nullptr, hh_init, nullptr);
         if (st != SSM2D_OK) return st;
         gate_bwd_kernel<T, TW><<<dim3(nblk), dim3(256), 0, s>>>(dy, y0, z, dz, g, total);
         const hipError_t e = hipGetLastError();
@@ -1042,7 +1072,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
     }
     st = scan_bwd<TW>(xw, dstep, A, d_state ? Bw : nullptr, d_state ? Cw : nullptr, D, g, dxw, ddw, dA,
                       d_state ? dBw : nullptr, d_state ? dCw : nullptr, dD, batch, d_inner, d_state, H, W, stream, dirs,
-                      h_init, dh_last, dh_init);
+                      h_init, dh_last, dh_init, hh_init, dhh_last, dhh_init);
     if (st != SSM2D_OK) return st;
     // d delta with respect to the raw step size, d bias (and the rounding)
     if (prep || WIDE) {
@@ -1186,23 +1216,27 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
 
 int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,
                          const float *D, const float *z, const float *delta_bias, const float *h_init,
-                         const float *dh_last, const float *dy, float *dx, float *ddelta, float *dA, float *dB,
-                         float *dC, float *dD, float *dz, float *ddelta_bias, float *dh_init, int64_t batch,
-                         int64_t d_inner, int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
+                         const float *dh_last, const float *hh_init, const float *dhh_last, const float *dy,
+                         float *dx, float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
+                         float *ddelta_bias, float *dh_init, float *dhh_init, int64_t batch, int64_t d_inner,
+                         int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
-    return scan_bwd_mamba<float>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, dy, dx, ddelta, dA, dB, dC, dD,
-                                 dz, ddelta_bias, dh_init, batch, d_inner, d_state, H, W, flags, stream);
+    return scan_bwd_mamba<float>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, hh_init, dhh_last, dy, dx,
+                                 ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh_init, dhh_init, batch, d_inner, d_state,
+                                 H, W, flags, stream);
 }
 
 int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B,
                               const uint16_t *C, const float *D, const uint16_t *z, const float *delta_bias,
-                              const float *h_init, const float *dh_last, const uint16_t *dy, uint16_t *dx,
-                              uint16_t *ddelta, float *dA, uint16_t *dB, uint16_t *dC, float *dD, uint16_t *dz,
-                              float *ddelta_bias, float *dh_init, int64_t batch, int64_t d_inner, int64_t d_state,
+                              const float *h_init, const float *dh_last, const float *hh_init,
+                              const float *dhh_last, const uint16_t *dy, uint16_t *dx, uint16_t *ddelta, float *dA,
+                              uint16_t *dB, uint16_t *dC, float *dD, uint16_t *dz, float *ddelta_bias,
+                              float *dh_init, float *dhh_init, int64_t batch, int64_t d_inner, int64_t d_state,
                               int64_t H, int64_t W, uint32_t flags, void *stream)
 {
-    return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, dy, dx, ddelta, dA, dB, dC,
-                                    dD, dz, ddelta_bias, dh_init, batch, d_inner, d_state, H, W, flags, stream);
+    return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, z, delta_bias, h_init, dh_last, hh_init, dhh_last, dy, dx,
+                                    ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh_init, dhh_init, batch, d_inner,
+                                    d_state, H, W, flags, stream);
 }
 
 const char *ssm2d_status_string(int status)

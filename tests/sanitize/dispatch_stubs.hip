@@ -21,7 +21,10 @@ namespace ssm2d_impl {
     SSM2D_STUB(TT, dispatch_bwd_ltr_edges) SSM2D_STUB(TT, dispatch_gate) SSM2D_STUB(TT, dispatch_gate_vfirst) \
     SSM2D_STUB(TT, dispatch_gate_flipw) SSM2D_STUB(TT, dispatch_gate_flipw_vfirst)                            \
     SSM2D_STUB(TT, dispatch_rowc) SSM2D_STUB(TT, dispatch_rowc_flipw) SSM2D_STUB(TT, dispatch_rowc_vfirst)    \
-    SSM2D_STUB(TT, dispatch_rowc_flipw_vfirst)
+    SSM2D_STUB(TT, dispatch_rowc_flipw_vfirst) SSM2D_STUB(TT, dispatch_states_rowc)                             \
+    SSM2D_STUB(TT, dispatch_states_flipw_rowc) SSM2D_STUB(TT, dispatch_bwd_rowc)                              \
+    SSM2D_STUB(TT, dispatch_bwd_edges_rowc) SSM2D_STUB(TT, dispatch_bwd_ltr_rowc)                             \
+    SSM2D_STUB(TT, dispatch_bwd_ltr_edges_rowc)
 SSM2D_STUBS(float)
 SSM2D_STUBS(uint16_t)
 #undef SSM2D_STUBS

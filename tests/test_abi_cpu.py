@@ -210,20 +210,19 @@ def test_bwd_ex_validation(lib, bf16):
 def test_bwd_mamba_validation(lib, bf16):
     fn = lib.ssm2d_scan_bwd_mamba_bf16 if bf16 else lib.ssm2d_scan_bwd_mamba
     call = lambda ptrs, dims, flags: fn(*(ctypes.c_void_p(p) for p in ptrs), *dims, flags, None)
-    # x delta A B C D z bias h_init dh_last dy | dx ddelta dA dB dC dD dz dbias dh_init
-    full = [FAKE] * 20
+    # x delta A B C D z bias h_init dh_last hh_init dhh_last dy | dx ddelta dA dB dC dD dz dbias dh_init dhh_init
+    full = [FAKE] * 23
     for flags in (pkg.ACCUMULATE, pkg.FOUR_WAY, 128):
         assert call(full, [1, 2, 3, 4, 5], flags) == pkg.ERR_BAD_FLAGS, flags
-    assert call(full, [1, -2, 3, 4, 5], pkg.FLIP_H | pkg.FLIP_W) == pkg.ERR_BAD_DIM  # directions accepted
-    assert call([0] * 20, [1, 0, 3, 4, 5], 0) == pkg.OK                   # d_inner = 0: nothing to do
-    # carried states: not with the vertical-first order; aligned
-    assert call(full, [1, 2, 3, 4, 5], pkg.VERTICAL_FIRST) == pkg.ERR_UNSUPPORTED
-    for k in (8, 9, 19):
+    assert call(full, [1, -2, 3, 4, 5], pkg.FLIP_H | pkg.FLIP_W | pkg.VERTICAL_FIRST) == pkg.ERR_BAD_DIM
+    assert call([0] * 23, [1, 0, 3, 4, 5], 0) == pkg.OK                   # d_inner = 0: nothing to do
+    # carried states: aligned
+    for k in (8, 9, 10, 11, 21, 22):
         odd = list(full)
         odd[k] = FAKE + 4
         assert call(odd, [1, 2, 3, 4, 5], 0) == pkg.ERR_MISALIGNED, k
     no_dz = list(full)
-    no_dz[17] = 0
+    no_dz[19] = 0
     assert call(no_dz, [1, 2, 3, 4, 5], 0) == pkg.ERR_NULLPTR             # z given, dz missing
     no_bias = list(full)
     no_bias[7] = 0

@@ -8,6 +8,8 @@ of terms: their bar is tol (1 + |g_ref|) with the cell count folded in as
 tol = 1e-4 * max(1, sqrt(cells / 4096)). tol = 1e-4 for fp32 inputs, 2e-2 for
 bf16 inputs and outputs (fp32 state and arithmetic).
 """
+import itertools
+
 import numpy as np
 import pytest
 
@@ -368,3 +370,43 @@ def test_carried_state_backward_with_options(dtype):
         err = float(np.max(np.abs(got[k] - ref[k]) / (1.0 + np.abs(ref[k]))))
         _say(f"  {k}: {err:.3e}")
         assert err <= TOL[dtype if k == "dz" else "f32"], k
+
+
+TILE_CASES = [((1, 16, 16, 9, 64), None), ((2, 9, 8, 7, 23), None), ((1, 8, 16, 1, 29), None),
+              ((1, 5, 16, 27, 1), None), ((1, 16, 16, 13, 40), "1"), ((1, 16, 16, 140, 96), None)]
+
+
+@pytest.mark.parametrize("d", list(itertools.product((False, True), repeat=3)),
+                         ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", TILE_CASES, ids=str)
+def test_tile_backward(case, dtype, d, monkeypatch):
+    """The backward of a tile: both carried states in, dL/d(both last states)
+    in, every gradient plus dL/dh_init and dL/dhh_init out, against the
+    oracle in every direction and order."""
+    shape, waves = case
+    if waves:
+        monkeypatch.setenv("SSM2D_WAVES", waves)
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    _say(f"tile backward {shape} {dtype} {d} waves={waves}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 71, dtype=dtype)
+    b, di, n, H, W = shape
+    r = np.random.default_rng(sum(shape) + 72)
+    h0 = r.standard_normal((b, di, n, W)).astype(np.float32)
+    gl = r.standard_normal((b, di, n, W)).astype(np.float32)
+    g0 = r.standard_normal((b, di, n, H)).astype(np.float32)
+    ggl = r.standard_normal((b, di, n, H)).astype(np.float32)
+    dy, dy_dev = make_dy(t, dtype, sum(shape) + 73)
+    cu = lambda a: torch.from_numpy(a).cuda()
+    g = pkg.scan_bwd_mamba(*to_dev(t, dtype), dy_dev, h_init=cu(h0), dh_last=cu(gl), hh_init=cu(g0),
+                           dhh_last=cu(ggl), **kw)
+    pkg.sync_check()
+    got = {k: v.double().cpu().numpy() for k, v in g.items()}
+    ref = oracle.bwd(*(t[k] for k in ("x", "delta", "A", "B", "C", "D")), dy, h_init=h0, dh_last=gl, hh_init=g0,
+                     dhh_last=ggl, **kw)
+    check_grads(got, ref, dtype, b * H * W, f"tile {shape} {d}")
+    for k, length in (("dh_init", H), ("dhh_init", W)):
+        err = float(np.max(np.abs(got[k] - ref[k]) / (1.0 + np.abs(ref[k])))) if ref[k].size else 0.0
+        _say(f"  {k}: {err:.3e}")
+        assert err <= TOL["f32"] * max(1.0, np.sqrt(max(H, W) / 64.0)), k
