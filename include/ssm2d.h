@@ -80,7 +80,7 @@ extern "C" {
 #endif
 
 #define SSM2D_MAX_STATE 64
-#define SSM2D_MAX_STATE_BWD 32
+#define SSM2D_MAX_STATE_BWD 32   /* states the backward's kernels hold at once */
 #define SSM2D_MAX_SIDE 65535
 
 typedef enum {
@@ -244,10 +244,13 @@ int ssm2d_scan_fwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const fl
  * or the end of the process). dA and dD are accumulated with
  * atomics, so their last bits may differ from run to run; every other output
  * is deterministic.
+ * More than SSM2D_MAX_STATE_BWD states (up to SSM2D_MAX_STATE): the states'
+ * recurrences are independent, so the backward runs on chunks of at most
+ * SSM2D_MAX_STATE_BWD states gathered into scratch tensors and sums the
+ * chunks' dx and d delta (in fp32; bf16 calls are widened to fp32 first).
  * Errors as for ssm2d_scan_fwd (with d_state == 0, A, B, C, dA, dB and dC
- * are not touched and may be NULL), plus: d_state > SSM2D_MAX_STATE_BWD ->
- * SSM2D_ERR_UNSUPPORTED. d_inner == 0: nothing to do. batch, H or W == 0:
- * dA and dD are zeroed, nothing else is touched. */
+ * are not touched and may be NULL). d_inner == 0: nothing to do. batch, H
+ * or W == 0: dA and dD are zeroed, nothing else is touched. */
 int ssm2d_scan_bwd(const float *x, const float *delta, const float *A, const float *B,
                    const float *C, const float *D, const float *dy, float *dx, float *ddelta,
                    float *dA, float *dB, float *dC, float *dD, int64_t batch, int64_t d_inner,

@@ -281,6 +281,36 @@ __global__ void bwd_prepare_kernel(float *dA, long n_a, float *dD, long n_d)
     if (t < n_d) dD[t] = 0.0f;
 }
 
+// States [n0, n0 + nc) of an [outer][N][inner] tensor to an [outer][nc][inner]
+// one, or back (scatter).
+template <typename T>
+__global__ void state_slice_kernel(const T *src, T *dst, long outer, long N, long n0, long nc, long inner, int scatter)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= outer * nc * inner) return;
+    const long i = t % inner, j = (t / inner) % nc, o = t / (inner * nc);
+    const long full = (o * N + n0 + j) * inner + i;
+    if (scatter) dst[full] = src[t];
+    else dst[t] = src[full];
+}
+
+template <typename T>
+int state_slice(const T *src, T *dst, long outer, long N, long n0, long nc, long inner, bool scatter, hipStream_t s)
+{
+    const long n = outer * nc * inner;
+    if (n == 0) return SSM2D_OK;
+    state_slice_kernel<T><<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(src, dst, outer, N, n0, nc,
+                                                                                           inner, scatter ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSM2D_OK : hip_fail(e);
+}
+
+__global__ void add_into_kernel(float *dst, const float *src, long n)
+{
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t < n) dst[t] += src[t];
+}
+
 __device__ __forceinline__ void put(float *p, float v) { *p = v; }
 __device__ __forceinline__ void put(uint16_t *p, float v) { *p = static_cast<uint16_t>(bf16_bits(v)); }
 
@@ -620,7 +650,8 @@ enum : int {
     kSlotStep = 0, kSlotY0 = 1, kSlotG = 2,
     kSlotX32 = 3, kSlotD32 = 4, kSlotB32 = 5, kSlotC32 = 6, kSlotY32 = 7, kSlotG32 = 8,
     kSlotDX32 = 9, kSlotDD32 = 10, kSlotDB32 = 11, kSlotDC32 = 12,
-    kSlotT0 = 13  // 13 .. 21: the transposed tensors of the vertical-first backward
+    kSlotT0 = 13,  // 13 .. 21: the transposed tensors of the vertical-first backward
+    kSlotK0 = 22   // 22 .. 37: the state chunks of a backward with more than 32 states
 };
 
 template <typename T>
@@ -813,6 +844,82 @@ int scan_bwd_vfirst(const T *x, const T *delta, const float *A, const T *B, cons
     return SSM2D_OK;
 }
 
+// More than SSM2D_MAX_STATE_BWD states (fp32): the states' recurrences are
+// independent and y sums over them, so the backward runs on chunks of at most
+// that many states, gathered into scratch tensors, and adds the chunks' dx
+// and d delta; the skip term's gradients come from the first chunk alone (the
+// others get D = 0 and their dD is dropped). dA, dB, dC and the carried
+// states' gradients are scattered back by state.
+int scan_bwd_chunked(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                     const float *D, const float *dy, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                     float *dD, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, void *stream,
+                     unsigned flags, const float *h_init, const float *dh_last, float *dh_init, const float *hh_init,
+                     const float *dhh_last, float *dhh_init, int dev)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const long CH = SSM2D_MAX_STATE_BWD, HW = H * W, BD = batch * d_inner;
+    const size_t fs = sizeof(float);
+    // scratch: A, B, C, dA, dB, dC of a chunk; dx, d delta of the later
+    // chunks; a zero D and a dropped dD; the carried states of a chunk
+    const size_t sizes[16] = {static_cast<size_t>(d_inner * CH) * fs, static_cast<size_t>(batch * CH * HW) * fs,
+                              static_cast<size_t>(batch * CH * HW) * fs, static_cast<size_t>(d_inner * CH) * fs,
+                              static_cast<size_t>(batch * CH * HW) * fs, static_cast<size_t>(batch * CH * HW) * fs,
+                              static_cast<size_t>(BD * HW) * fs, static_cast<size_t>(BD * HW) * fs,
+                              static_cast<size_t>(d_inner) * fs, static_cast<size_t>(d_inner) * fs,
+                              static_cast<size_t>(BD * CH * W) * fs, static_cast<size_t>(BD * CH * W) * fs,
+                              static_cast<size_t>(BD * CH * W) * fs, static_cast<size_t>(BD * CH * H) * fs,
+                              static_cast<size_t>(BD * CH * H) * fs, static_cast<size_t>(BD * CH * H) * fs};
+    float *w[16] = {};
+    for (int k = 0; k < 16; ++k) {
+        void *v = nullptr;
+        const int st = get_aux_ws(dev, stream, kSlotK0 + k, sizes[k] + 256, &v);
+        if (st != SSM2D_OK) return st;
+        w[k] = static_cast<float *>(v);
+    }
+    float *Ac = w[0], *Bc = w[1], *Cc = w[2], *dAc = w[3], *dBc = w[4], *dCc = w[5], *dxc = w[6], *ddc = w[7];
+    float *zD = w[8], *dDc = w[9], *h0c = w[10], *glc = w[11], *dh0c = w[12], *g0c = w[13], *gglc = w[14];
+    float *dg0c = w[15];
+    int st = zero_async(zD, static_cast<size_t>(d_inner) * fs, s);
+    if (st != SSM2D_OK) return st;
+    for (long n0 = 0; n0 < d_state; n0 += CH) {
+        const long nc = std::min<long>(CH, d_state - n0);
+        const bool first = n0 == 0;
+        if ((st = state_slice(A, Ac, d_inner, d_state, n0, nc, 1, false, s)) != SSM2D_OK) return st;
+        if ((st = state_slice(B, Bc, batch, d_state, n0, nc, HW, false, s)) != SSM2D_OK) return st;
+        if ((st = state_slice(C, Cc, batch, d_state, n0, nc, HW, false, s)) != SSM2D_OK) return st;
+        if (h_init && (st = state_slice(h_init, h0c, BD, d_state, n0, nc, W, false, s)) != SSM2D_OK) return st;
+        if (dh_last && (st = state_slice(dh_last, glc, BD, d_state, n0, nc, W, false, s)) != SSM2D_OK) return st;
+        if (hh_init && (st = state_slice(hh_init, g0c, BD, d_state, n0, nc, H, false, s)) != SSM2D_OK) return st;
+        if (dhh_last && (st = state_slice(dhh_last, gglc, BD, d_state, n0, nc, H, false, s)) != SSM2D_OK) return st;
+        st = scan_bwd<float>(x, delta, Ac, Bc, Cc, first ? D : zD, dy, first ? dx : dxc, first ? ddelta : ddc, dAc,
+                             dBc, dCc, first ? dD : dDc, batch, d_inner, nc, H, W, stream,
+                             flags, h_init ? h0c : nullptr, dh_last ? glc : nullptr, dh_init ? dh0c : nullptr,
+                             hh_init ? g0c : nullptr, dhh_last ? gglc : nullptr, dhh_init ? dg0c : nullptr);
+        if (st != SSM2D_OK) return st;
+        if ((st = state_slice(static_cast<const float *>(dAc), dA, d_inner, d_state, n0, nc, 1, true, s)) != SSM2D_OK)
+            return st;
+        if ((st = state_slice(static_cast<const float *>(dBc), dB, batch, d_state, n0, nc, HW, true, s)) != SSM2D_OK)
+            return st;
+        if ((st = state_slice(static_cast<const float *>(dCc), dC, batch, d_state, n0, nc, HW, true, s)) != SSM2D_OK)
+            return st;
+        if (dh_init &&
+            (st = state_slice(static_cast<const float *>(dh0c), dh_init, BD, d_state, n0, nc, W, true, s)) != SSM2D_OK)
+            return st;
+        if (dhh_init &&
+            (st = state_slice(static_cast<const float *>(dg0c), dhh_init, BD, d_state, n0, nc, H, true, s)) != SSM2D_OK)
+            return st;
+        if (!first) {
+            const long n = BD * HW;
+            const unsigned nb = static_cast<unsigned>((n + 255) / 256);
+            add_into_kernel<<<dim3(nb), dim3(256), 0, s>>>(dx, dxc, n);
+            add_into_kernel<<<dim3(nb), dim3(256), 0, s>>>(ddelta, ddc, n);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    }
+    return SSM2D_OK;
+}
+
 // flags: SSM2D_FLIP_H / SSM2D_FLIP_W / SSM2D_VERTICAL_FIRST, the direction
 // and order of the forward scan. h_init (may be null): the carried vertical
 // state the forward started from; dh_last (may be null): dL/dh_last for the
@@ -830,7 +937,10 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const bool f_h = (flags & SSM2D_FLIP_H) != 0, f_w = (flags & SSM2D_FLIP_W) != 0;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
     if (d_inner == 0) return SSM2D_OK;
-    if (d_state > SSM2D_MAX_STATE_BWD || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
+    if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
+    // more states than the kernels hold: fp32 runs in chunks of states; bf16
+    // callers widen first (the chunks' dx and d delta are summed in fp32)
+    if (d_state > SSM2D_MAX_STATE_BWD && !std::is_same<T, float>::value) return SSM2D_ERR_UNSUPPORTED;
     const int64_t lim = (int64_t{1} << 31) - 1;
     const int64_t nstrips = (W + 3) / 4, pad = 4 * nstrips - W;
     const int64_t n_dblk = (d_inner + 7) / 8;
@@ -869,6 +979,11 @@ int scan_bwd(const T *x, const T *delta, const float *A, const T *B, const T *C,
         copy_or_zero_kernel<<<dim3(static_cast<unsigned>((rn + 255) / 256)), dim3(256), 0, s0>>>(rsrc, rdst, rn);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
+    }
+    if constexpr (std::is_same<T, float>::value) {
+        if (d_state > SSM2D_MAX_STATE_BWD && work)
+            return scan_bwd_chunked(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H,
+                                    W, stream, flags, h_init, dh_last, dh_init, hh_init, dhh_last, dhh_init, dev);
     }
     if (vf && work)
         return scan_bwd_vfirst<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
@@ -1001,7 +1116,10 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e);
     }
-    if (total == 0 || d_state > SSM2D_MAX_STATE_BWD || (!prep && !z))  // the backward alone (it also reports sizes)
+    // (bf16 with more states than the kernels hold: the widened fp32 path,
+    // whose backward runs in chunks of states)
+    const bool wide_states = std::is_same<T, uint16_t>::value && d_state > SSM2D_MAX_STATE_BWD;
+    if (total == 0 || d_state > SSM2D_MAX_STATE || (!prep && !z && !wide_states))  // the backward alone (it also reports sizes)
         return scan_bwd<T>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
                            stream, dirs, h_init, dh_last, dh_init, hh_init, dhh_last, dhh_init);
     if (!x || !delta || !dy || !dx || !ddelta || !D || (d_state > 0 && (!A || !B || !C || !dB || !dC || !dA)) || !dD)
@@ -1201,6 +1319,11 @@ int ssm2d_scan_bwd_ex_bf16(const uint16_t *x, const uint16_t *delta, const float
                            float *dA, uint16_t *dB, uint16_t *dC, float *dD, int64_t batch, int64_t d_inner,
                            int64_t d_state, int64_t H, int64_t W, uint32_t flags, void *stream)
 {
+    if (d_state > SSM2D_MAX_STATE_BWD && d_state <= SSM2D_MAX_STATE && !(flags & SSM2D_DELTA_SOFTPLUS))
+        // (more states than the kernels hold: widened to fp32, in chunks of states)
+        return scan_bwd_mamba<uint16_t>(x, delta, A, B, C, D, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dy,
+                                        dx, ddelta, dA, dB, dC, dD, nullptr, nullptr, nullptr, nullptr, batch, d_inner,
+                                        d_state, H, W, flags, stream);
     return scan_bwd<uint16_t>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
                               stream, flags);
 }
@@ -1210,8 +1333,8 @@ int ssm2d_scan_bwd_bf16(const uint16_t *x, const uint16_t *delta, const float *A
                         float *dA, uint16_t *dB, uint16_t *dC, float *dD, int64_t batch, int64_t d_inner,
                         int64_t d_state, int64_t H, int64_t W, void *stream)
 {
-    return scan_bwd<uint16_t>(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
-                              stream);
+    return ssm2d_scan_bwd_ex_bf16(x, delta, A, B, C, D, dy, dx, ddelta, dA, dB, dC, dD, batch, d_inner, d_state, H, W,
+                                  0u, stream);
 }
 
 int ssm2d_scan_bwd_mamba(const float *x, const float *delta, const float *A, const float *B, const float *C,

@@ -178,7 +178,8 @@ def test_bwd_validation(lib, bf16):
         dims = [1, 2, 3, 4, 5]
         dims[k] = -1
         assert _call_bwd(lib, dims, bf16=bf16) == pkg.ERR_BAD_DIM
-    assert _call_bwd(lib, [1, 2, 33, 4, 5], bf16=bf16) == pkg.ERR_UNSUPPORTED   # d_state > 32
+    assert _call_bwd(lib, [1, 2, 65, 4, 5], bf16=bf16) == pkg.ERR_UNSUPPORTED   # d_state > 64
+    assert _call_bwd(lib, [1, 2, 33, 4, 5], bf16=bf16) not in (pkg.ERR_UNSUPPORTED, pkg.ERR_BAD_DIM)  # in chunks
     assert _call_bwd(lib, [1, 2, 4, 65536, 5], bf16=bf16) == pkg.ERR_UNSUPPORTED
     assert _call_bwd(lib, [1, 0, 3, 4, 5], ptrs=[0] * 13, bf16=bf16) == pkg.OK  # d_inner = 0: nothing
     # with d_state = 0, A, B, C, dA, dB, dC may be NULL

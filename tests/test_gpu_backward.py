@@ -410,3 +410,36 @@ def test_tile_backward(case, dtype, d, monkeypatch):
         err = float(np.max(np.abs(got[k] - ref[k]) / (1.0 + np.abs(ref[k])))) if ref[k].size else 0.0
         _say(f"  {k}: {err:.3e}")
         assert err <= TOL["f32"] * max(1.0, np.sqrt(max(H, W) / 64.0)), k
+
+
+@pytest.mark.parametrize("d", [(False, False, False), (True, True, False), (False, True, True)],
+                         ids=lambda d: "".join("HWV"[i] if v else "-" for i, v in enumerate(d)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 9, 40, 7, 23), (2, 8, 64, 13, 40), (1, 16, 33, 5, 64)], ids=str)
+def test_many_states_backward(shape, dtype, d):
+    """More states than the backward's kernels hold (32): chunks of states,
+    their dx and d delta summed; plain, and with both carried states."""
+    fh, fw, vf = d
+    kw = dict(flip_h=fh, flip_w=fw, vertical_first=vf)
+    _say(f"many-state backward {shape} {dtype} {d}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 81, dtype=dtype)
+    b, di, n, H, W = shape
+    dy, dy_dev = make_dy(t, dtype, sum(shape) + 82)
+    keys = ("x", "delta", "A", "B", "C", "D")
+    if not any(d):
+        got = run_bwd(t, dtype, dy_dev)
+        check_grads(got, oracle.bwd(*(t[k] for k in keys), dy), dtype, b * H * W, f"{n} states {shape}")
+    r = np.random.default_rng(sum(shape) + 83)
+    h0, gl = (r.standard_normal((b, di, n, W)).astype(np.float32) for _ in range(2))
+    g0, ggl = (r.standard_normal((b, di, n, H)).astype(np.float32) for _ in range(2))
+    cu = lambda a: torch.from_numpy(a).cuda()
+    g = pkg.scan_bwd_mamba(*to_dev(t, dtype), dy_dev, h_init=cu(h0), dh_last=cu(gl), hh_init=cu(g0),
+                           dhh_last=cu(ggl), **kw)
+    pkg.sync_check()
+    got = {k: v.double().cpu().numpy() for k, v in g.items()}
+    ref = oracle.bwd(*(t[k] for k in keys), dy, h_init=h0, dh_last=gl, hh_init=g0, dhh_last=ggl, **kw)
+    check_grads(got, ref, dtype, b * H * W, f"{n} states, carried {shape} {d}")
+    for k in ("dh_init", "dhh_init"):
+        err = float(np.max(np.abs(got[k] - ref[k]) / (1.0 + np.abs(ref[k]))))
+        _say(f"  {k}: {err:.3e}")
+        assert err <= TOL["f32"] * max(1.0, np.sqrt(max(H, W) / 64.0)), k
