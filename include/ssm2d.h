@@ -45,14 +45,19 @@
  * launches never take each other's words.
  *
  * Carry waits: when a map's chain of tiles spans several workgroups, a tile
- * waits for its left neighbour's carries; with a bounded carry ring the
- * producer also waits for its consumer. All workgroups of such a launch must
- * be able to run at once; kernels of other streams or processes that hold the
- * GPU's compute units can delay them. A wait gives up after a bound (about a
- * second; ssm2d_set_spin_limit): the outputs from that point on are NaN, the
- * next call on the same (device, stream) returns SSM2D_ERR_DEVICE_TIMEOUT
- * without enqueueing anything (read from a host-visible flag, no wait), and
- * ssm2d_sync_check reports it too.
+ * waits for its left neighbour's carries, produced by a workgroup that started
+ * earlier (workgroups take tickets in the order they start). With a bounded
+ * carry ring (chosen when the launch's whole grid fits the GPU at once) the
+ * producer also waits for its consumer. Tickets are then dealt in blocks of
+ * a few chains, so only the started workgroups of the last block's chains can
+ * wait on a consumer that has not started, and the block size keeps them
+ * under half the GPU's slots: kernels of other streams or processes (another
+ * such ssm2d launch too) that hold part of the GPU delay a launch but do not
+ * block it, as long as they release their compute units in time. A wait
+ * gives up after a bound (about a second; ssm2d_set_spin_limit): the outputs
+ * from that point on are NaN, the next call on the same (device, stream)
+ * returns SSM2D_ERR_DEVICE_TIMEOUT without enqueueing anything (read from a
+ * host-visible flag, no wait), and ssm2d_sync_check reports it too.
  *
  * Errors: every function returns a status and never throws or aborts.
  *   batch, d_inner, d_state, H or W < 0          -> SSM2D_ERR_BAD_DIM
@@ -416,7 +421,11 @@ int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state,
  *   SSM2D_VECSTORE=0|1   cell-by-cell output stores, or each channel's cells
  *                        gathered into wider stores (default: 1 for 4-column
  *                        strips, 0 for 8-column strips)
- *   SSM2D_RING=n         depth of the global carry ring when the grid is co-resident
+ *   SSM2D_RING=n         depth of the bounded global carry ring (used when the
+ *                        grid fits the GPU at once; n >= H: one slot a row)
+ *   SSM2D_TICKET_BLOCK=n chains per block of tickets with the bounded ring
+ *                        (default: the most that keeps two launches' waiting
+ *                        workgroups under the GPU's slots, in 8s)
  *   SSM2D_LDSRING=4|16|32  depth of the LDS carry rings
  *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD
  *   SSM2D_FAST=0|1|2     the general kernel for every plain forward (0);

@@ -133,8 +133,8 @@ void scan2d_fast_kernel(Params p)
     } else {
         wg = blockIdx.x;
     }
-    const int chain = wg % p.n_chains;
-    const int grp = wg / p.n_chains;
+    int chain, grp;
+    ticket_tile(p, wg, chain, grp);
     const int b = chain / p.n_dblk;
     const int dblk = chain % p.n_dblk;
     const int H = p.H, W = p.W;
@@ -574,18 +574,14 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const int threads = kWave * (pl.s_local + (CHAINED ? 2 : 0));
     const size_t lds = Sh::lds_bytes(pl.s_local);
     pl.qg = H;
+    pl.tblk = pl.n_chains;
     if constexpr (CHAINED) {
-        // global ring depth: bounded (with back-pressure) only if the whole
-        // grid is co-resident, so that a producer never waits on a consumer
-        // that cannot run
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, G, NPL, K, true>, threads,
-                                                         lds) == hipSuccess) {
-            const int qg = env_int("SSM2D_RING", 32);
-            if (static_cast<long>(per_cu) * device_cus(dev) >= pl.total_wg && qg >= 8 && qg < H) pl.qg = qg;
-        } else {
+                                                         lds) == hipSuccess)
+            bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H);
+        else
             (void)hipGetLastError();
-        }
     }
     const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
     const WsEntry *e = pl.fixed_ws;

@@ -31,8 +31,10 @@
 //   * Multi-workgroup chains take tickets from an atomic counter; ticket order
 //     puts every producer before its consumer, so a waiting workgroup's
 //     producer is resident or done. A bounded global ring with back-pressure
-//     is used only when the whole grid is co-resident; otherwise every row has
-//     its own slot and nothing ever waits on a consumer.
+//     (chosen when the whole grid fits the device at once) deals tickets in
+//     blocks of a few chains, so only the chains of the last block begun can
+//     have a producer waiting on a consumer not yet started; otherwise every
+//     row has its own slot and nothing ever waits on a consumer.
 //   * The sum over n: each lane holds K partial sums over its NPL states; two
 //     permlane swaps (32- and 16-lane) transpose-reduce them across the 4 state
 //     groups, leaving each lane with K/4 finished cells.
@@ -124,6 +126,7 @@ struct Params {
     long gring_words, cons_words;      // cleared when the epoch wraps
     int batch, d_inner, d_state, H, W;
     int nstrips, s_local, groups, n_dblk, n_chains, total_wg;
+    int tblk;                          // chains per block of tickets
     int ring_rows;                     // LDS ring depth between waves
     int qg;                            // global ring depth (== H: no reuse)
     int use_ticket;                    // chains span workgroups
@@ -501,6 +504,25 @@ __device__ __forceinline__ void lds_poke(int *c, int v)
 }
 __device__ __forceinline__ void signal_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+// Tile of a ticket. Tickets are dealt in blocks of tblk chains: within a
+// block, strip group by strip group, chain by chain. Workgroups start (and take
+// tickets) in the order they are dealt to the 8 XCDs round-robin, so with a
+// multiple of 8 chains a block each chain's workgroups share one XCD. With the
+// bounded ring (back-pressure) tblk is small: only the chains of the last
+// block begun can wait on a consumer that has not started, every earlier block
+// is wholly running or done and drains, so the grid finishes while other work
+// holds part of the device. With one slot a row tblk = n_chains.
+__device__ __forceinline__ void ticket_tile(const Params &p, int wg, int &chain, int &grp)
+{
+    const int per_blk = p.tblk * p.groups;
+    const int blk = wg / per_blk;
+    const int c0 = blk * p.tblk;
+    const int nb = min(p.tblk, p.n_chains - c0);   // chains in this block (the last may hold fewer)
+    const int r = wg - blk * per_blk;
+    grp = r / nb;
+    chain = c0 + r % nb;
+}
+
 // Polls counter *c until it exceeds `need` (returns the value seen), or
 // until `limit` polls have failed (sets `timed_out`).
 __device__ __forceinline__ int wait_counter_above(const int *c, int need, long long limit, bool &timed_out)
@@ -752,8 +774,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
     } else {
         wg = blockIdx.x;
     }
-    const int chain = wg % p.n_chains;
-    const int grp = wg / p.n_chains;
+    int chain, grp;
+    ticket_tile(p, wg, chain, grp);
     const int b = chain / p.n_dblk;
     const int dblk = chain % p.n_dblk;
     const int H = p.H, W = p.W;
@@ -1626,6 +1648,7 @@ struct BwdArgs {
 
 struct Plan {
     int G, K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
+    int tblk;        // chains per block of tickets (0: n_chains)
     int coop_slots;  // rows of the shared row ring with cooperative loads, 0 = per-wave packets
     int mode;        // kMode* bits
     int flip_h;      // rows bottom to top
@@ -1691,22 +1714,40 @@ size_t lds_bytes(const Plan &pl)
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
 
-// Global ring depth: bounded (with back-pressure) only if the whole grid is
-// co-resident, so that a producer never waits on a consumer that cannot run.
-template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
-int choose_qg(const Plan &pl, int dev, int H)
+// Global ring: bounded (with back-pressure) when the whole grid fits the device
+// at once, its smaller footprint being the faster one there. Only the started
+// workgroups of partly started chains can then wait on a consumer that has not
+// started; tickets dealt in blocks of tblk chains cap them at
+// tblk * (groups - 1), kept below half the device's slots, so that even two
+// such launches sharing the device leave slots free and both drain. Blocks of
+// 8 chains keep each chain's workgroups on one XCD. Otherwise one slot a row:
+// nothing waits on a consumer, and tickets go strip group by strip group.
+inline void bound_ring(Plan &pl, long resident, int H)
 {
-    if (pl.groups <= 1 || (pl.mode & kModeEdges)) return H;
+    pl.qg = H;
+    pl.tblk = pl.n_chains;
+    const int qg = env_int("SSM2D_RING", 32);
+    if (pl.groups <= 1 || resident < pl.total_wg || qg < 8 || qg >= H) return;
+    const int forced = env_int("SSM2D_TICKET_BLOCK", 0);
+    long tb = forced > 0 ? forced : (resident - 1) / (2L * (pl.groups - 1));
+    if (forced <= 0 && tb >= 8) tb -= tb % 8;
+    pl.qg = qg;
+    pl.tblk = static_cast<int>(tb < 1 ? 1 : (tb < pl.n_chains ? tb : pl.n_chains));
+}
+
+template <typename T, int K, int NPL, int ALIGN, int G, bool COOP, int MODE>
+void choose_ring(Plan &pl, int dev, int H)
+{
+    pl.qg = H;
+    pl.tblk = pl.n_chains;
+    if (pl.groups <= 1 || (pl.mode & kModeEdges)) return;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE>, block_threads(pl),
                                                      lds_bytes<T, K, NPL, G, MODE>(pl)) != hipSuccess) {
         (void)hipGetLastError();
-        return H;
+        return;
     }
-    const long resident = static_cast<long>(per_cu) * device_cus(dev);
-    const int qg = env_int("SSM2D_RING", 32);
-    if (resident >= pl.total_wg && qg >= 8 && qg < H) return qg;
-    return H;
+    bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H);
 }
 
 template <int NPL>
@@ -1727,7 +1768,7 @@ int run(const T *x, const T *delta, const float *A, const T *B, const T *C, cons
         int d_inner, int d_state, int H, int W, Plan pl, int dev, void *stream)
 {
     if (!COOP) pl.coop_slots = 0;
-    pl.qg = choose_qg<T, K, NPL, ALIGN, G, COOP, MODE>(pl, dev, H);
+    choose_ring<T, K, NPL, ALIGN, G, COOP, MODE>(pl, dev, H);
     const WsNeed need = ws_need<NPL>(pl, d_inner, H, W);
     if (pl.fixed_ws) {
         // a workspace of fixed size (no allocation): the plan must fit it
@@ -1766,6 +1807,7 @@ inline Params make_params(const void *x, const void *delta, const float *A, cons
     prm.nstrips = pl.nstrips; prm.s_local = pl.s_local; prm.groups = pl.groups; prm.n_dblk = pl.n_dblk;
     prm.n_chains = pl.n_chains; prm.total_wg = pl.total_wg; prm.ring_rows = pl.ring_rows; prm.qg = pl.qg;
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
+    prm.tblk = pl.tblk > 0 && pl.tblk < pl.n_chains ? pl.tblk : pl.n_chains;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;
     // Gathered stores pay for 4-column strips (one row swap, two cells a lane).
     // Gathering the eight cells of an 8-column strip costs more VALU work than

@@ -1,6 +1,7 @@
 """GPU tests of the library's launch machinery around the scan: HIP-graph
 capture and replay, the carry-tag epoch and its wrap, timeouts that surface on
-the next call, and the release of workspaces.
+the next call, the release of workspaces, and launches with a bounded carry
+ring that share the device with each other.
 
 The carry words that link the tiles of one map across workgroups are tagged
 with an epoch kept in device memory; every launch (every replay of a captured
@@ -179,3 +180,56 @@ def test_release_workspaces_and_reuse():
                     shape[3] * shape[4], f"backward, round {r}")
         check(as_f64(yb), oracle.fwd_mamba(*(t[k] for k in KEYS), delta_softplus=True), "f32", f"options, round {r}")
         pkg.release_workspaces()
+
+
+def test_concurrent_streams_with_bounded_rings():
+    """Three streams each launch the giga-pixel map (384 x 512, 128 channels,
+    16 states: chains across workgroups with the bounded carry ring, a grid
+    that alone fills the device) several times without waiting, so the
+    launches compete for the compute units. A chain's workgroups take
+    consecutive tickets there, so every launch drains: no wait gives up, and
+    each output equals (bit for bit) the same call run alone; sampled maps
+    match the oracle."""
+    shape = (1, 128, 16, 384, 512)
+    assert pkg.fwd_kernels(*shape) == (1, 0)
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    ts = [make_random_inputs(*shape, seed=130 + i) for i in range(3)]
+    args, alone = [], []
+    for s, t in zip(streams, ts):
+        with torch.cuda.stream(s):
+            a = to_dev(t, "f32")
+            args.append(a)
+            alone.append(pkg.scan_fwd(*a))
+        s.synchronize()
+        pkg.sync_check(s)
+    maps = [0, 63, 127]
+    check(as_f64(alone[0]).reshape(-1, 384, 512)[maps], ref_of(ts[0], maps=maps), "f32", "giga-pixel map alone")
+    outs = [[torch.empty_like(alone[i]) for _ in range(4)] for i in range(3)]
+    for r in range(4):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                pkg.scan_fwd(*args[i], y=outs[i][r])
+    for i, s in enumerate(streams):
+        s.synchronize()
+        pkg.sync_check(s)
+        for r in range(4):
+            assert torch.equal(outs[i][r], alone[i]), f"stream {i} launch {r}"
+    _say("  12 overlapping launches on 3 streams: all equal to the lone runs")
+
+
+@pytest.mark.parametrize("tblk", ["1", "3", "8", "64"])
+def test_ticket_blocks(tblk, monkeypatch):
+    """Tickets dealt in blocks of 1, 3, 8 chains, and all chains at once
+    (10 chains: a partial last block), through the two-rows-per-step forward
+    and the general kernel; exact against the oracle on every map."""
+    monkeypatch.setenv("SSM2D_TICKET_BLOCK", tblk)
+    shape = (2, 40, 16, 96, 512)
+    t = make_random_inputs(*shape, seed=140 + int(tblk))
+    args = to_dev(t, "f32")
+    ref = ref_of(t)
+    for fast in ("1", "0"):
+        monkeypatch.setenv("SSM2D_FAST", fast)
+        _say(f"ticket blocks of {tblk} chains, SSM2D_FAST={fast}")
+        y = pkg.scan_fwd(*args)
+        pkg.sync_check()
+        check(as_f64(y), ref, "f32", f"tblk={tblk} fast={fast}")
