@@ -258,7 +258,7 @@ def cpu_baseline_bwd(wl, t, keys, seconds: float):
 
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
-             "python bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline{v}")
+             "python bench.py --workload {w} --steps {s} --warmup {wu} --no-cpu-baseline{v}")
 # One counter per run (rocprofv3 does not split counters over passes).
 PMC_SCAN_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d <dir> -o pmc -- "
                 "python bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline{v}")
@@ -266,16 +266,18 @@ PMC_COPY_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d 
                 "python bench.py --copy-probe {mb} --steps 5")
 
 
-def trace_summary(workload: str, run_dir: str, variant: str = "fwd", out_dir: str = PROFILES) -> None:
+def trace_summary(workload: str, run_dir: str, variant: str = "fwd", out_dir: str = PROFILES, steps: int = 20,
+                  warmup: int = 5) -> None:
     """Writes profiles/kernel_stats_<workload>[_<variant>].txt from the kernel
-    statistics of a rocprofv3 --kernel-trace --stats run of this benchmark."""
+    statistics of a rocprofv3 --kernel-trace --stats run of this benchmark
+    (made with the given --steps and --warmup)."""
     files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {run_dir}")
     rows = list(csv.DictReader(open(files[0])))
     vopt = "" if variant == "fwd" else f" --variant {variant}"
     lines = [f"# rocprofv3 kernel statistics, workload {workload}, variant {variant}",
-             f"# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && {TRACE_CMD.format(w=workload, v=vopt)}",
+             f"# command: cd /tmp && export TMPDIR=/tmp && cd <repo> && {TRACE_CMD.format(w=workload, v=vopt, s=steps, wu=warmup)}",
              f"# kernel source sha256[:16] {kernel_source_hash()}",
              "# name | calls | total ns | average ns | min ns | max ns | percent"]
     for r in rows:
@@ -404,7 +406,8 @@ def main():
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output directories")
     ap.add_argument("--copy-mb", type=int, default=512)
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
-                    help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run")
+                    help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run "
+                         "(pass the --steps and --warmup that run used)")
     ap.add_argument("--shape-sweep", metavar="HxW,...",
                     help="time the forward at other map heights and widths (fill against row rate)")
     ap.add_argument("--counter-table", nargs="+", metavar="PMC_DIR",
@@ -414,7 +417,7 @@ def main():
         counter_table(args.workload, args.counter_table)
         return
     if args.trace_summary:
-        trace_summary(args.workload, args.trace_summary, args.variant)
+        trace_summary(args.workload, args.trace_summary, args.variant, steps=args.steps, warmup=args.warmup)
         return
     if args.pmc_summary:
         pmc_summary(args.workload, *args.pmc_summary, copy_mb=args.copy_mb, variant=args.variant)
