@@ -976,9 +976,12 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
 #pragma unroll
             for (int c = 0; c < KO; ++c) zoff[c] = (ystep[c] != 0) ? dist : 0;
         }
-        float dAacc[NPL], dDacc = 0.0f;  // backward: this lane's parts of dA and dD
+        // backward: this lane's parts of dA and dD. Each row's terms are summed
+        // in fp32 and the row sums in fp64, so the rounding of these long sums
+        // (every cell of the strip) does not grow with the map's height.
+        double dAacc[NPL], dDacc = 0.0;
 #pragma unroll
-        for (int k = 0; k < NPL; ++k) dAacc[k] = 0.0f;
+        for (int k = 0; k < NPL; ++k) dAacc[k] = 0.0;
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -1364,7 +1367,9 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                     // ---- local derivatives. With hh = h - Abar h(row above)
                     // and u = Bx, the decay's adjoint times Abar is
                     // g_a Abar = g_hh (hh - u) + g_h (h - hh).
-                    float ddp[K], dxp[K], dBv[NPL][K], dCv[NPL][K];
+                    float ddp[K], dxp[K], dBv[NPL][K], dCv[NPL][K], dAr[NPL], dDr = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) dAr[k] = 0.0f;
 #pragma unroll
                     for (int c = 0; c < K; ++c) {
                         float sdd = 0.0f, sdx = 0.0f;
@@ -1380,12 +1385,15 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
                             sdx = __builtin_fmaf(gb, o.dv[c], sdx);
                             dBv[k][c] = hc[c][k] * (o.dv[c] * o.xv[c]);
                             dCv[k][c] = dyv[c] * hcu;
-                            dAacc[k] = __builtin_fmaf(gaa, o.dv[c], dAacc[k]);
+                            dAr[k] = __builtin_fmaf(gaa, o.dv[c], dAr[k]);
                         }
                         ddp[c] = sdd;
                         dxp[c] = sdx;
-                        dDacc = __builtin_fmaf(dyv[c], o.xv[c], dDacc);
+                        dDr = __builtin_fmaf(dyv[c], o.xv[c], dDr);
                     }
+#pragma unroll
+                    for (int k = 0; k < NPL; ++k) dAacc[k] += static_cast<double>(dAr[k]);
+                    dDacc += static_cast<double>(dDr);
                     // sums over the state groups; dx takes the skip term's dy D
                     float ddo[KO], dxo[KO];
                     reduce_groups<K, G>(ddp, ddo, g);
@@ -1624,8 +1632,8 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
             // lane per channel)
 #pragma unroll
             for (int k = 0; k < NPL; ++k)
-                if (hok[k]) (void)unsafeAtomicAdd(p.dA + d * p.d_state + g * NPL + k, dAacc[k]);
-            if (d_ok && g == 0) (void)unsafeAtomicAdd(p.dD + d, dDacc);
+                if (hok[k]) (void)unsafeAtomicAdd(p.dA + d * p.d_state + g * NPL + k, static_cast<float>(dAacc[k]));
+            if (d_ok && g == 0) (void)unsafeAtomicAdd(p.dD + d, static_cast<float>(dDacc));
         }
         if (timed_out) report_timeout(p);
     }

@@ -1,12 +1,11 @@
 """GPU parity of the backward pass (ssm2d_scan_bwd / _bf16) against the fp64
 oracle's backward, gradient by gradient, on the same seeded inputs.
 
-Bars. Elementwise gradients (dx, d delta) and the channel sums dB, dC:
-max |g - g_ref| <= tol (1 + |g_ref|). The parameter gradients dA and dD are
-sums over every cell of the batch, whose fp32 rounding grows with the number
-of terms: their bar is tol (1 + |g_ref|) with the cell count folded in as
-tol = 1e-4 * max(1, sqrt(cells / 4096)). tol = 1e-4 for fp32 inputs, 2e-2 for
-bf16 inputs and outputs (fp32 state and arithmetic).
+Bars. Every gradient: max |g - g_ref| <= tol (1 + |g_ref|), tol = 1e-4 for
+fp32 inputs, 2e-2 for bf16 inputs and outputs (fp32 state and arithmetic).
+The parameter gradients dA and dD are sums over every cell of the batch: the
+kernels sum each row's terms in fp32 and the row sums in fp64, so their
+rounding does not grow with the number of cells and the same bar holds.
 """
 import itertools
 
@@ -46,8 +45,6 @@ def run_bwd(t, dtype, dy_dev):
 def check_grads(got, ref, dtype, cells, what):
     for k in NAMES:
         tol = TOL[dtype]
-        if k in ("dA", "dD"):
-            tol = tol * max(1.0, np.sqrt(cells / 4096.0))
         g, r = got[k], ref[k]
         assert g.shape == r.shape, (k, g.shape, r.shape)
         if g.size == 0:
