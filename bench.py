@@ -115,7 +115,7 @@ def copy_probe(mb: int, steps: int) -> None:
 
 
 # The scan kernels: the general one and the two-rows-per-step forward of tall maps.
-SCAN_KERNELS = ("scan2d_fwd_kernel", "scan2d_fast_kernel")
+SCAN_KERNELS = ("scan2d_fwd_kernel", "scan2d_fast_kernel", "scan2d_narrow_kernel")
 
 
 def is_scan_kernel(name: str) -> bool:
@@ -125,15 +125,17 @@ def is_scan_kernel(name: str) -> bool:
 def kernel_name(wl, variant: str) -> str:
     """The scan kernel(s) a step of the workload launches, as the library plans
     them (ssm2d_fwd_kernels): the two-rows-per-step forward, the general
-    kernel, or both joined by '+' (a four-corner sum can use both)."""
+    kernel, the whole-row kernel for narrow maps, or several joined by '+'
+    (a four-corner sum can use two)."""
     import selective_state_space_ssm2d_amd as pkg
 
     kw, _ = VARIANTS[variant]
     if kw == "bwd":
         return "scan2d_fwd_kernel"  # the stored-state and adjoint passes
-    fast, general = pkg.fwd_kernels(wl.batch, wl.d_inner, wl.d_state, wl.H, wl.W, bf16=wl.dtype == "bf16",
-                                    **(kw or {}))
-    names = (["scan2d_fast_kernel"] if fast else []) + (["scan2d_fwd_kernel"] if general else [])
+    fast, general, narrow = pkg.fwd_kernels(wl.batch, wl.d_inner, wl.d_state, wl.H, wl.W, bf16=wl.dtype == "bf16",
+                                            **(kw or {}))
+    names = ((["scan2d_fast_kernel"] if fast else []) + (["scan2d_fwd_kernel"] if general else [])
+             + (["scan2d_narrow_kernel"] if narrow else []))
     return "+".join(names)
 
 

@@ -92,7 +92,7 @@ def load_library(path: str = LIB_PATH):
     lib.ssm2d_release_workspaces.restype = ctypes.c_int
     lib.ssm2d_test_set_epoch.argtypes = [vp, ctypes.c_uint32]
     lib.ssm2d_test_set_epoch.restype = ctypes.c_int
-    lib.ssm2d_fwd_kernels.argtypes = [ctypes.c_int] + [i64] * 5 + [ctypes.c_uint32, vp, vp]
+    lib.ssm2d_fwd_kernels.argtypes = [ctypes.c_int] + [i64] * 5 + [ctypes.c_uint32, vp, vp, vp]
     lib.ssm2d_fwd_kernels.restype = ctypes.c_int
     lib.ssm2d_version.argtypes = []
     lib.ssm2d_version.restype = ctypes.c_int
@@ -154,17 +154,18 @@ def set_epoch_for_test(epoch: int, stream=None) -> None:
 def fwd_kernels(batch, d_inner, d_state, H, W, bf16=False, flip_h=False, flip_w=False, vertical_first=False,
                 accumulate=False, four_way=False, delta_softplus=False):
     """(launches of the two-rows-per-step forward, launches of the general
-    kernel) that a forward call of these sizes and options makes (no gate,
-    delta bias or carried states). Host-side planning only: no GPU needed."""
+    kernel, launches of the whole-row kernel for narrow maps) that a forward
+    call of these sizes and options makes (no gate, delta bias or carried
+    states). Host-side planning only: no GPU needed."""
     flags = ((FLIP_H if flip_h else 0) | (FLIP_W if flip_w else 0) | (VERTICAL_FIRST if vertical_first else 0)
              | (ACCUMULATE if accumulate else 0) | (FOUR_WAY if four_way else 0)
              | (DELTA_SOFTPLUS if delta_softplus else 0))
-    fast, general = ctypes.c_int(0), ctypes.c_int(0)
+    fast, general, narrow = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     s = load_library().ssm2d_fwd_kernels(int(bool(bf16)), batch, d_inner, d_state, H, W, flags,
-                                         ctypes.byref(fast), ctypes.byref(general))
+                                         ctypes.byref(fast), ctypes.byref(general), ctypes.byref(narrow))
     if s != OK:
         raise Ssm2dError(s, "ssm2d_fwd_kernels")
-    return fast.value, general.value
+    return fast.value, general.value, narrow.value
 
 
 def _check(x, delta, A, B, C, D, y, need_d):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 _VARIANTS = ("g4", "g8", "flipw", "vfirst", "flipw_vfirst", "acc", "flipw_acc", "vfirst_acc", "flipw_vfirst_acc",
              "states", "bwd", "bwd_edges", "states_flipw", "bwd_ltr", "bwd_ltr_edges", "gate", "gate_flipw", "fast",
              "rowc", "rowc_vfirst", "states_rowc", "states_flipw_rowc", "bwd_rowc", "bwd_edges_rowc", "bwd_ltr_rowc",
-             "bwd_ltr_edges_rowc")
+             "bwd_ltr_edges_rowc", "narrow")
 SOURCES = ["ssm2d.hip"] + [f"scan2d_{t}_{v}.hip" for t in ("f32", "bf16") for v in _VARIANTS]
 LIB = os.path.join(PKG, "libssm2d.so")
 INCLUDE = os.path.join(ROOT, "include")

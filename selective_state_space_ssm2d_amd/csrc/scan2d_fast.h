@@ -579,7 +579,7 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, G, NPL, K, true>, threads,
                                                          lds) == hipSuccess)
-            bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H);
+            bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H, NPL);
         else
             (void)hipGetLastError();
     }

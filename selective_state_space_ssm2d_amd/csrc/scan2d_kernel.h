@@ -30,11 +30,11 @@
 //     pipeline, one row deep per strip.
 //   * Multi-workgroup chains take tickets from an atomic counter; ticket order
 //     puts every producer before its consumer, so a waiting workgroup's
-//     producer is resident or done. A bounded global ring with back-pressure
-//     (chosen when the whole grid fits the device at once) deals tickets in
-//     blocks of a few chains, so only the chains of the last block begun can
-//     have a producer waiting on a consumer not yet started; otherwise every
-//     row has its own slot and nothing ever waits on a consumer.
+//     producer is resident or done. The global ring has a slot per row, so
+//     nothing waits on a consumer; a bounded ring with back-pressure (asked
+//     for, or forced by a fixed-size workspace) deals tickets in blocks of a
+//     few chains, so only the chains of the last block begun can have a
+//     producer waiting on a consumer not yet started.
 //   * The sum over n: each lane holds K partial sums over its NPL states; two
 //     permlane swaps (32- and 16-lane) transpose-reduce them across the 4 state
 //     groups, leaving each lane with K/4 finished cells.
@@ -1722,22 +1722,37 @@ size_t lds_bytes(const Plan &pl)
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
 
-// Global ring: bounded (with back-pressure) when the whole grid fits the device
-// at once, its smaller footprint being the faster one there. Only the started
-// workgroups of partly started chains can then wait on a consumer that has not
-// started; tickets dealt in blocks of tblk chains cap them at
-// tblk * (groups - 1), kept below half the device's slots, so that even two
-// such launches sharing the device leave slots free and both drain. Blocks of
-// 8 chains keep each chain's workgroups on one XCD. Otherwise one slot a row:
-// nothing waits on a consumer, and tickets go strip group by strip group.
-inline void bound_ring(Plan &pl, long resident, int H)
+// Global ring. By default one slot a row: a producer never waits on its
+// consumer, only consumers wait, on producers that took earlier tickets, so a
+// launch drains whatever else holds the GPU's compute units (other streams,
+// other processes, any number of other launches), and tickets go strip group
+// by strip group (every chain's first tile starts at once). A bounded ring of
+// qg rows with back-pressure, when asked for (SSM2D_RING=qg) or when a
+// workspace of fixed size cannot hold a slot a row, is used only if the whole
+// grid fits the GPU at once. Its producers wait on consumers: only the started
+// workgroups of partly started chains can then wait on one that has not
+// started, and tickets dealt in blocks of tblk chains cap them at
+// tblk * (groups - 1). Asked for, tblk keeps that under half the GPU's slots
+// (two such launches sharing the GPU still drain), in multiples of 8 so that
+// each chain's workgroups share an XCD; a fixed workspace takes one chain a
+// block (groups - 1 workgroups at most).
+inline void bound_ring(Plan &pl, long resident, int H, int npl)
 {
     pl.qg = H;
     pl.tblk = pl.n_chains;
-    const int qg = env_int("SSM2D_RING", 32);
-    if (pl.groups <= 1 || resident < pl.total_wg || qg < 8 || qg >= H) return;
+    if (pl.groups <= 1) return;
+    int qg = env_int("SSM2D_RING", 0);
+    bool one_chain = false;
+    if (pl.fixed_ws) {
+        const size_t row_bytes = static_cast<size_t>(pl.n_chains) * (pl.groups - 1) * npl * kWave * sizeof(unsigned long long);
+        if (row_bytes * H > pl.fixed_ws->gring_bytes) {
+            qg = 32;
+            one_chain = true;
+        }
+    }
+    if (resident < pl.total_wg || qg < 8 || qg >= H) return;
     const int forced = env_int("SSM2D_TICKET_BLOCK", 0);
-    long tb = forced > 0 ? forced : (resident - 1) / (2L * (pl.groups - 1));
+    long tb = forced > 0 ? forced : (one_chain ? 1 : (resident - 1) / (2L * (pl.groups - 1)));
     if (forced <= 0 && tb >= 8) tb -= tb % 8;
     pl.qg = qg;
     pl.tblk = static_cast<int>(tb < 1 ? 1 : (tb < pl.n_chains ? tb : pl.n_chains));
@@ -1755,7 +1770,7 @@ void choose_ring(Plan &pl, int dev, int H)
         (void)hipGetLastError();
         return;
     }
-    bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H);
+    bound_ring(pl, static_cast<long>(per_cu) * device_cus(dev), H, NPL);
 }
 
 template <int NPL>
@@ -1934,6 +1949,14 @@ SSM2D_DISPATCH_DECL(uint16_t, dispatch_g8)
 constexpr int kNoFastPath = -1;
 SSM2D_DISPATCH_DECL(float, dispatch_fast)
 SSM2D_DISPATCH_DECL(uint16_t, dispatch_fast)
+// The plain forward of narrow maps, one wave a whole row (scan2d_narrow.h):
+// rows of at most 16 columns, at most 16 states.
+int dispatch_narrow(const float *x, const float *delta, const float *A, const float *B, const float *C,
+                    const float *D, float *y, int batch, int d_inner, int d_state, int H, int W, int flip_h,
+                    void *stream);
+int dispatch_narrow(const uint16_t *x, const uint16_t *delta, const float *A, const uint16_t *B, const uint16_t *C,
+                    const float *D, uint16_t *y, int batch, int d_inner, int d_state, int H, int W, int flip_h,
+                    void *stream);
 // Whether dispatch_fast takes a plan (for inputs of type T; rows of a
 // multiple of `align` columns).
 template <typename T>

@@ -594,6 +594,22 @@ bool takes_fast(Plan &pl, int64_t W, int align)
     return fast_path_taken<T>(pl, align);
 }
 
+// Whether a launch runs in the whole-row kernel for narrow maps: the plain
+// forward (rows in either direction, no gate or carried states) of rows of at
+// most 16 columns with at most 16 states. There one wave of 16 channels does
+// a whole row, against a chain of up to four strip waves handing the row's
+// carry on in the general kernel; taken when the map is short or the batch
+// gives at least 256 such waves (one a CU), else the general kernel's strips
+// spread a few tall maps over more waves. SSM2D_NARROW=0 never takes it,
+// SSM2D_NARROW=2 always where it applies.
+inline bool takes_narrow(int mode, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
+                         bool carries)
+{
+    const int env = env_int("SSM2D_NARROW", 1);
+    if (env <= 0 || mode != 0 || carries || W > 16 || d_state > 16) return false;
+    return env >= 2 || H <= 128 || batch * ((d_inner + 15) / 16) >= 256;
+}
+
 template <typename T>
 int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int64_t batch,
            int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int flip_h, int dev, void *stream,
@@ -601,6 +617,9 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
            const WsEntry *fixed_ws = nullptr, const float *hh_init = nullptr, float *hh_last = nullptr)
 {
     if (hh_init || hh_last) mode |= kModeRowCarry;
+    if (takes_narrow(mode, batch, d_inner, d_state, H, W, z || h_init || h_last))
+        return dispatch_narrow(x, delta, A, B, C, D, y, static_cast<int>(batch), static_cast<int>(d_inner),
+                               static_cast<int>(d_state), static_cast<int>(H), static_cast<int>(W), flip_h, stream);
     Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
     pl.flip_h = flip_h;
     pl.z = z;
@@ -1213,7 +1232,7 @@ int scan_bwd_mamba(const T *x, const T *delta, const float *A, const T *B, const
 // each kernel, as scan_fwd and launch() plan them.
 template <typename T>
 void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, unsigned flags,
-                        int *two_row, int *general)
+                        int *two_row, int *general, int *narrow)
 {
     const int vf = (flags & SSM2D_VERTICAL_FIRST) ? kModeVFirst : 0;
     const int acc = (flags & SSM2D_ACCUMULATE) ? kModeAccumulate : 0;
@@ -1222,6 +1241,10 @@ void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t
         const int mode = (flags & SSM2D_FOUR_WAY)
                              ? (((q & 2) ? kModeFlipW : 0) | vf | (q == 0 ? acc : kModeAccumulate))
                              : (((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc);
+        if (takes_narrow(mode, batch, d_inner, d_state, H, W, false)) {
+            ++*narrow;
+            continue;
+        }
         Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
         const int align = row_align(W);
         choose_coop<T>(pl, H, align);
@@ -1234,10 +1257,10 @@ void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t
 extern "C" {
 
 int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                      uint32_t flags, int *two_row, int *general)
+                      uint32_t flags, int *two_row, int *general, int *narrow)
 {
-    if (!two_row || !general) return SSM2D_ERR_NULLPTR;
-    *two_row = *general = 0;
+    if (!two_row || !general || !narrow) return SSM2D_ERR_NULLPTR;
+    *two_row = *general = *narrow = 0;
     if ((flags & ~kKnownFlags) != 0 || ((flags & SSM2D_FOUR_WAY) && (flags & (SSM2D_FLIP_H | SSM2D_FLIP_W))))
         return SSM2D_ERR_BAD_FLAGS;
     if (batch < 0 || d_inner < 0 || d_state < 0 || H < 0 || W < 0) return SSM2D_ERR_BAD_DIM;
@@ -1245,9 +1268,9 @@ int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state,
     if (d_state > SSM2D_MAX_STATE || H > SSM2D_MAX_SIDE || W > SSM2D_MAX_SIDE) return SSM2D_ERR_UNSUPPORTED;
     // bf16 four-corner sums and softplus step sizes run the fp32 kernels
     if (bf16 && !(flags & (SSM2D_FOUR_WAY | SSM2D_DELTA_SOFTPLUS)))
-        count_fwd_launches<uint16_t>(batch, d_inner, d_state, H, W, flags, two_row, general);
+        count_fwd_launches<uint16_t>(batch, d_inner, d_state, H, W, flags, two_row, general, narrow);
     else
-        count_fwd_launches<float>(batch, d_inner, d_state, H, W, flags, two_row, general);
+        count_fwd_launches<float>(batch, d_inner, d_state, H, W, flags, two_row, general, narrow);
     return SSM2D_OK;
 }
 

@@ -30,6 +30,16 @@ SSM2D_STUBS(uint16_t)
 #undef SSM2D_STUBS
 #undef SSM2D_STUB
 
+#define SSM2D_NARROW_STUB(TT)                                                                                      \
+    int dispatch_narrow(const TT *, const TT *, const float *, const TT *, const TT *, const float *, TT *, int, int, \
+                        int, int, int, int, void *)                                                               \
+    {                                                                                                             \
+        return SSM2D_ERR_UNSUPPORTED;                                                                             \
+    }
+SSM2D_NARROW_STUB(float)
+SSM2D_NARROW_STUB(uint16_t)
+#undef SSM2D_NARROW_STUB
+
 template <>
 bool fast_path_taken<float>(const Plan &pl, int align)
 {

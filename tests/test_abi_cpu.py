@@ -254,34 +254,50 @@ def test_python_binding_rejects_bad_tensors():
 
 def test_fwd_kernels_query(lib, monkeypatch):
     """ssm2d_fwd_kernels: host-side planning only (no GPU), one count per scan
-    launch, the two-rows-per-step kernel for the plain forward of rows of a
+    launch: the two-rows-per-step kernel for the plain forward of rows of a
     multiple of 4 columns whose chains span workgroups (every such layout
-    with SSM2D_FAST=2), the general kernel for direction/order bits, ragged
-    rows and SSM2D_FAST=0; argument errors as the forward's."""
-    assert pkg.fwd_kernels(1, 128, 16, 384, 512) == (1, 0)
-    assert pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True) == (0, 1)   # chains in one workgroup
-    assert pkg.fwd_kernels(1, 128, 16, 384, 512, flip_h=True) == (1, 0)
-    assert pkg.fwd_kernels(1, 128, 16, 384, 512, flip_w=True) == (0, 1)
-    assert pkg.fwd_kernels(1, 128, 16, 384, 512, vertical_first=True) == (0, 1)
-    assert pkg.fwd_kernels(1, 128, 16, 384, 510) == (0, 1)   # rows of 2 mod 4 columns
-    assert pkg.fwd_kernels(64, 768, 16, 14, 14) == (0, 1)
-    fast, general = pkg.fwd_kernels(1, 128, 16, 384, 512, four_way=True)
-    assert (fast, general) == (1, 3)   # the first corner is the plain scan
+    with SSM2D_FAST=2), the whole-row kernel for the plain forward of narrow
+    maps (short, or a batch of at least 256 waves; every narrow map with
+    SSM2D_NARROW=2, none with 0), the general kernel for direction/order bits,
+    ragged rows and SSM2D_FAST=0; argument errors as the forward's."""
+    assert pkg.fwd_kernels(1, 128, 16, 384, 512) == (1, 0, 0)
+    assert pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True) == (0, 1, 0)   # chains in one workgroup
+    assert pkg.fwd_kernels(1, 128, 16, 384, 512, flip_h=True) == (1, 0, 0)
+    assert pkg.fwd_kernels(1, 128, 16, 384, 512, flip_w=True) == (0, 1, 0)
+    assert pkg.fwd_kernels(1, 128, 16, 384, 512, vertical_first=True) == (0, 1, 0)
+    assert pkg.fwd_kernels(1, 128, 16, 384, 510) == (0, 1, 0)   # rows of 2 mod 4 columns
+    assert pkg.fwd_kernels(64, 768, 16, 14, 14) == (0, 0, 1)     # 3072 waves of 16 channels
+    assert pkg.fwd_kernels(64, 768, 16, 14, 14, flip_h=True) == (0, 0, 1)
+    assert pkg.fwd_kernels(64, 768, 16, 14, 14, flip_w=True) == (0, 1, 0)
+    assert pkg.fwd_kernels(64, 768, 16, 14, 14, four_way=True) == (0, 3, 1)
+    assert pkg.fwd_kernels(64, 768, 17, 14, 14) == (0, 1, 0)     # more than 16 states
+    assert pkg.fwd_kernels(64, 768, 16, 14, 17) == (0, 1, 0)     # more than 16 columns
+    assert pkg.fwd_kernels(1, 16, 16, 4096, 16) == (0, 1, 0)     # one tall map: strips
+    assert pkg.fwd_kernels(1, 16, 16, 128, 16) == (0, 0, 1)      # a short one: whole rows
+    fast, general, narrow = pkg.fwd_kernels(1, 128, 16, 384, 512, four_way=True)
+    assert (fast, general, narrow) == (1, 3, 0)   # the first corner is the plain scan
     assert sum(pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True, four_way=True)) == 4
-    assert pkg.fwd_kernels(0, 128, 16, 384, 512) == (0, 0)
+    assert pkg.fwd_kernels(0, 128, 16, 384, 512) == (0, 0, 0)
     monkeypatch.setenv("SSM2D_FAST", "0")
-    assert pkg.fwd_kernels(1, 128, 16, 384, 512) == (0, 1)
+    assert pkg.fwd_kernels(1, 128, 16, 384, 512) == (0, 1, 0)
     monkeypatch.setenv("SSM2D_FAST", "2")
-    assert pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True) == (1, 0)
-    assert pkg.fwd_kernels(1, 4, 4, 8, 8) == (1, 0)
+    assert pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True) == (1, 0, 0)
+    assert pkg.fwd_kernels(1, 4, 4, 8, 8) == (0, 0, 1)
+    monkeypatch.setenv("SSM2D_NARROW", "0")
+    assert pkg.fwd_kernels(1, 4, 4, 8, 8) == (1, 0, 0)
     monkeypatch.delenv("SSM2D_FAST")
-    assert pkg.fwd_kernels(1, 4, 4, 8, 8) == (0, 1)
+    assert pkg.fwd_kernels(1, 4, 4, 8, 8) == (0, 1, 0)
+    monkeypatch.setenv("SSM2D_NARROW", "2")
+    assert pkg.fwd_kernels(1, 16, 16, 4096, 16) == (0, 0, 1)
+    monkeypatch.delenv("SSM2D_NARROW")
     with pytest.raises(pkg.Ssm2dError):
         pkg.fwd_kernels(1, 8, 16, 8, 8, flip_h=True, four_way=True)
     with pytest.raises(pkg.Ssm2dError):
         pkg.fwd_kernels(1, -8, 16, 8, 8)
     with pytest.raises(pkg.Ssm2dError):
         pkg.fwd_kernels(1, 8, 65, 8, 8)
-    two, gen = ctypes.c_int(), ctypes.c_int()
-    assert lib.ssm2d_fwd_kernels(0, 1, 8, 16, 8, 8, 1 << 10, ctypes.byref(two), ctypes.byref(gen)) == pkg.ERR_BAD_FLAGS
-    assert lib.ssm2d_fwd_kernels(0, 1, 8, 16, 8, 8, 0, None, ctypes.byref(gen)) == pkg.ERR_NULLPTR
+    two, gen, nar = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.ssm2d_fwd_kernels(0, 1, 8, 16, 8, 8, 1 << 10, ctypes.byref(two), ctypes.byref(gen),
+                                 ctypes.byref(nar)) == pkg.ERR_BAD_FLAGS
+    assert lib.ssm2d_fwd_kernels(0, 1, 8, 16, 8, 8, 0, None, ctypes.byref(gen), ctypes.byref(nar)) == pkg.ERR_NULLPTR
+    assert lib.ssm2d_fwd_kernels(0, 1, 8, 16, 8, 8, 0, ctypes.byref(two), ctypes.byref(gen), None) == pkg.ERR_NULLPTR

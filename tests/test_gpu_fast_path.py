@@ -107,7 +107,7 @@ def test_fast_path_layouts(case, monkeypatch):
     args = to_dev(t, dtype)
     ref = ref_of(t)
     monkeypatch.setenv("SSM2D_FAST", "2")  # chains in one workgroup too
-    assert pkg.fwd_kernels(*shape, bf16=dtype == "bf16") == (1, 0)
+    assert pkg.fwd_kernels(*shape, bf16=dtype == "bf16") == (1, 0, 0)
     y = pkg.scan_fwd(*args)
     pkg.sync_check()
     check(as_f64(y), ref, dtype, f"fast {shape}")

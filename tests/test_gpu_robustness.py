@@ -1,7 +1,7 @@
 """GPU tests of the library's launch machinery around the scan: HIP-graph
 capture and replay, the carry-tag epoch and its wrap, timeouts that surface on
-the next call, the release of workspaces, and launches with a bounded carry
-ring that share the device with each other.
+the next call, the release of workspaces, launches that share the GPU with
+each other, and the bounded carry ring's blocks of tickets.
 
 The carry words that link the tiles of one map across workgroups are tagged
 with an epoch kept in device memory; every launch (every replay of a captured
@@ -20,10 +20,10 @@ from test_gpu_parity import KEYS, _say, _setup, as_f64, check, ref_of, to_dev  #
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-# chains cut into several workgroups: the giga-pixel layout (bounded global
-# ring when the grid is co-resident) and forced one-strip workgroups
+# chains cut into several workgroups: the giga-pixel layout (a carry slot a
+# row, or a bounded ring of 32 rows) and forced one-strip workgroups
 # (couriers on every boundary)
-CHAIN_CASES = [((1, 32, 16, 96, 512), None), ((1, 16, 16, 40, 96), "1")]
+CHAIN_CASES = [((1, 32, 16, 96, 512), None, None), ((1, 32, 16, 96, 512), None, "32"), ((1, 16, 16, 40, 96), "1", None)]
 
 
 def _copy_inputs(dst, t):
@@ -36,9 +36,11 @@ def test_graph_replays_forward(case, monkeypatch):
     """A forward captured in a HIP graph and replayed with new inputs copied
     in before each replay, with eager calls on the same stream in between:
     every replay and every eager call matches the oracle."""
-    shape, waves = case
+    shape, waves, ring = case
     if waves:
         monkeypatch.setenv("SSM2D_WAVES", waves)
+    if ring:
+        monkeypatch.setenv("SSM2D_RING", ring)
     s = torch.cuda.Stream()
     t0 = make_random_inputs(*shape, seed=60)
     with torch.cuda.stream(s):
@@ -182,18 +184,23 @@ def test_release_workspaces_and_reuse():
         pkg.release_workspaces()
 
 
-def test_concurrent_streams_with_bounded_rings():
-    """Three streams each launch the giga-pixel map (384 x 512, 128 channels,
-    16 states: chains across workgroups with the bounded carry ring, a grid
-    that alone fills the device) several times without waiting, so the
-    launches compete for the compute units. A chain's workgroups take
-    consecutive tickets there, so every launch drains: no wait gives up, and
-    each output equals (bit for bit) the same call run alone; sampled maps
-    match the oracle."""
+@pytest.mark.parametrize("ring", [None, "32"])
+def test_concurrent_streams(ring, monkeypatch):
+    """Streams each launch the giga-pixel map (384 x 512, 128 channels, 16
+    states: chains across workgroups, a grid that alone fills the GPU)
+    several times without waiting, so the launches compete for the compute
+    units: three streams with a carry slot a row (no producer waits on a
+    consumer), two with the bounded ring of 32 rows (tickets in blocks of 8
+    chains: at most 120 waiting workgroups a launch). Every launch drains: no
+    wait gives up, and each output equals (bit for bit) the same call run
+    alone; sampled maps match the oracle."""
+    if ring:
+        monkeypatch.setenv("SSM2D_RING", ring)
+    nstreams = 2 if ring else 3
     shape = (1, 128, 16, 384, 512)
-    assert pkg.fwd_kernels(*shape) == (1, 0)
-    streams = [torch.cuda.Stream() for _ in range(3)]
-    ts = [make_random_inputs(*shape, seed=130 + i) for i in range(3)]
+    assert pkg.fwd_kernels(*shape) == (1, 0, 0)
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    ts = [make_random_inputs(*shape, seed=130 + i) for i in range(nstreams)]
     args, alone = [], []
     for s, t in zip(streams, ts):
         with torch.cuda.stream(s):
@@ -204,7 +211,7 @@ def test_concurrent_streams_with_bounded_rings():
         pkg.sync_check(s)
     maps = [0, 63, 127]
     check(as_f64(alone[0]).reshape(-1, 384, 512)[maps], ref_of(ts[0], maps=maps), "f32", "giga-pixel map alone")
-    outs = [[torch.empty_like(alone[i]) for _ in range(4)] for i in range(3)]
+    outs = [[torch.empty_like(alone[i]) for _ in range(4)] for i in range(nstreams)]
     for r in range(4):
         for i, s in enumerate(streams):
             with torch.cuda.stream(s):
@@ -214,14 +221,16 @@ def test_concurrent_streams_with_bounded_rings():
         pkg.sync_check(s)
         for r in range(4):
             assert torch.equal(outs[i][r], alone[i]), f"stream {i} launch {r}"
-    _say("  12 overlapping launches on 3 streams: all equal to the lone runs")
+    _say(f"  {4 * nstreams} overlapping launches on {nstreams} streams (ring {ring}): all equal to the lone runs")
 
 
 @pytest.mark.parametrize("tblk", ["1", "3", "8", "64"])
 def test_ticket_blocks(tblk, monkeypatch):
-    """Tickets dealt in blocks of 1, 3, 8 chains, and all chains at once
-    (10 chains: a partial last block), through the two-rows-per-step forward
-    and the general kernel; exact against the oracle on every map."""
+    """The bounded ring with tickets dealt in blocks of 1, 3, 8 chains, and
+    all chains at once (10 chains: a partial last block), through the
+    two-rows-per-step forward and the general kernel; exact against the
+    oracle on every map."""
+    monkeypatch.setenv("SSM2D_RING", "32")
     monkeypatch.setenv("SSM2D_TICKET_BLOCK", tblk)
     shape = (2, 40, 16, 96, 512)
     t = make_random_inputs(*shape, seed=140 + int(tblk))

@@ -1,8 +1,10 @@
 """ssm2d_scan_fwd_noalloc: the forward in a static device array, through the C
-ABI, against the allocating entry point ssm2d_scan_fwd (same kernels, same
-plan: bitwise equal) and the oracle, on two calls in a row, the second on a
-smaller map; and a map whose workspace exceeds the array is refused before
-anything runs."""
+ABI, against the allocating entry point ssm2d_scan_fwd (same kernels and
+arithmetic; on the giga-pixel map the array holds a bounded carry ring where
+the allocating call has a slot a row, which carries the same values: bitwise
+equal) and the oracle, on two calls in a row, the second on a smaller map;
+and a map whose workspace exceeds the array is refused before anything
+runs."""
 import ctypes
 
 import numpy as np
