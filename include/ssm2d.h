@@ -46,21 +46,21 @@
  *
  * Carry waits: when a map's chain of tiles spans several workgroups, a tile
  * waits for its left neighbour's carries, produced by a workgroup that started
- * earlier (workgroups take tickets in the order they start). Each row's
- * carries have their own slot, so a producer never waits for its consumer:
- * kernels of other streams or processes (other ssm2d launches too, any number
- * of them) that hold part of the GPU delay a launch but cannot block it, as
- * long as they release their compute units in time. A bounded ring of carry
- * rows with back-pressure (SSM2D_RING below, or ssm2d_scan_fwd_noalloc when
- * its array cannot hold a slot a row) makes producers wait for consumers too;
- * tickets are then dealt in blocks of a few chains, so only the started
- * workgroups of the last block's chains can wait on a consumer that has not
- * started (under half the GPU's slots, or one chain's workgroups for
- * ssm2d_scan_fwd_noalloc). A wait gives up after a bound (about a second;
- * ssm2d_set_spin_limit): the outputs from that point on are NaN, the next
- * call on the same (device, stream) returns SSM2D_ERR_DEVICE_TIMEOUT without
- * enqueueing anything (read from a host-visible flag, no wait), and
- * ssm2d_sync_check reports it too.
+ * earlier (workgroups take tickets in the order they start). The carries go
+ * through a bounded ring of rows (32; where the launch's grid fits the GPU at
+ * once) followed by overflow rows: a producer waits for room only once its
+ * consumer has reported progress, and otherwise writes on into the overflow
+ * rows. So no producer waits on a consumer that has not started: kernels of
+ * other streams or processes (other ssm2d launches too, any number of them)
+ * that hold part of the GPU delay a launch but cannot block it, as long as
+ * they release their compute units in time. ssm2d_scan_fwd_noalloc, when its
+ * array cannot hold the overflow rows, runs the ring alone; its producers
+ * may then wait on consumers that have not started, and its tickets are
+ * dealt one chain at a time, so at most one chain's workgroups wait so.
+ * A wait gives up after a bound (about a second; ssm2d_set_spin_limit): the
+ * outputs from that point on are NaN, the next call on the same (device,
+ * stream) returns SSM2D_ERR_DEVICE_TIMEOUT without enqueueing anything (read
+ * from a host-visible flag, no wait), and ssm2d_sync_check reports it too.
  *
  * Errors: every function returns a status and never throws or aborts.
  *   batch, d_inner, d_state, H or W < 0          -> SSM2D_ERR_BAD_DIM
@@ -356,10 +356,11 @@ int ssm2d_scan_bwd_mamba_bf16(const uint16_t *x, const uint16_t *delta, const fl
  * Limits: the zero page holds 1 MiB (H * W <= 262128 cells) and the carry
  * ring about 15 MiB (chains of tiles that span workgroups need
  * n_chains * (workgroups per chain - 1) * ring rows * 64 lanes * 8 bytes per
- * state a lane, with a row per map row where that fits, else a bounded ring
- * of 32 rows when the grid fits the GPU at once; the giga-pixel map, 384 x 512
- * with 128 channels and 16 states, takes the bounded ring: 7.5 MiB). A call
- * whose plan exceeds them returns SSM2D_ERR_TOO_LARGE and enqueues nothing.
+ * state a lane, with 32 rows plus a row per map row where that fits, else
+ * the 32 rows alone (where the grid fits the GPU at once); the giga-pixel
+ * map, 384 x 512 with 128 channels and 16 states, takes the 32 rows alone:
+ * 7.5 MiB). A call whose plan exceeds them returns SSM2D_ERR_TOO_LARGE and
+ * enqueues nothing.
  * Every call on a GPU shares that GPU's array, whose head words (tickets,
  * tag epoch) carry over from call to call: calls that overlap on one GPU
  * (other streams, other threads) race and must be ordered by the caller.
@@ -428,12 +429,16 @@ int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state,
  *   SSM2D_VECSTORE=0|1   cell-by-cell output stores, or each channel's cells
  *                        gathered into wider stores (default: 1 for 4-column
  *                        strips, 0 for 8-column strips)
- *   SSM2D_RING=n         a bounded global carry ring of n >= 8 rows, with
- *                        back-pressure, where the grid fits the GPU at once
- *                        (default 0: one slot a row)
- *   SSM2D_TICKET_BLOCK=n chains per block of tickets with the bounded ring
- *                        (default: the most that keeps two launches' waiting
- *                        workgroups under the GPU's slots, in 8s)
+ *   SSM2D_RING=n         rows of the bounded global carry ring (default 32;
+ *                        n < 8 or n >= H: one slot a row)
+ *   SSM2D_OVERFLOW=0|1|2 overflow rows after the bounded ring: none (then
+ *                        producers may wait on consumers that have not
+ *                        started), for consumers that have not started (1,
+ *                        default), from every producer's ninth row (2, a test)
+ *   SSM2D_TICKET_BLOCK=n chains per block of tickets (default: all chains
+ *                        at once; without overflow rows, the most that keeps
+ *                        two launches' waiting workgroups under the GPU's
+ *                        slots, in 8s)
  *   SSM2D_LDSRING=4|16|32  depth of the LDS carry rings
  *   SSM2D_XCD_REMAP=0    no placement of consecutive chains on one XCD
  *   SSM2D_NARROW=0|1|2   the whole-row kernel for narrow maps: never (0),

@@ -575,6 +575,7 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
     const size_t lds = Sh::lds_bytes(pl.s_local);
     pl.qg = H;
     pl.tblk = pl.n_chains;
+    pl.ovf = 0;
     if constexpr (CHAINED) {
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fast_kernel<T, G, NPL, K, true>, threads,

@@ -30,11 +30,11 @@
 //     pipeline, one row deep per strip.
 //   * Multi-workgroup chains take tickets from an atomic counter; ticket order
 //     puts every producer before its consumer, so a waiting workgroup's
-//     producer is resident or done. The global ring has a slot per row, so
-//     nothing waits on a consumer; a bounded ring with back-pressure (asked
-//     for, or forced by a fixed-size workspace) deals tickets in blocks of a
-//     few chains, so only the chains of the last block begun can have a
-//     producer waiting on a consumer not yet started.
+//     producer is resident or done. The global ring is bounded, with
+//     back-pressure, and followed by overflow rows: a producer waits for a
+//     consumer only once that consumer has reported progress, and otherwise
+//     moves on to the overflow rows, so none waits on a consumer that has not
+//     started (bound_ring below).
 //   * The sum over n: each lane holds K partial sums over its NPL states; two
 //     permlane swaps (32- and 16-lane) transpose-reduce them across the 4 state
 //     groups, leaving each lane with K/4 finished cells.
@@ -121,14 +121,17 @@ struct Params {
     // values run 0 .. 65534; a launch's tags use stored + 1.
     unsigned int *epoch;
     unsigned int *herr;                // host-visible timeout flag (may be null)
-    unsigned long long *gring;         // [n_bound][qg][NPL][64] tagged carries
-    unsigned long long *cons;          // [n_bound] consumer progress: epoch<<32 | rows
+    unsigned long long *gring;         // [n_bound][qg (+ H)][NPL][64] tagged carries
+    unsigned long long *cons;          // [n_bound][2]: consumer progress, first overflow row (epoch<<32 | row)
     long gring_words, cons_words;      // cleared when the epoch wraps
     int batch, d_inner, d_state, H, W;
     int nstrips, s_local, groups, n_dblk, n_chains, total_wg;
     int tblk;                          // chains per block of tickets
     int ring_rows;                     // LDS ring depth between waves
     int qg;                            // global ring depth (== H: no reuse)
+    int ovf;                           // bounded ring: 0 no overflow rows, 1 overflow rows for a
+                                       // consumer that has not started, 2 (test) every producer
+                                       // moves to them after its first 8 rows
     int use_ticket;                    // chains span workgroups
     int xcd_remap;                     // spread chains over XCDs in contiguous blocks
     int vec_store;                     // gather each channel's cells and store whole chunks
@@ -613,11 +616,18 @@ __device__ __forceinline__ void courier_wave(const Params &p, const int wave, co
 {
     const int H = p.H;
     const long nb_per_chain = p.groups - 1;
-    const long gstride = static_cast<long>(p.qg) * NPL * kWave;
+    // a boundary's slots: qg ring rows, then (bounded ring with overflow) a
+    // row per map row
+    const long gstride = static_cast<long>(p.qg + (p.ovf ? H : 0)) * NPL * kWave;
     const unsigned int etag = s_epoch << 16;
     const unsigned long long ctag = static_cast<unsigned long long>(s_epoch) << 32;
     long idle = 0;
     bool timed_out = false;
+    // rows at or past ovf_from sit in the overflow rows (as last seen)
+    int ovf_from = H;
+    auto slot_of = [&](int row) __attribute__((always_inline)) {
+        return row >= ovf_from ? p.qg + row : row % p.qg;
+    };
     if (wave == p.s_local && grp > 0) {
         const long bound_in = chain * nb_per_chain + (grp - 1);
         const unsigned long long *gin = p.gring + bound_in * gstride + lane;
@@ -634,7 +644,7 @@ __device__ __forceinline__ void courier_wave(const Params &p, const int wave, co
                     if (r < nb)
 #pragma unroll
                         for (int k = 0; k < NPL; ++k)
-                            w[r][k] = ld_relaxed(gin + (static_cast<long>((in_next + r) % p.qg) * NPL + k) * kWave);
+                            w[r][k] = ld_relaxed(gin + (static_cast<long>(slot_of(in_next + r)) * NPL + k) * kWave);
 #pragma unroll
                 for (int r = 0; r < kCourierBatch; ++r) {
                     if (r < nb && v == r) {
@@ -654,9 +664,15 @@ __device__ __forceinline__ void courier_wave(const Params &p, const int wave, co
             if (v > 0) {
                 in_next += v;
                 lds_publish(&s_done[0], in_next);
-                if (p.qg < H) st_relaxed(p.cons + bound_in, ctag | static_cast<unsigned>(in_next));
+                if (p.qg < H) st_relaxed(p.cons + 2 * bound_in, ctag | static_cast<unsigned>(in_next));
                 idle = 0;
             } else {
+                // nothing new: has the producer moved to the overflow rows?
+                if (p.ovf && ovf_from == H) {
+                    const unsigned long long f = ld_relaxed(p.cons + 2 * bound_in + 1);
+                    if ((f & 0xffffffff00000000ull) == ctag)
+                        ovf_from = __builtin_amdgcn_readfirstlane(static_cast<int>(f & 0xffffffffu));
+                }
                 if (++idle > p.spin_limit) { timed_out = true; break; }
                 sleep_a_bit();
             }
@@ -672,13 +688,32 @@ __device__ __forceinline__ void courier_wave(const Params &p, const int wave, co
         unsigned long long *gout = p.gring + bound_out * gstride + lane;
         const float *ringS = lring + static_cast<long>(p.s_local) * ring_floats;
         int out_next = 0, cons_seen = 0;
+        bool started = false;  // the consumer has reported progress
         while (out_next < H) {
             const int avail = lds_counter(&s_done[p.s_local]);
             int nb = min(kCourierBatch, avail - out_next);
-            if (p.qg < H && nb > 0 && out_next + nb > cons_seen + p.qg) {
-                const unsigned long long c = ld_relaxed(p.cons + bound_out);
-                if ((c & 0xffffffff00000000ull) == ctag) cons_seen = static_cast<int>(c & 0xffffffffu);
-                nb = min(nb, cons_seen + p.qg - out_next);
+            if (p.ovf == 2 && ovf_from == H && out_next >= 8) {
+                // (test of the overflow rows: every producer moves there
+                // after its first 8 rows)
+                ovf_from = out_next;
+                st_relaxed(p.cons + 2 * bound_out + 1, ctag | static_cast<unsigned>(ovf_from));
+            }
+            if (p.qg < H && nb > 0 && out_next < ovf_from && out_next + nb > cons_seen + p.qg) {
+                const unsigned long long c = ld_relaxed(p.cons + 2 * bound_out);
+                if ((c & 0xffffffff00000000ull) == ctag) {
+                    cons_seen = static_cast<int>(c & 0xffffffffu);
+                    started = true;
+                }
+                const int room = cons_seen + p.qg - out_next;
+                if (room < nb && p.ovf != 0 && !started) {
+                    // The ring is full and the consumer may not be able to
+                    // start (other work holds the GPU): rather than wait,
+                    // write the rows from here on to the overflow rows.
+                    ovf_from = out_next + room;
+                    st_relaxed(p.cons + 2 * bound_out + 1, ctag | static_cast<unsigned>(ovf_from));
+                } else {
+                    nb = min(nb, room);
+                }
             }
             if (nb > 0) {
 #pragma unroll
@@ -689,7 +724,7 @@ __device__ __forceinline__ void courier_wave(const Params &p, const int wave, co
                         const unsigned long long tagw = static_cast<unsigned long long>(etag | static_cast<unsigned>(row)) << 32;
 #pragma unroll
                         for (int k = 0; k < NPL; ++k)
-                            st_relaxed(gout + (static_cast<long>(row % p.qg) * NPL + k) * kWave,
+                            st_relaxed(gout + (static_cast<long>(slot_of(row)) * NPL + k) * kWave,
                                        tagw | __float_as_uint(src_c[k]));
                     }
                 }
@@ -1656,6 +1691,7 @@ struct BwdArgs {
 
 struct Plan {
     int G, K, npl, nstrips, s_local, groups, n_dblk, n_chains, total_wg, ring_rows, qg;
+    int ovf;         // overflow rows after the bounded ring (Params::ovf)
     int tblk;        // chains per block of tickets (0: n_chains)
     int coop_slots;  // rows of the shared row ring with cooperative loads, 0 = per-wave packets
     int mode;        // kMode* bits
@@ -1722,39 +1758,51 @@ size_t lds_bytes(const Plan &pl)
            static_cast<size_t>(pl.s_local + 1) * pl.ring_rows * kWave * NPL * sizeof(float);
 }
 
-// Global ring. By default one slot a row: a producer never waits on its
-// consumer, only consumers wait, on producers that took earlier tickets, so a
-// launch drains whatever else holds the GPU's compute units (other streams,
-// other processes, any number of other launches), and tickets go strip group
-// by strip group (every chain's first tile starts at once). A bounded ring of
-// qg rows with back-pressure, when asked for (SSM2D_RING=qg) or when a
-// workspace of fixed size cannot hold a slot a row, is used only if the whole
-// grid fits the GPU at once. Its producers wait on consumers: only the started
-// workgroups of partly started chains can then wait on one that has not
-// started, and tickets dealt in blocks of tblk chains cap them at
-// tblk * (groups - 1). Asked for, tblk keeps that under half the GPU's slots
-// (two such launches sharing the GPU still drain), in multiples of 8 so that
-// each chain's workgroups share an XCD; a fixed workspace takes one chain a
-// block (groups - 1 workgroups at most).
+// Global ring between the workgroups of a chain. Where the whole grid fits
+// the GPU at once, a bounded ring of qg = 32 rows (SSM2D_RING) with
+// back-pressure, followed by a row per map row of overflow: a producer whose
+// ring is full waits for its consumer only once the consumer has reported
+// progress; before that (the consumer may not have started: other work holds
+// the GPU) it moves on to the overflow rows and tells the consumer from which
+// row. So no producer waits on a consumer that has not started, and a launch
+// drains whatever else holds the GPU. Tickets go strip group by strip group
+// (every chain's first tile starts at once). A workspace of fixed size that
+// cannot hold the overflow rows takes the ring alone; its producers may then
+// wait on consumers that have not started, and tickets are dealt in blocks of
+// one chain, so only the started workgroups of the last chain begun (groups -
+// 1 at most) can wait so. SSM2D_OVERFLOW=0 leaves the overflow rows out (then
+// tblk keeps two launches' waiting workgroups under the GPU's slots, in
+// multiples of 8 so that a chain's workgroups share an XCD), =2 makes every
+// producer move to them after its first 8 rows (a test of that path). Grids
+// larger than the GPU, or SSM2D_RING < 8 or >= H, take a slot a row.
 inline void bound_ring(Plan &pl, long resident, int H, int npl)
 {
     pl.qg = H;
     pl.tblk = pl.n_chains;
+    pl.ovf = 0;
     if (pl.groups <= 1) return;
-    int qg = env_int("SSM2D_RING", 0);
+    const int qg = env_int("SSM2D_RING", 32);
+    if (resident < pl.total_wg || qg < 8 || qg >= H) return;
+    int ovf = env_int("SSM2D_OVERFLOW", 1);
+    ovf = ovf < 0 ? 0 : (ovf > 2 ? 2 : ovf);
     bool one_chain = false;
     if (pl.fixed_ws) {
         const size_t row_bytes = static_cast<size_t>(pl.n_chains) * (pl.groups - 1) * npl * kWave * sizeof(unsigned long long);
-        if (row_bytes * H > pl.fixed_ws->gring_bytes) {
-            qg = 32;
+        if (ovf && row_bytes * (qg + H) > pl.fixed_ws->gring_bytes) {
+            ovf = 0;
             one_chain = true;
         }
     }
-    if (resident < pl.total_wg || qg < 8 || qg >= H) return;
-    const int forced = env_int("SSM2D_TICKET_BLOCK", 0);
-    long tb = forced > 0 ? forced : (one_chain ? 1 : (resident - 1) / (2L * (pl.groups - 1)));
-    if (forced <= 0 && tb >= 8) tb -= tb % 8;
     pl.qg = qg;
+    pl.ovf = ovf;
+    const int forced = env_int("SSM2D_TICKET_BLOCK", 0);
+    long tb = pl.n_chains;
+    if (forced > 0) {
+        tb = forced;
+    } else if (!ovf) {
+        tb = one_chain ? 1 : (resident - 1) / (2L * (pl.groups - 1));
+        if (tb >= 8) tb -= tb % 8;
+    }
     pl.tblk = static_cast<int>(tb < 1 ? 1 : (tb < pl.n_chains ? tb : pl.n_chains));
 }
 
@@ -1763,6 +1811,7 @@ void choose_ring(Plan &pl, int dev, int H)
 {
     pl.qg = H;
     pl.tblk = pl.n_chains;
+    pl.ovf = 0;
     if (pl.groups <= 1 || (pl.mode & kModeEdges)) return;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan2d_fwd_kernel<T, K, NPL, ALIGN, G, COOP, MODE>, block_threads(pl),
@@ -1778,11 +1827,11 @@ WsNeed ws_need(const Plan &pl, int d_inner, int H, int W)
 {
     const long n_bound = static_cast<long>(pl.n_chains) * (pl.groups - 1);
     WsNeed n{};
-    n.gring_bytes = static_cast<size_t>(n_bound) * pl.qg * NPL * kWave * sizeof(unsigned long long);
+    n.gring_bytes = static_cast<size_t>(n_bound) * (pl.qg + (pl.ovf ? H : 0)) * NPL * kWave * sizeof(unsigned long long);
     // zero page: whole rows of any input type, and a zero D (no skip term)
     n.zero_bytes = static_cast<size_t>(H) * W * 4 + 64;
     if (n.zero_bytes < static_cast<size_t>(d_inner) * 4 + 64) n.zero_bytes = static_cast<size_t>(d_inner) * 4 + 64;
-    n.cons_count = static_cast<size_t>(n_bound > 0 ? n_bound : 1);
+    n.cons_count = static_cast<size_t>(n_bound > 0 ? 2 * n_bound : 1);
     return n;
 }
 
@@ -1829,6 +1878,7 @@ inline Params make_params(const void *x, const void *delta, const float *A, cons
     prm.batch = batch; prm.d_inner = d_inner; prm.d_state = d_state; prm.H = H; prm.W = W;
     prm.nstrips = pl.nstrips; prm.s_local = pl.s_local; prm.groups = pl.groups; prm.n_dblk = pl.n_dblk;
     prm.n_chains = pl.n_chains; prm.total_wg = pl.total_wg; prm.ring_rows = pl.ring_rows; prm.qg = pl.qg;
+    prm.ovf = pl.qg < H ? pl.ovf : 0;
     prm.use_ticket = pl.groups > 1 ? 1 : 0;
     prm.tblk = pl.tblk > 0 && pl.tblk < pl.n_chains ? pl.tblk : pl.n_chains;
     prm.xcd_remap = (pl.groups == 1 && pl.total_wg % 8 == 0 && env_int("SSM2D_XCD_REMAP", 1)) ? 1 : 0;

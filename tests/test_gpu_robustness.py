@@ -1,7 +1,8 @@
 """GPU tests of the library's launch machinery around the scan: HIP-graph
 capture and replay, the carry-tag epoch and its wrap, timeouts that surface on
 the next call, the release of workspaces, launches that share the GPU with
-each other, and the bounded carry ring's blocks of tickets.
+each other, the carry ring's overflow rows and the bounded ring's blocks of
+tickets.
 
 The carry words that link the tiles of one map across workgroups are tagged
 with an epoch kept in device memory; every launch (every replay of a captured
@@ -20,10 +21,10 @@ from test_gpu_parity import KEYS, _say, _setup, as_f64, check, ref_of, to_dev  #
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-# chains cut into several workgroups: the giga-pixel layout (a carry slot a
-# row, or a bounded ring of 32 rows) and forced one-strip workgroups
-# (couriers on every boundary)
-CHAIN_CASES = [((1, 32, 16, 96, 512), None, None), ((1, 32, 16, 96, 512), None, "32"), ((1, 16, 16, 40, 96), "1", None)]
+# chains cut into several workgroups: the giga-pixel layout (the bounded
+# carry ring with overflow rows, or a slot a row) and forced one-strip
+# workgroups (couriers on every boundary)
+CHAIN_CASES = [((1, 32, 16, 96, 512), None, None), ((1, 32, 16, 96, 512), None, "0"), ((1, 16, 16, 40, 96), "1", None)]
 
 
 def _copy_inputs(dst, t):
@@ -184,19 +185,24 @@ def test_release_workspaces_and_reuse():
         pkg.release_workspaces()
 
 
-@pytest.mark.parametrize("ring", [None, "32"])
-def test_concurrent_streams(ring, monkeypatch):
+# (SSM2D_RING, SSM2D_OVERFLOW, streams): the bounded ring with overflow rows
+# (default), a slot a row, the bounded ring alone (tickets in blocks of 8
+# chains: at most 120 waiting workgroups a launch, so two launches)
+RING_MODES = [(None, None, 3), ("0", None, 3), ("32", "0", 2)]
+
+
+@pytest.mark.parametrize("mode", RING_MODES, ids=str)
+def test_concurrent_streams(mode, monkeypatch):
     """Streams each launch the giga-pixel map (384 x 512, 128 channels, 16
     states: chains across workgroups, a grid that alone fills the GPU)
     several times without waiting, so the launches compete for the compute
-    units: three streams with a carry slot a row (no producer waits on a
-    consumer), two with the bounded ring of 32 rows (tickets in blocks of 8
-    chains: at most 120 waiting workgroups a launch). Every launch drains: no
-    wait gives up, and each output equals (bit for bit) the same call run
-    alone; sampled maps match the oracle."""
+    units. Every launch drains: no wait gives up, and each output equals (bit
+    for bit) the same call run alone; sampled maps match the oracle."""
+    ring, ovf, nstreams = mode
     if ring:
         monkeypatch.setenv("SSM2D_RING", ring)
-    nstreams = 2 if ring else 3
+    if ovf:
+        monkeypatch.setenv("SSM2D_OVERFLOW", ovf)
     shape = (1, 128, 16, 384, 512)
     assert pkg.fwd_kernels(*shape) == (1, 0, 0)
     streams = [torch.cuda.Stream() for _ in range(nstreams)]
@@ -221,16 +227,40 @@ def test_concurrent_streams(ring, monkeypatch):
         pkg.sync_check(s)
         for r in range(4):
             assert torch.equal(outs[i][r], alone[i]), f"stream {i} launch {r}"
-    _say(f"  {4 * nstreams} overlapping launches on {nstreams} streams (ring {ring}): all equal to the lone runs")
+    _say(f"  {4 * nstreams} overlapping launches on {nstreams} streams {mode}: all equal to the lone runs")
+
+
+@pytest.mark.parametrize("shape", [(1, 128, 16, 384, 512), (2, 40, 16, 96, 512), (1, 16, 16, 80, 96)], ids=str)
+@pytest.mark.parametrize("fast", ["1", "0"])
+def test_overflow_rows(shape, fast, monkeypatch):
+    """Every producer moves to the overflow rows after its first 8 rows
+    (SSM2D_OVERFLOW=2; one-strip workgroups on the small map), through the
+    two-rows-per-step forward and the general kernel: exact against the
+    oracle on sampled maps, and bit for bit equal to the bounded ring's run."""
+    monkeypatch.setenv("SSM2D_FAST", fast)
+    if shape[4] < 512:
+        monkeypatch.setenv("SSM2D_WAVES", "1")
+    t = make_random_inputs(*shape, seed=150 + shape[3])
+    args = to_dev(t, "f32")
+    y0 = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    monkeypatch.setenv("SSM2D_OVERFLOW", "2")
+    _say(f"overflow rows {shape} fast={fast}")
+    y = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    assert torch.equal(y, y0)
+    nmaps = shape[0] * shape[1]
+    maps = sorted({0, nmaps // 2, nmaps - 1})
+    check(as_f64(y).reshape(nmaps, shape[3], shape[4])[maps], ref_of(t, maps=maps), "f32", f"overflow {shape}")
 
 
 @pytest.mark.parametrize("tblk", ["1", "3", "8", "64"])
 def test_ticket_blocks(tblk, monkeypatch):
-    """The bounded ring with tickets dealt in blocks of 1, 3, 8 chains, and
-    all chains at once (10 chains: a partial last block), through the
+    """The bounded ring without overflow rows, tickets dealt in blocks of 1,
+    3, 8 chains, and all chains at once (10 chains: a partial last block), through the
     two-rows-per-step forward and the general kernel; exact against the
     oracle on every map."""
-    monkeypatch.setenv("SSM2D_RING", "32")
+    monkeypatch.setenv("SSM2D_OVERFLOW", "0")
     monkeypatch.setenv("SSM2D_TICKET_BLOCK", tblk)
     shape = (2, 40, 16, 96, 512)
     t = make_random_inputs(*shape, seed=140 + int(tblk))
