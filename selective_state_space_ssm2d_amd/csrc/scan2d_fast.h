@@ -36,6 +36,7 @@ constexpr int kFastAhead = 3;       // steps a wave writes its share ahead of pr
 constexpr int kFastPrefetch = SSM2D_FAST_PREFETCH;    // steps a share's loads are issued ahead of writing it
 constexpr int kFastCarryRows = 8;   // rows of each LDS carry ring
 constexpr int kFastStrips = 8;      // strips a workgroup of a chain across workgroups holds (with two couriers)
+constexpr int kFastStripsWide = 4;  // the same for 8-column strips (one compute wave a SIMD)
 constexpr int kFastStripsOne = 16;  // strips a workgroup holding a whole chain can hold (light layouts)
 
 // Input ring: the invariant that keeps a slot from being rewritten while it is
@@ -74,13 +75,15 @@ struct FastShape {
         return static_cast<size_t>(s + 1) * kFastCarryRows * kWave * NPL * 4;
     }
     static constexpr size_t lds_bytes(int s) { return ring_bytes(s) + carry_bytes(s); }
-    // Strips a workgroup can hold: 8 (and two couriers) for chains across
-    // workgroups; 16 for a whole chain in the layouts light enough in
+    // Strips a workgroup can hold: 8 (and two couriers) for chains of
+    // 4-column strips across workgroups, 4 for 8-column strips (one compute
+    // wave a SIMD, 256 registers a wave); 16 for a whole chain in the layouts light enough in
     // registers for 16 waves a CU (4-column strips with 1 state a lane, or
     // bf16 inputs), else 8.
     static constexpr int max_strips(bool chained)
     {
-        return chained ? kFastStrips : ((K == 4 && (NPL == 1 || sizeof(T) == 2)) ? kFastStripsOne : kFastStrips);
+        if (chained) return K == 8 ? kFastStripsWide : kFastStrips;
+        return (K == 4 && (NPL == 1 || sizeof(T) == 2)) ? kFastStripsOne : kFastStrips;
     }
 };
 
@@ -602,15 +605,13 @@ int run_fast(const T *x, const T *delta, const float *A, const T *B, const T *C,
     return err == hipSuccess ? SSM2D_OK : hip_fail(err);
 }
 
-// Whether a plan fits a layout's kernel: 8-column strips only for chains held
-// in one workgroup (with couriers their registers would spill), at most
-// max_strips strips a workgroup, LDS within the CU's.
+// Whether a plan fits a layout's kernel: at most max_strips strips a
+// workgroup, LDS within the CU's.
 template <typename T, int G, int NPL, int K>
 bool fast_layout_ok(const Plan &pl)
 {
     using Sh = FastShape<T, G, NPL, K>;
     const bool chained = pl.groups > 1;
-    if (K == 8 && chained) return false;
     return pl.s_local >= 1 && pl.s_local <= Sh::max_strips(chained) && Sh::lds_bytes(pl.s_local) <= kFastLdsMax;
 }
 
@@ -618,13 +619,8 @@ template <typename T, int G, int NPL, int K>
 int run_fast_layout(const T *x, const T *delta, const float *A, const T *B, const T *C, const float *D, T *y, int batch,
                     int d_inner, int d_state, int H, int W, const Plan &pl, int dev, void *stream)
 {
-    if constexpr (K == 4) {
-        if (pl.groups > 1)
-            return run_fast<T, G, NPL, K, true>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev,
-                                                stream);
-    } else {
-        if (pl.groups > 1) return kNoFastPath;  // (no chained instance)
-    }
+    if (pl.groups > 1)
+        return run_fast<T, G, NPL, K, true>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
     return run_fast<T, G, NPL, K, false>(x, delta, A, B, C, D, y, batch, d_inner, d_state, H, W, pl, dev, stream);
 }
 

@@ -14,7 +14,9 @@ int env_int(const char *name, int dflt)
     return (s && *s) ? std::atoi(s) : dflt;
 }
 
-Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode)
+// k_want = 8: 8-column strips wherever the mode allows them (the plain
+// forward's choice for long chains across workgroups, below).
+Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, int k_want = 0)
 {
     Plan pl{};
     pl.mode = mode;
@@ -60,6 +62,7 @@ Plan make_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64
         pl.K = 8;
     const int kenv = env_int("SSM2D_STRIP", 0);
     if (kenv == 4 || (kenv == 8 && wide_ok)) pl.K = kenv;
+    else if (k_want == 8 && wide_ok) pl.K = 8;
     if ((mode & (kModeStates | kModeBackward)) || (mode != 0 && G == 4)) pl.K = 4;
     const int maxw = max_waves(pl.K, npl, G, mode);
     pl.nstrips = static_cast<int>((W + pl.K - 1) / pl.K);
@@ -594,6 +597,25 @@ bool takes_fast(Plan &pl, int64_t W, int align)
     return fast_path_taken<T>(pl, align);
 }
 
+// The plan of a forward launch. For the plain forward of chains cut into
+// several workgroups, 8-column strips (4 a workgroup with two couriers, one
+// compute wave a SIMD) in the two-rows-per-step kernel where that plan still
+// gives the chip 256 workgroups: half the strips a chain, so half the carry
+// hops, at the same work a SIMD (giga-pixel map: 270 us against 276-281 us
+// for 4-column strips, two compute waves a SIMD). Narrower maps keep 4-column
+// strips (with 8-column ones their chains would fill only part of the chip).
+// `carries`: a gate or carried states, which the two-rows-per-step kernel
+// does not take.
+template <typename T>
+Plan forward_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W, int mode, bool carries)
+{
+    Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
+    if (mode != 0 || carries || pl.groups <= 1 || pl.K != 4 || env_int("SSM2D_STRIP", 0) != 0) return pl;
+    Plan p8 = make_plan(batch, d_inner, d_state, H, W, mode, 8);
+    if (p8.K == 8 && p8.groups > 1 && p8.total_wg >= 256 && fast_path_taken<T>(p8, row_align(W))) return p8;
+    return pl;
+}
+
 // Whether a launch runs in the whole-row kernel for narrow maps: the plain
 // forward (rows in either direction, no gate or carried states) of rows of at
 // most 16 columns with at most 16 states. There one wave of 16 channels does
@@ -620,7 +642,7 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
     if (takes_narrow(mode, batch, d_inner, d_state, H, W, z || h_init || h_last))
         return dispatch_narrow(x, delta, A, B, C, D, y, static_cast<int>(batch), static_cast<int>(d_inner),
                                static_cast<int>(d_state), static_cast<int>(H), static_cast<int>(W), flip_h, stream);
-    Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
+    Plan pl = forward_plan<T>(batch, d_inner, d_state, H, W, mode, z || h_init || h_last || hh_init || hh_last);
     pl.flip_h = flip_h;
     pl.z = z;
     pl.h_init = h_init;
@@ -1245,7 +1267,7 @@ void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t
             ++*narrow;
             continue;
         }
-        Plan pl = make_plan(batch, d_inner, d_state, H, W, mode);
+        Plan pl = forward_plan<T>(batch, d_inner, d_state, H, W, mode, false);
         const int align = row_align(W);
         choose_coop<T>(pl, H, align);
         ++*(takes_fast<T>(pl, W, align) ? two_row : general);

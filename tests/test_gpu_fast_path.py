@@ -115,3 +115,39 @@ def test_fast_path_layouts(case, monkeypatch):
     yg = pkg.scan_fwd(*args)
     pkg.sync_check()
     check(as_f64(yg), ref, dtype, f"general {shape}")
+
+
+# 8-column strips in chains across workgroups (at most 4 strips and two
+# couriers a workgroup): whole and partial last groups, a half-full last
+# strip, an odd last row, padded states and channels, bf16, both row orders
+WIDE_CHAIN_SHAPES = [
+    ((1, 16, 16, 160, 96), "f32", "4"),    # 12 strips: 3 workgroups a chain
+    ((1, 32, 16, 131, 200), "f32", "4"),   # 25 strips: a last workgroup of 1 strip, odd H
+    ((2, 12, 12, 144, 100), "f32", "3"),   # a half-full last strip, padded channels and states
+    ((1, 16, 16, 136, 512), "bf16", "4"),  # giga-pixel width in bf16
+    ((1, 8, 8, 150, 64), "f32", "2"),      # 1 state a lane, 2 strips a workgroup
+]
+
+
+@pytest.mark.parametrize("flip_h", [False, True])
+@pytest.mark.parametrize("case", WIDE_CHAIN_SHAPES, ids=str)
+def test_fast_path_wide_chains(case, flip_h, monkeypatch):
+    shape, dtype, waves = case
+    monkeypatch.setenv("SSM2D_STRIP", "8")
+    monkeypatch.setenv("SSM2D_WAVES", waves)
+    assert pkg.fwd_kernels(*shape, bf16=dtype == "bf16") == (1, 0, 0)
+    _say(f"fast path, 8-column strips across workgroups {shape} {dtype} waves={waves} flip_h={flip_h}")
+    t = make_random_inputs(*shape, seed=sum(shape) + 260 + flip_h, dtype=dtype)
+    args = to_dev(t, dtype)
+    if flip_h:
+        import oracle
+
+        ref = oracle.fwd(*(t[k] for k in KEYS), flip_h=True)
+    else:
+        ref = ref_of(t)
+    y = pkg.scan_fwd_ex(*args, flip_h=flip_h)
+    pkg.sync_check()
+    check(as_f64(y), ref, dtype, f"fast wide chains {shape}")
+    y2 = pkg.scan_fwd_ex(*args, flip_h=flip_h)
+    pkg.sync_check()
+    assert torch.equal(y, y2)
