@@ -238,6 +238,7 @@ void scan2d_fast_kernel(Params p)
         bool cell_ok[KO];
 #pragma unroll
         for (int c = 0; c < KO; ++c) cell_ok[c] = d_ok && c_out + c < valid;
+        T *const ysink = static_cast<T *>(p.sink) + lane * 2 * KO;  // (8-column strips)
 
         const bool has_left = strip > 0;
         const bool has_right = strip + 1 < p.nstrips;
@@ -478,13 +479,14 @@ void scan2d_fast_kernel(Params p)
                 const long ro = static_cast<long>(i) * rs;
                 const bool second = !TAIL || i + 1 < H;
                 if constexpr (K == 8) {
-                    // each lane its own cells
+                    // each lane its own cells; cells outside the map go to the
+                    // sink, so the stores need no branch (a branch around them
+                    // makes the next step's staging wait for their completion)
 #pragma unroll
-                    for (int c = 0; c < KO; ++c)
-                        if (cell_ok[c]) {
-                            store_elem(yv + ro + c, out[0][c]);
-                            if (second) store_elem(yv + ro + rs + c, out[1][c]);
-                        }
+                    for (int c = 0; c < KO; ++c) {
+                        store_elem(cell_ok[c] ? yv + ro + c : ysink + c, out[0][c]);
+                        if (second) store_elem(cell_ok[c] ? yv + ro + rs + c : ysink + KO + c, out[1][c]);
+                    }
                 } else if constexpr (std::is_same<T, float>::value) {
                     float lo[2], hi[2];
 #pragma unroll
