@@ -22,6 +22,13 @@
 // or bottom to top (runtime row stride). Columns past the map's width are
 // zero-padded: their decay is 1 and their inputs 0, and they are never stored.
 // Padded states (B = C = 0) stay exactly 0.
+//
+// The row loop has no branch: loads and stores go through buffer resources
+// (a lane outside the block or the map uses an offset past the buffer's end:
+// its load reads 0 and its store is dropped by the hardware), and tile
+// writes of such lanes land in spare LDS rows. With branches around them the
+// compiler cannot count the memory operations in flight, and each row began
+// by waiting for every one of them, the last row's output stores included.
 #pragma once
 
 #include "scan2d_kernel.h"
@@ -35,6 +42,31 @@ constexpr int kNarrowWaves = 4;    // waves a workgroup (independent of each oth
 // elements of one row a wave loads per tensor: x and delta hold 16 channel
 // rows, B and C 16 state rows, of at most 16 columns
 constexpr int kNarrowLoads = kNarrowCh * kNarrowMaxW / kWave;
+// a buffer offset past the end of every buffer the kernel addresses (each
+// holds fewer than 2^31 bytes): loads there read 0, stores are dropped
+constexpr unsigned kNarrowOff = 0x80000000u;
+constexpr int kBufferWord3 = 0x00020000;  // descriptor word 3 of a raw gfx9 buffer
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t narrow_rsrc(const void *base, long bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, float)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), soff, 0));
+}
+__device__ __forceinline__ uint16_t buf_load(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, uint16_t)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), soff, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, float v, float)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff), soff, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, float v, uint16_t)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(bf16_bits(v)), r, static_cast<int>(voff), soff, 0);
+}
 
 struct NarrowParams {
     const void *x, *delta, *B, *C;
@@ -49,8 +81,9 @@ template <typename T, int NPL, int WW>
 __global__ __launch_bounds__(kWave *kNarrowWaves) void scan2d_narrow_kernel(const NarrowParams p)
 {
     // one tile per wave: rows of x, delta (16 channels) and B, C (16 states),
-    // WW columns each, fp32
-    __shared__ __align__(16) float s_tile[kNarrowWaves][4][kNarrowCh][WW];
+    // WW columns each, fp32; then 4 spare rows that take the writes of lanes
+    // outside the block
+    __shared__ __align__(16) float s_tile[kNarrowWaves][4][kNarrowCh + 4][WW];
     constexpr int KO = WW / 4;  // finished cells a lane holds after the group sum
 
     const int lane = threadIdx.x % kWave;
@@ -65,30 +98,36 @@ __global__ __launch_bounds__(kWave *kNarrowWaves) void scan2d_narrow_kernel(cons
     const bool d_ok = d < p.d_inner;
     const int H = p.H, W = p.W;
     const long HW = static_cast<long>(H) * W;
-    float(*tile)[kNarrowCh][WW] = s_tile[wave];
+    float(*tile)[kNarrowCh + 4][WW] = s_tile[wave];
 
     // What each lane loads of a row: element e = lane + 64 j of the 16 x W
-    // block, as (row r of the block: channel or state, column c). Offsets of
-    // the row-0 element in its tensor (x / delta and B / C share them; every
-    // tensor has fewer than 2^31 elements), and the tile position; -1 where
-    // the element is outside the tensor.
-    const T *xs = static_cast<const T *>(p.x);
-    const T *ds = static_cast<const T *>(p.delta);
-    const T *bs = static_cast<const T *>(p.B);
-    const T *cs = static_cast<const T *>(p.C);
-    int off_xd[kNarrowLoads], off_bc[kNarrowLoads];
+    // block, as (row r of the block: channel or state, column c). Byte
+    // offsets of the row-0 element in its tensor (x / delta and B / C share
+    // them; every tensor has fewer than 2^31 bytes), kNarrowOff where the
+    // element is outside the tensor, and the tile position (a spare row
+    // outside the block).
+    const long xd_bytes = static_cast<long>(p.batch) * p.d_inner * HW * sizeof(T);
+    const long bc_bytes = static_cast<long>(p.batch) * p.d_state * HW * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rx = narrow_rsrc(p.x, xd_bytes), rd = narrow_rsrc(p.delta, xd_bytes);
+    const __amdgpu_buffer_rsrc_t rb = narrow_rsrc(p.B, bc_bytes), rc = narrow_rsrc(p.C, bc_bytes);
+    const __amdgpu_buffer_rsrc_t ry = narrow_rsrc(p.y, xd_bytes);
+    unsigned off_xd[kNarrowLoads], off_bc[kNarrowLoads];
     int tpos[kNarrowLoads];
 #pragma unroll
     for (int j = 0; j < kNarrowLoads; ++j) {
         const int e = lane + kWave * j;
         const int r = e / W, c = e % W;
         const bool in_block = e < kNarrowCh * W;
-        tpos[j] = in_block ? r * WW + c : -1;
-        off_xd[j] = (in_block && d0 + r < p.d_inner) ? static_cast<int>((static_cast<long>(b) * p.d_inner + d0 + r) * HW + c) : -1;
-        off_bc[j] = (in_block && r < p.d_state) ? static_cast<int>((static_cast<long>(b) * p.d_state + r) * HW + c) : -1;
+        tpos[j] = in_block ? r * WW + c : kNarrowCh * WW + (lane & (4 * WW - 1));
+        off_xd[j] = (in_block && d0 + r < p.d_inner)
+                        ? static_cast<unsigned>(((static_cast<long>(b) * p.d_inner + d0 + r) * HW + c) * sizeof(T))
+                        : kNarrowOff;
+        off_bc[j] = (in_block && r < p.d_state)
+                        ? static_cast<unsigned>(((static_cast<long>(b) * p.d_state + r) * HW + c) * sizeof(T))
+                        : kNarrowOff;
     }
     // the padding of every row stays zero
-    for (int k = lane; k < 4 * kNarrowCh * WW; k += kWave) (&tile[0][0][0])[k] = 0.0f;
+    for (int k = lane; k < 4 * (kNarrowCh + 4) * WW; k += kWave) (&tile[0][0][0])[k] = 0.0f;
 
     float Ap[NPL];
 #pragma unroll
@@ -105,21 +144,36 @@ __global__ __launch_bounds__(kWave *kNarrowWaves) void scan2d_narrow_kernel(cons
 
     const int rs = p.flip_h ? -W : W;
     const int row0 = p.flip_h ? static_cast<int>(HW) - W : 0;
-    T *yv = static_cast<T *>(p.y) + (d_ok ? (static_cast<long>(b) * p.d_inner + d) * HW : 0);
+    // byte offsets of this lane's output cells in row 0 (kNarrowOff: not stored)
+    unsigned off_y[KO];
+#pragma unroll
+    for (int c = 0; c < KO; ++c) {
+        const int col = g * KO + c;
+        off_y[c] = (d_ok && col < W) ? static_cast<unsigned>(((static_cast<long>(b) * p.d_inner + d) * HW + col) * sizeof(T))
+                                     : kNarrowOff;
+    }
 
     // the first row's elements
     T ex[kNarrowLoads], ed[kNarrowLoads], eb[kNarrowLoads], ec[kNarrowLoads];
     auto load_row = [&](int ro) __attribute__((always_inline)) {
+        const int so = ro * static_cast<int>(sizeof(T));
 #pragma unroll
         for (int j = 0; j < kNarrowLoads; ++j) {
-            const bool xd = off_xd[j] >= 0, bc = off_bc[j] >= 0;
-            ex[j] = xd ? xs[off_xd[j] + ro] : T(0);
-            ed[j] = xd ? ds[off_xd[j] + ro] : T(0);
-            eb[j] = bc ? bs[off_bc[j] + ro] : T(0);
-            ec[j] = bc ? cs[off_bc[j] + ro] : T(0);
+            ex[j] = buf_load(rx, off_xd[j], so, T());
+            ed[j] = buf_load(rd, off_xd[j], so, T());
+            eb[j] = buf_load(rb, off_bc[j], so, T());
+            ec[j] = buf_load(rc, off_bc[j], so, T());
         }
     };
     load_row(row0);
+
+    // a row's outputs are stored at the start of the next row, after that
+    // row's loads: the wait at the top of a row (for the loads issued a row
+    // earlier) then never waits on stores just issued
+    float pend[KO];
+#pragma unroll
+    for (int c = 0; c < KO; ++c) pend[c] = 0.0f;
+    int pend_so = 0;
 
     for (int t = 0; t < H; ++t) {
         const int ro = row0 + t * rs;
@@ -127,15 +181,17 @@ __global__ __launch_bounds__(kWave *kNarrowWaves) void scan2d_narrow_kernel(cons
         // LDS accesses of one wave complete in order)
 #pragma unroll
         for (int j = 0; j < kNarrowLoads; ++j) {
-            if (tpos[j] >= 0) {
-                (&tile[0][0][0])[tpos[j]] = elem_value(ex[j]);
-                (&tile[1][0][0])[tpos[j]] = elem_value(ed[j]);
-                (&tile[2][0][0])[tpos[j]] = elem_value(eb[j]);
-                (&tile[3][0][0])[tpos[j]] = elem_value(ec[j]);
-            }
+            (&tile[0][0][0])[tpos[j]] = elem_value(ex[j]);
+            (&tile[1][0][0])[tpos[j]] = elem_value(ed[j]);
+            (&tile[2][0][0])[tpos[j]] = elem_value(eb[j]);
+            (&tile[3][0][0])[tpos[j]] = elem_value(ec[j]);
         }
-        // the next row's loads, in flight during this row's arithmetic
-        if (t + 1 < H) load_row(ro + rs);
+        // the next row's loads (the last row loads itself again), in flight
+        // during this row's arithmetic
+        load_row(t + 1 < H ? ro + rs : ro);
+        // the previous row's outputs (none before the first row)
+#pragma unroll
+        for (int c = 0; c < KO; ++c) buf_store(ry, t > 0 ? off_y[c] : kNarrowOff, pend_so, pend[c], T());
 
         float acc[WW];
 #pragma unroll
@@ -168,14 +224,12 @@ __global__ __launch_bounds__(kWave *kNarrowWaves) void scan2d_narrow_kernel(cons
         float out[KO];
         reduce_groups<WW, 4>(acc, out, g);
         const float *xrow = &tile[0][chl][g * KO];
-        if (d_ok) {
 #pragma unroll
-            for (int c = 0; c < KO; ++c) {
-                const int col = g * KO + c;
-                if (col < W) store_elem(yv + ro + col, __builtin_fmaf(Dd, xrow[c], out[c]));
-            }
-        }
+        for (int c = 0; c < KO; ++c) pend[c] = __builtin_fmaf(Dd, xrow[c], out[c]);
+        pend_so = ro * static_cast<int>(sizeof(T));
     }
+#pragma unroll
+    for (int c = 0; c < KO; ++c) buf_store(ry, off_y[c], pend_so, pend[c], T());
 }
 
 template <typename T>

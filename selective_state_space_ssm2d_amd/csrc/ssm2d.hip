@@ -625,10 +625,13 @@ Plan forward_plan(int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, in
 // spread a few tall maps over more waves. SSM2D_NARROW=0 never takes it,
 // SSM2D_NARROW=2 always where it applies.
 inline bool takes_narrow(int mode, int64_t batch, int64_t d_inner, int64_t d_state, int64_t H, int64_t W,
-                         bool carries)
+                         bool carries, int elem_bytes)
 {
     const int env = env_int("SSM2D_NARROW", 1);
     if (env <= 0 || mode != 0 || carries || W > 16 || d_state > 16) return false;
+    // its buffer offsets are 32-bit: every tensor under 2^31 bytes
+    const int64_t limit = int64_t{1} << 31;
+    if (batch * d_inner * H * W * elem_bytes >= limit || batch * d_state * H * W * elem_bytes >= limit) return false;
     return env >= 2 || H <= 128 || batch * ((d_inner + 15) / 16) >= 256;
 }
 
@@ -639,7 +642,7 @@ int launch(const T *x, const T *delta, const float *A, const T *B, const T *C, c
            const WsEntry *fixed_ws = nullptr, const float *hh_init = nullptr, float *hh_last = nullptr)
 {
     if (hh_init || hh_last) mode |= kModeRowCarry;
-    if (takes_narrow(mode, batch, d_inner, d_state, H, W, z || h_init || h_last))
+    if (takes_narrow(mode, batch, d_inner, d_state, H, W, z || h_init || h_last, static_cast<int>(sizeof(T))))
         return dispatch_narrow(x, delta, A, B, C, D, y, static_cast<int>(batch), static_cast<int>(d_inner),
                                static_cast<int>(d_state), static_cast<int>(H), static_cast<int>(W), flip_h, stream);
     Plan pl = forward_plan<T>(batch, d_inner, d_state, H, W, mode, z || h_init || h_last || hh_init || hh_last);
@@ -1263,7 +1266,7 @@ void count_fwd_launches(int64_t batch, int64_t d_inner, int64_t d_state, int64_t
         const int mode = (flags & SSM2D_FOUR_WAY)
                              ? (((q & 2) ? kModeFlipW : 0) | vf | (q == 0 ? acc : kModeAccumulate))
                              : (((flags & SSM2D_FLIP_W) ? kModeFlipW : 0) | vf | acc);
-        if (takes_narrow(mode, batch, d_inner, d_state, H, W, false)) {
+        if (takes_narrow(mode, batch, d_inner, d_state, H, W, false, static_cast<int>(sizeof(T)))) {
             ++*narrow;
             continue;
         }
