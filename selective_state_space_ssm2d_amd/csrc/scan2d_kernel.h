@@ -984,10 +984,13 @@ __global__ __launch_bounds__(kWave * max_waves(K, NPL, G, MODE)) void scan2d_fwd
         T *ybase[KO];  // row 0 of the scan (accumulating calls read y there)
 #pragma unroll
         for (int c = 0; c < KO; ++c) ybase[c] = ydst[c];
-        // Whole-strip stores: with 4-aligned rows and a full strip, each
-        // channel's cells are gathered into one lane of row 0 and stored as
-        // chunks; other strips, and accumulating calls, store cell by cell.
-        const bool vec_store = !ACC && (ALIGN == 4) && (valid == K) && p.vec_store;
+        // Whole-strip stores: with 4-aligned rows and a full 4-column strip,
+        // each channel's cells are gathered into one lane of row 0 and stored
+        // as chunks; other strips, and accumulating calls, store cell by cell.
+        // (8-column strips store cell by cell at compile time: a second store
+        // form under a branch makes the compiler's wait counts after the
+        // stores pessimistic, and gathering 8 cells costs more than it saves.)
+        const bool vec_store = K == 4 && !ACC && (ALIGN == 4) && (valid == K) && p.vec_store;
         const bool vec_lane = (pair_lane<K, G>(lane) < CPW) && d_ok;
         T *yvec = static_cast<T *>(p.y) + (static_cast<long>(b) * p.d_inner + (vec_lane ? d : 0)) * HW + row0 +
                   (FW ? W - j0 - K : j0) + pair_offset<K, G, FW>(lane);

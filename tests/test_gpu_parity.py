@@ -125,10 +125,11 @@ def test_wide_strips(shape, groups, monkeypatch):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_row_store_forms(vec, strip, groups, dtype, monkeypatch):
     """Both output store forms (one cell per lane, or a channel's cells
-    gathered into wider stores) for every strip width, lane layout and type,
-    scanning rows left to right and right to left (the other directions run
-    8 groups and 4-column strips). Rows are 4-aligned; with 8-column strips the
-    last strip is partial and stores its cells one by one."""
+    gathered into wider stores; 8-column strips always store cell by cell,
+    so there SSM2D_VECSTORE=1 must change nothing) for every strip width,
+    lane layout and type, scanning rows left to right and right to left (the
+    other directions run 8 groups and 4-column strips). Rows are 4-aligned;
+    with 8-column strips the last strip is partial."""
     monkeypatch.setenv("SSM2D_VECSTORE", vec)
     monkeypatch.setenv("SSM2D_STRIP", strip)
     monkeypatch.setenv("SSM2D_GROUPS", groups)
