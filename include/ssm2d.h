@@ -427,8 +427,9 @@ int ssm2d_fwd_kernels(int bf16, int64_t batch, int64_t d_inner, int64_t d_state,
  *   SSM2D_WAVES=n        strips per workgroup (forces chains across workgroups)
  *   SSM2D_COOP=0         per-wave input packets instead of the shared row ring
  *   SSM2D_VECSTORE=0|1   cell-by-cell output stores, or each channel's cells
- *                        gathered into wider stores (default: 1 for 4-column
- *                        strips, 0 for 8-column strips)
+ *                        gathered into wider stores (default 1; 4-column
+ *                        strips only: 8-column strips always store cell by
+ *                        cell)
  *   SSM2D_RING=n         rows of the bounded global carry ring (default 32;
  *                        n < 8 or n >= H: one slot a row)
  *   SSM2D_OVERFLOW=0|1|2 overflow rows after the bounded ring: none (then
