@@ -257,8 +257,8 @@ def test_fwd_kernels_query(lib, monkeypatch):
     launch: the two-rows-per-step kernel for the plain forward of rows of a
     multiple of 4 columns whose chains span workgroups (every such layout
     with SSM2D_FAST=2), the whole-row kernel for the plain forward of narrow
-    maps (short, or a batch of at least 256 waves; every narrow map with
-    SSM2D_NARROW=2, none with 0), the general kernel for direction/order bits,
+    maps (short, or a batch of at least 256 waves, every tensor under 2^31
+    bytes; every narrow map with SSM2D_NARROW=2, none with 0), the general kernel for direction/order bits,
     ragged rows and SSM2D_FAST=0; argument errors as the forward's."""
     assert pkg.fwd_kernels(1, 128, 16, 384, 512) == (1, 0, 0)
     assert pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True) == (0, 1, 0)   # chains in one workgroup
@@ -274,6 +274,10 @@ def test_fwd_kernels_query(lib, monkeypatch):
     assert pkg.fwd_kernels(64, 768, 16, 14, 17) == (0, 1, 0)     # more than 16 columns
     assert pkg.fwd_kernels(1, 16, 16, 4096, 16) == (0, 1, 0)     # one tall map: strips
     assert pkg.fwd_kernels(1, 16, 16, 128, 16) == (0, 0, 1)      # a short one: whole rows
+    # the whole-row kernel addresses its tensors with 32-bit buffer offsets:
+    # x of 4096 x 1024 x 14 x 14 is 3.3 GB in fp32 (strips), 1.6 GB in bf16
+    assert pkg.fwd_kernels(4096, 1024, 16, 14, 14) == (0, 1, 0)
+    assert pkg.fwd_kernels(4096, 1024, 16, 14, 14, bf16=True) == (0, 0, 1)
     fast, general, narrow = pkg.fwd_kernels(1, 128, 16, 384, 512, four_way=True)
     assert (fast, general, narrow) == (1, 3, 0)   # the first corner is the plain scan
     assert sum(pkg.fwd_kernels(32, 192, 16, 56, 56, bf16=True, four_way=True)) == 4
