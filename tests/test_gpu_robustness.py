@@ -272,3 +272,25 @@ def test_ticket_blocks(tblk, monkeypatch):
         y = pkg.scan_fwd(*args)
         pkg.sync_check()
         check(as_f64(y), ref, "f32", f"tblk={tblk} fast={fast}")
+
+
+@pytest.mark.parametrize("tblk", ["1", "8"])
+def test_ticket_blocks_wide_chains(tblk, monkeypatch):
+    """The giga-pixel map in 8-column strips across workgroups (4 strips and
+    two couriers a workgroup) with the bounded ring alone, tickets dealt in
+    blocks of 1 and 8 chains: bit for bit equal to the default plan's run,
+    sampled maps exact against the oracle."""
+    shape = (1, 128, 16, 384, 512)
+    t = make_random_inputs(*shape, seed=150)
+    args = to_dev(t, "f32")
+    y0 = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    monkeypatch.setenv("SSM2D_OVERFLOW", "0")
+    monkeypatch.setenv("SSM2D_TICKET_BLOCK", tblk)
+    assert pkg.fwd_kernels(*shape) == (1, 0, 0)
+    _say(f"wide chains, ticket blocks of {tblk}")
+    y = pkg.scan_fwd(*args)
+    pkg.sync_check()
+    assert torch.equal(y, y0)
+    maps = [0, 77, 127]
+    check(as_f64(y).reshape(128, 384, 512)[maps], ref_of(t, maps=maps), "f32", f"wide chains tblk={tblk}")
